@@ -1,0 +1,113 @@
+"""fp64 CPU oracle for the RWKV-7 WKV7 forward -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The HIP product path never imports it,
+and it imports nothing from the product package.
+
+The arithmetic lives in ``wkv7_oracle.c`` (plain sequential fp64, libm
+``exp``, no fast-math); this module only builds it with gcc, loads it with
+ctypes and converts numpy arrays to contiguous float64.  The recurrence and
+the reading of the pages it follows are documented in the C file's header
+(rwkv-ops README, section "rwkv7op 使用方法" and section
+"rwkv7_op_rnn 使用方法").
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "wkv7_oracle.c")
+_LIB = os.path.join(_HERE, "libwkv7_oracle.so")
+_lib = None
+
+
+def build(force=True):
+    """Compile the oracle with gcc (-O2, OpenMP, no fast-math)."""
+    cmd = ["gcc", "-O2", "-fno-fast-math", "-fopenmp", "-shared", "-fPIC",
+           "-std=c99", _SRC, "-o", _LIB + ".tmp", "-lm"]
+    if force or not os.path.exists(_LIB):
+        subprocess.check_call(cmd)
+        os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build(force=True)
+    lib = ctypes.CDLL(_LIB)
+    d = ctypes.c_void_p
+    i = ctypes.c_int
+    lib.wkv7_oracle_fwd.argtypes = [i, i, i, i, i] + [d] * 10
+    lib.wkv7_oracle_fwd.restype = i
+    lib.wkv7_oracle_step.argtypes = [i, i, i, i] + [d] * 8
+    lib.wkv7_oracle_step.restype = i
+    lib.wkv7_oracle_max_threads.restype = i
+    lib.wkv7_oracle_set_threads.argtypes = [i]
+    _lib = lib
+    return lib
+
+
+def _f64(x):
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(x):
+    return None if x is None else x.ctypes.data_as(ctypes.c_void_p)
+
+
+def fwd(r, w, k, v, a, b, initial_state=None, mask=None):
+    """WKV7 forward.  r,w,k,a,b: [B,T,H,K]; v: [B,T,H,V];
+    initial_state: [B,H,K,V] or None (zeros); mask: [B,T] (nonzero updates)
+    or None.  Returns (o [B,T,H,V], final_state [B,H,K,V]) in float64."""
+    lib = _load()
+    r, w, k, v, a, b = (_f64(x) for x in (r, w, k, v, a, b))
+    B, T, H, K = r.shape
+    V = v.shape[-1]
+    for x in (w, k, a, b):
+        assert x.shape == (B, T, H, K)
+    assert v.shape == (B, T, H, V)
+    s0 = None if initial_state is None else _f64(initial_state)
+    if s0 is not None:
+        assert s0.shape == (B, H, K, V)
+    m = None
+    if mask is not None:
+        m = np.ascontiguousarray((np.asarray(mask) != 0).astype(np.uint8))
+        assert m.shape == (B, T)
+    o = np.zeros((B, T, H, V), np.float64)
+    sf = np.zeros((B, H, K, V), np.float64)
+    rc = lib.wkv7_oracle_fwd(B, T, H, K, V, _ptr(r), _ptr(w), _ptr(k), _ptr(v),
+                             _ptr(a), _ptr(b), _ptr(s0), _ptr(m), _ptr(o), _ptr(sf))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return o, sf
+
+
+def step(r, w, k, v, a, b, state):
+    """One decode token.  r,w,k,a,b: [B,H,K]; v: [B,H,V]; state: [B,H,K,V].
+    Returns (o [B,H,V], new_state) in float64; the input array is not
+    modified."""
+    lib = _load()
+    r, w, k, v, a, b = (_f64(x) for x in (r, w, k, v, a, b))
+    B, H, K = r.shape
+    V = v.shape[-1]
+    st = _f64(state).copy()
+    assert st.shape == (B, H, K, V)
+    o = np.zeros((B, H, V), np.float64)
+    rc = lib.wkv7_oracle_step(B, H, K, V, _ptr(r), _ptr(w), _ptr(k), _ptr(v),
+                              _ptr(a), _ptr(b), _ptr(st), _ptr(o))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return o, st
+
+
+def max_threads():
+    return _load().wkv7_oracle_max_threads()
+
+
+def set_threads(n):
+    _load().wkv7_oracle_set_threads(int(n))

@@ -1,0 +1,163 @@
+/*
+ * wkv7_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, sequential fp64 CPU evaluation of the RWKV-7 WKV7
+ * generalized-delta-rule forward recurrence.  It exists so that the HIP
+ * kernels can be checked against something obviously correct.  Only the
+ * test-suite, the smoke check and the CPU-baseline leg of the benchmark may
+ * load it; the product path never calls it and shares no code with it.
+ *
+ * What it computes (per sequence b and head h, independently):
+ *
+ *   S      : K x V state, starts at initial_state[b,h] (zeros when absent)
+ *   for t = 0 .. T-1:
+ *     if mask[b,t] != 0 (or no mask):
+ *       sb[j]   = sum_i b_t[i] * S[i][j]                       (old state)
+ *       S[i][j] = exp(w_t[i]) * S[i][j] + a_t[i] * sb[j] + k_t[i] * v_t[j]
+ *     o_t[j] = sum_i r_t[i] * S[i][j]                          (new state)
+ *   final_state[b,h] = S
+ *
+ * Sources (rwkv-ops README, PyPI page rwkv-ops 0.7.4 and the rwkv_ops 0.9.0
+ * wheel METADATA, section "rwkv7op 使用方法", docstring of
+ * generalized_delta_rule):
+ *   - r, w, k, a, b are [B,T,H,K], v and o are [B,T,H,V], seq-first layout;
+ *   - w ("gk") is the decay in log space, so the per-channel factor is exp(w);
+ *   - mask [B,T]: 1 updates the state, 0 leaves it unchanged;
+ *   - initial_state / final_state are [N,H,K,V] with N = number of sequences,
+ *     and a missing initial state means zeros (section "rwkv7_op_rnn 使用方法"
+ *     states the same for the single-step operator).
+ * The pages do not print the update equation itself.  The reading used here
+ * is the generalized delta rule written above: the low-rank term a_t (b_t^T S)
+ * acts on the state before this token's decay, a sits on the K side, b
+ * contracts with the state, and o_t reads the updated state S_t, with no
+ * scale on r and no bonus term.  A masked token keeps S and still emits
+ * o_t = S^T r_t.
+ *
+ * Layouts (row-major, C order):
+ *   r,w,k,a,b : [B][T][H][K]     v, o : [B][T][H][V]
+ *   state     : [B][H][K][V]     mask : [B][T] uint8
+ *
+ * Parity pins (closed forms, invariants and a hand-worked example) live in
+ * tests/test_oracle_pins.py; every function here is pinned by them.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define IDX_TOK(b, t, h, i, T, H, D) ((((size_t)(b) * (T) + (t)) * (H) + (h)) * (D) + (i))
+#define IDX_ST(b, h, i, j, H, K, V) ((((size_t)(b) * (H) + (h)) * (K) + (i)) * (V) + (j))
+
+/* One token of the recurrence on a single K x V state (row-major, in place).
+ * sb is caller scratch of length V. */
+static void one_token(int K, int V, double *S, const double *r, const double *w,
+                      const double *k, const double *v, const double *a,
+                      const double *b, int update, double *o, double *sb)
+{
+    if (update) {
+        for (int j = 0; j < V; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < K; ++i) acc += b[i] * S[(size_t)i * V + j];
+            sb[j] = acc;
+        }
+        for (int i = 0; i < K; ++i) {
+            double d = exp(w[i]);
+            for (int j = 0; j < V; ++j) {
+                double *s = &S[(size_t)i * V + j];
+                *s = d * (*s) + a[i] * sb[j] + k[i] * v[j];
+            }
+        }
+    }
+    for (int j = 0; j < V; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < K; ++i) acc += r[i] * S[(size_t)i * V + j];
+        o[j] = acc;
+    }
+}
+
+/* Forward over a whole sequence for every (b, h).
+ * s0 may be NULL (zeros), mask may be NULL (all tokens update),
+ * s_final may be NULL (not written).  s_final may alias s0.
+ * Returns 0, or -1 on bad sizes / missing buffers. */
+int wkv7_oracle_fwd(int B, int T, int H, int K, int V,
+                    const double *r, const double *w, const double *k,
+                    const double *v, const double *a, const double *b,
+                    const double *s0, const uint8_t *mask,
+                    double *o, double *s_final)
+{
+    if (B < 0 || T < 0 || H < 0 || K <= 0 || V <= 0) return -1;
+    if (T > 0 && (!r || !w || !k || !v || !a || !b || !o)) return -1;
+    const long long nseq = (long long)B * H;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long long bh = 0; bh < nseq; ++bh) {
+        const int bb = (int)(bh / H), h = (int)(bh % H);
+        double *S = (double *)malloc(sizeof(double) * (size_t)K * V);
+        double *sb = (double *)malloc(sizeof(double) * (size_t)V);
+        if (s0)
+            memcpy(S, &s0[IDX_ST(bb, h, 0, 0, H, K, V)], sizeof(double) * (size_t)K * V);
+        else
+            memset(S, 0, sizeof(double) * (size_t)K * V);
+        for (int t = 0; t < T; ++t) {
+            const int upd = mask ? (mask[(size_t)bb * T + t] != 0) : 1;
+            one_token(K, V, S,
+                      &r[IDX_TOK(bb, t, h, 0, T, H, K)], &w[IDX_TOK(bb, t, h, 0, T, H, K)],
+                      &k[IDX_TOK(bb, t, h, 0, T, H, K)], &v[IDX_TOK(bb, t, h, 0, T, H, V)],
+                      &a[IDX_TOK(bb, t, h, 0, T, H, K)], &b[IDX_TOK(bb, t, h, 0, T, H, K)],
+                      upd, &o[IDX_TOK(bb, t, h, 0, T, H, V)], sb);
+        }
+        if (s_final)
+            memcpy(&s_final[IDX_ST(bb, h, 0, 0, H, K, V)], S, sizeof(double) * (size_t)K * V);
+        free(sb);
+        free(S);
+    }
+    return 0;
+}
+
+/* Single-token decode for every (b, h): inputs are [B][H][K] ([B][H][V] for
+ * v and o); state [B][H][K][V] is read and overwritten in place.  This is
+ * the T = 1 case of the forward (section "rwkv7_op_rnn 使用方法": the
+ * single-step operator reuses the rwkv7_op definition). */
+int wkv7_oracle_step(int B, int H, int K, int V,
+                     const double *r, const double *w, const double *k,
+                     const double *v, const double *a, const double *b,
+                     double *state, double *o)
+{
+    if (B < 0 || H < 0 || K <= 0 || V <= 0) return -1;
+    if ((long long)B * H > 0 && (!r || !w || !k || !v || !a || !b || !state || !o)) return -1;
+    const long long nseq = (long long)B * H;
+
+#pragma omp parallel for schedule(static)
+    for (long long bh = 0; bh < nseq; ++bh) {
+        double *sb = (double *)malloc(sizeof(double) * (size_t)V);
+        one_token(K, V, &state[(size_t)bh * K * V],
+                  &r[(size_t)bh * K], &w[(size_t)bh * K], &k[(size_t)bh * K],
+                  &v[(size_t)bh * V], &a[(size_t)bh * K], &b[(size_t)bh * K],
+                  1, &o[(size_t)bh * V], sb);
+        free(sb);
+    }
+    return 0;
+}
+
+/* Thread control for the OpenMP loop over (b, h); used to report how many
+ * host threads a timed oracle run used. */
+int wkv7_oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void wkv7_oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
