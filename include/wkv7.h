@@ -1,0 +1,123 @@
+/*
+ * wkv7.h -- C ABI of libwkv7.so: the RWKV-7 WKV7 generalized-delta-rule
+ * forward and single-token decode on MI355X (gfx950).
+ *
+ * Operation (rwkv-ops README, PyPI rwkv-ops 0.7.4 and rwkv_ops 0.9.0 METADATA,
+ * section "rwkv7op 使用方法", docstring of generalized_delta_rule; the
+ * single-token form is section "rwkv7_op_rnn 使用方法"):
+ *
+ *   per sequence b and head h, with a K x V fp32 state S (rows K, columns V):
+ *     if mask[b,t] != 0:  S = diag(exp(w_t)) S + a_t (b_t^T S) + k_t v_t^T
+ *     o_t = S^T r_t
+ *   w is the decay in log space (normally <= 0).  A token whose mask byte is
+ *   0 leaves S unchanged and still emits o_t = S^T r_t.  The update formula
+ *   itself is not printed on those pages; this is the generalized delta rule
+ *   reading (low-rank term from the state before this token's decay, a on the
+ *   K side, b contracting with the state, output from the updated state, no
+ *   scale on r, no bonus term).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers, row-major and contiguous,
+ *     16-byte aligned.  The caller owns every buffer; the library allocates
+ *     no device memory and keeps no pointer after the call returns.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
+ *     default stream).  No call synchronises; results are ready when the
+ *     stream reaches them.
+ *   - Every call returns a wkv7_status_t.  Nothing aborts or throws.  Size,
+ *     pointer, dtype and alignment checks run on the host before any HIP
+ *     call, so they work on a machine without a GPU.  Data values are not
+ *     inspected: NaN / Inf propagate.
+ *   - Supported sizes: K == V, K in {64, 128}.
+ *   - Thread safety: the library holds no mutable global state; concurrent
+ *     calls on different streams are independent.
+ */
+#ifndef WKV7_H
+#define WKV7_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    WKV7_F32 = 0,   /* fp32 inputs and output (the state is fp32 always)   */
+    WKV7_BF16 = 1   /* bf16 inputs and output; fp32 state                   */
+} wkv7_dtype_t;
+
+typedef enum {
+    WKV7_ALGO_AUTO = 0,       /* library chooses (see wkv7_fwd)            */
+    WKV7_ALGO_RECURRENT = 1,  /* token-by-token fp32 recurrence            */
+    WKV7_ALGO_CHUNKED = 2     /* 16-token chunks on bf16 MFMA (bf16 only)  */
+} wkv7_algo_t;
+
+typedef enum {
+    WKV7_OK = 0,
+    WKV7_ERR_INVALID_ARG = 1, /* NULL required pointer, bad size, misaligned */
+    WKV7_ERR_UNSUPPORTED = 2, /* valid request this build does not implement */
+    WKV7_ERR_HIP = 3          /* a HIP launch failed                         */
+} wkv7_status_t;
+
+/*
+ * wkv7_fwd -- forward over whole sequences (section "rwkv7op 使用方法").
+ *
+ *   dtype          WKV7_F32 or WKV7_BF16: element type of r,w,k,v,a,b and o.
+ *   B, T, H        batch, sequence length, heads.  B, H >= 1; T >= 0.
+ *   K, V           key and value head size; K == V in {64, 128}.
+ *   r,w,k,a,b      [B,T,H,K] dtype (seq-first layout).  Read only.
+ *   v              [B,T,H,V] dtype.  Read only.
+ *   initial_state  [B,H,K,V] fp32, or NULL for a zero state.  Read only.
+ *   mask           [B,T] uint8 (nonzero = update, 0 = keep), or NULL for
+ *                  all tokens updating.  Read only.
+ *   o              [B,T,H,V] dtype.  Written (every element).
+ *   final_state    [B,H,K,V] fp32, or NULL to skip it.  Written.  It may be
+ *                  the same buffer as initial_state (in-place state passing);
+ *                  any other overlap between buffers is undefined.
+ *   algo           WKV7_ALGO_AUTO picks the chunked kernel for bf16 when the
+ *                  sequences are long enough to amortise it and the
+ *                  recurrent kernel otherwise; fp32 always runs the recurrent
+ *                  kernel.  WKV7_ALGO_CHUNKED with fp32 returns
+ *                  WKV7_ERR_UNSUPPORTED.
+ *   stream         hipStream_t to enqueue on.
+ * With T == 0, o is empty and final_state (if given) receives initial_state
+ * (zeros when initial_state is NULL).
+ */
+wkv7_status_t wkv7_fwd(int dtype, int B, int T, int H, int K, int V,
+                       const void *r, const void *w, const void *k,
+                       const void *v, const void *a, const void *b,
+                       const float *initial_state, const uint8_t *mask,
+                       void *o, float *final_state, int algo, void *stream);
+
+/*
+ * wkv7_step -- one decode token per sequence, state updated in place
+ * (section "rwkv7_op_rnn 使用方法": the T = 1 case of the forward).
+ *
+ *   dtype          WKV7_F32 or WKV7_BF16 for r,w,k,v,a,b and o.
+ *   B, H, K, V     as for wkv7_fwd; B, H >= 1; K == V in {64, 128}.
+ *   r,w,k,a,b      [B,H,K] dtype.  Read only.
+ *   v              [B,H,V] dtype.  Read only.
+ *   state          [B,H,K,V] fp32.  Read, then overwritten with the new state.
+ *   o              [B,H,V] dtype.  Written.  Must not overlap state.
+ *   stream         hipStream_t to enqueue on.
+ */
+wkv7_status_t wkv7_step(int dtype, int B, int H, int K, int V,
+                        const void *r, const void *w, const void *k,
+                        const void *v, const void *a, const void *b,
+                        float *state, void *o, void *stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *wkv7_strerror(int status);
+
+/* Which kernel wkv7_fwd would launch for these arguments under algo:
+ * returns WKV7_ALGO_RECURRENT or WKV7_ALGO_CHUNKED, or -1 if the arguments
+ * would be rejected.  Host only; launches nothing. */
+int wkv7_fwd_path(int dtype, int B, int T, int H, int K, int V, int algo);
+
+/* ABI version of this header (major * 100 + minor). */
+int wkv7_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WKV7_H */

@@ -1,0 +1,125 @@
+// C ABI of libwkv7.so: argument validation, path choice and launches.
+// Declarations and the contract of every entry point: include/wkv7.h.
+#include <stdint.h>
+
+#include "../../include/wkv7.h"
+#include "wkv7_common.hpp"
+#include "wkv7_internal.hpp"
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Sequences shorter than this run on the recurrent kernel under AUTO: the
+// chunked kernel's per-chunk set-up only pays off across several chunks.
+constexpr int kChunkedMinT = 64;
+
+wkv7_status_t check_common(int dtype, int B, int H, int K, int V)
+{
+    if (dtype != WKV7_F32 && dtype != WKV7_BF16) return WKV7_ERR_INVALID_ARG;
+    if (B <= 0 || H <= 0 || K <= 0 || V <= 0) return WKV7_ERR_INVALID_ARG;
+    if (K != V || (K != 64 && K != 128)) return WKV7_ERR_UNSUPPORTED;
+    if ((long long)B * H > (1ll << 30)) return WKV7_ERR_UNSUPPORTED;
+    return WKV7_OK;
+}
+
+int choose_path(int dtype, int T, int algo)
+{
+    if (algo == WKV7_ALGO_RECURRENT) return WKV7_ALGO_RECURRENT;
+    if (algo == WKV7_ALGO_CHUNKED) return dtype == WKV7_BF16 ? WKV7_ALGO_CHUNKED : -1;
+    if (algo != WKV7_ALGO_AUTO) return -1;
+    if (dtype == WKV7_F32) return WKV7_ALGO_RECURRENT;
+    return T >= kChunkedMinT ? WKV7_ALGO_CHUNKED : WKV7_ALGO_RECURRENT;
+}
+
+}  // namespace
+
+extern "C" {
+
+int wkv7_version(void) { return 100; }
+
+const char *wkv7_strerror(int status)
+{
+    switch (status) {
+    case WKV7_OK: return "ok";
+    case WKV7_ERR_INVALID_ARG: return "invalid argument (null pointer, bad size, dtype or alignment)";
+    case WKV7_ERR_UNSUPPORTED: return "unsupported configuration (K == V in {64, 128} required; chunked path is bf16 only)";
+    case WKV7_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+int wkv7_fwd_path(int dtype, int B, int T, int H, int K, int V, int algo)
+{
+    if (check_common(dtype, B, H, K, V) != WKV7_OK || T < 0) return -1;
+    return choose_path(dtype, T, algo);
+}
+
+wkv7_status_t wkv7_fwd(int dtype, int B, int T, int H, int K, int V,
+                       const void *r, const void *w, const void *k,
+                       const void *v, const void *a, const void *b,
+                       const float *initial_state, const uint8_t *mask,
+                       void *o, float *final_state, int algo, void *stream)
+{
+    wkv7_status_t st = check_common(dtype, B, H, K, V);
+    if (st != WKV7_OK) return st;
+    if (T < 0) return WKV7_ERR_INVALID_ARG;
+    if ((long long)B * T * H * K > (1ll << 40)) return WKV7_ERR_UNSUPPORTED;
+    if (algo != WKV7_ALGO_AUTO && algo != WKV7_ALGO_RECURRENT && algo != WKV7_ALGO_CHUNKED)
+        return WKV7_ERR_INVALID_ARG;
+    if (T > 0) {
+        const void *req[] = {r, w, k, v, a, b, o};
+        for (const void *p : req)
+            if (!p || !aligned16(p)) return WKV7_ERR_INVALID_ARG;
+    }
+    if (initial_state && !aligned16(initial_state)) return WKV7_ERR_INVALID_ARG;
+    if (final_state && !aligned16(final_state)) return WKV7_ERR_INVALID_ARG;
+    const int path = choose_path(dtype, T, algo);
+    if (path < 0) return WKV7_ERR_UNSUPPORTED;
+
+    hipStream_t s = (hipStream_t)stream;
+    if (T == 0) {
+        if (!final_state) return WKV7_OK;
+        const size_t n = (size_t)B * H * K * V;
+        return wkv7::launch_state_copy(initial_state, final_state, n, s) == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
+    }
+    wkv7::FwdArgs args{B, T, H, K, r, w, k, v, a, b, initial_state, mask, o, final_state};
+    hipError_t e = path == WKV7_ALGO_CHUNKED ? wkv7::launch_chunked(args, s)
+                                             : wkv7::launch_recurrent(dtype, args, s);
+    return e == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
+}
+
+wkv7_status_t wkv7_step(int dtype, int B, int H, int K, int V,
+                        const void *r, const void *w, const void *k,
+                        const void *v, const void *a, const void *b,
+                        float *state, void *o, void *stream)
+{
+    wkv7_status_t st = check_common(dtype, B, H, K, V);
+    if (st != WKV7_OK) return st;
+    const void *req[] = {r, w, k, v, a, b, state, o};
+    for (const void *p : req)
+        if (!p || !aligned16(p)) return WKV7_ERR_INVALID_ARG;
+    wkv7::StepArgs args{B, H, K, r, w, k, v, a, b, state, o};
+    return wkv7::launch_step(dtype, args, (hipStream_t)stream) == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
+}
+
+}  // extern "C"
+
+namespace wkv7 {
+
+__global__ void state_copy_kernel(const float *__restrict__ src, float *__restrict__ dst, size_t n)
+{
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        dst[i] = src ? src[i] : 0.0f;
+}
+
+hipError_t launch_state_copy(const float *s0, float *sf, size_t n, hipStream_t stream)
+{
+    if (s0 == sf) return hipSuccess;
+    size_t blocks = (n + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(state_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, s0, sf, n);
+    return hipGetLastError();
+}
+
+}  // namespace wkv7

@@ -1,0 +1,443 @@
+// Chunked WKV7 forward on bf16 MFMA (bf16 I/O, fp32 state).
+//
+// The recurrence (rwkv-ops README, section "rwkv7op 使用方法", read as the
+// generalized delta rule) is evaluated 16 tokens at a time.  Within a chunk
+// with start state S (K x V, fp32), log-decay prefix G_i = sum_{m<=i} w_m and
+// G_{-1} = 0 (per channel), u_i = b_i^T S_{i-1} unrolls to
+//
+//   U   = T (B~ S + M_bk V)                    T = (I - M_ba)^-1
+//   O   = R~ S + M_ra U + M_rk V
+//   S' = diag(e^{G_L}) S + A~^T U + K~^T V
+//
+// with  R~ = r e^{G},  B~ = b e^{G_{i-1}},  A^ = a e^{-G},  K^ = k e^{-G},
+// A~ = a e^{G_L - G},  K~ = k e^{G_L - G},  M_ba = B~ A^^T and M_bk = B~ K^^T
+// strictly lower, M_ra = R~ A^^T and M_rk = R~ K^^T lower with diagonal.
+// Every factor of the form e^{G_i - G_j} with j <= i is <= 1, and the split
+// factors stay finite while the chunk's decay sum is above -60; chunks beyond
+// that (or with w > 0) take an exact token-by-token path instead.  A token
+// with mask 0 (or past T) gets w = a = k = 0, an exact identity step.
+//
+// Layout of the work.  One workgroup per (b, h) holds the state in MFMA
+// accumulator layout: wave w owns columns [16w, 16w+16), lane (g = l/16,
+// j = l%16) rows 16q + 4g + i of column 16w + j.  Each super-step handles NP
+// chunks: first wave p < NP prepares chunk c0 + p on its own (no cross-wave
+// traffic) and leaves every operand of the serial step in its LDS slot, in
+// per-lane fragment order; after a barrier all waves run the short S-dependent
+// chain for the NP chunks on their columns.  The raw tiles of the next
+// super-step are requested before the serial phase so their latency hides
+// behind it.
+//
+// Precision.  MFMA operands are bf16 with fp32 accumulation; the r.k and b.k
+// chunk matrices use a hi/lo split (3 products) and every product with the
+// exact-bf16 value tile V splits its left operand (2 products), which keeps the
+// error near the bf16 rounding of the output.
+#include "wkv7_common.hpp"
+#include "wkv7_internal.hpp"
+
+namespace wkv7 {
+
+constexpr float kMaxChunkDecay = 60.0f;
+
+template <int D> struct CK {
+    static constexpr int NW = D / 16;              // waves = 16-column state slices
+    static constexpr int NT = NW * kWave;
+    static constexpr int NP = (D == 64) ? 4 : 2;   // chunks per super-step
+    static constexpr int NCB = D / 32;             // 32-channel blocks
+    static constexpr int NRT = D / 16;             // 16-row state tiles
+    // Slot layout in bytes; fragments are 64 lanes x (16 or 8) bytes.
+    static constexpr int OFF_B = 0;                       // B~ A-frags, NCB x 1024
+    static constexpr int OFF_R = OFF_B + NCB * 1024;      // R~ A-frags
+    static constexpr int OFF_TINV = OFF_R + NCB * 1024;   // T A-frag (16x16x16)
+    static constexpr int OFF_NBKH = OFF_TINV + 512;
+    static constexpr int OFF_NBKL = OFF_NBKH + 512;
+    static constexpr int OFF_MRA = OFF_NBKL + 512;
+    static constexpr int OFF_MRKH = OFF_MRA + 512;
+    static constexpr int OFF_MRKL = OFF_MRKH + 512;
+    static constexpr int OFF_AT = OFF_MRKL + 512;         // A~^T A-frags, NRT x 512
+    static constexpr int OFF_KTH = OFF_AT + NRT * 512;
+    static constexpr int OFF_KTL = OFF_KTH + NRT * 512;
+    static constexpr int OFF_V = OFF_KTL + NRT * 512;     // V B-frags per 16 columns
+    static constexpr int OFF_EGL = OFF_V + NW * 512;      // e^{G_L}, D floats
+    static constexpr int OFF_FLAG = OFF_EGL + D * 4;
+    static constexpr int SLOT = OFF_FLAG + 16;
+    static constexpr int LDS = NP * SLOT;
+};
+
+// Raw bf16 tiles of one chunk in the precompute lane layout: lane (t = l%16,
+// g = l/16) holds token t, channels 32s + 4g + {0..3} (x[s][*][0]) and
+// 32s + 16 + 4g + {0..3} (x[s][*][1]).  Array order: r, w, k, a, b, v.
+template <int D> struct RawTile {
+    u32x2 x[CK<D>::NCB][6][2];
+    int upd;     // token updates the state
+    int valid;   // token exists (t0 + t < T)
+};
+
+template <int D>
+__device__ __forceinline__ void load_raw(RawTile<D> &rt, const uint16_t *const *src,
+                                         const uint8_t *mask, int T, int H, int bb, int h,
+                                         int chunk, int lane)
+{
+    const int t = lane & 15, g = lane >> 4;
+    const int tok = chunk * 16 + t;
+    rt.valid = tok < T;
+    rt.upd = rt.valid && (mask == nullptr || mask[(size_t)bb * T + tok] != 0);
+    const size_t base = (((size_t)bb * T + (rt.valid ? tok : 0)) * H + h) * D + 4 * g;
+#pragma unroll
+    for (int s = 0; s < CK<D>::NCB; ++s)
+#pragma unroll
+        for (int arr = 0; arr < 6; ++arr)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                u32x2 val = {0u, 0u};
+                if (rt.valid) val = *(const u32x2 *)(src[arr] + base + 32 * s + 16 * hh);
+                rt.x[s][arr][hh] = val;
+            }
+}
+
+__device__ __forceinline__ void unpack8(const u32x2 *x, float *out)
+{
+    out[0] = bf16_lo(x[0][0]); out[1] = bf16_hi(x[0][0]);
+    out[2] = bf16_lo(x[0][1]); out[3] = bf16_hi(x[0][1]);
+    out[4] = bf16_lo(x[1][0]); out[5] = bf16_hi(x[1][0]);
+    out[6] = bf16_lo(x[1][1]); out[7] = bf16_hi(x[1][1]);
+}
+
+__device__ __forceinline__ bf16x8 pack8(const float *x)
+{
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+        bf16x2 p = cvt2(x[e], x[e + 1]);
+        o[e] = p[0];
+        o[e + 1] = p[1];
+    }
+    return o;
+}
+
+// hi/lo split: hi = bf16(x), lo = bf16(x - hi).
+__device__ __forceinline__ void split8(const float *x, bf16x8 &hi, bf16x8 &lo)
+{
+    hi = pack8(x);
+    float rem[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rem[e] = x[e] - (float)hi[e];
+    lo = pack8(rem);
+}
+
+__device__ __forceinline__ void split4(f32x4 x, bf16x4 &hi, bf16x4 &lo)
+{
+    hi = cvt4(x);
+    f32x4 rem;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rem[i] = x[i] - (float)hi[i];
+    lo = cvt4(rem);
+}
+
+__device__ __forceinline__ void st8(char *p, bf16x4 v) { *(bf16x4 *)p = v; }
+__device__ __forceinline__ void st16(char *p, bf16x8 v) { *(bf16x8 *)p = v; }
+__device__ __forceinline__ bf16x4 ld8(const char *p) { return *(const bf16x4 *)p; }
+__device__ __forceinline__ bf16x8 ld16(const char *p) { return *(const bf16x8 *)p; }
+
+// Prepare every S-independent operand of one chunk into its LDS slot.
+// Executed by one wave; `psel[hh]` is the B-fragment that copies channel half
+// hh of a 32-channel block to a token-contiguous (transposed) accumulator.
+template <int D>
+__device__ void precompute(const RawTile<D> &rt, char *slot, int lane, const bf16x8 *psel)
+{
+    using C = CK<D>;
+    const int t = lane & 15, g = lane >> 4;
+    (void)t;
+    f32x4 mraT = zero4(), mrkT = zero4(), mba = zero4(), mbaT = zero4(), mbk = zero4();
+    bool extreme = false;
+
+#pragma unroll
+    for (int s = 0; s < C::NCB; ++s) {
+        float rv[8], wv[8], kv[8], av[8], bv[8];
+        unpack8(rt.x[s][0], rv);
+        unpack8(rt.x[s][1], wv);
+        unpack8(rt.x[s][2], kv);
+        unpack8(rt.x[s][3], av);
+        unpack8(rt.x[s][4], bv);
+        float Rt[8], Bt[8], Ah[8], Kh[8], At[8], Kt[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float we = rt.upd ? wv[e] : 0.0f;
+            const float ae = rt.upd ? av[e] : 0.0f;
+            const float ke = rt.upd ? kv[e] : 0.0f;
+            extreme |= we > 0.0f;
+            const float G = row_scan16(we);
+            const float GL = row_bcast15(G);
+            extreme |= GL < -kMaxChunkDecay;
+            const float eG = __expf(G);
+            const float enG = __expf(-G);
+            const float eGp = row_shr<1>(eG, 1.0f);
+            const float eGL = row_bcast15(eG);
+            const float ft = enG * eGL;
+            Rt[e] = rv[e] * eG;
+            Bt[e] = bv[e] * eGp;
+            Ah[e] = ae * enG;
+            Kh[e] = ke * enG;
+            At[e] = ae * ft;
+            Kt[e] = ke * ft;
+            if (t == 0) {
+                const int ch = 32 * s + 4 * g + (e & 3) + 16 * (e >> 2);
+                *(float *)(slot + C::OFF_EGL + ch * 4) = eGL;
+            }
+        }
+        bf16x8 Rh, Rl, Bh, Bl, Khh, Khl, Kth, Ktl;
+        split8(Rt, Rh, Rl);
+        split8(Bt, Bh, Bl);
+        split8(Kh, Khh, Khl);
+        split8(Kt, Kth, Ktl);
+        const bf16x8 Ahh = pack8(Ah);
+        const bf16x8 Ath = pack8(At);
+        bf16x8 Vb;
+        {
+            float vv[8];
+            unpack8(rt.x[s][5], vv);
+            Vb = pack8(vv);   // exact: v already holds bf16 values
+        }
+
+        // Chunk matrices, contraction over this block's 32 channels.
+        mraT = mfma32(Ahh, Rh, mraT);                 // (R~ A^^T)^T
+        mrkT = mfma32(Khh, Rh, mrkT);                 // (R~ K^^T)^T, hi/lo split
+        mrkT = mfma32(Khl, Rh, mrkT);
+        mrkT = mfma32(Khh, Rl, mrkT);
+        mba = mfma32(Bh, Ahh, mba);                   // B~ A^^T
+        mbaT = mfma32(Ahh, Bh, mbaT);                 // (B~ A^^T)^T
+        mbk = mfma32(Bh, Khh, mbk);                   // B~ K^^T, hi/lo split
+        mbk = mfma32(Bh, Khl, mbk);
+        mbk = mfma32(Bl, Khh, mbk);
+
+        // Operands contracted over channels with the state: fragment order.
+        st16(slot + C::OFF_B + s * 1024 + lane * 16, Bh);
+        st16(slot + C::OFF_R + s * 1024 + lane * 16, Rh);
+
+        // Operands contracted over tokens: transpose with a selection MFMA
+        // (exact: bf16 values times 1.0 accumulated in fp32).
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int q = 2 * s + hh;
+            st8(slot + C::OFF_AT + q * 512 + lane * 8, cvt4(mfma32(Ath, psel[hh], zero4())));
+            st8(slot + C::OFF_KTH + q * 512 + lane * 8, cvt4(mfma32(Kth, psel[hh], zero4())));
+            st8(slot + C::OFF_KTL + q * 512 + lane * 8, cvt4(mfma32(Ktl, psel[hh], zero4())));
+            st8(slot + C::OFF_V + q * 512 + lane * 8, cvt4(mfma32(Vb, psel[hh], zero4())));
+        }
+    }
+
+    // Causal masks in accumulator layout: element (row = 4g + i, col = j).
+    const int j = lane & 15;
+    f32x4 eye;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 4 * g + i;
+        mba[i] = row > j ? mba[i] : 0.0f;       // M_ba strictly lower
+        mbk[i] = row > j ? mbk[i] : 0.0f;       // M_bk strictly lower
+        mbaT[i] = j > row ? mbaT[i] : 0.0f;     // transpose of strictly lower
+        mraT[i] = j >= row ? mraT[i] : 0.0f;    // transpose of lower with diagonal
+        mrkT[i] = j >= row ? mrkT[i] : 0.0f;
+        eye[i] = row == j ? 1.0f : 0.0f;
+    }
+
+    // T = (I - M_ba)^-1 = (I + N^8)(I + N^4)(I + N^2)(I + N), N = M_ba
+    // nilpotent.  Each matrix X is carried as acc(X) and acc(X^T); then
+    // acc(XY) = mfma(acc(X^T), acc(Y)) and acc((XY)^T) = mfma(acc(Y), acc(X^T)).
+    const bf16x4 n1 = cvt4(mba), n1t = cvt4(mbaT);
+    const f32x4 p2 = mfma16(n1t, n1, zero4()), p2t = mfma16(n1, n1t, zero4());
+    const bf16x4 n2 = cvt4(p2), n2t = cvt4(p2t);
+    const f32x4 p4 = mfma16(n2t, n2, zero4()), p4t = mfma16(n2, n2t, zero4());
+    const bf16x4 n4 = cvt4(p4), n4t = cvt4(p4t);
+    const bf16x4 n8t = cvt4(mfma16(n4, n4t, zero4()));
+    const f32x4 t1 = eye + mba, t1t = eye + mbaT;
+    const bf16x4 t1b = cvt4(t1);
+    const f32x4 t2 = mfma16(n2t, t1b, t1), t2t = mfma16(t1b, n2t, t1t);
+    const bf16x4 t2b = cvt4(t2);
+    const f32x4 t4 = mfma16(n4t, t2b, t2), t4t = mfma16(t2b, n4t, t2t);
+    const f32x4 t8t = mfma16(cvt4(t4), n8t, t4t);        // acc(T^T) = A-frag of T
+    const bf16x4 tinv = cvt4(t8t);
+    st8(slot + C::OFF_TINV + lane * 8, tinv);
+
+    // N_bk = T M_bk, stored as A-frag: acc(N_bk^T) = mfma(acc(M_bk), acc(T^T)).
+    bf16x4 hi, lo;
+    split4(mfma16(cvt4(mbk), tinv, zero4()), hi, lo);
+    st8(slot + C::OFF_NBKH + lane * 8, hi);
+    st8(slot + C::OFF_NBKL + lane * 8, lo);
+    st8(slot + C::OFF_MRA + lane * 8, cvt4(mraT));
+    split4(mrkT, hi, lo);
+    st8(slot + C::OFF_MRKH + lane * 8, hi);
+    st8(slot + C::OFF_MRKL + lane * 8, lo);
+
+    const int any_extreme = __any((int)extreme);
+    if (lane == 0) *(int *)(slot + C::OFF_FLAG) = any_extreme;
+}
+
+// Exact fp32 token-by-token update of this wave's 16 columns for one chunk.
+template <int D>
+__device__ void chunk_exact(f32x4 *S, const uint16_t *r, const uint16_t *w, const uint16_t *k,
+                            const uint16_t *v, const uint16_t *a, const uint16_t *b,
+                            const uint8_t *mask, uint16_t *o, int T, int H, int bb, int h,
+                            int chunk, int wave, int lane)
+{
+    const int g = lane >> 4, j = lane & 15;
+    const int col = wave * 16 + j;
+    for (int tt = 0; tt < 16; ++tt) {
+        const int tok = chunk * 16 + tt;
+        if (tok >= T) break;
+        const bool upd = mask == nullptr || mask[(size_t)bb * T + tok] != 0;
+        const size_t base = (((size_t)bb * T + tok) * H + h) * D;
+        if (upd) {
+            float sb = 0.0f;
+#pragma unroll
+            for (int q = 0; q < D / 16; ++q) {
+                const u32x2 bq = *(const u32x2 *)(b + base + 16 * q + 4 * g);
+                sb += bf16_lo(bq[0]) * S[q][0] + bf16_hi(bq[0]) * S[q][1] +
+                      bf16_lo(bq[1]) * S[q][2] + bf16_hi(bq[1]) * S[q][3];
+            }
+            sb = xor_sum(sb, 16);
+            sb = xor_sum(sb, 32);
+            const float vj = bf16_bits_to_f32(v[base + col]);
+#pragma unroll
+            for (int q = 0; q < D / 16; ++q) {
+                const u32x2 wq = *(const u32x2 *)(w + base + 16 * q + 4 * g);
+                const u32x2 aq = *(const u32x2 *)(a + base + 16 * q + 4 * g);
+                const u32x2 kq = *(const u32x2 *)(k + base + 16 * q + 4 * g);
+                const float we[4] = {bf16_lo(wq[0]), bf16_hi(wq[0]), bf16_lo(wq[1]), bf16_hi(wq[1])};
+                const float ae[4] = {bf16_lo(aq[0]), bf16_hi(aq[0]), bf16_lo(aq[1]), bf16_hi(aq[1])};
+                const float ke[4] = {bf16_lo(kq[0]), bf16_hi(kq[0]), bf16_lo(kq[1]), bf16_hi(kq[1])};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S[q][i] = fmaf(__expf(we[i]), S[q][i], fmaf(ae[i], sb, ke[i] * vj));
+            }
+        }
+        float ov = 0.0f;
+#pragma unroll
+        for (int q = 0; q < D / 16; ++q) {
+            const u32x2 rq = *(const u32x2 *)(r + base + 16 * q + 4 * g);
+            ov += bf16_lo(rq[0]) * S[q][0] + bf16_hi(rq[0]) * S[q][1] +
+                  bf16_lo(rq[1]) * S[q][2] + bf16_hi(rq[1]) * S[q][3];
+        }
+        ov = xor_sum(ov, 16);
+        ov = xor_sum(ov, 32);
+        if (g == 0) o[base + col] = f32_to_bf16_bits(ov);
+    }
+}
+
+// The S-dependent part of one chunk for this wave's 16 columns.
+template <int D>
+__device__ __forceinline__ void chunk_serial(f32x4 *S, const char *slot, uint16_t *o, int T, int H,
+                                             int bb, int h, int chunk, int wave, int lane)
+{
+    using C = CK<D>;
+    const int g = lane >> 4, j = lane & 15;
+    f32x4 X = zero4(), O = zero4();
+#pragma unroll
+    for (int s = 0; s < C::NCB; ++s) {
+        const bf16x4 lo4 = cvt4(S[2 * s]), hi4 = cvt4(S[2 * s + 1]);
+        const bf16x8 sb = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        X = mfma32(ld16(slot + C::OFF_B + s * 1024 + lane * 16), sb, X);
+        O = mfma32(ld16(slot + C::OFF_R + s * 1024 + lane * 16), sb, O);
+    }
+    const bf16x4 vf = ld8(slot + C::OFF_V + wave * 512 + lane * 8);
+    f32x4 U = mfma16(ld8(slot + C::OFF_NBKH + lane * 8), vf, zero4());
+    U = mfma16(ld8(slot + C::OFF_NBKL + lane * 8), vf, U);
+    U = mfma16(ld8(slot + C::OFF_TINV + lane * 8), cvt4(X), U);
+    const bf16x4 ub = cvt4(U);
+    O = mfma16(ld8(slot + C::OFF_MRKH + lane * 8), vf, O);
+    O = mfma16(ld8(slot + C::OFF_MRKL + lane * 8), vf, O);
+    O = mfma16(ld8(slot + C::OFF_MRA + lane * 8), ub, O);
+#pragma unroll
+    for (int q = 0; q < C::NRT; ++q) {
+        const f32x4 eg = *(const f32x4 *)(slot + C::OFF_EGL + (16 * q + 4 * g) * 4);
+        f32x4 acc = S[q] * eg;
+        acc = mfma16(ld8(slot + C::OFF_KTH + q * 512 + lane * 8), vf, acc);
+        acc = mfma16(ld8(slot + C::OFF_KTL + q * 512 + lane * 8), vf, acc);
+        acc = mfma16(ld8(slot + C::OFF_AT + q * 512 + lane * 8), ub, acc);
+        S[q] = acc;
+    }
+    const int col = wave * 16 + j;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int tok = chunk * 16 + 4 * g + i;
+        if (tok < T) o[(((size_t)bb * T + tok) * H + h) * D + col] = f32_to_bf16_bits(O[i]);
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(CK<D>::NT) void chunked_kernel(
+    int T, int H, const uint16_t *__restrict__ r, const uint16_t *__restrict__ w,
+    const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, const uint16_t *__restrict__ a,
+    const uint16_t *__restrict__ b, const float *__restrict__ s0, const uint8_t *__restrict__ mask,
+    uint16_t *__restrict__ o, float *__restrict__ sf)
+{
+    using C = CK<D>;
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    const int bh = blockIdx.x;
+    const int bb = bh / H, h = bh % H;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int g = lane >> 4, j = lane & 15;
+    const uint16_t *src[6] = {r, w, k, a, b, v};
+
+    // Selection fragments: element e of lane (g, n) is 1 where channel
+    // 4g + (e & 3) + 16 (e >> 2) of a block equals 16 hh + n.
+    bf16x8 psel[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            psel[hh][e] = (__bf16)(((e >> 2) == hh && 4 * g + (e & 3) == j) ? 1.0f : 0.0f);
+
+    // State tile: rows 16q + 4g + i, column 16 * wave + j.
+    f32x4 S[C::NRT];
+    const size_t st_base = (size_t)bh * D * D;
+#pragma unroll
+    for (int q = 0; q < C::NRT; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            S[q][i] = s0 ? s0[st_base + (size_t)(16 * q + 4 * g + i) * D + 16 * wave + j] : 0.0f;
+
+    const int nchunks = (T + 15) / 16;
+    RawTile<D> cur;
+    if (wave < C::NP) load_raw<D>(cur, src, mask, T, H, bb, h, wave, lane);
+    for (int c0 = 0; c0 < nchunks; c0 += C::NP) {
+        if (wave < C::NP && c0 + wave < nchunks) precompute<D>(cur, lds + wave * C::SLOT, lane, psel);
+        __syncthreads();
+        if (wave < C::NP && c0 + C::NP + wave < nchunks)
+            load_raw<D>(cur, src, mask, T, H, bb, h, c0 + C::NP + wave, lane);
+#pragma unroll 1
+        for (int p = 0; p < C::NP; ++p) {
+            const int c = c0 + p;
+            if (c >= nchunks) break;
+            const char *slot = lds + p * C::SLOT;
+            if (*(const int *)(slot + C::OFF_FLAG))
+                chunk_exact<D>(S, r, w, k, v, a, b, mask, o, T, H, bb, h, c, wave, lane);
+            else
+                chunk_serial<D>(S, slot, o, T, H, bb, h, c, wave, lane);
+        }
+        __syncthreads();
+    }
+
+    if (sf) {
+#pragma unroll
+        for (int q = 0; q < C::NRT; ++q)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                sf[st_base + (size_t)(16 * q + 4 * g + i) * D + 16 * wave + j] = S[q][i];
+    }
+}
+
+template <int D>
+static hipError_t launch_ck(const FwdArgs &p, hipStream_t stream)
+{
+    const dim3 grid((unsigned)(p.B * p.H)), block(CK<D>::NT);
+    hipLaunchKernelGGL((chunked_kernel<D>), grid, block, CK<D>::LDS, stream, p.T, p.H,
+                       (const uint16_t *)p.r, (const uint16_t *)p.w, (const uint16_t *)p.k,
+                       (const uint16_t *)p.v, (const uint16_t *)p.a, (const uint16_t *)p.b, p.s0,
+                       p.mask, (uint16_t *)p.o, p.sf);
+    return hipGetLastError();
+}
+
+hipError_t launch_chunked(const FwdArgs &p, hipStream_t stream)
+{
+    return p.D == 64 ? launch_ck<64>(p, stream) : launch_ck<128>(p, stream);
+}
+
+}  // namespace wkv7

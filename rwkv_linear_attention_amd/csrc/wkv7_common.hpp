@@ -1,0 +1,92 @@
+// Device helpers shared by the WKV7 kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wkv7 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---- bf16 <-> fp32 -------------------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xffff0000u); }
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t bits) { return __uint_as_float((uint32_t)bits << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 pair (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16x2 cvt2(float a, float b) {
+    f32x2 v = {a, b};
+    return __builtin_convertvector(v, bf16x2);
+}
+__device__ __forceinline__ uint32_t cvt2_bits(float a, float b) {
+    bf16x2 p = cvt2(a, b);
+    return __builtin_bit_cast(uint32_t, p);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float a) {
+    return (uint16_t)(cvt2_bits(a, 0.0f) & 0xffffu);
+}
+__device__ __forceinline__ bf16x4 cvt4(f32x4 v) { return __builtin_convertvector(v, bf16x4); }
+
+// Element loaders for the two I/O types.  bf16 travels as raw uint16_t.
+template <typename T> struct io;
+template <> struct io<float> {
+    __device__ __forceinline__ static float load(const float *p, size_t i) { return p[i]; }
+    __device__ __forceinline__ static void store(float *p, size_t i, float x) { p[i] = x; }
+};
+template <> struct io<uint16_t> {
+    __device__ __forceinline__ static float load(const uint16_t *p, size_t i) { return bf16_bits_to_f32(p[i]); }
+    __device__ __forceinline__ static void store(uint16_t *p, size_t i, float x) { p[i] = f32_to_bf16_bits(x); }
+};
+
+// ---- cross-lane ----------------------------------------------------------
+
+// row_shr:n inside each 16-lane row; lanes without a source receive `fill`.
+template <int N>
+__device__ __forceinline__ float row_shr(float x, float fill) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(fill), __float_as_int(x),
+                                                      0x110 + N, 0xF, 0xF, false));
+}
+// Broadcast lane 15 of each 16-lane row to the whole row (row_newbcast:15).
+__device__ __forceinline__ float row_bcast15(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x15F, 0xF, 0xF, false));
+}
+// Inclusive prefix sum over the 16 lanes of each row (Hillis-Steele).
+__device__ __forceinline__ float row_scan16(float x) {
+    x += row_shr<1>(x, 0.0f);
+    x += row_shr<2>(x, 0.0f);
+    x += row_shr<4>(x, 0.0f);
+    x += row_shr<8>(x, 0.0f);
+    return x;
+}
+
+__device__ __forceinline__ float xor_sum(float x, int mask) { return x + __shfl_xor(x, mask, kWave); }
+
+// ---- MFMA ----------------------------------------------------------------
+// 16x16x32 bf16: lane l supplies A[m = l%16][8 k-slots of group l/16] and
+// B[8 k-slots of group l/16][n = l%16]; the accumulator holds
+// D[4*(l/16) + i][l%16], i = 0..3.  16x16x16 is the same with 4 k-slots.
+
+__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Wave-local LDS ordering: all LDS traffic issued so far has completed.
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+}  // namespace wkv7

@@ -1,0 +1,121 @@
+// Token-by-token WKV7 forward in fp32 (fp32 or bf16 I/O).
+//
+// Recurrence (rwkv-ops README, section "rwkv7op 使用方法"; update read as the
+// generalized delta rule): for every (b, h) and token t with mask != 0
+//   sb = b_t^T S ;  S = diag(exp(w_t)) S + a_t sb^T + k_t v_t^T
+// and for every token  o_t = S^T r_t.
+//
+// One workgroup per (b, h) with D/16 waves; wave w owns state columns
+// [16w, 16w+16).  Lane (j = l%16, g = l/16) keeps rows [g*D/4, (g+1)*D/4) of
+// column 16w + j in VGPRs, so b^T S and S^T r are in-lane FMA chains over D/4
+// rows plus a 4-way cross-lane sum.  Tokens are staged in LDS 16 at a time
+// (fp32, exp(w) precomputed); all lanes of a row group read the same LDS
+// address (broadcast).  This path is latency-bound and serves fp32 I/O,
+// short sequences and few (b, h) pairs.
+#include "wkv7_common.hpp"
+#include "wkv7_internal.hpp"
+
+namespace wkv7 {
+
+template <int D, typename T_IO>
+__global__ __launch_bounds__(D * 4) void recurrent_kernel(
+    int T, int H, const T_IO *__restrict__ r, const T_IO *__restrict__ w,
+    const T_IO *__restrict__ k, const T_IO *__restrict__ v, const T_IO *__restrict__ a,
+    const T_IO *__restrict__ b, const float *__restrict__ s0, const uint8_t *__restrict__ mask,
+    T_IO *__restrict__ o, float *__restrict__ sf)
+{
+    constexpr int TB = 16;          // tokens staged per block
+    constexpr int RPL = D / 4;      // state rows per lane
+    constexpr int NT = D * 4;       // threads
+    __shared__ float s_ew[TB][D], s_a[TB][D], s_b[TB][D], s_k[TB][D], s_r[TB][D], s_v[TB][D];
+    __shared__ int s_upd[TB];
+
+    const int bh = blockIdx.x;
+    const int bb = bh / H, h = bh % H;
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave, lane = tid % kWave;
+    const int col = wave * 16 + (lane & 15);
+    const int g = lane >> 4;
+    const int row0 = g * RPL;
+
+    float S[RPL];
+    const size_t st_base = (size_t)bh * D * D;
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) S[i] = s0 ? s0[st_base + (size_t)(row0 + i) * D + col] : 0.0f;
+
+    for (int t0 = 0; t0 < T; t0 += TB) {
+        const int nt = min(TB, T - t0);
+        __syncthreads();
+        for (int idx = tid; idx < TB * D; idx += NT) {
+            const int tl = idx / D, c = idx % D;
+            float ew = 1.f, av = 0.f, bv = 0.f, kv = 0.f, rv = 0.f, vv = 0.f;
+            if (tl < nt) {
+                const size_t gi = (((size_t)bb * T + t0 + tl) * H + h) * D + c;
+                ew = __expf(io<T_IO>::load(w, gi));
+                av = io<T_IO>::load(a, gi);
+                bv = io<T_IO>::load(b, gi);
+                kv = io<T_IO>::load(k, gi);
+                rv = io<T_IO>::load(r, gi);
+                vv = io<T_IO>::load(v, gi);
+            }
+            s_ew[tl][c] = ew; s_a[tl][c] = av; s_b[tl][c] = bv;
+            s_k[tl][c] = kv; s_r[tl][c] = rv; s_v[tl][c] = vv;
+        }
+        if (tid < TB) s_upd[tid] = (tid < nt) && (mask ? mask[(size_t)bb * T + t0 + tid] != 0 : 1);
+        __syncthreads();
+
+        for (int tl = 0; tl < nt; ++tl) {
+            if (s_upd[tl]) {
+                float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
+#pragma unroll
+                for (int i = 0; i < RPL; i += 4) {
+                    p0 += s_b[tl][row0 + i + 0] * S[i + 0];
+                    p1 += s_b[tl][row0 + i + 1] * S[i + 1];
+                    p2 += s_b[tl][row0 + i + 2] * S[i + 2];
+                    p3 += s_b[tl][row0 + i + 3] * S[i + 3];
+                }
+                float sb = (p0 + p1) + (p2 + p3);
+                sb = xor_sum(sb, 16);
+                sb = xor_sum(sb, 32);
+                const float vj = s_v[tl][col];
+#pragma unroll
+                for (int i = 0; i < RPL; ++i)
+                    S[i] = fmaf(s_ew[tl][row0 + i], S[i], fmaf(s_a[tl][row0 + i], sb, s_k[tl][row0 + i] * vj));
+            }
+            float q0 = 0.f, q1 = 0.f, q2 = 0.f, q3 = 0.f;
+#pragma unroll
+            for (int i = 0; i < RPL; i += 4) {
+                q0 += s_r[tl][row0 + i + 0] * S[i + 0];
+                q1 += s_r[tl][row0 + i + 1] * S[i + 1];
+                q2 += s_r[tl][row0 + i + 2] * S[i + 2];
+                q3 += s_r[tl][row0 + i + 3] * S[i + 3];
+            }
+            float ov = (q0 + q1) + (q2 + q3);
+            ov = xor_sum(ov, 16);
+            ov = xor_sum(ov, 32);
+            if (g == 0) io<T_IO>::store(o, (((size_t)bb * T + t0 + tl) * H + h) * D + col, ov);
+        }
+    }
+    if (sf) {
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) sf[st_base + (size_t)(row0 + i) * D + col] = S[i];
+    }
+}
+
+template <int D, typename T_IO>
+static hipError_t launch_rec(const FwdArgs &p, hipStream_t stream)
+{
+    const dim3 grid((unsigned)(p.B * p.H)), block(D * 4);
+    hipLaunchKernelGGL((recurrent_kernel<D, T_IO>), grid, block, 0, stream, p.T, p.H,
+                       (const T_IO *)p.r, (const T_IO *)p.w, (const T_IO *)p.k, (const T_IO *)p.v,
+                       (const T_IO *)p.a, (const T_IO *)p.b, p.s0, p.mask, (T_IO *)p.o, p.sf);
+    return hipGetLastError();
+}
+
+hipError_t launch_recurrent(int dtype, const FwdArgs &p, hipStream_t stream)
+{
+    if (p.D == 64) return dtype == 0 ? launch_rec<64, float>(p, stream) : launch_rec<64, uint16_t>(p, stream);
+    return dtype == 0 ? launch_rec<128, float>(p, stream) : launch_rec<128, uint16_t>(p, stream);
+}
+
+}  // namespace wkv7

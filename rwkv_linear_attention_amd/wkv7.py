@@ -1,0 +1,144 @@
+"""ctypes binding of libwkv7.so (C ABI declared in include/wkv7.h).
+
+Argument marshalling only: shapes and dtypes are checked, torch allocates the
+outputs, and the library enqueues its kernels on torch's current stream.
+Nothing here computes any part of the operator; if the library is missing the
+call raises instead of falling back.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwkv7.so")
+
+F32, BF16 = 0, 1
+ALGO_AUTO, ALGO_RECURRENT, ALGO_CHUNKED = 0, 1, 2
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
+
+_lib = None
+
+
+def lib():
+    """Load libwkv7.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing; build it with __graft_entry__.build() "
+                           "or python -m rwkv_linear_attention_amd.build")
+    L = ctypes.CDLL(LIB_PATH)
+    p, i = ctypes.c_void_p, ctypes.c_int
+    L.wkv7_fwd.argtypes = [i, i, i, i, i, i] + [p] * 10 + [i, p]
+    L.wkv7_fwd.restype = i
+    L.wkv7_step.argtypes = [i, i, i, i, i] + [p] * 8 + [p]
+    L.wkv7_step.restype = i
+    L.wkv7_strerror.argtypes = [i]
+    L.wkv7_strerror.restype = ctypes.c_char_p
+    L.wkv7_fwd_path.argtypes = [i] * 7
+    L.wkv7_fwd_path.restype = i
+    L.wkv7_version.restype = i
+    _lib = L
+    return L
+
+
+class WKV7Error(ValueError):
+    def __init__(self, status):
+        self.status = status
+        super().__init__(f"wkv7 status {status}: {lib().wkv7_strerror(status).decode()}")
+
+
+def _dtype_code(t):
+    if t == torch.float32:
+        return F32
+    if t == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t}; use float32 or bfloat16")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(t, name, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def fwd(r, w, k, v, a, b, initial_state=None, mask=None, output_final_state=True,
+        algo=ALGO_AUTO, out=None, final_state=None):
+    """WKV7 forward.  r, w, k, a, b: [B,T,H,K]; v: [B,T,H,V] (float32 or
+    bfloat16, one device); initial_state: [B,H,K,V] float32 or None (zeros);
+    mask: [B,T] bool/uint8 (nonzero = update) or None.  Returns
+    (o [B,T,H,V] in the input dtype, final_state [B,H,K,V] float32 or None).
+    `final_state` may be passed as an output buffer, including the
+    initial_state tensor itself for in-place state passing."""
+    dev = r.device
+    B, T, H, K = r.shape
+    V = v.shape[-1]
+    dt = r.dtype
+    code = _dtype_code(dt)
+    for name, t in (("r", r), ("w", w), ("k", k), ("a", a), ("b", b)):
+        _check(t, name, (B, T, H, K), dt, dev)
+    _check(v, "v", (B, T, H, V), dt, dev)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", (B, H, K, V), torch.float32, dev)
+    m = None
+    if mask is not None:
+        if mask.dtype == torch.bool:
+            m = mask.view(torch.uint8)
+        elif mask.dtype == torch.uint8:
+            m = mask
+        else:
+            raise ValueError("mask must be bool or uint8")
+        _check(m, "mask", (B, T), torch.uint8, dev)
+    o = out if out is not None else torch.empty((B, T, H, V), dtype=dt, device=dev)
+    _check(o, "out", (B, T, H, V), dt, dev)
+    sf = None
+    if output_final_state:
+        sf = final_state if final_state is not None else torch.empty((B, H, K, V), dtype=torch.float32, device=dev)
+        _check(sf, "final_state", (B, H, K, V), torch.float32, dev)
+    st = lib().wkv7_fwd(code, B, T, H, K, V, _ptr(r), _ptr(w), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
+                        _ptr(initial_state), _ptr(m), _ptr(o), _ptr(sf), int(algo), _stream(dev))
+    if st != OK:
+        raise WKV7Error(st)
+    return o, sf
+
+
+def step(r, w, k, v, a, b, state, out=None):
+    """One decode token.  r, w, k, a, b: [B,H,K]; v: [B,H,V]; state:
+    [B,H,K,V] float32, updated in place.  Returns o [B,H,V] (input dtype)."""
+    dev = r.device
+    B, H, K = r.shape
+    V = v.shape[-1]
+    dt = r.dtype
+    code = _dtype_code(dt)
+    for name, t in (("r", r), ("w", w), ("k", k), ("a", a), ("b", b)):
+        _check(t, name, (B, H, K), dt, dev)
+    _check(v, "v", (B, H, V), dt, dev)
+    _check(state, "state", (B, H, K, V), torch.float32, dev)
+    o = out if out is not None else torch.empty((B, H, V), dtype=dt, device=dev)
+    _check(o, "out", (B, H, V), dt, dev)
+    st = lib().wkv7_step(code, B, H, K, V, _ptr(r), _ptr(w), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
+                         _ptr(state), _ptr(o), _stream(dev))
+    if st != OK:
+        raise WKV7Error(st)
+    return o
+
+
+def fwd_path(dtype, B, T, H, K, V, algo=ALGO_AUTO):
+    """Kernel wkv7_fwd would launch (ALGO_RECURRENT / ALGO_CHUNKED), or -1."""
+    return lib().wkv7_fwd_path(_dtype_code(dtype), B, T, H, K, V, int(algo))

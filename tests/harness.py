@@ -1,0 +1,79 @@
+"""Shared helpers for the GPU parity tests: seeded inputs, both sides, and
+the comparison rules.
+
+Tolerances (from the operator's accuracy target):
+  fp32 I/O: max |o - o_ref| <= 1e-4 and max |S - S_ref| <= 1e-4.
+  bf16 I/O: max_i |o_i - o_ref,i| <= 0.02 * RMS(o_ref) + 2^-8 * |o_ref,i|
+            (the RMS-relative bound plus one bf16 half-ulp, since rounding
+            an exact output to bf16 alone already costs up to 2^-9 |o|), and
+            max |S - S_ref| <= 0.02 * RMS(S_ref) for the fp32 final state.
+"""
+import numpy as np
+
+import oracle
+from rwkv_linear_attention_amd import synth
+
+ARRAYS = ("r", "w", "k", "v", "a", "b")
+
+
+def to_dev(inp, device="cuda"):
+    import torch
+    dt = inp["dtype"]
+    out = {n: synth.to_torch(inp[n], dt, device) for n in ARRAYS}
+    out["s0"] = None if inp["s0"] is None else torch.from_numpy(inp["s0"]).to(device)
+    out["mask"] = None if inp["mask"] is None else torch.from_numpy(inp["mask"]).to(device)
+    return out
+
+
+def gpu_fwd(dev, algo=0, output_final_state=True):
+    from rwkv_linear_attention_amd import wkv7
+    return wkv7.fwd(dev["r"], dev["w"], dev["k"], dev["v"], dev["a"], dev["b"],
+                    initial_state=dev["s0"], mask=dev["mask"],
+                    output_final_state=output_final_state, algo=algo)
+
+
+def to_np(t):
+    import torch
+    return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
+
+
+def oracle_fwd(inp, bh=None):
+    """Oracle on all (b, h) or on the listed (b, h) pairs (returns lists)."""
+    if bh is None:
+        return oracle.fwd(inp["r"], inp["w"], inp["k"], inp["v"], inp["a"], inp["b"],
+                          inp["s0"], inp["mask"])
+    outs = []
+    for (bb, h) in bh:
+        sl = lambda x: x[bb:bb + 1, :, h:h + 1]
+        s0 = None if inp["s0"] is None else inp["s0"][bb:bb + 1, h:h + 1]
+        m = None if inp["mask"] is None else inp["mask"][bb:bb + 1]
+        o, s = oracle.fwd(sl(inp["r"]), sl(inp["w"]), sl(inp["k"]), sl(inp["v"]),
+                          sl(inp["a"]), sl(inp["b"]), s0, m)
+        outs.append((o[0, :, 0], s[0, 0]))
+    return outs
+
+
+def check(dtype, o, o_ref, s=None, s_ref=None, what="", scale=1.0):
+    """scale=2 compares two GPU results, each within the bound of the exact
+    value (triangle inequality)."""
+    o = np.asarray(o, np.float64)
+    o_ref = np.asarray(o_ref, np.float64)
+    assert o.shape == o_ref.shape, (o.shape, o_ref.shape)
+    assert np.all(np.isfinite(o)), f"{what}: non-finite output"
+    err = np.abs(o - o_ref)
+    if dtype == "f32":
+        assert err.max(initial=0.0) <= 1e-4 * scale, f"{what}: max |do| = {err.max()}"
+        if s is not None:
+            es = np.abs(np.asarray(s) - s_ref).max(initial=0.0)
+            assert es <= 1e-4 * scale, f"{what}: max |dS| = {es}"
+        return err.max(initial=0.0)
+    rms = float(np.sqrt(np.mean(o_ref ** 2))) if o_ref.size else 0.0
+    allow = scale * (0.02 * rms + 2.0 ** -8 * np.abs(o_ref))
+    ratio = float(np.max(err / np.maximum(allow, 1e-30))) if o.size else 0.0
+    assert ratio <= 1.0, f"{what}: worst error {ratio:.3f} x tolerance (RMS {rms:.4g})"
+    if s is not None:
+        s = np.asarray(s, np.float64)
+        srms = float(np.sqrt(np.mean(np.asarray(s_ref) ** 2)))
+        es = float(np.abs(s - s_ref).max(initial=0.0))
+        assert es <= scale * 0.02 * srms or es == 0.0, f"{what}: max |dS| = {es:.3g} vs 0.02*RMS = {0.02 * srms:.3g}"
+    return ratio

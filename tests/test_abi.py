@@ -1,0 +1,113 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/wkv7.h declares, and rejects bad arguments on the host before any
+HIP call (contract stated in include/wkv7.h)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from rwkv_linear_attention_amd import build, wkv7
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wkv7.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    build.build(force=False)
+    return wkv7.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(wkv7_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert {"wkv7_fwd", "wkv7_step", "wkv7_strerror", "wkv7_fwd_path", "wkv7_version"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in wkv7.h but not exported"
+
+
+def test_version_and_strerror(L):
+    assert L.wkv7_version() == 100
+    for code in range(4):
+        assert len(L.wkv7_strerror(code)) > 0
+    assert L.wkv7_strerror(99) == b"unknown status"
+
+
+P = ctypes.c_void_p
+GOOD = P(0x100000)       # 16-byte aligned stand-in; never dereferenced on the error paths
+ODD = P(0x100002)
+
+
+def fwd(L, dtype=1, B=1, T=4, H=1, K=64, V=64, ptrs=None, s0=None, mask=None, sf=None, algo=0):
+    ptrs = ptrs or [GOOD] * 7
+    r, w, k, v, a, b, o = ptrs
+    return L.wkv7_fwd(dtype, B, T, H, K, V, r, w, k, v, a, b, s0, mask, o, sf, algo, None)
+
+
+def step(L, dtype=1, B=1, H=1, K=64, V=64, ptrs=None):
+    ptrs = ptrs or [GOOD] * 8
+    return L.wkv7_step(dtype, B, H, K, V, *ptrs, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), wkv7.ERR_INVALID_ARG),
+    (dict(dtype=-1), wkv7.ERR_INVALID_ARG),
+    (dict(B=0), wkv7.ERR_INVALID_ARG),
+    (dict(H=-3), wkv7.ERR_INVALID_ARG),
+    (dict(T=-1), wkv7.ERR_INVALID_ARG),
+    (dict(K=0), wkv7.ERR_INVALID_ARG),
+    (dict(K=64, V=128), wkv7.ERR_UNSUPPORTED),
+    (dict(K=32, V=32), wkv7.ERR_UNSUPPORTED),
+    (dict(K=256, V=256), wkv7.ERR_UNSUPPORTED),
+    (dict(algo=7), wkv7.ERR_INVALID_ARG),
+    (dict(dtype=0, algo=2), wkv7.ERR_UNSUPPORTED),
+])
+def test_fwd_rejects(L, kw, code):
+    assert fwd(L, **kw) == code
+
+
+@pytest.mark.parametrize("slot", range(7))
+def test_fwd_rejects_null_and_misaligned(L, slot):
+    ptrs = [GOOD] * 7
+    ptrs[slot] = None
+    assert fwd(L, ptrs=ptrs) == wkv7.ERR_INVALID_ARG
+    ptrs[slot] = ODD
+    assert fwd(L, ptrs=ptrs) == wkv7.ERR_INVALID_ARG
+
+
+def test_fwd_rejects_misaligned_states(L):
+    assert fwd(L, s0=ODD) == wkv7.ERR_INVALID_ARG
+    assert fwd(L, sf=ODD) == wkv7.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("slot", range(8))
+def test_step_rejects_null_and_misaligned(L, slot):
+    ptrs = [GOOD] * 8
+    ptrs[slot] = None
+    assert step(L, ptrs=ptrs) == wkv7.ERR_INVALID_ARG
+    ptrs[slot] = ODD
+    assert step(L, ptrs=ptrs) == wkv7.ERR_INVALID_ARG
+
+
+def test_step_rejects_sizes(L):
+    assert step(L, B=0) == wkv7.ERR_INVALID_ARG
+    assert step(L, K=64, V=32) == wkv7.ERR_UNSUPPORTED
+    assert step(L, dtype=5) == wkv7.ERR_INVALID_ARG
+
+
+def test_path_choice(L):
+    R, C = wkv7.ALGO_RECURRENT, wkv7.ALGO_CHUNKED
+    assert L.wkv7_fwd_path(1, 8, 4096, 64, 64, 64, 0) == C
+    assert L.wkv7_fwd_path(1, 16, 4096, 32, 128, 128, 0) == C
+    assert L.wkv7_fwd_path(0, 1, 64, 1, 64, 64, 0) == R          # fp32 is never chunked
+    assert L.wkv7_fwd_path(0, 1, 64, 1, 64, 64, 2) == -1
+    assert L.wkv7_fwd_path(1, 1, 8, 1, 64, 64, 0) == R           # very short sequences
+    assert L.wkv7_fwd_path(1, 1, 8, 1, 64, 64, 2) == C           # forced
+    assert L.wkv7_fwd_path(1, 1, 4096, 1, 64, 64, 1) == R        # forced
+    assert L.wkv7_fwd_path(1, 1, 4096, 1, 48, 48, 0) == -1

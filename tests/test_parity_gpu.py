@@ -1,0 +1,256 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the fp64 oracle.
+
+Inputs come from the seeded generator shared by both sides; the oracle sees
+exactly the values the GPU sees (already rounded to the I/O dtype).  Small
+cases are compared element by element over every output; the full-size
+workloads are compared on sampled (b, h) sequences that the oracle evaluates
+one by one.
+"""
+import numpy as np
+import pytest
+
+import harness as hz
+import oracle
+from rwkv_linear_attention_amd import synth, wkv7
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+REC, CHK = wkv7.ALGO_RECURRENT, wkv7.ALGO_CHUNKED
+
+
+def run_case(inp, algo, what):
+    dev = hz.to_dev(inp)
+    o, sf = hz.gpu_fwd(dev, algo=algo)
+    torch.cuda.synchronize()
+    o_ref, s_ref = hz.oracle_fwd(inp)
+    return hz.check(inp["dtype"], hz.to_np(o), o_ref, hz.to_np(sf), s_ref, what)
+
+
+# ---- the named workloads ------------------------------------------------------
+
+def test_workload0_fp32_full():
+    inp = synth.make(0)
+    assert wkv7.fwd_path(torch.float32, 1, 64, 1, 64, 64) == REC
+    run_case(inp, wkv7.ALGO_AUTO, "workload 0")
+
+
+@pytest.mark.parametrize("algo", [REC, CHK, wkv7.ALGO_AUTO])
+def test_workload1_bf16_mask_state_full(algo):
+    run_case(synth.make(1), algo, f"workload 1 algo {algo}")
+
+
+def sampled_pairs(B, H):
+    pairs = {(0, 0), (B - 1, H - 1), (0, H - 1), (B - 1, 0), (B // 2, H // 2), (1 % B, 3 % H)}
+    return sorted(pairs)
+
+
+@pytest.mark.parametrize("idx", [2, 3])
+def test_full_size_workload_sampled(idx):
+    """Full-size workloads in the launch configuration the benchmark times
+    (ALGO_AUTO -> chunked kernel), checked on sampled sequences."""
+    inp = synth.make(idx)
+    B, T, H, D = inp["r"].shape
+    assert wkv7.fwd_path(torch.bfloat16, B, T, H, D, D) == CHK
+    dev = hz.to_dev(inp)
+    o, sf = hz.gpu_fwd(dev)
+    torch.cuda.synchronize()
+    pairs = sampled_pairs(B, H)
+    refs = hz.oracle_fwd(inp, pairs)
+    for (bb, h), (o_ref, s_ref) in zip(pairs, refs):
+        hz.check("bf16", hz.to_np(o[bb, :, h]), o_ref, hz.to_np(sf[bb, h]), s_ref,
+                 f"workload {idx} (b={bb}, h={h})")
+    assert torch.isfinite(o.float()).all()
+
+
+def test_workload4_decode_steps_sampled():
+    """256 consecutive wkv7_step calls on B=512, H=40, d=64 (state in place),
+    checked on sampled sequences against 256 oracle steps."""
+    inp = synth.make(4)
+    B, T, H, D = inp["r"].shape
+    dev = hz.to_dev(inp)
+    state = dev["s0"].clone()
+    pairs = sampled_pairs(B, H)
+    o_hist = []
+    for t in range(T):
+        o = wkv7.step(*(dev[n][:, t].contiguous() for n in hz.ARRAYS), state)
+        o_hist.append(torch.stack([o[bb, h] for bb, h in pairs]).float().cpu())
+    torch.cuda.synchronize()
+    o_hist = torch.stack(o_hist, 1).numpy().astype(np.float64)    # [pairs, T, V]
+    for pi, (bb, h) in enumerate(pairs):
+        S = inp["s0"][bb:bb + 1, h:h + 1].astype(np.float64)
+        o_ref = np.zeros((T, D))
+        for t in range(T):
+            sl = lambda n: inp[n][bb:bb + 1, t, h:h + 1]
+            ot, S = oracle.step(sl("r"), sl("w"), sl("k"), sl("v"), sl("a"), sl("b"), S)
+            o_ref[t] = ot[0, 0]
+        hz.check("bf16", o_hist[pi], o_ref, hz.to_np(state[bb, h]), S[0, 0],
+                 f"decode (b={bb}, h={h})")
+
+
+# ---- shapes, tails and both kernels -----------------------------------------
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 63, 65, 1000])
+@pytest.mark.parametrize("algo", [REC, CHK])
+def test_shapes_bf16(D, T, algo):
+    inp = synth.make(1, B=1, T=T, H=3, K=D, seed=7 * T + D)
+    run_case(inp, algo, f"D={D} T={T} algo={algo}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("T", [1, 17, 200])
+def test_shapes_fp32(D, T):
+    wl = dict(synth.WORKLOADS[0], dtype="f32")
+    inp = synth.make(wl, B=3, T=T, H=1, K=D, seed=11 * T + D, init=True, mask="bernoulli")
+    run_case(inp, REC, f"fp32 D={D} T={T}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_chunked_equals_recurrent(D):
+    """Both GPU kernels agree on the same inputs, and each agrees with the oracle."""
+    inp = synth.make(1, B=2, T=300, H=2, K=D, seed=99 + D)
+    dev = hz.to_dev(inp)
+    o1, s1 = hz.gpu_fwd(dev, algo=REC)
+    o2, s2 = hz.gpu_fwd(dev, algo=CHK)
+    torch.cuda.synchronize()
+    o_ref, s_ref = hz.oracle_fwd(inp)
+    hz.check("bf16", hz.to_np(o1), o_ref, hz.to_np(s1), s_ref, "recurrent")
+    hz.check("bf16", hz.to_np(o2), o_ref, hz.to_np(s2), s_ref, "chunked")
+    hz.check("bf16", hz.to_np(o2), hz.to_np(o1), hz.to_np(s2), hz.to_np(s1), "chunked vs recurrent", scale=2.0)
+
+
+# ---- masks and state handling ------------------------------------------------
+
+@pytest.mark.parametrize("algo", [REC, CHK])
+@pytest.mark.parametrize("kind", ["zeros", "ones", "bernoulli", "trailing", "leading"])
+def test_masks(algo, kind):
+    inp = synth.make(1, B=3, T=100, H=2, K=64, seed=5)
+    B, T = 3, 100
+    if kind == "zeros":
+        inp["mask"] = np.zeros((B, T), np.uint8)
+    elif kind == "ones":
+        inp["mask"] = np.ones((B, T), np.uint8)
+    elif kind == "trailing":
+        inp["mask"] = np.ones((B, T), np.uint8)
+        inp["mask"][:, 77:] = 0
+    elif kind == "leading":
+        inp["mask"] = np.ones((B, T), np.uint8)
+        inp["mask"][:, :40] = 0
+    run_case(inp, algo, f"mask {kind} algo {algo}")
+    if kind == "zeros":
+        dev = hz.to_dev(inp)
+        _, sf = hz.gpu_fwd(dev, algo=algo)
+        assert torch.equal(sf, dev["s0"]), "all-masked sequence must leave the state bit-exact"
+
+
+@pytest.mark.parametrize("algo", [REC, CHK])
+def test_state_aliasing_and_null_states(algo):
+    inp = synth.make(1, B=2, T=70, H=2, K=64, seed=3)
+    dev = hz.to_dev(inp)
+    o_ref, s_ref = hz.oracle_fwd(inp)
+    # final_state aliasing initial_state
+    st = dev["s0"].clone()
+    o, sf = wkv7.fwd(*(dev[n] for n in hz.ARRAYS), initial_state=st, mask=dev["mask"],
+                     algo=algo, final_state=st)
+    torch.cuda.synchronize()
+    assert sf.data_ptr() == st.data_ptr()
+    hz.check("bf16", hz.to_np(o), o_ref, hz.to_np(st), s_ref, "aliased state")
+    # NULL initial state equals an explicit zero state
+    z = torch.zeros_like(dev["s0"])
+    o1, s1 = wkv7.fwd(*(dev[n] for n in hz.ARRAYS), initial_state=None, mask=dev["mask"], algo=algo)
+    o2, s2 = wkv7.fwd(*(dev[n] for n in hz.ARRAYS), initial_state=z, mask=dev["mask"], algo=algo)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    # NULL final state: output unchanged, nothing else written
+    o3, s3 = wkv7.fwd(*(dev[n] for n in hz.ARRAYS), initial_state=None, mask=dev["mask"],
+                      algo=algo, output_final_state=False)
+    assert s3 is None and torch.equal(o3, o1)
+
+
+def test_state_passing_composition():
+    """fwd over [0, T) equals fwd over [T1, T) from fwd([0, T1)).final."""
+    inp = synth.make(1, B=2, T=160, H=2, K=64, seed=8)
+    dev = hz.to_dev(inp)
+    o, sf = hz.gpu_fwd(dev, algo=CHK)
+    T1 = 48
+    part = lambda lo, hi: {n: dev[n][:, lo:hi].contiguous() for n in hz.ARRAYS}
+    p1, p2 = part(0, T1), part(T1, 160)
+    m1 = dev["mask"][:, :T1].contiguous()
+    m2 = dev["mask"][:, T1:].contiguous()
+    oa, sa = wkv7.fwd(*(p1[n] for n in hz.ARRAYS), initial_state=dev["s0"], mask=m1, algo=CHK)
+    ob, sb = wkv7.fwd(*(p2[n] for n in hz.ARRAYS), initial_state=sa, mask=m2, algo=CHK)
+    torch.cuda.synchronize()
+    o_ref, s_ref = hz.oracle_fwd(inp)
+    hz.check("bf16", hz.to_np(torch.cat([oa, ob], 1)), o_ref, hz.to_np(sb), s_ref, "composed")
+
+
+def test_empty_sequence():
+    inp = synth.make(1, B=2, T=1, H=2, K=64, seed=1)
+    dev = hz.to_dev(inp)
+    empty = {n: dev[n][:, :0].contiguous() for n in hz.ARRAYS}
+    o, sf = wkv7.fwd(*(empty[n] for n in hz.ARRAYS), initial_state=dev["s0"])
+    o2, sf2 = wkv7.fwd(*(empty[n] for n in hz.ARRAYS), initial_state=None)
+    torch.cuda.synchronize()
+    assert o.shape == (2, 0, 2, 64)
+    assert torch.equal(sf, dev["s0"]) and torch.count_nonzero(sf2) == 0
+
+
+@pytest.mark.parametrize("algo", [REC, CHK])
+def test_extreme_decay_tokens(algo):
+    """w = -1e9 on some tokens (a full reset of those channels) and a few
+    positive w: the chunked kernel must take its exact path; outputs stay
+    finite and match the oracle."""
+    inp = synth.make(1, B=2, T=90, H=2, K=64, seed=21)
+    rng = np.random.default_rng(0)
+    w = inp["w"].copy()
+    w[:, 20] = -1e9
+    w[1, 55, :, :8] = -1e9
+    w[0, 70, 1, 3] = 0.05
+    inp["w"] = synth.round_to(w, "bf16")
+    run_case(inp, algo, f"extreme decay algo {algo}")
+
+
+@pytest.mark.parametrize("algo", [REC, CHK])
+def test_outputs_fully_written_and_guarded(algo):
+    """NaN-prefilled output and guard bands around o and the final state:
+    every output element is written and nothing outside is touched."""
+    inp = synth.make(1, B=2, T=37, H=3, K=64, seed=4)
+    dev = hz.to_dev(inp)
+    B, T, H, D = 2, 37, 3, 64
+    n_o = B * T * H * D
+    guard = 1024
+    obuf = torch.full((n_o + 2 * guard,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    sbuf = torch.full((B * H * D * D + 2 * guard,), float("nan"), dtype=torch.float32, device="cuda")
+    o = obuf[guard:guard + n_o].view(B, T, H, D)
+    s = sbuf[guard:guard + B * H * D * D].view(B, H, D, D)
+    wkv7.fwd(*(dev[n] for n in hz.ARRAYS), initial_state=dev["s0"], mask=dev["mask"], algo=algo,
+             out=o, final_state=s)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(s).all()
+    assert torch.isnan(obuf[:guard].float()).all() and torch.isnan(obuf[-guard:].float()).all()
+    assert torch.isnan(sbuf[:guard]).all() and torch.isnan(sbuf[-guard:]).all()
+
+
+def test_step_matches_forward_and_oracle():
+    """T consecutive decode steps equal the forward over T tokens (d=64 and 128)."""
+    for D in (64, 128):
+        inp = synth.make(1, B=3, T=12, H=2, K=D, seed=D, mask="none")
+        dev = hz.to_dev(inp)
+        o_f, s_f = hz.gpu_fwd(dev, algo=REC)
+        st = dev["s0"].clone()
+        outs = [wkv7.step(*(dev[n][:, t].contiguous() for n in hz.ARRAYS), st) for t in range(12)]
+        torch.cuda.synchronize()
+        o_ref, s_ref = hz.oracle_fwd(inp)
+        hz.check("bf16", hz.to_np(torch.stack(outs, 1)), o_ref, hz.to_np(st), s_ref, f"step D={D}")
+        hz.check("bf16", hz.to_np(o_f), o_ref, hz.to_np(s_f), s_ref, f"fwd D={D}")
+
+
+def test_step_fp32():
+    wl = dict(synth.WORKLOADS[4], dtype="f32")
+    inp = synth.make(wl, B=4, T=3, H=5, K=64, seed=77)
+    dev = hz.to_dev(inp)
+    st = dev["s0"].clone()
+    outs = [wkv7.step(*(dev[n][:, t].contiguous() for n in hz.ARRAYS), st) for t in range(3)]
+    torch.cuda.synchronize()
+    o_ref, s_ref = hz.oracle_fwd(inp)
+    hz.check("f32", hz.to_np(torch.stack(outs, 1)), o_ref, hz.to_np(st), s_ref, "step fp32")
