@@ -36,7 +36,9 @@
 
 namespace wkv7 {
 
-constexpr float kMaxChunkDecay = 60.0f;
+// A chunk whose summed decay factor exp(G_L) falls below e^-60 in any channel
+// would need factors up to e^60 in the split form; it takes the exact path.
+constexpr float kMinChunkFactor = 8.75651076e-27f;   // e^-60
 
 template <int D> struct CK {
     static constexpr int NW = D / 16;              // waves = 16-column state slices
@@ -82,16 +84,21 @@ __device__ __forceinline__ void load_raw(RawTile<D> &rt, const uint16_t *const *
     rt.valid = tok < T;
     rt.upd = rt.valid && (mask == nullptr || mask[(size_t)bb * T + tok] != 0);
     const size_t base = (((size_t)bb * T + (rt.valid ? tok : 0)) * H + h) * D + 4 * g;
+    // w, k, a of a token that does not update are loaded as zeros: that makes
+    // it an exact identity step without any select in the arithmetic.
 #pragma unroll
-    for (int s = 0; s < CK<D>::NCB; ++s)
+    for (int arr = 0; arr < 6; ++arr) {
+        const bool take = (arr == 1 || arr == 2 || arr == 3) ? rt.upd : rt.valid;
+        const u32x2 *p = (const u32x2 *)(src[arr] + base);   // 8-byte units
 #pragma unroll
-        for (int arr = 0; arr < 6; ++arr)
+        for (int s = 0; s < CK<D>::NCB; ++s)
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 u32x2 val = {0u, 0u};
-                if (rt.valid) val = *(const u32x2 *)(src[arr] + base + 32 * s + 16 * hh);
+                if (take) val = p[8 * s + 4 * hh];
                 rt.x[s][arr][hh] = val;
             }
+    }
 }
 
 __device__ __forceinline__ void unpack8(const u32x2 *x, float *out)
@@ -159,31 +166,30 @@ __device__ void precompute(const RawTile<D> &rt, char *slot, int lane, const bf1
         unpack8(rt.x[s][3], av);
         unpack8(rt.x[s][4], bv);
         float Rt[8], Bt[8], Ah[8], Kh[8], At[8], Kt[8];
+        int wmax = (int)0x80000000;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float we = rt.upd ? wv[e] : 0.0f;
-            const float ae = rt.upd ? av[e] : 0.0f;
-            const float ke = rt.upd ? kv[e] : 0.0f;
-            extreme |= we > 0.0f;
-            const float G = row_scan16(we);
-            const float GL = row_bcast15(G);
-            extreme |= GL < -kMaxChunkDecay;
-            const float eG = __expf(G);
-            const float enG = __expf(-G);
+            // Positive w (as signed integer bits: > 0) leaves the fast path.
+            wmax = max(wmax, __float_as_int(wv[e]));
+            // Prefix in log2 units: e^{G} = 2^{G2}.
+            const float G2 = row_scan16(wv[e] * 1.4426950408889634f);
+            const float eG = __builtin_amdgcn_exp2f(G2);
+            const float enG = __builtin_amdgcn_exp2f(-G2);
             const float eGp = row_shr<1>(eG, 1.0f);
             const float eGL = row_bcast15(eG);
-            const float ft = enG * eGL;
+            extreme |= eGL < kMinChunkFactor;
             Rt[e] = rv[e] * eG;
             Bt[e] = bv[e] * eGp;
-            Ah[e] = ae * enG;
-            Kh[e] = ke * enG;
-            At[e] = ae * ft;
-            Kt[e] = ke * ft;
+            Ah[e] = av[e] * enG;
+            Kh[e] = kv[e] * enG;
+            At[e] = Ah[e] * eGL;
+            Kt[e] = Kh[e] * eGL;
             if (t == 0) {
                 const int ch = 32 * s + 4 * g + (e & 3) + 16 * (e >> 2);
                 *(float *)(slot + C::OFF_EGL + ch * 4) = eGL;
             }
         }
+        extreme |= wmax > 0;
         bf16x8 Rh, Rl, Bh, Bl, Khh, Khl, Kth, Ktl;
         split8(Rt, Rh, Rl);
         split8(Bt, Bh, Bl);
@@ -191,12 +197,9 @@ __device__ void precompute(const RawTile<D> &rt, char *slot, int lane, const bf1
         split8(Kt, Kth, Ktl);
         const bf16x8 Ahh = pack8(Ah);
         const bf16x8 Ath = pack8(At);
-        bf16x8 Vb;
-        {
-            float vv[8];
-            unpack8(rt.x[s][5], vv);
-            Vb = pack8(vv);   // exact: v already holds bf16 values
-        }
+        // v already holds bf16 values: reinterpret the raw bits.
+        const u32x4 vbits = {rt.x[s][5][0][0], rt.x[s][5][0][1], rt.x[s][5][1][0], rt.x[s][5][1][1]};
+        const bf16x8 Vb = __builtin_bit_cast(bf16x8, vbits);
 
         // Chunk matrices, contraction over this block's 32 channels.
         mraT = mfma32(Ahh, Rh, mraT);                 // (R~ A^^T)^T
@@ -362,7 +365,7 @@ __device__ __forceinline__ void chunk_serial(f32x4 *S, const char *slot, uint16_
 }
 
 template <int D>
-__global__ __launch_bounds__(CK<D>::NT) void chunked_kernel(
+__global__ __launch_bounds__(CK<D>::NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void chunked_kernel(
     int T, int H, const uint16_t *__restrict__ r, const uint16_t *__restrict__ w,
     const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, const uint16_t *__restrict__ a,
     const uint16_t *__restrict__ b, const float *__restrict__ s0, const uint8_t *__restrict__ mask,
@@ -424,6 +427,436 @@ __global__ __launch_bounds__(CK<D>::NT) void chunked_kernel(
     }
 }
 
+// ===========================================================================
+// Warp-specialised variant (K = V = 64).
+//
+// One workgroup per (b, h) with four waves.  Wave 0 is the consumer: it keeps
+// the whole 64 x 64 fp32 state in MFMA accumulator registers and runs only the
+// S-dependent chain.  Waves 1..3 are producers: producer p prepares chunks
+// c = p, p + 3, ... from raw tiles that are streamed into a private LDS buffer
+// with asynchronous global->LDS loads one chunk ahead, and hands the chunk's
+// operands to the consumer through a two-slot LDS ring.  Hand-off uses LDS
+// counters (ready[slot] = chunk + 1 once a slot is filled; done = number of
+// chunks whose operands the consumer has copied out), so producers and the
+// consumer never meet at a workgroup barrier.  Every wait is bounded.
+//
+// Products on the consumer side pair operands along k so that each
+// 16x16x32 MFMA carries two 16-token contractions, and the output is formed
+// transposed (O^T = S^T R~^T + [U;V]^T [M_ra | M_rk]^T) so that each lane
+// stores four adjacent bf16 outputs of one token.
+// ===========================================================================
+
+struct WS64 {
+    static constexpr int D = 64;
+    static constexpr int NCB = 2, NRT = 4, NCT = 4;   // channel blocks, row / column tiles
+    static constexpr int NPROD = 3;
+    static constexpr int NSLOT = 2;
+    // slot layout (bytes)
+    static constexpr int OFF_B = 0;                   // B~ frags, NCB x 1024
+    static constexpr int OFF_R = 2048;                // R~ frags, NCB x 1024
+    static constexpr int OFF_TN = 4096;               // [T | N_bk hi] A-frags, 1024
+    static constexpr int OFF_NBKL = 5120;             // N_bk lo A-frag, 512
+    static constexpr int OFF_MM = 5632;               // [M_ra^T | M_rk^T hi] B-frags, 1024
+    static constexpr int OFF_MRKL = 6656;             // M_rk^T lo B-frag, 512
+    static constexpr int OFF_ATK = 7168;              // [A~^T | K~^T hi] A-frags, NRT x 1024
+    static constexpr int OFF_KTL = 11264;             // K~^T lo A-frags, NRT x 512
+    static constexpr int OFF_V = 13312;               // V frags per column tile, NCT x 512
+    static constexpr int OFF_EGL = 15360;             // e^{G_L}, 64 floats
+    static constexpr int OFF_FLAG = 15616;
+    static constexpr int SLOT = 15632;
+    static constexpr int RAW = 6 * NCB * 1024;        // raw tile of one chunk
+    static constexpr int OFF_SLOTS = 0;
+    static constexpr int OFF_RAW = NSLOT * SLOT;
+    static constexpr int OFF_SYNC = OFF_RAW + NPROD * RAW;
+    static constexpr int LDS = OFF_SYNC + 64;
+};
+
+constexpr int kSpinLimit = 1 << 20;
+
+__device__ __forceinline__ int lds_load_relaxed(int *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_store_relaxed(int *p, int v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+// Wait until *p >= target; gives up after kSpinLimit polls so that a broken
+// hand-off ends the kernel (with wrong results) instead of hanging it.
+__device__ __forceinline__ void spin_ge(int *p, int target)
+{
+    for (int it = 0; it < kSpinLimit; ++it) {
+        if (lds_load_relaxed(p) >= target) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    asm volatile("" ::: "memory");
+}
+
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+// Producer: stream the raw tile of `chunk` into `raw` (6 arrays x NCB blocks,
+// 1 KB each).  Lane l of each load fetches the 16 bytes of token l%16,
+// channels 32s + 8(l/16) .. +7; tokens past T read token T-1 (discarded).
+__device__ __forceinline__ void ws_issue_raw(char *raw, const uint16_t *const *src, int T, int H,
+                                             int bb, int h, int chunk, int lane)
+{
+    constexpr int D = WS64::D;
+    const int t = lane & 15, v = lane >> 4;
+    const int tok = min(chunk * 16 + t, T - 1);
+    const size_t base = (((size_t)bb * T + tok) * H + h) * D + 8 * v;
+#pragma unroll
+    for (int arr = 0; arr < 6; ++arr)
+#pragma unroll
+        for (int s = 0; s < WS64::NCB; ++s)
+            __builtin_amdgcn_global_load_lds(src[arr] + base + 32 * s,
+                                             (lds_ptr_t)(raw + (arr * WS64::NCB + s) * 1024), 16, 0, 0);
+}
+
+// Producer: read the staged raw tile into the register layout used by the
+// precompute (lane (t, g): channels 32s + 16hh + 4g .. +3 of token t).
+__device__ __forceinline__ void ws_read_raw(RawTile<64> &rt, const char *raw, int lane)
+{
+    const int t = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int arr = 0; arr < 6; ++arr)
+#pragma unroll
+        for (int s = 0; s < WS64::NCB; ++s)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+                rt.x[s][arr][hh] = *(const u32x2 *)(raw + (arr * WS64::NCB + s) * 1024 +
+                                                    16 * (t + 16 * (2 * hh + (g >> 1))) + 8 * (g & 1));
+}
+
+// Producer: prepare one chunk's operands into `slot` (layout WS64).
+__device__ void ws_precompute(const RawTile<64> &rt, char *slot, int lane, const bf16x8 *psel)
+{
+    using C = WS64;
+    const int t = lane & 15, g = lane >> 4;
+    f32x4 mraT = zero4(), mrkT = zero4(), mba = zero4(), mbaT = zero4(), mbk = zero4();
+    bool extreme = false;
+
+#pragma unroll
+    for (int s = 0; s < C::NCB; ++s) {
+        float rv[8], wv[8], kv[8], av[8], bv[8];
+        unpack8(rt.x[s][0], rv);
+        unpack8(rt.x[s][1], wv);
+        unpack8(rt.x[s][2], kv);
+        unpack8(rt.x[s][3], av);
+        unpack8(rt.x[s][4], bv);
+        float Rt[8], Bt[8], Ah[8], Kh[8], At[8], Kt[8];
+        int wmax = (int)0x80000000;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            wmax = max(wmax, __float_as_int(wv[e]));
+            const float G2 = row_scan16(wv[e] * 1.4426950408889634f);
+            const float eG = __builtin_amdgcn_exp2f(G2);
+            const float enG = __builtin_amdgcn_exp2f(-G2);
+            const float eGp = row_shr<1>(eG, 1.0f);
+            const float eGL = row_bcast15(eG);
+            extreme |= eGL < kMinChunkFactor;
+            Rt[e] = rv[e] * eG;
+            Bt[e] = bv[e] * eGp;
+            Ah[e] = av[e] * enG;
+            Kh[e] = kv[e] * enG;
+            At[e] = Ah[e] * eGL;
+            Kt[e] = Kh[e] * eGL;
+            if (t == 0) {
+                const int ch = 32 * s + 4 * g + (e & 3) + 16 * (e >> 2);
+                *(float *)(slot + C::OFF_EGL + ch * 4) = eGL;
+            }
+        }
+        extreme |= wmax > 0;
+        bf16x8 Rh, Rl, Bh, Bl, Khh, Khl, Kth, Ktl;
+        split8(Rt, Rh, Rl);
+        split8(Bt, Bh, Bl);
+        split8(Kh, Khh, Khl);
+        split8(Kt, Kth, Ktl);
+        const bf16x8 Ahh = pack8(Ah);
+        const bf16x8 Ath = pack8(At);
+        const u32x4 vbits = {rt.x[s][5][0][0], rt.x[s][5][0][1], rt.x[s][5][1][0], rt.x[s][5][1][1]};
+        const bf16x8 Vb = __builtin_bit_cast(bf16x8, vbits);
+
+        mraT = mfma32(Ahh, Rh, mraT);
+        mrkT = mfma32(Khh, Rh, mrkT);
+        mrkT = mfma32(Khl, Rh, mrkT);
+        mrkT = mfma32(Khh, Rl, mrkT);
+        mba = mfma32(Bh, Ahh, mba);
+        mbaT = mfma32(Ahh, Bh, mbaT);
+        mbk = mfma32(Bh, Khh, mbk);
+        mbk = mfma32(Bh, Khl, mbk);
+        mbk = mfma32(Bl, Khh, mbk);
+
+        st16(slot + C::OFF_B + s * 1024 + lane * 16, Bh);
+        st16(slot + C::OFF_R + s * 1024 + lane * 16, Rh);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int q = 2 * s + hh;
+            st8(slot + C::OFF_ATK + q * 1024 + lane * 16, cvt4(mfma32(Ath, psel[hh], zero4())));
+            st8(slot + C::OFF_ATK + q * 1024 + lane * 16 + 8, cvt4(mfma32(Kth, psel[hh], zero4())));
+            st8(slot + C::OFF_KTL + q * 512 + lane * 8, cvt4(mfma32(Ktl, psel[hh], zero4())));
+            st8(slot + C::OFF_V + q * 512 + lane * 8, cvt4(mfma32(Vb, psel[hh], zero4())));
+        }
+    }
+
+    const int j = lane & 15;
+    f32x4 eye;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 4 * g + i;
+        mba[i] = row > j ? mba[i] : 0.0f;
+        mbk[i] = row > j ? mbk[i] : 0.0f;
+        mbaT[i] = j > row ? mbaT[i] : 0.0f;
+        mraT[i] = j >= row ? mraT[i] : 0.0f;
+        mrkT[i] = j >= row ? mrkT[i] : 0.0f;
+        eye[i] = row == j ? 1.0f : 0.0f;
+    }
+    const bf16x4 n1 = cvt4(mba), n1t = cvt4(mbaT);
+    const f32x4 p2 = mfma16(n1t, n1, zero4()), p2t = mfma16(n1, n1t, zero4());
+    const bf16x4 n2 = cvt4(p2), n2t = cvt4(p2t);
+    const f32x4 p4 = mfma16(n2t, n2, zero4()), p4t = mfma16(n2, n2t, zero4());
+    const bf16x4 n4 = cvt4(p4), n4t = cvt4(p4t);
+    const bf16x4 n8t = cvt4(mfma16(n4, n4t, zero4()));
+    const f32x4 t1 = eye + mba, t1t = eye + mbaT;
+    const bf16x4 t1b = cvt4(t1);
+    const f32x4 t2 = mfma16(n2t, t1b, t1), t2t = mfma16(t1b, n2t, t1t);
+    const bf16x4 t2b = cvt4(t2);
+    const f32x4 t4 = mfma16(n4t, t2b, t2), t4t = mfma16(t2b, n4t, t2t);
+    const bf16x4 tinv = cvt4(mfma16(cvt4(t4), n8t, t4t));
+    bf16x4 hi, lo;
+    split4(mfma16(cvt4(mbk), tinv, zero4()), hi, lo);
+    st8(slot + C::OFF_TN + lane * 16, tinv);
+    st8(slot + C::OFF_TN + lane * 16 + 8, hi);
+    st8(slot + C::OFF_NBKL + lane * 8, lo);
+    st8(slot + C::OFF_MM + lane * 16, cvt4(mraT));
+    split4(mrkT, hi, lo);
+    st8(slot + C::OFF_MM + lane * 16 + 8, hi);
+    st8(slot + C::OFF_MRKL + lane * 8, lo);
+    const int any_extreme = __any((int)extreme);
+    if (lane == 0) *(int *)(slot + C::OFF_FLAG) = any_extreme;
+}
+
+__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b)
+{
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// Consumer, exact path: token-by-token fp32 update of the whole state.
+__device__ void ws_chunk_exact(f32x4 (*S)[4], const uint16_t *r, const uint16_t *w,
+                               const uint16_t *k, const uint16_t *v, const uint16_t *a,
+                               const uint16_t *b, const uint8_t *mask, uint16_t *o, int T, int H,
+                               int bb, int h, int chunk, int lane)
+{
+    constexpr int D = 64;
+    const int g = lane >> 4, j = lane & 15;
+    for (int tt = 0; tt < 16; ++tt) {
+        const int tok = chunk * 16 + tt;
+        if (tok >= T) break;
+        const bool upd = mask == nullptr || mask[(size_t)bb * T + tok] != 0;
+        const size_t base = (((size_t)bb * T + tok) * H + h) * D;
+        if (upd) {
+            float sb[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const u32x2 bq = *(const u32x2 *)(b + base + 16 * q + 4 * g);
+                const float be[4] = {bf16_lo(bq[0]), bf16_hi(bq[0]), bf16_lo(bq[1]), bf16_hi(bq[1])};
+#pragma unroll
+                for (int n = 0; n < 4; ++n)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sb[n] = fmaf(be[i], S[q][n][i], sb[n]);
+            }
+#pragma unroll
+            for (int n = 0; n < 4; ++n) sb[n] = xor_sum(xor_sum(sb[n], 16), 32);
+            float vj[4];
+#pragma unroll
+            for (int n = 0; n < 4; ++n) vj[n] = bf16_bits_to_f32(v[base + 16 * n + j]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const u32x2 wq = *(const u32x2 *)(w + base + 16 * q + 4 * g);
+                const u32x2 aq = *(const u32x2 *)(a + base + 16 * q + 4 * g);
+                const u32x2 kq = *(const u32x2 *)(k + base + 16 * q + 4 * g);
+                const float we[4] = {bf16_lo(wq[0]), bf16_hi(wq[0]), bf16_lo(wq[1]), bf16_hi(wq[1])};
+                const float ae[4] = {bf16_lo(aq[0]), bf16_hi(aq[0]), bf16_lo(aq[1]), bf16_hi(aq[1])};
+                const float ke[4] = {bf16_lo(kq[0]), bf16_hi(kq[0]), bf16_lo(kq[1]), bf16_hi(kq[1])};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float d = __expf(we[i]);
+#pragma unroll
+                    for (int n = 0; n < 4; ++n)
+                        S[q][n][i] = fmaf(d, S[q][n][i], fmaf(ae[i], sb[n], ke[i] * vj[n]));
+                }
+            }
+        }
+        float ov[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const u32x2 rq = *(const u32x2 *)(r + base + 16 * q + 4 * g);
+            const float re[4] = {bf16_lo(rq[0]), bf16_hi(rq[0]), bf16_lo(rq[1]), bf16_hi(rq[1])};
+#pragma unroll
+            for (int n = 0; n < 4; ++n)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ov[n] = fmaf(re[i], S[q][n][i], ov[n]);
+        }
+#pragma unroll
+        for (int n = 0; n < 4; ++n) ov[n] = xor_sum(xor_sum(ov[n], 16), 32);
+        if (g == 0) {
+#pragma unroll
+            for (int n = 0; n < 4; ++n) o[base + 16 * n + j] = f32_to_bf16_bits(ov[n]);
+        }
+    }
+}
+
+// Consumer: the S-dependent part of one chunk for all 64 columns.
+__device__ __forceinline__ void ws_chunk_serial(f32x4 (*S)[4], const char *slot, int *done, int chunk_done,
+                                                uint16_t *o, int T, int H, int bb, int h, int chunk, int lane)
+{
+    using C = WS64;
+    const int g = lane >> 4, t = lane & 15;
+    bf16x8 bt[2], rt[2], atk[4];
+    bf16x4 ktl[4], vf[4];
+    f32x4 egl[4];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        bt[s] = ld16(slot + C::OFF_B + s * 1024 + lane * 16);
+        rt[s] = ld16(slot + C::OFF_R + s * 1024 + lane * 16);
+    }
+    const bf16x8 tn = ld16(slot + C::OFF_TN + lane * 16);
+    const bf16x4 nbkl = ld8(slot + C::OFF_NBKL + lane * 8);
+    const bf16x8 mm = ld16(slot + C::OFF_MM + lane * 16);
+    const bf16x4 mrkl = ld8(slot + C::OFF_MRKL + lane * 8);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        atk[q] = ld16(slot + C::OFF_ATK + q * 1024 + lane * 16);
+        ktl[q] = ld8(slot + C::OFF_KTL + q * 512 + lane * 8);
+        vf[q] = ld8(slot + C::OFF_V + q * 512 + lane * 8);
+        egl[q] = *(const f32x4 *)(slot + C::OFF_EGL + (16 * q + 4 * g) * 4);
+    }
+    // Everything is in registers: release the slot to the producers.
+    lds_wait();
+    lds_store_relaxed(done, chunk_done);
+
+    const int tok = chunk * 16 + t;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+        const bf16x8 sb0 = cat8(cvt4(S[0][n]), cvt4(S[1][n]));
+        const bf16x8 sb1 = cat8(cvt4(S[2][n]), cvt4(S[3][n]));
+        f32x4 X = mfma32(bt[0], sb0, zero4());
+        X = mfma32(bt[1], sb1, X);
+        f32x4 U = mfma16(nbkl, vf[n], zero4());
+        U = mfma32(tn, cat8(cvt4(X), vf[n]), U);
+        const bf16x4 ub = cvt4(U);
+        const bf16x8 uv = cat8(ub, vf[n]);
+        f32x4 Ot = mfma16(vf[n], mrkl, zero4());
+        Ot = mfma32(sb0, rt[0], Ot);
+        Ot = mfma32(sb1, rt[1], Ot);
+        Ot = mfma32(uv, mm, Ot);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            f32x4 acc = S[q][n] * egl[q];
+            acc = mfma16(ktl[q], vf[n], acc);
+            S[q][n] = mfma32(atk[q], uv, acc);
+        }
+        if (tok < T) {
+            const uint32_t lo = cvt2_bits(Ot[0], Ot[1]), hi = cvt2_bits(Ot[2], Ot[3]);
+            *(u32x2 *)(o + (((size_t)bb * T + tok) * H + h) * 64 + 16 * n + 4 * g) = u32x2{lo, hi};
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void chunked64_ws_kernel(
+    int T, int H, const uint16_t *__restrict__ r, const uint16_t *__restrict__ w,
+    const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, const uint16_t *__restrict__ a,
+    const uint16_t *__restrict__ b, const float *__restrict__ s0, const uint8_t *__restrict__ mask,
+    uint16_t *__restrict__ o, float *__restrict__ sf)
+{
+    using C = WS64;
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    const int bh = blockIdx.x;
+    const int bb = bh / H, h = bh % H;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int g = lane >> 4, j = lane & 15;
+    int *ready = (int *)(lds + C::OFF_SYNC);     // ready[NSLOT]
+    int *done = ready + C::NSLOT;
+    const int nchunks = (T + 15) / 16;
+
+    if (threadIdx.x < C::NSLOT + 1) ready[threadIdx.x] = 0;
+    __syncthreads();
+
+    if (wave == 0) {
+        // ---------------- consumer ----------------
+        f32x4 S[4][4];   // S[q][n]: rows 16q + 4g + i, column 16n + j
+        const size_t st_base = (size_t)bh * 64 * 64;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int n = 0; n < 4; ++n)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    S[q][n][i] = s0 ? s0[st_base + (size_t)(16 * q + 4 * g + i) * 64 + 16 * n + j] : 0.0f;
+        for (int c = 0; c < nchunks; ++c) {
+            const char *slot = lds + C::OFF_SLOTS + (c % C::NSLOT) * C::SLOT;
+            spin_ge(&ready[c % C::NSLOT], c + 1);
+            if (*(const int *)(slot + C::OFF_FLAG)) {
+                lds_wait();
+                lds_store_relaxed(done, c + 1);
+                ws_chunk_exact(S, r, w, k, v, a, b, mask, o, T, H, bb, h, c, lane);
+            } else {
+                ws_chunk_serial(S, slot, done, c + 1, o, T, H, bb, h, c, lane);
+            }
+        }
+        if (sf) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int n = 0; n < 4; ++n)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        sf[st_base + (size_t)(16 * q + 4 * g + i) * 64 + 16 * n + j] = S[q][n][i];
+        }
+    } else {
+        // ---------------- producers ----------------
+        const int p = wave - 1;
+        char *raw = lds + C::OFF_RAW + p * C::RAW;
+        const uint16_t *src[6] = {r, w, k, a, b, v};
+        bf16x8 psel[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                psel[hh][e] = (__bf16)(((e >> 2) == hh && 4 * g + (e & 3) == j) ? 1.0f : 0.0f);
+        if (p < nchunks) ws_issue_raw(raw, src, T, H, bb, h, p, lane);
+        for (int c = p; c < nchunks; c += C::NPROD) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            RawTile<64> rt;
+            ws_read_raw(rt, raw, lane);
+            lds_wait();
+            if (c + C::NPROD < nchunks) ws_issue_raw(raw, src, T, H, bb, h, c + C::NPROD, lane);
+            // Tokens that do not update (mask 0, or past T) are identity steps:
+            // zero their w, k, a; tokens past T also get r = b = v = 0.
+            const int tok = c * 16 + (lane & 15);
+            const bool valid = tok < T;
+            const bool upd = valid && (mask == nullptr || mask[(size_t)bb * T + tok] != 0);
+            if (!__all((int)upd)) {
+#pragma unroll
+                for (int s = 0; s < C::NCB; ++s)
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+                        for (int arr = 1; arr <= 3; ++arr)
+                            rt.x[s][arr][hh] = upd ? rt.x[s][arr][hh] : u32x2{0u, 0u};
+                        rt.x[s][0][hh] = valid ? rt.x[s][0][hh] : u32x2{0u, 0u};
+                        rt.x[s][4][hh] = valid ? rt.x[s][4][hh] : u32x2{0u, 0u};
+                        rt.x[s][5][hh] = valid ? rt.x[s][5][hh] : u32x2{0u, 0u};
+                    }
+            }
+            char *slot = lds + C::OFF_SLOTS + (c % C::NSLOT) * C::SLOT;
+            spin_ge(done, c - C::NSLOT + 1);   // the slot's previous chunk is copied out
+            ws_precompute(rt, slot, lane, psel);
+            lds_wait();
+            lds_store_relaxed(&ready[c % C::NSLOT], c + 1);
+        }
+    }
+}
+
 template <int D>
 static hipError_t launch_ck(const FwdArgs &p, hipStream_t stream)
 {
@@ -435,9 +868,23 @@ static hipError_t launch_ck(const FwdArgs &p, hipStream_t stream)
     return hipGetLastError();
 }
 
+static hipError_t launch_ws64(const FwdArgs &p, hipStream_t stream)
+{
+    // More than 64 KB of dynamic LDS needs an explicit opt-in (idempotent).
+    hipError_t e = hipFuncSetAttribute((const void *)chunked64_ws_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, WS64::LDS);
+    if (e != hipSuccess) return e;
+    const dim3 grid((unsigned)(p.B * p.H)), block(256);
+    hipLaunchKernelGGL(chunked64_ws_kernel, grid, block, WS64::LDS, stream, p.T, p.H,
+                       (const uint16_t *)p.r, (const uint16_t *)p.w, (const uint16_t *)p.k,
+                       (const uint16_t *)p.v, (const uint16_t *)p.a, (const uint16_t *)p.b, p.s0,
+                       p.mask, (uint16_t *)p.o, p.sf);
+    return hipGetLastError();
+}
+
 hipError_t launch_chunked(const FwdArgs &p, hipStream_t stream)
 {
-    return p.D == 64 ? launch_ck<64>(p, stream) : launch_ck<128>(p, stream);
+    return p.D == 64 ? launch_ws64(p, stream) : launch_ck<128>(p, stream);
 }
 
 }  // namespace wkv7
