@@ -84,21 +84,35 @@ __device__ __forceinline__ void load_raw(RawTile<D> &rt, const uint16_t *const *
     rt.valid = tok < T;
     rt.upd = rt.valid && (mask == nullptr || mask[(size_t)bb * T + tok] != 0);
     const size_t base = (((size_t)bb * T + (rt.valid ? tok : 0)) * H + h) * D + 4 * g;
-    // w, k, a of a token that does not update are loaded as zeros: that makes
-    // it an exact identity step without any select in the arithmetic.
+    // Unconditional loads (tokens past T read token 0 of the sequence); the
+    // values of tokens that do not update are zeroed where they are used.
 #pragma unroll
     for (int arr = 0; arr < 6; ++arr) {
-        const bool take = (arr == 1 || arr == 2 || arr == 3) ? rt.upd : rt.valid;
         const u32x2 *p = (const u32x2 *)(src[arr] + base);   // 8-byte units
 #pragma unroll
         for (int s = 0; s < CK<D>::NCB; ++s)
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                u32x2 val = {0u, 0u};
-                if (take) val = p[8 * s + 4 * hh];
-                rt.x[s][arr][hh] = val;
-            }
+            for (int hh = 0; hh < 2; ++hh) rt.x[s][arr][hh] = p[8 * s + 4 * hh];
     }
+}
+
+// Make a token that does not update an exact identity step (w = k = a = 0),
+// and a token past T inert (r = b = v = 0 as well).
+template <int D>
+__device__ __forceinline__ void zero_inactive(RawTile<D> &rt, int narr)
+{
+    if (__all(rt.upd)) return;
+#pragma unroll
+    for (int s = 0; s < CK<D>::NCB; ++s)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+            for (int arr = 1; arr <= 3; ++arr)
+                rt.x[s][arr][hh] = rt.upd ? rt.x[s][arr][hh] : u32x2{0u, 0u};
+            rt.x[s][0][hh] = rt.valid ? rt.x[s][0][hh] : u32x2{0u, 0u};
+            rt.x[s][4][hh] = rt.valid ? rt.x[s][4][hh] : u32x2{0u, 0u};
+            if (narr > 5) rt.x[s][5][hh] = rt.valid ? rt.x[s][5][hh] : u32x2{0u, 0u};
+        }
 }
 
 __device__ __forceinline__ void unpack8(const u32x2 *x, float *out)
@@ -149,13 +163,14 @@ __device__ __forceinline__ bf16x8 ld16(const char *p) { return *(const bf16x8 *)
 // Executed by one wave; `psel[hh]` is the B-fragment that copies channel half
 // hh of a 32-channel block to a token-contiguous (transposed) accumulator.
 template <int D>
-__device__ void precompute(const RawTile<D> &rt, char *slot, int lane, const bf16x8 *psel)
+__device__ void precompute(RawTile<D> rt, char *slot, int lane, const bf16x8 *psel)
 {
     using C = CK<D>;
     const int t = lane & 15, g = lane >> 4;
     (void)t;
     f32x4 mraT = zero4(), mrkT = zero4(), mba = zero4(), mbaT = zero4(), mbk = zero4();
     bool extreme = false;
+    zero_inactive<D>(rt, 6);
 
 #pragma unroll
     for (int s = 0; s < C::NCB; ++s) {
@@ -450,12 +465,11 @@ struct WS64 {
     static constexpr int D = 64;
     static constexpr int NCB = 2, NRT = 4, NCT = 4;   // channel blocks, row / column tiles
     static constexpr int NPROD = 3;
-    static constexpr int NSLOT = 2;
+    static constexpr int NSLOT = 3;
     // slot layout (bytes)
     static constexpr int OFF_B = 0;                   // B~ frags, NCB x 1024
     static constexpr int OFF_R = 2048;                // R~ frags, NCB x 1024
-    static constexpr int OFF_TN = 4096;               // [T | N_bk hi] A-frags, 1024
-    static constexpr int OFF_NBKL = 5120;             // N_bk lo A-frag, 512
+    static constexpr int OFF_TN = 4096;               // [T | N_bk] A-frags, 1024
     static constexpr int OFF_MM = 5632;               // [M_ra^T | M_rk^T hi] B-frags, 1024
     static constexpr int OFF_MRKL = 6656;             // M_rk^T lo B-frag, 512
     static constexpr int OFF_ATK = 7168;              // [A~^T | K~^T hi] A-frags, NRT x 1024
@@ -464,7 +478,7 @@ struct WS64 {
     static constexpr int OFF_EGL = 15360;             // e^{G_L}, 64 floats
     static constexpr int OFF_FLAG = 15616;
     static constexpr int SLOT = 15632;
-    static constexpr int RAW = 6 * NCB * 1024;        // raw tile of one chunk
+    static constexpr int RAW = 5 * NCB * 1024;        // raw r, w, k, a, b tiles of one chunk
     static constexpr int OFF_SLOTS = 0;
     static constexpr int OFF_RAW = NSLOT * SLOT;
     static constexpr int OFF_SYNC = OFF_RAW + NPROD * RAW;
@@ -492,10 +506,25 @@ __device__ __forceinline__ void spin_ge(int *p, int target)
     asm volatile("" ::: "memory");
 }
 
-typedef __attribute__((address_space(3))) void *lds_ptr_t;
+typedef __attribute__((address_space(3))) char *lds_ptr_t;
 
-// Producer: stream the raw tile of `chunk` into `raw` (6 arrays x NCB blocks,
-// 1 KB each).  Lane l of each load fetches the 16 bytes of token l%16,
+// Asynchronous 16-byte-per-lane global -> LDS copy: lane l's 16 bytes land at
+// LDS byte address lds_base + 16 l.  Written out so that the compiler does not
+// treat every later LDS access as dependent on it (it would insert a wait for
+// all outstanding loads before each one); the copy has no register result, and
+// every reader of the destination waits with an explicit s_waitcnt vmcnt(0).
+__device__ __forceinline__ void copy16_to_lds(const void *gptr, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(gptr), "s"(lds_base) : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const char *p)
+{
+    return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_ptr_t)p);
+}
+
+// Producer: stream the raw r, w, k, a, b tiles of `chunk` into `raw`
+// (5 arrays x NCB blocks, 1 KB each).  Lane l of each load fetches the 16 bytes of token l%16,
 // channels 32s + 8(l/16) .. +7; tokens past T read token T-1 (discarded).
 __device__ __forceinline__ void ws_issue_raw(char *raw, const uint16_t *const *src, int T, int H,
                                              int bb, int h, int chunk, int lane)
@@ -505,11 +534,10 @@ __device__ __forceinline__ void ws_issue_raw(char *raw, const uint16_t *const *s
     const int tok = min(chunk * 16 + t, T - 1);
     const size_t base = (((size_t)bb * T + tok) * H + h) * D + 8 * v;
 #pragma unroll
-    for (int arr = 0; arr < 6; ++arr)
+    for (int arr = 0; arr < 5; ++arr)
 #pragma unroll
         for (int s = 0; s < WS64::NCB; ++s)
-            __builtin_amdgcn_global_load_lds(src[arr] + base + 32 * s,
-                                             (lds_ptr_t)(raw + (arr * WS64::NCB + s) * 1024), 16, 0, 0);
+            copy16_to_lds(src[arr] + base + 32 * s, lds_addr(raw + (arr * WS64::NCB + s) * 1024));
 }
 
 // Producer: read the staged raw tile into the register layout used by the
@@ -518,7 +546,7 @@ __device__ __forceinline__ void ws_read_raw(RawTile<64> &rt, const char *raw, in
 {
     const int t = lane & 15, g = lane >> 4;
 #pragma unroll
-    for (int arr = 0; arr < 6; ++arr)
+    for (int arr = 0; arr < 5; ++arr)
 #pragma unroll
         for (int s = 0; s < WS64::NCB; ++s)
 #pragma unroll
@@ -527,7 +555,42 @@ __device__ __forceinline__ void ws_read_raw(RawTile<64> &rt, const char *raw, in
                                                     16 * (t + 16 * (2 * hh + (g >> 1))) + 8 * (g & 1));
 }
 
+// Producer: request the chunk's value tile in MFMA B-fragment order: lane
+// (g, j) gets V[4g + i][16q + j], i = 0..3, for column tile q, as 16 zero-
+// extended halves (packed by ws_pack_v once they have arrived).  Tokens past
+// T read token T-1: a token that does not update has k = 0, so its value row
+// is multiplied by zero everywhere.  Loads are unconditional and their
+// results are consumed only after the explicit wait at the top of the next
+// iteration, so that issuing them never forces a wait on the prefetch.
+__device__ __forceinline__ void ws_load_v(uint32_t (*x)[4], const uint16_t *v, int T, int H,
+                                          int bb, int h, int chunk, int lane)
+{
+    const int g = lane >> 4, j = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int tok = min(chunk * 16 + 4 * g + i, T - 1);
+        const uint16_t *p = v + (((size_t)bb * T + tok) * H + h) * 64 + j;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) x[q][i] = p[16 * q];
+    }
+}
+
+__device__ __forceinline__ void ws_pack_v(uint32_t (*vq)[2], const uint32_t (*x)[4])
+{
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        vq[q][0] = x[q][0] | (x[q][1] << 16);
+        vq[q][1] = x[q][2] | (x[q][3] << 16);
+    }
+}
+
 // Producer: prepare one chunk's operands into `slot` (layout WS64).
+//
+// Precision: the r.k matrix M_rk (whose entries multiply the value tile
+// directly in the output) is formed from hi/lo bf16 splits of both factors
+// (three products); the other chunk matrices are single bf16 products with
+// fp32 accumulation.  Products with the value tile keep a hi/lo split of their
+// left operand (M_rk and K~).
 __device__ void ws_precompute(const RawTile<64> &rt, char *slot, int lane, const bf16x8 *psel)
 {
     using C = WS64;
@@ -566,25 +629,19 @@ __device__ void ws_precompute(const RawTile<64> &rt, char *slot, int lane, const
             }
         }
         extreme |= wmax > 0;
-        bf16x8 Rh, Rl, Bh, Bl, Khh, Khl, Kth, Ktl;
+        bf16x8 Rh, Rl, Khh, Khl, Kth, Ktl;
         split8(Rt, Rh, Rl);
-        split8(Bt, Bh, Bl);
         split8(Kh, Khh, Khl);
         split8(Kt, Kth, Ktl);
-        const bf16x8 Ahh = pack8(Ah);
-        const bf16x8 Ath = pack8(At);
-        const u32x4 vbits = {rt.x[s][5][0][0], rt.x[s][5][0][1], rt.x[s][5][1][0], rt.x[s][5][1][1]};
-        const bf16x8 Vb = __builtin_bit_cast(bf16x8, vbits);
+        const bf16x8 Bh = pack8(Bt), Ahh = pack8(Ah), Ath = pack8(At);
 
-        mraT = mfma32(Ahh, Rh, mraT);
-        mrkT = mfma32(Khh, Rh, mrkT);
+        mraT = mfma32(Ahh, Rh, mraT);   // (R~ A^^T)^T
+        mrkT = mfma32(Khh, Rh, mrkT);   // (R~ K^^T)^T, hi/lo split
         mrkT = mfma32(Khl, Rh, mrkT);
         mrkT = mfma32(Khh, Rl, mrkT);
-        mba = mfma32(Bh, Ahh, mba);
-        mbaT = mfma32(Ahh, Bh, mbaT);
-        mbk = mfma32(Bh, Khh, mbk);
-        mbk = mfma32(Bh, Khl, mbk);
-        mbk = mfma32(Bl, Khh, mbk);
+        mba = mfma32(Bh, Ahh, mba);     // B~ A^^T
+        mbaT = mfma32(Ahh, Bh, mbaT);   // (B~ A^^T)^T
+        mbk = mfma32(Bh, Khh, mbk);     // B~ K^^T
 
         st16(slot + C::OFF_B + s * 1024 + lane * 16, Bh);
         st16(slot + C::OFF_R + s * 1024 + lane * 16, Rh);
@@ -594,7 +651,6 @@ __device__ void ws_precompute(const RawTile<64> &rt, char *slot, int lane, const
             st8(slot + C::OFF_ATK + q * 1024 + lane * 16, cvt4(mfma32(Ath, psel[hh], zero4())));
             st8(slot + C::OFF_ATK + q * 1024 + lane * 16 + 8, cvt4(mfma32(Kth, psel[hh], zero4())));
             st8(slot + C::OFF_KTL + q * 512 + lane * 8, cvt4(mfma32(Ktl, psel[hh], zero4())));
-            st8(slot + C::OFF_V + q * 512 + lane * 8, cvt4(mfma32(Vb, psel[hh], zero4())));
         }
     }
 
@@ -622,12 +678,10 @@ __device__ void ws_precompute(const RawTile<64> &rt, char *slot, int lane, const
     const bf16x4 t2b = cvt4(t2);
     const f32x4 t4 = mfma16(n4t, t2b, t2), t4t = mfma16(t2b, n4t, t2t);
     const bf16x4 tinv = cvt4(mfma16(cvt4(t4), n8t, t4t));
-    bf16x4 hi, lo;
-    split4(mfma16(cvt4(mbk), tinv, zero4()), hi, lo);
     st8(slot + C::OFF_TN + lane * 16, tinv);
-    st8(slot + C::OFF_TN + lane * 16 + 8, hi);
-    st8(slot + C::OFF_NBKL + lane * 8, lo);
+    st8(slot + C::OFF_TN + lane * 16 + 8, cvt4(mfma16(cvt4(mbk), tinv, zero4())));
     st8(slot + C::OFF_MM + lane * 16, cvt4(mraT));
+    bf16x4 hi, lo;
     split4(mrkT, hi, lo);
     st8(slot + C::OFF_MM + lane * 16 + 8, hi);
     st8(slot + C::OFF_MRKL + lane * 8, lo);
@@ -705,60 +759,70 @@ __device__ void ws_chunk_exact(f32x4 (*S)[4], const uint16_t *r, const uint16_t 
     }
 }
 
-// Consumer: the S-dependent part of one chunk for all 64 columns.
-__device__ __forceinline__ void ws_chunk_serial(f32x4 (*S)[4], const char *slot, int *done, int chunk_done,
-                                                uint16_t *o, int T, int H, int bb, int h, int chunk, int lane)
+// Consumer: the S-dependent part of one chunk for all 64 columns.  Work is
+// issued in dependency order across the four independent column tiles, and
+// the S-independent products are placed where they fill the latency of the
+// S -> X -> U -> S' chain.
+__device__ __forceinline__ void ws_chunk_serial(f32x4 (*S)[4], const char *slot, uint16_t *o, int T,
+                                                int H, int bb, int h, int chunk, int lane)
 {
     using C = WS64;
     const int g = lane >> 4, t = lane & 15;
-    bf16x8 bt[2], rt[2], atk[4];
-    bf16x4 ktl[4], vf[4];
-    f32x4 egl[4];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        bt[s] = ld16(slot + C::OFF_B + s * 1024 + lane * 16);
-        rt[s] = ld16(slot + C::OFF_R + s * 1024 + lane * 16);
-    }
-    const bf16x8 tn = ld16(slot + C::OFF_TN + lane * 16);
-    const bf16x4 nbkl = ld8(slot + C::OFF_NBKL + lane * 8);
-    const bf16x8 mm = ld16(slot + C::OFF_MM + lane * 16);
-    const bf16x4 mrkl = ld8(slot + C::OFF_MRKL + lane * 8);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        atk[q] = ld16(slot + C::OFF_ATK + q * 1024 + lane * 16);
-        ktl[q] = ld8(slot + C::OFF_KTL + q * 512 + lane * 8);
-        vf[q] = ld8(slot + C::OFF_V + q * 512 + lane * 8);
-        egl[q] = *(const f32x4 *)(slot + C::OFF_EGL + (16 * q + 4 * g) * 4);
-    }
-    // Everything is in registers: release the slot to the producers.
-    lds_wait();
-    lds_store_relaxed(done, chunk_done);
-
-    const int tok = chunk * 16 + t;
+    bf16x8 sb0[4], sb1[4];
+    bf16x4 vf[4];
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
-        const bf16x8 sb0 = cat8(cvt4(S[0][n]), cvt4(S[1][n]));
-        const bf16x8 sb1 = cat8(cvt4(S[2][n]), cvt4(S[3][n]));
-        f32x4 X = mfma32(bt[0], sb0, zero4());
-        X = mfma32(bt[1], sb1, X);
-        f32x4 U = mfma16(nbkl, vf[n], zero4());
-        U = mfma32(tn, cat8(cvt4(X), vf[n]), U);
-        const bf16x4 ub = cvt4(U);
-        const bf16x8 uv = cat8(ub, vf[n]);
-        f32x4 Ot = mfma16(vf[n], mrkl, zero4());
-        Ot = mfma32(sb0, rt[0], Ot);
-        Ot = mfma32(sb1, rt[1], Ot);
-        Ot = mfma32(uv, mm, Ot);
+        sb0[n] = cat8(cvt4(S[0][n]), cvt4(S[1][n]));
+        sb1[n] = cat8(cvt4(S[2][n]), cvt4(S[3][n]));
+        vf[n] = ld8(slot + C::OFF_V + n * 512 + lane * 8);
+    }
+    const bf16x8 bt0 = ld16(slot + C::OFF_B + lane * 16), bt1 = ld16(slot + C::OFF_B + 1024 + lane * 16);
+    // X = B~ S
+    f32x4 X[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            f32x4 acc = S[q][n] * egl[q];
-            acc = mfma16(ktl[q], vf[n], acc);
-            S[q][n] = mfma32(atk[q], uv, acc);
-        }
-        if (tok < T) {
-            const uint32_t lo = cvt2_bits(Ot[0], Ot[1]), hi = cvt2_bits(Ot[2], Ot[3]);
-            *(u32x2 *)(o + (((size_t)bb * T + tok) * H + h) * 64 + 16 * n + 4 * g) = u32x2{lo, hi};
-        }
+    for (int n = 0; n < 4; ++n) X[n] = mfma32(bt0, sb0[n], zero4());
+    // S <- diag(e^{G_L}) S + K~lo^T V  (independent of X)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const f32x4 eg = *(const f32x4 *)(slot + C::OFF_EGL + (16 * q + 4 * g) * 4);
+        const bf16x4 ktl = ld8(slot + C::OFF_KTL + q * 512 + lane * 8);
+#pragma unroll
+        for (int n = 0; n < 4; ++n) S[q][n] = mfma16(ktl, vf[n], S[q][n] * eg);
+    }
+#pragma unroll
+    for (int n = 0; n < 4; ++n) X[n] = mfma32(bt1, sb1[n], X[n]);
+    // O^T, S-part (old S)
+    const bf16x8 rt0 = ld16(slot + C::OFF_R + lane * 16), rt1 = ld16(slot + C::OFF_R + 1024 + lane * 16);
+    const bf16x4 mrkl = ld8(slot + C::OFF_MRKL + lane * 8);
+    f32x4 Ot[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) Ot[n] = mfma32(sb0[n], rt0, zero4());
+    // U = T X + N_bk V
+    const bf16x8 tn = ld16(slot + C::OFF_TN + lane * 16);
+    bf16x8 uv[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) uv[n] = cat8(cvt4(mfma32(tn, cat8(cvt4(X[n]), vf[n]), zero4())), vf[n]);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) Ot[n] = mfma32(sb1[n], rt1, Ot[n]);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) Ot[n] = mfma16(vf[n], mrkl, Ot[n]);
+    // S += [A~^T | K~^T] [U; V]
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const bf16x8 atk = ld16(slot + C::OFF_ATK + q * 1024 + lane * 16);
+#pragma unroll
+        for (int n = 0; n < 4; ++n) S[q][n] = mfma32(atk, uv[n], S[q][n]);
+    }
+    // O^T += [U; V]^T [M_ra | M_rk]^T
+    const bf16x8 mm = ld16(slot + C::OFF_MM + lane * 16);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) Ot[n] = mfma32(uv[n], mm, Ot[n]);
+    const int tok = chunk * 16 + t;
+    if (tok < T) {
+        uint16_t *op = o + (((size_t)bb * T + tok) * H + h) * 64 + 4 * g;
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+            *(u32x2 *)(op + 16 * n) = u32x2{cvt2_bits(Ot[n][0], Ot[n][1]), cvt2_bits(Ot[n][2], Ot[n][3])};
     }
 }
 
@@ -769,12 +833,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     uint16_t *__restrict__ o, float *__restrict__ sf)
 {
     using C = WS64;
-    extern __shared__ __attribute__((aligned(16))) char lds[];
+    // Three separate LDS objects: the compiler must wait for outstanding
+    // global->LDS loads before touching the object they write (the raw
+    // buffers), but not before the slot ring or the hand-off counters.
+    __shared__ __attribute__((aligned(16))) char lds_slots[C::NSLOT * C::SLOT];
+    __shared__ __attribute__((aligned(16))) char lds_raw[C::NPROD * C::RAW];
+    __shared__ int lds_sync[16];
+    char *const lds = lds_slots;
     const int bh = blockIdx.x;
     const int bb = bh / H, h = bh % H;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int g = lane >> 4, j = lane & 15;
-    int *ready = (int *)(lds + C::OFF_SYNC);     // ready[NSLOT]
+    int *ready = lds_sync;     // ready[NSLOT]
     int *done = ready + C::NSLOT;
     const int nchunks = (T + 15) / 16;
 
@@ -795,13 +865,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int c = 0; c < nchunks; ++c) {
             const char *slot = lds + C::OFF_SLOTS + (c % C::NSLOT) * C::SLOT;
             spin_ge(&ready[c % C::NSLOT], c + 1);
-            if (*(const int *)(slot + C::OFF_FLAG)) {
-                lds_wait();
-                lds_store_relaxed(done, c + 1);
+            if (*(const int *)(slot + C::OFF_FLAG))
                 ws_chunk_exact(S, r, w, k, v, a, b, mask, o, T, H, bb, h, c, lane);
-            } else {
-                ws_chunk_serial(S, slot, done, c + 1, o, T, H, bb, h, c, lane);
-            }
+            else
+                ws_chunk_serial(S, slot, o, T, H, bb, h, c, lane);
+            lds_wait();                          // all reads of the slot have returned
+            lds_store_relaxed(done, c + 1);
         }
         if (sf) {
 #pragma unroll
@@ -815,42 +884,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     } else {
         // ---------------- producers ----------------
         const int p = wave - 1;
-        char *raw = lds + C::OFF_RAW + p * C::RAW;
-        const uint16_t *src[6] = {r, w, k, a, b, v};
+        char *raw = lds_raw + p * C::RAW;
+        const uint16_t *src[5] = {r, w, k, a, b};
         bf16x8 psel[2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 psel[hh][e] = (__bf16)(((e >> 2) == hh && 4 * g + (e & 3) == j) ? 1.0f : 0.0f);
-        if (p < nchunks) ws_issue_raw(raw, src, T, H, bb, h, p, lane);
+        // Loop-carried requests for this producer's next chunk: value halves and
+        // the mask byte of token (next chunk, lane & 15).
+        uint32_t vn[4][4];
+        uint32_t mnext = 1;
+        const int t = lane & 15;
+        if (p < nchunks) {
+            ws_issue_raw(raw, src, T, H, bb, h, p, lane);
+            ws_load_v(vn, v, T, H, bb, h, p, lane);
+            if (mask) mnext = mask[(size_t)bb * T + min(p * 16 + t, T - 1)];
+        }
         for (int c = p; c < nchunks; c += C::NPROD) {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            uint32_t vq[4][2];
+            ws_pack_v(vq, vn);
+            const uint32_t mcur = mnext;
             RawTile<64> rt;
             ws_read_raw(rt, raw, lane);
             lds_wait();
-            if (c + C::NPROD < nchunks) ws_issue_raw(raw, src, T, H, bb, h, c + C::NPROD, lane);
-            // Tokens that do not update (mask 0, or past T) are identity steps:
-            // zero their w, k, a; tokens past T also get r = b = v = 0.
-            const int tok = c * 16 + (lane & 15);
-            const bool valid = tok < T;
-            const bool upd = valid && (mask == nullptr || mask[(size_t)bb * T + tok] != 0);
-            if (!__all((int)upd)) {
-#pragma unroll
-                for (int s = 0; s < C::NCB; ++s)
-#pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-                        for (int arr = 1; arr <= 3; ++arr)
-                            rt.x[s][arr][hh] = upd ? rt.x[s][arr][hh] : u32x2{0u, 0u};
-                        rt.x[s][0][hh] = valid ? rt.x[s][0][hh] : u32x2{0u, 0u};
-                        rt.x[s][4][hh] = valid ? rt.x[s][4][hh] : u32x2{0u, 0u};
-                        rt.x[s][5][hh] = valid ? rt.x[s][5][hh] : u32x2{0u, 0u};
-                    }
+            if (c + C::NPROD < nchunks) {
+                const int cn = c + C::NPROD;
+                ws_issue_raw(raw, src, T, H, bb, h, cn, lane);
+                ws_load_v(vn, v, T, H, bb, h, cn, lane);
+                if (mask) mnext = mask[(size_t)bb * T + min(cn * 16 + t, T - 1)];
             }
+            const int tok = c * 16 + t;
+            rt.valid = tok < T;
+            rt.upd = rt.valid && mcur != 0;
+            zero_inactive<64>(rt, 5);
             char *slot = lds + C::OFF_SLOTS + (c % C::NSLOT) * C::SLOT;
-            spin_ge(done, c - C::NSLOT + 1);   // the slot's previous chunk is copied out
+            spin_ge(done, c - C::NSLOT + 1);   // the slot's previous chunk is consumed
             ws_precompute(rt, slot, lane, psel);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) *(u32x2 *)(slot + C::OFF_V + q * 512 + lane * 8) = u32x2{vq[q][0], vq[q][1]};
             lds_wait();
             lds_store_relaxed(&ready[c % C::NSLOT], c + 1);
         }
@@ -870,12 +944,8 @@ static hipError_t launch_ck(const FwdArgs &p, hipStream_t stream)
 
 static hipError_t launch_ws64(const FwdArgs &p, hipStream_t stream)
 {
-    // More than 64 KB of dynamic LDS needs an explicit opt-in (idempotent).
-    hipError_t e = hipFuncSetAttribute((const void *)chunked64_ws_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, WS64::LDS);
-    if (e != hipSuccess) return e;
     const dim3 grid((unsigned)(p.B * p.H)), block(256);
-    hipLaunchKernelGGL(chunked64_ws_kernel, grid, block, WS64::LDS, stream, p.T, p.H,
+    hipLaunchKernelGGL(chunked64_ws_kernel, grid, block, 0, stream, p.T, p.H,
                        (const uint16_t *)p.r, (const uint16_t *)p.w, (const uint16_t *)p.k,
                        (const uint16_t *)p.v, (const uint16_t *)p.a, (const uint16_t *)p.b, p.s0,
                        p.mask, (uint16_t *)p.o, p.sf);

@@ -8,6 +8,9 @@ Tolerances (from the operator's accuracy target):
             an exact output to bf16 alone already costs up to 2^-9 |o|), and
             max |S - S_ref| <= 0.02 * RMS(S_ref) for the fp32 final state.
 """
+import json
+import os
+
 import numpy as np
 
 import oracle
@@ -53,6 +56,14 @@ def oracle_fwd(inp, bh=None):
     return outs
 
 
+def _log(what, ratio):
+    """Record the worst error / tolerance ratio when WKV7_PARITY_LOG names a file."""
+    path = os.environ.get("WKV7_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps({"case": what, "ratio": round(float(ratio), 4)}) + "\n")
+
+
 def check(dtype, o, o_ref, s=None, s_ref=None, what="", scale=1.0):
     """scale=2 compares two GPU results, each within the bound of the exact
     value (triangle inequality)."""
@@ -70,6 +81,7 @@ def check(dtype, o, o_ref, s=None, s_ref=None, what="", scale=1.0):
     rms = float(np.sqrt(np.mean(o_ref ** 2))) if o_ref.size else 0.0
     allow = scale * (0.02 * rms + 2.0 ** -8 * np.abs(o_ref))
     ratio = float(np.max(err / np.maximum(allow, 1e-30))) if o.size else 0.0
+    _log(what, ratio)
     assert ratio <= 1.0, f"{what}: worst error {ratio:.3f} x tolerance (RMS {rms:.4g})"
     if s is not None:
         s = np.asarray(s, np.float64)
