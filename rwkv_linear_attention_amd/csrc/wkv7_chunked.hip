@@ -476,8 +476,7 @@ struct WS64 {
     static constexpr int OFF_KTL = 11264;             // K~^T lo A-frags, NRT x 512
     static constexpr int OFF_V = 13312;               // V frags per column tile, NCT x 512
     static constexpr int OFF_EGL = 15360;             // e^{G_L}, 64 floats
-    static constexpr int OFF_FLAG = 15616;
-    static constexpr int SLOT = 15632;
+    static constexpr int SLOT = 15616;
     static constexpr int RAW = 5 * NCB * 1024;        // raw r, w, k, a, b tiles of one chunk
     static constexpr int OFF_SLOTS = 0;
     static constexpr int OFF_RAW = NSLOT * SLOT;
@@ -497,13 +496,16 @@ __device__ __forceinline__ void lds_store_relaxed(int *p, int v)
 }
 // Wait until *p >= target; gives up after kSpinLimit polls so that a broken
 // hand-off ends the kernel (with wrong results) instead of hanging it.
-__device__ __forceinline__ void spin_ge(int *p, int target)
+__device__ __forceinline__ int spin_ge(int *p, int target)
 {
+    int v = 0;
     for (int it = 0; it < kSpinLimit; ++it) {
-        if (lds_load_relaxed(p) >= target) break;
+        v = lds_load_relaxed(p);
+        if (v >= target) break;
         __builtin_amdgcn_s_sleep(1);
     }
     asm volatile("" ::: "memory");
+    return v;
 }
 
 typedef __attribute__((address_space(3))) char *lds_ptr_t;
@@ -584,39 +586,69 @@ __device__ __forceinline__ void ws_pack_v(uint32_t (*vq)[2], const uint32_t (*x)
     }
 }
 
+__device__ __forceinline__ f32x4 mfma_f32_4(float a, float b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 // Producer: prepare one chunk's operands into `slot` (layout WS64).
 //
+// The per-channel decay prefix G_t = sum_{m<=t} w_m is formed on the matrix
+// cores: w is first transposed to a token-contiguous fragment (selection
+// MFMA, exact), then multiplied by the 16x16 upper-triangular ones matrix
+// (`ltri`), which yields G in the same register layout as r, k, a, b.
 // Precision: the r.k matrix M_rk (whose entries multiply the value tile
-// directly in the output) is formed from hi/lo bf16 splits of both factors
-// (three products); the other chunk matrices are single bf16 products with
-// fp32 accumulation.  Products with the value tile keep a hi/lo split of their
-// left operand (M_rk and K~).
-__device__ void ws_precompute(const RawTile<64> &rt, char *slot, int lane, const bf16x8 *psel)
+// directly in the output) is accumulated with fp32 MFMAs from fp32 operands;
+// the other chunk matrices are single bf16 products with fp32 accumulation.
+// Products with the value tile split their left operand into hi/lo bf16
+// (M_rk and K~).
+// Returns the wave-uniform extreme-decay flag of the chunk.
+__device__ int ws_precompute(const RawTile<64> &rt, char *slot, int lane, const bf16x8 *psel,
+                             bf16x4 ltri)
 {
     using C = WS64;
     const int t = lane & 15, g = lane >> 4;
-    f32x4 mraT = zero4(), mrkT = zero4(), mba = zero4(), mbaT = zero4(), mbk = zero4();
-    bool extreme = false;
+    f32x4 mraT = zero4(), mrkT0 = zero4(), mrkT1 = zero4(), mba = zero4(), mbaT = zero4(), mbk = zero4();
+    float emin = 1.0f;
+    // Positive w (signed 16-bit view of the bf16 bits > 0) leaves the fast path.
+    typedef short s16x2 __attribute__((ext_vector_type(2)));
+    s16x2 wmax = {(short)0x8000, (short)0x8000};
+#pragma unroll
+    for (int s = 0; s < C::NCB; ++s)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            wmax = __builtin_elementwise_max(wmax, __builtin_bit_cast(s16x2, rt.x[s][1][hh][0]));
+            wmax = __builtin_elementwise_max(wmax, __builtin_bit_cast(s16x2, rt.x[s][1][hh][1]));
+        }
+
+    // Decay prefixes for all four 16-channel tiles (element e = 4hh + i of
+    // block s holds channel 32s + 16hh + 4g + i of token t).
+    f32x4 Gq[C::NCB][2];
+#pragma unroll
+    for (int s = 0; s < C::NCB; ++s) {
+        const u32x4 wbits = {rt.x[s][1][0][0], rt.x[s][1][0][1], rt.x[s][1][1][0], rt.x[s][1][1][1]};
+        const bf16x8 wb = __builtin_bit_cast(bf16x8, wbits);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+            Gq[s][hh] = mfma16(cvt4(mfma32(wb, psel[hh], zero4())), ltri, zero4());
+    }
 
 #pragma unroll
     for (int s = 0; s < C::NCB; ++s) {
-        float rv[8], wv[8], kv[8], av[8], bv[8];
+        float rv[8], kv[8], av[8], bv[8];
         unpack8(rt.x[s][0], rv);
-        unpack8(rt.x[s][1], wv);
         unpack8(rt.x[s][2], kv);
         unpack8(rt.x[s][3], av);
         unpack8(rt.x[s][4], bv);
         float Rt[8], Bt[8], Ah[8], Kh[8], At[8], Kt[8];
-        int wmax = (int)0x80000000;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            wmax = max(wmax, __float_as_int(wv[e]));
-            const float G2 = row_scan16(wv[e] * 1.4426950408889634f);
+            const float G2 = Gq[s][e >> 2][e & 3] * 1.4426950408889634f;
             const float eG = __builtin_amdgcn_exp2f(G2);
             const float enG = __builtin_amdgcn_exp2f(-G2);
             const float eGp = row_shr<1>(eG, 1.0f);
             const float eGL = row_bcast15(eG);
-            extreme |= eGL < kMinChunkFactor;
+            emin = fminf(emin, eGL);
             Rt[e] = rv[e] * eG;
             Bt[e] = bv[e] * eGp;
             Ah[e] = av[e] * enG;
@@ -627,18 +659,16 @@ __device__ void ws_precompute(const RawTile<64> &rt, char *slot, int lane, const
                 const int ch = 32 * s + 4 * g + (e & 3) + 16 * (e >> 2);
                 *(float *)(slot + C::OFF_EGL + ch * 4) = eGL;
             }
+            // (R~ K^^T)^T in fp32: k-slot g of this MFMA is channel (s, g, e).
+            if (e & 1) mrkT1 = mfma_f32_4(Kh[e], Rt[e], mrkT1);
+            else mrkT0 = mfma_f32_4(Kh[e], Rt[e], mrkT0);
         }
-        extreme |= wmax > 0;
-        bf16x8 Rh, Rl, Khh, Khl, Kth, Ktl;
-        split8(Rt, Rh, Rl);
-        split8(Kh, Khh, Khl);
+        bf16x8 Kth, Ktl;
         split8(Kt, Kth, Ktl);
-        const bf16x8 Bh = pack8(Bt), Ahh = pack8(Ah), Ath = pack8(At);
+        const bf16x8 Rh = pack8(Rt), Bh = pack8(Bt), Khh = pack8(Kh);
+        const bf16x8 Ahh = pack8(Ah), Ath = pack8(At);
 
         mraT = mfma32(Ahh, Rh, mraT);   // (R~ A^^T)^T
-        mrkT = mfma32(Khh, Rh, mrkT);   // (R~ K^^T)^T, hi/lo split
-        mrkT = mfma32(Khl, Rh, mrkT);
-        mrkT = mfma32(Khh, Rl, mrkT);
         mba = mfma32(Bh, Ahh, mba);     // B~ A^^T
         mbaT = mfma32(Ahh, Bh, mbaT);   // (B~ A^^T)^T
         mbk = mfma32(Bh, Khh, mbk);     // B~ K^^T
@@ -653,6 +683,7 @@ __device__ void ws_precompute(const RawTile<64> &rt, char *slot, int lane, const
             st8(slot + C::OFF_KTL + q * 512 + lane * 8, cvt4(mfma32(Ktl, psel[hh], zero4())));
         }
     }
+    f32x4 mrkT = mrkT0 + mrkT1;
 
     const int j = lane & 15;
     f32x4 eye;
@@ -685,8 +716,7 @@ __device__ void ws_precompute(const RawTile<64> &rt, char *slot, int lane, const
     split4(mrkT, hi, lo);
     st8(slot + C::OFF_MM + lane * 16 + 8, hi);
     st8(slot + C::OFF_MRKL + lane * 8, lo);
-    const int any_extreme = __any((int)extreme);
-    if (lane == 0) *(int *)(slot + C::OFF_FLAG) = any_extreme;
+    return __any((int)(emin < kMinChunkFactor || wmax[0] > 0 || wmax[1] > 0)) ? 1 : 0;
 }
 
 __device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b)
@@ -763,11 +793,26 @@ __device__ void ws_chunk_exact(f32x4 (*S)[4], const uint16_t *r, const uint16_t 
 // issued in dependency order across the four independent column tiles, and
 // the S-independent products are placed where they fill the latency of the
 // S -> X -> U -> S' chain.
+// Store one chunk's output tile held as O^T fragments (lane (g, t): token t,
+// columns 16n + 4g .. +3).
+__device__ __forceinline__ void ws_store_out(const f32x4 *Ot, uint16_t *o, int T, int H, int bb, int h,
+                                             int chunk, int lane)
+{
+    const int g = lane >> 4, t = lane & 15;
+    const int tok = chunk * 16 + t;
+    if (chunk >= 0 && tok < T) {
+        uint16_t *op = o + (((size_t)bb * T + tok) * H + h) * 64 + 4 * g;
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+            *(u32x2 *)(op + 16 * n) = u32x2{cvt2_bits(Ot[n][0], Ot[n][1]), cvt2_bits(Ot[n][2], Ot[n][3])};
+    }
+}
+
 __device__ __forceinline__ void ws_chunk_serial(f32x4 (*S)[4], const char *slot, uint16_t *o, int T,
                                                 int H, int bb, int h, int chunk, int lane)
 {
     using C = WS64;
-    const int g = lane >> 4, t = lane & 15;
+    const int g = lane >> 4;
     bf16x8 sb0[4], sb1[4];
     bf16x4 vf[4];
 #pragma unroll
@@ -817,13 +862,7 @@ __device__ __forceinline__ void ws_chunk_serial(f32x4 (*S)[4], const char *slot,
     const bf16x8 mm = ld16(slot + C::OFF_MM + lane * 16);
 #pragma unroll
     for (int n = 0; n < 4; ++n) Ot[n] = mfma32(uv[n], mm, Ot[n]);
-    const int tok = chunk * 16 + t;
-    if (tok < T) {
-        uint16_t *op = o + (((size_t)bb * T + tok) * H + h) * 64 + 4 * g;
-#pragma unroll
-        for (int n = 0; n < 4; ++n)
-            *(u32x2 *)(op + 16 * n) = u32x2{cvt2_bits(Ot[n][0], Ot[n][1]), cvt2_bits(Ot[n][2], Ot[n][3])};
-    }
+    ws_store_out(Ot, o, T, H, bb, h, chunk, lane);
 }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void chunked64_ws_kernel(
@@ -848,10 +887,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     int *done = ready + C::NSLOT;
     const int nchunks = (T + 15) / 16;
 
+    // Role assignment by SIMD: the wave that runs on the lowest-numbered SIMD
+    // becomes the consumer.  With two resident workgroups per CU both
+    // consumers then share one SIMD (their work is mostly MFMA) and the
+    // VALU-heavy producers pair up on the other three.  Correctness does not
+    // depend on the placement; it only picks which wave does what.
+    int *simd_of = lds_sync + 8;   // 4 entries
     if (threadIdx.x < C::NSLOT + 1) ready[threadIdx.x] = 0;
+    if (lane == 0) {
+        unsigned hw;
+        asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+        simd_of[wave] = (int)((hw >> 4) & 3) * 4 + wave;   // unique key: (simd, wave)
+    }
     __syncthreads();
+    int cons = 0;
+#pragma unroll
+    for (int w2 = 1; w2 < 4; ++w2) cons = simd_of[w2] < simd_of[cons] ? w2 : cons;
+    const int role = (wave - cons + 4) & 3;   // 0 = consumer, 1..3 = producers
 
-    if (wave == 0) {
+    if (role == 0) {
         // ---------------- consumer ----------------
         f32x4 S[4][4];   // S[q][n]: rows 16q + 4g + i, column 16n + j
         const size_t st_base = (size_t)bh * 64 * 64;
@@ -864,8 +918,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     S[q][n][i] = s0 ? s0[st_base + (size_t)(16 * q + 4 * g + i) * 64 + 16 * n + j] : 0.0f;
         for (int c = 0; c < nchunks; ++c) {
             const char *slot = lds + C::OFF_SLOTS + (c % C::NSLOT) * C::SLOT;
-            spin_ge(&ready[c % C::NSLOT], c + 1);
-            if (*(const int *)(slot + C::OFF_FLAG))
+            // ready[slot] = 2 (c + 1) + extreme-decay flag once chunk c is in the slot
+            const int rv = spin_ge(&ready[c % C::NSLOT], 2 * (c + 1));
+            if (rv & 1)
                 ws_chunk_exact(S, r, w, k, v, a, b, mask, o, T, H, bb, h, c, lane);
             else
                 ws_chunk_serial(S, slot, o, T, H, bb, h, c, lane);
@@ -883,7 +938,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
     } else {
         // ---------------- producers ----------------
-        const int p = wave - 1;
+        const int p = role - 1;
         char *raw = lds_raw + p * C::RAW;
         const uint16_t *src[5] = {r, w, k, a, b};
         bf16x8 psel[2];
@@ -892,6 +947,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 psel[hh][e] = (__bf16)(((e >> 2) == hh && 4 * g + (e & 3) == j) ? 1.0f : 0.0f);
+        // B-fragment of the inclusive prefix-sum matrix: [token' <= token].
+        bf16x4 ltri;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ltri[i] = (__bf16)((4 * g + i <= j) ? 1.0f : 0.0f);
         // Loop-carried requests for this producer's next chunk: value halves and
         // the mask byte of token (next chunk, lane & 15).
         uint32_t vn[4][4];
@@ -922,11 +981,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             zero_inactive<64>(rt, 5);
             char *slot = lds + C::OFF_SLOTS + (c % C::NSLOT) * C::SLOT;
             spin_ge(done, c - C::NSLOT + 1);   // the slot's previous chunk is consumed
-            ws_precompute(rt, slot, lane, psel);
+            const int flag = ws_precompute(rt, slot, lane, psel, ltri);
 #pragma unroll
             for (int q = 0; q < 4; ++q) *(u32x2 *)(slot + C::OFF_V + q * 512 + lane * 8) = u32x2{vq[q][0], vq[q][1]};
             lds_wait();
-            lds_store_relaxed(&ready[c % C::NSLOT], c + 1);
+            lds_store_relaxed(&ready[c % C::NSLOT], 2 * (c + 1) + flag);
         }
     }
 }
