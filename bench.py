@@ -40,17 +40,20 @@ def algorithmic_bytes(B, T, H, D, dtype_bytes, has_s0, has_final, has_mask):
     return 6 * tok + tok + (st if has_s0 else 0) + (st if has_final else 0) + (B * T if has_mask else 0)
 
 
-def measured_traffic(sha, launches_per_step=1):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on this exact kernel source; otherwise None."""
+def measured_traffic(sha):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE in KiB per dispatch, each scaled by what the
+    counter reads for a plain copy of known size), if it was taken on this
+    exact kernel source; otherwise None."""
     if not os.path.exists(PROFILE_NOTE):
         return None
     txt = open(PROFILE_NOTE).read()
-    m = re.search(r"traffic: source_sha=(\w+) fetch_kib=([\d.]+) write_kib=([\d.]+) scale=([\d.]+)", txt)
+    m = re.search(r"traffic: source_sha=(\w+) fetch_kib=([\d.]+) fetch_scale=([\d.]+) "
+                  r"write_kib=([\d.]+) write_scale=([\d.]+)", txt)
     if not m or m.group(1) != sha:
         return None
-    fetch, write, scale = float(m.group(2)), float(m.group(3)), float(m.group(4))
-    return (fetch + write) * 1024.0 * scale / launches_per_step
+    fk, fs, wk, ws = (float(m.group(i)) for i in range(2, 6))
+    return round((fk * fs + wk * ws) * 1024.0)
 
 
 def cpu_baseline(inp, H, T, budget_s=12.0, max_threads=16):
@@ -88,6 +91,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--all", action="store_true",
+                    help="also time the head-size-128 workload and the 256-step decode")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -171,7 +176,85 @@ def main():
     if not args.no_cpu:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(inp, H, T)
+    if args.all:
+        del dev, o, sf, inp
+        result["others"] = other_workloads(args.steps, args.warmup)
     print(json.dumps(result), flush=True)
+
+
+def _time_launches(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn(0)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def other_workloads(steps, warmup):
+    """Head size 128 forward (B16 T4096 H32, trailing-padding mask, S0) and the
+    decode step (B512 H40 d64, 256 consecutive in-place steps)."""
+    import torch
+    from rwkv_linear_attention_amd import synth, wkv7
+    out = {}
+    wl = synth.WORKLOADS[3]
+    B, T, H, D = wl["B"], wl["T"], wl["H"], wl["K"]
+    print(f"[bench] generating workload {wl['name']}", file=sys.stderr, flush=True)
+    inp = synth.make(3)
+    dev = {n: synth.to_torch(inp[n], "bf16", "cuda") for n in ("r", "w", "k", "v", "a", "b")}
+    s0 = torch.from_numpy(inp["s0"]).cuda()
+    mask = torch.from_numpy(inp["mask"]).cuda()
+    o = torch.empty((B, T, H, D), dtype=torch.bfloat16, device="cuda")
+    sf = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
+    ms = _time_launches(lambda i: wkv7.fwd(*(dev[n] for n in ("r", "w", "k", "v", "a", "b")),
+                                           initial_state=s0, mask=mask, out=o, final_state=sf),
+                        max(3, steps // 2), warmup)
+    nbytes = algorithmic_bytes(B, T, H, D, 2, True, True, True)
+    out[wl["name"]] = {"ms": round(ms, 5), "Mtokens_per_s": round(B * T / ms / 1e3, 3),
+                       "GB_per_s": round(nbytes / ms / 1e6, 1), "frac_of_8TBps": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
+                       "algorithmic_bytes": nbytes, "kernel": "chunked d128"}
+    del dev, s0, mask, o, sf, inp
+    torch.cuda.empty_cache()
+
+    wl = synth.WORKLOADS[4]
+    B, NSTEP, H, D = wl["B"], wl["T"], wl["H"], wl["K"]
+    print(f"[bench] generating workload {wl['name']} (32 distinct steps, cycled)", file=sys.stderr, flush=True)
+    inp = synth.make(4, T=32)
+    dev = {n: synth.to_torch(inp[n], "bf16", "cuda") for n in ("r", "w", "k", "v", "a", "b")}
+    per_step = [{n: dev[n][:, t].contiguous() for n in dev} for t in range(32)]
+    state0 = torch.from_numpy(inp["s0"]).cuda()
+    state = state0.clone()
+    obuf = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
+
+    def run(i):
+        state.copy_(state0)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for t in range(NSTEP):
+            x = per_step[t % 32]
+            wkv7.step(x["r"], x["w"], x["k"], x["v"], x["a"], x["b"], state, out=obuf)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    run(0)
+    times = [run(i) for i in range(3)]
+    ms_total = min(times)
+    step_bytes = 2 * B * H * D * D * 4 + 6 * B * H * D * 2 + B * H * D * 2
+    out[wl["name"]] = {"ms_256_steps": round(ms_total, 4), "us_per_step": round(ms_total * 1e3 / NSTEP, 2),
+                       "GB_per_s": round(step_bytes * NSTEP / ms_total / 1e6, 1),
+                       "frac_of_8TBps": round(step_bytes * NSTEP / ms_total / 1e6 / HBM_PEAK_GBS, 4),
+                       "bytes_per_step": step_bytes, "kernel": "step d64",
+                       "note": "inputs of 32 distinct steps cycled; state reset outside the timed region"}
+    return out
 
 
 if __name__ == "__main__":
