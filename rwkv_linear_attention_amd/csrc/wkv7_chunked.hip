@@ -125,14 +125,9 @@ __device__ __forceinline__ void unpack8(const u32x2 *x, float *out)
 
 __device__ __forceinline__ bf16x8 pack8(const float *x)
 {
-    bf16x8 o;
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-        bf16x2 p = cvt2(x[e], x[e + 1]);
-        o[e] = p[0];
-        o[e + 1] = p[1];
-    }
-    return o;
+    const u32x4 p = {cvt2_bits(x[0], x[1]), cvt2_bits(x[2], x[3]), cvt2_bits(x[4], x[5]),
+                     cvt2_bits(x[6], x[7])};
+    return __builtin_bit_cast(bf16x8, p);
 }
 
 // hi/lo split: hi = bf16(x), lo = bf16(x - hi).
@@ -466,6 +461,7 @@ struct WS64 {
     static constexpr int NCB = 2, NRT = 4, NCT = 4;   // channel blocks, row / column tiles
     static constexpr int NPROD = 3;
     static constexpr int NSLOT = 3;
+    static constexpr int NSEQ = 2;                    // sequences per workgroup
     // slot layout (bytes)
     static constexpr int OFF_B = 0;                   // B~ frags, NCB x 1024
     static constexpr int OFF_R = 2048;                // R~ frags, NCB x 1024
@@ -479,9 +475,6 @@ struct WS64 {
     static constexpr int SLOT = 15616;
     static constexpr int RAW = 5 * NCB * 1024;        // raw r, w, k, a, b tiles of one chunk
     static constexpr int OFF_SLOTS = 0;
-    static constexpr int OFF_RAW = NSLOT * SLOT;
-    static constexpr int OFF_SYNC = OFF_RAW + NPROD * RAW;
-    static constexpr int LDS = OFF_SYNC + 64;
 };
 
 constexpr int kSpinLimit = 1 << 20;
@@ -528,18 +521,18 @@ __device__ __forceinline__ uint32_t lds_addr(const char *p)
 // Producer: stream the raw r, w, k, a, b tiles of `chunk` into `raw`
 // (5 arrays x NCB blocks, 1 KB each).  Lane l of each load fetches the 16 bytes of token l%16,
 // channels 32s + 8(l/16) .. +7; tokens past T read token T-1 (discarded).
-__device__ __forceinline__ void ws_issue_raw(char *raw, const uint16_t *const *src, int T, int H,
-                                             int bb, int h, int chunk, int lane)
+__device__ __forceinline__ void ws_issue_raw(uint32_t raw_lds, const uint16_t *const *src,
+                                             size_t seq_base, uint32_t tok_stride, int T, int chunk,
+                                             int lane)
 {
-    constexpr int D = WS64::D;
     const int t = lane & 15, v = lane >> 4;
-    const int tok = min(chunk * 16 + t, T - 1);
-    const size_t base = (((size_t)bb * T + tok) * H + h) * D + 8 * v;
+    const uint32_t tok = (uint32_t)min(chunk * 16 + t, T - 1);
+    const size_t base = seq_base + (size_t)tok * tok_stride + 8 * v;
 #pragma unroll
     for (int arr = 0; arr < 5; ++arr)
 #pragma unroll
         for (int s = 0; s < WS64::NCB; ++s)
-            copy16_to_lds(src[arr] + base + 32 * s, lds_addr(raw + (arr * WS64::NCB + s) * 1024));
+            copy16_to_lds(src[arr] + base + 32 * s, raw_lds + (arr * WS64::NCB + s) * 1024);
 }
 
 // Producer: read the staged raw tile into the register layout used by the
@@ -564,14 +557,14 @@ __device__ __forceinline__ void ws_read_raw(RawTile<64> &rt, const char *raw, in
 // is multiplied by zero everywhere.  Loads are unconditional and their
 // results are consumed only after the explicit wait at the top of the next
 // iteration, so that issuing them never forces a wait on the prefetch.
-__device__ __forceinline__ void ws_load_v(uint32_t (*x)[4], const uint16_t *v, int T, int H,
-                                          int bb, int h, int chunk, int lane)
+__device__ __forceinline__ void ws_load_v(uint32_t (*x)[4], const uint16_t *v, size_t seq_base,
+                                          uint32_t tok_stride, int T, int chunk, int lane)
 {
     const int g = lane >> 4, j = lane & 15;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int tok = min(chunk * 16 + 4 * g + i, T - 1);
-        const uint16_t *p = v + (((size_t)bb * T + tok) * H + h) * 64 + j;
+        const uint32_t tok = (uint32_t)min(chunk * 16 + 4 * g + i, T - 1);
+        const uint16_t *p = v + seq_base + (size_t)tok * tok_stride + j;
 #pragma unroll
         for (int q = 0; q < 4; ++q) x[q][i] = p[16 * q];
     }
@@ -586,11 +579,6 @@ __device__ __forceinline__ void ws_pack_v(uint32_t (*vq)[2], const uint32_t (*x)
     }
 }
 
-__device__ __forceinline__ f32x4 mfma_f32_4(float a, float b, f32x4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
 // Producer: prepare one chunk's operands into `slot` (layout WS64).
 //
 // The per-channel decay prefix G_t = sum_{m<=t} w_m is formed on the matrix
@@ -598,8 +586,9 @@ __device__ __forceinline__ f32x4 mfma_f32_4(float a, float b, f32x4 c)
 // MFMA, exact), then multiplied by the 16x16 upper-triangular ones matrix
 // (`ltri`), which yields G in the same register layout as r, k, a, b.
 // Precision: the r.k matrix M_rk (whose entries multiply the value tile
-// directly in the output) is accumulated with fp32 MFMAs from fp32 operands;
-// the other chunk matrices are single bf16 products with fp32 accumulation.
+// directly in the output) is formed from hi/lo bf16 splits of both operands
+// (three products, relative error about 2^-16); the other chunk matrices are
+// single bf16 products with fp32 accumulation.
 // Products with the value tile split their left operand into hi/lo bf16
 // (M_rk and K~).
 // Returns the wave-uniform extreme-decay flag of the chunk.
@@ -641,6 +630,7 @@ __device__ int ws_precompute(const RawTile<64> &rt, char *slot, int lane, const 
         unpack8(rt.x[s][3], av);
         unpack8(rt.x[s][4], bv);
         float Rt[8], Bt[8], Ah[8], Kh[8], At[8], Kt[8];
+        f32x4 eGL4[2];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float G2 = Gq[s][e >> 2][e & 3] * 1.4426950408889634f;
@@ -648,6 +638,7 @@ __device__ int ws_precompute(const RawTile<64> &rt, char *slot, int lane, const 
             const float enG = __builtin_amdgcn_exp2f(-G2);
             const float eGp = row_shr<1>(eG, 1.0f);
             const float eGL = row_bcast15(eG);
+            eGL4[e >> 2][e & 3] = eGL;
             emin = fminf(emin, eGL);
             Rt[e] = rv[e] * eG;
             Bt[e] = bv[e] * eGp;
@@ -655,18 +646,31 @@ __device__ int ws_precompute(const RawTile<64> &rt, char *slot, int lane, const 
             Kh[e] = kv[e] * enG;
             At[e] = Ah[e] * eGL;
             Kt[e] = Kh[e] * eGL;
-            if (t == 0) {
-                const int ch = 32 * s + 4 * g + (e & 3) + 16 * (e >> 2);
-                *(float *)(slot + C::OFF_EGL + ch * 4) = eGL;
-            }
-            // (R~ K^^T)^T in fp32: k-slot g of this MFMA is channel (s, g, e).
-            if (e & 1) mrkT1 = mfma_f32_4(Kh[e], Rt[e], mrkT1);
-            else mrkT0 = mfma_f32_4(Kh[e], Rt[e], mrkT0);
+        }
+        // e^{G_L} of channels 32s + 16hh + 4g .. +3 (one writer per row).
+        if (t == 0) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+                *(f32x4 *)(slot + C::OFF_EGL + (32 * s + 16 * hh + 4 * g) * 4) = eGL4[hh];
         }
         bf16x8 Kth, Ktl;
         split8(Kt, Kth, Ktl);
         const bf16x8 Rh = pack8(Rt), Bh = pack8(Bt), Khh = pack8(Kh);
         const bf16x8 Ahh = pack8(Ah), Ath = pack8(At);
+        // (R~ K^^T)^T to about 16 bits: hi.hi + hi.lo + lo.hi.
+        bf16x8 Rl, Khl;
+        {
+            float rem[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) rem[e] = Rt[e] - (float)Rh[e];
+            Rl = pack8(rem);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) rem[e] = Kh[e] - (float)Khh[e];
+            Khl = pack8(rem);
+        }
+        mrkT0 = mfma32(Khh, Rh, mrkT0);
+        mrkT1 = mfma32(Khh, Rl, mrkT1);
+        mrkT1 = mfma32(Khl, Rh, mrkT1);
 
         mraT = mfma32(Ahh, Rh, mraT);   // (R~ A^^T)^T
         mba = mfma32(Bh, Ahh, mba);     // B~ A^^T
@@ -865,45 +869,48 @@ __device__ __forceinline__ void ws_chunk_serial(f32x4 (*S)[4], const char *slot,
     ws_store_out(Ot, o, T, H, bb, h, chunk, lane);
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void chunked64_ws_kernel(
-    int T, int H, const uint16_t *__restrict__ r, const uint16_t *__restrict__ w,
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void chunked64_ws_kernel(
+    int T, int H, int nbh, const uint16_t *__restrict__ r, const uint16_t *__restrict__ w,
     const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, const uint16_t *__restrict__ a,
     const uint16_t *__restrict__ b, const float *__restrict__ s0, const uint8_t *__restrict__ mask,
     uint16_t *__restrict__ o, float *__restrict__ sf)
 {
     using C = WS64;
-    // Three separate LDS objects: the compiler must wait for outstanding
+    // Separate LDS objects: the compiler must wait for outstanding
     // global->LDS loads before touching the object they write (the raw
-    // buffers), but not before the slot ring or the hand-off counters.
-    __shared__ __attribute__((aligned(16))) char lds_slots[C::NSLOT * C::SLOT];
-    __shared__ __attribute__((aligned(16))) char lds_raw[C::NPROD * C::RAW];
-    __shared__ int lds_sync[16];
-    char *const lds = lds_slots;
-    const int bh = blockIdx.x;
-    const int bb = bh / H, h = bh % H;
+    // buffers), but not before the slot rings or the hand-off counters.
+    __shared__ __attribute__((aligned(16))) char lds_slots[C::NSEQ * C::NSLOT * C::SLOT];
+    __shared__ __attribute__((aligned(16))) char lds_raw[C::NSEQ * C::NPROD * C::RAW];
+    __shared__ int lds_sync[32];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int g = lane >> 4, j = lane & 15;
-    int *ready = lds_sync;     // ready[NSLOT]
-    int *done = ready + C::NSLOT;
     const int nchunks = (T + 15) / 16;
 
-    // Role assignment by SIMD: the wave that runs on the lowest-numbered SIMD
-    // becomes the consumer.  With two resident workgroups per CU both
-    // consumers then share one SIMD (their work is mostly MFMA) and the
-    // VALU-heavy producers pair up on the other three.  Correctness does not
-    // depend on the placement; it only picks which wave does what.
-    int *simd_of = lds_sync + 8;   // 4 entries
-    if (threadIdx.x < C::NSLOT + 1) ready[threadIdx.x] = 0;
+    // Role assignment by SIMD.  The eight waves are ranked by (SIMD, wave
+    // index); ranks 0-3 serve the workgroup's first sequence and 4-7 its
+    // second, rank 0 of each group being the consumer.  With the usual two
+    // waves per SIMD the two consumers (whose work is mostly MFMA) land on
+    // different SIMDs, each sharing it with one producer, and the remaining
+    // producers pair up on the other two.  Correctness does not depend on the
+    // placement; it only picks which wave does what.
+    int *key_of = lds_sync + 16;   // 8 entries
+    if (threadIdx.x < 16) lds_sync[threadIdx.x] = 0;
     if (lane == 0) {
         unsigned hw;
         asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
-        simd_of[wave] = (int)((hw >> 4) & 3) * 4 + wave;   // unique key: (simd, wave)
+        key_of[wave] = (int)((hw >> 4) & 3) * 8 + wave;   // unique key: (simd, wave)
     }
     __syncthreads();
-    int cons = 0;
+    int rank = 0;
 #pragma unroll
-    for (int w2 = 1; w2 < 4; ++w2) cons = simd_of[w2] < simd_of[cons] ? w2 : cons;
-    const int role = (wave - cons + 4) & 3;   // 0 = consumer, 1..3 = producers
+    for (int w2 = 0; w2 < 8; ++w2) rank += key_of[w2] < key_of[wave] ? 1 : 0;
+    const int seq = rank >> 2, role = rank & 3;   // role 0 = consumer, 1..3 = producers
+    const int bh = blockIdx.x * C::NSEQ + seq;
+    if (bh >= nbh) return;
+    const int bb = bh / H, h = bh % H;
+    char *const lds = lds_slots + seq * C::NSLOT * C::SLOT;
+    int *ready = lds_sync + 8 * seq;   // ready[NSLOT], then done
+    int *done = ready + C::NSLOT;
 
     if (role == 0) {
         // ---------------- consumer ----------------
@@ -939,7 +946,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     } else {
         // ---------------- producers ----------------
         const int p = role - 1;
-        char *raw = lds_raw + p * C::RAW;
+        char *raw = lds_raw + (seq * C::NPROD + p) * C::RAW;
+        const uint32_t raw_lds = lds_addr(raw);
+        // Element offset of (bb, token 0, h, channel 0) and between tokens.
+        const size_t seq_base = ((size_t)bb * T * H + h) * 64;
+        const uint32_t tok_stride = (uint32_t)H * 64;
         const uint16_t *src[5] = {r, w, k, a, b};
         bf16x8 psel[2];
 #pragma unroll
@@ -957,8 +968,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         uint32_t mnext = 1;
         const int t = lane & 15;
         if (p < nchunks) {
-            ws_issue_raw(raw, src, T, H, bb, h, p, lane);
-            ws_load_v(vn, v, T, H, bb, h, p, lane);
+            ws_issue_raw(raw_lds, src, seq_base, tok_stride, T, p, lane);
+            ws_load_v(vn, v, seq_base, tok_stride, T, p, lane);
             if (mask) mnext = mask[(size_t)bb * T + min(p * 16 + t, T - 1)];
         }
         for (int c = p; c < nchunks; c += C::NPROD) {
@@ -971,8 +982,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             lds_wait();
             if (c + C::NPROD < nchunks) {
                 const int cn = c + C::NPROD;
-                ws_issue_raw(raw, src, T, H, bb, h, cn, lane);
-                ws_load_v(vn, v, T, H, bb, h, cn, lane);
+                ws_issue_raw(raw_lds, src, seq_base, tok_stride, T, cn, lane);
+                ws_load_v(vn, v, seq_base, tok_stride, T, cn, lane);
                 if (mask) mnext = mask[(size_t)bb * T + min(cn * 16 + t, T - 1)];
             }
             const int tok = c * 16 + t;
@@ -1003,8 +1014,9 @@ static hipError_t launch_ck(const FwdArgs &p, hipStream_t stream)
 
 static hipError_t launch_ws64(const FwdArgs &p, hipStream_t stream)
 {
-    const dim3 grid((unsigned)(p.B * p.H)), block(256);
-    hipLaunchKernelGGL(chunked64_ws_kernel, grid, block, 0, stream, p.T, p.H,
+    const int nbh = p.B * p.H;
+    const dim3 grid((unsigned)((nbh + WS64::NSEQ - 1) / WS64::NSEQ)), block(64 * 4 * WS64::NSEQ);
+    hipLaunchKernelGGL(chunked64_ws_kernel, grid, block, 0, stream, p.T, p.H, nbh,
                        (const uint16_t *)p.r, (const uint16_t *)p.w, (const uint16_t *)p.k,
                        (const uint16_t *)p.v, (const uint16_t *)p.a, (const uint16_t *)p.b, p.s0,
                        p.mask, (uint16_t *)p.o, p.sf);

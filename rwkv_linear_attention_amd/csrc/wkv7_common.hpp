@@ -35,7 +35,12 @@ __device__ __forceinline__ uint32_t cvt2_bits(float a, float b) {
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float a) {
     return (uint16_t)(cvt2_bits(a, 0.0f) & 0xffffu);
 }
-__device__ __forceinline__ bf16x4 cvt4(f32x4 v) { return __builtin_convertvector(v, bf16x4); }
+// Written as two pair conversions: a whole-vector conversion can be lowered
+// to one conversion per element plus byte permutes.
+__device__ __forceinline__ bf16x4 cvt4(f32x4 v) {
+    const u32x2 p = {cvt2_bits(v[0], v[1]), cvt2_bits(v[2], v[3])};
+    return __builtin_bit_cast(bf16x4, p);
+}
 
 // Element loaders for the two I/O types.  bf16 travels as raw uint16_t.
 template <typename T> struct io;
