@@ -459,9 +459,10 @@ __global__ __launch_bounds__(CK<D>::NT) __attribute__((amdgpu_waves_per_eu(2, 2)
 struct WS64 {
     static constexpr int D = 64;
     static constexpr int NCB = 2, NRT = 4, NCT = 4;   // channel blocks, row / column tiles
-    static constexpr int NPROD = 3;
+    static constexpr int NPROD = 3;                   // producers per sequence
     static constexpr int NSLOT = 3;
     static constexpr int NSEQ = 2;                    // sequences per workgroup
+    static constexpr int NWAVE = NSEQ * (1 + NPROD);
     // slot layout (bytes)
     static constexpr int OFF_B = 0;                   // B~ frags, NCB x 1024
     static constexpr int OFF_R = 2048;                // R~ frags, NCB x 1024
@@ -869,7 +870,7 @@ __device__ __forceinline__ void ws_chunk_serial(f32x4 (*S)[4], const char *slot,
     ws_store_out(Ot, o, T, H, bb, h, chunk, lane);
 }
 
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void chunked64_ws_kernel(
+__global__ __launch_bounds__(64 * WS64::NWAVE) __attribute__((amdgpu_waves_per_eu(2, 2))) void chunked64_ws_kernel(
     int T, int H, int nbh, const uint16_t *__restrict__ r, const uint16_t *__restrict__ w,
     const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, const uint16_t *__restrict__ a,
     const uint16_t *__restrict__ b, const float *__restrict__ s0, const uint8_t *__restrict__ mask,
@@ -886,14 +887,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int g = lane >> 4, j = lane & 15;
     const int nchunks = (T + 15) / 16;
 
-    // Role assignment by SIMD.  The eight waves are ranked by (SIMD, wave
-    // index); ranks 0-3 serve the workgroup's first sequence and 4-7 its
-    // second, rank 0 of each group being the consumer.  With the usual two
-    // waves per SIMD the two consumers (whose work is mostly MFMA) land on
-    // different SIMDs, each sharing it with one producer, and the remaining
-    // producers pair up on the other two.  Correctness does not depend on the
-    // placement; it only picks which wave does what.
-    int *key_of = lds_sync + 16;   // 8 entries
+    // Role assignment by SIMD placement.  The consumers (mostly MFMA work,
+    // slowed down by sharing a SIMD with VALU-heavy producers) are taken
+    // from the SIMDs with the fewest workgroup waves, at most one per SIMD
+    // while that is possible.  The other waves become producers, alternating
+    // between the sequences in (SIMD, wave) order so that each sequence's
+    // producers are spread over different SIMDs.  (Measured: eight waves
+    // with three producers per sequence beat six waves with two, where the
+    // consumers run alone on a SIMD but production falls behind.)
+    // Correctness does not depend on the placement; it only picks which wave
+    // does what.
+    int *key_of = lds_sync + 16;   // NWAVE entries
     if (threadIdx.x < 16) lds_sync[threadIdx.x] = 0;
     if (lane == 0) {
         unsigned hw;
@@ -901,10 +905,31 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         key_of[wave] = (int)((hw >> 4) & 3) * 8 + wave;   // unique key: (simd, wave)
     }
     __syncthreads();
-    int rank = 0;
+    int ckey[C::NWAVE];   // (rank on the SIMD, waves on the SIMD, SIMD, wave)
 #pragma unroll
-    for (int w2 = 0; w2 < 8; ++w2) rank += key_of[w2] < key_of[wave] ? 1 : 0;
-    const int seq = rank >> 2, role = rank & 3;   // role 0 = consumer, 1..3 = producers
+    for (int w1 = 0; w1 < C::NWAVE; ++w1) {
+        int n = 0, before = 0;
+#pragma unroll
+        for (int w2 = 0; w2 < C::NWAVE; ++w2) {
+            const bool same = (key_of[w2] >> 3) == (key_of[w1] >> 3);
+            n += same ? 1 : 0;
+            before += (same && key_of[w2] < key_of[w1]) ? 1 : 0;
+        }
+        ckey[w1] = (before * 16 + n) * 32 + key_of[w1];
+    }
+    int crank = 0, prank = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < C::NWAVE; ++w2) crank += ckey[w2] < ckey[wave] ? 1 : 0;
+    const bool is_cons = crank < C::NSEQ;
+#pragma unroll
+    for (int w2 = 0; w2 < C::NWAVE; ++w2) {
+        int cr = 0;
+#pragma unroll
+        for (int w3 = 0; w3 < C::NWAVE; ++w3) cr += ckey[w3] < ckey[w2] ? 1 : 0;
+        prank += (cr >= C::NSEQ && key_of[w2] < key_of[wave]) ? 1 : 0;
+    }
+    const int seq = is_cons ? crank : prank % C::NSEQ;
+    const int role = is_cons ? 0 : 1 + prank / C::NSEQ;   // 0 = consumer, 1.. = producers
     const int bh = blockIdx.x * C::NSEQ + seq;
     if (bh >= nbh) return;
     const int bb = bh / H, h = bh % H;
@@ -1015,7 +1040,7 @@ static hipError_t launch_ck(const FwdArgs &p, hipStream_t stream)
 static hipError_t launch_ws64(const FwdArgs &p, hipStream_t stream)
 {
     const int nbh = p.B * p.H;
-    const dim3 grid((unsigned)((nbh + WS64::NSEQ - 1) / WS64::NSEQ)), block(64 * 4 * WS64::NSEQ);
+    const dim3 grid((unsigned)((nbh + WS64::NSEQ - 1) / WS64::NSEQ)), block(64 * WS64::NWAVE);
     hipLaunchKernelGGL(chunked64_ws_kernel, grid, block, 0, stream, p.T, p.H, nbh,
                        (const uint16_t *)p.r, (const uint16_t *)p.w, (const uint16_t *)p.k,
                        (const uint16_t *)p.v, (const uint16_t *)p.a, (const uint16_t *)p.b, p.s0,
