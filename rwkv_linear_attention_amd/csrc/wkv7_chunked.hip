@@ -96,8 +96,10 @@ __device__ __forceinline__ void load_raw(RawTile<D> &rt, const uint16_t *const *
     }
 }
 
-// Make a token that does not update an exact identity step (w = k = a = 0),
-// and a token past T inert (r = b = v = 0 as well).
+// Make a token that does not update an exact identity step: w, k, a, b (and
+// v when staged) are cleared, so that whatever they hold (even inf or nan)
+// cannot reach the state; r stays, since such a token still emits an
+// output.  A token past T is inert (r = 0 as well).
 template <int D>
 __device__ __forceinline__ void zero_inactive(RawTile<D> &rt, int narr)
 {
@@ -107,11 +109,10 @@ __device__ __forceinline__ void zero_inactive(RawTile<D> &rt, int narr)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
-            for (int arr = 1; arr <= 3; ++arr)
+            for (int arr = 1; arr <= 4; ++arr)
                 rt.x[s][arr][hh] = rt.upd ? rt.x[s][arr][hh] : u32x2{0u, 0u};
             rt.x[s][0][hh] = rt.valid ? rt.x[s][0][hh] : u32x2{0u, 0u};
-            rt.x[s][4][hh] = rt.valid ? rt.x[s][4][hh] : u32x2{0u, 0u};
-            if (narr > 5) rt.x[s][5][hh] = rt.valid ? rt.x[s][5][hh] : u32x2{0u, 0u};
+            if (narr > 5) rt.x[s][5][hh] = rt.upd ? rt.x[s][5][hh] : u32x2{0u, 0u};
         }
 }
 
@@ -440,20 +441,25 @@ __global__ __launch_bounds__(CK<D>::NT) __attribute__((amdgpu_waves_per_eu(2, 2)
 // ===========================================================================
 // Warp-specialised variant (K = V = 64).
 //
-// One workgroup per (b, h) with four waves.  Wave 0 is the consumer: it keeps
-// the whole 64 x 64 fp32 state in MFMA accumulator registers and runs only the
-// S-dependent chain.  Waves 1..3 are producers: producer p prepares chunks
-// c = p, p + 3, ... from raw tiles that are streamed into a private LDS buffer
-// with asynchronous global->LDS loads one chunk ahead, and hands the chunk's
-// operands to the consumer through a two-slot LDS ring.  Hand-off uses LDS
-// counters (ready[slot] = chunk + 1 once a slot is filled; done = number of
-// chunks whose operands the consumer has copied out), so producers and the
+// One workgroup of eight waves runs two (b, h) sequences.  Per sequence one
+// wave is the consumer: it keeps the whole 64 x 64 fp32 state in MFMA
+// accumulator registers and runs only the S-dependent chain.  Three waves
+// are producers: producer p prepares chunks c = p, p + 3, ... from raw tiles
+// that are streamed into a private LDS buffer with asynchronous global->LDS
+// loads one chunk ahead, and hands the chunk's operands to the consumer
+// through a three-slot LDS ring.  Hand-off uses LDS counters (ready[slot] =
+// 2 (chunk + 1) + extreme-decay flag once a slot is filled; done = number of
+// chunks whose operands the consumer has read), so producers and the
 // consumer never meet at a workgroup barrier.  Every wait is bounded.
 //
 // Products on the consumer side pair operands along k so that each
 // 16x16x32 MFMA carries two 16-token contractions, and the output is formed
 // transposed (O^T = S^T R~^T + [U;V]^T [M_ra | M_rk]^T) so that each lane
-// stores four adjacent bf16 outputs of one token.
+// stores four adjacent bf16 outputs of one token.  The chunk-end decay is
+// applied by the consumer after the rank-16 updates,
+// S' = diag(e^{G_L}) (S + A^^T U + K^^T V), so that the producer hands over
+// A^ and K^ (row-major token x channel tiles, read back as MFMA fragments
+// with transposing LDS reads) instead of scaled, transposed copies.
 // ===========================================================================
 
 struct WS64 {
@@ -463,17 +469,18 @@ struct WS64 {
     static constexpr int NSLOT = 3;
     static constexpr int NSEQ = 2;                    // sequences per workgroup
     static constexpr int NWAVE = NSEQ * (1 + NPROD);
-    // slot layout (bytes)
+    // slot layout (bytes); tiles are 16 tokens x 64 channels bf16, swizzled
     static constexpr int OFF_B = 0;                   // B~ frags, NCB x 1024
     static constexpr int OFF_R = 2048;                // R~ frags, NCB x 1024
     static constexpr int OFF_TN = 4096;               // [T | N_bk] A-frags, 1024
-    static constexpr int OFF_MM = 5632;               // [M_ra^T | M_rk^T hi] B-frags, 1024
-    static constexpr int OFF_MRKL = 6656;             // M_rk^T lo B-frag, 512
-    static constexpr int OFF_ATK = 7168;              // [A~^T | K~^T hi] A-frags, NRT x 1024
-    static constexpr int OFF_KTL = 11264;             // K~^T lo A-frags, NRT x 512
-    static constexpr int OFF_V = 13312;               // V frags per column tile, NCT x 512
-    static constexpr int OFF_EGL = 15360;             // e^{G_L}, 64 floats
-    static constexpr int SLOT = 15616;
+    static constexpr int OFF_MM = 5120;               // [M_ra^T | M_rk^T hi] B-frags, 1024
+    static constexpr int OFF_MRKL = 6144;             // M_rk^T lo B-frag, 512
+    static constexpr int OFF_EGL = 6656;              // e^{G_L}, 64 floats
+    static constexpr int OFF_AH = 6912;               // A^ tile, 2048
+    static constexpr int OFF_KH = 8960;               // K^ hi tile, 2048
+    static constexpr int OFF_KL = 11008;              // K^ lo tile, 2048
+    static constexpr int OFF_V = 13056;               // V tile, 2048 (global->LDS copy)
+    static constexpr int SLOT = 15104;
     static constexpr int RAW = 5 * NCB * 1024;        // raw r, w, k, a, b tiles of one chunk
     static constexpr int OFF_SLOTS = 0;
 };
@@ -551,32 +558,44 @@ __device__ __forceinline__ void ws_read_raw(RawTile<64> &rt, const char *raw, in
                                                     16 * (t + 16 * (2 * hh + (g >> 1))) + 8 * (g & 1));
 }
 
-// Producer: request the chunk's value tile in MFMA B-fragment order: lane
-// (g, j) gets V[4g + i][16q + j], i = 0..3, for column tile q, as 16 zero-
-// extended halves (packed by ws_pack_v once they have arrived).  Tokens past
-// T read token T-1: a token that does not update has k = 0, so its value row
-// is multiplied by zero everywhere.  Loads are unconditional and their
-// results are consumed only after the explicit wait at the top of the next
-// iteration, so that issuing them never forces a wait on the prefetch.
-__device__ __forceinline__ void ws_load_v(uint32_t (*x)[4], const uint16_t *v, size_t seq_base,
-                                          uint32_t tok_stride, int T, int chunk, int lane)
+// Swizzled 16 x 64 bf16 tile: the 16-byte chunk c (channels 8c .. 8c + 7) of
+// row r is stored at chunk position 8 r + (c ^ (r & 7)).  Row writes (one
+// row per lane group) and transposing column reads (four rows per 16-lane
+// group) then spread over all LDS banks.  Byte offset of the four channels
+// col .. col + 3 (col a multiple of 4) of row r:
+__device__ __forceinline__ int tile_off(int r, int col)
 {
-    const int g = lane >> 4, j = lane & 15;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t tok = (uint32_t)min(chunk * 16 + 4 * g + i, T - 1);
-        const uint16_t *p = v + seq_base + (size_t)tok * tok_stride + j;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) x[q][i] = p[16 * q];
-    }
+    return (r * 8 + ((col >> 3) ^ (r & 7))) * 16 + (col & 4) * 2;
 }
 
-__device__ __forceinline__ void ws_pack_v(uint32_t (*vq)[2], const uint32_t (*x)[4])
+// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane
+// l supplies the address of four consecutive elements; lanes 4k .. 4k + 3
+// together describe row k of a 4 x 16 block, and lane l receives column l.
+// Here the group reads rows row0 .. row0 + 3, columns col0 .. col0 + 15 of
+// a swizzled tile, so lane l gets X[row0 + k][col0 + l], k = 0..3: an MFMA
+// B-fragment of X (k = token) or A-fragment of X^T.
+__device__ __forceinline__ bf16x4 tile_tr(const char *tile, int row0, int col0, int lane)
+{
+    typedef __attribute__((address_space(3))) bf16x4 *lds_bf16x4_ptr;
+    const int l = lane & 15;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4_ptr)(tile + tile_off(row0 + (l >> 2), col0 + 4 * (l & 3))));
+}
+
+// Producer: copy the chunk's value tile (16 tokens x 64 channels) into the
+// swizzled tile at LDS byte address `tile_lds` with two asynchronous
+// global->LDS loads; lane l of load j fills chunk position 64 j + l.  Tokens
+// past T read token T-1: a token that does not update has k = 0, so its
+// value row is multiplied by zero everywhere.
+__device__ __forceinline__ void ws_issue_v(uint32_t tile_lds, const uint16_t *v, size_t seq_base,
+                                           uint32_t tok_stride, int T, int chunk, int lane)
 {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        vq[q][0] = x[q][0] | (x[q][1] << 16);
-        vq[q][1] = x[q][2] | (x[q][3] << 16);
+    for (int jl = 0; jl < 2; ++jl) {
+        const int row = 8 * jl + (lane >> 3);
+        const int c = (lane & 7) ^ (row & 7);
+        const uint32_t tok = (uint32_t)min(chunk * 16 + row, T - 1);
+        copy16_to_lds(v + seq_base + (size_t)tok * tok_stride + 8 * c, tile_lds + 1024 * jl);
     }
 }
 
@@ -589,9 +608,8 @@ __device__ __forceinline__ void ws_pack_v(uint32_t (*vq)[2], const uint32_t (*x)
 // Precision: the r.k matrix M_rk (whose entries multiply the value tile
 // directly in the output) is formed from hi/lo bf16 splits of both operands
 // (three products, relative error about 2^-16); the other chunk matrices are
-// single bf16 products with fp32 accumulation.
-// Products with the value tile split their left operand into hi/lo bf16
-// (M_rk and K~).
+// single bf16 products with fp32 accumulation.  K^ is handed over as a hi/lo
+// pair, as is M_rk, since both multiply the value tile.
 // Returns the wave-uniform extreme-decay flag of the chunk.
 __device__ int ws_precompute(const RawTile<64> &rt, char *slot, int lane, const bf16x8 *psel,
                              bf16x4 ltri)
@@ -630,7 +648,7 @@ __device__ int ws_precompute(const RawTile<64> &rt, char *slot, int lane, const 
         unpack8(rt.x[s][2], kv);
         unpack8(rt.x[s][3], av);
         unpack8(rt.x[s][4], bv);
-        float Rt[8], Bt[8], Ah[8], Kh[8], At[8], Kt[8];
+        float Rt[8], Bt[8], Ah[8], Kh[8];
         f32x4 eGL4[2];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -645,8 +663,6 @@ __device__ int ws_precompute(const RawTile<64> &rt, char *slot, int lane, const 
             Bt[e] = bv[e] * eGp;
             Ah[e] = av[e] * enG;
             Kh[e] = kv[e] * enG;
-            At[e] = Ah[e] * eGL;
-            Kt[e] = Kh[e] * eGL;
         }
         // e^{G_L} of channels 32s + 16hh + 4g .. +3 (one writer per row).
         if (t == 0) {
@@ -654,10 +670,7 @@ __device__ int ws_precompute(const RawTile<64> &rt, char *slot, int lane, const 
             for (int hh = 0; hh < 2; ++hh)
                 *(f32x4 *)(slot + C::OFF_EGL + (32 * s + 16 * hh + 4 * g) * 4) = eGL4[hh];
         }
-        bf16x8 Kth, Ktl;
-        split8(Kt, Kth, Ktl);
-        const bf16x8 Rh = pack8(Rt), Bh = pack8(Bt), Khh = pack8(Kh);
-        const bf16x8 Ahh = pack8(Ah), Ath = pack8(At);
+        const bf16x8 Rh = pack8(Rt), Bh = pack8(Bt), Khh = pack8(Kh), Ahh = pack8(Ah);
         // (R~ K^^T)^T to about 16 bits: hi.hi + hi.lo + lo.hi.
         bf16x8 Rl, Khl;
         {
@@ -680,12 +693,15 @@ __device__ int ws_precompute(const RawTile<64> &rt, char *slot, int lane, const 
 
         st16(slot + C::OFF_B + s * 1024 + lane * 16, Bh);
         st16(slot + C::OFF_R + s * 1024 + lane * 16, Rh);
+        // Row t of the A^, K^ hi and K^ lo tiles, channels 32s + 16hh + 4g .. +3.
+        const u32x4 ab = __builtin_bit_cast(u32x4, Ahh), kb = __builtin_bit_cast(u32x4, Khh),
+                    lb = __builtin_bit_cast(u32x4, Khl);
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-            const int q = 2 * s + hh;
-            st8(slot + C::OFF_ATK + q * 1024 + lane * 16, cvt4(mfma32(Ath, psel[hh], zero4())));
-            st8(slot + C::OFF_ATK + q * 1024 + lane * 16 + 8, cvt4(mfma32(Kth, psel[hh], zero4())));
-            st8(slot + C::OFF_KTL + q * 512 + lane * 8, cvt4(mfma32(Ktl, psel[hh], zero4())));
+            const int off = tile_off(t, 32 * s + 16 * hh + 4 * g);
+            *(u32x2 *)(slot + C::OFF_AH + off) = u32x2{ab[2 * hh], ab[2 * hh + 1]};
+            *(u32x2 *)(slot + C::OFF_KH + off) = u32x2{kb[2 * hh], kb[2 * hh + 1]};
+            *(u32x2 *)(slot + C::OFF_KL + off) = u32x2{lb[2 * hh], lb[2 * hh + 1]};
         }
     }
     f32x4 mrkT = mrkT0 + mrkT1;
@@ -824,20 +840,19 @@ __device__ __forceinline__ void ws_chunk_serial(f32x4 (*S)[4], const char *slot,
     for (int n = 0; n < 4; ++n) {
         sb0[n] = cat8(cvt4(S[0][n]), cvt4(S[1][n]));
         sb1[n] = cat8(cvt4(S[2][n]), cvt4(S[3][n]));
-        vf[n] = ld8(slot + C::OFF_V + n * 512 + lane * 8);
+        vf[n] = tile_tr(slot + C::OFF_V, 4 * g, 16 * n, lane);   // V[4g + i][16n + j]
     }
     const bf16x8 bt0 = ld16(slot + C::OFF_B + lane * 16), bt1 = ld16(slot + C::OFF_B + 1024 + lane * 16);
     // X = B~ S
     f32x4 X[4];
 #pragma unroll
     for (int n = 0; n < 4; ++n) X[n] = mfma32(bt0, sb0[n], zero4());
-    // S <- diag(e^{G_L}) S + K~lo^T V  (independent of X)
+    // S += K^lo^T V  (independent of X; the decay is applied at the end)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const f32x4 eg = *(const f32x4 *)(slot + C::OFF_EGL + (16 * q + 4 * g) * 4);
-        const bf16x4 ktl = ld8(slot + C::OFF_KTL + q * 512 + lane * 8);
+        const bf16x4 ktl = tile_tr(slot + C::OFF_KL, 4 * g, 16 * q, lane);
 #pragma unroll
-        for (int n = 0; n < 4; ++n) S[q][n] = mfma16(ktl, vf[n], S[q][n] * eg);
+        for (int n = 0; n < 4; ++n) S[q][n] = mfma16(ktl, vf[n], S[q][n]);
     }
 #pragma unroll
     for (int n = 0; n < 4; ++n) X[n] = mfma32(bt1, sb1[n], X[n]);
@@ -856,12 +871,14 @@ __device__ __forceinline__ void ws_chunk_serial(f32x4 (*S)[4], const char *slot,
     for (int n = 0; n < 4; ++n) Ot[n] = mfma32(sb1[n], rt1, Ot[n]);
 #pragma unroll
     for (int n = 0; n < 4; ++n) Ot[n] = mfma16(vf[n], mrkl, Ot[n]);
-    // S += [A~^T | K~^T] [U; V]
+    // S <- diag(e^{G_L}) (S + [A^^T | K^hi^T] [U; V])
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const bf16x8 atk = ld16(slot + C::OFF_ATK + q * 1024 + lane * 16);
+        const bf16x8 atk = cat8(tile_tr(slot + C::OFF_AH, 4 * g, 16 * q, lane),
+                                tile_tr(slot + C::OFF_KH, 4 * g, 16 * q, lane));
+        const f32x4 eg = *(const f32x4 *)(slot + C::OFF_EGL + (16 * q + 4 * g) * 4);
 #pragma unroll
-        for (int n = 0; n < 4; ++n) S[q][n] = mfma32(atk, uv[n], S[q][n]);
+        for (int n = 0; n < 4; ++n) S[q][n] = mfma32(atk, uv[n], S[q][n]) * eg;
     }
     // O^T += [U; V]^T [M_ra | M_rk]^T
     const bf16x8 mm = ld16(slot + C::OFF_MM + lane * 16);
@@ -987,20 +1004,16 @@ __global__ __launch_bounds__(64 * WS64::NWAVE) __attribute__((amdgpu_waves_per_e
         bf16x4 ltri;
 #pragma unroll
         for (int i = 0; i < 4; ++i) ltri[i] = (__bf16)((4 * g + i <= j) ? 1.0f : 0.0f);
-        // Loop-carried requests for this producer's next chunk: value halves and
-        // the mask byte of token (next chunk, lane & 15).
-        uint32_t vn[4][4];
+        // Loop-carried request for this producer's next chunk: the mask byte
+        // of token (next chunk, lane & 15).
         uint32_t mnext = 1;
         const int t = lane & 15;
         if (p < nchunks) {
             ws_issue_raw(raw_lds, src, seq_base, tok_stride, T, p, lane);
-            ws_load_v(vn, v, seq_base, tok_stride, T, p, lane);
             if (mask) mnext = mask[(size_t)bb * T + min(p * 16 + t, T - 1)];
         }
         for (int c = p; c < nchunks; c += C::NPROD) {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            uint32_t vq[4][2];
-            ws_pack_v(vq, vn);
             const uint32_t mcur = mnext;
             RawTile<64> rt;
             ws_read_raw(rt, raw, lane);
@@ -1008,7 +1021,6 @@ __global__ __launch_bounds__(64 * WS64::NWAVE) __attribute__((amdgpu_waves_per_e
             if (c + C::NPROD < nchunks) {
                 const int cn = c + C::NPROD;
                 ws_issue_raw(raw_lds, src, seq_base, tok_stride, T, cn, lane);
-                ws_load_v(vn, v, seq_base, tok_stride, T, cn, lane);
                 if (mask) mnext = mask[(size_t)bb * T + min(cn * 16 + t, T - 1)];
             }
             const int tok = c * 16 + t;
@@ -1017,9 +1029,20 @@ __global__ __launch_bounds__(64 * WS64::NWAVE) __attribute__((amdgpu_waves_per_e
             zero_inactive<64>(rt, 5);
             char *slot = lds + C::OFF_SLOTS + (c % C::NSLOT) * C::SLOT;
             spin_ge(done, c - C::NSLOT + 1);   // the slot's previous chunk is consumed
-            const int flag = ws_precompute(rt, slot, lane, psel, ltri);
+            ws_issue_v(lds_addr(slot + C::OFF_V), v, seq_base, tok_stride, T, c, lane);
+            if (!__all(rt.upd)) {
+                // Value rows of tokens that do not update are cleared, so that
+                // whatever they hold (even inf or nan) cannot reach the state.
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                if (!rt.upd) {
+                    const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int q = 0; q < 4; ++q) *(u32x2 *)(slot + C::OFF_V + q * 512 + lane * 8) = u32x2{vq[q][0], vq[q][1]};
+                    for (int hh = 0; hh < 2; ++hh)
+                        *(u32x4 *)(slot + C::OFF_V + tile_off(t, 16 * g + 8 * hh)) = zero;
+                }
+            }
+            const int flag = ws_precompute(rt, slot, lane, psel, ltri);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the value tile has landed
             lds_wait();
             lds_store_relaxed(&ready[c % C::NSLOT], 2 * (c + 1) + flag);
         }

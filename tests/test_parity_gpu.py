@@ -145,6 +145,25 @@ def test_masks(algo, kind):
 
 
 @pytest.mark.parametrize("algo", [REC, CHK])
+@pytest.mark.parametrize("D", [64, 128])
+def test_masked_tokens_ignore_nonfinite_inputs(algo, D):
+    """A masked token leaves the state alone whatever its w, k, v, a, b hold
+    (padding may be uninitialised memory); its r still produces an output."""
+    inp = synth.make(1, B=2, T=100, H=2, K=D, seed=21 + D, init=True, mask="bernoulli")
+    o_ref, s_ref = hz.oracle_fwd(inp)
+    bad = dict(inp)
+    masked = inp["mask"] == 0
+    assert masked.any() and (~masked).any()
+    for n, val in zip("wkvab", (np.nan, np.inf, np.nan, -np.inf, np.nan)):
+        x = np.array(inp[n], copy=True)
+        x[masked] = val
+        bad[n] = x
+    o, sf = hz.gpu_fwd(hz.to_dev(bad), algo=algo)
+    torch.cuda.synchronize()
+    hz.check("bf16", hz.to_np(o), o_ref, hz.to_np(sf), s_ref, f"non-finite masked tokens D={D} algo={algo}")
+
+
+@pytest.mark.parametrize("algo", [REC, CHK])
 def test_state_aliasing_and_null_states(algo):
     inp = synth.make(1, B=2, T=70, H=2, K=64, seed=3)
     dev = hz.to_dev(inp)
