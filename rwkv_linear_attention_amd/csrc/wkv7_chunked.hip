@@ -17,10 +17,11 @@
 // token-by-token path instead.  A token with mask 0 (or past T) gets
 // w = a = k = b = 0, an exact identity step.
 //
-// Layout of the work (warp specialisation).  Per (b, h) sequence, D / 64
-// consumer waves each keep a D x 64 column slice of the fp32 state in MFMA
-// accumulator registers and run only the S-dependent chain; the column split
-// is exact (U, O and S' of a column slice depend only on that slice).
+// Layout of the work (warp specialisation).  Per (b, h) sequence, consumer
+// waves each keep a column slice of the fp32 state (64 columns at D = 64,
+// 32 at D = 128) in MFMA accumulator registers and run only the
+// S-dependent chain; the column split is exact (U, O and S' of a column
+// slice depend only on that slice).
 // Producer waves prepare chunks c = p, p + NPROD, ... from raw tiles streamed
 // into a private LDS buffer with asynchronous global->LDS loads one chunk
 // ahead, and hand each chunk's operands to the consumers through a
@@ -28,8 +29,8 @@
 // 2 (chunk + 1) + extreme-decay flag once a slot is filled; done = number of
 // (consumer, chunk) pairs finished), so producers and consumers never meet at
 // a workgroup barrier.  Every wait is bounded.  At D = 64 one workgroup runs
-// two sequences with three producers each (eight waves); at D = 128 one
-// sequence with two producers (four waves).
+// two sequences of one consumer and three producers (eight waves); at
+// D = 128 one sequence of four consumers and three producers (seven waves).
 //
 // Products on the consumer side pair operands along k so that each
 // 16x16x32 MFMA carries two 16-token contractions, and the output is formed
@@ -56,12 +57,14 @@ template <int D> struct WS {
     static_assert(D == 64 || D == 128, "head size");
     static constexpr int NCB = D / 32;                 // 32-channel blocks
     static constexpr int NQ = D / 16;                  // 16-row tiles of the state
-    static constexpr int NCONS = D / 64;               // consumers per sequence, 64 columns each
-    // D = 64: two sequences of one consumer and three producers, two waves
-    // per SIMD.  D = 128: one sequence of two consumers and two producers,
-    // one wave per SIMD, so that a consumer can hold its 128 x 64 state slice
-    // and working set in up to 512 registers.
-    static constexpr int NPROD = D == 64 ? 3 : 2;      // producers per sequence
+    // D = 64: two sequences of one consumer (64 state columns) and three
+    // producers.  D = 128: one sequence of four consumers (32 columns each,
+    // so that a 128 x 32 state slice and its working set stay in ordinary
+    // VGPRs) and three producers.  Two waves per SIMD in both cases.
+    static constexpr int NCONS = D == 64 ? 1 : 4;      // consumers per sequence
+    static constexpr int CW = D / NCONS;               // state columns per consumer
+    static constexpr int NT = CW / 16;                 // 16-column tiles per consumer
+    static constexpr int NPROD = 3;                    // producers per sequence
     static constexpr int NSLOT = 3;                    // slot ring depth per sequence
     static constexpr int NSEQ = D == 64 ? 2 : 1;       // sequences per workgroup
     static constexpr int NWAVE = NSEQ * (NCONS + NPROD);
@@ -419,16 +422,16 @@ __device__ int ws_precompute(const RawTile<D> &rt, char *slot, int lane, const b
 // ---- consumer ----------------------------------------------------------------
 //
 // S[q][n] holds rows 16q + 4g + i, column cbase + 16n + j of the state (lane
-// (g = l/16, j = l%16)); cbase = 64 x the consumer's column slice.
+// (g = l/16, j = l%16)), n < NT; cbase = CW x the consumer's index.
 
 // Exact path: token-by-token fp32 update of the consumer's column slice.
 template <int D>
-__device__ void ws_chunk_exact(f32x4 (*S)[4], const uint16_t *r, const uint16_t *w,
+__device__ void ws_chunk_exact(f32x4 (*S)[WS<D>::NT], const uint16_t *r, const uint16_t *w,
                                const uint16_t *k, const uint16_t *v, const uint16_t *a,
                                const uint16_t *b, const uint8_t *mask, uint16_t *o, int T, int H,
                                int bb, int h, int chunk, int cbase, int lane)
 {
-    constexpr int NQ = D / 16;
+    constexpr int NQ = D / 16, NT = WS<D>::NT;
     const int g = lane >> 4, j = lane & 15;
     for (int tt = 0; tt < 16; ++tt) {
         const int tok = chunk * 16 + tt;
@@ -436,23 +439,25 @@ __device__ void ws_chunk_exact(f32x4 (*S)[4], const uint16_t *r, const uint16_t 
         const bool upd = mask == nullptr || mask[(size_t)bb * T + tok] != 0;
         const size_t base = (((size_t)bb * T + tok) * H + h) * D;
         if (upd) {
-            float sb[4] = {0.f, 0.f, 0.f, 0.f};
+            float sb[NT] = {};
 #pragma unroll
             for (int q = 0; q < NQ; ++q) {
+                if constexpr (NQ > 4) __builtin_amdgcn_sched_barrier(0);   // bound the hoisted loads
                 const u32x2 bq = *(const u32x2 *)(b + base + 16 * q + 4 * g);
                 const float be[4] = {bf16_lo(bq[0]), bf16_hi(bq[0]), bf16_lo(bq[1]), bf16_hi(bq[1])};
 #pragma unroll
-                for (int n = 0; n < 4; ++n)
+                for (int n = 0; n < NT; ++n)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) sb[n] = fmaf(be[i], S[q][n][i], sb[n]);
             }
 #pragma unroll
-            for (int n = 0; n < 4; ++n) sb[n] = xor_sum(xor_sum(sb[n], 16), 32);
-            float vj[4];
+            for (int n = 0; n < NT; ++n) sb[n] = xor_sum(xor_sum(sb[n], 16), 32);
+            float vj[NT];
 #pragma unroll
-            for (int n = 0; n < 4; ++n) vj[n] = bf16_bits_to_f32(v[base + cbase + 16 * n + j]);
+            for (int n = 0; n < NT; ++n) vj[n] = bf16_bits_to_f32(v[base + cbase + 16 * n + j]);
 #pragma unroll
             for (int q = 0; q < NQ; ++q) {
+                if constexpr (NQ > 4) __builtin_amdgcn_sched_barrier(0);
                 const u32x2 wq = *(const u32x2 *)(w + base + 16 * q + 4 * g);
                 const u32x2 aq = *(const u32x2 *)(a + base + 16 * q + 4 * g);
                 const u32x2 kq = *(const u32x2 *)(k + base + 16 * q + 4 * g);
@@ -463,26 +468,27 @@ __device__ void ws_chunk_exact(f32x4 (*S)[4], const uint16_t *r, const uint16_t 
                 for (int i = 0; i < 4; ++i) {
                     const float d = __expf(we[i]);
 #pragma unroll
-                    for (int n = 0; n < 4; ++n)
+                    for (int n = 0; n < NT; ++n)
                         S[q][n][i] = fmaf(d, S[q][n][i], fmaf(ae[i], sb[n], ke[i] * vj[n]));
                 }
             }
         }
-        float ov[4] = {0.f, 0.f, 0.f, 0.f};
+        float ov[NT] = {};
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
+            if constexpr (NQ > 4) __builtin_amdgcn_sched_barrier(0);
             const u32x2 rq = *(const u32x2 *)(r + base + 16 * q + 4 * g);
             const float re[4] = {bf16_lo(rq[0]), bf16_hi(rq[0]), bf16_lo(rq[1]), bf16_hi(rq[1])};
 #pragma unroll
-            for (int n = 0; n < 4; ++n)
+            for (int n = 0; n < NT; ++n)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) ov[n] = fmaf(re[i], S[q][n][i], ov[n]);
         }
 #pragma unroll
-        for (int n = 0; n < 4; ++n) ov[n] = xor_sum(xor_sum(ov[n], 16), 32);
+        for (int n = 0; n < NT; ++n) ov[n] = xor_sum(xor_sum(ov[n], 16), 32);
         if (g == 0) {
 #pragma unroll
-            for (int n = 0; n < 4; ++n) o[base + cbase + 16 * n + j] = f32_to_bf16_bits(ov[n]);
+            for (int n = 0; n < NT; ++n) o[base + cbase + 16 * n + j] = f32_to_bf16_bits(ov[n]);
         }
     }
 }
@@ -498,7 +504,7 @@ __device__ __forceinline__ void ws_store_out(const f32x4 *Ot, uint16_t *o, int T
     if (tok < T) {
         uint16_t *op = o + (((size_t)bb * T + tok) * H + h) * D + cbase + 4 * g;
 #pragma unroll
-        for (int n = 0; n < 4; ++n)
+        for (int n = 0; n < WS<D>::NT; ++n)
             *(u32x2 *)(op + 16 * n) = u32x2{cvt2_bits(Ot[n][0], Ot[n][1]), cvt2_bits(Ot[n][2], Ot[n][3])};
     }
 }
@@ -508,71 +514,77 @@ __device__ __forceinline__ void ws_store_out(const f32x4 *Ot, uint16_t *o, int T
 // the S-independent products are placed where they fill the latency of the
 // S -> X -> U -> S' chain.
 template <int D>
-__device__ __forceinline__ void ws_chunk_serial(f32x4 (*S)[4], const char *slot, uint16_t *o, int T,
+__device__ __forceinline__ void ws_chunk_serial(f32x4 (*S)[WS<D>::NT], const char *slot, uint16_t *o, int T,
                                                 int H, int bb, int h, int chunk, int cbase, int lane)
 {
     using C = WS<D>;
+    constexpr int NT = C::NT;
     const int g = lane >> 4;
     // bf16 copy of the chunk-start state as MFMA fragments: block s pairs row
     // tiles 2s and 2s + 1 (k-slot 4hh + i of lane group g is channel
     // 32s + 16hh + 4g + i, the producer's channel order).
-    bf16x8 sb[C::NCB][4];
-    bf16x4 vf[4];
+    bf16x8 sb[C::NCB][NT];
+    bf16x4 vf[NT];
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
+    for (int n = 0; n < NT; ++n) {
 #pragma unroll
         for (int s = 0; s < C::NCB; ++s) sb[s][n] = cat8(cvt4(S[2 * s][n]), cvt4(S[2 * s + 1][n]));
         vf[n] = tile_tr<D>(slot + C::OFF_V, 4 * g, cbase + 16 * n, lane);   // V[4g + i][cbase + 16n + j]
     }
     // X = B~ S
-    f32x4 X[4];
+    f32x4 X[NT];
     {
         const bf16x8 bt = ld16(slot + C::OFF_B + lane * 16);
 #pragma unroll
-        for (int n = 0; n < 4; ++n) X[n] = mfma32(bt, sb[0][n], zero4());
+        for (int n = 0; n < NT; ++n) X[n] = mfma32(bt, sb[0][n], zero4());
     }
     // S += K^lo^T V  (independent of X; the decay is applied at the end)
 #pragma unroll
     for (int q = 0; q < C::NQ; ++q) {
         const bf16x4 ktl = tile_tr<D>(slot + C::OFF_KL, 4 * g, 16 * q, lane);
 #pragma unroll
-        for (int n = 0; n < 4; ++n) S[q][n] = mfma16(ktl, vf[n], S[q][n]);
+        for (int n = 0; n < NT; ++n) S[q][n] = mfma16(ktl, vf[n], S[q][n]);
     }
 #pragma unroll
     for (int s = 1; s < C::NCB; ++s) {
         const bf16x8 bt = ld16(slot + C::OFF_B + s * 1024 + lane * 16);
 #pragma unroll
-        for (int n = 0; n < 4; ++n) X[n] = mfma32(bt, sb[s][n], X[n]);
+        for (int n = 0; n < NT; ++n) X[n] = mfma32(bt, sb[s][n], X[n]);
     }
     // O^T, S-part (chunk-start state)
-    f32x4 Ot[4];
+    f32x4 Ot[NT];
 #pragma unroll
     for (int s = 0; s < C::NCB; ++s) {
         const bf16x8 rt = ld16(slot + C::OFF_R + s * 1024 + lane * 16);
 #pragma unroll
-        for (int n = 0; n < 4; ++n) Ot[n] = mfma32(sb[s][n], rt, s == 0 ? zero4() : Ot[n]);
+        for (int n = 0; n < NT; ++n) Ot[n] = mfma32(sb[s][n], rt, s == 0 ? zero4() : Ot[n]);
     }
     // U = T X + N_bk V
     const bf16x8 tn = ld16(slot + C::OFF_TN + lane * 16);
-    bf16x8 uv[4];
+    bf16x8 uv[NT];
 #pragma unroll
-    for (int n = 0; n < 4; ++n) uv[n] = cat8(cvt4(mfma32(tn, cat8(cvt4(X[n]), vf[n]), zero4())), vf[n]);
+    for (int n = 0; n < NT; ++n) uv[n] = cat8(cvt4(mfma32(tn, cat8(cvt4(X[n]), vf[n]), zero4())), vf[n]);
     const bf16x4 mrkl = ld8(slot + C::OFF_MRKL + lane * 8);
 #pragma unroll
-    for (int n = 0; n < 4; ++n) Ot[n] = mfma16(vf[n], mrkl, Ot[n]);
+    for (int n = 0; n < NT; ++n) Ot[n] = mfma16(vf[n], mrkl, Ot[n]);
     // S <- diag(e^{G_L}) (S + [A^^T | K^hi^T] [U; V])
 #pragma unroll
     for (int q = 0; q < C::NQ; ++q) {
+        // At D = 128 the operand reads of the 8 row tiles are not all hoisted
+        // to the top (that would not fit in the register file).
+        if constexpr (C::NQ > 4) {
+            if (q % 4 == 0) __builtin_amdgcn_sched_barrier(0);
+        }
         const bf16x8 atk = cat8(tile_tr<D>(slot + C::OFF_AH, 4 * g, 16 * q, lane),
                                 tile_tr<D>(slot + C::OFF_KH, 4 * g, 16 * q, lane));
         const f32x4 eg = *(const f32x4 *)(slot + C::OFF_EGL + (16 * q + 4 * g) * 4);
 #pragma unroll
-        for (int n = 0; n < 4; ++n) S[q][n] = mfma32(atk, uv[n], S[q][n]) * eg;
+        for (int n = 0; n < NT; ++n) S[q][n] = mfma32(atk, uv[n], S[q][n]) * eg;
     }
     // O^T += [U; V]^T [M_ra | M_rk]^T
     const bf16x8 mm = ld16(slot + C::OFF_MM + lane * 16);
 #pragma unroll
-    for (int n = 0; n < 4; ++n) Ot[n] = mfma32(uv[n], mm, Ot[n]);
+    for (int n = 0; n < NT; ++n) Ot[n] = mfma32(uv[n], mm, Ot[n]);
     ws_store_out<D>(Ot, o, T, H, bb, h, chunk, cbase, lane);
 }
 
@@ -648,17 +660,23 @@ __attribute__((amdgpu_waves_per_eu(WS<D>::WAVES_PER_SIMD, WS<D>::WAVES_PER_SIMD)
     int *done = ready + C::NSLOT;
 
     if (is_cons) {
-        // ---------------- consumer: columns cbase .. cbase + 63 ----------------
-        const int cbase = 64 * (crank / C::NSEQ);
-        f32x4 S[C::NQ][4];
+        // ---------------- consumer: columns cbase .. cbase + CW - 1 ----------------
+        const int cbase = C::CW * (crank / C::NSEQ);
+        f32x4 S[C::NQ][C::NT];
         const size_t st_base = (size_t)bh * D * D;
 #pragma unroll
         for (int q = 0; q < C::NQ; ++q)
 #pragma unroll
-            for (int n = 0; n < 4; ++n)
+            for (int n = 0; n < C::NT; ++n) S[q][n] = zero4();
+        if (s0) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    S[q][n][i] = s0 ? s0[st_base + (size_t)(16 * q + 4 * g + i) * D + cbase + 16 * n + j] : 0.0f;
+            for (int q = 0; q < C::NQ; ++q)
+#pragma unroll
+                for (int n = 0; n < C::NT; ++n)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        S[q][n][i] = s0[st_base + (size_t)(16 * q + 4 * g + i) * D + cbase + 16 * n + j];
+        }
         for (int c = 0; c < nchunks; ++c) {
             const char *slot = lds + (c % C::NSLOT) * C::SLOT;
             // ready[slot] = 2 (c + 1) + extreme-decay flag once chunk c is in the slot
@@ -674,7 +692,7 @@ __attribute__((amdgpu_waves_per_eu(WS<D>::WAVES_PER_SIMD, WS<D>::WAVES_PER_SIMD)
 #pragma unroll
             for (int q = 0; q < C::NQ; ++q)
 #pragma unroll
-                for (int n = 0; n < 4; ++n)
+                for (int n = 0; n < C::NT; ++n)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         sf[st_base + (size_t)(16 * q + 4 * g + i) * D + cbase + 16 * n + j] = S[q][n][i];
