@@ -95,6 +95,9 @@ def main():
                     help="also time the head-size-128 workload and the 256-step decode")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--dispatch-sweep", action="store_true",
+                    help="time the recurrent and chunked kernels over T and B*H (bf16) and print "
+                         "one JSON line per shape; used to set the AUTO thresholds")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the operator is independent per (batch, head), "
@@ -104,6 +107,10 @@ def main():
 
     import torch
     from rwkv_linear_attention_amd import synth, wkv7
+
+    if args.dispatch_sweep:
+        dispatch_sweep()
+        return
 
     if args.copy_calibration:
         n = 1 << 30
@@ -180,6 +187,29 @@ def main():
         del dev, o, sf, inp
         result["others"] = other_workloads(args.steps, args.warmup)
     print(json.dumps(result), flush=True)
+
+
+def dispatch_sweep(reps=10):
+    """Recurrent vs chunked launch time (bf16, no state in, final state out)
+    for head sizes 64 and 128, B*H sequences in {1, 8, 64, 512} (as B = 1,
+    H = B*H), T from 16 to 2048.  One JSON line per shape."""
+    import torch
+    from rwkv_linear_attention_amd import synth, wkv7
+    for D in (64, 128):
+        for BH in (1, 8, 64, 512):
+            for T in (1, 2, 4, 8, 16, 32, 48, 64, 96, 128, 256, 512, 1024, 2048):
+                inp = synth.make(2, B=1, T=T, H=BH, K=D, seed=7)
+                dev = {n: synth.to_torch(inp[n], "bf16", "cuda") for n in ("r", "w", "k", "v", "a", "b")}
+                o = torch.empty((1, T, BH, D), dtype=torch.bfloat16, device="cuda")
+                sf = torch.empty((1, BH, D, D), dtype=torch.float32, device="cuda")
+                res = {"D": D, "BH": BH, "T": T}
+                for name, algo in (("recurrent_us", wkv7.ALGO_RECURRENT), ("chunked_us", wkv7.ALGO_CHUNKED)):
+                    ms = _time_launches(lambda i: wkv7.fwd(*(dev[n] for n in ("r", "w", "k", "v", "a", "b")),
+                                                           out=o, final_state=sf, algo=algo), reps, 2)
+                    res[name] = round(ms * 1e3, 2)
+                res["auto"] = "chunked" if wkv7.fwd_path(torch.bfloat16, 1, T, BH, D, D) == wkv7.ALGO_CHUNKED else "recurrent"
+                print(json.dumps(res), flush=True)
+                del dev, o, sf, inp
 
 
 def _time_launches(fn, steps, warmup):

@@ -108,6 +108,8 @@ def test_path_choice(L):
     assert L.wkv7_fwd_path(0, 1, 64, 1, 64, 64, 0) == R          # fp32 is never chunked
     assert L.wkv7_fwd_path(0, 1, 64, 1, 64, 64, 2) == -1
     assert L.wkv7_fwd_path(1, 1, 8, 1, 64, 64, 0) == R           # very short sequences
+    assert L.wkv7_fwd_path(1, 1, 15, 1, 128, 128, 0) == R
+    assert L.wkv7_fwd_path(1, 1, 16, 1, 64, 64, 0) == C          # measured crossover
     assert L.wkv7_fwd_path(1, 1, 8, 1, 64, 64, 2) == C           # forced
     assert L.wkv7_fwd_path(1, 1, 4096, 1, 64, 64, 1) == R        # forced
     assert L.wkv7_fwd_path(1, 1, 4096, 1, 48, 48, 0) == -1
