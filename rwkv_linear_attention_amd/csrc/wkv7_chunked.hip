@@ -26,8 +26,8 @@
 // into a private LDS buffer with asynchronous global->LDS loads one chunk
 // ahead, and hand each chunk's operands to the consumers through a
 // three-slot LDS ring.  Hand-off uses LDS counters (ready[slot] =
-// 2 (chunk + 1) + extreme-decay flag once a slot is filled; done = number of
-// (consumer, chunk) pairs finished), so producers and consumers never meet at
+// 2 (chunk + 1) + extreme-decay flag once a slot is filled; done[i] = chunks
+// consumer i has finished reading), so producers and consumers never meet at
 // a workgroup barrier.  Every wait is bounded.  At D = 64 one workgroup runs
 // two sequences of one consumer and three producers (eight waves); at
 // D = 128 one sequence of four consumers and three producers (seven waves).
@@ -160,10 +160,6 @@ __device__ __forceinline__ void lds_store_relaxed(int *p, int v)
 {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
-__device__ __forceinline__ void lds_add_relaxed(int *p, int v)
-{
-    __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
 // Wait until *p >= target; gives up after kSpinLimit polls so that a broken
 // hand-off ends the kernel (with wrong results) instead of hanging it.
 __device__ __forceinline__ int spin_ge(int *p, int target)
@@ -176,6 +172,19 @@ __device__ __forceinline__ int spin_ge(int *p, int target)
     }
     asm volatile("" ::: "memory");
     return v;
+}
+// Wait until p[0..n) are all >= target (bounded like spin_ge).
+template <int N>
+__device__ __forceinline__ void spin_all_ge(int *p, int target)
+{
+    for (int it = 0; it < kSpinLimit; ++it) {
+        int v = lds_load_relaxed(p);
+#pragma unroll
+        for (int i = 1; i < N; ++i) v = min(v, lds_load_relaxed(p + i));
+        if (v >= target) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    asm volatile("" ::: "memory");
 }
 
 // ---- global -> LDS staging ----------------------------------------------------
@@ -290,10 +299,19 @@ __device__ __forceinline__ void ws_issue_v(uint32_t tile_lds, const uint16_t *v,
 // accumulation.  T = (I - M_ba)^-1 uses the nilpotent doubling product
 // (I + N^8)(I + N^4)(I + N^2)(I + N), every factor kept both as X and X^T
 // (MFMA accumulators of X^T are the A-fragments of X).
-// Returns the wave-uniform extreme-decay flag of the chunk.
+// Everything is formed in registers first (ChunkOps) and written to the slot
+// afterwards, so that a producer only needs its slot back for the short write.
+template <int D> struct ChunkOps {
+    bf16x8 B[D / 32], R[D / 32];        // B~, R~ A-fragments per 32-channel block
+    u32x4 ah[D / 32], kh[D / 32], kl[D / 32];   // row t of the A^, K^ hi, K^ lo tiles
+    f32x4 egl[D / 32][2];               // e^{G_L} of channels 32s + 16hh + 4g .. +3
+    bf16x4 tinv, tnbk, mra, mrkh, mrkl;
+    int flag;                           // wave-uniform extreme-decay flag
+};
+
 template <int D>
-__device__ int ws_precompute(const RawTile<D> &rt, char *slot, int lane, const bf16x8 *psel,
-                             bf16x4 ltri)
+__device__ void ws_precompute(const RawTile<D> &rt, ChunkOps<D> &op, int lane, const bf16x8 *psel,
+                              bf16x4 ltri)
 {
     using C = WS<D>;
     const int t = lane & 15, g = lane >> 4;
@@ -328,7 +346,6 @@ __device__ int ws_precompute(const RawTile<D> &rt, char *slot, int lane, const b
         unpack8(rt.x[s][3], av);
         unpack8(rt.x[s][4], bv);
         float Rt[8], Bt[8], Ah[8], Kh[8];
-        f32x4 eGL4[2];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float G2 = Gq[e >> 2][e & 3] * 1.4426950408889634f;
@@ -336,18 +353,12 @@ __device__ int ws_precompute(const RawTile<D> &rt, char *slot, int lane, const b
             const float enG = __builtin_amdgcn_exp2f(-G2);
             const float eGp = row_shr<1>(eG, 1.0f);
             const float eGL = row_bcast15(eG);
-            eGL4[e >> 2][e & 3] = eGL;
+            op.egl[s][e >> 2][e & 3] = eGL;
             emin = fminf(emin, eGL);
             Rt[e] = rv[e] * eG;
             Bt[e] = bv[e] * eGp;
             Ah[e] = av[e] * enG;
             Kh[e] = kv[e] * enG;
-        }
-        // e^{G_L} of channels 32s + 16hh + 4g .. +3 (one writer per row).
-        if (t == 0) {
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-                *(f32x4 *)(slot + C::OFF_EGL + (32 * s + 16 * hh + 4 * g) * 4) = eGL4[hh];
         }
         const bf16x8 Rh = pack8(Rt), Bh = pack8(Bt), Khh = pack8(Kh), Ahh = pack8(Ah);
         // (R~ K^^T)^T to about 16 bits: hi.hi + hi.lo + lo.hi.
@@ -370,18 +381,11 @@ __device__ int ws_precompute(const RawTile<D> &rt, char *slot, int lane, const b
         mbaT = mfma32(Ahh, Bh, mbaT);   // (B~ A^^T)^T
         mbk = mfma32(Bh, Khh, mbk);     // B~ K^^T
 
-        st16(slot + C::OFF_B + s * 1024 + lane * 16, Bh);
-        st16(slot + C::OFF_R + s * 1024 + lane * 16, Rh);
-        // Row t of the A^, K^ hi and K^ lo tiles, channels 32s + 16hh + 4g .. +3.
-        const u32x4 ab = __builtin_bit_cast(u32x4, Ahh), kb = __builtin_bit_cast(u32x4, Khh),
-                    lb = __builtin_bit_cast(u32x4, Khl);
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const int off = tile_off<D>(t, 32 * s + 16 * hh + 4 * g);
-            *(u32x2 *)(slot + C::OFF_AH + off) = u32x2{ab[2 * hh], ab[2 * hh + 1]};
-            *(u32x2 *)(slot + C::OFF_KH + off) = u32x2{kb[2 * hh], kb[2 * hh + 1]};
-            *(u32x2 *)(slot + C::OFF_KL + off) = u32x2{lb[2 * hh], lb[2 * hh + 1]};
-        }
+        op.B[s] = Bh;
+        op.R[s] = Rh;
+        op.ah[s] = __builtin_bit_cast(u32x4, Ahh);
+        op.kh[s] = __builtin_bit_cast(u32x4, Khh);
+        op.kl[s] = __builtin_bit_cast(u32x4, Khl);
     }
     f32x4 mrkT = mrkT0 + mrkT1;
 
@@ -408,15 +412,43 @@ __device__ int ws_precompute(const RawTile<D> &rt, char *slot, int lane, const b
     const f32x4 t2 = mfma16(n2t, t1b, t1), t2t = mfma16(t1b, n2t, t1t);
     const bf16x4 t2b = cvt4(t2);
     const f32x4 t4 = mfma16(n4t, t2b, t2), t4t = mfma16(t2b, n4t, t2t);
-    const bf16x4 tinv = cvt4(mfma16(cvt4(t4), n8t, t4t));
-    st8(slot + C::OFF_TN + lane * 16, tinv);
-    st8(slot + C::OFF_TN + lane * 16 + 8, cvt4(mfma16(cvt4(mbk), tinv, zero4())));
-    st8(slot + C::OFF_MM + lane * 16, cvt4(mraT));
-    bf16x4 hi, lo;
-    split4(mrkT, hi, lo);
-    st8(slot + C::OFF_MM + lane * 16 + 8, hi);
-    st8(slot + C::OFF_MRKL + lane * 8, lo);
-    return __any((int)(emin < kMinChunkFactor || wmax[0] > 0 || wmax[1] > 0)) ? 1 : 0;
+    op.tinv = cvt4(mfma16(cvt4(t4), n8t, t4t));
+    op.tnbk = cvt4(mfma16(cvt4(mbk), op.tinv, zero4()));
+    op.mra = cvt4(mraT);
+    split4(mrkT, op.mrkh, op.mrkl);
+    op.flag = __any((int)(emin < kMinChunkFactor || wmax[0] > 0 || wmax[1] > 0)) ? 1 : 0;
+}
+
+// Producer: write one chunk's operands into `slot` (layout WS<D>).
+template <int D>
+__device__ __forceinline__ void ws_store_ops(const ChunkOps<D> &op, char *slot, int lane)
+{
+    using C = WS<D>;
+    const int t = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < C::NCB; ++s) {
+        st16(slot + C::OFF_B + s * 1024 + lane * 16, op.B[s]);
+        st16(slot + C::OFF_R + s * 1024 + lane * 16, op.R[s]);
+        // Row t of the A^, K^ hi and K^ lo tiles, channels 32s + 16hh + 4g .. +3.
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int off = tile_off<D>(t, 32 * s + 16 * hh + 4 * g);
+            *(u32x2 *)(slot + C::OFF_AH + off) = u32x2{op.ah[s][2 * hh], op.ah[s][2 * hh + 1]};
+            *(u32x2 *)(slot + C::OFF_KH + off) = u32x2{op.kh[s][2 * hh], op.kh[s][2 * hh + 1]};
+            *(u32x2 *)(slot + C::OFF_KL + off) = u32x2{op.kl[s][2 * hh], op.kl[s][2 * hh + 1]};
+        }
+        // e^{G_L} (one writer per row)
+        if (t == 0) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+                *(f32x4 *)(slot + C::OFF_EGL + (32 * s + 16 * hh + 4 * g) * 4) = op.egl[s][hh];
+        }
+    }
+    st8(slot + C::OFF_TN + lane * 16, op.tinv);
+    st8(slot + C::OFF_TN + lane * 16 + 8, op.tnbk);
+    st8(slot + C::OFF_MM + lane * 16, op.mra);
+    st8(slot + C::OFF_MM + lane * 16 + 8, op.mrkh);
+    st8(slot + C::OFF_MRKL + lane * 8, op.mrkl);
 }
 
 // ---- consumer ----------------------------------------------------------------
@@ -656,8 +688,12 @@ __attribute__((amdgpu_waves_per_eu(WS<D>::WAVES_PER_SIMD, WS<D>::WAVES_PER_SIMD)
     if (bh >= nbh) return;
     const int bb = bh / H, h = bh % H;
     char *const lds = lds_slots + seq * C::NSLOT * C::SLOT;
-    int *ready = lds_sync + 8 * seq;   // ready[NSLOT], then done
+    // Per sequence: ready[NSLOT], then one done counter per consumer (a sum
+    // over consumers would let a consumer running ahead release a slot that
+    // a slower one is still reading).
+    int *ready = lds_sync + 8 * seq;
     int *done = ready + C::NSLOT;
+    static_assert(C::NSLOT + C::NCONS <= 8, "hand-off counters of one sequence");
 
     if (is_cons) {
         // ---------------- consumer: columns cbase .. cbase + CW - 1 ----------------
@@ -686,7 +722,7 @@ __attribute__((amdgpu_waves_per_eu(WS<D>::WAVES_PER_SIMD, WS<D>::WAVES_PER_SIMD)
             else
                 ws_chunk_serial<D>(S, slot, o, T, H, bb, h, c, cbase, lane);
             lds_wait();                          // all reads of the slot have returned
-            if (lane == 0) lds_add_relaxed(done, 1);   // one count per consumer wave
+            lds_store_relaxed(&done[crank / C::NSEQ], c + 1);
         }
         if (sf) {
 #pragma unroll
@@ -739,25 +775,25 @@ __attribute__((amdgpu_waves_per_eu(WS<D>::WAVES_PER_SIMD, WS<D>::WAVES_PER_SIMD)
             rt.valid = tok < T;
             rt.upd = rt.valid && mcur != 0;
             zero_inactive<D>(rt);
+            const bool all_upd = __all(rt.upd);
+            ChunkOps<D> op;
+            ws_precompute<D>(rt, op, lane, psel, ltri);
             char *slot = lds + (c % C::NSLOT) * C::SLOT;
             // the slot's previous chunk is consumed by every consumer
-            spin_ge(done, C::NCONS * (c - C::NSLOT + 1));
+            spin_all_ge<C::NCONS>(done, c - C::NSLOT + 1);
             ws_issue_v<D>(lds_addr(slot + C::OFF_V), v, seq_base, tok_stride, T, c, lane);
-            if (!__all(rt.upd)) {
+            ws_store_ops<D>(op, slot, lane);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the value tile has landed
+            if (!all_upd && !rt.upd) {
                 // Value rows of tokens that do not update are cleared, so that
                 // whatever they hold (even inf or nan) cannot reach the state.
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                if (!rt.upd) {
-                    const u32x4 zero = {0u, 0u, 0u, 0u};
+                const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-                    for (int cc = 0; cc < D / 32; ++cc)
-                        *(u32x4 *)(slot + C::OFF_V + tile_off<D>(t, (D / 4) * g + 8 * cc)) = zero;
-                }
+                for (int cc = 0; cc < D / 32; ++cc)
+                    *(u32x4 *)(slot + C::OFF_V + tile_off<D>(t, (D / 4) * g + 8 * cc)) = zero;
             }
-            const int flag = ws_precompute<D>(rt, slot, lane, psel, ltri);
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the value tile has landed
             lds_wait();
-            lds_store_relaxed(&ready[c % C::NSLOT], 2 * (c + 1) + flag);
+            lds_store_relaxed(&ready[c % C::NSLOT], 2 * (c + 1) + op.flag);
         }
     }
 }
