@@ -92,7 +92,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--all", action="store_true",
-                    help="also time the head-size-128 workload and the 256-step decode")
+                    help="also time the head-size-128 workload, a packed variable-length batch and the "
+                         "256-step decode")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (reference for HBM byte counters)")
     ap.add_argument("--dispatch-sweep", action="store_true",
@@ -212,6 +213,48 @@ def dispatch_sweep(reps=10):
                 del dev, o, sf, inp
 
 
+def varlen_lengths(total, n, seed):
+    """Seeded mix of n sequence lengths in [16, 4096) summing to total."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    x = rng.lognormal(mean=0.0, sigma=0.8, size=n)
+    lens = np.maximum(16, np.floor(x / x.sum() * total)).astype(np.int64)
+    lens = np.minimum(lens, 4095)
+    lens[np.argmax(lens)] += total - int(lens.sum())
+    return lens
+
+
+def varlen_workload(steps, warmup):
+    """Packed variable-length forward: the 32768 tokens x 64 heads (d64) of
+    the B8 T4096 workload as 32 sequences of mixed lengths, each starting from
+    one of 8 pooled initial states (state_map), final states written."""
+    import numpy as np
+    import torch
+    from rwkv_linear_attention_amd import synth, wkv7
+    H, D, N, TT = 64, 64, 32, 8 * 4096
+    lens = varlen_lengths(TT, N, seed=1207)
+    print(f"[bench] generating packed workload (N={N}, lengths {int(lens.min())}..{int(lens.max())})",
+          file=sys.stderr, flush=True)
+    inp = synth.make(2, B=1, T=TT, H=H, K=D, seed=1207)
+    dev = {n: synth.to_torch(inp[n][0], "bf16", "cuda") for n in ("r", "w", "k", "v", "a", "b")}
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).cuda()
+    rng = np.random.default_rng(1208)
+    pool = torch.from_numpy((rng.standard_normal((8, H, D, D)) * 0.1).astype(np.float32)).cuda()
+    smap = torch.from_numpy(rng.integers(0, 8, size=N).astype(np.int32)).cuda()
+    o = torch.empty((TT, H, D), dtype=torch.bfloat16, device="cuda")
+    sf = torch.empty((N, H, D, D), dtype=torch.float32, device="cuda")
+    ms = _time_launches(lambda i: wkv7.fwd_varlen(*(dev[n] for n in ("r", "w", "k", "v", "a", "b")), cu,
+                                                  initial_state=pool, state_map=smap, out=o, final_state=sf),
+                        steps, warmup)
+    # inputs and o once, one mapped initial state read and one final state written per sequence
+    nbytes = 7 * TT * H * D * 2 + 2 * N * H * D * D * 4
+    name = f"fwd_varlen_bf16_N{N}_T{TT}_H{H}_d{D}_statemap8"
+    return {name: {"ms": round(ms, 5), "Mtokens_per_s": round(TT / ms / 1e3, 3),
+                   "GB_per_s": round(nbytes / ms / 1e6, 1),
+                   "frac_of_8TBps": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes,
+                   "lengths": [int(x) for x in lens], "kernel": "chunked d64 (packed)"}}
+
+
 def _time_launches(fn, steps, warmup):
     import torch
     for _ in range(warmup):
@@ -251,6 +294,8 @@ def other_workloads(steps, warmup):
                        "algorithmic_bytes": nbytes, "kernel": "chunked d128"}
     del dev, s0, mask, o, sf, inp
     torch.cuda.empty_cache()
+
+    out.update(varlen_workload(steps, warmup))
 
     wl = synth.WORKLOADS[4]
     B, NSTEP, H, D = wl["B"], wl["T"], wl["H"], wl["K"]

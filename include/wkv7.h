@@ -89,6 +89,53 @@ wkv7_status_t wkv7_fwd(int dtype, int B, int T, int H, int K, int V,
                        void *o, float *final_state, int algo, void *stream);
 
 /*
+ * wkv7_fwd_varlen -- forward over N variable-length sequences packed back to
+ * back along one token axis, each starting from an entry of a pool of
+ * initial states.  Packed variable-length input follows the rwkv-fla page
+ * (its news note on kernels with variable-length inputs); the state index
+ * per sample follows the state_map argument of the rwkv-ops README
+ * operator interface (an index per sample into an [n_state, H, K, V]
+ * initial state; n_state = 1 shares one state).  Sequence n computes
+ * exactly what wkv7_fwd computes for one sequence of length
+ * cu_seqlens[n+1] - cu_seqlens[n].
+ *
+ *   dtype          as for wkv7_fwd.
+ *   N              number of sequences, >= 1.
+ *   total_T        length of the packed token axis, >= 0.
+ *   H, K, V        as for wkv7_fwd.
+ *   cu_seqlens     DEVICE int32 [N+1], 4-byte aligned: sequence n owns tokens
+ *                  [cu_seqlens[n], cu_seqlens[n+1]).  Expected nondecreasing
+ *                  from 0 to total_T; the kernels clamp every offset into
+ *                  [0, total_T] and treat a decreasing pair as an empty
+ *                  sequence, so malformed offsets give wrong results but
+ *                  never an out-of-bounds access.  Read only.
+ *   r,w,k,a,b      [total_T,H,K] dtype.  Read only.
+ *   v              [total_T,H,V] dtype.  Read only.
+ *   initial_state  [n_state,H,K,V] fp32 pool, or NULL for zero states.
+ *   n_state        rows of the pool (>= 1 when initial_state is given).
+ *   state_map      DEVICE int32 [N], 4-byte aligned, or NULL.  Sequence n
+ *                  starts from pool row state_map[n]; an entry outside
+ *                  [0, n_state) means a zero state.  NULL means row n, which
+ *                  requires n_state == N when initial_state is given.
+ *   mask           [total_T] uint8 (nonzero = update), or NULL.
+ *   o              [total_T,H,V] dtype.  Written at every token of every
+ *                  sequence (tokens outside all sequences are not written).
+ *   final_state    [N,H,K,V] fp32, or NULL.  Written.  May alias
+ *                  initial_state only when state_map is NULL.
+ *   algo           as for wkv7_fwd; under AUTO (bf16) the chunked kernel is
+ *                  chosen when the mean sequence length total_T / N is at
+ *                  least 16.
+ *   stream         hipStream_t to enqueue on.
+ */
+wkv7_status_t wkv7_fwd_varlen(int dtype, int N, int total_T, int H, int K, int V,
+                              const int32_t *cu_seqlens,
+                              const void *r, const void *w, const void *k,
+                              const void *v, const void *a, const void *b,
+                              const float *initial_state, int n_state,
+                              const int32_t *state_map, const uint8_t *mask,
+                              void *o, float *final_state, int algo, void *stream);
+
+/*
  * wkv7_step -- one decode token per sequence, state updated in place
  * (section "rwkv7_op_rnn 使用方法": the T = 1 case of the forward).
  *
@@ -113,7 +160,7 @@ const char *wkv7_strerror(int status);
  * would be rejected.  Host only; launches nothing. */
 int wkv7_fwd_path(int dtype, int B, int T, int H, int K, int V, int algo);
 
-/* ABI version of this header (major * 100 + minor). */
+/* ABI version of this header (major * 100 + minor): 101 adds wkv7_fwd_varlen. */
 int wkv7_version(void);
 
 #ifdef __cplusplus

@@ -460,16 +460,16 @@ __device__ __forceinline__ void ws_store_ops(const ChunkOps<D> &op, char *slot, 
 template <int D>
 __device__ void ws_chunk_exact(f32x4 (*S)[WS<D>::NT], const uint16_t *r, const uint16_t *w,
                                const uint16_t *k, const uint16_t *v, const uint16_t *a,
-                               const uint16_t *b, const uint8_t *mask, uint16_t *o, int T, int H,
-                               int bb, int h, int chunk, int cbase, int lane)
+                               const uint16_t *b, const uint8_t *mask, uint16_t *o, size_t tok0, int Tn,
+                               int H, int h, int chunk, int cbase, int lane)
 {
     constexpr int NQ = D / 16, NT = WS<D>::NT;
     const int g = lane >> 4, j = lane & 15;
     for (int tt = 0; tt < 16; ++tt) {
         const int tok = chunk * 16 + tt;
-        if (tok >= T) break;
-        const bool upd = mask == nullptr || mask[(size_t)bb * T + tok] != 0;
-        const size_t base = (((size_t)bb * T + tok) * H + h) * D;
+        if (tok >= Tn) break;
+        const bool upd = mask == nullptr || mask[tok0 + tok] != 0;
+        const size_t base = ((tok0 + tok) * H + h) * D;
         if (upd) {
             float sb[NT] = {};
 #pragma unroll
@@ -528,13 +528,13 @@ __device__ void ws_chunk_exact(f32x4 (*S)[WS<D>::NT], const uint16_t *r, const u
 // Store one chunk's output tile held as O^T fragments (lane (g, t): token t,
 // columns cbase + 16n + 4g .. +3).
 template <int D>
-__device__ __forceinline__ void ws_store_out(const f32x4 *Ot, uint16_t *o, int T, int H, int bb, int h,
-                                             int chunk, int cbase, int lane)
+__device__ __forceinline__ void ws_store_out(const f32x4 *Ot, uint16_t *o, size_t tok0, int Tn, int H,
+                                             int h, int chunk, int cbase, int lane)
 {
     const int g = lane >> 4, t = lane & 15;
     const int tok = chunk * 16 + t;
-    if (tok < T) {
-        uint16_t *op = o + (((size_t)bb * T + tok) * H + h) * D + cbase + 4 * g;
+    if (tok < Tn) {
+        uint16_t *op = o + ((tok0 + tok) * H + h) * D + cbase + 4 * g;
 #pragma unroll
         for (int n = 0; n < WS<D>::NT; ++n)
             *(u32x2 *)(op + 16 * n) = u32x2{cvt2_bits(Ot[n][0], Ot[n][1]), cvt2_bits(Ot[n][2], Ot[n][3])};
@@ -546,8 +546,9 @@ __device__ __forceinline__ void ws_store_out(const f32x4 *Ot, uint16_t *o, int T
 // the S-independent products are placed where they fill the latency of the
 // S -> X -> U -> S' chain.
 template <int D>
-__device__ __forceinline__ void ws_chunk_serial(f32x4 (*S)[WS<D>::NT], const char *slot, uint16_t *o, int T,
-                                                int H, int bb, int h, int chunk, int cbase, int lane)
+__device__ __forceinline__ void ws_chunk_serial(f32x4 (*S)[WS<D>::NT], const char *slot, uint16_t *o,
+                                                size_t tok0, int Tn, int H, int h, int chunk, int cbase,
+                                                int lane)
 {
     using C = WS<D>;
     constexpr int NT = C::NT;
@@ -617,7 +618,7 @@ __device__ __forceinline__ void ws_chunk_serial(f32x4 (*S)[WS<D>::NT], const cha
     const bf16x8 mm = ld16(slot + C::OFF_MM + lane * 16);
 #pragma unroll
     for (int n = 0; n < NT; ++n) Ot[n] = mfma32(uv[n], mm, Ot[n]);
-    ws_store_out<D>(Ot, o, T, H, bb, h, chunk, cbase, lane);
+    ws_store_out<D>(Ot, o, tok0, Tn, H, h, chunk, cbase, lane);
 }
 
 // ---- kernel --------------------------------------------------------------------
@@ -625,7 +626,8 @@ __device__ __forceinline__ void ws_chunk_serial(f32x4 (*S)[WS<D>::NT], const cha
 template <int D>
 __global__ __launch_bounds__(64 * WS<D>::NWAVE)
 __attribute__((amdgpu_waves_per_eu(WS<D>::WAVES_PER_SIMD, WS<D>::WAVES_PER_SIMD))) void chunked_ws_kernel(
-    int T, int H, int nbh, const uint16_t *__restrict__ r, const uint16_t *__restrict__ w,
+    int T, int H, int nbh, const int32_t *__restrict__ cu_seqlens, const int32_t *__restrict__ state_map,
+    int n_state, const uint16_t *__restrict__ r, const uint16_t *__restrict__ w,
     const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, const uint16_t *__restrict__ a,
     const uint16_t *__restrict__ b, const float *__restrict__ s0, const uint8_t *__restrict__ mask,
     uint16_t *__restrict__ o, float *__restrict__ sf)
@@ -639,7 +641,6 @@ __attribute__((amdgpu_waves_per_eu(WS<D>::WAVES_PER_SIMD, WS<D>::WAVES_PER_SIMD)
     __shared__ int lds_sync[32];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int g = lane >> 4, j = lane & 15;
-    const int nchunks = (T + 15) / 16;
     constexpr int NC = C::NSEQ * C::NCONS;   // consumers per workgroup
 
     // Role assignment by SIMD placement.  The consumers (mostly MFMA work,
@@ -686,7 +687,26 @@ __attribute__((amdgpu_waves_per_eu(WS<D>::WAVES_PER_SIMD, WS<D>::WAVES_PER_SIMD)
     const int seq = is_cons ? crank % C::NSEQ : prank % C::NSEQ;
     const int bh = blockIdx.x * C::NSEQ + seq;
     if (bh >= nbh) return;
-    const int bb = bh / H, h = bh % H;
+    // Sequence sq = bh / H: tokens [tok0, tok0 + Tn) of the (packed) token
+    // axis, initial state row sidx of the state pool (-1: zeros).  Offsets
+    // and state indices read from device memory are clamped into range.
+    const int sq = bh / H, h = bh % H;
+    size_t tok0;
+    int Tn, sidx = sq;
+    if (cu_seqlens) {
+        const int t_beg = min(max(cu_seqlens[sq], 0), T);
+        const int t_end = min(max(cu_seqlens[sq + 1], t_beg), T);
+        tok0 = (size_t)t_beg;
+        Tn = t_end - t_beg;
+    } else {
+        tok0 = (size_t)sq * T;
+        Tn = T;
+    }
+    if (state_map) {
+        sidx = state_map[sq];
+        if (sidx < 0 || sidx >= n_state) sidx = -1;
+    }
+    const int nchunks = (Tn + 15) / 16;
     char *const lds = lds_slots + seq * C::NSLOT * C::SLOT;
     // Per sequence: ready[NSLOT], then one done counter per consumer (a sum
     // over consumers would let a consumer running ahead release a slot that
@@ -699,28 +719,29 @@ __attribute__((amdgpu_waves_per_eu(WS<D>::WAVES_PER_SIMD, WS<D>::WAVES_PER_SIMD)
         // ---------------- consumer: columns cbase .. cbase + CW - 1 ----------------
         const int cbase = C::CW * (crank / C::NSEQ);
         f32x4 S[C::NQ][C::NT];
-        const size_t st_base = (size_t)bh * D * D;
+        const size_t st_base = (size_t)bh * D * D;                     // final state [N, H, D, D]
+        const size_t st_in = ((size_t)(sidx < 0 ? 0 : sidx) * H + h) * D * D;   // initial state pool
 #pragma unroll
         for (int q = 0; q < C::NQ; ++q)
 #pragma unroll
             for (int n = 0; n < C::NT; ++n) S[q][n] = zero4();
-        if (s0) {
+        if (s0 && sidx >= 0) {
 #pragma unroll
             for (int q = 0; q < C::NQ; ++q)
 #pragma unroll
                 for (int n = 0; n < C::NT; ++n)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        S[q][n][i] = s0[st_base + (size_t)(16 * q + 4 * g + i) * D + cbase + 16 * n + j];
+                        S[q][n][i] = s0[st_in + (size_t)(16 * q + 4 * g + i) * D + cbase + 16 * n + j];
         }
         for (int c = 0; c < nchunks; ++c) {
             const char *slot = lds + (c % C::NSLOT) * C::SLOT;
             // ready[slot] = 2 (c + 1) + extreme-decay flag once chunk c is in the slot
             const int rv = spin_ge(&ready[c % C::NSLOT], 2 * (c + 1));
             if (rv & 1)
-                ws_chunk_exact<D>(S, r, w, k, v, a, b, mask, o, T, H, bb, h, c, cbase, lane);
+                ws_chunk_exact<D>(S, r, w, k, v, a, b, mask, o, tok0, Tn, H, h, c, cbase, lane);
             else
-                ws_chunk_serial<D>(S, slot, o, T, H, bb, h, c, cbase, lane);
+                ws_chunk_serial<D>(S, slot, o, tok0, Tn, H, h, c, cbase, lane);
             lds_wait();                          // all reads of the slot have returned
             lds_store_relaxed(&done[crank / C::NSEQ], c + 1);
         }
@@ -739,7 +760,7 @@ __attribute__((amdgpu_waves_per_eu(WS<D>::WAVES_PER_SIMD, WS<D>::WAVES_PER_SIMD)
         char *raw = lds_raw + (seq * C::NPROD + p) * C::RAW;
         const uint32_t raw_lds = lds_addr(raw);
         // Element offset of (bb, token 0, h, channel 0) and between tokens.
-        const size_t seq_base = ((size_t)bb * T * H + h) * D;
+        const size_t seq_base = (tok0 * H + h) * D;
         const uint32_t tok_stride = (uint32_t)H * D;
         const uint16_t *src[5] = {r, w, k, a, b};
         bf16x8 psel[2];
@@ -757,8 +778,8 @@ __attribute__((amdgpu_waves_per_eu(WS<D>::WAVES_PER_SIMD, WS<D>::WAVES_PER_SIMD)
         uint32_t mnext = 1;
         const int t = lane & 15;
         if (p < nchunks) {
-            ws_issue_raw<D>(raw_lds, src, seq_base, tok_stride, T, p, lane);
-            if (mask) mnext = mask[(size_t)bb * T + min(p * 16 + t, T - 1)];
+            ws_issue_raw<D>(raw_lds, src, seq_base, tok_stride, Tn, p, lane);
+            if (mask) mnext = mask[tok0 + min(p * 16 + t, Tn - 1)];
         }
         for (int c = p; c < nchunks; c += C::NPROD) {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -768,11 +789,11 @@ __attribute__((amdgpu_waves_per_eu(WS<D>::WAVES_PER_SIMD, WS<D>::WAVES_PER_SIMD)
             lds_wait();
             if (c + C::NPROD < nchunks) {
                 const int cn = c + C::NPROD;
-                ws_issue_raw<D>(raw_lds, src, seq_base, tok_stride, T, cn, lane);
-                if (mask) mnext = mask[(size_t)bb * T + min(cn * 16 + t, T - 1)];
+                ws_issue_raw<D>(raw_lds, src, seq_base, tok_stride, Tn, cn, lane);
+                if (mask) mnext = mask[tok0 + min(cn * 16 + t, Tn - 1)];
             }
             const int tok = c * 16 + t;
-            rt.valid = tok < T;
+            rt.valid = tok < Tn;
             rt.upd = rt.valid && mcur != 0;
             zero_inactive<D>(rt);
             const bool all_upd = __all(rt.upd);
@@ -781,7 +802,7 @@ __attribute__((amdgpu_waves_per_eu(WS<D>::WAVES_PER_SIMD, WS<D>::WAVES_PER_SIMD)
             char *slot = lds + (c % C::NSLOT) * C::SLOT;
             // the slot's previous chunk is consumed by every consumer
             spin_all_ge<C::NCONS>(done, c - C::NSLOT + 1);
-            ws_issue_v<D>(lds_addr(slot + C::OFF_V), v, seq_base, tok_stride, T, c, lane);
+            ws_issue_v<D>(lds_addr(slot + C::OFF_V), v, seq_base, tok_stride, Tn, c, lane);
             ws_store_ops<D>(op, slot, lane);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the value tile has landed
             if (!all_upd && !rt.upd) {
@@ -804,7 +825,8 @@ static hipError_t launch_ws(const FwdArgs &p, hipStream_t stream)
     using C = WS<D>;
     const int nbh = p.B * p.H;
     const dim3 grid((unsigned)((nbh + C::NSEQ - 1) / C::NSEQ)), block(64 * C::NWAVE);
-    hipLaunchKernelGGL((chunked_ws_kernel<D>), grid, block, 0, stream, p.T, p.H, nbh,
+    hipLaunchKernelGGL((chunked_ws_kernel<D>), grid, block, 0, stream, p.T, p.H, nbh, p.cu_seqlens,
+                       p.state_map, p.n_state,
                        (const uint16_t *)p.r, (const uint16_t *)p.w, (const uint16_t *)p.k,
                        (const uint16_t *)p.v, (const uint16_t *)p.a, (const uint16_t *)p.b, p.s0,
                        p.mask, (uint16_t *)p.o, p.sf);

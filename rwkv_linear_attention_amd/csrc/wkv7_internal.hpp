@@ -6,13 +6,21 @@
 
 namespace wkv7 {
 
+// Fixed-length form: B sequences of T tokens, [B,T,H,D] arrays,
+// cu_seqlens == state_map == nullptr, n_state == B.  Packed form: B
+// sequences with token ranges [cu_seqlens[n], cu_seqlens[n+1]) of a
+// [T,H,D] token axis (T = total tokens), initial state row state_map[n]
+// of an [n_state,H,D,D] pool (state_map == nullptr: row n).
 struct FwdArgs {
     int B, T, H, D;                      // D = K = V
-    const void *r, *w, *k, *v, *a, *b;   // [B,T,H,D], I/O dtype
-    const float *s0;                     // [B,H,D,D] or nullptr
-    const uint8_t *mask;                 // [B,T] or nullptr
-    void *o;                             // [B,T,H,D], I/O dtype
+    const void *r, *w, *k, *v, *a, *b;   // I/O dtype
+    const float *s0;                     // state pool [n_state,H,D,D] or nullptr
+    const uint8_t *mask;                 // one byte per token or nullptr
+    void *o;                             // I/O dtype
     float *sf;                           // [B,H,D,D] or nullptr
+    const int32_t *cu_seqlens = nullptr; // device, [B+1]
+    const int32_t *state_map = nullptr;  // device, [B]
+    int n_state = 0;
 };
 
 struct StepArgs {

@@ -5,6 +5,9 @@
 //   sb = b_t^T S ;  S = diag(exp(w_t)) S + a_t sb^T + k_t v_t^T
 // and for every token  o_t = S^T r_t.
 //
+// Sequences come either as [B,T,H,D] arrays or packed ([T_total,H,D] with
+// cu_seqlens offsets and a state_map into a pool of initial states).
+//
 // One workgroup per (b, h) with D/16 waves; wave w owns state columns
 // [16w, 16w+16).  Lane (j = l%16, g = l/16) keeps rows [g*D/4, (g+1)*D/4) of
 // column 16w + j in VGPRs, so b^T S and S^T r are in-lane FMA chains over D/4
@@ -19,7 +22,8 @@ namespace wkv7 {
 
 template <int D, typename T_IO>
 __global__ __launch_bounds__(D * 4) void recurrent_kernel(
-    int T, int H, const T_IO *__restrict__ r, const T_IO *__restrict__ w,
+    int T, int H, const int32_t *__restrict__ cu_seqlens, const int32_t *__restrict__ state_map,
+    int n_state, const T_IO *__restrict__ r, const T_IO *__restrict__ w,
     const T_IO *__restrict__ k, const T_IO *__restrict__ v, const T_IO *__restrict__ a,
     const T_IO *__restrict__ b, const float *__restrict__ s0, const uint8_t *__restrict__ mask,
     T_IO *__restrict__ o, float *__restrict__ sf)
@@ -31,7 +35,25 @@ __global__ __launch_bounds__(D * 4) void recurrent_kernel(
     __shared__ int s_upd[TB];
 
     const int bh = blockIdx.x;
-    const int bb = bh / H, h = bh % H;
+    // Sequence sq: tokens [tok0, tok0 + Tn) of the token axis (packed form:
+    // from cu_seqlens, clamped into range), initial state row sidx of the
+    // state pool (-1: zeros).
+    const int sq = bh / H, h = bh % H;
+    size_t tok0;
+    int Tn, sidx = sq;
+    if (cu_seqlens) {
+        const int t_beg = min(max(cu_seqlens[sq], 0), T);
+        const int t_end = min(max(cu_seqlens[sq + 1], t_beg), T);
+        tok0 = (size_t)t_beg;
+        Tn = t_end - t_beg;
+    } else {
+        tok0 = (size_t)sq * T;
+        Tn = T;
+    }
+    if (state_map) {
+        sidx = state_map[sq];
+        if (sidx < 0 || sidx >= n_state) sidx = -1;
+    }
     const int tid = threadIdx.x;
     const int wave = tid / kWave, lane = tid % kWave;
     const int col = wave * 16 + (lane & 15);
@@ -40,17 +62,22 @@ __global__ __launch_bounds__(D * 4) void recurrent_kernel(
 
     float S[RPL];
     const size_t st_base = (size_t)bh * D * D;
+    const size_t st_in = ((size_t)(sidx < 0 ? 0 : sidx) * H + h) * D * D;
 #pragma unroll
-    for (int i = 0; i < RPL; ++i) S[i] = s0 ? s0[st_base + (size_t)(row0 + i) * D + col] : 0.0f;
+    for (int i = 0; i < RPL; ++i) S[i] = 0.0f;
+    if (s0 && sidx >= 0) {
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) S[i] = s0[st_in + (size_t)(row0 + i) * D + col];
+    }
 
-    for (int t0 = 0; t0 < T; t0 += TB) {
-        const int nt = min(TB, T - t0);
+    for (int t0 = 0; t0 < Tn; t0 += TB) {
+        const int nt = min(TB, Tn - t0);
         __syncthreads();
         for (int idx = tid; idx < TB * D; idx += NT) {
             const int tl = idx / D, c = idx % D;
             float ew = 1.f, av = 0.f, bv = 0.f, kv = 0.f, rv = 0.f, vv = 0.f;
             if (tl < nt) {
-                const size_t gi = (((size_t)bb * T + t0 + tl) * H + h) * D + c;
+                const size_t gi = ((tok0 + t0 + tl) * H + h) * D + c;
                 ew = __expf(io<T_IO>::load(w, gi));
                 av = io<T_IO>::load(a, gi);
                 bv = io<T_IO>::load(b, gi);
@@ -61,7 +88,7 @@ __global__ __launch_bounds__(D * 4) void recurrent_kernel(
             s_ew[tl][c] = ew; s_a[tl][c] = av; s_b[tl][c] = bv;
             s_k[tl][c] = kv; s_r[tl][c] = rv; s_v[tl][c] = vv;
         }
-        if (tid < TB) s_upd[tid] = (tid < nt) && (mask ? mask[(size_t)bb * T + t0 + tid] != 0 : 1);
+        if (tid < TB) s_upd[tid] = (tid < nt) && (mask ? mask[tok0 + t0 + tid] != 0 : 1);
         __syncthreads();
 
         for (int tl = 0; tl < nt; ++tl) {
@@ -93,7 +120,7 @@ __global__ __launch_bounds__(D * 4) void recurrent_kernel(
             float ov = (q0 + q1) + (q2 + q3);
             ov = xor_sum(ov, 16);
             ov = xor_sum(ov, 32);
-            if (g == 0) io<T_IO>::store(o, (((size_t)bb * T + t0 + tl) * H + h) * D + col, ov);
+            if (g == 0) io<T_IO>::store(o, ((tok0 + t0 + tl) * H + h) * D + col, ov);
         }
     }
     if (sf) {
@@ -106,7 +133,8 @@ template <int D, typename T_IO>
 static hipError_t launch_rec(const FwdArgs &p, hipStream_t stream)
 {
     const dim3 grid((unsigned)(p.B * p.H)), block(D * 4);
-    hipLaunchKernelGGL((recurrent_kernel<D, T_IO>), grid, block, 0, stream, p.T, p.H,
+    hipLaunchKernelGGL((recurrent_kernel<D, T_IO>), grid, block, 0, stream, p.T, p.H, p.cu_seqlens,
+                       p.state_map, p.n_state,
                        (const T_IO *)p.r, (const T_IO *)p.w, (const T_IO *)p.k, (const T_IO *)p.v,
                        (const T_IO *)p.a, (const T_IO *)p.b, p.s0, p.mask, (T_IO *)p.o, p.sf);
     return hipGetLastError();

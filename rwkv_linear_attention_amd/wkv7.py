@@ -32,6 +32,8 @@ def lib():
     p, i = ctypes.c_void_p, ctypes.c_int
     L.wkv7_fwd.argtypes = [i, i, i, i, i, i] + [p] * 10 + [i, p]
     L.wkv7_fwd.restype = i
+    L.wkv7_fwd_varlen.argtypes = [i, i, i, i, i, i, p] + [p] * 7 + [i, p, p, p, p, i, p]
+    L.wkv7_fwd_varlen.restype = i
     L.wkv7_step.argtypes = [i, i, i, i, i] + [p] * 8 + [p]
     L.wkv7_step.restype = i
     L.wkv7_strerror.argtypes = [i]
@@ -96,14 +98,8 @@ def fwd(r, w, k, v, a, b, initial_state=None, mask=None, output_final_state=True
     _check(v, "v", (B, T, H, V), dt, dev)
     if initial_state is not None:
         _check(initial_state, "initial_state", (B, H, K, V), torch.float32, dev)
-    m = None
-    if mask is not None:
-        if mask.dtype == torch.bool:
-            m = mask.view(torch.uint8)
-        elif mask.dtype == torch.uint8:
-            m = mask
-        else:
-            raise ValueError("mask must be bool or uint8")
+    m = _mask_u8(mask)
+    if m is not None:
         _check(m, "mask", (B, T), torch.uint8, dev)
     o = out if out is not None else torch.empty((B, T, H, V), dtype=dt, device=dev)
     _check(o, "out", (B, T, H, V), dt, dev)
@@ -116,6 +112,67 @@ def fwd(r, w, k, v, a, b, initial_state=None, mask=None, output_final_state=True
     if st != OK:
         raise WKV7Error(st)
     return o, sf
+
+
+def _mask_u8(mask):
+    if mask is None:
+        return None
+    if mask.dtype == torch.bool:
+        return mask.view(torch.uint8)
+    if mask.dtype == torch.uint8:
+        return mask
+    raise ValueError("mask must be bool or uint8")
+
+
+def fwd_varlen(r, w, k, v, a, b, cu_seqlens, initial_state=None, state_map=None, mask=None,
+               output_final_state=True, algo=ALGO_AUTO, out=None, final_state=None):
+    """WKV7 forward over packed variable-length sequences.  r, w, k, a, b:
+    [T_total,H,K] (or [1,T_total,H,K]); v: [T_total,H,V]; cu_seqlens: int32
+    [N+1] token offsets (device); initial_state: [n_state,H,K,V] float32 pool
+    or None; state_map: int32 [N] pool row per sequence (out of range: zero
+    state) or None (row n); mask: [T_total] bool/uint8 or None.  Returns
+    (o shaped like v, final_state [N,H,K,V] float32 or None)."""
+    dev = r.device
+    lead1 = r.dim() == 4
+    if lead1:
+        if r.shape[0] != 1:
+            raise ValueError("packed inputs take a leading dimension of 1, or none")
+        r, w, k, v, a, b = (t.squeeze(0) for t in (r, w, k, v, a, b))
+    TT, H, K = r.shape
+    V = v.shape[-1]
+    dt = r.dtype
+    code = _dtype_code(dt)
+    for name, t in (("r", r), ("w", w), ("k", k), ("a", a), ("b", b)):
+        _check(t, name, (TT, H, K), dt, dev)
+    _check(v, "v", (TT, H, V), dt, dev)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be [N+1] with N >= 1")
+    N = cu_seqlens.numel() - 1
+    _check(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    n_state = 0
+    if initial_state is not None:
+        n_state = initial_state.shape[0]
+        _check(initial_state, "initial_state", (n_state, H, K, V), torch.float32, dev)
+    if state_map is not None:
+        _check(state_map, "state_map", (N,), torch.int32, dev)
+    m = _mask_u8(mask)
+    if m is not None:
+        _check(m, "mask", (TT,), torch.uint8, dev)
+    if out is not None:
+        o = out.squeeze(0) if (lead1 and out.dim() == 4) else out
+    else:
+        o = torch.empty((TT, H, V), dtype=dt, device=dev)
+    _check(o, "out", (TT, H, V), dt, dev)
+    sf = None
+    if output_final_state:
+        sf = final_state if final_state is not None else torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
+        _check(sf, "final_state", (N, H, K, V), torch.float32, dev)
+    st = lib().wkv7_fwd_varlen(code, N, TT, H, K, V, _ptr(cu_seqlens), _ptr(r), _ptr(w), _ptr(k), _ptr(v),
+                               _ptr(a), _ptr(b), _ptr(initial_state), n_state, _ptr(state_map), _ptr(m),
+                               _ptr(o), _ptr(sf), int(algo), _stream(dev))
+    if st != OK:
+        raise WKV7Error(st)
+    return (o.unsqueeze(0) if lead1 else o), sf
 
 
 def step(r, w, k, v, a, b, state, out=None):

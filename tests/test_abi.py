@@ -27,13 +27,14 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert {"wkv7_fwd", "wkv7_step", "wkv7_strerror", "wkv7_fwd_path", "wkv7_version"} <= set(names)
+    assert {"wkv7_fwd", "wkv7_fwd_varlen", "wkv7_step", "wkv7_strerror", "wkv7_fwd_path",
+            "wkv7_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"{n} declared in wkv7.h but not exported"
 
 
 def test_version_and_strerror(L):
-    assert L.wkv7_version() == 100
+    assert L.wkv7_version() == 101
     for code in range(4):
         assert len(L.wkv7_strerror(code)) > 0
     assert L.wkv7_strerror(99) == b"unknown status"
@@ -113,3 +114,36 @@ def test_path_choice(L):
     assert L.wkv7_fwd_path(1, 1, 8, 1, 64, 64, 2) == C           # forced
     assert L.wkv7_fwd_path(1, 1, 4096, 1, 64, 64, 1) == R        # forced
     assert L.wkv7_fwd_path(1, 1, 4096, 1, 48, 48, 0) == -1
+
+
+def varlen(L, dtype=1, N=2, TT=40, H=1, K=64, V=64, cu=GOOD, ptrs=None, s0=None, n_state=0, smap=None,
+           mask=None, sf=None, algo=0):
+    ptrs = ptrs or [GOOD] * 7
+    r, w, k, v, a, b, o = ptrs
+    return L.wkv7_fwd_varlen(dtype, N, TT, H, K, V, cu, r, w, k, v, a, b, s0, n_state, smap, mask, o, sf,
+                             algo, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=0), wkv7.ERR_INVALID_ARG),
+    (dict(TT=-1), wkv7.ERR_INVALID_ARG),
+    (dict(cu=None), wkv7.ERR_INVALID_ARG),
+    (dict(cu=P(0x100002)), wkv7.ERR_INVALID_ARG),                  # cu_seqlens not 4-byte aligned
+    (dict(smap=P(0x100001)), wkv7.ERR_INVALID_ARG),                # state_map not 4-byte aligned
+    (dict(s0=GOOD, n_state=0), wkv7.ERR_INVALID_ARG),              # pool without rows
+    (dict(s0=GOOD, n_state=3), wkv7.ERR_INVALID_ARG),              # no map: pool must have N rows
+    (dict(s0=GOOD, n_state=1, smap=GOOD, sf=GOOD), wkv7.ERR_INVALID_ARG),   # mapped pool aliased by output
+    (dict(s0=ODD, n_state=2), wkv7.ERR_INVALID_ARG),
+    (dict(ptrs=[GOOD] * 6 + [None]), wkv7.ERR_INVALID_ARG),
+    (dict(K=64, V=128), wkv7.ERR_UNSUPPORTED),
+    (dict(dtype=0, algo=2), wkv7.ERR_UNSUPPORTED),
+    (dict(algo=7), wkv7.ERR_INVALID_ARG),
+])
+def test_varlen_validation(L, kw, code):
+    assert varlen(L, **kw) == code
+
+
+def test_varlen_accepts_empty_token_axis_without_launch_checks(L):
+    # total_T == 0 needs no token buffers; the call would launch (so only the
+    # argument checks are exercised here: a NULL token pointer is not an error)
+    assert varlen(L, TT=0, ptrs=[None] * 7, cu=None) == wkv7.ERR_INVALID_ARG   # cu_seqlens still required
