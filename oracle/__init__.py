@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for the RWKV-7 WKV7 forward -- TEST INFRASTRUCTURE ONLY.
+"""fp64 CPU oracle for the RWKV-7 WKV7 forward and the Gated DeltaNet forward
+-- TEST INFRASTRUCTURE ONLY.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  The HIP product path never imports it,
@@ -46,6 +47,8 @@ def _load():
     lib.wkv7_oracle_fwd.restype = i
     lib.wkv7_oracle_step.argtypes = [i, i, i, i] + [d] * 8
     lib.wkv7_oracle_step.restype = i
+    lib.gdn_oracle_fwd.argtypes = [i, i, i, i, i] + [d] * 6 + [i, d, d]
+    lib.gdn_oracle_fwd.restype = i
     lib.wkv7_oracle_max_threads.restype = i
     lib.wkv7_oracle_set_threads.argtypes = [i]
     _lib = lib
@@ -103,6 +106,31 @@ def step(r, w, k, v, a, b, state):
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return o, st
+
+
+def gdn_fwd(q, k, v, g, beta, initial_state=None):
+    """Gated DeltaNet forward (textbook gated delta rule; see the C file).
+    q, k: [B,T,H,K]; v: [B,T,H,V]; g, beta: [B,T,H]; initial_state:
+    [B,H,K,V], [1,H,K,V] (shared) or None.  Returns (o, final_state) in
+    float64."""
+    lib = _load()
+    q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    assert k.shape == (B, T, H, K) and v.shape == (B, T, H, V)
+    assert g.shape == (B, T, H) and beta.shape == (B, T, H)
+    s0 = None if initial_state is None else _f64(initial_state)
+    n_s0 = 0
+    if s0 is not None:
+        n_s0 = s0.shape[0]
+        assert s0.shape == (n_s0, H, K, V) and n_s0 in (1, B)
+    o = np.zeros((B, T, H, V), np.float64)
+    sf = np.zeros((B, H, K, V), np.float64)
+    rc = lib.gdn_oracle_fwd(B, T, H, K, V, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                            _ptr(s0), n_s0, _ptr(o), _ptr(sf))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return o, sf
 
 
 def max_threads():

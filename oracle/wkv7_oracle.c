@@ -142,6 +142,88 @@ int wkv7_oracle_step(int B, int H, int K, int V,
     return 0;
 }
 
+/* ------------------------------------------------------------------------
+ * Gated DeltaNet forward (rwkv-ops README, section "gdn_recurrent 使用方法",
+ * interface of gated_delta_net_recurrent; the same interface is listed for
+ * the chunkwise gated_delta_net_chunk).  The page fixes the interface:
+ *   q, k [B,T,H,K] are L2-normalised inside the operator; v [B,T,H,V];
+ *   g [B,T,H] is a log-space decay gate; beta [B,T,H] is a write strength
+ *   already passed through a sigmoid (in (0,1)); initial_state is [B,H,K,V]
+ *   or [1,H,K,V] (shared); out has v's shape.
+ * It does not print the recurrence.  The reading used is the textbook gated
+ * delta rule with a K x V state:
+ *
+ *   qn = q / sqrt(sum q^2 + eps),  kn = k / sqrt(sum k^2 + eps),  eps = 1e-6
+ *   S  = exp(g) * (I - beta kn kn^T) S  +  beta kn v^T
+ *   o  = S^T qn
+ *
+ * (no scale on q).  n_s0 is 1 (one shared initial state) or B.
+ * ------------------------------------------------------------------------ */
+int gdn_oracle_fwd(int B, int T, int H, int K, int V,
+                   const double *q, const double *k, const double *v,
+                   const double *g, const double *beta,
+                   const double *s0, int n_s0, double *o, double *s_final)
+{
+    if (B < 0 || T < 0 || H < 0 || K <= 0 || V <= 0) return -1;
+    if (T > 0 && (!q || !k || !v || !g || !beta || !o)) return -1;
+    if (s0 && n_s0 != 1 && n_s0 != B) return -1;
+    const double eps = 1e-6;
+    const long long nseq = (long long)B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long long bh = 0; bh < nseq; ++bh) {
+        const int bb = (int)(bh / H), h = (int)(bh % H);
+        double *S = (double *)malloc(sizeof(double) * (size_t)K * V);
+        double *kS = (double *)malloc(sizeof(double) * (size_t)V);
+        double *qn = (double *)malloc(sizeof(double) * (size_t)K);
+        double *kn = (double *)malloc(sizeof(double) * (size_t)K);
+        if (s0)
+            memcpy(S, &s0[IDX_ST(n_s0 == 1 ? 0 : bb, h, 0, 0, H, K, V)], sizeof(double) * (size_t)K * V);
+        else
+            memset(S, 0, sizeof(double) * (size_t)K * V);
+        for (int t = 0; t < T; ++t) {
+            const double *qt = &q[IDX_TOK(bb, t, h, 0, T, H, K)];
+            const double *kt = &k[IDX_TOK(bb, t, h, 0, T, H, K)];
+            const double *vt = &v[IDX_TOK(bb, t, h, 0, T, H, V)];
+            const double gt = g[((size_t)bb * T + t) * H + h];
+            const double bt = beta[((size_t)bb * T + t) * H + h];
+            double nq = 0.0, nk = 0.0;
+            for (int i = 0; i < K; ++i) {
+                nq += qt[i] * qt[i];
+                nk += kt[i] * kt[i];
+            }
+            nq = 1.0 / sqrt(nq + eps);
+            nk = 1.0 / sqrt(nk + eps);
+            for (int i = 0; i < K; ++i) {
+                qn[i] = qt[i] * nq;
+                kn[i] = kt[i] * nk;
+            }
+            for (int j = 0; j < V; ++j) {
+                double acc = 0.0;
+                for (int i = 0; i < K; ++i) acc += kn[i] * S[(size_t)i * V + j];
+                kS[j] = acc;
+            }
+            const double alpha = exp(gt);
+            for (int i = 0; i < K; ++i)
+                for (int j = 0; j < V; ++j) {
+                    double *s = &S[(size_t)i * V + j];
+                    *s = alpha * (*s - bt * kn[i] * kS[j]) + bt * kn[i] * vt[j];
+                }
+            double *ot = &o[IDX_TOK(bb, t, h, 0, T, H, V)];
+            for (int j = 0; j < V; ++j) {
+                double acc = 0.0;
+                for (int i = 0; i < K; ++i) acc += qn[i] * S[(size_t)i * V + j];
+                ot[j] = acc;
+            }
+        }
+        if (s_final) memcpy(&s_final[IDX_ST(bb, h, 0, 0, H, K, V)], S, sizeof(double) * (size_t)K * V);
+        free(kn);
+        free(qn);
+        free(kS);
+        free(S);
+    }
+    return 0;
+}
+
 /* Thread control for the OpenMP loop over (b, h); used to report how many
  * host threads a timed oracle run used. */
 int wkv7_oracle_max_threads(void)
