@@ -255,6 +255,30 @@ def varlen_workload(steps, warmup):
                    "lengths": [int(x) for x in lens], "kernel": "chunked d64 (packed)"}}
 
 
+def gdn_workload(steps, warmup):
+    """Gated DeltaNet forward on the chunked kernel at the B8 T4096 H64 d64
+    shape (bf16, no initial state, final state written)."""
+    import torch
+    from rwkv_linear_attention_amd import synth, wkv7
+    B, T, H, D = 8, 4096, 64, 64
+    print(f"[bench] generating Gated DeltaNet workload B{B} T{T} H{H} d{D}", file=sys.stderr, flush=True)
+    inp = synth.make_gdn(B, T, H, D, seed=1301)
+    names = ("q", "k", "v", "g", "beta")
+    dev = {n: synth.to_torch(inp[n], "bf16", "cuda") for n in names}
+    o = torch.empty((B, T, H, D), dtype=torch.bfloat16, device="cuda")
+    sf = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
+    ms = _time_launches(lambda i: wkv7.gdn_fwd(*(dev[n] for n in names), out=o, final_state=sf),
+                        steps, warmup)
+    # q, k, v and o once (D channels each), g and beta once (one element per
+    # token and head), the final state written once
+    nbytes = 4 * B * T * H * D * 2 + 2 * B * T * H * 2 + B * H * D * D * 4
+    name = f"gdn_fwd_bf16_B{B}_T{T}_H{H}_d{D}"
+    return {name: {"ms": round(ms, 5), "Mtokens_per_s": round(B * T / ms / 1e3, 3),
+                   "GB_per_s": round(nbytes / ms / 1e6, 1),
+                   "frac_of_8TBps": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes,
+                   "kernel": "chunked d64 (Gated DeltaNet)"}}
+
+
 def _time_launches(fn, steps, warmup):
     import torch
     for _ in range(warmup):
@@ -271,7 +295,8 @@ def _time_launches(fn, steps, warmup):
 
 
 def other_workloads(steps, warmup):
-    """Head size 128 forward (B16 T4096 H32, trailing-padding mask, S0) and the
+    """Head size 128 forward (B16 T4096 H32, trailing-padding mask, S0), the
+    packed variable-length forward, Gated DeltaNet (B8 T4096 H64 d64) and the
     decode step (B512 H40 d64, 256 consecutive in-place steps)."""
     import torch
     from rwkv_linear_attention_amd import synth, wkv7
@@ -296,6 +321,9 @@ def other_workloads(steps, warmup):
     torch.cuda.empty_cache()
 
     out.update(varlen_workload(steps, warmup))
+    torch.cuda.empty_cache()
+    out.update(gdn_workload(steps, warmup))
+    torch.cuda.empty_cache()
 
     wl = synth.WORKLOADS[4]
     B, NSTEP, H, D = wl["B"], wl["T"], wl["H"], wl["K"]

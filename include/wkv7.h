@@ -136,6 +136,43 @@ wkv7_status_t wkv7_fwd_varlen(int dtype, int N, int total_T, int H, int K, int V
                               void *o, float *final_state, int algo, void *stream);
 
 /*
+ * wkv7_gdn_fwd -- Gated DeltaNet forward over whole sequences (rwkv-ops
+ * README, section "gdn_recurrent 使用方法", argument table of
+ * gated_delta_net_recurrent; the chunked form "gdn_chunk 使用方法" computes
+ * the same).  Per sequence and head, with a K x V fp32 state S:
+ *     qn = q_t / sqrt(|q_t|^2 + 1e-6),  kn = k_t / sqrt(|k_t|^2 + 1e-6)
+ *     S  = e^{g_t} S,  then  S = S + beta_t kn (v_t - S^T kn)^T
+ *        (that is, S = e^{g_t} (I - beta_t kn kn^T) S + beta_t kn v_t^T)
+ *     o_t = S^T qn
+ * The pages name the inputs, the internal L2 normalisation of q and k, the
+ * log-space gate g and the strength beta in (0, 1); the update itself is not
+ * printed there and is read as the gated delta rule (decay first, then the
+ * delta-rule correction and write, no scale on q; 1e-6 inside the norm is
+ * this library's choice).  It is the generalized delta rule of wkv7_fwd with
+ * r = qn, w = g on every channel, k = beta kn, a = -e^g beta kn, b = kn.
+ *
+ *   dtype          WKV7_F32 or WKV7_BF16: element type of q,k,v,g,beta and o.
+ *   B, T, H, K, V  as for wkv7_fwd; K == V in {64, 128}.
+ *   q, k           [B,T,H,K] dtype, raw (normalised inside).  Read only.
+ *   v              [B,T,H,V] dtype.  Read only.
+ *   g              [B,T,H] dtype, log-space gate (normally <= 0).  Read only.
+ *   beta           [B,T,H] dtype, write strength.  Read only.
+ *   initial_state  [n_state,H,K,V] fp32 with n_state 1 (shared by all B
+ *                  sequences) or B, or NULL for a zero state.  Read only.
+ *   n_state        1 or B when initial_state is given; ignored otherwise.
+ *   o              [B,T,H,V] dtype.  Written.
+ *   final_state    [B,H,K,V] fp32, or NULL.  Written.  May be the same buffer
+ *                  as initial_state only when n_state == B (or B == 1).
+ *   algo           as for wkv7_fwd.
+ *   stream         hipStream_t to enqueue on.
+ */
+wkv7_status_t wkv7_gdn_fwd(int dtype, int B, int T, int H, int K, int V,
+                           const void *q, const void *k, const void *v,
+                           const void *g, const void *beta,
+                           const float *initial_state, int n_state,
+                           void *o, float *final_state, int algo, void *stream);
+
+/*
  * wkv7_step -- one decode token per sequence, state updated in place
  * (section "rwkv7_op_rnn 使用方法": the T = 1 case of the forward).
  *
@@ -160,7 +197,8 @@ const char *wkv7_strerror(int status);
  * would be rejected.  Host only; launches nothing. */
 int wkv7_fwd_path(int dtype, int B, int T, int H, int K, int V, int algo);
 
-/* ABI version of this header (major * 100 + minor): 101 adds wkv7_fwd_varlen. */
+/* ABI version of this header (major * 100 + minor): 101 adds wkv7_fwd_varlen,
+ * 102 adds wkv7_gdn_fwd. */
 int wkv7_version(void);
 
 #ifdef __cplusplus

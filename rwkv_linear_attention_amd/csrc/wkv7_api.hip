@@ -40,7 +40,7 @@ int choose_path(int dtype, int T, int algo)
 
 extern "C" {
 
-int wkv7_version(void) { return 101; }
+int wkv7_version(void) { return 102; }
 
 const char *wkv7_strerror(int status)
 {
@@ -129,6 +129,54 @@ wkv7_status_t wkv7_fwd_varlen(int dtype, int N, int total_T, int H, int K, int V
     args.state_map = state_map;
     args.n_state = initial_state ? n_state : 0;
     hipStream_t s = (hipStream_t)stream;
+    hipError_t e = path == WKV7_ALGO_CHUNKED ? wkv7::launch_chunked(args, s)
+                                             : wkv7::launch_recurrent(dtype, args, s);
+    return e == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
+}
+
+wkv7_status_t wkv7_gdn_fwd(int dtype, int B, int T, int H, int K, int V,
+                          const void *q, const void *k, const void *v,
+                          const void *g, const void *beta,
+                          const float *initial_state, int n_state,
+                          void *o, float *final_state, int algo, void *stream)
+{
+    wkv7_status_t st = check_common(dtype, B, H, K, V);
+    if (st != WKV7_OK) return st;
+    if (T < 0) return WKV7_ERR_INVALID_ARG;
+    if ((long long)B * T * H * K > (1ll << 40)) return WKV7_ERR_UNSUPPORTED;
+    if (algo != WKV7_ALGO_AUTO && algo != WKV7_ALGO_RECURRENT && algo != WKV7_ALGO_CHUNKED)
+        return WKV7_ERR_INVALID_ARG;
+    if (T > 0) {
+        const void *req[] = {q, k, v, g, beta, o};
+        for (const void *p : req)
+            if (!p || !aligned16(p)) return WKV7_ERR_INVALID_ARG;
+    }
+    if (initial_state) {
+        if (!aligned16(initial_state)) return WKV7_ERR_INVALID_ARG;
+        if (n_state != 1 && n_state != B) return WKV7_ERR_INVALID_ARG;
+        // a shared state is read by every sequence: writing finals over it races
+        if (n_state == 1 && B > 1 && final_state == initial_state) return WKV7_ERR_INVALID_ARG;
+    }
+    if (final_state && !aligned16(final_state)) return WKV7_ERR_INVALID_ARG;
+    const int path = choose_path(dtype, T, algo);
+    if (path < 0) return WKV7_ERR_UNSUPPORTED;
+
+    hipStream_t s = (hipStream_t)stream;
+    if (T == 0) {
+        if (!final_state) return WKV7_OK;
+        const size_t n = (size_t)B * H * K * V;
+        if (!initial_state || n_state == B)
+            return wkv7::launch_state_copy(initial_state, final_state, n, s) == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
+        const size_t one = (size_t)H * K * V;
+        for (int i = 0; i < B; ++i)
+            if (wkv7::launch_state_copy(initial_state, final_state + i * one, one, s) != hipSuccess)
+                return WKV7_ERR_HIP;
+        return WKV7_OK;
+    }
+    // q in the r slot, g in the w slot, beta in the a slot; b and mask unused
+    wkv7::FwdArgs args{B, T, H, K, q, g, k, v, beta, nullptr, initial_state, nullptr, o, final_state};
+    args.n_state = initial_state ? n_state : 0;
+    args.gdn = true;
     hipError_t e = path == WKV7_ALGO_CHUNKED ? wkv7::launch_chunked(args, s)
                                              : wkv7::launch_recurrent(dtype, args, s);
     return e == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;

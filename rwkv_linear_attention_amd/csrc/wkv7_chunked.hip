@@ -77,7 +77,8 @@ template <int D> struct WS {
     static constexpr int OFF_MM = OFF_TN + 1024;       // [M_ra^T | M_rk^T hi] B-frags, 1024
     static constexpr int OFF_MRKL = OFF_MM + 1024;     // M_rk^T lo B-frag, 512
     static constexpr int OFF_EGL = OFF_MRKL + 512;     // e^{G_L}, D floats
-    static constexpr int OFF_AH = (OFF_EGL + 4 * D + 255) / 256 * 256;   // A^ tile
+    static constexpr int OFF_SIG = OFF_EGL + 4 * D;    // Gated DeltaNet output scale, 16 floats
+    static constexpr int OFF_AH = (OFF_SIG + 64 + 255) / 256 * 256;   // A^ tile
     static constexpr int OFF_KH = OFF_AH + TILE;       // K^ hi tile
     static constexpr int OFF_KL = OFF_KH + TILE;       // K^ lo tile
     static constexpr int OFF_V = OFF_KL + TILE;        // V tile (global->LDS copy)
@@ -210,7 +211,7 @@ __device__ __forceinline__ uint32_t lds_addr(const char *p)
 // at `raw_lds` (5 arrays x NCB blocks, 1 KB each).  Lane l of each load
 // fetches the 16 bytes of token l%16, channels 32s + 8(l/16) .. +7; tokens
 // past T read token T-1 (discarded).
-template <int D>
+template <int D, bool GDN>
 __device__ __forceinline__ void ws_issue_raw(uint32_t raw_lds, const uint16_t *const *src,
                                              size_t seq_base, uint32_t tok_stride, int T, int chunk,
                                              int lane)
@@ -219,15 +220,17 @@ __device__ __forceinline__ void ws_issue_raw(uint32_t raw_lds, const uint16_t *c
     const uint32_t tok = (uint32_t)min(chunk * 16 + t, T - 1);
     const size_t base = seq_base + (size_t)tok * tok_stride + 8 * v;
 #pragma unroll
-    for (int arr = 0; arr < 5; ++arr)
+    for (int arr = 0; arr < 5; ++arr) {
+        if (GDN && arr != 0 && arr != 2) continue;   // Gated DeltaNet: q and k only
 #pragma unroll
         for (int s = 0; s < WS<D>::NCB; ++s)
             copy16_to_lds(src[arr] + base + 32 * s, raw_lds + (arr * WS<D>::NCB + s) * 1024);
+    }
 }
 
 // Producer: read the staged raw tile into the register layout used by the
 // precompute (lane (t, g): channels 32s + 16hh + 4g .. +3 of token t).
-template <int D>
+template <int D, bool GDN>
 __device__ __forceinline__ void ws_read_raw(RawTile<D> &rt, const char *raw, int lane)
 {
     const int t = lane & 15, g = lane >> 4;
@@ -237,8 +240,56 @@ __device__ __forceinline__ void ws_read_raw(RawTile<D> &rt, const char *raw, int
         for (int s = 0; s < WS<D>::NCB; ++s)
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh)
-                rt.x[s][arr][hh] = *(const u32x2 *)(raw + (arr * WS<D>::NCB + s) * 1024 +
-                                                    16 * (t + 16 * (2 * hh + (g >> 1))) + 8 * (g & 1));
+                rt.x[s][arr][hh] = (!GDN || arr == 0 || arr == 2)
+                                       ? *(const u32x2 *)(raw + (arr * WS<D>::NCB + s) * 1024 +
+                                                          16 * (t + 16 * (2 * hh + (g >> 1))) + 8 * (g & 1))
+                                       : u32x2{0u, 0u};   // Gated DeltaNet: unused
+}
+
+// Gated DeltaNet (rwkv-ops README, section "gdn_recurrent 使用方法": q, k
+// L2-normalised inside, g a log-space gate, beta a write strength), read as
+// the gated delta rule S = e^g (I - beta kn kn^T) S + beta kn v^T, o = S^T qn,
+// is the generalized delta rule with
+//   r = qn,  w = g (every channel),  k = beta kn,  a = -e^g beta kn,  b = kn.
+// Each of r, k, a, b is a raw bf16 input (q or k) times a per-token scalar,
+// so the producer keeps q and k as loaded and hands the precompute the four
+// scalars: they are applied in fp32 together with the decay factors, before
+// the one rounding to bf16 that the MFMA operands take anyway (rounding
+// qn, beta kn, ... to bf16 first would add a second rounding, which costs
+// about half of the bf16 error budget on random q and k).
+// Producer: gate into the w slot (every channel) and the token's scalars
+// sc = {1/|q|, beta/|k|, -e^g beta/|k|, 1/|k|} (norms with 1e-6 added to the
+// squared length).  The four lanes of a token (t, t + 16, t + 32, t + 48)
+// together hold its D channels.
+template <int D>
+__device__ __forceinline__ void gdn_scalars(RawTile<D> &rt, uint32_t gbits, float beta, float *sc)
+{
+    constexpr int NCB = D / 32;
+    float nq = 0.0f, nk = 0.0f;
+#pragma unroll
+    for (int s = 0; s < NCB; ++s) {
+        float qv[8], kv[8];
+        unpack8(rt.x[s][0], qv);
+        unpack8(rt.x[s][2], kv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            nq = fmaf(qv[e], qv[e], nq);
+            nk = fmaf(kv[e], kv[e], nk);
+        }
+    }
+    nq = xor_sum(xor_sum(nq, 16), 32);
+    nk = xor_sum(xor_sum(nk, 16), 32);
+    const float iq = 1.0f / sqrtf(nq + 1e-6f), ik = 1.0f / sqrtf(nk + 1e-6f);
+    const float gate = bf16_bits_to_f32((uint16_t)gbits);
+    sc[0] = iq;
+    sc[1] = beta * ik;
+    sc[2] = -__expf(gate) * beta * ik;
+    sc[3] = ik;
+    const uint32_t w2 = (gbits & 0xffffu) | (gbits << 16);
+#pragma unroll
+    for (int s = 0; s < NCB; ++s)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) rt.x[s][1][hh] = u32x2{w2, w2};
 }
 
 // Swizzled 16 x D bf16 tile: the 16-byte chunk c (channels 8c .. 8c + 7) of
@@ -306,12 +357,14 @@ template <int D> struct ChunkOps {
     u32x4 ah[D / 32], kh[D / 32], kl[D / 32];   // row t of the A^, K^ hi, K^ lo tiles
     f32x4 egl[D / 32][2];               // e^{G_L} of channels 32s + 16hh + 4g .. +3
     bf16x4 tinv, tnbk, mra, mrkh, mrkl;
+    float sig;                          // Gated DeltaNet: e^{G_t} / |q_t| of token t
     int flag;                           // wave-uniform extreme-decay flag
 };
 
-template <int D>
+// sc: per-token scalars of r, k, a, b (Gated DeltaNet only; see gdn_scalars).
+template <int D, bool GDN>
 __device__ void ws_precompute(const RawTile<D> &rt, ChunkOps<D> &op, int lane, const bf16x8 *psel,
-                              bf16x4 ltri)
+                              bf16x4 ltri, const float *sc)
 {
     using C = WS<D>;
     const int t = lane & 15, g = lane >> 4;
@@ -343,8 +396,10 @@ __device__ void ws_precompute(const RawTile<D> &rt, ChunkOps<D> &op, int lane, c
         float rv[8], kv[8], av[8], bv[8];
         unpack8(rt.x[s][0], rv);
         unpack8(rt.x[s][2], kv);
-        unpack8(rt.x[s][3], av);
-        unpack8(rt.x[s][4], bv);
+        if constexpr (!GDN) {
+            unpack8(rt.x[s][3], av);
+            unpack8(rt.x[s][4], bv);
+        }
         float Rt[8], Bt[8], Ah[8], Kh[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -355,10 +410,18 @@ __device__ void ws_precompute(const RawTile<D> &rt, ChunkOps<D> &op, int lane, c
             const float eGL = row_bcast15(eG);
             op.egl[s][e >> 2][e & 3] = eGL;
             emin = fminf(emin, eGL);
-            Rt[e] = rv[e] * eG;
-            Bt[e] = bv[e] * eGp;
-            Ah[e] = av[e] * enG;
-            Kh[e] = kv[e] * enG;
+            if constexpr (GDN) {
+                if (s == 0 && e == 0) op.sig = eG * sc[0];   // the gate is the same on every channel
+                Rt[e] = rv[e] * (eG * sc[0]);
+                Kh[e] = kv[e] * (enG * sc[1]);
+                Ah[e] = kv[e] * (enG * sc[2]);
+                Bt[e] = kv[e] * (eGp * sc[3]);
+            } else {
+                Rt[e] = rv[e] * eG;
+                Bt[e] = bv[e] * eGp;
+                Ah[e] = av[e] * enG;
+                Kh[e] = kv[e] * enG;
+            }
         }
         const bf16x8 Rh = pack8(Rt), Bh = pack8(Bt), Khh = pack8(Kh), Ahh = pack8(Ah);
         // (R~ K^^T)^T to about 16 bits: hi.hi + hi.lo + lo.hi.
@@ -382,7 +445,13 @@ __device__ void ws_precompute(const RawTile<D> &rt, ChunkOps<D> &op, int lane, c
         mbk = mfma32(Bh, Khh, mbk);     // B~ K^^T
 
         op.B[s] = Bh;
-        op.R[s] = Rh;
+        // Gated DeltaNet: R~ = (e^{G_t} / |q_t|) q_t with q_t exact in bf16, so the
+        // consumer multiplies q_t S instead and scales the result by op.sig.
+        if constexpr (GDN)
+            op.R[s] = __builtin_bit_cast(bf16x8, u32x4{rt.x[s][0][0][0], rt.x[s][0][0][1], rt.x[s][0][1][0],
+                                                       rt.x[s][0][1][1]});
+        else
+            op.R[s] = Rh;
         op.ah[s] = __builtin_bit_cast(u32x4, Ahh);
         op.kh[s] = __builtin_bit_cast(u32x4, Khh);
         op.kl[s] = __builtin_bit_cast(u32x4, Khl);
@@ -420,7 +489,7 @@ __device__ void ws_precompute(const RawTile<D> &rt, ChunkOps<D> &op, int lane, c
 }
 
 // Producer: write one chunk's operands into `slot` (layout WS<D>).
-template <int D>
+template <int D, bool GDN>
 __device__ __forceinline__ void ws_store_ops(const ChunkOps<D> &op, char *slot, int lane)
 {
     using C = WS<D>;
@@ -449,6 +518,9 @@ __device__ __forceinline__ void ws_store_ops(const ChunkOps<D> &op, char *slot, 
     st8(slot + C::OFF_MM + lane * 16, op.mra);
     st8(slot + C::OFF_MM + lane * 16 + 8, op.mrkh);
     st8(slot + C::OFF_MRKL + lane * 8, op.mrkl);
+    if constexpr (GDN) {
+        if (g == 0) *(float *)(slot + C::OFF_SIG + 4 * t) = op.sig;
+    }
 }
 
 // ---- consumer ----------------------------------------------------------------
@@ -525,6 +597,95 @@ __device__ void ws_chunk_exact(f32x4 (*S)[WS<D>::NT], const uint16_t *r, const u
     }
 }
 
+// Exact path, Gated DeltaNet inputs (q, k, v, per-token gate g and strength
+// beta); same state layout as ws_chunk_exact.
+template <int D>
+__device__ void ws_chunk_exact_gdn(f32x4 (*S)[WS<D>::NT], const uint16_t *q, const uint16_t *gg,
+                                   const uint16_t *k, const uint16_t *v, const uint16_t *beta,
+                                   uint16_t *o, size_t tok0, int Tn, int H, int h, int chunk, int cbase,
+                                   int lane)
+{
+    constexpr int NQ = D / 16, NT = WS<D>::NT;
+    const int g = lane >> 4, j = lane & 15;
+    auto ld4 = [&](const uint16_t *p, float *x) {
+        const u32x2 u = *(const u32x2 *)p;
+        x[0] = bf16_lo(u[0]); x[1] = bf16_hi(u[0]); x[2] = bf16_lo(u[1]); x[3] = bf16_hi(u[1]);
+    };
+    for (int tt = 0; tt < 16; ++tt) {
+        const int tok = chunk * 16 + tt;
+        if (tok >= Tn) break;
+        const size_t sidx = (tok0 + tok) * H + h;
+        const size_t base = sidx * D;
+        const float gate = bf16_bits_to_f32(gg[sidx]), bt = bf16_bits_to_f32(beta[sidx]);
+        // Norms (lanes of one row group hold the same channels: reduce over
+        // the groups only), then k^T S; q and k are re-read where used so
+        // that this rare path keeps few registers live.
+        float nq = 0.0f, nk = 0.0f;
+#pragma unroll
+        for (int qi = 0; qi < NQ; ++qi) {
+            if constexpr (NQ > 4) __builtin_amdgcn_sched_barrier(0);
+            float qe[4], ke[4];
+            ld4(q + base + 16 * qi + 4 * g, qe);
+            ld4(k + base + 16 * qi + 4 * g, ke);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                nq = fmaf(qe[i], qe[i], nq);
+                nk = fmaf(ke[i], ke[i], nk);
+            }
+        }
+        nq = xor_sum(xor_sum(nq, 16), 32);
+        nk = xor_sum(xor_sum(nk, 16), 32);
+        const float iq = 1.0f / sqrtf(nq + 1e-6f), ik = 1.0f / sqrtf(nk + 1e-6f);
+        const float alpha = __expf(gate);
+        float ks[NT] = {};
+#pragma unroll
+        for (int qi = 0; qi < NQ; ++qi) {
+            if constexpr (NQ > 4) __builtin_amdgcn_sched_barrier(0);
+            float ke[4];
+            ld4(k + base + 16 * qi + 4 * g, ke);
+#pragma unroll
+            for (int n = 0; n < NT; ++n)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ks[n] = fmaf(ke[i] * ik, S[qi][n][i], ks[n]);
+        }
+#pragma unroll
+        for (int n = 0; n < NT; ++n) ks[n] = xor_sum(xor_sum(ks[n], 16), 32);
+        float vj[NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) vj[n] = bf16_bits_to_f32(v[base + cbase + 16 * n + j]);
+#pragma unroll
+        for (int qi = 0; qi < NQ; ++qi) {
+            if constexpr (NQ > 4) __builtin_amdgcn_sched_barrier(0);
+            float ke[4];
+            ld4(k + base + 16 * qi + 4 * g, ke);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float kn = ke[i] * ik;
+#pragma unroll
+                for (int n = 0; n < NT; ++n)
+                    S[qi][n][i] = fmaf(alpha, fmaf(-bt * kn, ks[n], S[qi][n][i]), bt * kn * vj[n]);
+            }
+        }
+        float ov[NT] = {};
+#pragma unroll
+        for (int qi = 0; qi < NQ; ++qi) {
+            if constexpr (NQ > 4) __builtin_amdgcn_sched_barrier(0);
+            float qe[4];
+            ld4(q + base + 16 * qi + 4 * g, qe);
+#pragma unroll
+            for (int n = 0; n < NT; ++n)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ov[n] = fmaf(qe[i] * iq, S[qi][n][i], ov[n]);
+        }
+#pragma unroll
+        for (int n = 0; n < NT; ++n) ov[n] = xor_sum(xor_sum(ov[n], 16), 32);
+        if (g == 0) {
+#pragma unroll
+            for (int n = 0; n < NT; ++n) o[base + cbase + 16 * n + j] = f32_to_bf16_bits(ov[n]);
+        }
+    }
+}
+
 // Store one chunk's output tile held as O^T fragments (lane (g, t): token t,
 // columns cbase + 16n + 4g .. +3).
 template <int D>
@@ -545,7 +706,7 @@ __device__ __forceinline__ void ws_store_out(const f32x4 *Ot, uint16_t *o, size_
 // issued in dependency order across the four independent column tiles, and
 // the S-independent products are placed where they fill the latency of the
 // S -> X -> U -> S' chain.
-template <int D>
+template <int D, bool GDN>
 __device__ __forceinline__ void ws_chunk_serial(f32x4 (*S)[WS<D>::NT], const char *slot, uint16_t *o,
                                                 size_t tok0, int Tn, int H, int h, int chunk, int cbase,
                                                 int lane)
@@ -563,6 +724,28 @@ __device__ __forceinline__ void ws_chunk_serial(f32x4 (*S)[WS<D>::NT], const cha
 #pragma unroll
         for (int s = 0; s < C::NCB; ++s) sb[s][n] = cat8(cvt4(S[2 * s][n]), cvt4(S[2 * s + 1][n]));
         vf[n] = tile_tr<D>(slot + C::OFF_V, 4 * g, cbase + 16 * n, lane);   // V[4g + i][cbase + 16n + j]
+    }
+    f32x4 Ot[NT];   // O^T
+    if constexpr (GDN) {
+        // Gated DeltaNet: the S-part of the output is (e^{G_t} / |q_t|) q_t S
+        // with q_t exact; q_t S is taken to about 16 bits by adding the bf16
+        // state's remainder as a second term (computed here, before S
+        // changes).  On random q this output term is a small projection of a
+        // larger state, and a bf16 state alone costs most of the error budget.
+#pragma unroll
+        for (int s = 0; s < C::NCB; ++s) {
+            const bf16x8 rt = ld16(slot + C::OFF_R + s * 1024 + lane * 16);
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+                f32x4 l0 = S[2 * s][n], l1 = S[2 * s + 1][n];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    l0[i] -= (float)sb[s][n][i];
+                    l1[i] -= (float)sb[s][n][4 + i];
+                }
+                Ot[n] = mfma32(cat8(cvt4(l0), cvt4(l1)), rt, s == 0 ? zero4() : Ot[n]);
+            }
+        }
     }
     // X = B~ S
     f32x4 X[NT];
@@ -585,12 +768,16 @@ __device__ __forceinline__ void ws_chunk_serial(f32x4 (*S)[WS<D>::NT], const cha
         for (int n = 0; n < NT; ++n) X[n] = mfma32(bt, sb[s][n], X[n]);
     }
     // O^T, S-part (chunk-start state)
-    f32x4 Ot[NT];
 #pragma unroll
     for (int s = 0; s < C::NCB; ++s) {
         const bf16x8 rt = ld16(slot + C::OFF_R + s * 1024 + lane * 16);
 #pragma unroll
-        for (int n = 0; n < NT; ++n) Ot[n] = mfma32(sb[s][n], rt, s == 0 ? zero4() : Ot[n]);
+        for (int n = 0; n < NT; ++n) Ot[n] = mfma32(sb[s][n], rt, (s == 0 && !GDN) ? zero4() : Ot[n]);
+    }
+    if constexpr (GDN) {
+        const float sig = *(const float *)(slot + C::OFF_SIG + 4 * (lane & 15));
+#pragma unroll
+        for (int n = 0; n < NT; ++n) Ot[n] *= sig;
     }
     // U = T X + N_bk V
     const bf16x8 tn = ld16(slot + C::OFF_TN + lane * 16);
@@ -623,7 +810,10 @@ __device__ __forceinline__ void ws_chunk_serial(f32x4 (*S)[WS<D>::NT], const cha
 
 // ---- kernel --------------------------------------------------------------------
 
-template <int D>
+// GDN = false: generalized-delta-rule inputs r, w, k, v, a, b.  GDN = true:
+// Gated DeltaNet inputs in the same argument slots: r = q, k = k, v = v,
+// w = g [.., H], a = beta [.., H] (b and mask unused).
+template <int D, bool GDN>
 __global__ __launch_bounds__(64 * WS<D>::NWAVE)
 __attribute__((amdgpu_waves_per_eu(WS<D>::WAVES_PER_SIMD, WS<D>::WAVES_PER_SIMD))) void chunked_ws_kernel(
     int T, int H, int nbh, const int32_t *__restrict__ cu_seqlens, const int32_t *__restrict__ state_map,
@@ -705,6 +895,8 @@ __attribute__((amdgpu_waves_per_eu(WS<D>::WAVES_PER_SIMD, WS<D>::WAVES_PER_SIMD)
     if (state_map) {
         sidx = state_map[sq];
         if (sidx < 0 || sidx >= n_state) sidx = -1;
+    } else if (n_state == 1) {
+        sidx = 0;   // one initial state shared by every sequence
     }
     const int nchunks = (Tn + 15) / 16;
     char *const lds = lds_slots + seq * C::NSLOT * C::SLOT;
@@ -738,10 +930,13 @@ __attribute__((amdgpu_waves_per_eu(WS<D>::WAVES_PER_SIMD, WS<D>::WAVES_PER_SIMD)
             const char *slot = lds + (c % C::NSLOT) * C::SLOT;
             // ready[slot] = 2 (c + 1) + extreme-decay flag once chunk c is in the slot
             const int rv = spin_ge(&ready[c % C::NSLOT], 2 * (c + 1));
-            if (rv & 1)
-                ws_chunk_exact<D>(S, r, w, k, v, a, b, mask, o, tok0, Tn, H, h, c, cbase, lane);
-            else
-                ws_chunk_serial<D>(S, slot, o, tok0, Tn, H, h, c, cbase, lane);
+            if (rv & 1) {
+                if constexpr (GDN)
+                    ws_chunk_exact_gdn<D>(S, r, w, k, v, a, o, tok0, Tn, H, h, c, cbase, lane);
+                else
+                    ws_chunk_exact<D>(S, r, w, k, v, a, b, mask, o, tok0, Tn, H, h, c, cbase, lane);
+            } else
+                ws_chunk_serial<D, GDN>(S, slot, o, tok0, Tn, H, h, c, cbase, lane);
             lds_wait();                          // all reads of the slot have returned
             lds_store_relaxed(&done[crank / C::NSEQ], c + 1);
         }
@@ -773,37 +968,52 @@ __attribute__((amdgpu_waves_per_eu(WS<D>::WAVES_PER_SIMD, WS<D>::WAVES_PER_SIMD)
         bf16x4 ltri;
 #pragma unroll
         for (int i = 0; i < 4; ++i) ltri[i] = (__bf16)((4 * g + i <= j) ? 1.0f : 0.0f);
-        // Loop-carried request for this producer's next chunk: the mask byte
-        // of token (next chunk, lane & 15).
-        uint32_t mnext = 1;
+        // Loop-carried requests for this producer's next chunk: the mask byte
+        // (or, for Gated DeltaNet, the gate and strength) of token
+        // (next chunk, lane & 15).
+        uint32_t mnext = 1, gnext = 0, bnext = 0;
         const int t = lane & 15;
         if (p < nchunks) {
-            ws_issue_raw<D>(raw_lds, src, seq_base, tok_stride, Tn, p, lane);
-            if (mask) mnext = mask[tok0 + min(p * 16 + t, Tn - 1)];
+            ws_issue_raw<D, GDN>(raw_lds, src, seq_base, tok_stride, Tn, p, lane);
+            const size_t tk = tok0 + min(p * 16 + t, Tn - 1);
+            if constexpr (GDN) {
+                gnext = w[tk * H + h];
+                bnext = a[tk * H + h];
+            } else {
+                if (mask) mnext = mask[tk];
+            }
         }
         for (int c = p; c < nchunks; c += C::NPROD) {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            const uint32_t mcur = mnext;
+            const uint32_t mcur = mnext, gcur = gnext, bcur = bnext;
             RawTile<D> rt;
-            ws_read_raw<D>(rt, raw, lane);
+            ws_read_raw<D, GDN>(rt, raw, lane);
             lds_wait();
             if (c + C::NPROD < nchunks) {
                 const int cn = c + C::NPROD;
-                ws_issue_raw<D>(raw_lds, src, seq_base, tok_stride, Tn, cn, lane);
-                if (mask) mnext = mask[tok0 + min(cn * 16 + t, Tn - 1)];
+                ws_issue_raw<D, GDN>(raw_lds, src, seq_base, tok_stride, Tn, cn, lane);
+                const size_t tk = tok0 + min(cn * 16 + t, Tn - 1);
+                if constexpr (GDN) {
+                    gnext = w[tk * H + h];
+                    bnext = a[tk * H + h];
+                } else {
+                    if (mask) mnext = mask[tk];
+                }
             }
+            float sc[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+            if constexpr (GDN) gdn_scalars<D>(rt, gcur, bf16_bits_to_f32((uint16_t)bcur), sc);
             const int tok = c * 16 + t;
             rt.valid = tok < Tn;
             rt.upd = rt.valid && mcur != 0;
             zero_inactive<D>(rt);
             const bool all_upd = __all(rt.upd);
             ChunkOps<D> op;
-            ws_precompute<D>(rt, op, lane, psel, ltri);
+            ws_precompute<D, GDN>(rt, op, lane, psel, ltri, sc);
             char *slot = lds + (c % C::NSLOT) * C::SLOT;
             // the slot's previous chunk is consumed by every consumer
             spin_all_ge<C::NCONS>(done, c - C::NSLOT + 1);
             ws_issue_v<D>(lds_addr(slot + C::OFF_V), v, seq_base, tok_stride, Tn, c, lane);
-            ws_store_ops<D>(op, slot, lane);
+            ws_store_ops<D, GDN>(op, slot, lane);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the value tile has landed
             if (!all_upd && !rt.upd) {
                 // Value rows of tokens that do not update are cleared, so that
@@ -819,13 +1029,13 @@ __attribute__((amdgpu_waves_per_eu(WS<D>::WAVES_PER_SIMD, WS<D>::WAVES_PER_SIMD)
     }
 }
 
-template <int D>
+template <int D, bool GDN>
 static hipError_t launch_ws(const FwdArgs &p, hipStream_t stream)
 {
     using C = WS<D>;
     const int nbh = p.B * p.H;
     const dim3 grid((unsigned)((nbh + C::NSEQ - 1) / C::NSEQ)), block(64 * C::NWAVE);
-    hipLaunchKernelGGL((chunked_ws_kernel<D>), grid, block, 0, stream, p.T, p.H, nbh, p.cu_seqlens,
+    hipLaunchKernelGGL((chunked_ws_kernel<D, GDN>), grid, block, 0, stream, p.T, p.H, nbh, p.cu_seqlens,
                        p.state_map, p.n_state,
                        (const uint16_t *)p.r, (const uint16_t *)p.w, (const uint16_t *)p.k,
                        (const uint16_t *)p.v, (const uint16_t *)p.a, (const uint16_t *)p.b, p.s0,
@@ -835,7 +1045,8 @@ static hipError_t launch_ws(const FwdArgs &p, hipStream_t stream)
 
 hipError_t launch_chunked(const FwdArgs &p, hipStream_t stream)
 {
-    return p.D == 64 ? launch_ws<64>(p, stream) : launch_ws<128>(p, stream);
+    if (p.gdn) return p.D == 64 ? launch_ws<64, true>(p, stream) : launch_ws<128, true>(p, stream);
+    return p.D == 64 ? launch_ws<64, false>(p, stream) : launch_ws<128, false>(p, stream);
 }
 
 }  // namespace wkv7

@@ -20,7 +20,10 @@ struct FwdArgs {
     float *sf;                           // [B,H,D,D] or nullptr
     const int32_t *cu_seqlens = nullptr; // device, [B+1]
     const int32_t *state_map = nullptr;  // device, [B]
-    int n_state = 0;
+    int n_state = 0;                     // 1 with no state_map: one shared state
+    // Gated DeltaNet inputs in the same slots: r = q, k = k, v = v,
+    // w = gate g and a = strength beta, both one value per token and head.
+    bool gdn = false;
 };
 
 struct StepArgs {

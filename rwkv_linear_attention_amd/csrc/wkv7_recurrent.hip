@@ -20,7 +20,13 @@
 
 namespace wkv7 {
 
-template <int D, typename T_IO>
+// GDN = true takes Gated DeltaNet inputs in the same slots: r = q, k = k,
+// v = v, w = gate g [.., H], a = strength beta [.., H] (b and mask unused);
+// each staged token is turned into the generalized-delta-rule operands
+// r = qn, w = g, k = beta kn, a = -e^g beta kn, b = kn (q, k L2-normalised;
+// rwkv-ops README, section "gdn_recurrent 使用方法", read as the gated delta
+// rule).
+template <int D, typename T_IO, bool GDN>
 __global__ __launch_bounds__(D * 4) void recurrent_kernel(
     int T, int H, const int32_t *__restrict__ cu_seqlens, const int32_t *__restrict__ state_map,
     int n_state, const T_IO *__restrict__ r, const T_IO *__restrict__ w,
@@ -33,6 +39,7 @@ __global__ __launch_bounds__(D * 4) void recurrent_kernel(
     constexpr int NT = D * 4;       // threads
     __shared__ float s_ew[TB][D], s_a[TB][D], s_b[TB][D], s_k[TB][D], s_r[TB][D], s_v[TB][D];
     __shared__ int s_upd[TB];
+    __shared__ float s_gate[TB], s_beta[TB], s_iq[TB], s_ik[TB];
 
     const int bh = blockIdx.x;
     // Sequence sq: tokens [tok0, tok0 + Tn) of the token axis (packed form:
@@ -53,6 +60,8 @@ __global__ __launch_bounds__(D * 4) void recurrent_kernel(
     if (state_map) {
         sidx = state_map[sq];
         if (sidx < 0 || sidx >= n_state) sidx = -1;
+    } else if (n_state == 1) {
+        sidx = 0;   // one initial state shared by every sequence
     }
     const int tid = threadIdx.x;
     const int wave = tid / kWave, lane = tid % kWave;
@@ -73,22 +82,70 @@ __global__ __launch_bounds__(D * 4) void recurrent_kernel(
     for (int t0 = 0; t0 < Tn; t0 += TB) {
         const int nt = min(TB, Tn - t0);
         __syncthreads();
-        for (int idx = tid; idx < TB * D; idx += NT) {
-            const int tl = idx / D, c = idx % D;
-            float ew = 1.f, av = 0.f, bv = 0.f, kv = 0.f, rv = 0.f, vv = 0.f;
-            if (tl < nt) {
-                const size_t gi = ((tok0 + t0 + tl) * H + h) * D + c;
-                ew = __expf(io<T_IO>::load(w, gi));
-                av = io<T_IO>::load(a, gi);
-                bv = io<T_IO>::load(b, gi);
-                kv = io<T_IO>::load(k, gi);
-                rv = io<T_IO>::load(r, gi);
-                vv = io<T_IO>::load(v, gi);
+        if constexpr (GDN) {
+            // stage q, k, v and the per-token gate and strength
+            for (int idx = tid; idx < TB * D; idx += NT) {
+                const int tl = idx / D, c = idx % D;
+                float qv = 0.f, kv = 0.f, vv = 0.f;
+                if (tl < nt) {
+                    const size_t gi = ((tok0 + t0 + tl) * H + h) * D + c;
+                    qv = io<T_IO>::load(r, gi);
+                    kv = io<T_IO>::load(k, gi);
+                    vv = io<T_IO>::load(v, gi);
+                }
+                s_r[tl][c] = qv; s_b[tl][c] = kv; s_v[tl][c] = vv;
             }
-            s_ew[tl][c] = ew; s_a[tl][c] = av; s_b[tl][c] = bv;
-            s_k[tl][c] = kv; s_r[tl][c] = rv; s_v[tl][c] = vv;
+            if (tid < TB) {
+                const size_t si = (tok0 + t0 + min(tid, nt - 1)) * H + h;
+                s_gate[tid] = io<T_IO>::load(w, si);
+                s_beta[tid] = io<T_IO>::load(a, si);
+                s_upd[tid] = tid < nt;
+            }
+            __syncthreads();
+            // norms: four lanes per token, each over a quarter of the channels
+            if (tid < 4 * TB) {
+                const int tl = tid >> 2, part = tid & 3;
+                float nq = 0.f, nk = 0.f;
+                for (int c = part; c < D; c += 4) {
+                    nq = fmaf(s_r[tl][c], s_r[tl][c], nq);
+                    nk = fmaf(s_b[tl][c], s_b[tl][c], nk);
+                }
+                nq += __shfl_xor(nq, 1, kWave); nq += __shfl_xor(nq, 2, kWave);
+                nk += __shfl_xor(nk, 1, kWave); nk += __shfl_xor(nk, 2, kWave);
+                if (part == 0) {
+                    s_iq[tl] = 1.0f / sqrtf(nq + 1e-6f);
+                    s_ik[tl] = 1.0f / sqrtf(nk + 1e-6f);
+                }
+            }
+            __syncthreads();
+            for (int idx = tid; idx < TB * D; idx += NT) {
+                const int tl = idx / D, c = idx % D;
+                const float kn = s_b[tl][c] * s_ik[tl];
+                const float eg = __expf(s_gate[tl]);
+                s_r[tl][c] *= s_iq[tl];
+                s_b[tl][c] = kn;
+                s_k[tl][c] = s_beta[tl] * kn;
+                s_a[tl][c] = -eg * s_beta[tl] * kn;
+                s_ew[tl][c] = eg;
+            }
+        } else {
+            for (int idx = tid; idx < TB * D; idx += NT) {
+                const int tl = idx / D, c = idx % D;
+                float ew = 1.f, av = 0.f, bv = 0.f, kv = 0.f, rv = 0.f, vv = 0.f;
+                if (tl < nt) {
+                    const size_t gi = ((tok0 + t0 + tl) * H + h) * D + c;
+                    ew = __expf(io<T_IO>::load(w, gi));
+                    av = io<T_IO>::load(a, gi);
+                    bv = io<T_IO>::load(b, gi);
+                    kv = io<T_IO>::load(k, gi);
+                    rv = io<T_IO>::load(r, gi);
+                    vv = io<T_IO>::load(v, gi);
+                }
+                s_ew[tl][c] = ew; s_a[tl][c] = av; s_b[tl][c] = bv;
+                s_k[tl][c] = kv; s_r[tl][c] = rv; s_v[tl][c] = vv;
+            }
+            if (tid < TB) s_upd[tid] = (tid < nt) && (mask ? mask[tok0 + t0 + tid] != 0 : 1);
         }
-        if (tid < TB) s_upd[tid] = (tid < nt) && (mask ? mask[tok0 + t0 + tid] != 0 : 1);
         __syncthreads();
 
         for (int tl = 0; tl < nt; ++tl) {
@@ -133,7 +190,14 @@ template <int D, typename T_IO>
 static hipError_t launch_rec(const FwdArgs &p, hipStream_t stream)
 {
     const dim3 grid((unsigned)(p.B * p.H)), block(D * 4);
-    hipLaunchKernelGGL((recurrent_kernel<D, T_IO>), grid, block, 0, stream, p.T, p.H, p.cu_seqlens,
+    if (p.gdn) {
+        hipLaunchKernelGGL((recurrent_kernel<D, T_IO, true>), grid, block, 0, stream, p.T, p.H, p.cu_seqlens,
+                           p.state_map, p.n_state,
+                           (const T_IO *)p.r, (const T_IO *)p.w, (const T_IO *)p.k, (const T_IO *)p.v,
+                           (const T_IO *)p.a, (const T_IO *)p.b, p.s0, p.mask, (T_IO *)p.o, p.sf);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((recurrent_kernel<D, T_IO, false>), grid, block, 0, stream, p.T, p.H, p.cu_seqlens,
                        p.state_map, p.n_state,
                        (const T_IO *)p.r, (const T_IO *)p.w, (const T_IO *)p.k, (const T_IO *)p.v,
                        (const T_IO *)p.a, (const T_IO *)p.b, p.s0, p.mask, (T_IO *)p.o, p.sf);

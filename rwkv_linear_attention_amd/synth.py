@@ -100,6 +100,33 @@ def make(workload, B=None, T=None, H=None, K=None, seed=None, init=None, mask=No
     return out
 
 
+def make_gdn(B, T, H, K, seed, dtype="bf16", init=False, n_state=None):
+    """Draw one Gated DeltaNet workload (rwkv-ops README, section
+    "gdn_recurrent 使用方法": q, k [B,T,H,K], v [B,T,H,V], g and beta [B,T,H],
+    initial_state [B or 1,H,K,V]).
+
+    Value recipe: q, k, v ~ N(0, 1) (raw: the operator normalises q and k);
+    g = clip(-exp(N(-1.5, 0.75)), -8, -1e-3) (log-space gate, <= 0);
+    beta = sigmoid(N(0, 1)) in (0, 1); initial_state ~ N(0, 0.1) fp32 with
+    n_state rows (B by default) when init is set.  Draw order from
+    numpy.random.default_rng(seed): q, k, v, g, beta, initial_state; all
+    rounded to the I/O dtype except the fp32 state."""
+    rng = np.random.default_rng(seed)
+    f = np.float32
+    shp = (B, T, H, K)
+    q = rng.standard_normal(shp, dtype=f)
+    k = rng.standard_normal(shp, dtype=f)
+    v = rng.standard_normal(shp, dtype=f)
+    g = np.clip(-np.exp(rng.standard_normal((B, T, H), dtype=f) * f(0.75) - f(1.5)), f(-8.0), f(-1e-3))
+    beta = (1.0 / (1.0 + np.exp(-rng.standard_normal((B, T, H), dtype=f)))).astype(f)
+    ns = B if n_state is None else n_state
+    s0 = (rng.standard_normal((ns, H, K, K), dtype=f) * f(0.1)) if init else None
+    out = dict(dtype=dtype, s0=s0)
+    for name, x in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
+        out[name] = round_to(x, dtype)
+    return out
+
+
 def to_torch(x, dtype, device):
     """Move an array holding I/O-dtype values to a torch tensor of that dtype."""
     import torch

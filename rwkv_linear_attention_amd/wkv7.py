@@ -34,6 +34,8 @@ def lib():
     L.wkv7_fwd.restype = i
     L.wkv7_fwd_varlen.argtypes = [i, i, i, i, i, i, p] + [p] * 7 + [i, p, p, p, p, i, p]
     L.wkv7_fwd_varlen.restype = i
+    L.wkv7_gdn_fwd.argtypes = [i, i, i, i, i, i] + [p] * 6 + [i, p, p, i, p]
+    L.wkv7_gdn_fwd.restype = i
     L.wkv7_step.argtypes = [i, i, i, i, i] + [p] * 8 + [p]
     L.wkv7_step.restype = i
     L.wkv7_strerror.argtypes = [i]
@@ -173,6 +175,40 @@ def fwd_varlen(r, w, k, v, a, b, cu_seqlens, initial_state=None, state_map=None,
     if st != OK:
         raise WKV7Error(st)
     return (o.unsqueeze(0) if lead1 else o), sf
+
+
+def gdn_fwd(q, k, v, g, beta, initial_state=None, output_final_state=True, algo=ALGO_AUTO,
+            out=None, final_state=None):
+    """Gated DeltaNet forward (q, k L2-normalised inside; gated delta rule).
+    q, k: [B,T,H,K]; v: [B,T,H,V]; g, beta: [B,T,H] (one dtype, float32 or
+    bfloat16); initial_state: [B,H,K,V] or [1,H,K,V] float32 (shared) or
+    None.  Returns (o [B,T,H,V], final_state [B,H,K,V] float32 or None)."""
+    dev = q.device
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    dt = q.dtype
+    code = _dtype_code(dt)
+    _check(k, "k", (B, T, H, K), dt, dev)
+    _check(v, "v", (B, T, H, V), dt, dev)
+    _check(g, "g", (B, T, H), dt, dev)
+    _check(beta, "beta", (B, T, H), dt, dev)
+    n_state = 0
+    if initial_state is not None:
+        n_state = initial_state.shape[0]
+        if n_state not in (1, B):
+            raise ValueError(f"initial_state must have {B} or 1 rows, got {n_state}")
+        _check(initial_state, "initial_state", (n_state, H, K, V), torch.float32, dev)
+    o = out if out is not None else torch.empty((B, T, H, V), dtype=dt, device=dev)
+    _check(o, "out", (B, T, H, V), dt, dev)
+    sf = None
+    if output_final_state:
+        sf = final_state if final_state is not None else torch.empty((B, H, K, V), dtype=torch.float32, device=dev)
+        _check(sf, "final_state", (B, H, K, V), torch.float32, dev)
+    st = lib().wkv7_gdn_fwd(code, B, T, H, K, V, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                            _ptr(initial_state), n_state, _ptr(o), _ptr(sf), int(algo), _stream(dev))
+    if st != OK:
+        raise WKV7Error(st)
+    return o, sf
 
 
 def step(r, w, k, v, a, b, state, out=None):

@@ -27,14 +27,14 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert {"wkv7_fwd", "wkv7_fwd_varlen", "wkv7_step", "wkv7_strerror", "wkv7_fwd_path",
+    assert {"wkv7_fwd", "wkv7_fwd_varlen", "wkv7_gdn_fwd", "wkv7_step", "wkv7_strerror", "wkv7_fwd_path",
             "wkv7_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"{n} declared in wkv7.h but not exported"
 
 
 def test_version_and_strerror(L):
-    assert L.wkv7_version() == 101
+    assert L.wkv7_version() == 102
     for code in range(4):
         assert len(L.wkv7_strerror(code)) > 0
     assert L.wkv7_strerror(99) == b"unknown status"
@@ -147,3 +147,35 @@ def test_varlen_accepts_empty_token_axis_without_launch_checks(L):
     # total_T == 0 needs no token buffers; the call would launch (so only the
     # argument checks are exercised here: a NULL token pointer is not an error)
     assert varlen(L, TT=0, ptrs=[None] * 7, cu=None) == wkv7.ERR_INVALID_ARG   # cu_seqlens still required
+
+
+def gdn(L, dtype=1, B=2, T=4, H=1, K=64, V=64, ptrs=None, s0=None, n_state=0, sf=None, algo=0):
+    ptrs = ptrs or [GOOD] * 6
+    q, k, v, g, beta, o = ptrs
+    return L.wkv7_gdn_fwd(dtype, B, T, H, K, V, q, k, v, g, beta, s0, n_state, o, sf, algo, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), wkv7.ERR_INVALID_ARG),
+    (dict(T=-1), wkv7.ERR_INVALID_ARG),
+    (dict(dtype=3), wkv7.ERR_INVALID_ARG),
+    (dict(K=64, V=128), wkv7.ERR_UNSUPPORTED),
+    (dict(dtype=0, algo=2), wkv7.ERR_UNSUPPORTED),
+    (dict(algo=9), wkv7.ERR_INVALID_ARG),
+    (dict(s0=GOOD, n_state=0), wkv7.ERR_INVALID_ARG),            # state rows must be 1 or B
+    (dict(s0=GOOD, n_state=3), wkv7.ERR_INVALID_ARG),
+    (dict(s0=GOOD, n_state=1, sf=GOOD), wkv7.ERR_INVALID_ARG),   # shared state overwritten by finals
+    (dict(s0=ODD, n_state=2), wkv7.ERR_INVALID_ARG),
+    (dict(sf=ODD), wkv7.ERR_INVALID_ARG),
+])
+def test_gdn_validation(L, kw, code):
+    assert gdn(L, **kw) == code
+
+
+@pytest.mark.parametrize("slot", range(6))
+def test_gdn_rejects_null_and_misaligned(L, slot):
+    ptrs = [GOOD] * 6
+    ptrs[slot] = None
+    assert gdn(L, ptrs=ptrs) == wkv7.ERR_INVALID_ARG
+    ptrs[slot] = ODD
+    assert gdn(L, ptrs=ptrs) == wkv7.ERR_INVALID_ARG
