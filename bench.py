@@ -85,11 +85,31 @@ def cpu_baseline(inp, H, T, budget_s=12.0, max_threads=16):
                       f"{len(pairs)} sequences of the workload; fp64 C, OpenMP), {t_used:.1f} s"}
 
 
+SETTLE_MS = 100.0
+
+
+def settle(fn, ms=SETTLE_MS):
+    """Run fn (untimed) until `ms` of wall time have passed; returns the call
+    count.  From idle the GPU raises its clocks over the first ~25 ms of
+    sustained work (the B8 T4096 d64 forward measured 0.60 ms per launch in
+    its first 10 launches, 0.40 ms from about the 60th on), so a few warmup
+    steps alone would time the ramp rather than the kernel."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        n += 5
+    return n
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--all", action="store_true",
                     help="also time the head-size-128 workload, a packed variable-length batch and the "
@@ -137,10 +157,11 @@ def main():
         wkv7.fwd(dev["r"], dev["w"], dev["k"], dev["v"], dev["a"], dev["b"],
                  out=o, final_state=sf)
 
+    n_settle = settle(step)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    print(f"[bench] warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
+    print(f"[bench] clock settle ({n_settle} steps) and warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     t_all0 = torch.cuda.Event(enable_timing=True)
     t_all1 = torch.cuda.Event(enable_timing=True)
@@ -168,6 +189,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_settle": {"ms": SETTLE_MS, "steps": n_settle},
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -281,6 +303,7 @@ def gdn_workload(steps, warmup):
 
 def _time_launches(fn, steps, warmup):
     import torch
+    settle(lambda: fn(0))
     for _ in range(warmup):
         fn(0)
     torch.cuda.synchronize()
@@ -348,6 +371,8 @@ def other_workloads(steps, warmup):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1)
 
+    settle(lambda: wkv7.step(per_step[0]["r"], per_step[0]["w"], per_step[0]["k"], per_step[0]["v"],
+                             per_step[0]["a"], per_step[0]["b"], state, out=obuf))
     run(0)
     times = [run(i) for i in range(3)]
     ms_total = min(times)
