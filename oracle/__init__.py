@@ -1,5 +1,5 @@
-"""fp64 CPU oracle for the RWKV-7 WKV7 forward and the Gated DeltaNet forward
--- TEST INFRASTRUCTURE ONLY.
+"""fp64 CPU oracle for the RWKV-7 WKV7 forward, its backward and the Gated
+DeltaNet forward -- TEST INFRASTRUCTURE ONLY.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  The HIP product path never imports it,
@@ -47,6 +47,8 @@ def _load():
     lib.wkv7_oracle_fwd.restype = i
     lib.wkv7_oracle_step.argtypes = [i, i, i, i] + [d] * 8
     lib.wkv7_oracle_step.restype = i
+    lib.wkv7_oracle_bwd.argtypes = [i, i, i, i, i] + [d] * 17
+    lib.wkv7_oracle_bwd.restype = i
     lib.gdn_oracle_fwd.argtypes = [i, i, i, i, i] + [d] * 6 + [i, d, d]
     lib.gdn_oracle_fwd.restype = i
     lib.wkv7_oracle_max_threads.restype = i
@@ -88,6 +90,39 @@ def fwd(r, w, k, v, a, b, initial_state=None, mask=None):
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return o, sf
+
+
+def bwd(r, w, k, v, a, b, d_o, initial_state=None, mask=None, d_final_state=None):
+    """Backward of fwd (reverse-mode derivative of the same recurrence; see
+    the C file).  d_o: [B,T,H,V] gradient of the output; d_final_state:
+    [B,H,K,V] or None (zero).  Returns a dict of float64 gradients r, w, k, v,
+    a, b (input shapes) and s0 ([B,H,K,V])."""
+    lib = _load()
+    r, w, k, v, a, b, d_o = (_f64(x) for x in (r, w, k, v, a, b, d_o))
+    B, T, H, K = r.shape
+    V = v.shape[-1]
+    for x in (w, k, a, b):
+        assert x.shape == (B, T, H, K)
+    assert v.shape == (B, T, H, V) and d_o.shape == (B, T, H, V)
+    s0 = None if initial_state is None else _f64(initial_state)
+    if s0 is not None:
+        assert s0.shape == (B, H, K, V)
+    dsf = None if d_final_state is None else _f64(d_final_state)
+    if dsf is not None:
+        assert dsf.shape == (B, H, K, V)
+    m = None
+    if mask is not None:
+        m = np.ascontiguousarray((np.asarray(mask) != 0).astype(np.uint8))
+        assert m.shape == (B, T)
+    g = {n: np.zeros((B, T, H, K), np.float64) for n in ("r", "w", "k", "a", "b")}
+    g["v"] = np.zeros((B, T, H, V), np.float64)
+    g["s0"] = np.zeros((B, H, K, V), np.float64)
+    rc = lib.wkv7_oracle_bwd(B, T, H, K, V, _ptr(r), _ptr(w), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
+                             _ptr(s0), _ptr(m), _ptr(d_o), _ptr(dsf),
+                             *(_ptr(g[n]) for n in ("r", "w", "k", "v", "a", "b", "s0")))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments" if rc == -1 else "oracle ran out of memory")
+    return g
 
 
 def step(r, w, k, v, a, b, state):

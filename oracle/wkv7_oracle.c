@@ -37,8 +37,10 @@
  *   r,w,k,a,b : [B][T][H][K]     v, o : [B][T][H][V]
  *   state     : [B][H][K][V]     mask : [B][T] uint8
  *
- * Parity pins (closed forms, invariants and a hand-worked example) live in
- * tests/test_oracle_pins.py; every function here is pinned by them.
+ * Parity pins (closed forms, invariants, hand-worked examples, finite
+ * differences) live in tests/test_oracle_pins.py (forward and step),
+ * tests/test_oracle_bwd_pins.py (backward) and tests/test_oracle_gdn_pins.py
+ * (Gated DeltaNet); every function here is pinned by them.
  */
 #include <math.h>
 #include <stdint.h>
@@ -140,6 +142,138 @@ int wkv7_oracle_step(int B, int H, int K, int V,
         free(sb);
     }
     return 0;
+}
+
+/* ------------------------------------------------------------------------
+ * Backward of the forward above: the reverse-mode derivative of the same
+ * recurrence (the rwkv-ops README lists generalized_delta_rule as the
+ * trainable entry, section "rwkv7op 使用方法"; the derivative itself is not
+ * on the pages and follows from the recurrence by the chain rule).
+ *
+ * Given d_o = dL/do [B][T][H][V] and d_sf = dL/dS_T [B][H][K][V] (NULL for
+ * zero), it returns dL/d{r,w,k,v,a,b} and dL/dS_0.  With S_{t-1} the state
+ * before token t and S_t the state after it:
+ *
+ *   dS  <- d_sf
+ *   for t = T-1 .. 0:
+ *     dS     += r_t d_o_t^T                      (o_t = S_t^T r_t)
+ *     dr_t    = S_t d_o_t
+ *     if token t updates:
+ *       sb      = S_{t-1}^T b_t,   ad = dS^T a_t
+ *       dk_t    = dS v_t,          dv_t = dS^T k_t
+ *       da_t    = dS sb,           db_t = S_{t-1} ad
+ *       dw_t[i] = exp(w_t[i]) sum_j dS[i][j] S_{t-1}[i][j]
+ *       dS      = diag(exp(w_t)) dS + b_t ad^T   (dL/dS_{t-1})
+ *     else: dw, dk, dv, da, db of token t are 0 and dS passes through
+ *   d_s0 = dS
+ *
+ * Every state S_0 .. S_T of a sequence is kept (T+1 K x V fp64 matrices per
+ * sequence), so memory grows with T.  d_s0 may be NULL. */
+int wkv7_oracle_bwd(int B, int T, int H, int K, int V,
+                    const double *r, const double *w, const double *k,
+                    const double *v, const double *a, const double *b,
+                    const double *s0, const uint8_t *mask,
+                    const double *d_o, const double *d_sf,
+                    double *dr, double *dw, double *dk, double *dv,
+                    double *da, double *db, double *d_s0)
+{
+    if (B < 0 || T < 0 || H < 0 || K <= 0 || V <= 0) return -1;
+    if (T > 0 && (!r || !w || !k || !v || !a || !b || !d_o || !dr || !dw || !dk || !dv || !da || !db))
+        return -1;
+    const long long nseq = (long long)B * H;
+    const size_t KV = (size_t)K * V;
+    int failed = 0;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long long bh = 0; bh < nseq; ++bh) {
+        const int bb = (int)(bh / H), h = (int)(bh % H);
+        double *S = (double *)malloc(sizeof(double) * KV * ((size_t)T + 1));
+        double *dS = (double *)malloc(sizeof(double) * KV);
+        double *vec = (double *)malloc(sizeof(double) * (size_t)(V > K ? V : K) * 2);
+        if (!S || !dS || !vec) {
+            failed = 1;
+            free(S); free(dS); free(vec);
+            continue;
+        }
+        double *sb = vec, *ad = vec + (V > K ? V : K);
+        /* forward, keeping every state: S + t*KV is S_t */
+        if (s0)
+            memcpy(S, &s0[IDX_ST(bb, h, 0, 0, H, K, V)], sizeof(double) * KV);
+        else
+            memset(S, 0, sizeof(double) * KV);
+        for (int t = 0; t < T; ++t) {
+            const int upd = mask ? (mask[(size_t)bb * T + t] != 0) : 1;
+            memcpy(S + (size_t)(t + 1) * KV, S + (size_t)t * KV, sizeof(double) * KV);
+            double *o_unused = sb;   /* the forward's output is not needed here */
+            one_token(K, V, S + (size_t)(t + 1) * KV,
+                      &r[IDX_TOK(bb, t, h, 0, T, H, K)], &w[IDX_TOK(bb, t, h, 0, T, H, K)],
+                      &k[IDX_TOK(bb, t, h, 0, T, H, K)], &v[IDX_TOK(bb, t, h, 0, T, H, V)],
+                      &a[IDX_TOK(bb, t, h, 0, T, H, K)], &b[IDX_TOK(bb, t, h, 0, T, H, K)],
+                      upd, o_unused, ad);
+        }
+        /* reverse */
+        if (d_sf)
+            memcpy(dS, &d_sf[IDX_ST(bb, h, 0, 0, H, K, V)], sizeof(double) * KV);
+        else
+            memset(dS, 0, sizeof(double) * KV);
+        for (int t = T - 1; t >= 0; --t) {
+            const int upd = mask ? (mask[(size_t)bb * T + t] != 0) : 1;
+            const double *St = S + (size_t)(t + 1) * KV, *Sp = S + (size_t)t * KV;
+            const double *rt = &r[IDX_TOK(bb, t, h, 0, T, H, K)], *wt = &w[IDX_TOK(bb, t, h, 0, T, H, K)];
+            const double *kt = &k[IDX_TOK(bb, t, h, 0, T, H, K)], *vt = &v[IDX_TOK(bb, t, h, 0, T, H, V)];
+            const double *at = &a[IDX_TOK(bb, t, h, 0, T, H, K)], *bt = &b[IDX_TOK(bb, t, h, 0, T, H, K)];
+            const double *dot = &d_o[IDX_TOK(bb, t, h, 0, T, H, V)];
+            double *drt = &dr[IDX_TOK(bb, t, h, 0, T, H, K)], *dwt = &dw[IDX_TOK(bb, t, h, 0, T, H, K)];
+            double *dkt = &dk[IDX_TOK(bb, t, h, 0, T, H, K)], *dvt = &dv[IDX_TOK(bb, t, h, 0, T, H, V)];
+            double *dat = &da[IDX_TOK(bb, t, h, 0, T, H, K)], *dbt = &db[IDX_TOK(bb, t, h, 0, T, H, K)];
+            for (int i = 0; i < K; ++i)
+                for (int j = 0; j < V; ++j) dS[(size_t)i * V + j] += rt[i] * dot[j];
+            for (int i = 0; i < K; ++i) {
+                double acc = 0.0;
+                for (int j = 0; j < V; ++j) acc += St[(size_t)i * V + j] * dot[j];
+                drt[i] = acc;
+            }
+            if (!upd) {
+                for (int i = 0; i < K; ++i) dwt[i] = dkt[i] = dat[i] = dbt[i] = 0.0;
+                for (int j = 0; j < V; ++j) dvt[j] = 0.0;
+                continue;
+            }
+            for (int j = 0; j < V; ++j) {
+                double s1 = 0.0, s2 = 0.0, s3 = 0.0;
+                for (int i = 0; i < K; ++i) {
+                    s1 += bt[i] * Sp[(size_t)i * V + j];
+                    s2 += at[i] * dS[(size_t)i * V + j];
+                    s3 += kt[i] * dS[(size_t)i * V + j];
+                }
+                sb[j] = s1;
+                ad[j] = s2;
+                dvt[j] = s3;
+            }
+            for (int i = 0; i < K; ++i) {
+                double ck = 0.0, ca = 0.0, cb = 0.0, cw = 0.0;
+                for (int j = 0; j < V; ++j) {
+                    const double g = dS[(size_t)i * V + j], sp = Sp[(size_t)i * V + j];
+                    ck += g * vt[j];
+                    ca += g * sb[j];
+                    cb += sp * ad[j];
+                    cw += g * sp;
+                }
+                dkt[i] = ck;
+                dat[i] = ca;
+                dbt[i] = cb;
+                dwt[i] = exp(wt[i]) * cw;
+            }
+            for (int i = 0; i < K; ++i) {
+                const double d = exp(wt[i]);
+                for (int j = 0; j < V; ++j) dS[(size_t)i * V + j] = d * dS[(size_t)i * V + j] + bt[i] * ad[j];
+            }
+        }
+        if (d_s0) memcpy(&d_s0[IDX_ST(bb, h, 0, 0, H, K, V)], dS, sizeof(double) * KV);
+        free(vec);
+        free(dS);
+        free(S);
+    }
+    return failed ? -2 : 0;
 }
 
 /* ------------------------------------------------------------------------
