@@ -34,6 +34,7 @@
 #ifndef WKV7_H
 #define WKV7_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -173,6 +174,49 @@ wkv7_status_t wkv7_gdn_fwd(int dtype, int B, int T, int H, int K, int V,
                            void *o, float *final_state, int algo, void *stream);
 
 /*
+ * wkv7_bwd -- gradients of wkv7_fwd (rwkv-ops README, section
+ * "rwkv7op 使用方法": generalized_delta_rule is the trainable entry; the
+ * derivative follows from the recurrence by the chain rule).  For upstream
+ * gradients d_o (of every output) and d_final_state (of the final state) it
+ * returns the gradients of r, w, k, v, a, b and of the initial state.  A
+ * token whose mask byte is 0 receives zero gradient for w, k, v, a and b
+ * (its r still receives S_{t-1} d_o_t).  The forward is recomputed inside
+ * (fp32 state checkpoints every 16 tokens), so only the forward's inputs are
+ * needed; all arithmetic is fp32, also for bf16 I/O.
+ *
+ *   dtype          WKV7_F32 or WKV7_BF16: element type of r,w,k,v,a,b, d_o
+ *                  and of the gradients dr..db.
+ *   B,T,H,K,V      as for wkv7_fwd; K == V in {64, 128}.
+ *   r,w,k,v,a,b    the forward's inputs, as for wkv7_fwd.  Read only.
+ *   initial_state  [B,H,K,V] fp32 or NULL (zeros).  Read only.
+ *   mask           [B,T] uint8 or NULL.  Read only.
+ *   d_o            [B,T,H,V] dtype.  Read only.
+ *   d_final_state  [B,H,K,V] fp32 or NULL (zero).  Read only.
+ *   dr,dw,dk,da,db [B,T,H,K] dtype; dv [B,T,H,V] dtype.  Written (every element).
+ *   d_initial_state [B,H,K,V] fp32 or NULL (not written).  Written.
+ *   workspace      DEVICE buffer of at least wkv7_bwd_workspace_bytes(B,T,H,K,V)
+ *                  bytes, 16-byte aligned, owned by the caller; contents on
+ *                  entry are ignored and on return are unspecified.  May be
+ *                  NULL when T == 0.
+ *   stream         hipStream_t to enqueue on.
+ * Output buffers must not overlap any input or each other.  With T == 0,
+ * d_initial_state receives d_final_state (zeros when NULL).
+ */
+wkv7_status_t wkv7_bwd(int dtype, int B, int T, int H, int K, int V,
+                       const void *r, const void *w, const void *k,
+                       const void *v, const void *a, const void *b,
+                       const float *initial_state, const uint8_t *mask,
+                       const void *d_o, const float *d_final_state,
+                       void *dr, void *dw, void *dk, void *dv, void *da, void *db,
+                       float *d_initial_state, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+/* Workspace bytes wkv7_bwd needs: 4 B (2 ceil(T/16) + 1) H K V (two fp32
+ * states per 16-token chunk and sequence, plus one), or 0 for arguments
+ * wkv7_bwd would reject. */
+size_t wkv7_bwd_workspace_bytes(int B, int T, int H, int K, int V);
+
+/*
  * wkv7_step -- one decode token per sequence, state updated in place
  * (section "rwkv7_op_rnn 使用方法": the T = 1 case of the forward).
  *
@@ -198,7 +242,7 @@ const char *wkv7_strerror(int status);
 int wkv7_fwd_path(int dtype, int B, int T, int H, int K, int V, int algo);
 
 /* ABI version of this header (major * 100 + minor): 101 adds wkv7_fwd_varlen,
- * 102 adds wkv7_gdn_fwd. */
+ * 102 adds wkv7_gdn_fwd, 103 adds wkv7_bwd and wkv7_bwd_workspace_bytes. */
 int wkv7_version(void);
 
 #ifdef __cplusplus

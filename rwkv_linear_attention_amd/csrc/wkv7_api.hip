@@ -40,7 +40,7 @@ int choose_path(int dtype, int T, int algo)
 
 extern "C" {
 
-int wkv7_version(void) { return 102; }
+int wkv7_version(void) { return 103; }
 
 const char *wkv7_strerror(int status)
 {
@@ -180,6 +180,46 @@ wkv7_status_t wkv7_gdn_fwd(int dtype, int B, int T, int H, int K, int V,
     hipError_t e = path == WKV7_ALGO_CHUNKED ? wkv7::launch_chunked(args, s)
                                              : wkv7::launch_recurrent(dtype, args, s);
     return e == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
+}
+
+size_t wkv7_bwd_workspace_bytes(int B, int T, int H, int K, int V)
+{
+    if (check_common(WKV7_F32, B, H, K, V) != WKV7_OK || T < 0) return 0;
+    return wkv7::bwd_workspace_bytes(B, T, H, K);
+}
+
+wkv7_status_t wkv7_bwd(int dtype, int B, int T, int H, int K, int V,
+                       const void *r, const void *w, const void *k,
+                       const void *v, const void *a, const void *b,
+                       const float *initial_state, const uint8_t *mask,
+                       const void *d_o, const float *d_final_state,
+                       void *dr, void *dw, void *dk, void *dv, void *da, void *db,
+                       float *d_initial_state, void *workspace, size_t workspace_bytes,
+                       void *stream)
+{
+    wkv7_status_t st = check_common(dtype, B, H, K, V);
+    if (st != WKV7_OK) return st;
+    if (T < 0) return WKV7_ERR_INVALID_ARG;
+    if ((long long)B * T * H * K > (1ll << 40)) return WKV7_ERR_UNSUPPORTED;
+    if (T > 0) {
+        const void *req[] = {r, w, k, v, a, b, d_o, dr, dw, dk, dv, da, db, workspace};
+        for (const void *p : req)
+            if (!p || !aligned16(p)) return WKV7_ERR_INVALID_ARG;
+        if (workspace_bytes < wkv7::bwd_workspace_bytes(B, T, H, K)) return WKV7_ERR_INVALID_ARG;
+    }
+    const void *opt[] = {initial_state, d_final_state, d_initial_state};
+    for (const void *p : opt)
+        if (p && !aligned16(p)) return WKV7_ERR_INVALID_ARG;
+
+    hipStream_t s = (hipStream_t)stream;
+    if (T == 0) {
+        if (!d_initial_state) return WKV7_OK;
+        const size_t n = (size_t)B * H * K * V;
+        return wkv7::launch_state_copy(d_final_state, d_initial_state, n, s) == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
+    }
+    wkv7::BwdArgs args{B, T, H, K, r, w, k, v, a, b, initial_state, mask, d_o, d_final_state,
+                       dr, dw, dk, dv, da, db, d_initial_state, workspace};
+    return wkv7::launch_backward(dtype, args, s) == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
 }
 
 wkv7_status_t wkv7_step(int dtype, int B, int H, int K, int V,

@@ -1,0 +1,499 @@
+// Backward of the WKV7 forward: gradients of r, w, k, v, a, b and of the
+// initial state for upstream gradients d_o (of every output) and d_sf (of
+// the final state).
+//
+// The recurrence (rwkv-ops README, section "rwkv7op 使用方法", which lists
+// generalized_delta_rule as the trainable entry; update read as the
+// generalized delta rule) is, per (b, h) and updating token t,
+//   S_t = diag(e^{w_t}) S_{t-1} + a_t (b_t^T S_{t-1}) + k_t v_t^T,  o_t = S_t^T r_t.
+// Its reverse-mode derivative carries dS = dL/dS_t backwards:
+//   dS += r_t d_o_t^T;   dS_{t-1} = diag(e^{w_t}) dS + b_t (a_t^T dS).
+//
+// Three launches, with a caller-provided workspace and no allocation:
+//  1. the recurrent forward kernel in fp32 writes the state before every
+//     16-token chunk and after the last one (checkpoints);
+//  2. dstate_chain_kernel runs the dS recurrence backwards in fp32 (one
+//     workgroup per (b, h)) and stores, for every chunk, the gradient of the
+//     state at the chunk's end with respect to everything after the chunk;
+//  3. chunk_grad_kernel (one workgroup per (b, h, chunk), all chunks in
+//     parallel) recomputes the chunk in its unrolled form from the chunk's
+//     checkpoint and turns that end gradient into the token gradients.
+//
+// Chunk form (G the per-channel inclusive decay prefix inside the chunk,
+// G_{t-1} the exclusive one; R~ = r e^G, B~ = b e^{G_{t-1}}, A^ = a e^{-G},
+// K^ = k e^{-G}; M_xy the L x L products X Y^T, strictly lower for M_ba and
+// M_bk, lower with the diagonal for M_ra and M_rk; T = (I - M_ba)^{-1}):
+//   X = B~ S + M_bk V,  U = T X,  O = R~ S + M_ra U + M_rk V,
+//   S' = diag(e^{G_L}) (S + A^T U + K^T V).
+// Given dS' (the chunk-end gradient) and dO:
+//   dY = diag(e^{G_L}) dS',  dU = A^ dY + M_ra^T dO,  dX = T^T dU,
+//   dV = K^ dY + M_rk^T dO + M_bk^T dX,
+//   dM_ra = dO U^T, dM_rk = dO V^T, dM_ba = dX U^T, dM_bk = dX V^T (masked),
+//   dR~ = dO S^T + dM_ra A^ + dM_rk K^,   dB~ = dX S^T + dM_ba A^ + dM_bk K^,
+//   dA^ = U dY^T + dM_ra^T R~ + dM_ba^T B~, dK^ = V dY^T + dM_rk^T R~ + dM_bk^T B~,
+//   dr = dR~ e^G, db = dB~ e^{G_{t-1}}, da = dA^ e^{-G}, dk = dK^ e^{-G},
+//   dw_m = sum_{t >= m} (dr_t r_t - da_t a_t - dk_t k_t + db_{t+1} b_{t+1})
+//          + sum_j dS'[.,j] S'[.,j]     (the last term from the chunk end).
+// A chunk whose decay reaches e^{-60} on some channel, or with a positive w,
+// takes an exact token-by-token path instead (the split factors e^{-G} would
+// leave the fp32 range).  All arithmetic is fp32: the products run on the
+// fp32 matrix cores (v_mfma_f32_16x16x4_f32) over LDS tiles.
+#include "wkv7_common.hpp"
+#include "wkv7_internal.hpp"
+
+namespace wkv7 {
+namespace {
+
+constexpr int kL = 16;                  // chunk length (= checkpoint interval)
+constexpr float kMinChunkLogDecay = -60.0f;
+
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// acc (16 x 16) += A (16 x KC) B (KC x 16), elements fetched by fa(m, kk)
+// and fb(kk, n).  Lane l supplies A[l%16][kk0 + l/16] and B[kk0 + l/16][l%16]
+// per step; the result lane l holds rows 4(l/16) .. +3 of column l%16.
+template <int KC, class FA, class FB>
+__device__ __forceinline__ f32x4 mm16(f32x4 acc, FA fa, FB fb, int lane)
+{
+    const int m = lane & 15, q = lane >> 4;
+#pragma unroll
+    for (int k0 = 0; k0 < KC; k0 += 4) acc = mfma_f32(fa(m, k0 + q), fb(k0 + q, m), acc);
+    return acc;
+}
+
+// ---- 2. reverse state-gradient chain ------------------------------------------
+
+// One workgroup per (b, h), D/16 waves; lane (j, g) of wave w holds rows
+// [g D/4, (g+1) D/4) of column 16w + j of dS.  dck[bh][c] receives, for
+// chunk c, dL/dS at the chunk's last token from everything after it.
+template <int D, typename T_IO>
+__global__ __launch_bounds__(D * 4) void dstate_chain_kernel(
+    int T, int H, const T_IO *__restrict__ r, const T_IO *__restrict__ w, const T_IO *__restrict__ a,
+    const T_IO *__restrict__ b, const uint8_t *__restrict__ mask, const T_IO *__restrict__ d_o,
+    const float *__restrict__ d_sf, float *__restrict__ dck, float *__restrict__ d_s0)
+{
+    constexpr int TB = kL, RPL = D / 4, NT = D * 4;
+    __shared__ float s_ew[TB][D], s_a[TB][D], s_b[TB][D], s_r[TB][D], s_do[TB][D];
+    __shared__ int s_upd[TB];
+    const int bh = blockIdx.x, bb = bh / H, h = bh % H;
+    const size_t tok0 = (size_t)bb * T;
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int col = wave * 16 + (lane & 15), g = lane >> 4, row0 = g * RPL;
+    const size_t st = (size_t)bh * D * D;
+    float dS[RPL];
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) dS[i] = d_sf ? d_sf[st + (size_t)(row0 + i) * D + col] : 0.0f;
+    const int nck = (T + TB - 1) / TB;
+    for (int c = nck - 1; c >= 0; --c) {
+        const int t0 = c * TB, nt = min(TB, T - t0);
+        float *out = dck + ((size_t)bh * nck + c) * D * D;
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) out[(size_t)(row0 + i) * D + col] = dS[i];
+        __syncthreads();
+        for (int idx = tid; idx < TB * D; idx += NT) {
+            const int tl = idx / D, ch = idx % D;
+            float ew = 1.f, av = 0.f, bv = 0.f, rv = 0.f, dv = 0.f;
+            if (tl < nt) {
+                const size_t gi = ((tok0 + t0 + tl) * H + h) * D + ch;
+                ew = __expf(io<T_IO>::load(w, gi));
+                av = io<T_IO>::load(a, gi);
+                bv = io<T_IO>::load(b, gi);
+                rv = io<T_IO>::load(r, gi);
+                dv = io<T_IO>::load(d_o, gi);
+            }
+            s_ew[tl][ch] = ew; s_a[tl][ch] = av; s_b[tl][ch] = bv; s_r[tl][ch] = rv; s_do[tl][ch] = dv;
+        }
+        if (tid < TB) s_upd[tid] = (tid < nt) && (mask ? mask[tok0 + t0 + tid] != 0 : 1);
+        __syncthreads();
+        for (int tl = nt - 1; tl >= 0; --tl) {
+            const float doj = s_do[tl][col];
+#pragma unroll
+            for (int i = 0; i < RPL; ++i) dS[i] = fmaf(s_r[tl][row0 + i], doj, dS[i]);
+            if (s_upd[tl]) {
+                float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
+#pragma unroll
+                for (int i = 0; i < RPL; i += 4) {
+                    p0 += s_a[tl][row0 + i + 0] * dS[i + 0];
+                    p1 += s_a[tl][row0 + i + 1] * dS[i + 1];
+                    p2 += s_a[tl][row0 + i + 2] * dS[i + 2];
+                    p3 += s_a[tl][row0 + i + 3] * dS[i + 3];
+                }
+                float ad = (p0 + p1) + (p2 + p3);
+                ad = xor_sum(ad, 16);
+                ad = xor_sum(ad, 32);
+#pragma unroll
+                for (int i = 0; i < RPL; ++i) dS[i] = fmaf(s_ew[tl][row0 + i], dS[i], s_b[tl][row0 + i] * ad);
+            }
+        }
+    }
+    if (d_s0) {
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) d_s0[st + (size_t)(row0 + i) * D + col] = dS[i];
+    }
+}
+
+// ---- 3. per-chunk gradients -------------------------------------------------
+
+template <int D> struct GradLds {
+    static constexpr int LD = D + 1;    // padded row stride of the L x D tiles
+    float R[kL][LD], B[kL][LD], A[kL][LD], K[kL][LD], V[kL][LD], DO[kL][LD];
+    float G[kL][LD];                    // decay prefix
+    float W[kL][LD];                    // raw (masked) w, then X / dU
+    float U[kL][LD], DX[kL][LD];
+    float M[9][kL][kL + 1];             // M_ba, M_bk, M_ra, M_rk, T, dM_ra, dM_rk, dM_ba, dM_bk
+    float EGL[D];
+    float P[D / 16][2][kL][kL + 1];     // per-wave dG pieces
+    float RED[5][D / 16][D];            // exact path: per-wave row sums
+    int upd[kL];
+};
+
+enum { M_BA = 0, M_BK, M_RA, M_RK, M_T, DM_RA, DM_RK, DM_BA, DM_BK };
+
+// Exact path: tokens of the chunk in reverse, each step's gradients from the
+// per-token formulas (those of the oracle's derivative), with the states
+// S_{t-1} and S_t recomputed from the chunk's checkpoint.  Lane layout of the
+// recurrent kernel: lane (j, g) of wave w holds rows [g D/4, (g+1) D/4) of
+// column 16w + j.
+template <int D, typename T_IO>
+__device__ void chunk_grad_exact(GradLds<D> &s, const float *Sc, const float *dSe, int Lc, size_t tokbase,
+                                 int H, T_IO *dr, T_IO *dw, T_IO *dk, T_IO *dv, T_IO *da, T_IO *db)
+{
+    constexpr int RPL = D / 4, NW = D / 16;
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int col = wave * 16 + (lane & 15), g = lane >> 4, row0 = g * RPL;
+    auto colsum = [](float x) { return xor_sum(xor_sum(x, 16), 32); };
+    auto step = [&](float *P, int u) {   // P <- state after token u (P = state before it)
+        if (!s.upd[u]) return;
+        float sb = 0.f;
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) sb = fmaf(s.B[u][row0 + i], P[i], sb);
+        sb = colsum(sb);
+        const float vj = s.V[u][col];
+#pragma unroll
+        for (int i = 0; i < RPL; ++i)
+            P[i] = fmaf(__expf(s.W[u][row0 + i]), P[i], fmaf(s.A[u][row0 + i], sb, s.K[u][row0 + i] * vj));
+    };
+    float dS[RPL];
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) dS[i] = dSe[(size_t)(row0 + i) * D + col];
+    auto rowsum = [&](float y, int e, int row) {   // over the 16 columns of the wave
+        y += __shfl_xor(y, 1, kWave);
+        y += __shfl_xor(y, 2, kWave);
+        y += __shfl_xor(y, 4, kWave);
+        y += __shfl_xor(y, 8, kWave);
+        if ((lane & 15) == 0) s.RED[e][wave][row] = y;
+    };
+    for (int t = Lc - 1; t >= 0; --t) {
+        float P[RPL];   // S_{t-1}
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) P[i] = Sc[(size_t)(row0 + i) * D + col];
+        for (int u = 0; u < t; ++u) step(P, u);
+        const bool up = s.upd[t] != 0;
+        const float doj = s.DO[t][col], vj = s.V[t][col];
+        float sb = 0.f;
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) sb = fmaf(s.B[t][row0 + i], P[i], sb);
+        sb = colsum(sb);
+        // dr_t = S_t d_o_t with S_t formed element by element from S_{t-1}
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) {
+            const float st = up ? fmaf(__expf(s.W[t][row0 + i]), P[i], fmaf(s.A[t][row0 + i], sb, s.K[t][row0 + i] * vj))
+                                : P[i];
+            rowsum(st * doj, 0, row0 + i);
+        }
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) dS[i] = fmaf(s.R[t][row0 + i], doj, dS[i]);
+        float ad = 0.f, dvj = 0.f;
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) {
+            ad = fmaf(s.A[t][row0 + i], dS[i], ad);
+            dvj = fmaf(s.K[t][row0 + i], dS[i], dvj);
+        }
+        ad = colsum(ad);
+        dvj = colsum(dvj);
+        if (g == 0) io<T_IO>::store(dv, tokbase + (size_t)t * H * D + col, up ? dvj : 0.0f);
+        // row sums over this lane's column, then over the 16 columns of the
+        // wave, then (through LDS) over the waves
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) {
+            rowsum(dS[i] * vj, 1, row0 + i);
+            rowsum(dS[i] * sb, 2, row0 + i);
+            rowsum(P[i] * ad, 3, row0 + i);
+            rowsum(dS[i] * P[i], 4, row0 + i);
+        }
+        __syncthreads();
+        if (tid < D) {
+            float y[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+            for (int wv = 0; wv < NW; ++wv)
+#pragma unroll
+                for (int e = 0; e < 5; ++e) y[e] += s.RED[e][wv][tid];
+            const size_t gi = tokbase + (size_t)t * H * D + tid;
+            io<T_IO>::store(dr, gi, y[0]);
+            io<T_IO>::store(dk, gi, up ? y[1] : 0.0f);
+            io<T_IO>::store(da, gi, up ? y[2] : 0.0f);
+            io<T_IO>::store(db, gi, up ? y[3] : 0.0f);
+            io<T_IO>::store(dw, gi, up ? __expf(s.W[t][tid]) * y[4] : 0.0f);
+        }
+        __syncthreads();
+        if (up) {
+#pragma unroll
+            for (int i = 0; i < RPL; ++i)
+                dS[i] = fmaf(__expf(s.W[t][row0 + i]), dS[i], s.B[t][row0 + i] * ad);
+        }
+    }
+}
+
+// One workgroup per (b, h, chunk), D/16 waves.
+template <int D, typename T_IO>
+__global__ __launch_bounds__(D * 4) void chunk_grad_kernel(
+    int T, int H, int nck, const T_IO *__restrict__ r, const T_IO *__restrict__ w,
+    const T_IO *__restrict__ k, const T_IO *__restrict__ v, const T_IO *__restrict__ a,
+    const T_IO *__restrict__ b, const uint8_t *__restrict__ mask, const T_IO *__restrict__ d_o,
+    const float *__restrict__ ckpt, const float *__restrict__ dck, T_IO *__restrict__ dr,
+    T_IO *__restrict__ dw, T_IO *__restrict__ dk, T_IO *__restrict__ dv, T_IO *__restrict__ da,
+    T_IO *__restrict__ db)
+{
+    constexpr int NT = D * 4;
+    __shared__ GradLds<D> s;
+    const int bh = blockIdx.x / nck, c = blockIdx.x % nck;
+    const int bb = bh / H, h = bh % H;
+    const int t0 = c * kL, Lc = min(kL, T - t0);
+    const size_t tokbase = (((size_t)bb * T + t0) * H + h) * D;   // element of (token t0, channel 0)
+    const float *Sc = ckpt + ((size_t)bh * (nck + 1) + c) * D * D;
+    const float *Sn = Sc + (size_t)D * D;
+    const float *dSe = dck + ((size_t)bh * nck + c) * D * D;
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int q = lane >> 4, m = lane & 15;
+
+    // raw inputs of the chunk; a token that does not update gets w = k = a =
+    // b = 0 and v = 0 (an exact identity step), tokens past T are all zero
+    if (tid < kL) s.upd[tid] = (tid < Lc) && (mask ? mask[(size_t)bb * T + t0 + tid] != 0 : 1);
+    __syncthreads();
+    for (int idx = tid; idx < kL * D; idx += NT) {
+        const int t = idx / D, ch = idx % D;
+        const bool valid = t < Lc, up = s.upd[t] != 0;
+        const size_t gi = tokbase + (size_t)t * H * D + ch;
+        s.R[t][ch] = valid ? io<T_IO>::load(r, gi) : 0.0f;
+        s.DO[t][ch] = valid ? io<T_IO>::load(d_o, gi) : 0.0f;
+        const float wv = up ? io<T_IO>::load(w, gi) : 0.0f;
+        s.W[t][ch] = wv;
+        s.G[t][ch] = wv;
+        s.K[t][ch] = up ? io<T_IO>::load(k, gi) : 0.0f;
+        s.A[t][ch] = up ? io<T_IO>::load(a, gi) : 0.0f;
+        s.B[t][ch] = up ? io<T_IO>::load(b, gi) : 0.0f;
+        s.V[t][ch] = up ? io<T_IO>::load(v, gi) : 0.0f;
+    }
+    __syncthreads();
+    int extreme = 0;
+    for (int ch = tid; ch < D; ch += NT) {
+        float acc = 0.0f;
+        for (int t = 0; t < kL; ++t) {
+            extreme |= s.G[t][ch] > 0.0f;
+            acc += s.G[t][ch];
+            s.G[t][ch] = acc;
+        }
+        extreme |= acc < kMinChunkLogDecay;
+        s.EGL[ch] = __expf(acc);
+    }
+    if (__syncthreads_or(extreme)) {
+        chunk_grad_exact<D, T_IO>(s, Sc, dSe, Lc, tokbase, H, dr, dw, dk, dv, da, db);
+        return;
+    }
+    for (int idx = tid; idx < kL * D; idx += NT) {
+        const int t = idx / D, ch = idx % D;
+        const float G = s.G[t][ch], Gp = t ? s.G[t - 1][ch] : 0.0f;
+        const float enG = __expf(-G);
+        s.R[t][ch] *= __expf(G);
+        s.B[t][ch] *= __expf(Gp);
+        s.A[t][ch] *= enG;
+        s.K[t][ch] *= enG;
+    }
+    __syncthreads();
+    // chunk matrices
+    if (wave < 4) {
+        const float(*X)[GradLds<D>::LD] = wave < 2 ? s.B : s.R;
+        const float(*Y)[GradLds<D>::LD] = (wave & 1) ? s.K : s.A;
+        f32x4 acc = mm16<D>(f32x4{0.f, 0.f, 0.f, 0.f}, [&](int mm, int kk) { return X[mm][kk]; },
+                            [&](int kk, int n) { return Y[n][kk]; }, lane);
+        const bool strict = wave < 2;   // M_ba, M_bk strictly lower; M_ra, M_rk with the diagonal
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 4 * q + i;
+            s.M[wave][row][m] = (strict ? row > m : row >= m) ? acc[i] : 0.0f;
+        }
+    }
+    __syncthreads();
+    // T = (I - M_ba)^{-1} by forward substitution, one column per lane
+    if (tid < kL) {
+        float x[kL];
+#pragma unroll
+        for (int i = 0; i < kL; ++i) {
+            float acc = i == tid ? 1.0f : 0.0f;
+#pragma unroll
+            for (int mm = 0; mm < i; ++mm) acc = fmaf(s.M[M_BA][i][mm], x[mm], acc);
+            x[i] = acc;
+            s.M[M_T][i][tid] = acc;
+        }
+    }
+    __syncthreads();
+
+    // --- value-column slice c0 .. c0 + 15 of this wave ---
+    const int c0 = 16 * wave;
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    auto dY = [&](int kk, int n) { return s.EGL[kk] * dSe[(size_t)kk * D + c0 + n]; };
+    {
+        f32x4 X = mm16<D>(z, [&](int mm, int kk) { return s.B[mm][kk]; },
+                          [&](int kk, int n) { return Sc[(size_t)kk * D + c0 + n]; }, lane);
+        X = mm16<kL>(X, [&](int mm, int kk) { return s.M[M_BK][mm][kk]; },
+                     [&](int kk, int n) { return s.V[kk][c0 + n]; }, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s.W[4 * q + i][c0 + m] = X[i];
+    }
+    __syncthreads();
+    {
+        const f32x4 U = mm16<kL>(z, [&](int mm, int kk) { return s.M[M_T][mm][kk]; },
+                                 [&](int kk, int n) { return s.W[kk][c0 + n]; }, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s.U[4 * q + i][c0 + m] = U[i];
+    }
+    f32x4 dU = mm16<D>(z, [&](int mm, int kk) { return s.A[mm][kk]; }, dY, lane);
+    dU = mm16<kL>(dU, [&](int mm, int kk) { return s.M[M_RA][kk][mm]; },
+                  [&](int kk, int n) { return s.DO[kk][c0 + n]; }, lane);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s.W[4 * q + i][c0 + m] = dU[i];
+    __syncthreads();
+    {
+        const f32x4 dX = mm16<kL>(z, [&](int mm, int kk) { return s.M[M_T][kk][mm]; },
+                                  [&](int kk, int n) { return s.W[kk][c0 + n]; }, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s.DX[4 * q + i][c0 + m] = dX[i];
+    }
+    __syncthreads();
+    {
+        f32x4 dV = mm16<D>(z, [&](int mm, int kk) { return s.K[mm][kk]; }, dY, lane);
+        dV = mm16<kL>(dV, [&](int mm, int kk) { return s.M[M_RK][kk][mm]; },
+                      [&](int kk, int n) { return s.DO[kk][c0 + n]; }, lane);
+        dV = mm16<kL>(dV, [&](int mm, int kk) { return s.M[M_BK][kk][mm]; },
+                      [&](int kk, int n) { return s.DX[kk][c0 + n]; }, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = 4 * q + i;
+            if (t < Lc) io<T_IO>::store(dv, tokbase + (size_t)t * H * D + c0 + m, s.upd[t] ? dV[i] : 0.0f);
+        }
+    }
+    // --- gradients of the chunk matrices (contractions over the value columns) ---
+    if (wave < 4) {
+        const float(*X)[GradLds<D>::LD] = wave < 2 ? s.DO : s.DX;
+        const float(*Y)[GradLds<D>::LD] = (wave & 1) ? s.V : s.U;
+        const f32x4 acc = mm16<D>(z, [&](int mm, int kk) { return X[mm][kk]; },
+                                  [&](int kk, int n) { return Y[n][kk]; }, lane);
+        const bool strict = wave >= 2;   // dM_ba, dM_bk strictly lower
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 4 * q + i;
+            s.M[DM_RA + wave][row][m] = (strict ? row > m : row >= m) ? acc[i] : 0.0f;
+        }
+    }
+    __syncthreads();
+
+    // --- key-channel slice k0 .. k0 + 15 of this wave ---
+    const int k0 = 16 * wave;
+    auto ScT = [&](int kk, int n) { return Sc[(size_t)(k0 + n) * D + kk]; };
+    auto dYT = [&](int kk, int n) { return s.EGL[k0 + n] * dSe[(size_t)(k0 + n) * D + kk]; };
+    f32x4 dR = mm16<D>(z, [&](int mm, int kk) { return s.DO[mm][kk]; }, ScT, lane);
+    dR = mm16<kL>(dR, [&](int mm, int kk) { return s.M[DM_RA][mm][kk]; }, [&](int kk, int n) { return s.A[kk][k0 + n]; }, lane);
+    dR = mm16<kL>(dR, [&](int mm, int kk) { return s.M[DM_RK][mm][kk]; }, [&](int kk, int n) { return s.K[kk][k0 + n]; }, lane);
+    f32x4 dB = mm16<D>(z, [&](int mm, int kk) { return s.DX[mm][kk]; }, ScT, lane);
+    dB = mm16<kL>(dB, [&](int mm, int kk) { return s.M[DM_BA][mm][kk]; }, [&](int kk, int n) { return s.A[kk][k0 + n]; }, lane);
+    dB = mm16<kL>(dB, [&](int mm, int kk) { return s.M[DM_BK][mm][kk]; }, [&](int kk, int n) { return s.K[kk][k0 + n]; }, lane);
+    f32x4 dA = mm16<D>(z, [&](int mm, int kk) { return s.U[mm][kk]; }, dYT, lane);
+    dA = mm16<kL>(dA, [&](int mm, int kk) { return s.M[DM_RA][kk][mm]; }, [&](int kk, int n) { return s.R[kk][k0 + n]; }, lane);
+    dA = mm16<kL>(dA, [&](int mm, int kk) { return s.M[DM_BA][kk][mm]; }, [&](int kk, int n) { return s.B[kk][k0 + n]; }, lane);
+    f32x4 dK = mm16<D>(z, [&](int mm, int kk) { return s.V[mm][kk]; }, dYT, lane);
+    dK = mm16<kL>(dK, [&](int mm, int kk) { return s.M[DM_RK][kk][mm]; }, [&](int kk, int n) { return s.R[kk][k0 + n]; }, lane);
+    dK = mm16<kL>(dK, [&](int mm, int kk) { return s.M[DM_BK][kk][mm]; }, [&](int kk, int n) { return s.B[kk][k0 + n]; }, lane);
+    // chunk-end term of dw: sum_j dS'[ch][j] S'[ch][j] for channel ch = k0 + m
+    float dgl = 0.0f;
+    {
+        const size_t rowoff = (size_t)(k0 + m) * D;
+        for (int j = q; j < D; j += 4) dgl = fmaf(dSe[rowoff + j], Sn[rowoff + j], dgl);
+        dgl = xor_sum(xor_sum(dgl, 16), 32);
+    }
+    // token gradients; lane (q, m) holds tokens 4q + i of channel ch
+    const int ch = k0 + m;
+    float gr[4], gk[4], ga[4], gb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = 4 * q + i;
+        const float G = s.G[t][ch], Gp = t ? s.G[t - 1][ch] : 0.0f;
+        const float eG = __expf(G), enG = __expf(-G), eGp = __expf(Gp);
+        gr[i] = dR[i] * eG;
+        gb[i] = dB[i] * eGp;
+        ga[i] = dA[i] * enG;
+        gk[i] = dK[i] * enG;
+        // raw (masked) operands are the scaled ones times the inverse factors
+        const float rr = s.R[t][ch] * enG, kk = s.K[t][ch] * eG, aa = s.A[t][ch] * eG;
+        const float bv = s.B[t][ch] * (t ? __expf(-Gp) : 1.0f);
+        s.P[wave][0][t][m] = gr[i] * rr - ga[i] * aa - gk[i] * kk;
+        s.P[wave][1][t][m] = gb[i] * bv;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = 4 * q + i;
+        if (t >= Lc) continue;
+        float acc = dgl;
+        for (int u = kL - 1; u >= t; --u) acc += s.P[wave][0][u][m] + (u + 1 < kL ? s.P[wave][1][u + 1][m] : 0.0f);
+        const bool up = s.upd[t] != 0;
+        const size_t gi = tokbase + (size_t)t * H * D + ch;
+        io<T_IO>::store(dr, gi, gr[i]);
+        io<T_IO>::store(dw, gi, up ? acc : 0.0f);
+        io<T_IO>::store(dk, gi, up ? gk[i] : 0.0f);
+        io<T_IO>::store(da, gi, up ? ga[i] : 0.0f);
+        io<T_IO>::store(db, gi, up ? gb[i] : 0.0f);
+    }
+}
+
+template <int D, typename T_IO>
+hipError_t launch_bwd_d(const BwdArgs &p, hipStream_t stream)
+{
+    const int nck = (p.T + kL - 1) / kL;
+    const size_t nbh = (size_t)p.B * p.H;
+    float *ckpt = (float *)p.ws;
+    float *dck = ckpt + nbh * (nck + 1) * D * D;
+    FwdArgs fa{p.B, p.T, p.H, D, p.r, p.w, p.k, p.v, p.a, p.b, p.s0, p.mask, nullptr, nullptr};
+    fa.n_state = p.B;
+    fa.ckpt = ckpt;
+    hipError_t e = launch_recurrent(sizeof(T_IO) == 4 ? 0 : 1, fa, stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((dstate_chain_kernel<D, T_IO>), dim3((unsigned)nbh), dim3(D * 4), 0, stream, p.T, p.H,
+                       (const T_IO *)p.r, (const T_IO *)p.w, (const T_IO *)p.a, (const T_IO *)p.b, p.mask,
+                       (const T_IO *)p.d_o, p.d_sf, dck, p.d_s0);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((chunk_grad_kernel<D, T_IO>), dim3((unsigned)(nbh * nck)), dim3(D * 4), 0, stream, p.T,
+                       p.H, nck, (const T_IO *)p.r, (const T_IO *)p.w, (const T_IO *)p.k, (const T_IO *)p.v,
+                       (const T_IO *)p.a, (const T_IO *)p.b, p.mask, (const T_IO *)p.d_o, ckpt, dck,
+                       (T_IO *)p.dr, (T_IO *)p.dw, (T_IO *)p.dk, (T_IO *)p.dv, (T_IO *)p.da, (T_IO *)p.db);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(int B, int T, int H, int D)
+{
+    const size_t nck = ((size_t)T + kL - 1) / kL;
+    return sizeof(float) * (size_t)B * H * D * D * (2 * nck + 1);
+}
+
+hipError_t launch_backward(int dtype, const BwdArgs &p, hipStream_t stream)
+{
+    if (p.D == 64) return dtype == 0 ? launch_bwd_d<64, float>(p, stream) : launch_bwd_d<64, uint16_t>(p, stream);
+    return dtype == 0 ? launch_bwd_d<128, float>(p, stream) : launch_bwd_d<128, uint16_t>(p, stream);
+}
+
+}  // namespace wkv7

@@ -24,7 +24,27 @@ struct FwdArgs {
     // Gated DeltaNet inputs in the same slots: r = q, k = k, v = v,
     // w = gate g and a = strength beta, both one value per token and head.
     bool gdn = false;
+    // Recurrent kernel only: state checkpoints before every 16-token block
+    // and after the last, [B*H][ceil(T/16) + 1][D][D] fp32 (o may then be
+    // nullptr).
+    float *ckpt = nullptr;
 };
+
+// Backward (fixed-length form): gradients of the forward for upstream d_o
+// [B,T,H,D] and d_sf [B,H,D,D] (or nullptr); dr..db in the I/O dtype, d_s0
+// fp32 (or nullptr).  ws: workspace of bwd_workspace_bytes(B,T,H,D) bytes.
+struct BwdArgs {
+    int B, T, H, D;
+    const void *r, *w, *k, *v, *a, *b;
+    const float *s0;
+    const uint8_t *mask;
+    const void *d_o;
+    const float *d_sf;
+    void *dr, *dw, *dk, *dv, *da, *db;
+    float *d_s0;
+    void *ws;
+};
+size_t bwd_workspace_bytes(int B, int T, int H, int D);
 
 struct StepArgs {
     int B, H, D;
@@ -37,6 +57,7 @@ struct StepArgs {
 hipError_t launch_recurrent(int dtype, const FwdArgs &args, hipStream_t stream);
 hipError_t launch_chunked(const FwdArgs &args, hipStream_t stream);     // bf16 only
 hipError_t launch_step(int dtype, const StepArgs &args, hipStream_t stream);
+hipError_t launch_backward(int dtype, const BwdArgs &args, hipStream_t stream);
 // final_state = initial_state (or zeros) for T == 0.
 hipError_t launch_state_copy(const float *s0, float *sf, size_t n, hipStream_t stream);
 

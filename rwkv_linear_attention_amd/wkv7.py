@@ -36,6 +36,10 @@ def lib():
     L.wkv7_fwd_varlen.restype = i
     L.wkv7_gdn_fwd.argtypes = [i, i, i, i, i, i] + [p] * 6 + [i, p, p, i, p]
     L.wkv7_gdn_fwd.restype = i
+    L.wkv7_bwd.argtypes = [i, i, i, i, i, i] + [p] * 18 + [ctypes.c_size_t, p]
+    L.wkv7_bwd.restype = i
+    L.wkv7_bwd_workspace_bytes.argtypes = [i] * 5
+    L.wkv7_bwd_workspace_bytes.restype = ctypes.c_size_t
     L.wkv7_step.argtypes = [i, i, i, i, i] + [p] * 8 + [p]
     L.wkv7_step.restype = i
     L.wkv7_strerror.argtypes = [i]
@@ -175,6 +179,51 @@ def fwd_varlen(r, w, k, v, a, b, cu_seqlens, initial_state=None, state_map=None,
     if st != OK:
         raise WKV7Error(st)
     return (o.unsqueeze(0) if lead1 else o), sf
+
+
+def bwd_workspace_bytes(B, T, H, K, V):
+    """Bytes of device workspace bwd needs (0 if the sizes are rejected)."""
+    return int(lib().wkv7_bwd_workspace_bytes(B, T, H, K, V))
+
+
+def bwd(r, w, k, v, a, b, d_o, initial_state=None, mask=None, d_final_state=None, workspace=None,
+        need_initial_state_grad=True):
+    """Gradients of fwd.  Inputs as for fwd; d_o: [B,T,H,V] in the input
+    dtype; d_final_state: [B,H,K,V] float32 or None.  workspace: a uint8
+    device tensor of at least bwd_workspace_bytes(...) bytes, or None to
+    allocate one.  Returns a dict with r, w, k, v, a, b (input dtype) and s0
+    ([B,H,K,V] float32, or None when need_initial_state_grad is False)."""
+    dev = r.device
+    B, T, H, K = r.shape
+    V = v.shape[-1]
+    dt = r.dtype
+    code = _dtype_code(dt)
+    for name, t in (("r", r), ("w", w), ("k", k), ("a", a), ("b", b)):
+        _check(t, name, (B, T, H, K), dt, dev)
+    _check(v, "v", (B, T, H, V), dt, dev)
+    _check(d_o, "d_o", (B, T, H, V), dt, dev)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", (B, H, K, V), torch.float32, dev)
+    if d_final_state is not None:
+        _check(d_final_state, "d_final_state", (B, H, K, V), torch.float32, dev)
+    m = _mask_u8(mask)
+    if m is not None:
+        _check(m, "mask", (B, T), torch.uint8, dev)
+    need = bwd_workspace_bytes(B, T, H, K, V)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    elif workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
+    g = {n: torch.empty((B, T, H, K), dtype=dt, device=dev) for n in ("r", "w", "k", "a", "b")}
+    g["v"] = torch.empty((B, T, H, V), dtype=dt, device=dev)
+    g["s0"] = torch.empty((B, H, K, V), dtype=torch.float32, device=dev) if need_initial_state_grad else None
+    st = lib().wkv7_bwd(code, B, T, H, K, V, _ptr(r), _ptr(w), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
+                        _ptr(initial_state), _ptr(m), _ptr(d_o), _ptr(d_final_state),
+                        *(_ptr(g[n]) for n in ("r", "w", "k", "v", "a", "b", "s0")),
+                        _ptr(workspace), workspace.numel(), _stream(dev))
+    if st != OK:
+        raise WKV7Error(st)
+    return g
 
 
 def gdn_fwd(q, k, v, g, beta, initial_state=None, output_final_state=True, algo=ALGO_AUTO,

@@ -27,14 +27,14 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert {"wkv7_fwd", "wkv7_fwd_varlen", "wkv7_gdn_fwd", "wkv7_step", "wkv7_strerror", "wkv7_fwd_path",
+    assert {"wkv7_fwd", "wkv7_fwd_varlen", "wkv7_gdn_fwd", "wkv7_bwd", "wkv7_bwd_workspace_bytes", "wkv7_step", "wkv7_strerror", "wkv7_fwd_path",
             "wkv7_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"{n} declared in wkv7.h but not exported"
 
 
 def test_version_and_strerror(L):
-    assert L.wkv7_version() == 102
+    assert L.wkv7_version() == 103
     for code in range(4):
         assert len(L.wkv7_strerror(code)) > 0
     assert L.wkv7_strerror(99) == b"unknown status"
@@ -179,3 +179,46 @@ def test_gdn_rejects_null_and_misaligned(L, slot):
     assert gdn(L, ptrs=ptrs) == wkv7.ERR_INVALID_ARG
     ptrs[slot] = ODD
     assert gdn(L, ptrs=ptrs) == wkv7.ERR_INVALID_ARG
+
+
+def bwd(L, dtype=1, B=1, T=20, H=1, K=64, V=64, ptrs=None, s0=None, mask=None, dsf=None, ds0=None,
+        ws=GOOD, ws_bytes=None):
+    ptrs = ptrs or [GOOD] * 13
+    if ws_bytes is None:
+        ws_bytes = L.wkv7_bwd_workspace_bytes(B, T, H, K, V)
+    r, w, k, v, a, b, do, dr, dw, dk, dv, da, db = ptrs
+    return L.wkv7_bwd(dtype, B, T, H, K, V, r, w, k, v, a, b, s0, mask, do, dsf, dr, dw, dk, dv, da, db, ds0,
+                      ws, ws_bytes, None)
+
+
+def test_bwd_workspace_size(L):
+    # two fp32 states per 16-token chunk and sequence, plus one
+    assert L.wkv7_bwd_workspace_bytes(2, 33, 3, 64, 64) == 4 * 2 * 3 * 64 * 64 * (2 * 3 + 1)
+    assert L.wkv7_bwd_workspace_bytes(1, 16, 1, 128, 128) == 4 * 128 * 128 * 3
+    assert L.wkv7_bwd_workspace_bytes(1, 16, 1, 64, 32) == 0
+    assert L.wkv7_bwd_workspace_bytes(0, 16, 1, 64, 64) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), wkv7.ERR_INVALID_ARG),
+    (dict(B=0), wkv7.ERR_INVALID_ARG),
+    (dict(T=-1), wkv7.ERR_INVALID_ARG),
+    (dict(K=64, V=128), wkv7.ERR_UNSUPPORTED),
+    (dict(ws=None), wkv7.ERR_INVALID_ARG),
+    (dict(ws=ODD), wkv7.ERR_INVALID_ARG),
+    (dict(ws_bytes=1024), wkv7.ERR_INVALID_ARG),              # workspace too small
+    (dict(s0=ODD), wkv7.ERR_INVALID_ARG),
+    (dict(dsf=ODD), wkv7.ERR_INVALID_ARG),
+    (dict(ds0=ODD), wkv7.ERR_INVALID_ARG),
+])
+def test_bwd_validation(L, kw, code):
+    assert bwd(L, **kw) == code
+
+
+@pytest.mark.parametrize("slot", range(13))
+def test_bwd_rejects_null_and_misaligned(L, slot):
+    ptrs = [GOOD] * 13
+    ptrs[slot] = None
+    assert bwd(L, ptrs=ptrs) == wkv7.ERR_INVALID_ARG
+    ptrs[slot] = ODD
+    assert bwd(L, ptrs=ptrs) == wkv7.ERR_INVALID_ARG

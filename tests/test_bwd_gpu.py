@@ -1,0 +1,142 @@
+"""GPU parity of wkv7_bwd (gradients of the WKV7 forward) against the fp64
+backward oracle, which is pinned to the forward by finite differences
+(tests/test_oracle_bwd_pins.py).
+
+Tolerances, per gradient tensor g with oracle value g_ref:
+  bf16 I/O: the same rule as the forward's output,
+            |g_i - g_ref,i| <= 0.02 RMS(g_ref) + 2^-8 |g_ref,i|;
+            the backward computes in fp32 from the exact bf16 inputs, so the
+            final rounding to bf16 is the main error.
+  fp32 I/O: |g_i - g_ref,i| <= 1e-4 RMS(g_ref) + 1e-5 |g_ref,i|: fp32 sums of
+            about K*16 products per chunk matrix element and an fp32 state
+            and gradient chain over T tokens, a relative error of a few 1e-6
+            against the size of the terms, with headroom for cancellation in
+            dw (a sum of terms of both signs).
+  initial-state gradient (always fp32): the same rule with its own RMS.
+"""
+import numpy as np
+import pytest
+
+import harness as hz
+import oracle
+from rwkv_linear_attention_amd import synth, wkv7
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+NAMES = ("r", "w", "k", "v", "a", "b")
+
+
+def make_case(B, T, H, D, dtype, seed, init=True, mask=None, dsf=True):
+    inp = synth.make(1, B=B, T=T, H=H, K=D, seed=seed, init=init, mask=mask or "none")
+    inp["dtype"] = dtype
+    for n in NAMES:
+        inp[n] = synth.round_to(inp[n], dtype)
+    rng = np.random.default_rng(seed + 7)
+    d_o = synth.round_to(rng.standard_normal((B, T, H, D)).astype(np.float32), dtype)
+    d_sf = (rng.standard_normal((B, H, D, D)) * 0.5).astype(np.float32) if dsf else None
+    return inp, d_o, d_sf
+
+
+def run_gpu(inp, d_o, d_sf):
+    dt = inp["dtype"]
+    dev = {n: synth.to_torch(inp[n], dt, "cuda") for n in NAMES}
+    s0 = None if inp["s0"] is None else torch.from_numpy(inp["s0"]).cuda()
+    m = None if inp["mask"] is None else torch.from_numpy(inp["mask"]).cuda()
+    dsf = None if d_sf is None else torch.from_numpy(d_sf).cuda()
+    g = wkv7.bwd(*(dev[n] for n in NAMES), synth.to_torch(d_o, dt, "cuda"), initial_state=s0, mask=m,
+                 d_final_state=dsf)
+    torch.cuda.synchronize()
+    return {n: hz.to_np(x) for n, x in g.items()}
+
+
+def check_grad(dtype, got, ref, what):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape
+    assert np.all(np.isfinite(got)), f"{what}: non-finite gradient"
+    rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
+    if dtype == "bf16":
+        allow = 0.02 * rms + 2.0 ** -8 * np.abs(ref)
+    else:
+        allow = 1e-4 * rms + 1e-5 * np.abs(ref)
+    err = np.abs(got - ref)
+    ratio = float(np.max(err / np.maximum(allow, 1e-30))) if got.size else 0.0
+    hz._log(what, ratio)
+    assert ratio <= 1.0 or np.all(err == 0), f"{what}: worst error {ratio:.3f} x tolerance (RMS {rms:.3g})"
+
+
+def check_all(dtype, g, ref, what):
+    for n in NAMES:
+        check_grad(dtype, g[n], ref[n], f"{what} d{n}")
+    check_grad("f32", g["s0"], ref["s0"], f"{what} ds0")   # fp32 output in both dtypes
+
+
+def oracle_bwd(inp, d_o, d_sf):
+    return oracle.bwd(*(inp[n] for n in NAMES), d_o, inp["s0"], inp["mask"], d_sf)
+
+
+@pytest.mark.parametrize("dtype,D,B,T,H,mask,init,dsf", [
+    ("f32", 64, 2, 50, 2, None, True, True),
+    ("f32", 128, 1, 40, 2, "bernoulli", True, True),
+    ("f32", 64, 1, 16, 1, None, False, False),
+    ("bf16", 64, 2, 200, 2, "bernoulli", True, True),
+    ("bf16", 128, 2, 130, 1, "trailing", True, True),
+    ("bf16", 64, 1, 77, 3, None, False, False),
+])
+def test_bwd_parity(dtype, D, B, T, H, mask, init, dsf):
+    inp, d_o, d_sf = make_case(B, T, H, D, dtype, seed=5000 + T + D, init=init, mask=mask, dsf=dsf)
+    g = run_gpu(inp, d_o, d_sf)
+    ref = oracle_bwd(inp, d_o, d_sf)
+    check_all(dtype, g, ref, f"bwd {dtype} D{D} T{T}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 33])
+def test_bwd_short_and_ragged(D, T):
+    inp, d_o, d_sf = make_case(2, T, 1, D, "f32", seed=5200 + T, mask="bernoulli")
+    g = run_gpu(inp, d_o, d_sf)
+    check_all("f32", g, oracle_bwd(inp, d_o, d_sf), f"bwd ragged D{D} T{T}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_bwd_extreme_decay_chunks(D):
+    """Chunks whose decay leaves the range of the split factors (w = -20 on
+    whole chunks, a -1e9 padding-style token, a positive w) take the exact
+    token-by-token path; the gradients must still match."""
+    B, T, H = 2, 80, 1
+    inp, d_o, d_sf = make_case(B, T, H, D, "f32", seed=5300 + D)
+    w = inp["w"].copy()
+    w[0, 16:32] = -20.0
+    w[0, 40, 0, :5] = -1e9
+    w[1, 50, 0, 3] = 0.3
+    w[1, 64:80] = 0.0
+    inp["w"] = w.astype(np.float32)
+    g = run_gpu(inp, d_o, d_sf)
+    check_all("f32", g, oracle_bwd(inp, d_o, d_sf), f"bwd extreme D{D}")
+
+
+def test_bwd_empty_sequence():
+    inp, d_o, d_sf = make_case(2, 0, 1, 64, "f32", seed=5400)
+    g = run_gpu(inp, d_o, d_sf)
+    np.testing.assert_array_equal(g["s0"], d_sf)
+    assert g["r"].shape == (2, 0, 1, 64)
+
+
+@pytest.mark.parametrize("D,B,H", [(64, 8, 64), (128, 16, 32)])
+def test_bwd_full_size_sampled(D, B, H):
+    """The benchmark shapes (T = 4096), checked on sampled (sequence, head)
+    pairs that the oracle recomputes alone."""
+    T = 4096
+    inp, d_o, d_sf = make_case(B, T, H, D, "bf16", seed=5500 + D, init=(D == 128),
+                               mask="trailing" if D == 128 else None, dsf=False)
+    g = run_gpu(inp, d_o, d_sf)
+    rng = np.random.default_rng(5501)
+    for bb, h in zip(rng.integers(0, B, 2), rng.integers(0, H, 2)):
+        sl = {n: inp[n][bb:bb + 1, :, h:h + 1] for n in NAMES}
+        s0 = None if inp["s0"] is None else inp["s0"][bb:bb + 1, h:h + 1]
+        m = None if inp["mask"] is None else inp["mask"][bb:bb + 1]
+        ref = oracle.bwd(*(sl[n] for n in NAMES), d_o[bb:bb + 1, :, h:h + 1], s0, m, None)
+        for n in NAMES:
+            check_grad("bf16", g[n][bb, :, h], ref[n][0, :, 0], f"bwd full D{D} b{bb} h{h} d{n}")
+        check_grad("f32", g["s0"][bb, h], ref["s0"][0, 0], f"bwd full D{D} b{bb} h{h} ds0")
