@@ -137,15 +137,40 @@ __global__ __launch_bounds__(D * 4) void dstate_chain_kernel(
 
 // ---- 3. per-chunk gradients -------------------------------------------------
 
-template <int D> struct GradLds {
-    static constexpr int LD = D + 1;    // padded row stride of the L x D tiles
+// Four consecutive elements (index i a multiple of 4) as fp32.
+template <typename T> struct io4;
+template <> struct io4<float> {
+    __device__ __forceinline__ static f32x4 load(const float *p, size_t i) { return *(const f32x4 *)(p + i); }
+    __device__ __forceinline__ static void store(float *p, size_t i, f32x4 x) { *(f32x4 *)(p + i) = x; }
+};
+template <> struct io4<uint16_t> {
+    __device__ __forceinline__ static f32x4 load(const uint16_t *p, size_t i)
+    {
+        const u32x2 u = *(const u32x2 *)(p + i);
+        return f32x4{bf16_lo(u[0]), bf16_hi(u[0]), bf16_lo(u[1]), bf16_hi(u[1])};
+    }
+    __device__ __forceinline__ static void store(uint16_t *p, size_t i, f32x4 x)
+    {
+        *(u32x2 *)(p + i) = u32x2{cvt2_bits(x[0], x[1]), cvt2_bits(x[2], x[3])};
+    }
+};
+
+// row_shl:n inside each 16-lane row (lane i reads lane i + n); lanes without
+// a source receive `fill`.
+template <int N>
+__device__ __forceinline__ float row_shl(float x, float fill)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(fill), __float_as_int(x), 0x100 + N, 0xF,
+                                                      0xF, false));
+}
+
+template <int D> struct alignas(16) GradLds {
+    static constexpr int LD = D + 4;    // row stride of the L x D tiles (16-byte aligned rows)
     float R[kL][LD], B[kL][LD], A[kL][LD], K[kL][LD], V[kL][LD], DO[kL][LD];
     float G[kL][LD];                    // decay prefix
-    float W[kL][LD];                    // raw (masked) w, then X / dU
-    float U[kL][LD], DX[kL][LD];
+    float U[kL][LD], DX[kL][LD];        // X, then U; dU, then dX (exact path: raw w in U)
     float M[9][kL][kL + 1];             // M_ba, M_bk, M_ra, M_rk, T, dM_ra, dM_rk, dM_ba, dM_bk
     float EGL[D];
-    float P[D / 16][2][kL][kL + 1];     // per-wave dG pieces
     float RED[5][D / 16][D];            // exact path: per-wave row sums
     int upd[kL];
 };
@@ -156,7 +181,7 @@ enum { M_BA = 0, M_BK, M_RA, M_RK, M_T, DM_RA, DM_RK, DM_BA, DM_BK };
 // per-token formulas (those of the oracle's derivative), with the states
 // S_{t-1} and S_t recomputed from the chunk's checkpoint.  Lane layout of the
 // recurrent kernel: lane (j, g) of wave w holds rows [g D/4, (g+1) D/4) of
-// column 16w + j.
+// column 16w + j.  s.U holds the raw (masked) w.
 template <int D, typename T_IO>
 __device__ void chunk_grad_exact(GradLds<D> &s, const float *Sc, const float *dSe, int Lc, size_t tokbase,
                                  int H, T_IO *dr, T_IO *dw, T_IO *dk, T_IO *dv, T_IO *da, T_IO *db)
@@ -165,6 +190,7 @@ __device__ void chunk_grad_exact(GradLds<D> &s, const float *Sc, const float *dS
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int col = wave * 16 + (lane & 15), g = lane >> 4, row0 = g * RPL;
     auto colsum = [](float x) { return xor_sum(xor_sum(x, 16), 32); };
+    const auto &W = s.U;
     auto step = [&](float *P, int u) {   // P <- state after token u (P = state before it)
         if (!s.upd[u]) return;
         float sb = 0.f;
@@ -174,11 +200,8 @@ __device__ void chunk_grad_exact(GradLds<D> &s, const float *Sc, const float *dS
         const float vj = s.V[u][col];
 #pragma unroll
         for (int i = 0; i < RPL; ++i)
-            P[i] = fmaf(__expf(s.W[u][row0 + i]), P[i], fmaf(s.A[u][row0 + i], sb, s.K[u][row0 + i] * vj));
+            P[i] = fmaf(__expf(W[u][row0 + i]), P[i], fmaf(s.A[u][row0 + i], sb, s.K[u][row0 + i] * vj));
     };
-    float dS[RPL];
-#pragma unroll
-    for (int i = 0; i < RPL; ++i) dS[i] = dSe[(size_t)(row0 + i) * D + col];
     auto rowsum = [&](float y, int e, int row) {   // over the 16 columns of the wave
         y += __shfl_xor(y, 1, kWave);
         y += __shfl_xor(y, 2, kWave);
@@ -186,6 +209,9 @@ __device__ void chunk_grad_exact(GradLds<D> &s, const float *Sc, const float *dS
         y += __shfl_xor(y, 8, kWave);
         if ((lane & 15) == 0) s.RED[e][wave][row] = y;
     };
+    float dS[RPL];
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) dS[i] = dSe[(size_t)(row0 + i) * D + col];
     for (int t = Lc - 1; t >= 0; --t) {
         float P[RPL];   // S_{t-1}
 #pragma unroll
@@ -200,7 +226,7 @@ __device__ void chunk_grad_exact(GradLds<D> &s, const float *Sc, const float *dS
         // dr_t = S_t d_o_t with S_t formed element by element from S_{t-1}
 #pragma unroll
         for (int i = 0; i < RPL; ++i) {
-            const float st = up ? fmaf(__expf(s.W[t][row0 + i]), P[i], fmaf(s.A[t][row0 + i], sb, s.K[t][row0 + i] * vj))
+            const float st = up ? fmaf(__expf(W[t][row0 + i]), P[i], fmaf(s.A[t][row0 + i], sb, s.K[t][row0 + i] * vj))
                                 : P[i];
             rowsum(st * doj, 0, row0 + i);
         }
@@ -235,15 +261,35 @@ __device__ void chunk_grad_exact(GradLds<D> &s, const float *Sc, const float *dS
             io<T_IO>::store(dk, gi, up ? y[1] : 0.0f);
             io<T_IO>::store(da, gi, up ? y[2] : 0.0f);
             io<T_IO>::store(db, gi, up ? y[3] : 0.0f);
-            io<T_IO>::store(dw, gi, up ? __expf(s.W[t][tid]) * y[4] : 0.0f);
+            io<T_IO>::store(dw, gi, up ? __expf(W[t][tid]) * y[4] : 0.0f);
         }
         __syncthreads();
         if (up) {
 #pragma unroll
             for (int i = 0; i < RPL; ++i)
-                dS[i] = fmaf(__expf(s.W[t][row0 + i]), dS[i], s.B[t][row0 + i] * ad);
+                dS[i] = fmaf(__expf(W[t][row0 + i]), dS[i], s.B[t][row0 + i] * ad);
         }
     }
+}
+
+// Transposed product over a contraction of length D:
+//   acc(16 x 16) += A (16 x D) B (D x 16) with A[m][j] = a4(m, j0) and
+//   B[j][n] = b4(n, j0) fetched as four consecutive j = j0 .. j0 + 3.
+// The contraction index is permuted inside each block of 16 so that in step
+// s of block j0b lane (q, m) supplies j = j0b + 4q + s for both operands;
+// this lets each lane feed four steps from one 16-byte load of a row.
+template <int D, class FA, class FB>
+__device__ __forceinline__ f32x4 mm16_rows(f32x4 acc, FA a4, FB b4, int lane)
+{
+    const int m = lane & 15, q = lane >> 4;
+#pragma unroll
+    for (int j0b = 0; j0b < D; j0b += 16) {
+        const f32x4 x = a4(m, j0b + 4 * q);
+        const f32x4 y = b4(m, j0b + 4 * q);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) acc = mfma_f32(x[st], y[st], acc);
+    }
+    return acc;
 }
 
 // One workgroup per (b, h, chunk), D/16 waves.
@@ -257,7 +303,8 @@ __global__ __launch_bounds__(D * 4) void chunk_grad_kernel(
     T_IO *__restrict__ db)
 {
     constexpr int NT = D * 4;
-    __shared__ GradLds<D> s;
+    using Lds = GradLds<D>;
+    __shared__ Lds s;
     const int bh = blockIdx.x / nck, c = blockIdx.x % nck;
     const int bb = bh / H, h = bh % H;
     const int t0 = c * kL, Lc = min(kL, T - t0);
@@ -267,57 +314,76 @@ __global__ __launch_bounds__(D * 4) void chunk_grad_kernel(
     const float *dSe = dck + ((size_t)bh * nck + c) * D * D;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int q = lane >> 4, m = lane & 15;
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 
-    // raw inputs of the chunk; a token that does not update gets w = k = a =
-    // b = 0 and v = 0 (an exact identity step), tokens past T are all zero
+    // raw inputs of the chunk, four channels per thread; a token that does
+    // not update gets w = k = a = b = 0 and v = 0 (an exact identity step),
+    // tokens past T are all zero
     if (tid < kL) s.upd[tid] = (tid < Lc) && (mask ? mask[(size_t)bb * T + t0 + tid] != 0 : 1);
     __syncthreads();
-    for (int idx = tid; idx < kL * D; idx += NT) {
-        const int t = idx / D, ch = idx % D;
+    {
+        static_assert(NT == kL * D / 4, "one thread per (token, 4 channels)");
+        const int t = tid / (D / 4), c4 = 4 * (tid % (D / 4));
         const bool valid = t < Lc, up = s.upd[t] != 0;
-        const size_t gi = tokbase + (size_t)t * H * D + ch;
-        s.R[t][ch] = valid ? io<T_IO>::load(r, gi) : 0.0f;
-        s.DO[t][ch] = valid ? io<T_IO>::load(d_o, gi) : 0.0f;
-        const float wv = up ? io<T_IO>::load(w, gi) : 0.0f;
-        s.W[t][ch] = wv;
-        s.G[t][ch] = wv;
-        s.K[t][ch] = up ? io<T_IO>::load(k, gi) : 0.0f;
-        s.A[t][ch] = up ? io<T_IO>::load(a, gi) : 0.0f;
-        s.B[t][ch] = up ? io<T_IO>::load(b, gi) : 0.0f;
-        s.V[t][ch] = up ? io<T_IO>::load(v, gi) : 0.0f;
+        const size_t gi = tokbase + (size_t)t * H * D + c4;
+        *(f32x4 *)&s.R[t][c4] = valid ? io4<T_IO>::load(r, gi) : z;
+        *(f32x4 *)&s.DO[t][c4] = valid ? io4<T_IO>::load(d_o, gi) : z;
+        *(f32x4 *)&s.G[t][c4] = up ? io4<T_IO>::load(w, gi) : z;
+        *(f32x4 *)&s.K[t][c4] = up ? io4<T_IO>::load(k, gi) : z;
+        *(f32x4 *)&s.A[t][c4] = up ? io4<T_IO>::load(a, gi) : z;
+        *(f32x4 *)&s.B[t][c4] = up ? io4<T_IO>::load(b, gi) : z;
+        *(f32x4 *)&s.V[t][c4] = up ? io4<T_IO>::load(v, gi) : z;
     }
     __syncthreads();
     int extreme = 0;
-    for (int ch = tid; ch < D; ch += NT) {
+    if (tid < D) {
+        float x[kL];
+#pragma unroll
+        for (int t = 0; t < kL; ++t) x[t] = s.G[t][tid];
         float acc = 0.0f;
+#pragma unroll
         for (int t = 0; t < kL; ++t) {
-            extreme |= s.G[t][ch] > 0.0f;
-            acc += s.G[t][ch];
-            s.G[t][ch] = acc;
+            extreme |= x[t] > 0.0f;
+            acc += x[t];
+            s.G[t][tid] = acc;
         }
         extreme |= acc < kMinChunkLogDecay;
-        s.EGL[ch] = __expf(acc);
+        s.EGL[tid] = __expf(acc);
     }
     if (__syncthreads_or(extreme)) {
+        // raw w for the exact path (the prefix replaced it in G)
+        {
+            const int t = tid / (D / 4), c4 = 4 * (tid % (D / 4));
+            const size_t gi = tokbase + (size_t)t * H * D + c4;
+            *(f32x4 *)&s.U[t][c4] = s.upd[t] ? io4<T_IO>::load(w, gi) : z;
+        }
+        __syncthreads();
         chunk_grad_exact<D, T_IO>(s, Sc, dSe, Lc, tokbase, H, dr, dw, dk, dv, da, db);
         return;
     }
-    for (int idx = tid; idx < kL * D; idx += NT) {
-        const int t = idx / D, ch = idx % D;
-        const float G = s.G[t][ch], Gp = t ? s.G[t - 1][ch] : 0.0f;
-        const float enG = __expf(-G);
-        s.R[t][ch] *= __expf(G);
-        s.B[t][ch] *= __expf(Gp);
-        s.A[t][ch] *= enG;
-        s.K[t][ch] *= enG;
+    {
+        const int t = tid / (D / 4), c4 = 4 * (tid % (D / 4));
+        const f32x4 G = *(const f32x4 *)&s.G[t][c4];
+        const f32x4 Gp = t ? *(const f32x4 *)&s.G[t - 1][c4] : z;
+        f32x4 eG, enG, eGp;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            eG[i] = __expf(G[i]);
+            enG[i] = __expf(-G[i]);
+            eGp[i] = __expf(Gp[i]);
+        }
+        *(f32x4 *)&s.R[t][c4] *= eG;
+        *(f32x4 *)&s.B[t][c4] *= eGp;
+        *(f32x4 *)&s.A[t][c4] *= enG;
+        *(f32x4 *)&s.K[t][c4] *= enG;
     }
     __syncthreads();
     // chunk matrices
     if (wave < 4) {
-        const float(*X)[GradLds<D>::LD] = wave < 2 ? s.B : s.R;
-        const float(*Y)[GradLds<D>::LD] = (wave & 1) ? s.K : s.A;
-        f32x4 acc = mm16<D>(f32x4{0.f, 0.f, 0.f, 0.f}, [&](int mm, int kk) { return X[mm][kk]; },
-                            [&](int kk, int n) { return Y[n][kk]; }, lane);
+        const float(*X)[Lds::LD] = wave < 2 ? s.B : s.R;
+        const float(*Y)[Lds::LD] = (wave & 1) ? s.K : s.A;
+        const f32x4 acc = mm16_rows<D>(z, [&](int mm, int j) { return *(const f32x4 *)&X[mm][j]; },
+                                       [&](int n, int j) { return *(const f32x4 *)&Y[n][j]; }, lane);
         const bool strict = wave < 2;   // M_ba, M_bk strictly lower; M_ra, M_rk with the diagonal
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -342,7 +408,6 @@ __global__ __launch_bounds__(D * 4) void chunk_grad_kernel(
 
     // --- value-column slice c0 .. c0 + 15 of this wave ---
     const int c0 = 16 * wave;
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
     auto dY = [&](int kk, int n) { return s.EGL[kk] * dSe[(size_t)kk * D + c0 + n]; };
     {
         f32x4 X = mm16<D>(z, [&](int mm, int kk) { return s.B[mm][kk]; },
@@ -350,27 +415,26 @@ __global__ __launch_bounds__(D * 4) void chunk_grad_kernel(
         X = mm16<kL>(X, [&](int mm, int kk) { return s.M[M_BK][mm][kk]; },
                      [&](int kk, int n) { return s.V[kk][c0 + n]; }, lane);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s.W[4 * q + i][c0 + m] = X[i];
-    }
-    __syncthreads();
-    {
-        const f32x4 U = mm16<kL>(z, [&](int mm, int kk) { return s.M[M_T][mm][kk]; },
-                                 [&](int kk, int n) { return s.W[kk][c0 + n]; }, lane);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s.U[4 * q + i][c0 + m] = U[i];
+        for (int i = 0; i < 4; ++i) s.U[4 * q + i][c0 + m] = X[i];
     }
     f32x4 dU = mm16<D>(z, [&](int mm, int kk) { return s.A[mm][kk]; }, dY, lane);
     dU = mm16<kL>(dU, [&](int mm, int kk) { return s.M[M_RA][kk][mm]; },
                   [&](int kk, int n) { return s.DO[kk][c0 + n]; }, lane);
-    __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s.W[4 * q + i][c0 + m] = dU[i];
+    for (int i = 0; i < 4; ++i) s.DX[4 * q + i][c0 + m] = dU[i];
     __syncthreads();
     {
+        // this wave alone reads and writes columns c0 .. c0 + 15 of U and DX
+        const f32x4 U = mm16<kL>(z, [&](int mm, int kk) { return s.M[M_T][mm][kk]; },
+                                 [&](int kk, int n) { return s.U[kk][c0 + n]; }, lane);
         const f32x4 dX = mm16<kL>(z, [&](int mm, int kk) { return s.M[M_T][kk][mm]; },
-                                  [&](int kk, int n) { return s.W[kk][c0 + n]; }, lane);
+                                  [&](int kk, int n) { return s.DX[kk][c0 + n]; }, lane);
+        __syncthreads();
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s.DX[4 * q + i][c0 + m] = dX[i];
+        for (int i = 0; i < 4; ++i) {
+            s.U[4 * q + i][c0 + m] = U[i];
+            s.DX[4 * q + i][c0 + m] = dX[i];
+        }
     }
     __syncthreads();
     {
@@ -387,10 +451,10 @@ __global__ __launch_bounds__(D * 4) void chunk_grad_kernel(
     }
     // --- gradients of the chunk matrices (contractions over the value columns) ---
     if (wave < 4) {
-        const float(*X)[GradLds<D>::LD] = wave < 2 ? s.DO : s.DX;
-        const float(*Y)[GradLds<D>::LD] = (wave & 1) ? s.V : s.U;
-        const f32x4 acc = mm16<D>(z, [&](int mm, int kk) { return X[mm][kk]; },
-                                  [&](int kk, int n) { return Y[n][kk]; }, lane);
+        const float(*X)[Lds::LD] = wave < 2 ? s.DO : s.DX;
+        const float(*Y)[Lds::LD] = (wave & 1) ? s.V : s.U;
+        const f32x4 acc = mm16_rows<D>(z, [&](int mm, int j) { return *(const f32x4 *)&X[mm][j]; },
+                                       [&](int n, int j) { return *(const f32x4 *)&Y[n][j]; }, lane);
         const bool strict = wave >= 2;   // dM_ba, dM_bk strictly lower
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -400,61 +464,73 @@ __global__ __launch_bounds__(D * 4) void chunk_grad_kernel(
     }
     __syncthreads();
 
-    // --- key-channel slice k0 .. k0 + 15 of this wave ---
+    // --- key-channel slice k0 .. k0 + 15 of this wave, as transposed tiles:
+    // lane (q, m) ends with channels k0 + 4q + i of token m ---
     const int k0 = 16 * wave;
-    auto ScT = [&](int kk, int n) { return Sc[(size_t)(k0 + n) * D + kk]; };
-    auto dYT = [&](int kk, int n) { return s.EGL[k0 + n] * dSe[(size_t)(k0 + n) * D + kk]; };
-    f32x4 dR = mm16<D>(z, [&](int mm, int kk) { return s.DO[mm][kk]; }, ScT, lane);
-    dR = mm16<kL>(dR, [&](int mm, int kk) { return s.M[DM_RA][mm][kk]; }, [&](int kk, int n) { return s.A[kk][k0 + n]; }, lane);
-    dR = mm16<kL>(dR, [&](int mm, int kk) { return s.M[DM_RK][mm][kk]; }, [&](int kk, int n) { return s.K[kk][k0 + n]; }, lane);
-    f32x4 dB = mm16<D>(z, [&](int mm, int kk) { return s.DX[mm][kk]; }, ScT, lane);
-    dB = mm16<kL>(dB, [&](int mm, int kk) { return s.M[DM_BA][mm][kk]; }, [&](int kk, int n) { return s.A[kk][k0 + n]; }, lane);
-    dB = mm16<kL>(dB, [&](int mm, int kk) { return s.M[DM_BK][mm][kk]; }, [&](int kk, int n) { return s.K[kk][k0 + n]; }, lane);
-    f32x4 dA = mm16<D>(z, [&](int mm, int kk) { return s.U[mm][kk]; }, dYT, lane);
-    dA = mm16<kL>(dA, [&](int mm, int kk) { return s.M[DM_RA][kk][mm]; }, [&](int kk, int n) { return s.R[kk][k0 + n]; }, lane);
-    dA = mm16<kL>(dA, [&](int mm, int kk) { return s.M[DM_BA][kk][mm]; }, [&](int kk, int n) { return s.B[kk][k0 + n]; }, lane);
-    f32x4 dK = mm16<D>(z, [&](int mm, int kk) { return s.V[mm][kk]; }, dYT, lane);
-    dK = mm16<kL>(dK, [&](int mm, int kk) { return s.M[DM_RK][kk][mm]; }, [&](int kk, int n) { return s.R[kk][k0 + n]; }, lane);
-    dK = mm16<kL>(dK, [&](int mm, int kk) { return s.M[DM_BK][kk][mm]; }, [&](int kk, int n) { return s.B[kk][k0 + n]; }, lane);
-    // chunk-end term of dw: sum_j dS'[ch][j] S'[ch][j] for channel ch = k0 + m
-    float dgl = 0.0f;
-    {
-        const size_t rowoff = (size_t)(k0 + m) * D;
-        for (int j = q; j < D; j += 4) dgl = fmaf(dSe[rowoff + j], Sn[rowoff + j], dgl);
-        dgl = xor_sum(xor_sum(dgl, 16), 32);
-    }
-    // token gradients; lane (q, m) holds tokens 4q + i of channel ch
-    const int ch = k0 + m;
-    float gr[4], gk[4], ga[4], gb[4];
+    const size_t rowm = (size_t)(k0 + m) * D;   // state row of channel k0 + m
+    auto Srow = [&](int mm, int j) { return *(const f32x4 *)(Sc + rowm + j); };
+    float dgl = 0.0f;   // sum_j dS'[k0+m][j] S'[k0+m][j], over this lane's j
+    auto dYrow = [&](int mm, int j) {
+        const f32x4 d = *(const f32x4 *)(dSe + rowm + j), sn = *(const f32x4 *)(Sn + rowm + j);
+        dgl += d[0] * sn[0] + d[1] * sn[1] + d[2] * sn[2] + d[3] * sn[3];
+        return d * s.EGL[k0 + m];
+    };
+    auto tile = [&](const float(*X)[Lds::LD]) { return [X](int n, int j) { return *(const f32x4 *)&X[n][j]; }; };
+    f32x4 dR = mm16_rows<D>(z, Srow, tile(s.DO), lane);
+    f32x4 dB = mm16_rows<D>(z, Srow, tile(s.DX), lane);
+    f32x4 dA = mm16_rows<D>(z, dYrow, tile(s.U), lane);
+    f32x4 dK = mm16_rows<D>(z, [&](int mm, int j) { return *(const f32x4 *)(dSe + rowm + j) * s.EGL[k0 + m]; },
+                            tile(s.V), lane);
+    dgl = xor_sum(xor_sum(dgl, 16), 32);   // channel k0 + m, in every lane of column m
+    // small terms: (dM X)^T = X^T dM^T and (dM^T X)^T = X^T dM
+    auto colT = [&](const float(*X)[Lds::LD]) { return [X, k0](int mm, int kk) { return X[kk][k0 + mm]; }; };
+    auto dMt = [&](int idx) { return [idx](int kk, int n) { return s.M[idx][n][kk]; }; };
+    auto dMn = [&](int idx) { return [idx](int kk, int n) { return s.M[idx][kk][n]; }; };
+    dR = mm16<kL>(dR, colT(s.A), dMt(DM_RA), lane);
+    dR = mm16<kL>(dR, colT(s.K), dMt(DM_RK), lane);
+    dB = mm16<kL>(dB, colT(s.A), dMt(DM_BA), lane);
+    dB = mm16<kL>(dB, colT(s.K), dMt(DM_BK), lane);
+    dA = mm16<kL>(dA, colT(s.R), dMn(DM_RA), lane);
+    dA = mm16<kL>(dA, colT(s.B), dMn(DM_BA), lane);
+    dK = mm16<kL>(dK, colT(s.R), dMn(DM_RK), lane);
+    dK = mm16<kL>(dK, colT(s.B), dMn(DM_BK), lane);
+
+    // token gradients of token t = m, channels ch = k0 + 4q .. + 3
+    const int t = m, ch = k0 + 4 * q;
+    const f32x4 G = *(const f32x4 *)&s.G[t][ch];
+    const f32x4 Gp = t ? *(const f32x4 *)&s.G[t - 1][ch] : z;
+    const f32x4 Rs = *(const f32x4 *)&s.R[t][ch], Bs = *(const f32x4 *)&s.B[t][ch];
+    const f32x4 As = *(const f32x4 *)&s.A[t][ch], Ks = *(const f32x4 *)&s.K[t][ch];
+    f32x4 gr, gb, ga, gk, gw;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int t = 4 * q + i;
-        const float G = s.G[t][ch], Gp = t ? s.G[t - 1][ch] : 0.0f;
-        const float eG = __expf(G), enG = __expf(-G), eGp = __expf(Gp);
+        const float eG = __expf(G[i]), enG = __expf(-G[i]), eGp = __expf(Gp[i]);
         gr[i] = dR[i] * eG;
         gb[i] = dB[i] * eGp;
         ga[i] = dA[i] * enG;
         gk[i] = dK[i] * enG;
         // raw (masked) operands are the scaled ones times the inverse factors
-        const float rr = s.R[t][ch] * enG, kk = s.K[t][ch] * eG, aa = s.A[t][ch] * eG;
-        const float bv = s.B[t][ch] * (t ? __expf(-Gp) : 1.0f);
-        s.P[wave][0][t][m] = gr[i] * rr - ga[i] * aa - gk[i] * kk;
-        s.P[wave][1][t][m] = gb[i] * bv;
+        const float rr = Rs[i] * enG, kk = Ks[i] * eG, aa = As[i] * eG, bv = Bs[i] * __expf(-Gp[i]);
+        const float p = gr[i] * rr - ga[i] * aa - gk[i] * kk;
+        const float qb = gb[i] * bv;
+        // dG_t = p_t + qb_{t+1} (+ the chunk-end term at t = 15), then the
+        // suffix sum over t = m .. 15 within the 16-lane row
+        const float dglc = __shfl(dgl, 4 * q + i, 16);   // channel ch + i (every lane takes part)
+        float y = p + row_shl<1>(qb, 0.0f) + (t == kL - 1 ? dglc : 0.0f);
+        y += row_shl<1>(y, 0.0f);
+        y += row_shl<2>(y, 0.0f);
+        y += row_shl<4>(y, 0.0f);
+        y += row_shl<8>(y, 0.0f);
+        gw[i] = y;
     }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = 4 * q + i;
-        if (t >= Lc) continue;
-        float acc = dgl;
-        for (int u = kL - 1; u >= t; --u) acc += s.P[wave][0][u][m] + (u + 1 < kL ? s.P[wave][1][u + 1][m] : 0.0f);
+    if (t < Lc) {
         const bool up = s.upd[t] != 0;
         const size_t gi = tokbase + (size_t)t * H * D + ch;
-        io<T_IO>::store(dr, gi, gr[i]);
-        io<T_IO>::store(dw, gi, up ? acc : 0.0f);
-        io<T_IO>::store(dk, gi, up ? gk[i] : 0.0f);
-        io<T_IO>::store(da, gi, up ? ga[i] : 0.0f);
-        io<T_IO>::store(db, gi, up ? gb[i] : 0.0f);
+        io4<T_IO>::store(dr, gi, gr);
+        io4<T_IO>::store(dw, gi, up ? gw : z);
+        io4<T_IO>::store(dk, gi, up ? gk : z);
+        io4<T_IO>::store(da, gi, up ? ga : z);
+        io4<T_IO>::store(db, gi, up ? gb : z);
     }
 }
 
