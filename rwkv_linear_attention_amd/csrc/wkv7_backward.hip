@@ -122,8 +122,8 @@ __global__ __launch_bounds__(D * 4) void dstate_chain_kernel(
                     p3 += s_a[tl][row0 + i + 3] * dS[i + 3];
                 }
                 float ad = (p0 + p1) + (p2 + p3);
-                ad = xor_sum(ad, 16);
-                ad = xor_sum(ad, 32);
+                ad = xsum16(ad);
+                ad = xsum32(ad);
 #pragma unroll
                 for (int i = 0; i < RPL; ++i) dS[i] = fmaf(s_ew[tl][row0 + i], dS[i], s_b[tl][row0 + i] * ad);
             }
@@ -189,7 +189,7 @@ __device__ void chunk_grad_exact(GradLds<D> &s, const float *Sc, const float *dS
     constexpr int RPL = D / 4, NW = D / 16;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int col = wave * 16 + (lane & 15), g = lane >> 4, row0 = g * RPL;
-    auto colsum = [](float x) { return xor_sum(xor_sum(x, 16), 32); };
+    auto colsum = [](float x) { return xsum32(xsum16(x)); };
     const auto &W = s.U;
     auto step = [&](float *P, int u) {   // P <- state after token u (P = state before it)
         if (!s.upd[u]) return;
@@ -481,7 +481,7 @@ __global__ __launch_bounds__(D * 4) void chunk_grad_kernel(
     f32x4 dA = mm16_rows<D>(z, dYrow, tile(s.U), lane);
     f32x4 dK = mm16_rows<D>(z, [&](int mm, int j) { return *(const f32x4 *)(dSe + rowm + j) * s.EGL[k0 + m]; },
                             tile(s.V), lane);
-    dgl = xor_sum(xor_sum(dgl, 16), 32);   // channel k0 + m, in every lane of column m
+    dgl = xsum32(xsum16(dgl));   // channel k0 + m, in every lane of column m
     // small terms: (dM X)^T = X^T dM^T and (dM^T X)^T = X^T dM
     auto colT = [&](const float(*X)[Lds::LD]) { return [X, k0](int mm, int kk) { return X[kk][k0 + mm]; }; };
     auto dMt = [&](int idx) { return [idx](int kk, int n) { return s.M[idx][n][kk]; }; };

@@ -277,8 +277,8 @@ __device__ __forceinline__ void gdn_scalars(RawTile<D> &rt, uint32_t gbits, floa
             nk = fmaf(kv[e], kv[e], nk);
         }
     }
-    nq = xor_sum(xor_sum(nq, 16), 32);
-    nk = xor_sum(xor_sum(nk, 16), 32);
+    nq = xsum32(xsum16(nq));
+    nk = xsum32(xsum16(nk));
     const float iq = 1.0f / sqrtf(nq + 1e-6f), ik = 1.0f / sqrtf(nk + 1e-6f);
     const float gate = bf16_bits_to_f32((uint16_t)gbits);
     sc[0] = iq;
@@ -555,7 +555,7 @@ __device__ void ws_chunk_exact(f32x4 (*S)[WS<D>::NT], const uint16_t *r, const u
                     for (int i = 0; i < 4; ++i) sb[n] = fmaf(be[i], S[q][n][i], sb[n]);
             }
 #pragma unroll
-            for (int n = 0; n < NT; ++n) sb[n] = xor_sum(xor_sum(sb[n], 16), 32);
+            for (int n = 0; n < NT; ++n) sb[n] = xsum32(xsum16(sb[n]));
             float vj[NT];
 #pragma unroll
             for (int n = 0; n < NT; ++n) vj[n] = bf16_bits_to_f32(v[base + cbase + 16 * n + j]);
@@ -589,7 +589,7 @@ __device__ void ws_chunk_exact(f32x4 (*S)[WS<D>::NT], const uint16_t *r, const u
                 for (int i = 0; i < 4; ++i) ov[n] = fmaf(re[i], S[q][n][i], ov[n]);
         }
 #pragma unroll
-        for (int n = 0; n < NT; ++n) ov[n] = xor_sum(xor_sum(ov[n], 16), 32);
+        for (int n = 0; n < NT; ++n) ov[n] = xsum32(xsum16(ov[n]));
         if (g == 0) {
 #pragma unroll
             for (int n = 0; n < NT; ++n) o[base + cbase + 16 * n + j] = f32_to_bf16_bits(ov[n]);
@@ -633,8 +633,8 @@ __device__ void ws_chunk_exact_gdn(f32x4 (*S)[WS<D>::NT], const uint16_t *q, con
                 nk = fmaf(ke[i], ke[i], nk);
             }
         }
-        nq = xor_sum(xor_sum(nq, 16), 32);
-        nk = xor_sum(xor_sum(nk, 16), 32);
+        nq = xsum32(xsum16(nq));
+        nk = xsum32(xsum16(nk));
         const float iq = 1.0f / sqrtf(nq + 1e-6f), ik = 1.0f / sqrtf(nk + 1e-6f);
         const float alpha = __expf(gate);
         float ks[NT] = {};
@@ -649,7 +649,7 @@ __device__ void ws_chunk_exact_gdn(f32x4 (*S)[WS<D>::NT], const uint16_t *q, con
                 for (int i = 0; i < 4; ++i) ks[n] = fmaf(ke[i] * ik, S[qi][n][i], ks[n]);
         }
 #pragma unroll
-        for (int n = 0; n < NT; ++n) ks[n] = xor_sum(xor_sum(ks[n], 16), 32);
+        for (int n = 0; n < NT; ++n) ks[n] = xsum32(xsum16(ks[n]));
         float vj[NT];
 #pragma unroll
         for (int n = 0; n < NT; ++n) vj[n] = bf16_bits_to_f32(v[base + cbase + 16 * n + j]);
@@ -678,7 +678,7 @@ __device__ void ws_chunk_exact_gdn(f32x4 (*S)[WS<D>::NT], const uint16_t *q, con
                 for (int i = 0; i < 4; ++i) ov[n] = fmaf(qe[i] * iq, S[qi][n][i], ov[n]);
         }
 #pragma unroll
-        for (int n = 0; n < NT; ++n) ov[n] = xor_sum(xor_sum(ov[n], 16), 32);
+        for (int n = 0; n < NT; ++n) ov[n] = xsum32(xsum16(ov[n]));
         if (g == 0) {
 #pragma unroll
             for (int n = 0; n < NT; ++n) o[base + cbase + 16 * n + j] = f32_to_bf16_bits(ov[n]);

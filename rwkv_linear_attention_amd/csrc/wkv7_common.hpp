@@ -76,6 +76,24 @@ __device__ __forceinline__ float row_scan16(float x) {
 
 __device__ __forceinline__ float xor_sum(float x, int mask) { return x + __shfl_xor(x, mask, kWave); }
 
+// x plus its value in the lane 16 (32) apart, with gfx950's lane-swap VALU
+// instructions instead of an LDS permute: permlane16_swap exchanges the odd
+// 16-lane rows of one operand with the even rows of the other, so with x in
+// both operands the two results hold x and its partner (in some order) in
+// every lane; permlane32_swap does the same for the two 32-lane halves.
+// Addition is commutative, so the sums equal x + shfl_xor(x, 16 / 32) bit
+// for bit.
+__device__ __forceinline__ float xsum16(float x)
+{
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float xsum32(float x)
+{
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
 // ---- MFMA ----------------------------------------------------------------
 // 16x16x32 bf16: lane l supplies A[m = l%16][8 k-slots of group l/16] and
 // B[8 k-slots of group l/16][n = l%16]; the accumulator holds

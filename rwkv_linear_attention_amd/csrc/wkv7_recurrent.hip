@@ -167,8 +167,8 @@ __global__ __launch_bounds__(D * 4) void recurrent_kernel(
                     p3 += s_b[tl][row0 + i + 3] * S[i + 3];
                 }
                 float sb = (p0 + p1) + (p2 + p3);
-                sb = xor_sum(sb, 16);
-                sb = xor_sum(sb, 32);
+                sb = xsum16(sb);
+                sb = xsum32(sb);
                 const float vj = s_v[tl][col];
 #pragma unroll
                 for (int i = 0; i < RPL; ++i)
@@ -183,8 +183,8 @@ __global__ __launch_bounds__(D * 4) void recurrent_kernel(
                 q3 += s_r[tl][row0 + i + 3] * S[i + 3];
             }
             float ov = (q0 + q1) + (q2 + q3);
-            ov = xor_sum(ov, 16);
-            ov = xor_sum(ov, 32);
+            ov = xsum16(ov);
+            ov = xsum32(ov);
             if (g == 0 && o) io<T_IO>::store(o, ((tok0 + t0 + tl) * H + h) * D + col, ov);
         }
     }
