@@ -9,13 +9,13 @@
 // Its reverse-mode derivative carries dS = dL/dS_t backwards:
 //   dS += r_t d_o_t^T;   dS_{t-1} = diag(e^{w_t}) dS + b_t (a_t^T dS).
 //
-// Three launches, with a caller-provided workspace and no allocation:
-//  1. the recurrent forward kernel in fp32 writes the state before every
-//     16-token chunk and after the last one (checkpoints);
-//  2. dstate_chain_kernel runs the dS recurrence backwards in fp32 (one
-//     workgroup per (b, h)) and stores, for every chunk, the gradient of the
-//     state at the chunk's end with respect to everything after the chunk;
-//  3. chunk_grad_kernel (one workgroup per (b, h, chunk), all chunks in
+// Two launches, with a caller-provided workspace and no allocation:
+//  1. recur_pair_kernel runs, side by side, (a) the forward recurrence in
+//     fp32, storing the state before every 16-token chunk and after the last
+//     one (checkpoints), and (b) the dS recurrence backwards in fp32, storing
+//     for every chunk the gradient of the state at the chunk's end with
+//     respect to everything after the chunk;
+//  2. chunk_grad_kernel (one workgroup per (b, h, chunk), all chunks in
 //     parallel) recomputes the chunk in its unrolled form from the chunk's
 //     checkpoint and turns that end gradient into the token gradients.
 //
@@ -64,74 +64,128 @@ __device__ __forceinline__ f32x4 mm16(f32x4 acc, FA fa, FB fb, int lane)
     return acc;
 }
 
-// ---- 2. reverse state-gradient chain ------------------------------------------
+// ---- 1 + 2. the two recurrences, in one launch --------------------------------
 
-// One workgroup per (b, h), D/16 waves; lane (j, g) of wave w holds rows
-// [g D/4, (g+1) D/4) of column 16w + j of dS.  dck[bh][c] receives, for
-// chunk c, dL/dS at the chunk's last token from everything after it.
+// 2 B H workgroups of D/16 waves.  Workgroups [0, nbh) run the forward
+// recurrence of (b, h) and store the state before every 16-token chunk and
+// after the last one: ckpt[bh][c], c = 0 .. nck.  Workgroups [nbh, 2 nbh) run
+// the state-gradient recurrence backwards and store, for every chunk, dL/dS
+// at the chunk's last token from everything after it: dck[bh][c].  Neither
+// needs the other's result, so the two latency-bound loops run side by side.
+// Lane (j, g) of wave w holds rows [g D/4, (g+1) D/4) of column 16w + j.
+// At most 128 VGPRs (four waves per SIMD): two workgroups share a compute
+// unit also at D = 128.
 template <int D, typename T_IO>
-__global__ __launch_bounds__(D * 4) void dstate_chain_kernel(
-    int T, int H, const T_IO *__restrict__ r, const T_IO *__restrict__ w, const T_IO *__restrict__ a,
-    const T_IO *__restrict__ b, const uint8_t *__restrict__ mask, const T_IO *__restrict__ d_o,
-    const float *__restrict__ d_sf, float *__restrict__ dck, float *__restrict__ d_s0)
+__global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(4))) void recur_pair_kernel(
+    int T, int H, int nbh, const T_IO *__restrict__ r, const T_IO *__restrict__ w,
+    const T_IO *__restrict__ k, const T_IO *__restrict__ v, const T_IO *__restrict__ a,
+    const T_IO *__restrict__ b, const float *__restrict__ s0, const uint8_t *__restrict__ mask,
+    const T_IO *__restrict__ d_o, const float *__restrict__ d_sf, float *__restrict__ ckpt,
+    float *__restrict__ dck, float *__restrict__ d_s0)
 {
     constexpr int TB = kL, RPL = D / 4, NT = D * 4;
-    __shared__ float s_ew[TB][D], s_a[TB][D], s_b[TB][D], s_r[TB][D], s_do[TB][D];
+    // forward: e^w, a, b, k, v; backward: e^w, a, b, r, d_o
+    __shared__ float s_x[5][TB][D];
     __shared__ int s_upd[TB];
-    const int bh = blockIdx.x, bb = bh / H, h = bh % H;
+    const bool fwd = (int)blockIdx.x < nbh;
+    const int bh = fwd ? (int)blockIdx.x : (int)blockIdx.x - nbh;
+    const int bb = bh / H, h = bh % H;
     const size_t tok0 = (size_t)bb * T;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int col = wave * 16 + (lane & 15), g = lane >> 4, row0 = g * RPL;
     const size_t st = (size_t)bh * D * D;
-    float dS[RPL];
-#pragma unroll
-    for (int i = 0; i < RPL; ++i) dS[i] = d_sf ? d_sf[st + (size_t)(row0 + i) * D + col] : 0.0f;
     const int nck = (T + TB - 1) / TB;
-    for (int c = nck - 1; c >= 0; --c) {
+    const T_IO *const src[2][5] = {{w, a, b, k, v}, {w, a, b, r, d_o}};
+    auto stage = [&](int c) {
         const int t0 = c * TB, nt = min(TB, T - t0);
-        float *out = dck + ((size_t)bh * nck + c) * D * D;
-#pragma unroll
-        for (int i = 0; i < RPL; ++i) out[(size_t)(row0 + i) * D + col] = dS[i];
-        __syncthreads();
+#pragma unroll 1
         for (int idx = tid; idx < TB * D; idx += NT) {
             const int tl = idx / D, ch = idx % D;
-            float ew = 1.f, av = 0.f, bv = 0.f, rv = 0.f, dv = 0.f;
-            if (tl < nt) {
-                const size_t gi = ((tok0 + t0 + tl) * H + h) * D + ch;
-                ew = __expf(io<T_IO>::load(w, gi));
-                av = io<T_IO>::load(a, gi);
-                bv = io<T_IO>::load(b, gi);
-                rv = io<T_IO>::load(r, gi);
-                dv = io<T_IO>::load(d_o, gi);
+            const size_t gi = ((tok0 + t0 + tl) * H + h) * D + ch;
+#pragma unroll
+            for (int e = 0; e < 5; ++e) {
+                const float x = tl < nt ? io<T_IO>::load(src[fwd ? 0 : 1][e], gi) : 0.0f;
+                s_x[e][tl][ch] = e == 0 ? __expf(x) : x;
             }
-            s_ew[tl][ch] = ew; s_a[tl][ch] = av; s_b[tl][ch] = bv; s_r[tl][ch] = rv; s_do[tl][ch] = dv;
         }
         if (tid < TB) s_upd[tid] = (tid < nt) && (mask ? mask[tok0 + t0 + tid] != 0 : 1);
-        __syncthreads();
-        for (int tl = nt - 1; tl >= 0; --tl) {
-            const float doj = s_do[tl][col];
+        return nt;
+    };
+    float X[RPL];
+    if (fwd) {
 #pragma unroll
-            for (int i = 0; i < RPL; ++i) dS[i] = fmaf(s_r[tl][row0 + i], doj, dS[i]);
-            if (s_upd[tl]) {
+        for (int i = 0; i < RPL; ++i) X[i] = s0 ? s0[st + (size_t)(row0 + i) * D + col] : 0.0f;
+        float *ck = ckpt + (size_t)bh * (nck + 1) * D * D;
+        for (int c = 0; c < nck; ++c) {
+            // stores through one running pointer: unrolled, the compiler
+            // keeps a 64-bit address per row live across the chunk loop
+            float *pst = ck + (size_t)c * D * D + (size_t)row0 * D + col;
+#pragma unroll
+            for (int i = 0; i < RPL; ++i) {
+                *pst = X[i];
+                pst += D;
+                asm volatile("" : "+v"(pst));
+            }
+            __syncthreads();
+            const int nt = stage(c);
+            __syncthreads();
+#pragma unroll 1
+            for (int tl = 0; tl < nt; ++tl) {
+                if (!s_upd[tl]) continue;
                 float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
 #pragma unroll
                 for (int i = 0; i < RPL; i += 4) {
-                    p0 += s_a[tl][row0 + i + 0] * dS[i + 0];
-                    p1 += s_a[tl][row0 + i + 1] * dS[i + 1];
-                    p2 += s_a[tl][row0 + i + 2] * dS[i + 2];
-                    p3 += s_a[tl][row0 + i + 3] * dS[i + 3];
+                    p0 += s_x[2][tl][row0 + i + 0] * X[i + 0];
+                    p1 += s_x[2][tl][row0 + i + 1] * X[i + 1];
+                    p2 += s_x[2][tl][row0 + i + 2] * X[i + 2];
+                    p3 += s_x[2][tl][row0 + i + 3] * X[i + 3];
                 }
-                float ad = (p0 + p1) + (p2 + p3);
-                ad = xsum16(ad);
-                ad = xsum32(ad);
+                const float sb = xsum32(xsum16((p0 + p1) + (p2 + p3)));
+                const float vj = s_x[4][tl][col];
 #pragma unroll
-                for (int i = 0; i < RPL; ++i) dS[i] = fmaf(s_ew[tl][row0 + i], dS[i], s_b[tl][row0 + i] * ad);
+                for (int i = 0; i < RPL; ++i)
+                    X[i] = fmaf(s_x[0][tl][row0 + i], X[i], fmaf(s_x[1][tl][row0 + i], sb, s_x[3][tl][row0 + i] * vj));
             }
         }
-    }
-    if (d_s0) {
 #pragma unroll
-        for (int i = 0; i < RPL; ++i) d_s0[st + (size_t)(row0 + i) * D + col] = dS[i];
+        for (int i = 0; i < RPL; ++i) ck[(size_t)nck * D * D + (size_t)(row0 + i) * D + col] = X[i];
+    } else {
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) X[i] = d_sf ? d_sf[st + (size_t)(row0 + i) * D + col] : 0.0f;
+        for (int c = nck - 1; c >= 0; --c) {
+            float *pst = dck + ((size_t)bh * nck + c) * D * D + (size_t)row0 * D + col;
+#pragma unroll
+            for (int i = 0; i < RPL; ++i) {
+                *pst = X[i];
+                pst += D;
+                asm volatile("" : "+v"(pst));
+            }
+            __syncthreads();
+            const int nt = stage(c);
+            __syncthreads();
+#pragma unroll 1
+            for (int tl = nt - 1; tl >= 0; --tl) {
+                const float doj = s_x[4][tl][col];
+#pragma unroll
+                for (int i = 0; i < RPL; ++i) X[i] = fmaf(s_x[3][tl][row0 + i], doj, X[i]);
+                if (!s_upd[tl]) continue;
+                float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
+#pragma unroll
+                for (int i = 0; i < RPL; i += 4) {
+                    p0 += s_x[1][tl][row0 + i + 0] * X[i + 0];
+                    p1 += s_x[1][tl][row0 + i + 1] * X[i + 1];
+                    p2 += s_x[1][tl][row0 + i + 2] * X[i + 2];
+                    p3 += s_x[1][tl][row0 + i + 3] * X[i + 3];
+                }
+                const float ad = xsum32(xsum16((p0 + p1) + (p2 + p3)));
+#pragma unroll
+                for (int i = 0; i < RPL; ++i) X[i] = fmaf(s_x[0][tl][row0 + i], X[i], s_x[2][tl][row0 + i] * ad);
+            }
+        }
+        if (d_s0) {
+#pragma unroll
+            for (int i = 0; i < RPL; ++i) d_s0[st + (size_t)(row0 + i) * D + col] = X[i];
+        }
     }
 }
 
@@ -541,15 +595,11 @@ hipError_t launch_bwd_d(const BwdArgs &p, hipStream_t stream)
     const size_t nbh = (size_t)p.B * p.H;
     float *ckpt = (float *)p.ws;
     float *dck = ckpt + nbh * (nck + 1) * D * D;
-    FwdArgs fa{p.B, p.T, p.H, D, p.r, p.w, p.k, p.v, p.a, p.b, p.s0, p.mask, nullptr, nullptr};
-    fa.n_state = p.B;
-    fa.ckpt = ckpt;
-    hipError_t e = launch_recurrent(sizeof(T_IO) == 4 ? 0 : 1, fa, stream);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((dstate_chain_kernel<D, T_IO>), dim3((unsigned)nbh), dim3(D * 4), 0, stream, p.T, p.H,
-                       (const T_IO *)p.r, (const T_IO *)p.w, (const T_IO *)p.a, (const T_IO *)p.b, p.mask,
-                       (const T_IO *)p.d_o, p.d_sf, dck, p.d_s0);
-    e = hipGetLastError();
+    hipLaunchKernelGGL((recur_pair_kernel<D, T_IO>), dim3((unsigned)(2 * nbh)), dim3(D * 4), 0, stream, p.T,
+                       p.H, (int)nbh, (const T_IO *)p.r, (const T_IO *)p.w, (const T_IO *)p.k,
+                       (const T_IO *)p.v, (const T_IO *)p.a, (const T_IO *)p.b, p.s0, p.mask,
+                       (const T_IO *)p.d_o, p.d_sf, ckpt, dck, p.d_s0);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((chunk_grad_kernel<D, T_IO>), dim3((unsigned)(nbh * nck)), dim3(D * 4), 0, stream, p.T,
                        p.H, nck, (const T_IO *)p.r, (const T_IO *)p.w, (const T_IO *)p.k, (const T_IO *)p.v,

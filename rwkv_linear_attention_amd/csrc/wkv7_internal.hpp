@@ -24,10 +24,6 @@ struct FwdArgs {
     // Gated DeltaNet inputs in the same slots: r = q, k = k, v = v,
     // w = gate g and a = strength beta, both one value per token and head.
     bool gdn = false;
-    // Recurrent kernel only: state checkpoints before every 16-token block
-    // and after the last, [B*H][ceil(T/16) + 1][D][D] fp32 (o may then be
-    // nullptr).
-    float *ckpt = nullptr;
 };
 
 // Backward (fixed-length form): gradients of the forward for upstream d_o

@@ -32,9 +32,9 @@ __global__ __launch_bounds__(D * 4) void recurrent_kernel(
     int n_state, const T_IO *__restrict__ r, const T_IO *__restrict__ w,
     const T_IO *__restrict__ k, const T_IO *__restrict__ v, const T_IO *__restrict__ a,
     const T_IO *__restrict__ b, const float *__restrict__ s0, const uint8_t *__restrict__ mask,
-    T_IO *__restrict__ o, float *__restrict__ sf, float *__restrict__ ckpt)
+    T_IO *__restrict__ o, float *__restrict__ sf)
 {
-    constexpr int TB = 16;          // tokens staged per block (= checkpoint interval)
+    constexpr int TB = 16;          // tokens staged per block
     constexpr int RPL = D / 4;      // state rows per lane
     constexpr int NT = D * 4;       // threads
     __shared__ float s_ew[TB][D], s_a[TB][D], s_b[TB][D], s_k[TB][D], s_r[TB][D], s_v[TB][D];
@@ -79,16 +79,8 @@ __global__ __launch_bounds__(D * 4) void recurrent_kernel(
         for (int i = 0; i < RPL; ++i) S[i] = s0[st_in + (size_t)(row0 + i) * D + col];
     }
 
-    // Checkpoints (backward support): the state before every 16-token block
-    // and after the last one, [B*H][ceil(Tn/16) + 1][D][D].
-    const int nck = (Tn + TB - 1) / TB;
-    float *const ck = ckpt ? ckpt + (size_t)bh * (nck + 1) * D * D : nullptr;
     for (int t0 = 0; t0 < Tn; t0 += TB) {
         const int nt = min(TB, Tn - t0);
-        if (ck) {
-#pragma unroll
-            for (int i = 0; i < RPL; ++i) ck[(size_t)(t0 / TB) * D * D + (size_t)(row0 + i) * D + col] = S[i];
-        }
         __syncthreads();
         if constexpr (GDN) {
             // stage q, k, v and the per-token gate and strength
@@ -185,12 +177,8 @@ __global__ __launch_bounds__(D * 4) void recurrent_kernel(
             float ov = (q0 + q1) + (q2 + q3);
             ov = xsum16(ov);
             ov = xsum32(ov);
-            if (g == 0 && o) io<T_IO>::store(o, ((tok0 + t0 + tl) * H + h) * D + col, ov);
+            if (g == 0) io<T_IO>::store(o, ((tok0 + t0 + tl) * H + h) * D + col, ov);
         }
-    }
-    if (ck) {
-#pragma unroll
-        for (int i = 0; i < RPL; ++i) ck[(size_t)nck * D * D + (size_t)(row0 + i) * D + col] = S[i];
     }
     if (sf) {
 #pragma unroll
@@ -206,13 +194,13 @@ static hipError_t launch_rec(const FwdArgs &p, hipStream_t stream)
         hipLaunchKernelGGL((recurrent_kernel<D, T_IO, true>), grid, block, 0, stream, p.T, p.H, p.cu_seqlens,
                            p.state_map, p.n_state,
                            (const T_IO *)p.r, (const T_IO *)p.w, (const T_IO *)p.k, (const T_IO *)p.v,
-                           (const T_IO *)p.a, (const T_IO *)p.b, p.s0, p.mask, (T_IO *)p.o, p.sf, p.ckpt);
+                           (const T_IO *)p.a, (const T_IO *)p.b, p.s0, p.mask, (T_IO *)p.o, p.sf);
         return hipGetLastError();
     }
     hipLaunchKernelGGL((recurrent_kernel<D, T_IO, false>), grid, block, 0, stream, p.T, p.H, p.cu_seqlens,
                        p.state_map, p.n_state,
                        (const T_IO *)p.r, (const T_IO *)p.w, (const T_IO *)p.k, (const T_IO *)p.v,
-                       (const T_IO *)p.a, (const T_IO *)p.b, p.s0, p.mask, (T_IO *)p.o, p.sf, p.ckpt);
+                       (const T_IO *)p.a, (const T_IO *)p.b, p.s0, p.mask, (T_IO *)p.o, p.sf);
     return hipGetLastError();
 }
 
