@@ -112,8 +112,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--all", action="store_true",
-                    help="also time the head-size-128 workload, a packed variable-length batch and the "
-                         "256-step decode")
+                    help="also time the head-size-128 workload, a packed variable-length batch, Gated "
+                         "DeltaNet, the backward and the 256-step decode")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (reference for HBM byte counters)")
     ap.add_argument("--dispatch-sweep", action="store_true",
@@ -301,6 +301,40 @@ def gdn_workload(steps, warmup):
                    "kernel": "chunked d64 (Gated DeltaNet)"}}
 
 
+def bwd_workload(steps, warmup, idx):
+    """Backward (wkv7_bwd) on a forward workload's shape and inputs, with a
+    seeded N(0, 1) output gradient rounded to bf16; the initial state and the
+    mask of the workload are used, no final-state gradient."""
+    import numpy as np
+    import torch
+    from rwkv_linear_attention_amd import synth, wkv7
+    wl = synth.WORKLOADS[idx]
+    B, T, H, D = wl["B"], wl["T"], wl["H"], wl["K"]
+    print(f"[bench] generating backward workload on {wl['name']}", file=sys.stderr, flush=True)
+    inp = synth.make(idx)
+    names = ("r", "w", "k", "v", "a", "b")
+    dev = {n: synth.to_torch(inp[n], "bf16", "cuda") for n in names}
+    s0 = None if inp["s0"] is None else torch.from_numpy(inp["s0"]).cuda()
+    mask = None if inp["mask"] is None else torch.from_numpy(inp["mask"]).cuda()
+    rng = np.random.default_rng(1400 + idx)
+    d_o = synth.to_torch(rng.standard_normal((B, T, H, D), dtype=np.float32), "bf16", "cuda")
+    del inp
+    ws = torch.empty(wkv7.bwd_workspace_bytes(B, T, H, D, D), dtype=torch.uint8, device="cuda")
+    ms = _time_launches(lambda i: wkv7.bwd(*(dev[n] for n in names), d_o, initial_state=s0, mask=mask,
+                                           workspace=ws), max(3, steps // 4), max(1, warmup // 4))
+    tok = B * T * H * D * 2
+    st = B * H * D * D * 4
+    # inputs and d_o read once, six gradients written once, the initial
+    # state read (if any) and its gradient written, the mask once
+    nbytes = 7 * tok + 6 * tok + (st if s0 is not None else 0) + st + (B * T if mask is not None else 0)
+    name = "bwd_" + wl["name"].replace("fwd_", "")
+    return {name: {"ms": round(ms, 4), "Mtokens_per_s": round(B * T / ms / 1e3, 3),
+                   "GB_per_s": round(nbytes / ms / 1e6, 1),
+                   "frac_of_8TBps": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes,
+                   "workspace_bytes": ws.numel(),
+                   "kernel": f"recurrences + per-chunk gradients, d{D}"}}
+
+
 def _time_launches(fn, steps, warmup):
     import torch
     settle(lambda: fn(0))
@@ -319,8 +353,9 @@ def _time_launches(fn, steps, warmup):
 
 def other_workloads(steps, warmup):
     """Head size 128 forward (B16 T4096 H32, trailing-padding mask, S0), the
-    packed variable-length forward, Gated DeltaNet (B8 T4096 H64 d64) and the
-    decode step (B512 H40 d64, 256 consecutive in-place steps)."""
+    packed variable-length forward, Gated DeltaNet (B8 T4096 H64 d64), the
+    backward on the d64 and d128 shapes and the decode step (B512 H40 d64,
+    256 consecutive in-place steps)."""
     import torch
     from rwkv_linear_attention_amd import synth, wkv7
     out = {}
@@ -346,6 +381,10 @@ def other_workloads(steps, warmup):
     out.update(varlen_workload(steps, warmup))
     torch.cuda.empty_cache()
     out.update(gdn_workload(steps, warmup))
+    torch.cuda.empty_cache()
+    out.update(bwd_workload(steps, warmup, 2))
+    torch.cuda.empty_cache()
+    out.update(bwd_workload(steps, warmup, 3))
     torch.cuda.empty_cache()
 
     wl = synth.WORKLOADS[4]

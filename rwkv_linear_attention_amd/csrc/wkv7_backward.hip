@@ -223,9 +223,11 @@ template <int D> struct alignas(16) GradLds {
     float R[kL][LD], B[kL][LD], A[kL][LD], K[kL][LD], V[kL][LD], DO[kL][LD];
     float G[kL][LD];                    // decay prefix
     float U[kL][LD], DX[kL][LD];        // X, then U; dU, then dX (exact path: raw w in U)
-    float M[9][kL][kL + 1];             // M_ba, M_bk, M_ra, M_rk, T, dM_ra, dM_rk, dM_ba, dM_bk
+    union {                             // the exact path needs no chunk matrices
+        float M[9][kL][kL + 1];         // M_ba, M_bk, M_ra, M_rk, T, dM_ra, dM_rk, dM_ba, dM_bk
+        float RED[5][D / 16][D];        // exact path: per-wave row sums
+    };
     float EGL[D];
-    float RED[5][D / 16][D];            // exact path: per-wave row sums
     int upd[kL];
 };
 
