@@ -10,11 +10,11 @@
 //   dS += r_t d_o_t^T;   dS_{t-1} = diag(e^{w_t}) dS + b_t (a_t^T dS).
 //
 // Two launches, with a caller-provided workspace and no allocation:
-//  1. recur_pair_kernel runs, side by side, (a) the forward recurrence in
-//     fp32, storing the state before every 16-token chunk and after the last
-//     one (checkpoints), and (b) the dS recurrence backwards in fp32, storing
-//     for every chunk the gradient of the state at the chunk's end with
-//     respect to everything after the chunk;
+//  1. chain_kernel runs, side by side, (a) the forward recurrence in chunk
+//     form, storing the state before every 16-token chunk and after the last
+//     one (checkpoints), and (b) the dS recurrence backwards in chunk form,
+//     storing for every chunk the gradient of the state at the chunk's end
+//     with respect to everything after the chunk;
 //  2. chunk_grad_kernel (one workgroup per (b, h, chunk), all chunks in
 //     parallel) recomputes the chunk in its unrolled form from the chunk's
 //     checkpoint and turns that end gradient into the token gradients.
@@ -64,138 +64,30 @@ __device__ __forceinline__ f32x4 mm16(f32x4 acc, FA fa, FB fb, int lane)
     return acc;
 }
 
-// ---- 1 + 2. the two recurrences, in one launch --------------------------------
-
-// 2 B H workgroups of D/16 waves.  Workgroups [0, nbh) run the forward
-// recurrence of (b, h) and store the state before every 16-token chunk and
-// after the last one: ckpt[bh][c], c = 0 .. nck.  Workgroups [nbh, 2 nbh) run
-// the state-gradient recurrence backwards and store, for every chunk, dL/dS
-// at the chunk's last token from everything after it: dck[bh][c].  Neither
-// needs the other's result, so the two latency-bound loops run side by side.
-// Lane (j, g) of wave w holds rows [g D/4, (g+1) D/4) of column 16w + j.
-// At most 128 VGPRs (four waves per SIMD): two workgroups share a compute
-// unit also at D = 128.
-template <int D, typename T_IO>
-__global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(4))) void recur_pair_kernel(
-    int T, int H, int nbh, const T_IO *__restrict__ r, const T_IO *__restrict__ w,
-    const T_IO *__restrict__ k, const T_IO *__restrict__ v, const T_IO *__restrict__ a,
-    const T_IO *__restrict__ b, const float *__restrict__ s0, const uint8_t *__restrict__ mask,
-    const T_IO *__restrict__ d_o, const float *__restrict__ d_sf, float *__restrict__ ckpt,
-    float *__restrict__ dck, float *__restrict__ d_s0)
-{
-    constexpr int TB = kL, RPL = D / 4, NT = D * 4;
-    // forward: e^w, a, b, k, v; backward: e^w, a, b, r, d_o
-    __shared__ float s_x[5][TB][D];
-    __shared__ int s_upd[TB];
-    const bool fwd = (int)blockIdx.x < nbh;
-    const int bh = fwd ? (int)blockIdx.x : (int)blockIdx.x - nbh;
-    const int bb = bh / H, h = bh % H;
-    const size_t tok0 = (size_t)bb * T;
-    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-    const int col = wave * 16 + (lane & 15), g = lane >> 4, row0 = g * RPL;
-    const size_t st = (size_t)bh * D * D;
-    const int nck = (T + TB - 1) / TB;
-    const T_IO *const src[2][5] = {{w, a, b, k, v}, {w, a, b, r, d_o}};
-    auto stage = [&](int c) {
-        const int t0 = c * TB, nt = min(TB, T - t0);
-#pragma unroll 1
-        for (int idx = tid; idx < TB * D; idx += NT) {
-            const int tl = idx / D, ch = idx % D;
-            const size_t gi = ((tok0 + t0 + tl) * H + h) * D + ch;
-#pragma unroll
-            for (int e = 0; e < 5; ++e) {
-                const float x = tl < nt ? io<T_IO>::load(src[fwd ? 0 : 1][e], gi) : 0.0f;
-                s_x[e][tl][ch] = e == 0 ? __expf(x) : x;
-            }
-        }
-        if (tid < TB) s_upd[tid] = (tid < nt) && (mask ? mask[tok0 + t0 + tid] != 0 : 1);
-        return nt;
-    };
-    float X[RPL];
-    if (fwd) {
-#pragma unroll
-        for (int i = 0; i < RPL; ++i) X[i] = s0 ? s0[st + (size_t)(row0 + i) * D + col] : 0.0f;
-        float *ck = ckpt + (size_t)bh * (nck + 1) * D * D;
-        for (int c = 0; c < nck; ++c) {
-            // stores through one running pointer: unrolled, the compiler
-            // keeps a 64-bit address per row live across the chunk loop
-            float *pst = ck + (size_t)c * D * D + (size_t)row0 * D + col;
-#pragma unroll
-            for (int i = 0; i < RPL; ++i) {
-                *pst = X[i];
-                pst += D;
-                asm volatile("" : "+v"(pst));
-            }
-            __syncthreads();
-            const int nt = stage(c);
-            __syncthreads();
-#pragma unroll 1
-            for (int tl = 0; tl < nt; ++tl) {
-                if (!s_upd[tl]) continue;
-                float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
-#pragma unroll
-                for (int i = 0; i < RPL; i += 4) {
-                    p0 += s_x[2][tl][row0 + i + 0] * X[i + 0];
-                    p1 += s_x[2][tl][row0 + i + 1] * X[i + 1];
-                    p2 += s_x[2][tl][row0 + i + 2] * X[i + 2];
-                    p3 += s_x[2][tl][row0 + i + 3] * X[i + 3];
-                }
-                const float sb = xsum32(xsum16((p0 + p1) + (p2 + p3)));
-                const float vj = s_x[4][tl][col];
-#pragma unroll
-                for (int i = 0; i < RPL; ++i)
-                    X[i] = fmaf(s_x[0][tl][row0 + i], X[i], fmaf(s_x[1][tl][row0 + i], sb, s_x[3][tl][row0 + i] * vj));
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < RPL; ++i) ck[(size_t)nck * D * D + (size_t)(row0 + i) * D + col] = X[i];
-    } else {
-#pragma unroll
-        for (int i = 0; i < RPL; ++i) X[i] = d_sf ? d_sf[st + (size_t)(row0 + i) * D + col] : 0.0f;
-        for (int c = nck - 1; c >= 0; --c) {
-            float *pst = dck + ((size_t)bh * nck + c) * D * D + (size_t)row0 * D + col;
-#pragma unroll
-            for (int i = 0; i < RPL; ++i) {
-                *pst = X[i];
-                pst += D;
-                asm volatile("" : "+v"(pst));
-            }
-            __syncthreads();
-            const int nt = stage(c);
-            __syncthreads();
-#pragma unroll 1
-            for (int tl = nt - 1; tl >= 0; --tl) {
-                const float doj = s_x[4][tl][col];
-#pragma unroll
-                for (int i = 0; i < RPL; ++i) X[i] = fmaf(s_x[3][tl][row0 + i], doj, X[i]);
-                if (!s_upd[tl]) continue;
-                float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
-#pragma unroll
-                for (int i = 0; i < RPL; i += 4) {
-                    p0 += s_x[1][tl][row0 + i + 0] * X[i + 0];
-                    p1 += s_x[1][tl][row0 + i + 1] * X[i + 1];
-                    p2 += s_x[1][tl][row0 + i + 2] * X[i + 2];
-                    p3 += s_x[1][tl][row0 + i + 3] * X[i + 3];
-                }
-                const float ad = xsum32(xsum16((p0 + p1) + (p2 + p3)));
-#pragma unroll
-                for (int i = 0; i < RPL; ++i) X[i] = fmaf(s_x[0][tl][row0 + i], X[i], s_x[2][tl][row0 + i] * ad);
-            }
-        }
-        if (d_s0) {
-#pragma unroll
-            for (int i = 0; i < RPL; ++i) d_s0[st + (size_t)(row0 + i) * D + col] = X[i];
-        }
-    }
-}
-
-// ---- 3. per-chunk gradients -------------------------------------------------
+// ---- launch 2: per-chunk gradients (and helpers shared with launch 1) --------
 
 // Four consecutive elements (index i a multiple of 4) as fp32.
 template <typename T> struct io4;
 template <> struct io4<float> {
     __device__ __forceinline__ static f32x4 load(const float *p, size_t i) { return *(const f32x4 *)(p + i); }
     __device__ __forceinline__ static void store(float *p, size_t i, f32x4 x) { *(f32x4 *)(p + i) = x; }
+};
+// Four consecutive elements kept in their I/O type (a prefetch register set).
+template <typename T> struct raw4;
+template <> struct raw4<float> {
+    typedef f32x4 type;
+    __device__ __forceinline__ static type load(const float *p, size_t i) { return *(const f32x4 *)(p + i); }
+    __device__ __forceinline__ static f32x4 f32(type x) { return x; }
+    __device__ __forceinline__ static type zero() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+};
+template <> struct raw4<uint16_t> {
+    typedef u32x2 type;
+    __device__ __forceinline__ static type load(const uint16_t *p, size_t i) { return *(const u32x2 *)(p + i); }
+    __device__ __forceinline__ static f32x4 f32(type u)
+    {
+        return f32x4{bf16_lo(u[0]), bf16_hi(u[0]), bf16_lo(u[1]), bf16_hi(u[1])};
+    }
+    __device__ __forceinline__ static type zero() { return u32x2{0u, 0u}; }
 };
 template <> struct io4<uint16_t> {
     __device__ __forceinline__ static f32x4 load(const uint16_t *p, size_t i)
@@ -590,6 +482,297 @@ __global__ __launch_bounds__(D * 4) void chunk_grad_kernel(
     }
 }
 
+// ---- launch 1: the two recurrences in chunk form -------------------------------
+
+template <int D> struct alignas(16) ChainLds {
+    static constexpr int LD = D + 4;    // row stride of the L x D tiles (16-byte aligned rows)
+    float W[kL][LD];                    // raw (masked) w
+    float G[kL][LD];                    // decay prefix
+    float A[kL][LD];                    // a, then A^ = a e^{-G}
+    float B[kL][LD];                    // b, then B~ = b e^{G_{t-1}}
+    float X[kL][LD];                    // forward: k, then K^ = k e^{-G}; backward: r, then R~ = r e^G
+    float Y[kL][LD];                    // forward: v; backward: d_o
+    float M[2][kL][kL + 1];             // M_ba; forward M_bk, backward M_ra
+    float Tm[kL][20];                   // T = (I - M_ba)^{-1}
+    float EGL[D];
+    int upd[kL];
+};
+
+// Store a state slice held as St[ti][i] = S[16 ti + 4q + i][c0 + m] (lane (q, m))
+// into a row-major D x D matrix, through one running pointer (a separate
+// address per row would stay live across the chunk loop).
+template <int D>
+__device__ __forceinline__ void store_slice(float *dst, const f32x4 *St, int q, int m, int c0)
+{
+    float *p = dst + (size_t)(4 * q) * D + c0 + m;
+#pragma unroll
+    for (int ti = 0; ti < D / 16; ++ti)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            *p = St[ti][i];
+            p += (i == 3) ? 13 * D : D;
+            asm volatile("" : "+v"(p));
+        }
+}
+
+// 2 B H workgroups of D/16 waves; wave w keeps columns 16w .. 16w + 15 of the
+// state (or state gradient) in MFMA accumulator layout, St[ti][i] = row
+// 16 ti + 4q + i, column 16w + m for lane (q, m).  Workgroups [0, nbh) run the
+// forward recurrence chunk by chunk,
+//   X = B~ S + M_bk V,  U = T X,  S <- diag(e^{G_L}) (S + A^T U + K^T V),
+// storing the state before every 16-token chunk and after the last one
+// (ckpt[bh][c], c = 0 .. nck).  Workgroups [nbh, 2 nbh) run the state-gradient
+// recurrence backwards, with dS' the gradient at the chunk's end,
+//   dY = diag(e^{G_L}) dS',  dU = A^ dY + M_ra^T dO,  dX = T^T dU,
+//   dS <- dY + R~^T dO + B~^T dX,
+// storing dS' of every chunk first (dck[bh][c]).  In every product that
+// contracts over the state's rows or over the chunk's tokens, the
+// contraction index is taken in the order the accumulator layout holds it
+// (step st of tile ti takes rows 16 ti + 4q + st), so the state and the
+// intermediate tiles feed the matrix cores straight from registers.  A chunk
+// with a positive w, or whose decay reaches e^{-60}, runs token by token.
+// The next chunk's inputs are loaded while the current one is processed.
+// At D = 64, at most 128 VGPRs (four waves per SIMD): the 2 B H workgroups
+// of the benchmark shape then all fit on the machine at once, with no tail
+// round.  (At D = 128 the same limit spills, and measured slower.)
+template <int D, typename T_IO>
+__global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 1))) void chain_kernel(
+    int T, int H, int nbh, const T_IO *__restrict__ r, const T_IO *__restrict__ w,
+    const T_IO *__restrict__ k, const T_IO *__restrict__ v, const T_IO *__restrict__ a,
+    const T_IO *__restrict__ b, const float *__restrict__ s0, const uint8_t *__restrict__ mask,
+    const T_IO *__restrict__ d_o, const float *__restrict__ d_sf, float *__restrict__ ckpt,
+    float *__restrict__ dck, float *__restrict__ d_s0)
+{
+    constexpr int NTILE = D / 16;
+    using Lds = ChainLds<D>;
+    __shared__ Lds s;
+    const bool fwd = (int)blockIdx.x < nbh;
+    const int bh = fwd ? (int)blockIdx.x : (int)blockIdx.x - nbh;
+    const int bb = bh / H, h = bh % H;
+    const size_t tok0 = (size_t)bb * T;
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int q = lane >> 4, m = lane & 15, c0 = 16 * wave;
+    const int nck = (T + kL - 1) / kL;
+    const size_t st = (size_t)bh * D * D;
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+
+    f32x4 St[NTILE];
+    {
+        const float *init = fwd ? s0 : d_sf;
+#pragma unroll
+        for (int ti = 0; ti < NTILE; ++ti)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                St[ti][i] = init ? init[st + (size_t)(16 * ti + 4 * q + i) * D + c0 + m] : 0.0f;
+    }
+    // one thread per (token tp, channels cp .. cp + 3) of a chunk's tiles
+    const int tp = tid / (D / 4), cp = 4 * (tid % (D / 4));
+    using R4 = raw4<T_IO>;
+    typename R4::type pf[5];
+    int pm = 0;
+    const T_IO *const x_src = fwd ? k : r, *const y_src = fwd ? v : d_o;
+    auto fetch = [&](int c) {
+        const int t0 = c * kL, nt = min(kL, T - t0);
+        const bool valid = tp < nt;
+        const bool up = valid && (mask ? mask[tok0 + t0 + tp] != 0 : 1);
+        const size_t gi = ((tok0 + t0 + tp) * H + h) * D + cp;
+        pf[0] = up ? R4::load(w, gi) : R4::zero();
+        pf[1] = up ? R4::load(a, gi) : R4::zero();
+        pf[2] = up ? R4::load(b, gi) : R4::zero();
+        // forward: k and v only where the token updates; backward: r and d_o
+        // at every valid token (a masked token still reads the state)
+        const bool xy = fwd ? up : valid;
+        pf[3] = xy ? R4::load(x_src, gi) : R4::zero();
+        pf[4] = xy ? R4::load(y_src, gi) : R4::zero();
+        pm = up;
+    };
+    if (nck > 0) fetch(fwd ? 0 : nck - 1);
+    for (int it = 0; it < nck; ++it) {
+        const int c = fwd ? it : nck - 1 - it;
+        const int Lc = min(kL, T - c * kL);
+        store_slice<D>(fwd ? ckpt + ((size_t)bh * (nck + 1) + c) * D * D : dck + ((size_t)bh * nck + c) * D * D,
+                       St, q, m, c0);
+        __syncthreads();
+        *(f32x4 *)&s.W[tp][cp] = R4::f32(pf[0]);
+        *(f32x4 *)&s.G[tp][cp] = R4::f32(pf[0]);
+        *(f32x4 *)&s.A[tp][cp] = R4::f32(pf[1]);
+        *(f32x4 *)&s.B[tp][cp] = R4::f32(pf[2]);
+        *(f32x4 *)&s.X[tp][cp] = R4::f32(pf[3]);
+        *(f32x4 *)&s.Y[tp][cp] = R4::f32(pf[4]);
+        if (cp == 0) s.upd[tp] = pm;
+        __syncthreads();
+        if (it + 1 < nck) fetch(fwd ? c + 1 : c - 1);
+        int extreme = 0;
+        if (tid < D) {
+            float x[kL];
+#pragma unroll
+            for (int t = 0; t < kL; ++t) x[t] = s.G[t][tid];
+            float acc = 0.0f;
+#pragma unroll
+            for (int t = 0; t < kL; ++t) {
+                extreme |= x[t] > 0.0f;
+                acc += x[t];
+                s.G[t][tid] = acc;
+            }
+            extreme |= acc < kMinChunkLogDecay;
+            s.EGL[tid] = __expf(acc);
+        }
+        if (__syncthreads_or(extreme)) {
+            // token by token on the raw operands
+            if (fwd) {
+                for (int t = 0; t < Lc; ++t) {
+                    if (!s.upd[t]) continue;
+                    float sb = 0.0f;
+#pragma unroll
+                    for (int ti = 0; ti < NTILE; ++ti)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) sb = fmaf(s.B[t][16 * ti + 4 * q + i], St[ti][i], sb);
+                    sb = xsum32(xsum16(sb));
+                    const float vj = s.Y[t][c0 + m];
+#pragma unroll
+                    for (int ti = 0; ti < NTILE; ++ti)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int row = 16 * ti + 4 * q + i;
+                            St[ti][i] = fmaf(__expf(s.W[t][row]), St[ti][i], fmaf(s.A[t][row], sb, s.X[t][row] * vj));
+                        }
+                }
+            } else {
+                for (int t = Lc - 1; t >= 0; --t) {
+                    const float doj = s.Y[t][c0 + m];
+#pragma unroll
+                    for (int ti = 0; ti < NTILE; ++ti)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) St[ti][i] = fmaf(s.X[t][16 * ti + 4 * q + i], doj, St[ti][i]);
+                    if (!s.upd[t]) continue;
+                    float ad = 0.0f;
+#pragma unroll
+                    for (int ti = 0; ti < NTILE; ++ti)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) ad = fmaf(s.A[t][16 * ti + 4 * q + i], St[ti][i], ad);
+                    ad = xsum32(xsum16(ad));
+#pragma unroll
+                    for (int ti = 0; ti < NTILE; ++ti)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int row = 16 * ti + 4 * q + i;
+                            St[ti][i] = fmaf(__expf(s.W[t][row]), St[ti][i], s.B[t][row] * ad);
+                        }
+                }
+            }
+            continue;
+        }
+        {
+            const f32x4 G = *(const f32x4 *)&s.G[tp][cp];
+            const f32x4 Gp = tp ? *(const f32x4 *)&s.G[tp - 1][cp] : z;
+            f32x4 eG, enG, eGp;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                eG[i] = __expf(G[i]);
+                enG[i] = __expf(-G[i]);
+                eGp[i] = __expf(Gp[i]);
+            }
+            *(f32x4 *)&s.A[tp][cp] *= enG;
+            *(f32x4 *)&s.B[tp][cp] *= eGp;
+            *(f32x4 *)&s.X[tp][cp] *= fwd ? enG : eG;
+        }
+        __syncthreads();
+        // M_ba (wave 0) and M_bk (forward) or M_ra (backward) (wave 1)
+        if (wave < 2) {
+            const float(*P)[Lds::LD] = (wave == 0 || fwd) ? s.B : s.X;
+            const float(*Q)[Lds::LD] = (wave == 1 && fwd) ? s.X : s.A;
+            const f32x4 acc = mm16_rows<D>(z, [&](int mm, int j) { return *(const f32x4 *)&P[mm][j]; },
+                                           [&](int n, int j) { return *(const f32x4 *)&Q[n][j]; }, lane);
+            const bool strict = wave == 0 || fwd;   // M_ba, M_bk strictly lower; M_ra with the diagonal
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 4 * q + i;
+                s.M[wave][row][m] = (strict ? row > m : row >= m) ? acc[i] : 0.0f;
+            }
+        }
+        __syncthreads();
+        // T = (I - M_ba)^{-1} column by column (x_i = delta_ij + sum_{l<i} M_ba[i][l] x_l),
+        // four lanes per column each summing over l = q (mod 4)
+        if (wave == 0) {
+            float xr[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < kL; ++i) {
+                float part = 0.0f;
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4) {
+                    const int l = q + 4 * s4;
+                    if (l < i) part = fmaf(s.M[0][i][l], xr[s4], part);
+                }
+                const float tot = xsum32(xsum16(part)) + (i == m ? 1.0f : 0.0f);
+                if ((i & 3) == q) xr[i >> 2] = tot;
+                if (q == 0) s.Tm[i][m] = tot;
+            }
+        }
+        __syncthreads();
+        if (fwd) {
+            // X = B~ S + M_bk V
+            f32x4 Xa = z;
+#pragma unroll
+            for (int ti = 0; ti < NTILE; ++ti) {
+                const f32x4 bt = *(const f32x4 *)&s.B[m][16 * ti + 4 * q];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Xa = mfma_f32(bt[i], St[ti][i], Xa);
+            }
+            Xa = mm16<kL>(Xa, [&](int mm, int kk) { return s.M[1][mm][kk]; },
+                          [&](int kk, int n) { return s.Y[kk][c0 + n]; }, lane);
+            // U = T X (X's token rows 4q + i are this lane's)
+            f32x4 U = z;
+            {
+                const f32x4 tr = *(const f32x4 *)&s.Tm[m][4 * q];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) U = mfma_f32(tr[i], Xa[i], U);
+            }
+            // S <- diag(e^{G_L}) (S + A^T U + K^T V)
+#pragma unroll
+            for (int ti = 0; ti < NTILE; ++ti) {
+                f32x4 acc = St[ti];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc = mfma_f32(s.A[4 * q + i][16 * ti + m], U[i], acc);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc = mfma_f32(s.X[4 * q + i][16 * ti + m], s.Y[4 * q + i][c0 + m], acc);
+                St[ti] = acc * *(const f32x4 *)&s.EGL[16 * ti + 4 * q];
+            }
+        } else {
+            // dY = diag(e^{G_L}) dS', formed tile by tile where it is used
+            auto dY = [&](int ti) { return St[ti] * *(const f32x4 *)&s.EGL[16 * ti + 4 * q]; };
+            // dU = A^ dY + M_ra^T dO
+            f32x4 dU = z;
+#pragma unroll
+            for (int ti = 0; ti < NTILE; ++ti) {
+                const f32x4 at = *(const f32x4 *)&s.A[m][16 * ti + 4 * q];
+                const f32x4 y = dY(ti);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dU = mfma_f32(at[i], y[i], dU);
+            }
+            dU = mm16<kL>(dU, [&](int mm, int kk) { return s.M[1][kk][mm]; },
+                          [&](int kk, int n) { return s.Y[kk][c0 + n]; }, lane);
+            // dX = T^T dU
+            f32x4 dX = z;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dX = mfma_f32(s.Tm[4 * q + i][m], dU[i], dX);
+            // dS <- dY + R~^T dO + B~^T dX
+#pragma unroll
+            for (int ti = 0; ti < NTILE; ++ti) {
+                f32x4 acc = dY(ti);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc = mfma_f32(s.X[4 * q + i][16 * ti + m], s.Y[4 * q + i][c0 + m], acc);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc = mfma_f32(s.B[4 * q + i][16 * ti + m], dX[i], acc);
+                St[ti] = acc;
+            }
+        }
+    }
+    if (fwd)
+        store_slice<D>(ckpt + ((size_t)bh * (nck + 1) + nck) * D * D, St, q, m, c0);
+    else if (d_s0)
+        store_slice<D>(d_s0 + st, St, q, m, c0);
+}
+
 template <int D, typename T_IO>
 hipError_t launch_bwd_d(const BwdArgs &p, hipStream_t stream)
 {
@@ -597,7 +780,7 @@ hipError_t launch_bwd_d(const BwdArgs &p, hipStream_t stream)
     const size_t nbh = (size_t)p.B * p.H;
     float *ckpt = (float *)p.ws;
     float *dck = ckpt + nbh * (nck + 1) * D * D;
-    hipLaunchKernelGGL((recur_pair_kernel<D, T_IO>), dim3((unsigned)(2 * nbh)), dim3(D * 4), 0, stream, p.T,
+    hipLaunchKernelGGL((chain_kernel<D, T_IO>), dim3((unsigned)(2 * nbh)), dim3(D * 4), 0, stream, p.T,
                        p.H, (int)nbh, (const T_IO *)p.r, (const T_IO *)p.w, (const T_IO *)p.k,
                        (const T_IO *)p.v, (const T_IO *)p.a, (const T_IO *)p.b, p.s0, p.mask,
                        (const T_IO *)p.d_o, p.d_sf, ckpt, dck, p.d_s0);
