@@ -211,9 +211,9 @@ wkv7_status_t wkv7_bwd(int dtype, int B, int T, int H, int K, int V,
                        float *d_initial_state, void *workspace, size_t workspace_bytes,
                        void *stream);
 
-/* Workspace bytes wkv7_bwd needs: 4 B (2 ceil(T/16) + 1) H K V (two fp32
- * states per 16-token chunk and sequence, plus one), or 0 for arguments
- * wkv7_bwd would reject. */
+/* Workspace bytes wkv7_bwd needs: 4 B 2 ceil(T/16) H K V (two fp32 states
+ * per 16-token chunk and sequence), or 0 for arguments wkv7_bwd would
+ * reject. */
 size_t wkv7_bwd_workspace_bytes(int B, int T, int H, int K, int V);
 
 /*

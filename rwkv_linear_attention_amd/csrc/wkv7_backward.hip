@@ -11,8 +11,7 @@
 //
 // Two launches, with a caller-provided workspace and no allocation:
 //  1. chain_kernel runs, side by side, (a) the forward recurrence in chunk
-//     form, storing the state before every 16-token chunk and after the last
-//     one (checkpoints), and (b) the dS recurrence backwards in chunk form,
+//     form, storing the state before every 16-token chunk (checkpoints), and (b) the dS recurrence backwards in chunk form,
 //     storing for every chunk the gradient of the state at the chunk's end
 //     with respect to everything after the chunk;
 //  2. chunk_grad_kernel (one workgroup per (b, h, chunk), all chunks in
@@ -33,7 +32,8 @@
 //   dA^ = U dY^T + dM_ra^T R~ + dM_ba^T B~, dK^ = V dY^T + dM_rk^T R~ + dM_bk^T B~,
 //   dr = dR~ e^G, db = dB~ e^{G_{t-1}}, da = dA^ e^{-G}, dk = dK^ e^{-G},
 //   dw_m = sum_{t >= m} (dr_t r_t - da_t a_t - dk_t k_t + db_{t+1} b_{t+1})
-//          + sum_j dS'[.,j] S'[.,j]     (the last term from the chunk end).
+//          + sum_j dS'[.,j] S'[.,j]     (the last term from the chunk end,
+//          formed from S, U, V and dS' without reading the next checkpoint).
 // A chunk whose decay reaches e^{-60} on some channel, or with a positive w,
 // takes an exact token-by-token path instead (the split factors e^{-G} would
 // leave the fp32 range).  All arithmetic is fp32: the products run on the
@@ -257,8 +257,7 @@ __global__ __launch_bounds__(D * 4) void chunk_grad_kernel(
     const int bb = bh / H, h = bh % H;
     const int t0 = c * kL, Lc = min(kL, T - t0);
     const size_t tokbase = (((size_t)bb * T + t0) * H + h) * D;   // element of (token t0, channel 0)
-    const float *Sc = ckpt + ((size_t)bh * (nck + 1) + c) * D * D;
-    const float *Sn = Sc + (size_t)D * D;
+    const float *Sc = ckpt + ((size_t)bh * nck + c) * D * D;
     const float *dSe = dck + ((size_t)bh * nck + c) * D * D;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int q = lane >> 4, m = lane & 15;
@@ -416,20 +415,47 @@ __global__ __launch_bounds__(D * 4) void chunk_grad_kernel(
     // lane (q, m) ends with channels k0 + 4q + i of token m ---
     const int k0 = 16 * wave;
     const size_t rowm = (size_t)(k0 + m) * D;   // state row of channel k0 + m
-    auto Srow = [&](int mm, int j) { return *(const f32x4 *)(Sc + rowm + j); };
-    float dgl = 0.0f;   // sum_j dS'[k0+m][j] S'[k0+m][j], over this lane's j
-    auto dYrow = [&](int mm, int j) {
-        const f32x4 d = *(const f32x4 *)(dSe + rowm + j), sn = *(const f32x4 *)(Sn + rowm + j);
-        dgl += d[0] * sn[0] + d[1] * sn[1] + d[2] * sn[2] + d[3] * sn[3];
-        return d * s.EGL[k0 + m];
-    };
-    auto tile = [&](const float(*X)[Lds::LD]) { return [X](int n, int j) { return *(const f32x4 *)&X[n][j]; }; };
-    f32x4 dR = mm16_rows<D>(z, Srow, tile(s.DO), lane);
-    f32x4 dB = mm16_rows<D>(z, Srow, tile(s.DX), lane);
-    f32x4 dA = mm16_rows<D>(z, dYrow, tile(s.U), lane);
-    f32x4 dK = mm16_rows<D>(z, [&](int mm, int j) { return *(const f32x4 *)(dSe + rowm + j) * s.EGL[k0 + m]; },
-                            tile(s.V), lane);
-    dgl = xsum32(xsum16(dgl));   // channel k0 + m, in every lane of column m
+    // The four products that contract over the value columns, with each row
+    // of S and dS' loaded once (the contraction index is permuted as in
+    // mm16_rows): dR~^T += S dO^T, dB~^T += S dX^T, dA^^T += dY U^T,
+    // dK^^T += dY V^T.  sds collects sum_j dS'[k0+m][j] S[k0+m][j].
+    f32x4 dR = z, dB = z, dA = z, dK = z;
+    float sds = 0.0f;
+    {
+        const float eglm = s.EGL[k0 + m];
+#pragma unroll
+        for (int j0b = 0; j0b < D; j0b += 16) {
+            const int j = j0b + 4 * q;
+            const f32x4 sr = *(const f32x4 *)(Sc + rowm + j), dr4 = *(const f32x4 *)(dSe + rowm + j);
+            sds += dr4[0] * sr[0] + dr4[1] * sr[1] + dr4[2] * sr[2] + dr4[3] * sr[3];
+            const f32x4 dy = dr4 * eglm;
+            const f32x4 yo = *(const f32x4 *)&s.DO[m][j], yx = *(const f32x4 *)&s.DX[m][j];
+            const f32x4 yu = *(const f32x4 *)&s.U[m][j], yv = *(const f32x4 *)&s.V[m][j];
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                dR = mfma_f32(sr[st], yo[st], dR);
+                dB = mfma_f32(sr[st], yx[st], dB);
+                dA = mfma_f32(dy[st], yu[st], dA);
+                dK = mfma_f32(dy[st], yv[st], dK);
+            }
+        }
+    }
+    sds = xsum32(xsum16(sds));   // channel k0 + m, in every lane of column m
+    // Chunk-end term of dw, sum_j dS'[c][j] S'[c][j] with S' = diag(e^{G_L})
+    // (S + A^^T U + K^^T V): e^{G_L,c} sds_c + sum_t A^[t][c] (U dY^T)[t][c]
+    // + sum_t K^[t][c] (V dY^T)[t][c]; the last two sums run over this row's
+    // 16 lanes (tokens), with dA and dK still holding only those products.
+    float dglc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int c = k0 + 4 * q + i;
+        float y = s.A[m][c] * dA[i] + s.K[m][c] * dK[i];
+        y += __shfl_xor(y, 1, kWave);
+        y += __shfl_xor(y, 2, kWave);
+        y += __shfl_xor(y, 4, kWave);
+        y += __shfl_xor(y, 8, kWave);
+        dglc[i] = s.EGL[c] * __shfl(sds, 4 * q + i, 16) + y;
+    }
     // small terms: (dM X)^T = X^T dM^T and (dM^T X)^T = X^T dM
     auto colT = [&](const float(*X)[Lds::LD]) { return [X, k0](int mm, int kk) { return X[kk][k0 + mm]; }; };
     auto dMt = [&](int idx) { return [idx](int kk, int n) { return s.M[idx][n][kk]; }; };
@@ -463,8 +489,7 @@ __global__ __launch_bounds__(D * 4) void chunk_grad_kernel(
         const float qb = gb[i] * bv;
         // dG_t = p_t + qb_{t+1} (+ the chunk-end term at t = 15), then the
         // suffix sum over t = m .. 15 within the 16-lane row
-        const float dglc = __shfl(dgl, 4 * q + i, 16);   // channel ch + i (every lane takes part)
-        float y = p + row_shl<1>(qb, 0.0f) + (t == kL - 1 ? dglc : 0.0f);
+        float y = p + row_shl<1>(qb, 0.0f) + (t == kL - 1 ? dglc[i] : 0.0f);
         y += row_shl<1>(y, 0.0f);
         y += row_shl<2>(y, 0.0f);
         y += row_shl<4>(y, 0.0f);
@@ -520,8 +545,7 @@ __device__ __forceinline__ void store_slice(float *dst, const f32x4 *St, int q, 
 // 16 ti + 4q + i, column 16w + m for lane (q, m).  Workgroups [0, nbh) run the
 // forward recurrence chunk by chunk,
 //   X = B~ S + M_bk V,  U = T X,  S <- diag(e^{G_L}) (S + A^T U + K^T V),
-// storing the state before every 16-token chunk and after the last one
-// (ckpt[bh][c], c = 0 .. nck).  Workgroups [nbh, 2 nbh) run the state-gradient
+// storing the state before every 16-token chunk (ckpt[bh][c]).  Workgroups [nbh, 2 nbh) run the state-gradient
 // recurrence backwards, with dS' the gradient at the chunk's end,
 //   dY = diag(e^{G_L}) dS',  dU = A^ dY + M_ra^T dO,  dX = T^T dU,
 //   dS <- dY + R~^T dO + B~^T dX,
@@ -590,8 +614,7 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(D == 64 ?
     for (int it = 0; it < nck; ++it) {
         const int c = fwd ? it : nck - 1 - it;
         const int Lc = min(kL, T - c * kL);
-        store_slice<D>(fwd ? ckpt + ((size_t)bh * (nck + 1) + c) * D * D : dck + ((size_t)bh * nck + c) * D * D,
-                       St, q, m, c0);
+        store_slice<D>((fwd ? ckpt : dck) + ((size_t)bh * nck + c) * D * D, St, q, m, c0);
         __syncthreads();
         *(f32x4 *)&s.W[tp][cp] = R4::f32(pf[0]);
         *(f32x4 *)&s.G[tp][cp] = R4::f32(pf[0]);
@@ -767,10 +790,7 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(D == 64 ?
             }
         }
     }
-    if (fwd)
-        store_slice<D>(ckpt + ((size_t)bh * (nck + 1) + nck) * D * D, St, q, m, c0);
-    else if (d_s0)
-        store_slice<D>(d_s0 + st, St, q, m, c0);
+    if (!fwd && d_s0) store_slice<D>(d_s0 + st, St, q, m, c0);
 }
 
 template <int D, typename T_IO>
@@ -779,7 +799,7 @@ hipError_t launch_bwd_d(const BwdArgs &p, hipStream_t stream)
     const int nck = (p.T + kL - 1) / kL;
     const size_t nbh = (size_t)p.B * p.H;
     float *ckpt = (float *)p.ws;
-    float *dck = ckpt + nbh * (nck + 1) * D * D;
+    float *dck = ckpt + nbh * nck * D * D;
     hipLaunchKernelGGL((chain_kernel<D, T_IO>), dim3((unsigned)(2 * nbh)), dim3(D * 4), 0, stream, p.T,
                        p.H, (int)nbh, (const T_IO *)p.r, (const T_IO *)p.w, (const T_IO *)p.k,
                        (const T_IO *)p.v, (const T_IO *)p.a, (const T_IO *)p.b, p.s0, p.mask,
@@ -798,7 +818,7 @@ hipError_t launch_bwd_d(const BwdArgs &p, hipStream_t stream)
 size_t bwd_workspace_bytes(int B, int T, int H, int D)
 {
     const size_t nck = ((size_t)T + kL - 1) / kL;
-    return sizeof(float) * (size_t)B * H * D * D * (2 * nck + 1);
+    return sizeof(float) * (size_t)B * H * D * D * 2 * nck;
 }
 
 hipError_t launch_backward(int dtype, const BwdArgs &p, hipStream_t stream)

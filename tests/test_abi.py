@@ -192,9 +192,9 @@ def bwd(L, dtype=1, B=1, T=20, H=1, K=64, V=64, ptrs=None, s0=None, mask=None, d
 
 
 def test_bwd_workspace_size(L):
-    # two fp32 states per 16-token chunk and sequence, plus one
-    assert L.wkv7_bwd_workspace_bytes(2, 33, 3, 64, 64) == 4 * 2 * 3 * 64 * 64 * (2 * 3 + 1)
-    assert L.wkv7_bwd_workspace_bytes(1, 16, 1, 128, 128) == 4 * 128 * 128 * 3
+    # two fp32 states per 16-token chunk and sequence
+    assert L.wkv7_bwd_workspace_bytes(2, 33, 3, 64, 64) == 4 * 2 * 3 * 64 * 64 * 2 * 3
+    assert L.wkv7_bwd_workspace_bytes(1, 16, 1, 128, 128) == 4 * 128 * 128 * 2
     assert L.wkv7_bwd_workspace_bytes(1, 16, 1, 64, 32) == 0
     assert L.wkv7_bwd_workspace_bytes(0, 16, 1, 64, 64) == 0
 
