@@ -385,16 +385,16 @@ __global__ __launch_bounds__(D * 4) void chunk_grad_kernel(
     }
     __syncthreads();
     {
-        f32x4 dV = mm16<D>(z, [&](int mm, int kk) { return s.K[mm][kk]; }, dY, lane);
-        dV = mm16<kL>(dV, [&](int mm, int kk) { return s.M[M_RK][kk][mm]; },
-                      [&](int kk, int n) { return s.DO[kk][c0 + n]; }, lane);
-        dV = mm16<kL>(dV, [&](int mm, int kk) { return s.M[M_BK][kk][mm]; },
-                      [&](int kk, int n) { return s.DX[kk][c0 + n]; }, lane);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = 4 * q + i;
-            if (t < Lc) io<T_IO>::store(dv, tokbase + (size_t)t * H * D + c0 + m, s.upd[t] ? dV[i] : 0.0f);
-        }
+        // dV = K^ dY + M_rk^T dO + M_bk^T dX, formed transposed (value columns
+        // c0 + 4q + i of token m in lane (q, m)) so that each lane stores four
+        // adjacent columns
+        f32x4 dVt = mm16<D>(z, [&](int mm, int kk) { return dY(kk, mm); },
+                            [&](int kk, int n) { return s.K[n][kk]; }, lane);
+        dVt = mm16<kL>(dVt, [&](int mm, int kk) { return s.DO[kk][c0 + mm]; },
+                       [&](int kk, int n) { return s.M[M_RK][kk][n]; }, lane);
+        dVt = mm16<kL>(dVt, [&](int mm, int kk) { return s.DX[kk][c0 + mm]; },
+                       [&](int kk, int n) { return s.M[M_BK][kk][n]; }, lane);
+        if (m < Lc) io4<T_IO>::store(dv, tokbase + (size_t)m * H * D + c0 + 4 * q, s.upd[m] ? dVt : z);
     }
     // --- gradients of the chunk matrices (contractions over the value columns) ---
     if (wave < 4) {
