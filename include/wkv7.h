@@ -233,6 +233,31 @@ wkv7_status_t wkv7_step(int dtype, int B, int H, int K, int V,
                         const void *v, const void *a, const void *b,
                         float *state, void *o, void *stream);
 
+/*
+ * wkv7_gdn_step -- one Gated DeltaNet decode token per sequence (rwkv-ops
+ * README, section "gdn_recurrent 使用方法", gated_delta_net_recurrent_single_step:
+ * the T = 1 case of wkv7_gdn_fwd, with the same reading of the update).
+ *
+ *   dtype          WKV7_F32 or WKV7_BF16 for q,k,v,g,beta and o.
+ *   B, H, K, V     as for wkv7_step.
+ *   q, k           [B,H,K] dtype, raw (normalised inside).  Read only.
+ *   v              [B,H,V] dtype.  Read only.
+ *   g, beta        [B,H] dtype.  Read only.
+ *   state_in       [n_state,H,K,V] fp32 with n_state 1 (shared) or B, or NULL
+ *                  for a zero state.  Read only.
+ *   n_state        1 or B when state_in is given.
+ *   state_out      [B,H,K,V] fp32.  Written with the next state.  May be the
+ *                  same buffer as state_in when n_state == B (or B == 1): an
+ *                  in-place update.
+ *   o              [B,H,V] dtype.  Written.  Must not overlap a state.
+ *   stream         hipStream_t to enqueue on.
+ */
+wkv7_status_t wkv7_gdn_step(int dtype, int B, int H, int K, int V,
+                            const void *q, const void *k, const void *v,
+                            const void *g, const void *beta,
+                            const float *state_in, int n_state, float *state_out,
+                            void *o, void *stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *wkv7_strerror(int status);
 
@@ -242,7 +267,8 @@ const char *wkv7_strerror(int status);
 int wkv7_fwd_path(int dtype, int B, int T, int H, int K, int V, int algo);
 
 /* ABI version of this header (major * 100 + minor): 101 adds wkv7_fwd_varlen,
- * 102 adds wkv7_gdn_fwd, 103 adds wkv7_bwd and wkv7_bwd_workspace_bytes. */
+ * 102 adds wkv7_gdn_fwd, 103 adds wkv7_bwd and wkv7_bwd_workspace_bytes,
+ * 104 adds wkv7_gdn_step. */
 int wkv7_version(void);
 
 #ifdef __cplusplus

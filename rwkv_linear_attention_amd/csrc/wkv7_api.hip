@@ -40,7 +40,7 @@ int choose_path(int dtype, int T, int algo)
 
 extern "C" {
 
-int wkv7_version(void) { return 103; }
+int wkv7_version(void) { return 104; }
 
 const char *wkv7_strerror(int status)
 {
@@ -233,6 +233,30 @@ wkv7_status_t wkv7_step(int dtype, int B, int H, int K, int V,
     for (const void *p : req)
         if (!p || !aligned16(p)) return WKV7_ERR_INVALID_ARG;
     wkv7::StepArgs args{B, H, K, r, w, k, v, a, b, state, o};
+    return wkv7::launch_step(dtype, args, (hipStream_t)stream) == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
+}
+
+wkv7_status_t wkv7_gdn_step(int dtype, int B, int H, int K, int V,
+                            const void *q, const void *k, const void *v,
+                            const void *g, const void *beta,
+                            const float *state_in, int n_state, float *state_out,
+                            void *o, void *stream)
+{
+    wkv7_status_t st = check_common(dtype, B, H, K, V);
+    if (st != WKV7_OK) return st;
+    const void *req[] = {q, k, v, g, beta, state_out, o};
+    for (const void *p : req)
+        if (!p || !aligned16(p)) return WKV7_ERR_INVALID_ARG;
+    if (state_in) {
+        if (!aligned16(state_in)) return WKV7_ERR_INVALID_ARG;
+        if (n_state != 1 && n_state != B) return WKV7_ERR_INVALID_ARG;
+        // a shared state read by every sequence may not be overwritten by them
+        if (n_state == 1 && B > 1 && state_in == state_out) return WKV7_ERR_INVALID_ARG;
+    }
+    wkv7::StepArgs args{B, H, K, q, g, k, v, beta, nullptr, state_out, o};
+    args.gdn = true;
+    args.state_in = state_in;
+    args.n_state_in = state_in ? n_state : 0;
     return wkv7::launch_step(dtype, args, (hipStream_t)stream) == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
 }
 

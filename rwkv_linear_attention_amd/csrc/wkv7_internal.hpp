@@ -45,8 +45,14 @@ size_t bwd_workspace_bytes(int B, int T, int H, int D);
 struct StepArgs {
     int B, H, D;
     const void *r, *w, *k, *v, *a, *b;   // [B,H,D]
-    float *state;                        // [B,H,D,D], in place
+    float *state;                        // [B,H,D,D], in place (Gated DeltaNet: written)
     void *o;                             // [B,H,D]
+    // Gated DeltaNet decode: r = q, w = g and a = beta ([B,H]); the state is
+    // read from state_in ([n_state_in,H,D,D], n_state_in 1 or B, or nullptr
+    // for zeros) and written to state.
+    bool gdn = false;
+    const float *state_in = nullptr;
+    int n_state_in = 0;
 };
 
 // dtype: 0 = fp32, 1 = bf16 (values of wkv7_dtype_t).

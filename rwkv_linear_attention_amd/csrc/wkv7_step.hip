@@ -39,11 +39,20 @@ template <> struct vec16<float> {
     }
 };
 
-template <int D, typename T_IO>
+// GDN = true: Gated DeltaNet decode (rwkv-ops README, section
+// "gdn_recurrent 使用方法", gated_delta_net_recurrent_single_step) in the same
+// slots: r = q, k = k, v = v, w = gate g [B,H], a = strength beta [B,H] (b
+// unused).  q and k are L2-normalised here (1e-6 added to the squared
+// length), and the step is the generalized-delta-rule step with r = qn,
+// w = g, k = beta kn, a = -e^g beta kn, b = kn.  The state is read from
+// s_in (row bh, or row h of a single shared state when n_in == 1; nullptr
+// reads zeros) and written to s_out (row bh); the two may be the same
+// buffer when every sequence has its own row.
+template <int D, typename T_IO, bool GDN>
 __global__ __launch_bounds__(256) void step_kernel(
-    int nwaves, const T_IO *__restrict__ r, const T_IO *__restrict__ w,
+    int nwaves, int H, const T_IO *__restrict__ r, const T_IO *__restrict__ w,
     const T_IO *__restrict__ k, const T_IO *__restrict__ v, const T_IO *__restrict__ a,
-    const T_IO *__restrict__ b, float *__restrict__ state, T_IO *__restrict__ o)
+    const T_IO *__restrict__ b, const float *s_in, int n_in, float *s_out, T_IO *__restrict__ o)
 {
     constexpr int CW = (D == 64) ? 64 : 32;   // columns per wave
     constexpr int NCG = CW / 4;               // column groups per wave
@@ -57,23 +66,55 @@ __global__ __launch_bounds__(256) void step_kernel(
     const int col0 = cs * CW + cg * 4;
     const int row0 = rg * 16;
 
-    float *Sp = state + (size_t)bh * D * D + (size_t)row0 * D + col0;
+    const size_t off = (size_t)row0 * D + col0;
+    const int sidx = (GDN && n_in == 1) ? bh % H : bh;
+    float *Sp = s_out + (size_t)bh * D * D + off;
     f32x4 S[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) S[i] = *(const f32x4 *)(Sp + (size_t)i * D);
+    for (int i = 0; i < 16; ++i)
+        S[i] = s_in ? *(const f32x4 *)(s_in + (size_t)sidx * D * D + off + (size_t)i * D) : f32x4{0.f, 0.f, 0.f, 0.f};
 
     const size_t vb = (size_t)bh * D;
     float rv[16], ev[16], kv[16], av[16], bv[16];
-    vec16<T_IO>::load(r + vb + row0, rv);
-    vec16<T_IO>::load(w + vb + row0, ev);
-    vec16<T_IO>::load(k + vb + row0, kv);
-    vec16<T_IO>::load(a + vb + row0, av);
-    vec16<T_IO>::load(b + vb + row0, bv);
     float vj[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) vj[c] = io<T_IO>::load(v, vb + col0 + c);
+    if constexpr (GDN) {
+        float qv[16], kr[16];
+        vec16<T_IO>::load(r + vb + row0, qv);
+        vec16<T_IO>::load(k + vb + row0, kr);
+        float nq = 0.f, nk = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) ev[i] = __expf(ev[i]);
+        for (int i = 0; i < 16; ++i) {
+            nq = fmaf(qv[i], qv[i], nq);
+            nk = fmaf(kr[i], kr[i], nk);
+        }
+#pragma unroll
+        for (int m = NCG; m < kWave; m <<= 1) {
+            nq = xor_sum(nq, m);
+            nk = xor_sum(nk, m);
+        }
+        const float iq = 1.0f / sqrtf(nq + 1e-6f), ik = 1.0f / sqrtf(nk + 1e-6f);
+        const float gate = io<T_IO>::load(w, bh), beta = io<T_IO>::load(a, bh);
+        const float eg = __expf(gate);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float kn = kr[i] * ik;
+            rv[i] = qv[i] * iq;
+            ev[i] = eg;
+            kv[i] = beta * kn;
+            av[i] = -eg * beta * kn;
+            bv[i] = kn;
+        }
+    } else {
+        vec16<T_IO>::load(r + vb + row0, rv);
+        vec16<T_IO>::load(w + vb + row0, ev);
+        vec16<T_IO>::load(k + vb + row0, kv);
+        vec16<T_IO>::load(a + vb + row0, av);
+        vec16<T_IO>::load(b + vb + row0, bv);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ev[i] = __expf(ev[i]);
+    }
 
     float sb[4];
 #pragma unroll
@@ -127,9 +168,15 @@ static hipError_t launch_st(const StepArgs &p, hipStream_t stream)
     constexpr int WPS = (D == 64) ? 1 : 4;
     const long long nwaves = (long long)p.B * p.H * WPS;
     const dim3 grid((unsigned)((nwaves + 3) / 4)), block(256);
-    hipLaunchKernelGGL((step_kernel<D, T_IO>), grid, block, 0, stream, (int)nwaves,
-                       (const T_IO *)p.r, (const T_IO *)p.w, (const T_IO *)p.k, (const T_IO *)p.v,
-                       (const T_IO *)p.a, (const T_IO *)p.b, p.state, (T_IO *)p.o);
+    if (p.gdn)
+        hipLaunchKernelGGL((step_kernel<D, T_IO, true>), grid, block, 0, stream, (int)nwaves, p.H,
+                           (const T_IO *)p.r, (const T_IO *)p.w, (const T_IO *)p.k, (const T_IO *)p.v,
+                           (const T_IO *)p.a, (const T_IO *)p.b, p.state_in, p.n_state_in, p.state,
+                           (T_IO *)p.o);
+    else
+        hipLaunchKernelGGL((step_kernel<D, T_IO, false>), grid, block, 0, stream, (int)nwaves, p.H,
+                           (const T_IO *)p.r, (const T_IO *)p.w, (const T_IO *)p.k, (const T_IO *)p.v,
+                           (const T_IO *)p.a, (const T_IO *)p.b, p.state, p.B, p.state, (T_IO *)p.o);
     return hipGetLastError();
 }
 

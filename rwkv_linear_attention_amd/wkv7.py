@@ -40,6 +40,8 @@ def lib():
     L.wkv7_bwd.restype = i
     L.wkv7_bwd_workspace_bytes.argtypes = [i] * 5
     L.wkv7_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.wkv7_gdn_step.argtypes = [i, i, i, i, i] + [p] * 6 + [i, p, p, p]
+    L.wkv7_gdn_step.restype = i
     L.wkv7_step.argtypes = [i, i, i, i, i] + [p] * 8 + [p]
     L.wkv7_step.restype = i
     L.wkv7_strerror.argtypes = [i]
@@ -258,6 +260,40 @@ def gdn_fwd(q, k, v, g, beta, initial_state=None, output_final_state=True, algo=
     if st != OK:
         raise WKV7Error(st)
     return o, sf
+
+
+def gdn_step(q, k, v, g, beta, state=None, out=None, next_state=None):
+    """One Gated DeltaNet decode token.  q, k: [B,H,K]; v: [B,H,V]; g, beta:
+    [B,H]; state: [B,H,K,V] or [1,H,K,V] float32 (shared) or None (zeros).
+    The next state goes to next_state ([B,H,K,V] float32); by default a state
+    with B rows is updated in place and otherwise a new tensor is returned.
+    Returns (o [B,H,V], next_state)."""
+    dev = q.device
+    B, H, K = q.shape
+    V = v.shape[-1]
+    dt = q.dtype
+    code = _dtype_code(dt)
+    _check(k, "k", (B, H, K), dt, dev)
+    _check(v, "v", (B, H, V), dt, dev)
+    _check(g, "g", (B, H), dt, dev)
+    _check(beta, "beta", (B, H), dt, dev)
+    n_state = 0
+    if state is not None:
+        n_state = state.shape[0]
+        if n_state not in (1, B):
+            raise ValueError(f"state must have {B} or 1 rows, got {n_state}")
+        _check(state, "state", (n_state, H, K, V), torch.float32, dev)
+    if next_state is None:
+        next_state = state if (state is not None and n_state == B) else \
+            torch.empty((B, H, K, V), dtype=torch.float32, device=dev)
+    _check(next_state, "next_state", (B, H, K, V), torch.float32, dev)
+    o = out if out is not None else torch.empty((B, H, V), dtype=dt, device=dev)
+    _check(o, "out", (B, H, V), dt, dev)
+    st = lib().wkv7_gdn_step(code, B, H, K, V, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                             _ptr(state), n_state, _ptr(next_state), _ptr(o), _stream(dev))
+    if st != OK:
+        raise WKV7Error(st)
+    return o, next_state
 
 
 def step(r, w, k, v, a, b, state, out=None):

@@ -27,14 +27,14 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert {"wkv7_fwd", "wkv7_fwd_varlen", "wkv7_gdn_fwd", "wkv7_bwd", "wkv7_bwd_workspace_bytes", "wkv7_step", "wkv7_strerror", "wkv7_fwd_path",
+    assert {"wkv7_fwd", "wkv7_fwd_varlen", "wkv7_gdn_fwd", "wkv7_bwd", "wkv7_bwd_workspace_bytes", "wkv7_gdn_step", "wkv7_step", "wkv7_strerror", "wkv7_fwd_path",
             "wkv7_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"{n} declared in wkv7.h but not exported"
 
 
 def test_version_and_strerror(L):
-    assert L.wkv7_version() == 103
+    assert L.wkv7_version() == 104
     for code in range(4):
         assert len(L.wkv7_strerror(code)) > 0
     assert L.wkv7_strerror(99) == b"unknown status"
@@ -222,3 +222,32 @@ def test_bwd_rejects_null_and_misaligned(L, slot):
     assert bwd(L, ptrs=ptrs) == wkv7.ERR_INVALID_ARG
     ptrs[slot] = ODD
     assert bwd(L, ptrs=ptrs) == wkv7.ERR_INVALID_ARG
+
+
+def gdn_step(L, dtype=1, B=2, H=1, K=64, V=64, ptrs=None, s_in=None, n_state=0, s_out=GOOD):
+    ptrs = ptrs or [GOOD] * 6
+    q, k, v, g, beta, o = ptrs
+    return L.wkv7_gdn_step(dtype, B, H, K, V, q, k, v, g, beta, s_in, n_state, s_out, o, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), wkv7.ERR_INVALID_ARG),
+    (dict(dtype=4), wkv7.ERR_INVALID_ARG),
+    (dict(K=64, V=32), wkv7.ERR_UNSUPPORTED),
+    (dict(s_out=None), wkv7.ERR_INVALID_ARG),
+    (dict(s_out=ODD), wkv7.ERR_INVALID_ARG),
+    (dict(s_in=ODD, n_state=2), wkv7.ERR_INVALID_ARG),
+    (dict(s_in=GOOD, n_state=3), wkv7.ERR_INVALID_ARG),
+    (dict(s_in=GOOD, n_state=1), wkv7.ERR_INVALID_ARG),     # shared state overwritten in place
+])
+def test_gdn_step_validation(L, kw, code):
+    assert gdn_step(L, **kw) == code
+
+
+@pytest.mark.parametrize("slot", range(6))
+def test_gdn_step_rejects_null_and_misaligned(L, slot):
+    ptrs = [GOOD] * 6
+    ptrs[slot] = None
+    assert gdn_step(L, ptrs=ptrs) == wkv7.ERR_INVALID_ARG
+    ptrs[slot] = ODD
+    assert gdn_step(L, ptrs=ptrs) == wkv7.ERR_INVALID_ARG

@@ -129,3 +129,39 @@ def test_gdn_full_size_sampled(D, B, H):
         sl = {n: inp[n][bb:bb + 1, :, h:h + 1] for n in NAMES}
         o_ref, s_ref = oracle.gdn_fwd(*(sl[n] for n in NAMES), None)
         hz.check("bf16", o[bb, :, h], o_ref[0, :, 0], sf[bb, h], s_ref[0, 0], what=f"gdn full D{D} b{bb} h{h}")
+
+
+@pytest.mark.parametrize("dtype,D,state", [("bf16", 64, "own"), ("bf16", 128, "shared"), ("f32", 64, "none"),
+                                           ("f32", 128, "own"), ("bf16", 64, "shared")])
+def test_gdn_step_matches_oracle(dtype, D, state):
+    """Single-token decode (the T = 1 case of the forward): output and next
+    state against the oracle's gated delta rule."""
+    B, H = 5, 3
+    inp = synth.make_gdn(B, 1, H, D, seed=4700 + D, dtype=dtype, init=state != "none",
+                         n_state=1 if state == "shared" else None)
+    dev = to_dev(inp)
+    one = {n: dev[n][:, 0].contiguous() for n in NAMES}
+    s_in = dev["s0"]
+    o, s_next = wkv7.gdn_step(*(one[n] for n in NAMES), state=s_in)
+    torch.cuda.synchronize()
+    if state == "own":
+        assert s_next.data_ptr() == s_in.data_ptr()      # B rows: updated in place
+    o_ref, s_ref = ref(inp)
+    hz.check(dtype, hz.to_np(o), o_ref[:, 0], hz.to_np(s_next), s_ref, what=f"gdn step {dtype} D{D} {state}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_gdn_steps_equal_forward(D):
+    """Twelve consecutive in-place decode steps reproduce the oracle's
+    forward over the same twelve tokens."""
+    B, T, H = 3, 12, 2
+    inp = synth.make_gdn(B, T, H, D, seed=4800 + D, init=True)
+    dev = to_dev(inp)
+    state = dev["s0"].clone()
+    outs = []
+    for t in range(T):
+        o, state = wkv7.gdn_step(*(dev[n][:, t].contiguous() for n in NAMES), state=state)
+        outs.append(hz.to_np(o))
+    torch.cuda.synchronize()
+    o_ref, s_ref = ref(inp)
+    hz.check("bf16", np.stack(outs, axis=1), o_ref, hz.to_np(state), s_ref, what=f"gdn steps D{D}")
