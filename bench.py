@@ -421,6 +421,44 @@ def other_workloads(steps, warmup):
                        "frac_of_8TBps": round(step_bytes * NSTEP / ms_total / 1e6 / HBM_PEAK_GBS, 4),
                        "bytes_per_step": step_bytes, "kernel": "step d64",
                        "note": "inputs of 32 distinct steps cycled; state reset outside the timed region"}
+    del per_step, state, state0, obuf
+    torch.cuda.empty_cache()
+
+    # Gated DeltaNet decode on the same shape: 256 consecutive in-place steps
+    names = ("q", "k", "v", "g", "beta")
+    print(f"[bench] generating Gated DeltaNet decode B{B} H{H} d{D} (32 distinct steps, cycled)",
+          file=sys.stderr, flush=True)
+    gin = synth.make_gdn(B, 32, H, D, seed=1302, init=True)
+    gdev = {n: synth.to_torch(gin[n], "bf16", "cuda") for n in names}
+    gsteps = [{n: gdev[n][:, t].contiguous() for n in names} for t in range(32)]
+    gstate0 = torch.from_numpy(gin["s0"]).cuda()
+    gstate = gstate0.clone()
+    gbuf = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
+
+    def grun(i):
+        gstate.copy_(gstate0)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for t in range(NSTEP):
+            x = gsteps[t % 32]
+            wkv7.gdn_step(x["q"], x["k"], x["v"], x["g"], x["beta"], state=gstate, out=gbuf)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    settle(lambda: wkv7.gdn_step(gsteps[0]["q"], gsteps[0]["k"], gsteps[0]["v"], gsteps[0]["g"],
+                                 gsteps[0]["beta"], state=gstate, out=gbuf))
+    grun(0)
+    ms_total = min(grun(i) for i in range(3))
+    gbytes = 2 * B * H * D * D * 4 + 3 * B * H * D * 2 + 2 * B * H * 2 + B * H * D * 2
+    out[f"gdn_step_bf16_B{B}_H{H}_d{D}_x{NSTEP}"] = {
+        "ms_256_steps": round(ms_total, 4), "us_per_step": round(ms_total * 1e3 / NSTEP, 2),
+        "GB_per_s": round(gbytes * NSTEP / ms_total / 1e6, 1),
+        "frac_of_8TBps": round(gbytes * NSTEP / ms_total / 1e6 / HBM_PEAK_GBS, 4),
+        "bytes_per_step": gbytes, "kernel": "step d64 (Gated DeltaNet)",
+        "note": "inputs of 32 distinct steps cycled; state reset outside the timed region"}
     return out
 
 
