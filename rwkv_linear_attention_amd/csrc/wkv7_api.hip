@@ -201,6 +201,8 @@ wkv7_status_t wkv7_bwd(int dtype, int B, int T, int H, int K, int V,
     if (st != WKV7_OK) return st;
     if (T < 0) return WKV7_ERR_INVALID_ARG;
     if ((long long)B * T * H * K > (1ll << 40)) return WKV7_ERR_UNSUPPORTED;
+    // launch grids: 2 B H workgroups, and B H ceil(T/16) workgroups
+    if (2ll * B * H > INT32_MAX || (long long)B * H * ((T + 15) / 16) > INT32_MAX) return WKV7_ERR_UNSUPPORTED;
     if (T > 0) {
         const void *req[] = {r, w, k, v, a, b, d_o, dr, dw, dk, dv, da, db, workspace};
         for (const void *p : req)

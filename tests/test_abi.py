@@ -210,6 +210,7 @@ def test_bwd_workspace_size(L):
     (dict(s0=ODD), wkv7.ERR_INVALID_ARG),
     (dict(dsf=ODD), wkv7.ERR_INVALID_ARG),
     (dict(ds0=ODD), wkv7.ERR_INVALID_ARG),
+    (dict(B=1 << 16, H=1 << 14, T=16), wkv7.ERR_UNSUPPORTED),      # 2 B H workgroups exceed the grid
 ])
 def test_bwd_validation(L, kw, code):
     assert bwd(L, **kw) == code
