@@ -231,6 +231,7 @@ wkv7_status_t wkv7_step(int dtype, int B, int H, int K, int V,
 {
     wkv7_status_t st = check_common(dtype, B, H, K, V);
     if (st != WKV7_OK) return st;
+    if (4ll * B * H > INT32_MAX) return WKV7_ERR_UNSUPPORTED;   // up to four waves per (b, h)
     const void *req[] = {r, w, k, v, a, b, state, o};
     for (const void *p : req)
         if (!p || !aligned16(p)) return WKV7_ERR_INVALID_ARG;
@@ -246,6 +247,7 @@ wkv7_status_t wkv7_gdn_step(int dtype, int B, int H, int K, int V,
 {
     wkv7_status_t st = check_common(dtype, B, H, K, V);
     if (st != WKV7_OK) return st;
+    if (4ll * B * H > INT32_MAX) return WKV7_ERR_UNSUPPORTED;   // up to four waves per (b, h)
     const void *req[] = {q, k, v, g, beta, state_out, o};
     for (const void *p : req)
         if (!p || !aligned16(p)) return WKV7_ERR_INVALID_ARG;

@@ -97,6 +97,8 @@ def test_step_rejects_null_and_misaligned(L, slot):
 
 
 def test_step_rejects_sizes(L):
+    assert step(L, B=1 << 15, H=1 << 14, K=128, V=128) == wkv7.ERR_UNSUPPORTED   # 4 B H waves exceed an int
+    assert gdn_step(L, B=1 << 15, H=1 << 14, K=128, V=128) == wkv7.ERR_UNSUPPORTED
     assert step(L, B=0) == wkv7.ERR_INVALID_ARG
     assert step(L, K=64, V=32) == wkv7.ERR_UNSUPPORTED
     assert step(L, dtype=5) == wkv7.ERR_INVALID_ARG
