@@ -174,6 +174,22 @@ wkv7_status_t wkv7_gdn_fwd(int dtype, int B, int T, int H, int K, int V,
                            void *o, float *final_state, int algo, void *stream);
 
 /*
+ * wkv7_gdn_fwd_varlen -- Gated DeltaNet forward over N variable-length
+ * sequences packed on one token axis, each starting from an entry of a pool
+ * of initial states: wkv7_gdn_fwd's operation with wkv7_fwd_varlen's packing
+ * and state indexing (same argument meanings; g and beta are [total_T,H]).
+ * With state_map NULL the pool has N rows (row n) or one shared row.  A
+ * mapped or shared pool may not be the final_state buffer.
+ */
+wkv7_status_t wkv7_gdn_fwd_varlen(int dtype, int N, int total_T, int H, int K, int V,
+                                  const int32_t *cu_seqlens,
+                                  const void *q, const void *k, const void *v,
+                                  const void *g, const void *beta,
+                                  const float *initial_state, int n_state,
+                                  const int32_t *state_map,
+                                  void *o, float *final_state, int algo, void *stream);
+
+/*
  * wkv7_bwd -- gradients of wkv7_fwd (rwkv-ops README, section
  * "rwkv7op 使用方法": generalized_delta_rule is the trainable entry; the
  * derivative follows from the recurrence by the chain rule).  For upstream
@@ -268,7 +284,7 @@ int wkv7_fwd_path(int dtype, int B, int T, int H, int K, int V, int algo);
 
 /* ABI version of this header (major * 100 + minor): 101 adds wkv7_fwd_varlen,
  * 102 adds wkv7_gdn_fwd, 103 adds wkv7_bwd and wkv7_bwd_workspace_bytes,
- * 104 adds wkv7_gdn_step. */
+ * 104 adds wkv7_gdn_step, 105 adds wkv7_gdn_fwd_varlen. */
 int wkv7_version(void);
 
 #ifdef __cplusplus

@@ -40,7 +40,7 @@ int choose_path(int dtype, int T, int algo)
 
 extern "C" {
 
-int wkv7_version(void) { return 104; }
+int wkv7_version(void) { return 105; }
 
 const char *wkv7_strerror(int status)
 {
@@ -177,6 +177,47 @@ wkv7_status_t wkv7_gdn_fwd(int dtype, int B, int T, int H, int K, int V,
     wkv7::FwdArgs args{B, T, H, K, q, g, k, v, beta, nullptr, initial_state, nullptr, o, final_state};
     args.n_state = initial_state ? n_state : 0;
     args.gdn = true;
+    hipError_t e = path == WKV7_ALGO_CHUNKED ? wkv7::launch_chunked(args, s)
+                                             : wkv7::launch_recurrent(dtype, args, s);
+    return e == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
+}
+
+wkv7_status_t wkv7_gdn_fwd_varlen(int dtype, int N, int total_T, int H, int K, int V,
+                                  const int32_t *cu_seqlens,
+                                  const void *q, const void *k, const void *v,
+                                  const void *g, const void *beta,
+                                  const float *initial_state, int n_state,
+                                  const int32_t *state_map,
+                                  void *o, float *final_state, int algo, void *stream)
+{
+    wkv7_status_t st = check_common(dtype, N, H, K, V);
+    if (st != WKV7_OK) return st;
+    if (total_T < 0) return WKV7_ERR_INVALID_ARG;
+    if ((long long)total_T * H * K > (1ll << 40)) return WKV7_ERR_UNSUPPORTED;
+    if (algo != WKV7_ALGO_AUTO && algo != WKV7_ALGO_RECURRENT && algo != WKV7_ALGO_CHUNKED)
+        return WKV7_ERR_INVALID_ARG;
+    if (!cu_seqlens || ((uintptr_t)cu_seqlens & 3u)) return WKV7_ERR_INVALID_ARG;
+    if (state_map && ((uintptr_t)state_map & 3u)) return WKV7_ERR_INVALID_ARG;
+    if (total_T > 0) {
+        const void *req[] = {q, k, v, g, beta, o};
+        for (const void *p : req)
+            if (!p || !aligned16(p)) return WKV7_ERR_INVALID_ARG;
+    }
+    if (initial_state) {
+        if (!aligned16(initial_state) || n_state < 1) return WKV7_ERR_INVALID_ARG;
+        if (!state_map && n_state != N && n_state != 1) return WKV7_ERR_INVALID_ARG;
+        // a pool read through a map, or one shared row, may not be overwritten
+        if ((state_map || (n_state == 1 && N > 1)) && final_state == initial_state) return WKV7_ERR_INVALID_ARG;
+    }
+    if (final_state && !aligned16(final_state)) return WKV7_ERR_INVALID_ARG;
+    const int path = choose_path(dtype, total_T / N, algo);
+    if (path < 0) return WKV7_ERR_UNSUPPORTED;
+    wkv7::FwdArgs args{N, total_T, H, K, q, g, k, v, beta, nullptr, initial_state, nullptr, o, final_state};
+    args.cu_seqlens = cu_seqlens;
+    args.state_map = state_map;
+    args.n_state = initial_state ? n_state : 0;
+    args.gdn = true;
+    hipStream_t s = (hipStream_t)stream;
     hipError_t e = path == WKV7_ALGO_CHUNKED ? wkv7::launch_chunked(args, s)
                                              : wkv7::launch_recurrent(dtype, args, s);
     return e == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;

@@ -40,6 +40,8 @@ def lib():
     L.wkv7_bwd.restype = i
     L.wkv7_bwd_workspace_bytes.argtypes = [i] * 5
     L.wkv7_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.wkv7_gdn_fwd_varlen.argtypes = [i, i, i, i, i, i, p] + [p] * 6 + [i, p, p, p, i, p]
+    L.wkv7_gdn_fwd_varlen.restype = i
     L.wkv7_gdn_step.argtypes = [i, i, i, i, i] + [p] * 6 + [i, p, p, p]
     L.wkv7_gdn_step.restype = i
     L.wkv7_step.argtypes = [i, i, i, i, i] + [p] * 8 + [p]
@@ -260,6 +262,55 @@ def gdn_fwd(q, k, v, g, beta, initial_state=None, output_final_state=True, algo=
     if st != OK:
         raise WKV7Error(st)
     return o, sf
+
+
+def gdn_fwd_varlen(q, k, v, g, beta, cu_seqlens, initial_state=None, state_map=None,
+                   output_final_state=True, algo=ALGO_AUTO, out=None, final_state=None):
+    """Gated DeltaNet forward over packed variable-length sequences.  q, k:
+    [T_total,H,K] (or [1,T_total,H,K]); v: [T_total,H,V]; g, beta:
+    [T_total,H]; cu_seqlens: int32 [N+1] token offsets (device);
+    initial_state: [n_state,H,K,V] float32 pool or None; state_map: int32 [N]
+    pool row per sequence (out of range: zero state) or None (row n, or the
+    single shared row).  Returns (o shaped like v, final_state [N,H,K,V])."""
+    dev = q.device
+    lead1 = q.dim() == 4
+    if lead1:
+        if q.shape[0] != 1:
+            raise ValueError("packed inputs take a leading dimension of 1, or none")
+        q, k, v, g, beta = (t.squeeze(0) for t in (q, k, v, g, beta))
+    TT, H, K = q.shape
+    V = v.shape[-1]
+    dt = q.dtype
+    code = _dtype_code(dt)
+    _check(k, "k", (TT, H, K), dt, dev)
+    _check(v, "v", (TT, H, V), dt, dev)
+    _check(g, "g", (TT, H), dt, dev)
+    _check(beta, "beta", (TT, H), dt, dev)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be [N+1] with N >= 1")
+    N = cu_seqlens.numel() - 1
+    _check(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    n_state = 0
+    if initial_state is not None:
+        n_state = initial_state.shape[0]
+        _check(initial_state, "initial_state", (n_state, H, K, V), torch.float32, dev)
+    if state_map is not None:
+        _check(state_map, "state_map", (N,), torch.int32, dev)
+    if out is not None:
+        o = out.squeeze(0) if (lead1 and out.dim() == 4) else out
+    else:
+        o = torch.empty((TT, H, V), dtype=dt, device=dev)
+    _check(o, "out", (TT, H, V), dt, dev)
+    sf = None
+    if output_final_state:
+        sf = final_state if final_state is not None else torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
+        _check(sf, "final_state", (N, H, K, V), torch.float32, dev)
+    st = lib().wkv7_gdn_fwd_varlen(code, N, TT, H, K, V, _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                   _ptr(beta), _ptr(initial_state), n_state, _ptr(state_map), _ptr(o), _ptr(sf),
+                                   int(algo), _stream(dev))
+    if st != OK:
+        raise WKV7Error(st)
+    return (o.unsqueeze(0) if lead1 else o), sf
 
 
 def gdn_step(q, k, v, g, beta, state=None, out=None, next_state=None):

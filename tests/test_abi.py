@@ -27,14 +27,14 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert {"wkv7_fwd", "wkv7_fwd_varlen", "wkv7_gdn_fwd", "wkv7_bwd", "wkv7_bwd_workspace_bytes", "wkv7_gdn_step", "wkv7_step", "wkv7_strerror", "wkv7_fwd_path",
+    assert {"wkv7_fwd", "wkv7_fwd_varlen", "wkv7_gdn_fwd", "wkv7_bwd", "wkv7_bwd_workspace_bytes", "wkv7_gdn_step", "wkv7_gdn_fwd_varlen", "wkv7_step", "wkv7_strerror", "wkv7_fwd_path",
             "wkv7_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"{n} declared in wkv7.h but not exported"
 
 
 def test_version_and_strerror(L):
-    assert L.wkv7_version() == 104
+    assert L.wkv7_version() == 105
     for code in range(4):
         assert len(L.wkv7_strerror(code)) > 0
     assert L.wkv7_strerror(99) == b"unknown status"
@@ -254,3 +254,28 @@ def test_gdn_step_rejects_null_and_misaligned(L, slot):
     assert gdn_step(L, ptrs=ptrs) == wkv7.ERR_INVALID_ARG
     ptrs[slot] = ODD
     assert gdn_step(L, ptrs=ptrs) == wkv7.ERR_INVALID_ARG
+
+
+def gdn_varlen(L, dtype=1, N=2, TT=40, H=1, K=64, V=64, cu=GOOD, ptrs=None, s0=None, n_state=0, smap=None,
+               sf=None, algo=0):
+    ptrs = ptrs or [GOOD] * 6
+    q, k, v, g, beta, o = ptrs
+    return L.wkv7_gdn_fwd_varlen(dtype, N, TT, H, K, V, cu, q, k, v, g, beta, s0, n_state, smap, o, sf, algo,
+                                 None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=0), wkv7.ERR_INVALID_ARG),
+    (dict(cu=None), wkv7.ERR_INVALID_ARG),
+    (dict(cu=P(0x100002)), wkv7.ERR_INVALID_ARG),
+    (dict(smap=P(0x100001)), wkv7.ERR_INVALID_ARG),
+    (dict(s0=GOOD, n_state=0), wkv7.ERR_INVALID_ARG),
+    (dict(s0=GOOD, n_state=3), wkv7.ERR_INVALID_ARG),             # no map: N rows or one shared row
+    (dict(s0=GOOD, n_state=1, sf=GOOD), wkv7.ERR_INVALID_ARG),    # shared row overwritten
+    (dict(s0=GOOD, n_state=4, smap=GOOD, sf=GOOD), wkv7.ERR_INVALID_ARG),   # mapped pool overwritten
+    (dict(ptrs=[GOOD] * 5 + [None]), wkv7.ERR_INVALID_ARG),
+    (dict(K=64, V=128), wkv7.ERR_UNSUPPORTED),
+    (dict(dtype=0, algo=2), wkv7.ERR_UNSUPPORTED),
+])
+def test_gdn_varlen_validation(L, kw, code):
+    assert gdn_varlen(L, **kw) == code

@@ -140,3 +140,14 @@ def test_bwd_full_size_sampled(D, B, H):
         for n in NAMES:
             check_grad("bf16", g[n][bb, :, h], ref[n][0, :, 0], f"bwd full D{D} b{bb} h{h} d{n}")
         check_grad("f32", g["s0"][bb, h], ref["s0"][0, 0], f"bwd full D{D} b{bb} h{h} ds0")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_bwd_deterministic(D):
+    """No atomics or order-dependent sums: two runs give bit-identical
+    gradients."""
+    inp, d_o, d_sf = make_case(4, 300, 8, D, "bf16", seed=5600 + D, mask="bernoulli")
+    g1 = run_gpu(inp, d_o, d_sf)
+    g2 = run_gpu(inp, d_o, d_sf)
+    for n in g1:
+        np.testing.assert_array_equal(g1[n], g2[n], err_msg=n)

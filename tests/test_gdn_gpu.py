@@ -165,3 +165,35 @@ def test_gdn_steps_equal_forward(D):
     torch.cuda.synchronize()
     o_ref, s_ref = ref(inp)
     hz.check("bf16", np.stack(outs, axis=1), o_ref, hz.to_np(state), s_ref, what=f"gdn steps D{D}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("algo", [REC, CHK])
+@pytest.mark.parametrize("pool", ["map", "shared", "rows"])
+def test_gdn_varlen(D, algo, pool):
+    """Packed sequences (mixed lengths, one empty) are independent runs of the
+    Gated DeltaNet forward, each from its pool row."""
+    lengths = [37, 0, 16, 101, 5]
+    N, TT, H = len(lengths), sum(lengths), 2
+    inp = synth.make_gdn(1, TT, H, D, seed=4900 + D, init=False)
+    rng = np.random.default_rng(4901)
+    n_pool = {"map": 3, "shared": 1, "rows": N}[pool]
+    poolv = (rng.standard_normal((n_pool, H, D, D)) * 0.1).astype(np.float32)
+    smap = np.array([2, 0, 7, 1, 2], np.int32) if pool == "map" else None     # 7: out of range -> zeros
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    dev = {n: synth.to_torch(inp[n][0], "bf16", "cuda") for n in NAMES}
+    o, sf = wkv7.gdn_fwd_varlen(*(dev[n] for n in NAMES), torch.from_numpy(cu).cuda(),
+                                initial_state=torch.from_numpy(poolv).cuda(),
+                                state_map=None if smap is None else torch.from_numpy(smap).cuda(), algo=algo)
+    torch.cuda.synchronize()
+    o, sf = hz.to_np(o), hz.to_np(sf)
+    for n in range(N):
+        s_, e_ = int(cu[n]), int(cu[n + 1])
+        row = {"map": None if smap is None else int(smap[n]), "shared": 0, "rows": n}[pool]
+        s0 = poolv[row:row + 1] if row is not None and 0 <= row < n_pool else None
+        sl = {x: inp[x][:, s_:e_] for x in NAMES}
+        o_ref, s_ref = oracle.gdn_fwd(*(sl[x] for x in NAMES), s0)
+        if e_ > s_:
+            hz.check("bf16", o[s_:e_], o_ref[0], sf[n], s_ref[0], what=f"gdn varlen D{D} seq{n}")
+        else:
+            np.testing.assert_array_equal(sf[n], s_ref[0])
