@@ -85,6 +85,26 @@ def cpu_baseline(inp, H, T, budget_s=12.0, max_threads=16):
                       f"{len(pairs)} sequences of the workload; fp64 C, OpenMP), {t_used:.1f} s"}
 
 
+def oracle_sample_rate(call, B, H, T, budget_s=4.0, max_threads=16):
+    """Time call(pairs) -- the fp64 oracle on a list of (b, h) sequences --
+    on growing batches until about budget_s seconds of work; report the rate
+    scaled to the whole workload (tokens of all heads) in Mtokens/s."""
+    import oracle
+    threads = min(max_threads, len(os.sched_getaffinity(0)))
+    oracle.set_threads(threads)
+    pairs = [(bb, h) for h in range(H) for bb in range(B)]
+    done, t_used, batch = 0, 0.0, threads
+    while t_used < budget_s and done < len(pairs):
+        sel = pairs[done:done + batch]
+        t0 = time.perf_counter()
+        call(sel)
+        t_used += time.perf_counter() - t0
+        done += len(sel)
+        batch = min(batch * 2, 8 * threads)
+    return {"value": round(done * T / H / t_used / 1e6, 5), "unit": "Mtokens/s", "cores": threads,
+            "kind": "oracle", "sample": f"{done} (b,h) sequences of T={T} (fp64 C, OpenMP), {t_used:.1f} s"}
+
+
 SETTLE_MS = 100.0
 
 
@@ -208,7 +228,7 @@ def main():
         result["cpu_baseline"] = cpu_baseline(inp, H, T)
     if args.all:
         del dev, o, sf, inp
-        result["others"] = other_workloads(args.steps, args.warmup)
+        result["others"] = other_workloads(args.steps, args.warmup, not args.no_cpu)
     print(json.dumps(result), flush=True)
 
 
@@ -277,7 +297,7 @@ def varlen_workload(steps, warmup):
                    "lengths": [int(x) for x in lens], "kernel": "chunked d64 (packed)"}}
 
 
-def gdn_workload(steps, warmup):
+def gdn_workload(steps, warmup, cpu=True):
     """Gated DeltaNet forward on the chunked kernel at the B8 T4096 H64 d64
     shape (bf16, no initial state, final state written)."""
     import torch
@@ -291,6 +311,16 @@ def gdn_workload(steps, warmup):
     sf = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
     ms = _time_launches(lambda i: wkv7.gdn_fwd(*(dev[n] for n in names), out=o, final_state=sf),
                         steps, warmup)
+    cpu_rate = None
+    if cpu:
+        import numpy as np
+        import oracle
+
+        def call(sel):
+            gsel = lambda x: np.stack([x[bb, :, h] for bb, h in sel])[:, :, None]
+            oracle.gdn_fwd(*(gsel(inp[n]) for n in names), None)
+        print("[bench] timing the CPU oracle (Gated DeltaNet) on a sample", file=sys.stderr, flush=True)
+        cpu_rate = oracle_sample_rate(call, B, H, T)
     # q, k, v and o once (D channels each), g and beta once (one element per
     # token and head), the final state written once
     nbytes = 4 * B * T * H * D * 2 + 2 * B * T * H * 2 + B * H * D * D * 4
@@ -298,10 +328,10 @@ def gdn_workload(steps, warmup):
     return {name: {"ms": round(ms, 5), "Mtokens_per_s": round(B * T / ms / 1e3, 3),
                    "GB_per_s": round(nbytes / ms / 1e6, 1),
                    "frac_of_8TBps": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes,
-                   "kernel": "chunked d64 (Gated DeltaNet)"}}
+                   "kernel": "chunked d64 (Gated DeltaNet)", "cpu_oracle": cpu_rate}}
 
 
-def bwd_workload(steps, warmup, idx):
+def bwd_workload(steps, warmup, idx, cpu=True):
     """Backward (wkv7_bwd) on a forward workload's shape and inputs, with a
     seeded N(0, 1) output gradient rounded to bf16; the initial state and the
     mask of the workload are used, no final-state gradient."""
@@ -317,8 +347,20 @@ def bwd_workload(steps, warmup, idx):
     s0 = None if inp["s0"] is None else torch.from_numpy(inp["s0"]).cuda()
     mask = None if inp["mask"] is None else torch.from_numpy(inp["mask"]).cuda()
     rng = np.random.default_rng(1400 + idx)
-    d_o = synth.to_torch(rng.standard_normal((B, T, H, D), dtype=np.float32), "bf16", "cuda")
-    del inp
+    d_o_np = synth.round_to(rng.standard_normal((B, T, H, D), dtype=np.float32), "bf16")
+    d_o = synth.to_torch(d_o_np, "bf16", "cuda")
+    cpu_rate = None
+    if cpu:
+        import oracle
+
+        def call(sel):
+            gsel = lambda x: np.stack([x[bb, :, h] for bb, h in sel])[:, :, None, :]
+            s0s = None if inp["s0"] is None else np.stack([inp["s0"][bb, h] for bb, h in sel])[:, None]
+            ms = None if inp["mask"] is None else np.stack([inp["mask"][bb] for bb, h in sel])
+            oracle.bwd(*(gsel(inp[n]) for n in names), gsel(d_o_np), s0s, ms, None)
+        print("[bench] timing the CPU oracle backward on a sample", file=sys.stderr, flush=True)
+        cpu_rate = oracle_sample_rate(call, B, H, T)
+    del inp, d_o_np
     ws = torch.empty(wkv7.bwd_workspace_bytes(B, T, H, D, D), dtype=torch.uint8, device="cuda")
     ms = _time_launches(lambda i: wkv7.bwd(*(dev[n] for n in names), d_o, initial_state=s0, mask=mask,
                                            workspace=ws), max(3, steps // 4), max(1, warmup // 4))
@@ -332,7 +374,7 @@ def bwd_workload(steps, warmup, idx):
                    "GB_per_s": round(nbytes / ms / 1e6, 1),
                    "frac_of_8TBps": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes,
                    "workspace_bytes": ws.numel(),
-                   "kernel": f"recurrences + per-chunk gradients, d{D}"}}
+                   "kernel": f"recurrences + per-chunk gradients, d{D}", "cpu_oracle": cpu_rate}}
 
 
 def _time_launches(fn, steps, warmup):
@@ -351,7 +393,7 @@ def _time_launches(fn, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
-def other_workloads(steps, warmup):
+def other_workloads(steps, warmup, cpu=True):
     """Head size 128 forward (B16 T4096 H32, trailing-padding mask, S0), the
     packed variable-length forward, Gated DeltaNet (B8 T4096 H64 d64), the
     backward on the d64 and d128 shapes and the decode step (B512 H40 d64,
@@ -380,11 +422,11 @@ def other_workloads(steps, warmup):
 
     out.update(varlen_workload(steps, warmup))
     torch.cuda.empty_cache()
-    out.update(gdn_workload(steps, warmup))
+    out.update(gdn_workload(steps, warmup, cpu))
     torch.cuda.empty_cache()
-    out.update(bwd_workload(steps, warmup, 2))
+    out.update(bwd_workload(steps, warmup, 2, cpu))
     torch.cuda.empty_cache()
-    out.update(bwd_workload(steps, warmup, 3))
+    out.update(bwd_workload(steps, warmup, 3, cpu))
     torch.cuda.empty_cache()
 
     wl = synth.WORKLOADS[4]
