@@ -79,10 +79,24 @@ def cpu_baseline(inp, H, T, budget_s=12.0, max_threads=16):
         batch = min(batch * 2, 4 * threads * 8)
     seq_tokens = done * T                    # single-head tokens processed
     full_tokens = seq_tokens / H             # = tokens of the workload (all heads)
+    # one thread on a few whole sequences, extrapolated to the workload
+    oracle.set_threads(1)
+    n1 = 8
+    sel = pairs[:n1]
+    g = lambda n: np.stack([inp[n][bb, :, h] for bb, h in sel])[:, :, None, :]
+    args = [g(n) for n in ("r", "w", "k", "v", "a", "b")]
+    t0 = time.perf_counter()
+    oracle.fwd(*args)
+    t1 = time.perf_counter() - t0
+    oracle.set_threads(threads)
     return {"value": full_tokens / t_used / 1e6, "unit": "Mtokens/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{done} (b,h) sequences of T={T} ({done / len(pairs):.2f} passes over the "
-                      f"{len(pairs)} sequences of the workload; fp64 C, OpenMP), {t_used:.1f} s"}
+                      f"{len(pairs)} sequences of the workload; fp64 C, OpenMP), {t_used:.1f} s",
+            "single_thread": {"value": round(n1 * T / H / t1 / 1e6, 6), "unit": "Mtokens/s",
+                              "extrapolated_workload_s": round(t1 / n1 * len(pairs), 1),
+                              "sample": f"{n1} (b,h) sequences of T={T} on one thread, {t1:.2f} s, "
+                                        f"extrapolated to the {len(pairs)} sequences of the workload"}}
 
 
 def oracle_sample_rate(call, B, H, T, budget_s=4.0, max_threads=16):
@@ -393,14 +407,43 @@ def _time_launches(fn, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
-def other_workloads(steps, warmup, cpu=True):
-    """Head size 128 forward (B16 T4096 H32, trailing-padding mask, S0), the
-    packed variable-length forward, Gated DeltaNet (B8 T4096 H64 d64), the
-    backward on the d64 and d128 shapes and the decode step (B512 H40 d64,
-    256 consecutive in-place steps)."""
+def small_latency(steps, warmup):
+    """Launch latency of the two small forward shapes (B1 T64 H1 d64 fp32;
+    B2 T1024 H4 d64 bf16 with initial state and mask), which hold too few
+    sequences to fill the GPU: reported as time per call under AUTO."""
     import torch
     from rwkv_linear_attention_amd import synth, wkv7
     out = {}
+    for idx in (0, 1):
+        wl = synth.WORKLOADS[idx]
+        B, T, H, D, dt = wl["B"], wl["T"], wl["H"], wl["K"], wl["dtype"]
+        inp = synth.make(idx)
+        dev = {n: synth.to_torch(inp[n], dt, "cuda") for n in ("r", "w", "k", "v", "a", "b")}
+        s0 = None if inp["s0"] is None else torch.from_numpy(inp["s0"]).cuda()
+        mask = None if inp["mask"] is None else torch.from_numpy(inp["mask"]).cuda()
+        tdt = torch.float32 if dt == "f32" else torch.bfloat16
+        o = torch.empty((B, T, H, D), dtype=tdt, device="cuda")
+        sf = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
+        ms = _time_launches(lambda i: wkv7.fwd(*(dev[n] for n in ("r", "w", "k", "v", "a", "b")),
+                                               initial_state=s0, mask=mask, out=o, final_state=sf),
+                            max(20, steps), warmup)
+        path = wkv7.fwd_path(tdt, B, T, H, D, D)
+        out[wl["name"]] = {"us_per_call": round(ms * 1e3, 2), "Mtokens_per_s": round(B * T / ms / 1e3, 3),
+                           "kernel": "chunked" if path == wkv7.ALGO_CHUNKED else "recurrent",
+                           "note": "latency only: too few sequences to fill the GPU"}
+        del dev, s0, mask, o, sf, inp
+    return out
+
+
+def other_workloads(steps, warmup, cpu=True):
+    """Latency of the two small forward shapes, then head size 128 forward
+    (B16 T4096 H32, trailing-padding mask, S0), the packed variable-length
+    forward, Gated DeltaNet (B8 T4096 H64 d64), the backward on the d64 and
+    d128 shapes and the decode step (B512 H40 d64, 256 consecutive in-place
+    steps)."""
+    import torch
+    from rwkv_linear_attention_amd import synth, wkv7
+    out = small_latency(steps, warmup)
     wl = synth.WORKLOADS[3]
     B, T, H, D = wl["B"], wl["T"], wl["H"], wl["K"]
     print(f"[bench] generating workload {wl['name']}", file=sys.stderr, flush=True)

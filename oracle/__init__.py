@@ -1,5 +1,5 @@
 """fp64 CPU oracle for the RWKV-7 WKV7 forward, its backward and the Gated
-DeltaNet forward -- TEST INFRASTRUCTURE ONLY.
+DeltaNet forward and backward -- TEST INFRASTRUCTURE ONLY.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  The HIP product path never imports it,
@@ -51,6 +51,8 @@ def _load():
     lib.wkv7_oracle_bwd.restype = i
     lib.gdn_oracle_fwd.argtypes = [i, i, i, i, i] + [d] * 6 + [i, d, d]
     lib.gdn_oracle_fwd.restype = i
+    lib.gdn_oracle_bwd.argtypes = [i, i, i, i, i] + [d] * 6 + [i] + [d] * 8
+    lib.gdn_oracle_bwd.restype = i
     lib.wkv7_oracle_max_threads.restype = i
     lib.wkv7_oracle_set_threads.argtypes = [i]
     _lib = lib
@@ -166,6 +168,36 @@ def gdn_fwd(q, k, v, g, beta, initial_state=None):
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return o, sf
+
+
+def gdn_bwd(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None):
+    """Backward of gdn_fwd (reverse-mode derivative of the gated delta rule
+    with the L2 normalisation of q and k; see the C file).  d_o: [B,T,H,V];
+    d_final_state: [B,H,K,V] or None (zero).  Returns a dict of float64
+    gradients q, k, v, g, beta (input shapes) and s0 ([n,H,K,V] with n the
+    initial state's leading size, B when there is none)."""
+    lib = _load()
+    q, k, v, g, beta, d_o = (_f64(x) for x in (q, k, v, g, beta, d_o))
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    assert k.shape == (B, T, H, K) and v.shape == (B, T, H, V) and d_o.shape == (B, T, H, V)
+    assert g.shape == (B, T, H) and beta.shape == (B, T, H)
+    s0 = None if initial_state is None else _f64(initial_state)
+    n_s0 = B
+    if s0 is not None:
+        n_s0 = s0.shape[0]
+        assert s0.shape == (n_s0, H, K, V) and n_s0 in (1, B)
+    dsf = None if d_final_state is None else _f64(d_final_state)
+    if dsf is not None:
+        assert dsf.shape == (B, H, K, V)
+    out = {"q": np.zeros((B, T, H, K)), "k": np.zeros((B, T, H, K)), "v": np.zeros((B, T, H, V)),
+           "g": np.zeros((B, T, H)), "beta": np.zeros((B, T, H)), "s0": np.zeros((n_s0, H, K, V))}
+    rc = lib.gdn_oracle_bwd(B, T, H, K, V, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                            _ptr(s0), n_s0 if s0 is not None else 0, _ptr(d_o), _ptr(dsf),
+                            *(_ptr(out[n]) for n in ("q", "k", "v", "g", "beta", "s0")))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments" if rc == -1 else "oracle ran out of memory")
+    return out
 
 
 def max_threads():

@@ -39,8 +39,9 @@
  *
  * Parity pins (closed forms, invariants, hand-worked examples, finite
  * differences) live in tests/test_oracle_pins.py (forward and step),
- * tests/test_oracle_bwd_pins.py (backward) and tests/test_oracle_gdn_pins.py
- * (Gated DeltaNet); every function here is pinned by them.
+ * tests/test_oracle_bwd_pins.py (backward), tests/test_oracle_gdn_pins.py
+ * (Gated DeltaNet forward) and tests/test_oracle_gdn_bwd_pins.py (Gated
+ * DeltaNet backward); every function here is pinned by them.
  */
 #include <math.h>
 #include <stdint.h>
@@ -356,6 +357,186 @@ int gdn_oracle_fwd(int B, int T, int H, int K, int V,
         free(S);
     }
     return 0;
+}
+
+/* ------------------------------------------------------------------------
+ * Backward of gdn_oracle_fwd: the reverse-mode derivative of the same
+ * recurrence (the pages list gated_delta_net_recurrent and
+ * gated_delta_net_chunk as trainable entries).  For upstream gradients d_o
+ * (of every output) and d_sf (of the final state, NULL = 0), walking the
+ * tokens backwards with dS = dL/dS_t, P = S_{t-1}, alpha = exp(g_t),
+ * y = P^T kn (the old state read at kn):
+ *
+ *   dS     += qn d_o_t^T
+ *   dqn     = S_t d_o_t
+ *   u       = dS^T kn
+ *   dv_t    = beta u
+ *   dbeta_t = sum_j u_j (v_j - alpha y_j)
+ *   dg_t    = sum_ij dS_ij (S_t - beta kn v^T)_ij
+ *   dkn     = beta dS v - alpha beta (dS y + P u)
+ *   dS      = alpha (dS - beta kn u^T)               (dL/dS_{t-1})
+ *
+ * and through the normalisation x -> x s, s = 1/sqrt(sum x^2 + eps):
+ *   dq = s (dqn - qn (qn . dqn)),  dk = s (dkn - kn (kn . dkn)).
+ * d_s0 is [n_s0,H,K,V]: with one shared initial state (n_s0 = 1) it is the
+ * sum over the B sequences; with no initial state it is the gradient of the
+ * zero start, [B,H,K,V].  Every state S_0 .. S_T of a sequence is kept.
+ * ------------------------------------------------------------------------ */
+int gdn_oracle_bwd(int B, int T, int H, int K, int V,
+                   const double *q, const double *k, const double *v,
+                   const double *g, const double *beta,
+                   const double *s0, int n_s0,
+                   const double *d_o, const double *d_sf,
+                   double *dq, double *dk, double *dv, double *dg, double *dbeta,
+                   double *d_s0)
+{
+    if (B < 0 || T < 0 || H < 0 || K <= 0 || V <= 0) return -1;
+    if (T > 0 && (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta))
+        return -1;
+    if (s0 && n_s0 != 1 && n_s0 != B) return -1;
+    const double eps = 1e-6;
+    const long long nseq = (long long)B * H;
+    const size_t KV = (size_t)K * V;
+    const int shared = s0 && n_s0 == 1;
+    /* per-sequence initial-state gradients, summed afterwards when shared */
+    double *ds_seq = NULL;
+    if (d_s0 && shared) {
+        ds_seq = (double *)calloc((size_t)nseq * KV, sizeof(double));
+        if (!ds_seq && nseq > 0) return -2;
+    }
+    int failed = 0;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long long bh = 0; bh < nseq; ++bh) {
+        const int bb = (int)(bh / H), h = (int)(bh % H);
+        const int KVmax = K > V ? K : V;
+        double *S = (double *)malloc(sizeof(double) * KV * ((size_t)T + 1));
+        double *dS = (double *)malloc(sizeof(double) * KV);
+        double *vec = (double *)malloc(sizeof(double) * (size_t)KVmax * 6);
+        if (!S || !dS || !vec) {
+            failed = 1;
+            free(S); free(dS); free(vec);
+            continue;
+        }
+        double *qn = vec, *kn = vec + KVmax, *y = vec + 2 * KVmax, *u = vec + 3 * KVmax;
+        double *dqn = vec + 4 * KVmax, *dkn = vec + 5 * KVmax;
+        if (s0)
+            memcpy(S, &s0[IDX_ST(shared ? 0 : bb, h, 0, 0, H, K, V)], sizeof(double) * KV);
+        else
+            memset(S, 0, sizeof(double) * KV);
+        /* forward, keeping every state: S + t*KV is S_t */
+        for (int t = 0; t < T; ++t) {
+            const double *kt = &k[IDX_TOK(bb, t, h, 0, T, H, K)];
+            const double *vt = &v[IDX_TOK(bb, t, h, 0, T, H, V)];
+            const double gt = g[((size_t)bb * T + t) * H + h];
+            const double bt = beta[((size_t)bb * T + t) * H + h];
+            double nk = 0.0;
+            for (int i = 0; i < K; ++i) nk += kt[i] * kt[i];
+            nk = 1.0 / sqrt(nk + eps);
+            for (int i = 0; i < K; ++i) kn[i] = kt[i] * nk;
+            const double *P = S + (size_t)t * KV;
+            double *Sn = S + (size_t)(t + 1) * KV;
+            for (int j = 0; j < V; ++j) {
+                double acc = 0.0;
+                for (int i = 0; i < K; ++i) acc += kn[i] * P[(size_t)i * V + j];
+                y[j] = acc;
+            }
+            const double alpha = exp(gt);
+            for (int i = 0; i < K; ++i)
+                for (int j = 0; j < V; ++j)
+                    Sn[(size_t)i * V + j] = alpha * (P[(size_t)i * V + j] - bt * kn[i] * y[j]) + bt * kn[i] * vt[j];
+        }
+        /* reverse */
+        if (d_sf)
+            memcpy(dS, &d_sf[IDX_ST(bb, h, 0, 0, H, K, V)], sizeof(double) * KV);
+        else
+            memset(dS, 0, sizeof(double) * KV);
+        for (int t = T - 1; t >= 0; --t) {
+            const double *qt = &q[IDX_TOK(bb, t, h, 0, T, H, K)];
+            const double *kt = &k[IDX_TOK(bb, t, h, 0, T, H, K)];
+            const double *vt = &v[IDX_TOK(bb, t, h, 0, T, H, V)];
+            const double *dot = &d_o[IDX_TOK(bb, t, h, 0, T, H, V)];
+            const size_t gi = ((size_t)bb * T + t) * H + h;
+            const double gt = g[gi], bt = beta[gi], alpha = exp(gt);
+            const double *P = S + (size_t)t * KV, *St = S + (size_t)(t + 1) * KV;
+            double sq = 0.0, sk = 0.0;
+            for (int i = 0; i < K; ++i) {
+                sq += qt[i] * qt[i];
+                sk += kt[i] * kt[i];
+            }
+            sq = 1.0 / sqrt(sq + eps);
+            sk = 1.0 / sqrt(sk + eps);
+            for (int i = 0; i < K; ++i) {
+                qn[i] = qt[i] * sq;
+                kn[i] = kt[i] * sk;
+            }
+            for (int i = 0; i < K; ++i)
+                for (int j = 0; j < V; ++j) dS[(size_t)i * V + j] += qn[i] * dot[j];
+            for (int i = 0; i < K; ++i) {
+                double acc = 0.0;
+                for (int j = 0; j < V; ++j) acc += St[(size_t)i * V + j] * dot[j];
+                dqn[i] = acc;
+            }
+            for (int j = 0; j < V; ++j) {
+                double ay = 0.0, au = 0.0;
+                for (int i = 0; i < K; ++i) {
+                    ay += kn[i] * P[(size_t)i * V + j];
+                    au += kn[i] * dS[(size_t)i * V + j];
+                }
+                y[j] = ay;
+                u[j] = au;
+            }
+            double db_acc = 0.0, dg_acc = 0.0;
+            for (int j = 0; j < V; ++j) {
+                dv[IDX_TOK(bb, t, h, j, T, H, V)] = bt * u[j];
+                db_acc += u[j] * (vt[j] - alpha * y[j]);
+            }
+            for (int i = 0; i < K; ++i)
+                for (int j = 0; j < V; ++j)
+                    dg_acc += dS[(size_t)i * V + j] * (St[(size_t)i * V + j] - bt * kn[i] * vt[j]);
+            dbeta[gi] = db_acc;
+            dg[gi] = dg_acc;
+            for (int i = 0; i < K; ++i) {
+                double dsv = 0.0, dsy = 0.0, pu = 0.0;
+                for (int j = 0; j < V; ++j) {
+                    dsv += dS[(size_t)i * V + j] * vt[j];
+                    dsy += dS[(size_t)i * V + j] * y[j];
+                    pu += P[(size_t)i * V + j] * u[j];
+                }
+                dkn[i] = bt * dsv - alpha * bt * (dsy + pu);
+            }
+            double pq = 0.0, pk = 0.0;
+            for (int i = 0; i < K; ++i) {
+                pq += qn[i] * dqn[i];
+                pk += kn[i] * dkn[i];
+            }
+            for (int i = 0; i < K; ++i) {
+                dq[IDX_TOK(bb, t, h, i, T, H, K)] = sq * (dqn[i] - qn[i] * pq);
+                dk[IDX_TOK(bb, t, h, i, T, H, K)] = sk * (dkn[i] - kn[i] * pk);
+            }
+            for (int i = 0; i < K; ++i)
+                for (int j = 0; j < V; ++j)
+                    dS[(size_t)i * V + j] = alpha * (dS[(size_t)i * V + j] - bt * kn[i] * u[j]);
+        }
+        if (d_s0) {
+            double *dst = shared ? ds_seq + (size_t)bh * KV : &d_s0[IDX_ST(bb, h, 0, 0, H, K, V)];
+            memcpy(dst, dS, sizeof(double) * KV);
+        }
+        free(vec);
+        free(dS);
+        free(S);
+    }
+    if (ds_seq) {
+        /* shared initial state: sum the B sequences' gradients, in order */
+        for (int h = 0; h < H; ++h)
+            for (size_t e = 0; e < KV; ++e) {
+                double acc = 0.0;
+                for (int bb = 0; bb < B; ++bb) acc += ds_seq[((size_t)bb * H + h) * KV + e];
+                d_s0[(size_t)h * KV + e] = acc;
+            }
+        free(ds_seq);
+    }
+    return failed ? -2 : 0;
 }
 
 /* Thread control for the OpenMP loop over (b, h); used to report how many
