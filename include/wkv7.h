@@ -233,6 +233,51 @@ wkv7_status_t wkv7_bwd(int dtype, int B, int T, int H, int K, int V,
 size_t wkv7_bwd_workspace_bytes(int B, int T, int H, int K, int V);
 
 /*
+ * wkv7_gdn_bwd -- gradients of wkv7_gdn_fwd (fixed-length form) for the
+ * upstream gradients of every output and of the final state (rwkv-ops
+ * README, sections "gdn_recurrent 使用方法" and "gdn_chunk 使用方法": the
+ * training entries gated_delta_net_recurrent and gated_delta_net_chunk
+ * backpropagate; same reading of the update as wkv7_gdn_fwd).
+ *
+ *   dtype          WKV7_F32 or WKV7_BF16 for q,k,v,g,beta, d_o and the five
+ *                  input gradients.  All arithmetic is fp32.
+ *   B, T, H, K, V  as for wkv7_gdn_fwd; T >= 0.
+ *   q,k,v,g,beta   exactly the forward's inputs.  Read only.
+ *   initial_state  [n_state,H,K,V] fp32 (n_state 1: one state shared by all
+ *                  B sequences) or NULL (zeros).  Read only.
+ *   n_state        1 or B when initial_state is given; ignored otherwise.
+ *   d_o            [B,T,H,V] dtype.  Read only.
+ *   d_final_state  [B,H,K,V] fp32 or NULL (zero).  Read only.
+ *   dq, dk         [B,T,H,K] dtype; dv [B,T,H,V] dtype; dg, dbeta [B,T,H]
+ *                  dtype.  Written (every element).
+ *   d_initial_state [n_state,H,K,V] fp32 ([B,H,K,V] without initial_state:
+ *                  the gradient of the zero start) or NULL (not written).
+ *                  With a shared state it is the sum over the B sequences.
+ *   workspace      DEVICE buffer of at least wkv7_gdn_bwd_workspace_bytes(...)
+ *                  bytes, 16-byte aligned, owned by the caller; contents on
+ *                  entry are ignored and on return are unspecified.  May be
+ *                  NULL when T == 0.
+ *   stream         hipStream_t to enqueue on.
+ * Output buffers must not overlap any input or each other.  With T == 0,
+ * d_initial_state receives d_final_state (summed over B for a shared state;
+ * zeros when NULL).
+ */
+wkv7_status_t wkv7_gdn_bwd(int dtype, int B, int T, int H, int K, int V,
+                           const void *q, const void *k, const void *v,
+                           const void *g, const void *beta,
+                           const float *initial_state, int n_state,
+                           const void *d_o, const float *d_final_state,
+                           void *dq, void *dk, void *dv, void *dg, void *dbeta,
+                           float *d_initial_state, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/* Workspace bytes wkv7_gdn_bwd needs: thirteen fp32 [B,T,H,K] planes (the
+ * WKV7 operands the update maps to, and their gradients), two fp32
+ * [B,H,K,V] state sets and the workspace of wkv7_bwd at the same sizes; 0
+ * for arguments wkv7_gdn_bwd would reject. */
+size_t wkv7_gdn_bwd_workspace_bytes(int B, int T, int H, int K, int V);
+
+/*
  * wkv7_step -- one decode token per sequence, state updated in place
  * (section "rwkv7_op_rnn 使用方法": the T = 1 case of the forward).
  *
@@ -284,7 +329,8 @@ int wkv7_fwd_path(int dtype, int B, int T, int H, int K, int V, int algo);
 
 /* ABI version of this header (major * 100 + minor): 101 adds wkv7_fwd_varlen,
  * 102 adds wkv7_gdn_fwd, 103 adds wkv7_bwd and wkv7_bwd_workspace_bytes,
- * 104 adds wkv7_gdn_step, 105 adds wkv7_gdn_fwd_varlen. */
+ * 104 adds wkv7_gdn_step, 105 adds wkv7_gdn_fwd_varlen, 106 adds wkv7_gdn_bwd and
+ * wkv7_gdn_bwd_workspace_bytes. */
 int wkv7_version(void);
 
 #ifdef __cplusplus

@@ -10,7 +10,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libwkv7.so")
-SOURCES = ["wkv7_api.hip", "wkv7_recurrent.hip", "wkv7_step.hip", "wkv7_chunked.hip", "wkv7_backward.hip"]
+SOURCES = ["wkv7_api.hip", "wkv7_recurrent.hip", "wkv7_step.hip", "wkv7_chunked.hip", "wkv7_backward.hip",
+           "wkv7_gdn_bwd.hip"]
 HEADERS = ["wkv7_common.hpp", "wkv7_internal.hpp"]
 
 HIPCC_FLAGS = [

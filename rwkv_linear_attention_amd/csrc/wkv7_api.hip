@@ -40,7 +40,7 @@ int choose_path(int dtype, int T, int algo)
 
 extern "C" {
 
-int wkv7_version(void) { return 105; }
+int wkv7_version(void) { return 106; }
 
 const char *wkv7_strerror(int status)
 {
@@ -263,6 +263,52 @@ wkv7_status_t wkv7_bwd(int dtype, int B, int T, int H, int K, int V,
     wkv7::BwdArgs args{B, T, H, K, r, w, k, v, a, b, initial_state, mask, d_o, d_final_state,
                        dr, dw, dk, dv, da, db, d_initial_state, workspace};
     return wkv7::launch_backward(dtype, args, s) == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
+}
+
+size_t wkv7_gdn_bwd_workspace_bytes(int B, int T, int H, int K, int V)
+{
+    if (check_common(WKV7_F32, B, H, K, V) != WKV7_OK || T < 0) return 0;
+    return wkv7::gdn_bwd_workspace_bytes(B, T, H, K);
+}
+
+wkv7_status_t wkv7_gdn_bwd(int dtype, int B, int T, int H, int K, int V,
+                           const void *q, const void *k, const void *v,
+                           const void *g, const void *beta,
+                           const float *initial_state, int n_state,
+                           const void *d_o, const float *d_final_state,
+                           void *dq, void *dk, void *dv, void *dg, void *dbeta,
+                           float *d_initial_state, void *workspace, size_t workspace_bytes,
+                           void *stream)
+{
+    wkv7_status_t st = check_common(dtype, B, H, K, V);
+    if (st != WKV7_OK) return st;
+    if (T < 0) return WKV7_ERR_INVALID_ARG;
+    if ((long long)B * T * H * K > (1ll << 40)) return WKV7_ERR_UNSUPPORTED;
+    // launch grids of the WKV7 backward it runs: 2 B H and B H ceil(T/16) workgroups
+    if (2ll * B * H > INT32_MAX || (long long)B * H * ((T + 15) / 16) > INT32_MAX) return WKV7_ERR_UNSUPPORTED;
+    if (T > 0) {
+        const void *req[] = {q, k, v, g, beta, d_o, dq, dk, dv, dg, dbeta, workspace};
+        for (const void *p : req)
+            if (!p || !aligned16(p)) return WKV7_ERR_INVALID_ARG;
+        if (workspace_bytes < wkv7::gdn_bwd_workspace_bytes(B, T, H, K)) return WKV7_ERR_INVALID_ARG;
+    }
+    if (initial_state && n_state != 1 && n_state != B) return WKV7_ERR_INVALID_ARG;
+    const void *opt[] = {initial_state, d_final_state, d_initial_state};
+    for (const void *p : opt)
+        if (p && !aligned16(p)) return WKV7_ERR_INVALID_ARG;
+    const int rows = initial_state ? n_state : B;   // rows of d_initial_state
+
+    hipStream_t s = (hipStream_t)stream;
+    if (T == 0) {
+        if (!d_initial_state) return WKV7_OK;
+        const size_t per = (size_t)H * K * V;
+        hipError_t e = rows == B ? wkv7::launch_state_copy(d_final_state, d_initial_state, (size_t)B * per, s)
+                                 : wkv7::launch_state_sum(d_final_state, d_initial_state, B, per, s);
+        return e == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
+    }
+    wkv7::GdnBwdArgs args{B, T, H, K, q, k, v, g, beta, initial_state, rows, d_o, d_final_state,
+                          dq, dk, dv, dg, dbeta, d_initial_state, workspace};
+    return wkv7::launch_gdn_backward(dtype, args, s) == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
 }
 
 wkv7_status_t wkv7_step(int dtype, int B, int H, int K, int V,

@@ -42,6 +42,24 @@ struct BwdArgs {
 };
 size_t bwd_workspace_bytes(int B, int T, int H, int D);
 
+// Gated DeltaNet backward (fixed-length form): q, k [B,T,H,D], v and d_o
+// [B,T,H,D], g and beta [B,T,H], all in the I/O dtype; s0 [n_state,H,D,D]
+// (n_state 1 or B) or nullptr; d_sf [B,H,D,D] or nullptr; dq .. dbeta in the
+// I/O dtype; d_s0 [n_state,H,D,D] (B rows without s0) or nullptr.
+// ws: workspace of gdn_bwd_workspace_bytes(B,T,H,D) bytes.
+struct GdnBwdArgs {
+    int B, T, H, D;
+    const void *q, *k, *v, *g, *beta;
+    const float *s0;
+    int n_state;
+    const void *d_o;
+    const float *d_sf;
+    void *dq, *dk, *dv, *dg, *dbeta;
+    float *d_s0;
+    void *ws;
+};
+size_t gdn_bwd_workspace_bytes(int B, int T, int H, int D);
+
 struct StepArgs {
     int B, H, D;
     const void *r, *w, *k, *v, *a, *b;   // [B,H,D]
@@ -60,6 +78,9 @@ hipError_t launch_recurrent(int dtype, const FwdArgs &args, hipStream_t stream);
 hipError_t launch_chunked(const FwdArgs &args, hipStream_t stream);     // bf16 only
 hipError_t launch_step(int dtype, const StepArgs &args, hipStream_t stream);
 hipError_t launch_backward(int dtype, const BwdArgs &args, hipStream_t stream);
+hipError_t launch_gdn_backward(int dtype, const GdnBwdArgs &args, hipStream_t stream);
+// dst = sum of the B states of src ([B][per] floats; src == nullptr: zeros).
+hipError_t launch_state_sum(const float *src, float *dst, int B, size_t per, hipStream_t stream);
 // final_state = initial_state (or zeros) for T == 0.
 hipError_t launch_state_copy(const float *s0, float *sf, size_t n, hipStream_t stream);
 

@@ -40,6 +40,10 @@ def lib():
     L.wkv7_bwd.restype = i
     L.wkv7_bwd_workspace_bytes.argtypes = [i] * 5
     L.wkv7_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.wkv7_gdn_bwd.argtypes = [i, i, i, i, i, i] + [p] * 6 + [i] + [p] * 9 + [ctypes.c_size_t, p]
+    L.wkv7_gdn_bwd.restype = i
+    L.wkv7_gdn_bwd_workspace_bytes.argtypes = [i] * 5
+    L.wkv7_gdn_bwd_workspace_bytes.restype = ctypes.c_size_t
     L.wkv7_gdn_fwd_varlen.argtypes = [i, i, i, i, i, i, p] + [p] * 6 + [i, p, p, p, i, p]
     L.wkv7_gdn_fwd_varlen.restype = i
     L.wkv7_gdn_step.argtypes = [i, i, i, i, i] + [p] * 6 + [i, p, p, p]
@@ -262,6 +266,57 @@ def gdn_fwd(q, k, v, g, beta, initial_state=None, output_final_state=True, algo=
     if st != OK:
         raise WKV7Error(st)
     return o, sf
+
+
+def gdn_bwd_workspace_bytes(B, T, H, K, V):
+    """Bytes of device workspace gdn_bwd needs (0 if the sizes are rejected)."""
+    return int(lib().wkv7_gdn_bwd_workspace_bytes(B, T, H, K, V))
+
+
+def gdn_bwd(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None, workspace=None,
+            need_initial_state_grad=True):
+    """Gradients of gdn_fwd.  Inputs as for gdn_fwd; d_o: [B,T,H,V] in the
+    input dtype; d_final_state: [B,H,K,V] float32 or None.  workspace: a
+    uint8 device tensor of at least gdn_bwd_workspace_bytes(...) bytes, or
+    None to allocate one.  Returns a dict with q, k, v, g, beta (input dtype)
+    and s0 (float32, shaped like initial_state, [B,H,K,V] without one; None
+    when need_initial_state_grad is False)."""
+    dev = q.device
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    dt = q.dtype
+    code = _dtype_code(dt)
+    _check(k, "k", (B, T, H, K), dt, dev)
+    _check(v, "v", (B, T, H, V), dt, dev)
+    _check(g, "g", (B, T, H), dt, dev)
+    _check(beta, "beta", (B, T, H), dt, dev)
+    _check(d_o, "d_o", (B, T, H, V), dt, dev)
+    n_state = B
+    if initial_state is not None:
+        n_state = initial_state.shape[0]
+        if n_state not in (1, B):
+            raise ValueError(f"initial_state must have {B} or 1 rows, got {n_state}")
+        _check(initial_state, "initial_state", (n_state, H, K, V), torch.float32, dev)
+    if d_final_state is not None:
+        _check(d_final_state, "d_final_state", (B, H, K, V), torch.float32, dev)
+    need = gdn_bwd_workspace_bytes(B, T, H, K, V)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    elif workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
+    out = {"q": torch.empty((B, T, H, K), dtype=dt, device=dev), "k": torch.empty((B, T, H, K), dtype=dt, device=dev),
+           "v": torch.empty((B, T, H, V), dtype=dt, device=dev), "g": torch.empty((B, T, H), dtype=dt, device=dev),
+           "beta": torch.empty((B, T, H), dtype=dt, device=dev)}
+    out["s0"] = (torch.empty((n_state, H, K, V), dtype=torch.float32, device=dev)
+                 if need_initial_state_grad else None)
+    st = lib().wkv7_gdn_bwd(code, B, T, H, K, V, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                            _ptr(initial_state), n_state if initial_state is not None else 0,
+                            _ptr(d_o), _ptr(d_final_state),
+                            *(_ptr(out[n]) for n in ("q", "k", "v", "g", "beta", "s0")),
+                            _ptr(workspace), workspace.numel(), _stream(dev))
+    if st != OK:
+        raise WKV7Error(st)
+    return out
 
 
 def gdn_fwd_varlen(q, k, v, g, beta, cu_seqlens, initial_state=None, state_map=None,

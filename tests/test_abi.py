@@ -27,14 +27,14 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert {"wkv7_fwd", "wkv7_fwd_varlen", "wkv7_gdn_fwd", "wkv7_bwd", "wkv7_bwd_workspace_bytes", "wkv7_gdn_step", "wkv7_gdn_fwd_varlen", "wkv7_step", "wkv7_strerror", "wkv7_fwd_path",
+    assert {"wkv7_fwd", "wkv7_fwd_varlen", "wkv7_gdn_fwd", "wkv7_bwd", "wkv7_bwd_workspace_bytes", "wkv7_gdn_step", "wkv7_gdn_fwd_varlen", "wkv7_gdn_bwd", "wkv7_gdn_bwd_workspace_bytes", "wkv7_step", "wkv7_strerror", "wkv7_fwd_path",
             "wkv7_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"{n} declared in wkv7.h but not exported"
 
 
 def test_version_and_strerror(L):
-    assert L.wkv7_version() == 105
+    assert L.wkv7_version() == 106
     for code in range(4):
         assert len(L.wkv7_strerror(code)) > 0
     assert L.wkv7_strerror(99) == b"unknown status"
@@ -225,6 +225,56 @@ def test_bwd_rejects_null_and_misaligned(L, slot):
     assert bwd(L, ptrs=ptrs) == wkv7.ERR_INVALID_ARG
     ptrs[slot] = ODD
     assert bwd(L, ptrs=ptrs) == wkv7.ERR_INVALID_ARG
+
+
+def gdn_bwd(L, dtype=1, B=2, T=20, H=1, K=64, V=64, ptrs=None, s0=None, n_state=0, dsf=None, ds0=None,
+            ws=GOOD, ws_bytes=None):
+    ptrs = ptrs or [GOOD] * 11
+    if ws_bytes is None:
+        ws_bytes = L.wkv7_gdn_bwd_workspace_bytes(B, T, H, K, V)
+    q, k, v, g, beta, do, dq, dk, dv, dg, dbeta = ptrs
+    return L.wkv7_gdn_bwd(dtype, B, T, H, K, V, q, k, v, g, beta, s0, n_state, do, dsf,
+                          dq, dk, dv, dg, dbeta, ds0, ws, ws_bytes, None)
+
+
+def test_gdn_bwd_workspace_size(L):
+    # 13 fp32 token planes, 2 state sets, then the WKV7 backward's workspace
+    B, T, H, D = 2, 33, 3, 64
+    plane = -(-B * T * H * D * 4 // 256) * 256
+    states = -(-B * H * D * D * 4 // 256) * 256
+    assert L.wkv7_gdn_bwd_workspace_bytes(B, T, H, D, D) == 13 * plane + 2 * states + \
+        L.wkv7_bwd_workspace_bytes(B, T, H, D, D)
+    assert L.wkv7_gdn_bwd_workspace_bytes(1, 16, 1, 64, 32) == 0
+    assert L.wkv7_gdn_bwd_workspace_bytes(1, -1, 1, 64, 64) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), wkv7.ERR_INVALID_ARG),
+    (dict(B=0), wkv7.ERR_INVALID_ARG),
+    (dict(T=-1), wkv7.ERR_INVALID_ARG),
+    (dict(K=128, V=64), wkv7.ERR_UNSUPPORTED),
+    (dict(K=96, V=96), wkv7.ERR_UNSUPPORTED),
+    (dict(ws=None), wkv7.ERR_INVALID_ARG),
+    (dict(ws=ODD), wkv7.ERR_INVALID_ARG),
+    (dict(ws_bytes=1024), wkv7.ERR_INVALID_ARG),              # workspace too small
+    (dict(s0=GOOD, n_state=3), wkv7.ERR_INVALID_ARG),         # neither 1 nor B rows
+    (dict(s0=GOOD, n_state=0), wkv7.ERR_INVALID_ARG),
+    (dict(s0=ODD, n_state=2), wkv7.ERR_INVALID_ARG),
+    (dict(dsf=ODD), wkv7.ERR_INVALID_ARG),
+    (dict(ds0=ODD), wkv7.ERR_INVALID_ARG),
+    (dict(B=1 << 16, H=1 << 14, T=16), wkv7.ERR_UNSUPPORTED),     # 2 B H workgroups exceed the grid
+])
+def test_gdn_bwd_validation(L, kw, code):
+    assert gdn_bwd(L, **kw) == code
+
+
+@pytest.mark.parametrize("slot", range(11))
+def test_gdn_bwd_rejects_null_and_misaligned(L, slot):
+    ptrs = [GOOD] * 11
+    ptrs[slot] = None
+    assert gdn_bwd(L, ptrs=ptrs) == wkv7.ERR_INVALID_ARG
+    ptrs[slot] = ODD
+    assert gdn_bwd(L, ptrs=ptrs) == wkv7.ERR_INVALID_ARG
 
 
 def gdn_step(L, dtype=1, B=2, H=1, K=64, V=64, ptrs=None, s_in=None, n_state=0, s_out=GOOD):
