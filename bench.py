@@ -387,8 +387,72 @@ def bwd_workload(steps, warmup, idx, cpu=True):
     return {name: {"ms": round(ms, 4), "Mtokens_per_s": round(B * T / ms / 1e3, 3),
                    "GB_per_s": round(nbytes / ms / 1e6, 1),
                    "frac_of_8TBps": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes,
+                   "roofline": bwd_mfma_roofline(B, T, H, D, ms),
                    "workspace_bytes": ws.numel(),
                    "kernel": f"recurrences + per-chunk gradients, d{D}", "cpu_oracle": cpu_rate}}
+
+
+FP32_MFMA_PEAK_TFLOPS = 157.3
+
+
+def bwd_flops(B, T, H, D, L=16):
+    """Matrix flops of the backward in chunk form: per 16-token chunk the
+    forward chain (3 L D^2 + 4 L^2 D multiply-adds), the reverse chain
+    (3 L D^2 + 4 L^2 D) and the per-chunk gradients (7 L D^2 + 22 L^2 D)."""
+    nck = B * H * ((T + L - 1) // L)
+    return 2 * nck * (13 * L * D * D + 30 * L * L * D)
+
+
+def bwd_mfma_roofline(B, T, H, D, ms):
+    """The backward computes in fp32 on the fp32 matrix cores: its bound is
+    their dense peak, not HBM."""
+    fl = bwd_flops(B, T, H, D)
+    tf = fl / (ms * 1e-3) / 1e12
+    return {"bound": "mfma", "unit": "TFLOP/s", "peak": FP32_MFMA_PEAK_TFLOPS, "achieved": round(tf, 2),
+            "frac": round(tf / FP32_MFMA_PEAK_TFLOPS, 4), "flops": fl, "dtype": "f32",
+            "note": "chunk-form matrix flops (13 L D^2 + 30 L^2 D multiply-adds per 16-token chunk)"}
+
+
+def gdn_bwd_workload(steps, warmup, cpu=True):
+    """Gated DeltaNet backward (wkv7_gdn_bwd) at the B8 T4096 H64 d64 shape
+    (bf16, no initial state), seeded N(0, 1) output gradient rounded to
+    bf16, no final-state gradient."""
+    import numpy as np
+    import torch
+    from rwkv_linear_attention_amd import synth, wkv7
+    B, T, H, D = 8, 4096, 64, 64
+    print(f"[bench] generating Gated DeltaNet backward workload B{B} T{T} H{H} d{D}", file=sys.stderr, flush=True)
+    inp = synth.make_gdn(B, T, H, D, seed=1301)
+    names = ("q", "k", "v", "g", "beta")
+    dev = {n: synth.to_torch(inp[n], "bf16", "cuda") for n in names}
+    rng = np.random.default_rng(1501)
+    d_o_np = synth.round_to(rng.standard_normal((B, T, H, D), dtype=np.float32), "bf16")
+    d_o = synth.to_torch(d_o_np, "bf16", "cuda")
+    cpu_rate = None
+    if cpu:
+        import oracle
+
+        def call(sel):
+            g3 = lambda x: np.stack([x[bb, :, h] for bb, h in sel])[:, :, None]
+            oracle.gdn_bwd(*(g3(inp[n]) for n in names), g3(d_o_np))
+        print("[bench] timing the CPU oracle (Gated DeltaNet backward) on a sample", file=sys.stderr, flush=True)
+        cpu_rate = oracle_sample_rate(call, B, H, T)
+    del inp, d_o_np
+    ws = torch.empty(wkv7.gdn_bwd_workspace_bytes(B, T, H, D, D), dtype=torch.uint8, device="cuda")
+    ms = _time_launches(lambda i: wkv7.gdn_bwd(*(dev[n] for n in names), d_o, workspace=ws),
+                        max(3, steps // 4), max(1, warmup // 4))
+    tok, tok1 = B * T * H * D * 2, B * T * H * 2
+    # q, k, v, d_o and g, beta read once; dq, dk, dv and dg, dbeta written once;
+    # the initial-state gradient written
+    nbytes = 4 * tok + 2 * tok1 + 3 * tok + 2 * tok1 + B * H * D * D * 4
+    name = f"gdn_bwd_bf16_B{B}_T{T}_H{H}_d{D}"
+    return {name: {"ms": round(ms, 4), "Mtokens_per_s": round(B * T / ms / 1e3, 3),
+                   "GB_per_s": round(nbytes / ms / 1e6, 1),
+                   "frac_of_8TBps": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes,
+                   "roofline": bwd_mfma_roofline(B, T, H, D, ms),
+                   "workspace_bytes": ws.numel(),
+                   "kernel": "map to fp32 WKV7 operands + WKV7 backward (fp32) + chain rule, d64",
+                   "cpu_oracle": cpu_rate}}
 
 
 def _time_launches(fn, steps, warmup):
@@ -439,8 +503,8 @@ def other_workloads(steps, warmup, cpu=True):
     """Latency of the two small forward shapes, then head size 128 forward
     (B16 T4096 H32, trailing-padding mask, S0), the packed variable-length
     forward, Gated DeltaNet (B8 T4096 H64 d64), the backward on the d64 and
-    d128 shapes and the decode step (B512 H40 d64, 256 consecutive in-place
-    steps)."""
+    d128 shapes, the Gated DeltaNet backward and the decode step (B512 H40
+    d64, 256 consecutive in-place steps)."""
     import torch
     from rwkv_linear_attention_amd import synth, wkv7
     out = small_latency(steps, warmup)
@@ -470,6 +534,8 @@ def other_workloads(steps, warmup, cpu=True):
     out.update(bwd_workload(steps, warmup, 2, cpu))
     torch.cuda.empty_cache()
     out.update(bwd_workload(steps, warmup, 3, cpu))
+    torch.cuda.empty_cache()
+    out.update(gdn_bwd_workload(steps, warmup, cpu))
     torch.cuda.empty_cache()
 
     wl = synth.WORKLOADS[4]
