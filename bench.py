@@ -122,6 +122,28 @@ def oracle_sample_rate(call, B, H, T, budget_s=4.0, max_threads=16):
 SETTLE_MS = 100.0
 
 
+def copy_context(nbytes=1 << 30, reps=20):
+    """Achievable-bandwidth context: a plain device-to-device copy of 1 GiB
+    (torch's copy kernel; 2 GiB moved per copy), timed after the clock
+    settle like the workloads."""
+    import torch
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    settle(lambda: dst.copy_(src))
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"kernel": "device-to-device copy of 1 GiB (read + write)", "ms": round(ms, 4),
+            "GB_per_s": round(2 * nbytes / ms / 1e6, 1), "frac_of_8TBps": round(2 * nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
+
+
 def settle(fn, ms=SETTLE_MS):
     """Run fn (untimed) until `ms` of wall time have passed; returns the call
     count.  From idle the GPU raises its clocks over the first ~25 ms of
@@ -237,6 +259,7 @@ def main():
                      "traffic": traffic, "algorithmic_bytes": alg_bytes,
                      "kernel_ms": round(launch_ms, 5), "kernel_sha": sha},
     }
+    result["copy_context"] = copy_context()
     if not args.no_cpu:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(inp, H, T)

@@ -110,20 +110,41 @@ __device__ __forceinline__ float row_shl(float x, float fill)
                                                       0xF, false));
 }
 
-template <int D> struct alignas(16) GradLds {
-    static constexpr int LD = D + 4;    // row stride of the L x D tiles (16-byte aligned rows)
-    float R[kL][LD], B[kL][LD], A[kL][LD], K[kL][LD], V[kL][LD], DO[kL][LD];
-    float G[kL][LD];                    // decay prefix
-    float U[kL][LD], DX[kL][LD];        // X, then U; dU, then dX (exact path: raw w in U)
-    union {                             // the exact path needs no chunk matrices
-        float M[9][kL][kL + 1];         // M_ba, M_bk, M_ra, M_rk, T, dM_ra, dM_rk, dM_ba, dM_bk
-        float RED[5][D / 16][D];        // exact path: per-wave row sums
+// LDS of one chunk.  v and d_o stay in the I/O type (they are exact inputs),
+// which at bf16 and D = 64 brings the total under 40 KB: four workgroups per
+// CU.
+template <int D, typename T_IO> struct alignas(16) GradLds {
+    static constexpr int LD = D + 4;                  // fp32 tile rows (16-byte aligned)
+    static constexpr int LDV = D + 16 / sizeof(T_IO); // I/O-type tile rows (16-byte aligned)
+    float R[kL][LD], B[kL][LD], A[kL][LD], K[kL][LD];
+    T_IO V[kL][LDV], DO[kL][LDV];
+    float U[kL][LD];                    // X, then U (exact path: raw w)
+    union {
+        struct {
+            float G[kL][LD];            // decay prefix
+            float DX[kL][LD];           // dU, then dX
+            // M_ba, then T in its place; M_bk, M_ra, M_rk; after the value
+            // gradient, dM_ra, dM_rk, dM_ba, dM_bk in the same four slots
+            float M[4][kL][kL + 1];
+        };
+        float RED[5][D / 16][D];        // exact path (which needs none of the above): per-wave row sums
     };
     float EGL[D];
     int upd[kL];
 };
 
-enum { M_BA = 0, M_BK, M_RA, M_RK, M_T, DM_RA, DM_RK, DM_BA, DM_BK };
+enum { M_BA = 0, M_BK = 1, M_RA = 2, M_RK = 3, M_T = 0, DM_RA = 0, DM_RK = 1, DM_BA = 2, DM_BK = 3 };
+
+// Element (row, col) of an I/O-type LDS tile as fp32, and four consecutive
+// elements (col a multiple of 4).
+__device__ __forceinline__ float tl(const float &x) { return x; }
+__device__ __forceinline__ float tl(const uint16_t &x) { return bf16_bits_to_f32(x); }
+__device__ __forceinline__ f32x4 tl4(const float *p) { return *(const f32x4 *)p; }
+__device__ __forceinline__ f32x4 tl4(const uint16_t *p)
+{
+    const u32x2 u = *(const u32x2 *)p;
+    return f32x4{bf16_lo(u[0]), bf16_hi(u[0]), bf16_lo(u[1]), bf16_hi(u[1])};
+}
 
 // Exact path: tokens of the chunk in reverse, each step's gradients from the
 // per-token formulas (those of the oracle's derivative), with the states
@@ -131,7 +152,7 @@ enum { M_BA = 0, M_BK, M_RA, M_RK, M_T, DM_RA, DM_RK, DM_BA, DM_BK };
 // recurrent kernel: lane (j, g) of wave w holds rows [g D/4, (g+1) D/4) of
 // column 16w + j.  s.U holds the raw (masked) w.
 template <int D, typename T_IO>
-__device__ void chunk_grad_exact(GradLds<D> &s, const float *Sc, const float *dSe, int Lc, size_t tokbase,
+__device__ void chunk_grad_exact(GradLds<D, T_IO> &s, const float *Sc, const float *dSe, int Lc, size_t tokbase,
                                  int H, T_IO *dr, T_IO *dw, T_IO *dk, T_IO *dv, T_IO *da, T_IO *db)
 {
     constexpr int RPL = D / 4, NW = D / 16;
@@ -145,7 +166,7 @@ __device__ void chunk_grad_exact(GradLds<D> &s, const float *Sc, const float *dS
 #pragma unroll
         for (int i = 0; i < RPL; ++i) sb = fmaf(s.B[u][row0 + i], P[i], sb);
         sb = colsum(sb);
-        const float vj = s.V[u][col];
+        const float vj = tl(s.V[u][col]);
 #pragma unroll
         for (int i = 0; i < RPL; ++i)
             P[i] = fmaf(__expf(W[u][row0 + i]), P[i], fmaf(s.A[u][row0 + i], sb, s.K[u][row0 + i] * vj));
@@ -166,7 +187,7 @@ __device__ void chunk_grad_exact(GradLds<D> &s, const float *Sc, const float *dS
         for (int i = 0; i < RPL; ++i) P[i] = Sc[(size_t)(row0 + i) * D + col];
         for (int u = 0; u < t; ++u) step(P, u);
         const bool up = s.upd[t] != 0;
-        const float doj = s.DO[t][col], vj = s.V[t][col];
+        const float doj = tl(s.DO[t][col]), vj = tl(s.V[t][col]);
         float sb = 0.f;
 #pragma unroll
         for (int i = 0; i < RPL; ++i) sb = fmaf(s.B[t][row0 + i], P[i], sb);
@@ -241,8 +262,13 @@ __device__ __forceinline__ f32x4 mm16_rows(f32x4 acc, FA a4, FB b4, int lane)
 }
 
 // One workgroup per (b, h, chunk), D/16 waves.
+// At D = 64 with bf16 I/O, 40 000 bytes of LDS and at most 128 VGPRs hold
+// four workgroups on a CU (the whole backward at B8 T4096 H64 measured
+// 5.82 -> 5.26 ms against three).  At D = 128 the same register limit spills, and a second
+// workgroup per CU would also push the second pass over the checkpoint and
+// the end gradient out of L2 (measured slower), so that size keeps one.
 template <int D, typename T_IO>
-__global__ __launch_bounds__(D * 4) void chunk_grad_kernel(
+__global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 1))) void chunk_grad_kernel(
     int T, int H, int nck, const T_IO *__restrict__ r, const T_IO *__restrict__ w,
     const T_IO *__restrict__ k, const T_IO *__restrict__ v, const T_IO *__restrict__ a,
     const T_IO *__restrict__ b, const uint8_t *__restrict__ mask, const T_IO *__restrict__ d_o,
@@ -251,7 +277,7 @@ __global__ __launch_bounds__(D * 4) void chunk_grad_kernel(
     T_IO *__restrict__ db)
 {
     constexpr int NT = D * 4;
-    using Lds = GradLds<D>;
+    using Lds = GradLds<D, T_IO>;
     __shared__ Lds s;
     const int bh = blockIdx.x / nck, c = blockIdx.x % nck;
     const int bb = bh / H, h = bh % H;
@@ -274,12 +300,13 @@ __global__ __launch_bounds__(D * 4) void chunk_grad_kernel(
         const bool valid = t < Lc, up = s.upd[t] != 0;
         const size_t gi = tokbase + (size_t)t * H * D + c4;
         *(f32x4 *)&s.R[t][c4] = valid ? io4<T_IO>::load(r, gi) : z;
-        *(f32x4 *)&s.DO[t][c4] = valid ? io4<T_IO>::load(d_o, gi) : z;
+        using R4 = raw4<T_IO>;
+        *(typename R4::type *)&s.DO[t][c4] = valid ? R4::load(d_o, gi) : R4::zero();
         *(f32x4 *)&s.G[t][c4] = up ? io4<T_IO>::load(w, gi) : z;
         *(f32x4 *)&s.K[t][c4] = up ? io4<T_IO>::load(k, gi) : z;
         *(f32x4 *)&s.A[t][c4] = up ? io4<T_IO>::load(a, gi) : z;
         *(f32x4 *)&s.B[t][c4] = up ? io4<T_IO>::load(b, gi) : z;
-        *(f32x4 *)&s.V[t][c4] = up ? io4<T_IO>::load(v, gi) : z;
+        *(typename R4::type *)&s.V[t][c4] = up ? R4::load(v, gi) : R4::zero();
     }
     __syncthreads();
     int extreme = 0;
@@ -360,13 +387,13 @@ __global__ __launch_bounds__(D * 4) void chunk_grad_kernel(
         f32x4 X = mm16<D>(z, [&](int mm, int kk) { return s.B[mm][kk]; },
                           [&](int kk, int n) { return Sc[(size_t)kk * D + c0 + n]; }, lane);
         X = mm16<kL>(X, [&](int mm, int kk) { return s.M[M_BK][mm][kk]; },
-                     [&](int kk, int n) { return s.V[kk][c0 + n]; }, lane);
+                     [&](int kk, int n) { return tl(s.V[kk][c0 + n]); }, lane);
 #pragma unroll
         for (int i = 0; i < 4; ++i) s.U[4 * q + i][c0 + m] = X[i];
     }
     f32x4 dU = mm16<D>(z, [&](int mm, int kk) { return s.A[mm][kk]; }, dY, lane);
     dU = mm16<kL>(dU, [&](int mm, int kk) { return s.M[M_RA][kk][mm]; },
-                  [&](int kk, int n) { return s.DO[kk][c0 + n]; }, lane);
+                  [&](int kk, int n) { return tl(s.DO[kk][c0 + n]); }, lane);
 #pragma unroll
     for (int i = 0; i < 4; ++i) s.DX[4 * q + i][c0 + m] = dU[i];
     __syncthreads();
@@ -390,23 +417,34 @@ __global__ __launch_bounds__(D * 4) void chunk_grad_kernel(
         // adjacent columns
         f32x4 dVt = mm16<D>(z, [&](int mm, int kk) { return dY(kk, mm); },
                             [&](int kk, int n) { return s.K[n][kk]; }, lane);
-        dVt = mm16<kL>(dVt, [&](int mm, int kk) { return s.DO[kk][c0 + mm]; },
+        dVt = mm16<kL>(dVt, [&](int mm, int kk) { return tl(s.DO[kk][c0 + mm]); },
                        [&](int kk, int n) { return s.M[M_RK][kk][n]; }, lane);
         dVt = mm16<kL>(dVt, [&](int mm, int kk) { return s.DX[kk][c0 + mm]; },
                        [&](int kk, int n) { return s.M[M_BK][kk][n]; }, lane);
         if (m < Lc) io4<T_IO>::store(dv, tokbase + (size_t)m * H * D + c0 + 4 * q, s.upd[m] ? dVt : z);
     }
-    // --- gradients of the chunk matrices (contractions over the value columns) ---
+    // --- gradients of the chunk matrices (contractions over the value columns):
+    // wave 0 dM_ra = dO U^T, wave 1 dM_rk = dO V^T, wave 2 dM_ba = dX U^T,
+    // wave 3 dM_bk = dX V^T; stored over the chunk matrices once every wave
+    // is past the value gradient ---
+    f32x4 dmacc = z;
+    {
+        auto rowDO = [&](int mm, int j) { return tl4(&s.DO[mm][j]); };
+        auto rowDX = [&](int mm, int j) { return *(const f32x4 *)&s.DX[mm][j]; };
+        auto rowU = [&](int n, int j) { return *(const f32x4 *)&s.U[n][j]; };
+        auto rowV = [&](int n, int j) { return tl4(&s.V[n][j]); };
+        if (wave == 0) dmacc = mm16_rows<D>(z, rowDO, rowU, lane);
+        else if (wave == 1) dmacc = mm16_rows<D>(z, rowDO, rowV, lane);
+        else if (wave == 2) dmacc = mm16_rows<D>(z, rowDX, rowU, lane);
+        else if (wave == 3) dmacc = mm16_rows<D>(z, rowDX, rowV, lane);
+    }
+    __syncthreads();
     if (wave < 4) {
-        const float(*X)[Lds::LD] = wave < 2 ? s.DO : s.DX;
-        const float(*Y)[Lds::LD] = (wave & 1) ? s.V : s.U;
-        const f32x4 acc = mm16_rows<D>(z, [&](int mm, int j) { return *(const f32x4 *)&X[mm][j]; },
-                                       [&](int n, int j) { return *(const f32x4 *)&Y[n][j]; }, lane);
         const bool strict = wave >= 2;   // dM_ba, dM_bk strictly lower
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 4 * q + i;
-            s.M[DM_RA + wave][row][m] = (strict ? row > m : row >= m) ? acc[i] : 0.0f;
+            s.M[DM_RA + wave][row][m] = (strict ? row > m : row >= m) ? dmacc[i] : 0.0f;
         }
     }
     __syncthreads();
@@ -429,8 +467,8 @@ __global__ __launch_bounds__(D * 4) void chunk_grad_kernel(
             const f32x4 sr = *(const f32x4 *)(Sc + rowm + j), dr4 = *(const f32x4 *)(dSe + rowm + j);
             sds += dr4[0] * sr[0] + dr4[1] * sr[1] + dr4[2] * sr[2] + dr4[3] * sr[3];
             const f32x4 dy = dr4 * eglm;
-            const f32x4 yo = *(const f32x4 *)&s.DO[m][j], yx = *(const f32x4 *)&s.DX[m][j];
-            const f32x4 yu = *(const f32x4 *)&s.U[m][j], yv = *(const f32x4 *)&s.V[m][j];
+            const f32x4 yo = tl4(&s.DO[m][j]), yx = *(const f32x4 *)&s.DX[m][j];
+            const f32x4 yu = *(const f32x4 *)&s.U[m][j], yv = tl4(&s.V[m][j]);
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
                 dR = mfma_f32(sr[st], yo[st], dR);
