@@ -474,7 +474,7 @@ def gdn_bwd_workload(steps, warmup, cpu=True):
                    "frac_of_8TBps": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes,
                    "roofline": bwd_mfma_roofline(B, T, H, D, ms),
                    "workspace_bytes": ws.numel(),
-                   "kernel": "map to fp32 WKV7 operands + WKV7 backward (fp32) + chain rule, d64",
+                   "kernel": "recurrences + per-chunk gradients in Gated DeltaNet mode, d64",
                    "cpu_oracle": cpu_rate}}
 
 

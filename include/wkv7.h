@@ -271,10 +271,9 @@ wkv7_status_t wkv7_gdn_bwd(int dtype, int B, int T, int H, int K, int V,
                            float *d_initial_state, void *workspace, size_t workspace_bytes,
                            void *stream);
 
-/* Workspace bytes wkv7_gdn_bwd needs: thirteen fp32 [B,T,H,K] planes (the
- * WKV7 operands the update maps to, and their gradients), two fp32
- * [B,H,K,V] state sets and the workspace of wkv7_bwd at the same sizes; 0
- * for arguments wkv7_gdn_bwd would reject. */
+/* Workspace bytes wkv7_gdn_bwd needs: two fp32 [B,H,K,V] state sets (each
+ * rounded up to 256 bytes) and the workspace of wkv7_bwd at the same sizes;
+ * 0 for arguments wkv7_gdn_bwd would reject. */
 size_t wkv7_gdn_bwd_workspace_bytes(int B, int T, int H, int K, int V);
 
 /*

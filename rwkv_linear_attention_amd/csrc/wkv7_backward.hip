@@ -130,6 +130,8 @@ template <int D, typename T_IO> struct alignas(16) GradLds {
         float RED[5][D / 16][D];        // exact path (which needs none of the above): per-wave row sums
     };
     float EGL[D];
+    float gs[4][kL];                    // Gated DeltaNet: g, beta, 1/|q|, 1/|k| per token
+    float gsum[5][2];                   // Gated DeltaNet exact path: per-wave channel sums
     int upd[kL];
 };
 
@@ -146,12 +148,38 @@ __device__ __forceinline__ f32x4 tl4(const uint16_t *p)
     return f32x4{bf16_lo(u[0]), bf16_hi(u[0]), bf16_lo(u[1]), bf16_hi(u[1])};
 }
 
+// Gated DeltaNet operands.  With kn = k / sqrt(|k|^2 + 1e-6) (qn likewise),
+// the gated delta rule S = e^g (I - beta kn kn^T) S + beta kn v^T, o = S^T qn
+// (rwkv-ops README, section "gdn_recurrent 使用方法", read as the textbook rule)
+// is the generalized rule with r = qn, w = g on every channel, k = beta kn,
+// a = -e^g beta kn and b = kn.  The staging steps below form those operands
+// from q, k, g and beta, one thread per four channels of a token; the D/4
+// threads of a token are adjacent lanes of one wave.
+constexpr float kGdnNormEps = 1e-6f;
+
+template <int D>
+__device__ __forceinline__ float token_sum(float x)
+{
+#pragma unroll
+    for (int msk = 1; msk < D / 4; msk <<= 1) x += __shfl_xor(x, msk, kWave);
+    return x;
+}
+
+__device__ __forceinline__ float dot4(f32x4 a, f32x4 b) { return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3]; }
+
+// 1 / sqrt(|x|^2 + eps) over the whole token row (x: this thread's 4 channels).
+template <int D>
+__device__ __forceinline__ float inv_norm(f32x4 x)
+{
+    return 1.0f / sqrtf(token_sum<D>(dot4(x, x)) + kGdnNormEps);
+}
+
 // Exact path: tokens of the chunk in reverse, each step's gradients from the
 // per-token formulas (those of the oracle's derivative), with the states
 // S_{t-1} and S_t recomputed from the chunk's checkpoint.  Lane layout of the
 // recurrent kernel: lane (j, g) of wave w holds rows [g D/4, (g+1) D/4) of
 // column 16w + j.  s.U holds the raw (masked) w.
-template <int D, typename T_IO>
+template <int D, typename T_IO, bool GDN>
 __device__ void chunk_grad_exact(GradLds<D, T_IO> &s, const float *Sc, const float *dSe, int Lc, size_t tokbase,
                                  int H, T_IO *dr, T_IO *dw, T_IO *dk, T_IO *dv, T_IO *da, T_IO *db)
 {
@@ -220,12 +248,46 @@ __device__ void chunk_grad_exact(GradLds<D, T_IO> &s, const float *Sc, const flo
             rowsum(dS[i] * P[i], 4, row0 + i);
         }
         __syncthreads();
+        float y[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
         if (tid < D) {
-            float y[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
             for (int wv = 0; wv < NW; ++wv)
 #pragma unroll
                 for (int e = 0; e < 5; ++e) y[e] += s.RED[e][wv][tid];
-            const size_t gi = tokbase + (size_t)t * H * D + tid;
+        }
+        const size_t gi = tokbase + (size_t)t * H * D + tid;
+        if constexpr (GDN) {
+            // the generalized-rule gradients of channel tid, then the chain
+            // rule through the operands (see gdn_token_grads)
+            const float gg = s.gs[0][t], bt = s.gs[1][t], eg = __expf(gg);
+            const bool ch = tid < D;
+            const int cc = ch ? tid : 0;   // channel of this thread (threads past D contribute zeros)
+            const float gr = y[0], gk = up ? y[1] : 0.0f, ga = up ? y[2] : 0.0f, gb = up ? y[3] : 0.0f;
+            const float gw = (up && ch) ? __expf(W[t][cc]) * y[4] : 0.0f;
+            const float qn = ch ? s.R[t][cc] : 0.0f, kn = ch ? s.B[t][cc] : 0.0f;
+            const float dkn = bt * gk - eg * bt * ga + gb;
+            float pr[5] = {qn * gr, kn * dkn, kn * gk, kn * ga, gw};
+#pragma unroll
+            for (int e = 0; e < 5; ++e) {
+#pragma unroll
+                for (int msk = 1; msk < kWave; msk <<= 1) pr[e] += __shfl_xor(pr[e], msk, kWave);
+            }
+            if (lane == 0 && wave < D / kWave)
+#pragma unroll
+                for (int e = 0; e < 5; ++e) s.gsum[e][wave] = pr[e];
+            __syncthreads();
+            if (ch) {
+                float S5[5];
+#pragma unroll
+                for (int e = 0; e < 5; ++e) S5[e] = D > kWave ? s.gsum[e][0] + s.gsum[e][1] : s.gsum[e][0];
+                io<T_IO>::store(dr, gi, s.gs[2][t] * (gr - qn * S5[0]));   // dq
+                io<T_IO>::store(dk, gi, s.gs[3][t] * (dkn - kn * S5[1]));
+                if (tid == 0) {
+                    const size_t si = tokbase / D + (size_t)t * H;
+                    io<T_IO>::store(da, si, S5[2] - eg * S5[3]);             // dbeta
+                    io<T_IO>::store(dw, si, S5[4] - eg * bt * S5[3]);        // dg
+                }
+            }
+        } else if (tid < D) {
             io<T_IO>::store(dr, gi, y[0]);
             io<T_IO>::store(dk, gi, up ? y[1] : 0.0f);
             io<T_IO>::store(da, gi, up ? y[2] : 0.0f);
@@ -261,13 +323,59 @@ __device__ __forceinline__ f32x4 mm16_rows(f32x4 acc, FA a4, FB b4, int lane)
     return acc;
 }
 
+// Gated DeltaNet: the chain rule from the generalized-rule gradients of
+// token t (lane (q, m) = (channel group, token): channels ch .. ch + 3) to
+// the Gated DeltaNet inputs,
+//   dkn = beta dk - e^g beta da + db,  dqn = dr,
+//   dq = (dqn - qn (qn . dqn)) / |q|,  dk = (dkn - kn (kn . dkn)) / |k|,
+//   dbeta = kn . dk - e^g kn . da,     dg = sum_c dw_c - e^g beta kn . da
+// (|x| = sqrt(sum x^2 + 1e-6)).  The five channel sums are taken over the
+// four lanes of the token in each wave, then across the waves through LDS
+// (the dX tile, which every wave has finished with once all have passed the
+// first barrier below).  qn and kn are the raw r and b operands.
+template <int D, typename T_IO>
+__device__ __forceinline__ void gdn_token_grads(GradLds<D, T_IO> &s, int t, int ch, int Lc, size_t tokbase, int H,
+                                                f32x4 gr, f32x4 gw, f32x4 gk, f32x4 ga, f32x4 gb, f32x4 qn,
+                                                f32x4 kn, T_IO *dq, T_IO *dg, T_IO *dk, T_IO *dbeta)
+{
+    constexpr int NW = D / 16;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave, q = lane >> 4;
+    const float gg = s.gs[0][t], bt = s.gs[1][t], eg = __expf(gg);
+    const f32x4 dkn = gk * bt - ga * (eg * bt) + gb;
+    float pr[5] = {dot4(qn, gr), dot4(kn, dkn), dot4(kn, gk), dot4(kn, ga), gw[0] + gw[1] + gw[2] + gw[3]};
+#pragma unroll
+    for (int e = 0; e < 5; ++e) pr[e] = xsum32(xsum16(pr[e]));
+    __syncthreads();
+    float(*red)[NW][kL] = reinterpret_cast<float(*)[NW][kL]>(&s.DX[0][0]);
+    static_assert(sizeof(float) * 5 * NW * kL <= sizeof(s.DX), "reduction fits the dX tile");
+    if (q == 0)
+#pragma unroll
+        for (int e = 0; e < 5; ++e) red[e][wave][t] = pr[e];
+    __syncthreads();
+    float S5[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 5; ++e)
+#pragma unroll
+        for (int wv = 0; wv < NW; ++wv) S5[e] += red[e][wv][t];
+    if (t < Lc) {
+        const size_t gi = tokbase + (size_t)t * H * D + ch;
+        io4<T_IO>::store(dq, gi, (gr - qn * S5[0]) * s.gs[2][t]);
+        io4<T_IO>::store(dk, gi, (dkn - kn * S5[1]) * s.gs[3][t]);
+        if (wave == 0 && q == 0) {
+            const size_t si = tokbase / D + (size_t)t * H;
+            io<T_IO>::store(dbeta, si, S5[2] - eg * S5[3]);
+            io<T_IO>::store(dg, si, S5[4] - eg * bt * S5[3]);
+        }
+    }
+}
+
 // One workgroup per (b, h, chunk), D/16 waves.
 // At D = 64 with bf16 I/O, 40 000 bytes of LDS and at most 128 VGPRs hold
 // four workgroups on a CU (the whole backward at B8 T4096 H64 measured
 // 5.82 -> 5.26 ms against three).  At D = 128 the same register limit spills, and a second
 // workgroup per CU would also push the second pass over the checkpoint and
 // the end gradient out of L2 (measured slower), so that size keeps one.
-template <int D, typename T_IO>
+template <int D, typename T_IO, bool GDN>
 __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 1))) void chunk_grad_kernel(
     int T, int H, int nck, const T_IO *__restrict__ r, const T_IO *__restrict__ w,
     const T_IO *__restrict__ k, const T_IO *__restrict__ v, const T_IO *__restrict__ a,
@@ -292,21 +400,40 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(D == 64 ?
     // raw inputs of the chunk, four channels per thread; a token that does
     // not update gets w = k = a = b = 0 and v = 0 (an exact identity step),
     // tokens past T are all zero
-    if (tid < kL) s.upd[tid] = (tid < Lc) && (mask ? mask[(size_t)bb * T + t0 + tid] != 0 : 1);
+    if (tid < kL) s.upd[tid] = (tid < Lc) && (GDN || !mask || mask[(size_t)bb * T + t0 + tid] != 0);
     __syncthreads();
     {
         static_assert(NT == kL * D / 4, "one thread per (token, 4 channels)");
         const int t = tid / (D / 4), c4 = 4 * (tid % (D / 4));
         const bool valid = t < Lc, up = s.upd[t] != 0;
         const size_t gi = tokbase + (size_t)t * H * D + c4;
-        *(f32x4 *)&s.R[t][c4] = valid ? io4<T_IO>::load(r, gi) : z;
         using R4 = raw4<T_IO>;
         *(typename R4::type *)&s.DO[t][c4] = valid ? R4::load(d_o, gi) : R4::zero();
-        *(f32x4 *)&s.G[t][c4] = up ? io4<T_IO>::load(w, gi) : z;
-        *(f32x4 *)&s.K[t][c4] = up ? io4<T_IO>::load(k, gi) : z;
-        *(f32x4 *)&s.A[t][c4] = up ? io4<T_IO>::load(a, gi) : z;
-        *(f32x4 *)&s.B[t][c4] = up ? io4<T_IO>::load(b, gi) : z;
         *(typename R4::type *)&s.V[t][c4] = up ? R4::load(v, gi) : R4::zero();
+        if constexpr (GDN) {
+            const size_t si = tokbase / D + (size_t)t * H;
+            const f32x4 q4 = valid ? io4<T_IO>::load(r, gi) : z, k4 = valid ? io4<T_IO>::load(k, gi) : z;
+            const float gg = valid ? io<T_IO>::load(w, si) : 0.0f, bt = valid ? io<T_IO>::load(a, si) : 0.0f;
+            const float iq = inv_norm<D>(q4), ik = inv_norm<D>(k4);
+            const f32x4 kn = k4 * ik;
+            *(f32x4 *)&s.R[t][c4] = q4 * iq;
+            *(f32x4 *)&s.G[t][c4] = f32x4{gg, gg, gg, gg};
+            *(f32x4 *)&s.K[t][c4] = kn * bt;
+            *(f32x4 *)&s.A[t][c4] = kn * (-__expf(gg) * bt);
+            *(f32x4 *)&s.B[t][c4] = kn;
+            if (c4 == 0) {
+                s.gs[0][t] = gg;
+                s.gs[1][t] = bt;
+                s.gs[2][t] = iq;
+                s.gs[3][t] = ik;
+            }
+        } else {
+            *(f32x4 *)&s.R[t][c4] = valid ? io4<T_IO>::load(r, gi) : z;
+            *(f32x4 *)&s.G[t][c4] = up ? io4<T_IO>::load(w, gi) : z;
+            *(f32x4 *)&s.K[t][c4] = up ? io4<T_IO>::load(k, gi) : z;
+            *(f32x4 *)&s.A[t][c4] = up ? io4<T_IO>::load(a, gi) : z;
+            *(f32x4 *)&s.B[t][c4] = up ? io4<T_IO>::load(b, gi) : z;
+        }
     }
     __syncthreads();
     int extreme = 0;
@@ -329,10 +456,15 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(D == 64 ?
         {
             const int t = tid / (D / 4), c4 = 4 * (tid % (D / 4));
             const size_t gi = tokbase + (size_t)t * H * D + c4;
-            *(f32x4 *)&s.U[t][c4] = s.upd[t] ? io4<T_IO>::load(w, gi) : z;
+            if constexpr (GDN) {
+                const float gg = s.gs[0][t];
+                *(f32x4 *)&s.U[t][c4] = s.upd[t] ? f32x4{gg, gg, gg, gg} : z;
+            } else {
+                *(f32x4 *)&s.U[t][c4] = s.upd[t] ? io4<T_IO>::load(w, gi) : z;
+            }
         }
         __syncthreads();
-        chunk_grad_exact<D, T_IO>(s, Sc, dSe, Lc, tokbase, H, dr, dw, dk, dv, da, db);
+        chunk_grad_exact<D, T_IO, GDN>(s, Sc, dSe, Lc, tokbase, H, dr, dw, dk, dv, da, db);
         return;
     }
     {
@@ -513,7 +645,7 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(D == 64 ?
     const f32x4 Gp = t ? *(const f32x4 *)&s.G[t - 1][ch] : z;
     const f32x4 Rs = *(const f32x4 *)&s.R[t][ch], Bs = *(const f32x4 *)&s.B[t][ch];
     const f32x4 As = *(const f32x4 *)&s.A[t][ch], Ks = *(const f32x4 *)&s.K[t][ch];
-    f32x4 gr, gb, ga, gk, gw;
+    f32x4 gr, gb, ga, gk, gw, rraw, braw;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const float eG = __expf(G[i]), enG = __expf(-G[i]), eGp = __expf(Gp[i]);
@@ -523,6 +655,8 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(D == 64 ?
         gk[i] = dK[i] * enG;
         // raw (masked) operands are the scaled ones times the inverse factors
         const float rr = Rs[i] * enG, kk = Ks[i] * eG, aa = As[i] * eG, bv = Bs[i] * __expf(-Gp[i]);
+        rraw[i] = rr;
+        braw[i] = bv;
         const float p = gr[i] * rr - ga[i] * aa - gk[i] * kk;
         const float qb = gb[i] * bv;
         // dG_t = p_t + qb_{t+1} (+ the chunk-end term at t = 15), then the
@@ -534,7 +668,9 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(D == 64 ?
         y += row_shl<8>(y, 0.0f);
         gw[i] = y;
     }
-    if (t < Lc) {
+    if constexpr (GDN) {
+        gdn_token_grads<D, T_IO>(s, t, ch, Lc, tokbase, H, gr, gw, gk, ga, gb, rraw, braw, dr, dw, dk, da);
+    } else if (t < Lc) {
         const bool up = s.upd[t] != 0;
         const size_t gi = tokbase + (size_t)t * H * D + ch;
         io4<T_IO>::store(dr, gi, gr);
@@ -597,7 +733,7 @@ __device__ __forceinline__ void store_slice(float *dst, const f32x4 *St, int q, 
 // At D = 64, at most 128 VGPRs (four waves per SIMD): the 2 B H workgroups
 // of the benchmark shape then all fit on the machine at once, with no tail
 // round.  (At D = 128 the same limit spills, and measured slower.)
-template <int D, typename T_IO>
+template <int D, typename T_IO, bool GDN>
 __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 1))) void chain_kernel(
     int T, int H, int nbh, const T_IO *__restrict__ r, const T_IO *__restrict__ w,
     const T_IO *__restrict__ k, const T_IO *__restrict__ v, const T_IO *__restrict__ a,
@@ -632,34 +768,61 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(D == 64 ?
     using R4 = raw4<T_IO>;
     typename R4::type pf[5];
     int pm = 0;
+    float pg = 0.0f, pb = 0.0f;   // Gated DeltaNet: g and beta of the token
     const T_IO *const x_src = fwd ? k : r, *const y_src = fwd ? v : d_o;
     auto fetch = [&](int c) {
         const int t0 = c * kL, nt = min(kL, T - t0);
         const bool valid = tp < nt;
-        const bool up = valid && (mask ? mask[tok0 + t0 + tp] != 0 : 1);
         const size_t gi = ((tok0 + t0 + tp) * H + h) * D + cp;
-        pf[0] = up ? R4::load(w, gi) : R4::zero();
-        pf[1] = up ? R4::load(a, gi) : R4::zero();
-        pf[2] = up ? R4::load(b, gi) : R4::zero();
-        // forward: k and v only where the token updates; backward: r and d_o
-        // at every valid token (a masked token still reads the state)
-        const bool xy = fwd ? up : valid;
-        pf[3] = xy ? R4::load(x_src, gi) : R4::zero();
-        pf[4] = xy ? R4::load(y_src, gi) : R4::zero();
-        pm = up;
+        if constexpr (GDN) {
+            // k, then v (forward) or d_o, then q (backward); every token updates
+            const size_t si = (tok0 + t0 + tp) * H + h;
+            pf[0] = valid ? R4::load(k, gi) : R4::zero();
+            pf[1] = valid ? R4::load(y_src, gi) : R4::zero();
+            pf[2] = (valid && !fwd) ? R4::load(r, gi) : R4::zero();
+            pg = valid ? io<T_IO>::load(w, si) : 0.0f;
+            pb = valid ? io<T_IO>::load(a, si) : 0.0f;
+            pm = valid;
+        } else {
+            const bool up = valid && (mask ? mask[tok0 + t0 + tp] != 0 : 1);
+            pf[0] = up ? R4::load(w, gi) : R4::zero();
+            pf[1] = up ? R4::load(a, gi) : R4::zero();
+            pf[2] = up ? R4::load(b, gi) : R4::zero();
+            // forward: k and v only where the token updates; backward: r and d_o
+            // at every valid token (a masked token still reads the state)
+            const bool xy = fwd ? up : valid;
+            pf[3] = xy ? R4::load(x_src, gi) : R4::zero();
+            pf[4] = xy ? R4::load(y_src, gi) : R4::zero();
+            pm = up;
+        }
     };
     if (nck > 0) fetch(fwd ? 0 : nck - 1);
     for (int it = 0; it < nck; ++it) {
         const int c = fwd ? it : nck - 1 - it;
         const int Lc = min(kL, T - c * kL);
         store_slice<D>((fwd ? ckpt : dck) + ((size_t)bh * nck + c) * D * D, St, q, m, c0);
-        __syncthreads();
-        *(f32x4 *)&s.W[tp][cp] = R4::f32(pf[0]);
-        *(f32x4 *)&s.G[tp][cp] = R4::f32(pf[0]);
-        *(f32x4 *)&s.A[tp][cp] = R4::f32(pf[1]);
-        *(f32x4 *)&s.B[tp][cp] = R4::f32(pf[2]);
-        *(f32x4 *)&s.X[tp][cp] = R4::f32(pf[3]);
-        *(f32x4 *)&s.Y[tp][cp] = R4::f32(pf[4]);
+        if constexpr (GDN) {
+            const f32x4 k4 = R4::f32(pf[0]);
+            const f32x4 kn = k4 * inv_norm<D>(k4);
+            const f32x4 q4 = R4::f32(pf[2]);
+            const float iq = inv_norm<D>(q4);   // unused in the forward role (q4 = 0 there)
+            __syncthreads();
+            const f32x4 g4 = {pg, pg, pg, pg};
+            *(f32x4 *)&s.W[tp][cp] = g4;
+            *(f32x4 *)&s.G[tp][cp] = g4;
+            *(f32x4 *)&s.A[tp][cp] = kn * (-__expf(pg) * pb);
+            *(f32x4 *)&s.B[tp][cp] = kn;
+            *(f32x4 *)&s.X[tp][cp] = fwd ? kn * pb : q4 * iq;
+            *(f32x4 *)&s.Y[tp][cp] = R4::f32(pf[1]);
+        } else {
+            __syncthreads();
+            *(f32x4 *)&s.W[tp][cp] = R4::f32(pf[0]);
+            *(f32x4 *)&s.G[tp][cp] = R4::f32(pf[0]);
+            *(f32x4 *)&s.A[tp][cp] = R4::f32(pf[1]);
+            *(f32x4 *)&s.B[tp][cp] = R4::f32(pf[2]);
+            *(f32x4 *)&s.X[tp][cp] = R4::f32(pf[3]);
+            *(f32x4 *)&s.Y[tp][cp] = R4::f32(pf[4]);
+        }
         if (cp == 0) s.upd[tp] = pm;
         __syncthreads();
         if (it + 1 < nck) fetch(fwd ? c + 1 : c - 1);
@@ -831,20 +994,20 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(D == 64 ?
     if (!fwd && d_s0) store_slice<D>(d_s0 + st, St, q, m, c0);
 }
 
-template <int D, typename T_IO>
+template <int D, typename T_IO, bool GDN>
 hipError_t launch_bwd_d(const BwdArgs &p, hipStream_t stream)
 {
     const int nck = (p.T + kL - 1) / kL;
     const size_t nbh = (size_t)p.B * p.H;
     float *ckpt = (float *)p.ws;
     float *dck = ckpt + nbh * nck * D * D;
-    hipLaunchKernelGGL((chain_kernel<D, T_IO>), dim3((unsigned)(2 * nbh)), dim3(D * 4), 0, stream, p.T,
+    hipLaunchKernelGGL((chain_kernel<D, T_IO, GDN>), dim3((unsigned)(2 * nbh)), dim3(D * 4), 0, stream, p.T,
                        p.H, (int)nbh, (const T_IO *)p.r, (const T_IO *)p.w, (const T_IO *)p.k,
                        (const T_IO *)p.v, (const T_IO *)p.a, (const T_IO *)p.b, p.s0, p.mask,
                        (const T_IO *)p.d_o, p.d_sf, ckpt, dck, p.d_s0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((chunk_grad_kernel<D, T_IO>), dim3((unsigned)(nbh * nck)), dim3(D * 4), 0, stream, p.T,
+    hipLaunchKernelGGL((chunk_grad_kernel<D, T_IO, GDN>), dim3((unsigned)(nbh * nck)), dim3(D * 4), 0, stream, p.T,
                        p.H, nck, (const T_IO *)p.r, (const T_IO *)p.w, (const T_IO *)p.k, (const T_IO *)p.v,
                        (const T_IO *)p.a, (const T_IO *)p.b, p.mask, (const T_IO *)p.d_o, ckpt, dck,
                        (T_IO *)p.dr, (T_IO *)p.dw, (T_IO *)p.dk, (T_IO *)p.dv, (T_IO *)p.da, (T_IO *)p.db);
@@ -859,10 +1022,17 @@ size_t bwd_workspace_bytes(int B, int T, int H, int D)
     return sizeof(float) * (size_t)B * H * D * D * 2 * nck;
 }
 
+template <bool GDN>
+hipError_t launch_bwd_g(int dtype, const BwdArgs &p, hipStream_t stream)
+{
+    if (p.D == 64)
+        return dtype == 0 ? launch_bwd_d<64, float, GDN>(p, stream) : launch_bwd_d<64, uint16_t, GDN>(p, stream);
+    return dtype == 0 ? launch_bwd_d<128, float, GDN>(p, stream) : launch_bwd_d<128, uint16_t, GDN>(p, stream);
+}
+
 hipError_t launch_backward(int dtype, const BwdArgs &p, hipStream_t stream)
 {
-    if (p.D == 64) return dtype == 0 ? launch_bwd_d<64, float>(p, stream) : launch_bwd_d<64, uint16_t>(p, stream);
-    return dtype == 0 ? launch_bwd_d<128, float>(p, stream) : launch_bwd_d<128, uint16_t>(p, stream);
+    return p.gdn ? launch_bwd_g<true>(dtype, p, stream) : launch_bwd_g<false>(dtype, p, stream);
 }
 
 }  // namespace wkv7

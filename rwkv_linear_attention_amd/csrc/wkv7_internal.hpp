@@ -39,6 +39,9 @@ struct BwdArgs {
     void *dr, *dw, *dk, *dv, *da, *db;
     float *d_s0;
     void *ws;
+    // Gated DeltaNet: r = q, w = g and a = beta ([B,T,H]), b and mask unused;
+    // dr = dq, dw = dg and da = dbeta ([B,T,H]), db unused.
+    bool gdn = false;
 };
 size_t bwd_workspace_bytes(int B, int T, int H, int D);
 

@@ -238,12 +238,11 @@ def gdn_bwd(L, dtype=1, B=2, T=20, H=1, K=64, V=64, ptrs=None, s0=None, n_state=
 
 
 def test_gdn_bwd_workspace_size(L):
-    # 13 fp32 token planes, 2 state sets, then the WKV7 backward's workspace
+    # two state sets (a shared initial state expanded, and its per-sequence
+    # gradients), then the WKV7 backward's workspace
     B, T, H, D = 2, 33, 3, 64
-    plane = -(-B * T * H * D * 4 // 256) * 256
     states = -(-B * H * D * D * 4 // 256) * 256
-    assert L.wkv7_gdn_bwd_workspace_bytes(B, T, H, D, D) == 13 * plane + 2 * states + \
-        L.wkv7_bwd_workspace_bytes(B, T, H, D, D)
+    assert L.wkv7_gdn_bwd_workspace_bytes(B, T, H, D, D) == 2 * states + L.wkv7_bwd_workspace_bytes(B, T, H, D, D)
     assert L.wkv7_gdn_bwd_workspace_bytes(1, 16, 1, 64, 32) == 0
     assert L.wkv7_gdn_bwd_workspace_bytes(1, -1, 1, 64, 64) == 0
 
