@@ -38,6 +38,12 @@
 // takes an exact token-by-token path instead (the split factors e^{-G} would
 // leave the fp32 range).  All arithmetic is fp32: the products run on the
 // fp32 matrix cores (v_mfma_f32_16x16x4_f32) over LDS tiles.
+//
+// Both launches also have a Gated DeltaNet mode (template flag GDN), used by
+// wkv7_gdn_bwd: they form the generalized-rule operands of the gated delta
+// rule from q, k, g and beta while staging each chunk, and the per-chunk
+// launch applies the chain rule back to q, k, g and beta when it stores the
+// token gradients (gdn_token_grads).
 #include "wkv7_common.hpp"
 #include "wkv7_internal.hpp"
 
