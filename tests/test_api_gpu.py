@@ -1,0 +1,92 @@
+"""GPU checks of the rwkv-ops-shaped entry points (api.py) against the fp64
+oracle: gradients through torch.autograd equal the oracle's backward (tolerances
+of tests/test_bwd_gpu.py), the inference twins return the same outputs
+without a graph, and the one-token forms equal one step of the oracle."""
+import numpy as np
+import pytest
+
+import harness as hz
+import oracle
+import rwkv_linear_attention_amd as m
+from rwkv_linear_attention_amd import synth
+from test_bwd_gpu import check_grad
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+NAMES = ("r", "w", "k", "v", "a", "b")
+GNAMES = ("q", "k", "v", "g", "beta")
+
+
+def leaf(x, dt):
+    return synth.to_torch(x, dt, "cuda").requires_grad_(True)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_generalized_delta_rule_autograd(dtype):
+    B, T, H, D = 2, 70, 2, 64
+    inp = synth.make(1, B=B, T=T, H=H, K=D, seed=8100, init=True, mask="bernoulli")
+    for n in NAMES:
+        inp[n] = synth.round_to(inp[n], dtype)
+    rng = np.random.default_rng(8101)
+    d_o = synth.round_to(rng.standard_normal((B, T, H, D)).astype(np.float32), dtype)
+    d_sf = (rng.standard_normal((B, H, D, D)) * 0.5).astype(np.float32)
+    x = {n: leaf(inp[n], dtype) for n in NAMES}
+    s0 = torch.from_numpy(inp["s0"]).cuda().requires_grad_(True)
+    mask = torch.from_numpy(inp["mask"]).cuda()
+    o, sf = m.generalized_delta_rule(*(x[n] for n in NAMES), initial_state=s0, mask=mask)
+    loss = (o.float() * synth.to_torch(d_o, "f32", "cuda")).sum() + (sf * torch.from_numpy(d_sf).cuda()).sum()
+    loss.backward()
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.fwd(*(inp[n] for n in NAMES), inp["s0"], inp["mask"])
+    hz.check(dtype, hz.to_np(o), o_ref, hz.to_np(sf), s_ref, what=f"api gdr {dtype} o")
+    ref = oracle.bwd(*(inp[n] for n in NAMES), d_o, inp["s0"], inp["mask"], d_sf)
+    for n in NAMES:
+        check_grad(dtype, hz.to_np(x[n].grad), ref[n], f"api gdr {dtype} d{n}")
+    check_grad("f32", hz.to_np(s0.grad), ref["s0"], f"api gdr {dtype} ds0")
+    # the gradient-free twin: same outputs, no graph
+    o2, sf2 = m.generalized_delta_rule_inference(*(x[n] for n in NAMES), initial_state=s0, mask=mask)
+    assert not o2.requires_grad
+    np.testing.assert_array_equal(hz.to_np(o2), hz.to_np(o))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_gated_delta_net_autograd_shared_state(dtype):
+    B, T, H, D = 3, 48, 2, 64
+    gi = synth.make_gdn(B, T, H, D, seed=8200, dtype=dtype, init=True, n_state=1)
+    rng = np.random.default_rng(8201)
+    d_o = synth.round_to(rng.standard_normal((B, T, H, D)).astype(np.float32), dtype)
+    x = {n: leaf(gi[n], dtype) for n in GNAMES}
+    s0 = torch.from_numpy(gi["s0"]).cuda().requires_grad_(True)
+    o, sf = m.gated_delta_net_chunk(*(x[n] for n in GNAMES), initial_state=s0)
+    (o.float() * synth.to_torch(d_o, "f32", "cuda")).sum().backward()
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.gdn_fwd(*(gi[n] for n in GNAMES), gi["s0"])
+    hz.check(dtype, hz.to_np(o), o_ref, hz.to_np(sf), s_ref, what=f"api gdn {dtype} o")
+    ref = oracle.gdn_bwd(*(gi[n] for n in GNAMES), d_o, gi["s0"])
+    for n in GNAMES:
+        check_grad(dtype, hz.to_np(x[n].grad), ref[n], f"api gdn {dtype} d{n}")
+    assert s0.grad.shape == (1, H, D, D)
+    check_grad("f32", hz.to_np(s0.grad), ref["s0"], f"api gdn {dtype} ds0")
+
+
+def test_one_token_forms():
+    B, H, D = 3, 2, 64
+    inp = synth.make(1, B=B, T=1, H=H, K=D, seed=8300, init=True, mask="none")
+    x = {n: synth.to_torch(inp[n], "bf16", "cuda") for n in NAMES}
+    s0 = torch.from_numpy(inp["s0"]).cuda()
+    keep = s0.clone()
+    o, nxt = m.rwkv7_op_rnn(*(x[n] for n in NAMES), initial_state=s0)
+    torch.cuda.synchronize()
+    assert o.shape == (B, 1, H, D)
+    assert torch.equal(s0, keep), "the initial state must not be modified"
+    o_ref, s_ref = oracle.step(*(inp[n][:, 0] for n in NAMES), inp["s0"])
+    hz.check("bf16", hz.to_np(o)[:, 0], o_ref, hz.to_np(nxt), s_ref, what="api rwkv7_op_rnn")
+
+    gi = synth.make_gdn(B, 1, H, D, seed=8301, init=True, n_state=1)
+    g1 = {n: synth.to_torch(gi[n][:, 0], "bf16", "cuda") for n in GNAMES}
+    gs0 = torch.from_numpy(gi["s0"]).cuda()
+    o, nxt = m.gated_delta_net_recurrent_single_step(*(g1[n] for n in GNAMES), initial_state=gs0)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.gdn_fwd(*(gi[n] for n in GNAMES), gi["s0"])
+    hz.check("bf16", hz.to_np(o), o_ref[:, 0], hz.to_np(nxt), s_ref, what="api gdn single step")
