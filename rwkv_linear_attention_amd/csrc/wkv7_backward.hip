@@ -163,11 +163,26 @@ __device__ __forceinline__ f32x4 tl4(const uint16_t *p)
 // threads of a token are adjacent lanes of one wave.
 constexpr float kGdnNormEps = 1e-6f;
 
+// Sum over the D/4 lanes of a token with DPP (no LDS traffic): swap lane
+// pairs, then pairs of pairs, then mirror within each 8- and 16-lane half
+// (row_half_mirror, row_mirror); at D = 128 also add the neighbouring 16-lane
+// row.  Each step adds two partial sums in either order, so every lane of the
+// token ends with the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
 template <int D>
 __device__ __forceinline__ float token_sum(float x)
 {
-#pragma unroll
-    for (int msk = 1; msk < D / 4; msk <<= 1) x += __shfl_xor(x, msk, kWave);
+    static_assert(D == 64 || D == 128, "a token spans 16 or 32 lanes");
+    x += dpp_mov<0xB1>(x);    // quad_perm [1,0,3,2]
+    x += dpp_mov<0x4E>(x);    // quad_perm [2,3,0,1]
+    x += dpp_mov<0x141>(x);   // row_half_mirror
+    x += dpp_mov<0x140>(x);   // row_mirror
+    if constexpr (D == 128) x = xsum16(x);
     return x;
 }
 
