@@ -494,7 +494,7 @@ def _time_launches(fn, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
-def small_latency(steps, warmup):
+def small_latency(steps, warmup, cpu=True):
     """Launch latency of the two small forward shapes (B1 T64 H1 d64 fp32;
     B2 T1024 H4 d64 bf16 with initial state and mask), which hold too few
     sequences to fill the GPU: reported as time per call under AUTO."""
@@ -518,6 +518,18 @@ def small_latency(steps, warmup):
         out[wl["name"]] = {"us_per_call": round(ms * 1e3, 2), "Mtokens_per_s": round(B * T / ms / 1e3, 3),
                            "kernel": "chunked" if path == wkv7.ALGO_CHUNKED else "recurrent",
                            "note": "latency only: too few sequences to fill the GPU"}
+        if cpu:
+            import oracle
+            oracle.set_threads(min(16, len(os.sched_getaffinity(0))))
+            t0 = time.perf_counter()
+            n = 0
+            while time.perf_counter() - t0 < 0.5:
+                oracle.fwd(*(inp[x] for x in ("r", "w", "k", "v", "a", "b")), inp["s0"], inp["mask"])
+                n += 1
+            dt = (time.perf_counter() - t0) / n
+            out[wl["name"]]["cpu_oracle"] = {"us_per_call": round(dt * 1e6, 1), "kind": "oracle",
+                                             "cores": min(16, len(os.sched_getaffinity(0))),
+                                             "sample": f"the whole workload, {n} calls"}
         del dev, s0, mask, o, sf, inp
     return out
 
@@ -530,7 +542,7 @@ def other_workloads(steps, warmup, cpu=True):
     d64, 256 consecutive in-place steps)."""
     import torch
     from rwkv_linear_attention_amd import synth, wkv7
-    out = small_latency(steps, warmup)
+    out = small_latency(steps, warmup, cpu)
     wl = synth.WORKLOADS[3]
     B, T, H, D = wl["B"], wl["T"], wl["H"], wl["K"]
     print(f"[bench] generating workload {wl['name']}", file=sys.stderr, flush=True)
@@ -547,6 +559,17 @@ def other_workloads(steps, warmup, cpu=True):
     out[wl["name"]] = {"ms": round(ms, 5), "Mtokens_per_s": round(B * T / ms / 1e3, 3),
                        "GB_per_s": round(nbytes / ms / 1e6, 1), "frac_of_8TBps": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
                        "algorithmic_bytes": nbytes, "kernel": "chunked d128"}
+    if cpu:
+        import numpy as np
+        import oracle
+
+        def call(sel):
+            g = lambda x: np.stack([x[bb, :, h] for bb, h in sel])[:, :, None, :]
+            s0s = np.stack([inp["s0"][bb, h] for bb, h in sel])[:, None]
+            ms_ = np.stack([inp["mask"][bb] for bb, h in sel])
+            oracle.fwd(*(g(inp[n]) for n in ("r", "w", "k", "v", "a", "b")), s0s, ms_)
+        print("[bench] timing the CPU oracle (head size 128) on a sample", file=sys.stderr, flush=True)
+        out[wl["name"]]["cpu_oracle"] = oracle_sample_rate(call, B, H, T)
     del dev, s0, mask, o, sf, inp
     torch.cuda.empty_cache()
 
@@ -595,6 +618,19 @@ def other_workloads(steps, warmup, cpu=True):
                        "frac_of_8TBps": round(step_bytes * NSTEP / ms_total / 1e6 / HBM_PEAK_GBS, 4),
                        "bytes_per_step": step_bytes, "kernel": "step d64",
                        "note": "inputs of 32 distinct steps cycled; state reset outside the timed region"}
+    if cpu:
+        import oracle
+        threads = min(16, len(os.sched_getaffinity(0)))
+        oracle.set_threads(threads)
+        sl = lambda n, t: inp[n][:, t]
+        t0 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t0 < 2.0:
+            oracle.step(*(sl(x, n % 32) for x in ("r", "w", "k", "v", "a", "b")), inp["s0"])
+            n += 1
+        dt = (time.perf_counter() - t0) / n
+        out[wl["name"]]["cpu_oracle"] = {"us_per_step": round(dt * 1e6, 1), "kind": "oracle", "cores": threads,
+                                         "sample": f"{n} whole steps (all B*H sequences)"}
     del per_step, state, state0, obuf
     torch.cuda.empty_cache()
 
