@@ -233,6 +233,51 @@ wkv7_status_t wkv7_bwd(int dtype, int B, int T, int H, int K, int V,
 size_t wkv7_bwd_workspace_bytes(int B, int T, int H, int K, int V);
 
 /*
+ * wkv7_bwd_varlen -- gradients of wkv7_fwd_varlen (N packed sequences; the
+ * pages' trainable generalized_delta_rule takes an initial state with N
+ * rows, one per sequence, and only its head-first layout excludes variable
+ * lengths: rwkv-ops README, section "rwkv7op 使用方法").  Sequence n gets
+ * exactly the gradients wkv7_bwd gives for that one sequence.
+ *
+ *   dtype, N, total_T, H, K, V, cu_seqlens, r,w,k,v,a,b, initial_state,
+ *   n_state, state_map, mask
+ *                  as for wkv7_fwd_varlen.  Read only.
+ *   d_o            [total_T,H,V] dtype.  Read only.
+ *   d_final_state  [N,H,K,V] fp32 or NULL (zero).  Read only.
+ *   dr,dw,dk,da,db [total_T,H,K] dtype; dv [total_T,H,V] dtype.  Written at
+ *                  every token of every sequence; tokens outside all
+ *                  sequences are not written.
+ *   d_initial_state [N,H,K,V] fp32 or NULL: row n is the gradient of the
+ *                  state sequence n started from (the gradient of a pool row
+ *                  is the sum of the rows of the sequences mapped to it,
+ *                  which is left to the caller).  Written.
+ *   workspace      DEVICE buffer of at least
+ *                  wkv7_bwd_varlen_workspace_bytes(N,total_T,H,K,V) bytes,
+ *                  16-byte aligned, owned by the caller; contents on entry
+ *                  are ignored, on return unspecified.  May be NULL when
+ *                  total_T == 0.
+ *   stream         hipStream_t to enqueue on.
+ * Malformed offsets give wrong results but never an out-of-bounds access
+ * (they are clamped as in wkv7_fwd_varlen, and the checkpoint storage is
+ * bounded).  Output buffers must not overlap any input or each other.
+ */
+wkv7_status_t wkv7_bwd_varlen(int dtype, int N, int total_T, int H, int K, int V,
+                              const int32_t *cu_seqlens,
+                              const void *r, const void *w, const void *k,
+                              const void *v, const void *a, const void *b,
+                              const float *initial_state, int n_state, const int32_t *state_map,
+                              const uint8_t *mask, const void *d_o, const float *d_final_state,
+                              void *dr, void *dw, void *dk, void *dv, void *da, void *db,
+                              float *d_initial_state, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/* Workspace bytes wkv7_bwd_varlen needs: two fp32 K x V states per head for
+ * each of ceil(total_T/16) + N chunks (a bound on the sequences' chunk
+ * count), then N + 1 int32 chunk offsets; 0 for arguments wkv7_bwd_varlen
+ * would reject. */
+size_t wkv7_bwd_varlen_workspace_bytes(int N, int total_T, int H, int K, int V);
+
+/*
  * wkv7_gdn_bwd -- gradients of wkv7_gdn_fwd (fixed-length form) for the
  * upstream gradients of every output and of the final state (rwkv-ops
  * README, sections "gdn_recurrent 使用方法" and "gdn_chunk 使用方法": the
@@ -329,7 +374,8 @@ int wkv7_fwd_path(int dtype, int B, int T, int H, int K, int V, int algo);
 /* ABI version of this header (major * 100 + minor): 101 adds wkv7_fwd_varlen,
  * 102 adds wkv7_gdn_fwd, 103 adds wkv7_bwd and wkv7_bwd_workspace_bytes,
  * 104 adds wkv7_gdn_step, 105 adds wkv7_gdn_fwd_varlen, 106 adds wkv7_gdn_bwd and
- * wkv7_gdn_bwd_workspace_bytes. */
+ * wkv7_gdn_bwd_workspace_bytes, 107 adds wkv7_bwd_varlen and
+ * wkv7_bwd_varlen_workspace_bytes. */
 int wkv7_version(void);
 
 #ifdef __cplusplus

@@ -53,6 +53,26 @@ namespace {
 constexpr int kL = 16;                  // chunk length (= checkpoint interval)
 constexpr float kMinChunkLogDecay = -60.0f;
 
+// Packed sequences (cu == nullptr: the fixed-length form).  Sequence n owns
+// tokens [cu[n], cu[n+1]) of the total_T-token axis, each offset clamped into
+// range as the forward does; its checkpoints are chunks ck_off[n] ..
+// ck_off[n+1] - 1 of the workspace (ck_off saturates at the capacity, so
+// malformed offsets give wrong results, never an access out of bounds).
+struct SeqGeom {
+    const int32_t *cu = nullptr;
+    const int32_t *ck_off = nullptr;
+    const int32_t *smap = nullptr;
+    int n_state = 0;
+    int nseq = 0;
+    int total_T = 0;
+};
+
+__device__ __forceinline__ void seq_range(const SeqGeom &vg, int n, int &tb, int &te)
+{
+    tb = min(max(vg.cu[n], 0), vg.total_T);
+    te = min(max(vg.cu[n + 1], tb), vg.total_T);
+}
+
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -403,17 +423,46 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(D == 64 ?
     const T_IO *__restrict__ b, const uint8_t *__restrict__ mask, const T_IO *__restrict__ d_o,
     const float *__restrict__ ckpt, const float *__restrict__ dck, T_IO *__restrict__ dr,
     T_IO *__restrict__ dw, T_IO *__restrict__ dk, T_IO *__restrict__ dv, T_IO *__restrict__ da,
-    T_IO *__restrict__ db)
+    T_IO *__restrict__ db, SeqGeom vg)
 {
     constexpr int NT = D * 4;
     using Lds = GradLds<D, T_IO>;
     __shared__ Lds s;
-    const int bh = blockIdx.x / nck, c = blockIdx.x % nck;
-    const int bb = bh / H, h = bh % H;
-    const int t0 = c * kL, Lc = min(kL, T - t0);
-    const size_t tokbase = (((size_t)bb * T + t0) * H + h) * D;   // element of (token t0, channel 0)
-    const float *Sc = ckpt + ((size_t)bh * nck + c) * D * D;
-    const float *dSe = dck + ((size_t)bh * nck + c) * D * D;
+    // chunk c of sequence n, head h; tokens from tok0 (packed: the sequence's
+    // first token; fixed-length: n T), checkpoint index ckid
+    int n, h, c, Tn;
+    size_t tok0, ckid;
+    if (vg.cu) {
+        const int gc = (int)(blockIdx.x / H);
+        h = (int)(blockIdx.x % H);
+        if (gc >= vg.ck_off[vg.nseq]) return;   // the whole workgroup, before any barrier
+        // the sequence owning global chunk gc: the last n with ck_off[n] <= gc
+        int lo = 0, hi = vg.nseq;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (vg.ck_off[mid] <= gc) lo = mid;
+            else hi = mid;
+        }
+        n = lo;
+        c = gc - vg.ck_off[n];
+        int tb, te;
+        seq_range(vg, n, tb, te);
+        tok0 = (size_t)tb;
+        Tn = te - tb;
+        ckid = (size_t)gc * H + h;
+    } else {
+        const int bh0 = (int)(blockIdx.x / nck);
+        c = (int)(blockIdx.x % nck);
+        n = bh0 / H;
+        h = bh0 % H;
+        tok0 = (size_t)n * T;
+        Tn = T;
+        ckid = (size_t)bh0 * nck + c;
+    }
+    const int t0 = c * kL, Lc = min(kL, Tn - t0);
+    const size_t tokbase = ((tok0 + t0) * H + h) * D;   // element of (token t0, channel 0)
+    const float *Sc = ckpt + ckid * D * D;
+    const float *dSe = dck + ckid * D * D;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int q = lane >> 4, m = lane & 15;
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
@@ -421,7 +470,7 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(D == 64 ?
     // raw inputs of the chunk, four channels per thread; a token that does
     // not update gets w = k = a = b = 0 and v = 0 (an exact identity step),
     // tokens past T are all zero
-    if (tid < kL) s.upd[tid] = (tid < Lc) && (GDN || !mask || mask[(size_t)bb * T + t0 + tid] != 0);
+    if (tid < kL) s.upd[tid] = (tid < Lc) && (GDN || !mask || mask[tok0 + t0 + tid] != 0);
     __syncthreads();
     {
         static_assert(NT == kL * D / 4, "one thread per (token, 4 channels)");
@@ -760,29 +809,52 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(D == 64 ?
     const T_IO *__restrict__ k, const T_IO *__restrict__ v, const T_IO *__restrict__ a,
     const T_IO *__restrict__ b, const float *__restrict__ s0, const uint8_t *__restrict__ mask,
     const T_IO *__restrict__ d_o, const float *__restrict__ d_sf, float *__restrict__ ckpt,
-    float *__restrict__ dck, float *__restrict__ d_s0)
+    float *__restrict__ dck, float *__restrict__ d_s0, SeqGeom vg)
 {
     constexpr int NTILE = D / 16;
     using Lds = ChainLds<D>;
     __shared__ Lds s;
     const bool fwd = (int)blockIdx.x < nbh;
     const int bh = fwd ? (int)blockIdx.x : (int)blockIdx.x - nbh;
-    const int bb = bh / H, h = bh % H;
-    const size_t tok0 = (size_t)bb * T;
+    const int bb = bh / H, h = bh % H;   // sequence, head
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int q = lane >> 4, m = lane & 15, c0 = 16 * wave;
-    const int nck = (T + kL - 1) / kL;
-    const size_t st = (size_t)bh * D * D;
+    const size_t st = (size_t)bh * D * D;   // this (sequence, head) in [B,H,D,D] arrays
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    // tokens tok0 .. tok0 + T - 1; chunk c's checkpoints at index ckidx(c),
+    // stored for c < nck_store (fewer than the chunks only for malformed
+    // packed offsets); initial state s0p (nullptr: zeros)
+    size_t tok0, ck0;
+    int nck_store;
+    const float *s0p = nullptr;
+    if (vg.cu) {
+        int tb, te;
+        seq_range(vg, bb, tb, te);
+        tok0 = (size_t)tb;
+        T = te - tb;
+        ck0 = (size_t)vg.ck_off[bb];
+        nck_store = vg.ck_off[bb + 1] - vg.ck_off[bb];
+        if (s0) {
+            const int srow = vg.smap ? vg.smap[bb] : bb;
+            if (srow >= 0 && srow < vg.n_state) s0p = s0 + ((size_t)srow * H + h) * D * D;
+        }
+    } else {
+        tok0 = (size_t)bb * T;
+        ck0 = (size_t)bh * ((T + kL - 1) / kL);
+        nck_store = (T + kL - 1) / kL;
+        if (s0) s0p = s0 + st;
+    }
+    const int nck = (T + kL - 1) / kL;
+    auto ckidx = [&](int c) { return vg.cu ? (ck0 + c) * H + h : ck0 + c; };
 
     f32x4 St[NTILE];
     {
-        const float *init = fwd ? s0 : d_sf;
+        const float *init = fwd ? s0p : (d_sf ? d_sf + st : nullptr);
 #pragma unroll
         for (int ti = 0; ti < NTILE; ++ti)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                St[ti][i] = init ? init[st + (size_t)(16 * ti + 4 * q + i) * D + c0 + m] : 0.0f;
+                St[ti][i] = init ? init[(size_t)(16 * ti + 4 * q + i) * D + c0 + m] : 0.0f;
     }
     // one thread per (token tp, channels cp .. cp + 3) of a chunk's tiles
     const int tp = tid / (D / 4), cp = 4 * (tid % (D / 4));
@@ -821,7 +893,7 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(D == 64 ?
     for (int it = 0; it < nck; ++it) {
         const int c = fwd ? it : nck - 1 - it;
         const int Lc = min(kL, T - c * kL);
-        store_slice<D>((fwd ? ckpt : dck) + ((size_t)bh * nck + c) * D * D, St, q, m, c0);
+        if (c < nck_store) store_slice<D>((fwd ? ckpt : dck) + ckidx(c) * D * D, St, q, m, c0);
         if constexpr (GDN) {
             const f32x4 k4 = R4::f32(pf[0]);
             const f32x4 kn = k4 * inv_norm<D>(k4);
@@ -1015,23 +1087,78 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(D == 64 ?
     if (!fwd && d_s0) store_slice<D>(d_s0 + st, St, q, m, c0);
 }
 
+// ck_off[0..nseq]: exclusive prefix sums of the sequences' chunk counts
+// (offsets clamped as in seq_range), saturating at cap.  One workgroup
+// scanning 256 sequences at a time.
+__global__ __launch_bounds__(256) void chunk_offsets_kernel(const int32_t *__restrict__ cu, int nseq, int total_T,
+                                                            long long cap, int32_t *__restrict__ ck_off)
+{
+    __shared__ long long part[256];
+    long long carry = 0;
+    SeqGeom vg;
+    vg.cu = cu;
+    vg.total_T = total_T;
+    for (int base = 0; base < nseq; base += 256) {
+        const int n = base + (int)threadIdx.x;
+        long long cnt = 0;
+        if (n < nseq) {
+            int tb, te;
+            seq_range(vg, n, tb, te);
+            cnt = (te - tb + kL - 1) / kL;
+        }
+        part[threadIdx.x] = cnt;
+        __syncthreads();
+        for (int off = 1; off < 256; off <<= 1) {
+            const long long add = threadIdx.x >= (unsigned)off ? part[threadIdx.x - off] : 0;
+            __syncthreads();
+            part[threadIdx.x] += add;
+            __syncthreads();
+        }
+        if (n < nseq) ck_off[n + 1] = (int32_t)min(carry + part[threadIdx.x], cap);
+        carry += part[255];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) ck_off[0] = 0;
+}
+
 template <int D, typename T_IO, bool GDN>
 hipError_t launch_bwd_d(const BwdArgs &p, hipStream_t stream)
 {
-    const int nck = (p.T + kL - 1) / kL;
     const size_t nbh = (size_t)p.B * p.H;
+    SeqGeom vg;
+    size_t nck, grid2;
+    if (p.cu_seqlens) {
+        // packed: checkpoints [capacity][H], then the chunk offsets
+        const long long cap = bwd_varlen_chunk_capacity(p.B, p.T);
+        nck = (size_t)cap;
+        int32_t *ck_off = (int32_t *)((char *)p.ws + sizeof(float) * (size_t)cap * p.H * D * D * 2);
+        hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(256), 0, stream, p.cu_seqlens, p.B, p.T, cap, ck_off);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        vg.cu = p.cu_seqlens;
+        vg.ck_off = ck_off;
+        vg.smap = p.state_map;
+        vg.n_state = p.n_state;
+        vg.nseq = p.B;
+        vg.total_T = p.T;
+        grid2 = (size_t)cap * p.H;
+    } else {
+        nck = (size_t)(p.T + kL - 1) / kL;
+        grid2 = nbh * nck;
+    }
     float *ckpt = (float *)p.ws;
-    float *dck = ckpt + nbh * nck * D * D;
+    float *dck = ckpt + (p.cu_seqlens ? nck * p.H : nbh * nck) * D * D;
     hipLaunchKernelGGL((chain_kernel<D, T_IO, GDN>), dim3((unsigned)(2 * nbh)), dim3(D * 4), 0, stream, p.T,
                        p.H, (int)nbh, (const T_IO *)p.r, (const T_IO *)p.w, (const T_IO *)p.k,
                        (const T_IO *)p.v, (const T_IO *)p.a, (const T_IO *)p.b, p.s0, p.mask,
-                       (const T_IO *)p.d_o, p.d_sf, ckpt, dck, p.d_s0);
+                       (const T_IO *)p.d_o, p.d_sf, ckpt, dck, p.d_s0, vg);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((chunk_grad_kernel<D, T_IO, GDN>), dim3((unsigned)(nbh * nck)), dim3(D * 4), 0, stream, p.T,
-                       p.H, nck, (const T_IO *)p.r, (const T_IO *)p.w, (const T_IO *)p.k, (const T_IO *)p.v,
+    if (grid2 == 0) return hipSuccess;
+    hipLaunchKernelGGL((chunk_grad_kernel<D, T_IO, GDN>), dim3((unsigned)grid2), dim3(D * 4), 0, stream, p.T,
+                       p.H, (int)nck, (const T_IO *)p.r, (const T_IO *)p.w, (const T_IO *)p.k, (const T_IO *)p.v,
                        (const T_IO *)p.a, (const T_IO *)p.b, p.mask, (const T_IO *)p.d_o, ckpt, dck,
-                       (T_IO *)p.dr, (T_IO *)p.dw, (T_IO *)p.dk, (T_IO *)p.dv, (T_IO *)p.da, (T_IO *)p.db);
+                       (T_IO *)p.dr, (T_IO *)p.dw, (T_IO *)p.dk, (T_IO *)p.dv, (T_IO *)p.da, (T_IO *)p.db, vg);
     return hipGetLastError();
 }
 
@@ -1041,6 +1168,17 @@ size_t bwd_workspace_bytes(int B, int T, int H, int D)
 {
     const size_t nck = ((size_t)T + kL - 1) / kL;
     return sizeof(float) * (size_t)B * H * D * D * 2 * nck;
+}
+
+long long bwd_varlen_chunk_capacity(int B, int T)
+{
+    return ((long long)T + kL - 1) / kL + B;
+}
+
+size_t bwd_varlen_workspace_bytes(int B, int T, int H, int D)
+{
+    const size_t cap = (size_t)bwd_varlen_chunk_capacity(B, T);
+    return sizeof(float) * cap * H * D * D * 2 + sizeof(int32_t) * ((size_t)B + 1);
 }
 
 template <bool GDN>

@@ -42,8 +42,21 @@ struct BwdArgs {
     // Gated DeltaNet: r = q, w = g and a = beta ([B,T,H]), b and mask unused;
     // dr = dq, dw = dg and da = dbeta ([B,T,H]), db unused.
     bool gdn = false;
+    // Packed form: B sequences with token ranges [cu_seqlens[n],
+    // cu_seqlens[n+1]) of a [T,H,D] token axis (T = total tokens), initial
+    // state row state_map[n] of an [n_state,H,D,D] pool (state_map ==
+    // nullptr: row n); d_sf and d_s0 are [B,H,D,D] (per sequence).  ws:
+    // bwd_varlen_workspace_bytes(B,T,H,D) bytes.
+    const int32_t *cu_seqlens = nullptr;
+    const int32_t *state_map = nullptr;
+    int n_state = 0;
 };
 size_t bwd_workspace_bytes(int B, int T, int H, int D);
+// Packed form: chunk capacity ceil(T/16) + B (an upper bound on the sum of
+// the sequences' chunk counts), two fp32 states per chunk and head, then the
+// per-sequence chunk offsets.
+long long bwd_varlen_chunk_capacity(int B, int T);
+size_t bwd_varlen_workspace_bytes(int B, int T, int H, int D);
 
 // Gated DeltaNet backward (fixed-length form): q, k [B,T,H,D], v and d_o
 // [B,T,H,D], g and beta [B,T,H], all in the I/O dtype; s0 [n_state,H,D,D]

@@ -40,6 +40,10 @@ def lib():
     L.wkv7_bwd.restype = i
     L.wkv7_bwd_workspace_bytes.argtypes = [i] * 5
     L.wkv7_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.wkv7_bwd_varlen.argtypes = [i] * 6 + [p] * 7 + [p, i, p, p, p, p] + [p] * 8 + [ctypes.c_size_t, p]
+    L.wkv7_bwd_varlen.restype = i
+    L.wkv7_bwd_varlen_workspace_bytes.argtypes = [i] * 5
+    L.wkv7_bwd_varlen_workspace_bytes.restype = ctypes.c_size_t
     L.wkv7_gdn_bwd.argtypes = [i, i, i, i, i, i] + [p] * 6 + [i] + [p] * 9 + [ctypes.c_size_t, p]
     L.wkv7_gdn_bwd.restype = i
     L.wkv7_gdn_bwd_workspace_bytes.argtypes = [i] * 5
@@ -231,6 +235,68 @@ def bwd(r, w, k, v, a, b, d_o, initial_state=None, mask=None, d_final_state=None
                         _ptr(workspace), workspace.numel(), _stream(dev))
     if st != OK:
         raise WKV7Error(st)
+    return g
+
+
+def bwd_varlen_workspace_bytes(N, total_T, H, K, V):
+    """Bytes of device workspace bwd_varlen needs (0 if the sizes are rejected)."""
+    return int(lib().wkv7_bwd_varlen_workspace_bytes(N, total_T, H, K, V))
+
+
+def bwd_varlen(r, w, k, v, a, b, cu_seqlens, d_o, initial_state=None, state_map=None, mask=None,
+               d_final_state=None, workspace=None, need_initial_state_grad=True):
+    """Gradients of fwd_varlen.  Inputs as for fwd_varlen ([T_total,H,K] or
+    [1,T_total,H,K]); d_o shaped like v; d_final_state: [N,H,K,V] float32 or
+    None.  Returns a dict with r, w, k, v, a, b (shaped like the inputs;
+    tokens outside every sequence are left as allocated) and s0 ([N,H,K,V]
+    float32: the gradient of each sequence's initial state, or None)."""
+    dev = r.device
+    lead1 = r.dim() == 4
+    if lead1:
+        if r.shape[0] != 1:
+            raise ValueError("packed inputs take a leading dimension of 1, or none")
+        r, w, k, v, a, b, d_o = (t.squeeze(0) for t in (r, w, k, v, a, b, d_o))
+    TT, H, K = r.shape
+    V = v.shape[-1]
+    dt = r.dtype
+    code = _dtype_code(dt)
+    for name, t in (("r", r), ("w", w), ("k", k), ("a", a), ("b", b)):
+        _check(t, name, (TT, H, K), dt, dev)
+    _check(v, "v", (TT, H, V), dt, dev)
+    _check(d_o, "d_o", (TT, H, V), dt, dev)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be [N+1] with N >= 1")
+    N = cu_seqlens.numel() - 1
+    _check(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    n_state = 0
+    if initial_state is not None:
+        n_state = initial_state.shape[0]
+        _check(initial_state, "initial_state", (n_state, H, K, V), torch.float32, dev)
+    if state_map is not None:
+        _check(state_map, "state_map", (N,), torch.int32, dev)
+    if d_final_state is not None:
+        _check(d_final_state, "d_final_state", (N, H, K, V), torch.float32, dev)
+    m = _mask_u8(mask)
+    if m is not None:
+        _check(m, "mask", (TT,), torch.uint8, dev)
+    need = bwd_varlen_workspace_bytes(N, TT, H, K, V)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    elif workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
+    g = {n: torch.empty((TT, H, K), dtype=dt, device=dev) for n in ("r", "w", "k", "a", "b")}
+    g["v"] = torch.empty((TT, H, V), dtype=dt, device=dev)
+    g["s0"] = torch.empty((N, H, K, V), dtype=torch.float32, device=dev) if need_initial_state_grad else None
+    st = lib().wkv7_bwd_varlen(code, N, TT, H, K, V, _ptr(cu_seqlens), _ptr(r), _ptr(w), _ptr(k), _ptr(v),
+                               _ptr(a), _ptr(b), _ptr(initial_state), n_state, _ptr(state_map), _ptr(m),
+                               _ptr(d_o), _ptr(d_final_state),
+                               *(_ptr(g[n]) for n in ("r", "w", "k", "v", "a", "b", "s0")),
+                               _ptr(workspace), workspace.numel(), _stream(dev))
+    if st != OK:
+        raise WKV7Error(st)
+    if lead1:
+        for n in ("r", "w", "k", "v", "a", "b"):
+            g[n] = g[n].unsqueeze(0)
     return g
 
 

@@ -27,14 +27,14 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert {"wkv7_fwd", "wkv7_fwd_varlen", "wkv7_gdn_fwd", "wkv7_bwd", "wkv7_bwd_workspace_bytes", "wkv7_gdn_step", "wkv7_gdn_fwd_varlen", "wkv7_gdn_bwd", "wkv7_gdn_bwd_workspace_bytes", "wkv7_step", "wkv7_strerror", "wkv7_fwd_path",
+    assert {"wkv7_fwd", "wkv7_fwd_varlen", "wkv7_gdn_fwd", "wkv7_bwd", "wkv7_bwd_workspace_bytes", "wkv7_gdn_step", "wkv7_gdn_fwd_varlen", "wkv7_gdn_bwd", "wkv7_gdn_bwd_workspace_bytes", "wkv7_bwd_varlen", "wkv7_bwd_varlen_workspace_bytes", "wkv7_step", "wkv7_strerror", "wkv7_fwd_path",
             "wkv7_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"{n} declared in wkv7.h but not exported"
 
 
 def test_version_and_strerror(L):
-    assert L.wkv7_version() == 106
+    assert L.wkv7_version() == 107
     for code in range(4):
         assert len(L.wkv7_strerror(code)) > 0
     assert L.wkv7_strerror(99) == b"unknown status"
@@ -274,6 +274,54 @@ def test_gdn_bwd_rejects_null_and_misaligned(L, slot):
     assert gdn_bwd(L, ptrs=ptrs) == wkv7.ERR_INVALID_ARG
     ptrs[slot] = ODD
     assert gdn_bwd(L, ptrs=ptrs) == wkv7.ERR_INVALID_ARG
+
+
+def bwd_varlen(L, dtype=1, N=3, TT=50, H=1, K=64, V=64, cu=GOOD, ptrs=None, s0=None, n_state=0, smap=None,
+               mask=None, dsf=None, ds0=None, ws=GOOD, ws_bytes=None):
+    ptrs = ptrs or [GOOD] * 13
+    if ws_bytes is None:
+        ws_bytes = L.wkv7_bwd_varlen_workspace_bytes(N, TT, H, K, V)
+    r, w, k, v, a, b, do, dr, dw, dk, dv, da, db = ptrs
+    return L.wkv7_bwd_varlen(dtype, N, TT, H, K, V, cu, r, w, k, v, a, b, s0, n_state, smap, mask, do, dsf,
+                             dr, dw, dk, dv, da, db, ds0, ws, ws_bytes, None)
+
+
+def test_bwd_varlen_workspace_size(L):
+    # two fp32 states per head for ceil(total_T / 16) + N chunks, then N + 1 offsets
+    assert L.wkv7_bwd_varlen_workspace_bytes(3, 100, 2, 64, 64) == 4 * (7 + 3) * 2 * 64 * 64 * 2 + 4 * 4
+    assert L.wkv7_bwd_varlen_workspace_bytes(1, 0, 1, 128, 128) == 4 * 1 * 128 * 128 * 2 + 8
+    assert L.wkv7_bwd_varlen_workspace_bytes(1, 16, 1, 64, 32) == 0
+    assert L.wkv7_bwd_varlen_workspace_bytes(0, 16, 1, 64, 64) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), wkv7.ERR_INVALID_ARG),
+    (dict(N=0), wkv7.ERR_INVALID_ARG),
+    (dict(TT=-1), wkv7.ERR_INVALID_ARG),
+    (dict(K=64, V=128), wkv7.ERR_UNSUPPORTED),
+    (dict(cu=None), wkv7.ERR_INVALID_ARG),
+    (dict(cu=P(0x100002)), wkv7.ERR_INVALID_ARG),            # cu_seqlens not 4-byte aligned
+    (dict(ws=None), wkv7.ERR_INVALID_ARG),
+    (dict(ws_bytes=1024), wkv7.ERR_INVALID_ARG),              # workspace too small
+    (dict(s0=GOOD, n_state=0), wkv7.ERR_INVALID_ARG),
+    (dict(s0=GOOD, n_state=2), wkv7.ERR_INVALID_ARG),         # no map: one row per sequence needed
+    (dict(s0=ODD, n_state=3), wkv7.ERR_INVALID_ARG),
+    (dict(smap=P(0x100002)), wkv7.ERR_INVALID_ARG),
+    (dict(dsf=ODD), wkv7.ERR_INVALID_ARG),
+    (dict(ds0=ODD), wkv7.ERR_INVALID_ARG),
+    (dict(N=1 << 16, H=1 << 14, TT=16), wkv7.ERR_UNSUPPORTED),    # 2 N H workgroups exceed the grid
+])
+def test_bwd_varlen_validation(L, kw, code):
+    assert bwd_varlen(L, **kw) == code
+
+
+@pytest.mark.parametrize("slot", range(13))
+def test_bwd_varlen_rejects_null_and_misaligned(L, slot):
+    ptrs = [GOOD] * 13
+    ptrs[slot] = None
+    assert bwd_varlen(L, ptrs=ptrs) == wkv7.ERR_INVALID_ARG
+    ptrs[slot] = ODD
+    assert bwd_varlen(L, ptrs=ptrs) == wkv7.ERR_INVALID_ARG
 
 
 def gdn_step(L, dtype=1, B=2, H=1, K=64, V=64, ptrs=None, s_in=None, n_state=0, s_out=GOOD):
