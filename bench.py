@@ -306,7 +306,8 @@ def varlen_lengths(total, n, seed):
 def varlen_workload(steps, warmup):
     """Packed variable-length forward: the 32768 tokens x 64 heads (d64) of
     the B8 T4096 workload as 32 sequences of mixed lengths, each starting from
-    one of 8 pooled initial states (state_map), final states written."""
+    one of 8 pooled initial states (state_map), final states written; then
+    the backward of the same packed forward."""
     import numpy as np
     import torch
     from rwkv_linear_attention_amd import synth, wkv7
@@ -328,10 +329,30 @@ def varlen_workload(steps, warmup):
     # inputs and o once, one mapped initial state read and one final state written per sequence
     nbytes = 7 * TT * H * D * 2 + 2 * N * H * D * D * 4
     name = f"fwd_varlen_bf16_N{N}_T{TT}_H{H}_d{D}_statemap8"
-    return {name: {"ms": round(ms, 5), "Mtokens_per_s": round(TT / ms / 1e3, 3),
-                   "GB_per_s": round(nbytes / ms / 1e6, 1),
-                   "frac_of_8TBps": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes,
-                   "lengths": [int(x) for x in lens], "kernel": "chunked d64 (packed)"}}
+    res = {name: {"ms": round(ms, 5), "Mtokens_per_s": round(TT / ms / 1e3, 3),
+                  "GB_per_s": round(nbytes / ms / 1e6, 1),
+                  "frac_of_8TBps": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes,
+                  "lengths": [int(x) for x in lens], "kernel": "chunked d64 (packed)"}}
+    del o, sf
+    # the backward of the same packed forward (seeded N(0, 1) output gradient)
+    d_o = synth.to_torch(synth.round_to(rng.standard_normal((TT, H, D), dtype=np.float32), "bf16"), "bf16", "cuda")
+    ws = torch.empty(wkv7.bwd_varlen_workspace_bytes(N, TT, H, D, D), dtype=torch.uint8, device="cuda")
+    ms = _time_launches(lambda i: wkv7.bwd_varlen(*(dev[n] for n in ("r", "w", "k", "v", "a", "b")), cu, d_o,
+                                                  initial_state=pool, state_map=smap, workspace=ws),
+                        max(3, steps // 4), max(1, warmup // 4))
+    tok = TT * H * D * 2
+    nbytes = 7 * tok + 6 * tok + 2 * N * H * D * D * 4
+    # the packed chunks: sum of ceil(len / 16), the flop count of bwd_flops
+    nck = int(sum((int(x) + 15) // 16 for x in lens))
+    fl = 2 * nck * H * (13 * 16 * D * D + 30 * 16 * 16 * D)
+    tf = fl / (ms * 1e-3) / 1e12
+    res[f"bwd_varlen_bf16_N{N}_T{TT}_H{H}_d{D}_statemap8"] = {
+        "ms": round(ms, 4), "Mtokens_per_s": round(TT / ms / 1e3, 3), "GB_per_s": round(nbytes / ms / 1e6, 1),
+        "frac_of_8TBps": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes,
+        "roofline": {"bound": "mfma", "unit": "TFLOP/s", "peak": FP32_MFMA_PEAK_TFLOPS, "achieved": round(tf, 2),
+                     "frac": round(tf / FP32_MFMA_PEAK_TFLOPS, 4), "flops": fl, "dtype": "f32"},
+        "workspace_bytes": ws.numel(), "kernel": "recurrences + per-chunk gradients, d64 (packed)"}
+    return res
 
 
 def gdn_workload(steps, warmup, cpu=True):
