@@ -51,17 +51,63 @@ class _GeneralizedDeltaRule(torch.autograd.Function):
         return g["r"], g["w"], g["k"], g["v"], g["a"], g["b"], g["s0"], None
 
 
+class _GeneralizedDeltaRulePacked(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, r, w, k, v, a, b, initial_state, cu_seqlens, state_map, mask):
+        o, sf = wkv7.fwd_varlen(r, w, k, v, a, b, cu_seqlens, initial_state=initial_state, state_map=state_map,
+                                mask=mask, output_final_state=True)
+        ctx.save_for_backward(r, w, k, v, a, b, initial_state, cu_seqlens, state_map, mask)
+        ctx.s0_grad = initial_state is not None and initial_state.requires_grad
+        return o, sf
+
+    @staticmethod
+    def backward(ctx, d_o, d_sf):
+        r, w, k, v, a, b, s0, cu, smap, mask = ctx.saved_tensors
+        if d_o is None:
+            d_o = torch.zeros_like(v)
+        g = wkv7.bwd_varlen(r, w, k, v, a, b, cu, d_o.contiguous(), initial_state=s0, state_map=smap, mask=mask,
+                            d_final_state=None if d_sf is None else d_sf.contiguous(),
+                            need_initial_state_grad=ctx.s0_grad)
+        ds0 = None
+        if ctx.s0_grad:
+            if smap is None:
+                ds0 = g["s0"]
+            else:
+                # pool rows: the sum over the sequences mapped to each row
+                # (a sequence whose entry is outside the pool started from zeros)
+                ok = (smap >= 0) & (smap < s0.shape[0])
+                ds0 = torch.zeros_like(s0).index_add_(0, smap[ok].long(), g["s0"][ok])
+        return g["r"], g["w"], g["k"], g["v"], g["a"], g["b"], ds0, None, None, None
+
+
 def generalized_delta_rule(r, w, k, v, a, b, initial_state=None, output_final_state=True, head_first=False,
-                           mask=None):
+                           mask=None, cu_seqlens=None, state_map=None):
     """WKV7 generalized delta rule with gradients.  r, w, k, a, b: [B,T,H,K];
     v: [B,T,H,V] (float32 or bfloat16); initial_state: [B,H,K,V] float32 or
     None; mask: [B,T] (nonzero = update) or None.  Returns (o, final_state or
-    None); gradients flow to r, w, k, v, a, b and initial_state."""
+    None); gradients flow to r, w, k, v, a, b and initial_state.
+
+    Packed sequences: with cu_seqlens (int32 [N+1] token offsets) the inputs
+    are [1,T,H,K] (N sequences back to back), mask is [T] or [1,T],
+    initial_state is [N,H,K,V] or, with state_map (int32 [N]), a pool of
+    rows; final_state is [N,H,K,V]."""
     _head_first(head_first)
     _require_device([("r", r), ("w", w), ("k", k), ("v", v), ("a", a), ("b", b),
-                     ("initial_state", initial_state), ("mask", mask)])
+                     ("initial_state", initial_state), ("mask", mask), ("cu_seqlens", cu_seqlens),
+                     ("state_map", state_map)])
     tensors = (r, w, k, v, a, b) + (() if initial_state is None else (initial_state,))
-    if torch.is_grad_enabled() and any(t.requires_grad for t in tensors):
+    grad = torch.is_grad_enabled() and any(t.requires_grad for t in tensors)
+    if cu_seqlens is not None:
+        if mask is not None and mask.dim() == 2:
+            mask = mask.reshape(-1)
+        if grad:
+            o, sf = _GeneralizedDeltaRulePacked.apply(r, w, k, v, a, b, initial_state, cu_seqlens, state_map, mask)
+        else:
+            o, sf = wkv7.fwd_varlen(r, w, k, v, a, b, cu_seqlens, initial_state=initial_state,
+                                    state_map=state_map, mask=mask, output_final_state=True)
+    elif state_map is not None:
+        raise ValueError("state_map needs cu_seqlens (packed sequences)")
+    elif grad:
         o, sf = _GeneralizedDeltaRule.apply(r, w, k, v, a, b, initial_state, mask)
     else:
         o, sf = wkv7.fwd(r, w, k, v, a, b, initial_state=initial_state, mask=mask, output_final_state=True)
@@ -107,10 +153,11 @@ rwkv7_op = generalized_delta_rule
 
 
 def generalized_delta_rule_inference(r, w, k, v, a, b, initial_state=None, output_final_state=True,
-                                     head_first=False, mask=None):
+                                     head_first=False, mask=None, cu_seqlens=None, state_map=None):
     """generalized_delta_rule without gradients."""
     with torch.no_grad():
-        return generalized_delta_rule(r, w, k, v, a, b, initial_state, output_final_state, head_first, mask)
+        return generalized_delta_rule(r, w, k, v, a, b, initial_state, output_final_state, head_first, mask,
+                                      cu_seqlens, state_map)
 
 
 def rwkv7_op_rnn(r, w, k, v, a, b, initial_state=None, output_final_state=True, head_first=False):

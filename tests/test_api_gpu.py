@@ -90,3 +90,43 @@ def test_one_token_forms():
     torch.cuda.synchronize()
     o_ref, s_ref = oracle.gdn_fwd(*(gi[n] for n in GNAMES), gi["s0"])
     hz.check("bf16", hz.to_np(o), o_ref[:, 0], hz.to_np(nxt), s_ref, what="api gdn single step")
+
+
+def test_generalized_delta_rule_packed_autograd():
+    """Packed sequences through autograd: the pool's gradient is the sum of
+    the oracle's per-sequence initial-state gradients over the sequences
+    mapped to each row (an entry outside the pool means a zero start)."""
+    lengths, H, D = [20, 0, 37, 16], 2, 64
+    TT = sum(lengths)
+    inp = synth.make(1, B=1, T=TT, H=H, K=D, seed=8400, init=False, mask="bernoulli")
+    rng = np.random.default_rng(8401)
+    pool_np = (rng.standard_normal((3, H, D, D)) * 0.1).astype(np.float32)
+    smap_np = np.array([2, 0, 2, 7], np.int32)
+    d_o = synth.round_to(rng.standard_normal((1, TT, H, D)).astype(np.float32), "bf16")
+    d_sf = (rng.standard_normal((len(lengths), H, D, D)) * 0.5).astype(np.float32)
+    cu_np = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    x = {n: leaf(inp[n], "bf16") for n in NAMES}
+    pool = torch.from_numpy(pool_np).cuda().requires_grad_(True)
+    o, sf = m.generalized_delta_rule(*(x[n] for n in NAMES), initial_state=pool,
+                                     mask=torch.from_numpy(inp["mask"]).cuda(),
+                                     cu_seqlens=torch.from_numpy(cu_np).cuda(),
+                                     state_map=torch.from_numpy(smap_np).cuda())
+    loss = (o.float() * synth.to_torch(d_o, "f32", "cuda")).sum() + (sf * torch.from_numpy(d_sf).cuda()).sum()
+    loss.backward()
+    torch.cuda.synchronize()
+    ds0_pool = np.zeros_like(pool_np, dtype=np.float64)
+    for n in range(len(lengths)):
+        tb, te = int(cu_np[n]), int(cu_np[n + 1])
+        row = int(smap_np[n])
+        s0 = pool_np[row][None] if 0 <= row < 3 else None
+        sl = {k: inp[k][:, tb:te] for k in NAMES}
+        msk = inp["mask"][:, tb:te]
+        o_ref, s_ref = oracle.fwd(*(sl[k] for k in NAMES), s0, msk)
+        hz.check("bf16", hz.to_np(o)[:, tb:te], o_ref, hz.to_np(sf)[n:n + 1], s_ref, what=f"api packed seq{n} o")
+        ref = oracle.bwd(*(sl[k] for k in NAMES), d_o[:, tb:te], s0, msk, d_sf[n][None])
+        for k in NAMES:
+            if te > tb:
+                check_grad("bf16", hz.to_np(x[k].grad)[:, tb:te], ref[k], f"api packed seq{n} d{k}")
+        if 0 <= row < 3:
+            ds0_pool[row] += ref["s0"][0]
+    check_grad("f32", hz.to_np(pool.grad), ds0_pool, "api packed pool ds0")
