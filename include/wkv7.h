@@ -322,6 +322,43 @@ wkv7_status_t wkv7_gdn_bwd(int dtype, int B, int T, int H, int K, int V,
 size_t wkv7_gdn_bwd_workspace_bytes(int B, int T, int H, int K, int V);
 
 /*
+ * wkv7_gdn_bwd_varlen -- gradients of wkv7_gdn_fwd_varlen (N packed Gated
+ * DeltaNet sequences; same reading of the update as wkv7_gdn_fwd).  Sequence
+ * n gets exactly the gradients wkv7_gdn_bwd gives for that one sequence.
+ *
+ *   dtype, N, total_T, H, K, V, cu_seqlens, q,k,v,g,beta, initial_state,
+ *   n_state, state_map
+ *                  as for wkv7_gdn_fwd_varlen (g and beta are [total_T,H];
+ *                  without a map the pool has N rows or one row shared by
+ *                  every sequence).  Read only.
+ *   d_o            [total_T,H,V] dtype.  Read only.
+ *   d_final_state  [N,H,K,V] fp32 or NULL (zero).  Read only.
+ *   dq, dk         [total_T,H,K] dtype; dv [total_T,H,V]; dg, dbeta
+ *                  [total_T,H].  Written at every token of every sequence.
+ *   d_initial_state [N,H,K,V] fp32 or NULL: row n is the gradient of the
+ *                  state sequence n started from (rows of sequences that
+ *                  share a pool entry are the caller's to add).  Written.
+ *   workspace      DEVICE buffer of at least
+ *                  wkv7_gdn_bwd_varlen_workspace_bytes(...) bytes, 16-byte
+ *                  aligned, owned by the caller.  May be NULL when
+ *                  total_T == 0.
+ *   stream         hipStream_t to enqueue on.
+ */
+wkv7_status_t wkv7_gdn_bwd_varlen(int dtype, int N, int total_T, int H, int K, int V,
+                                  const int32_t *cu_seqlens,
+                                  const void *q, const void *k, const void *v,
+                                  const void *g, const void *beta,
+                                  const float *initial_state, int n_state, const int32_t *state_map,
+                                  const void *d_o, const float *d_final_state,
+                                  void *dq, void *dk, void *dv, void *dg, void *dbeta,
+                                  float *d_initial_state, void *workspace, size_t workspace_bytes,
+                                  void *stream);
+
+/* Workspace bytes wkv7_gdn_bwd_varlen needs (the same as
+ * wkv7_bwd_varlen_workspace_bytes). */
+size_t wkv7_gdn_bwd_varlen_workspace_bytes(int N, int total_T, int H, int K, int V);
+
+/*
  * wkv7_step -- one decode token per sequence, state updated in place
  * (section "rwkv7_op_rnn 使用方法": the T = 1 case of the forward).
  *
@@ -375,7 +412,8 @@ int wkv7_fwd_path(int dtype, int B, int T, int H, int K, int V, int algo);
  * 102 adds wkv7_gdn_fwd, 103 adds wkv7_bwd and wkv7_bwd_workspace_bytes,
  * 104 adds wkv7_gdn_step, 105 adds wkv7_gdn_fwd_varlen, 106 adds wkv7_gdn_bwd and
  * wkv7_gdn_bwd_workspace_bytes, 107 adds wkv7_bwd_varlen and
- * wkv7_bwd_varlen_workspace_bytes. */
+ * wkv7_bwd_varlen_workspace_bytes, 108 adds wkv7_gdn_bwd_varlen and
+ * wkv7_gdn_bwd_varlen_workspace_bytes. */
 int wkv7_version(void);
 
 #ifdef __cplusplus

@@ -8,7 +8,7 @@ ctypes binding, and ``api`` maps the rwkv-ops function names
 torch.autograd.  Importing the package loads nothing; the library is loaded
 on first use and a missing library raises.
 """
-from .wkv7 import fwd, fwd_varlen, gdn_fwd, gdn_fwd_varlen, gdn_step, gdn_bwd, bwd, bwd_varlen, step, ALGO_AUTO, ALGO_RECURRENT, ALGO_CHUNKED  # noqa: F401
+from .wkv7 import fwd, fwd_varlen, gdn_fwd, gdn_fwd_varlen, gdn_step, gdn_bwd, gdn_bwd_varlen, bwd, bwd_varlen, step, ALGO_AUTO, ALGO_RECURRENT, ALGO_CHUNKED  # noqa: F401
 from .api import (generalized_delta_rule, generalized_delta_rule_inference, rwkv7_op, rwkv7_op_rnn,  # noqa: F401
                   gated_delta_net, gated_delta_net_recurrent, gated_delta_net_recurrent_inference,
                   gated_delta_net_recurrent_single_step, gated_delta_net_chunk)

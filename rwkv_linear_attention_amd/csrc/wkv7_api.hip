@@ -40,7 +40,7 @@ int choose_path(int dtype, int T, int algo)
 
 extern "C" {
 
-int wkv7_version(void) { return 107; }
+int wkv7_version(void) { return 108; }
 
 const char *wkv7_strerror(int status)
 {
@@ -363,6 +363,59 @@ wkv7_status_t wkv7_gdn_bwd(int dtype, int B, int T, int H, int K, int V,
     wkv7::GdnBwdArgs args{B, T, H, K, q, k, v, g, beta, initial_state, rows, d_o, d_final_state,
                           dq, dk, dv, dg, dbeta, d_initial_state, workspace};
     return wkv7::launch_gdn_backward(dtype, args, s) == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
+}
+
+size_t wkv7_gdn_bwd_varlen_workspace_bytes(int N, int total_T, int H, int K, int V)
+{
+    return wkv7_bwd_varlen_workspace_bytes(N, total_T, H, K, V);
+}
+
+wkv7_status_t wkv7_gdn_bwd_varlen(int dtype, int N, int total_T, int H, int K, int V,
+                                  const int32_t *cu_seqlens,
+                                  const void *q, const void *k, const void *v,
+                                  const void *g, const void *beta,
+                                  const float *initial_state, int n_state, const int32_t *state_map,
+                                  const void *d_o, const float *d_final_state,
+                                  void *dq, void *dk, void *dv, void *dg, void *dbeta,
+                                  float *d_initial_state, void *workspace, size_t workspace_bytes,
+                                  void *stream)
+{
+    wkv7_status_t st = check_common(dtype, N, H, K, V);
+    if (st != WKV7_OK) return st;
+    if (total_T < 0) return WKV7_ERR_INVALID_ARG;
+    if ((long long)total_T * H * K > (1ll << 40)) return WKV7_ERR_UNSUPPORTED;
+    if (2ll * N * H > INT32_MAX || wkv7::bwd_varlen_chunk_capacity(N, total_T) * H > INT32_MAX)
+        return WKV7_ERR_UNSUPPORTED;
+    if (total_T > 0) {
+        const void *req[] = {q, k, v, g, beta, d_o, dq, dk, dv, dg, dbeta, workspace};
+        for (const void *p : req)
+            if (!p || !aligned16(p)) return WKV7_ERR_INVALID_ARG;
+        if (!cu_seqlens || ((uintptr_t)cu_seqlens & 3)) return WKV7_ERR_INVALID_ARG;
+        if (workspace_bytes < wkv7::bwd_varlen_workspace_bytes(N, total_T, H, K)) return WKV7_ERR_INVALID_ARG;
+    }
+    if (initial_state) {
+        if (n_state < 1) return WKV7_ERR_INVALID_ARG;
+        if (!state_map && n_state != N && n_state != 1) return WKV7_ERR_INVALID_ARG;
+    }
+    if (state_map && ((uintptr_t)state_map & 3)) return WKV7_ERR_INVALID_ARG;
+    const void *opt[] = {initial_state, d_final_state, d_initial_state};
+    for (const void *p : opt)
+        if (p && !aligned16(p)) return WKV7_ERR_INVALID_ARG;
+
+    hipStream_t s = (hipStream_t)stream;
+    if (total_T == 0) {
+        if (!d_initial_state) return WKV7_OK;
+        const size_t n = (size_t)N * H * K * V;
+        return wkv7::launch_state_copy(d_final_state, d_initial_state, n, s) == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
+    }
+    // q in the r slot, g in the w slot, beta in the a slot (the kernels' Gated DeltaNet mode)
+    wkv7::BwdArgs args{N, total_T, H, K, q, g, k, v, beta, nullptr, initial_state, nullptr, d_o, d_final_state,
+                       dq, dg, dk, dv, dbeta, nullptr, d_initial_state, workspace};
+    args.gdn = true;
+    args.cu_seqlens = cu_seqlens;
+    args.state_map = state_map;
+    args.n_state = initial_state ? n_state : 0;
+    return wkv7::launch_backward(dtype, args, s) == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
 }
 
 wkv7_status_t wkv7_step(int dtype, int B, int H, int K, int V,

@@ -835,7 +835,9 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(D == 64 ?
         ck0 = (size_t)vg.ck_off[bb];
         nck_store = vg.ck_off[bb + 1] - vg.ck_off[bb];
         if (s0) {
-            const int srow = vg.smap ? vg.smap[bb] : bb;
+            // pool row: state_map[n]; without a map row n, or row 0 when the
+            // pool holds one state shared by every sequence
+            const int srow = vg.smap ? vg.smap[bb] : (vg.n_state == 1 ? 0 : bb);
             if (srow >= 0 && srow < vg.n_state) s0p = s0 + ((size_t)srow * H + h) * D * D;
         }
     } else {

@@ -44,6 +44,10 @@ def lib():
     L.wkv7_bwd_varlen.restype = i
     L.wkv7_bwd_varlen_workspace_bytes.argtypes = [i] * 5
     L.wkv7_bwd_varlen_workspace_bytes.restype = ctypes.c_size_t
+    L.wkv7_gdn_bwd_varlen.argtypes = [i] * 6 + [p] * 6 + [p, i, p, p, p] + [p] * 7 + [ctypes.c_size_t, p]
+    L.wkv7_gdn_bwd_varlen.restype = i
+    L.wkv7_gdn_bwd_varlen_workspace_bytes.argtypes = [i] * 5
+    L.wkv7_gdn_bwd_varlen_workspace_bytes.restype = ctypes.c_size_t
     L.wkv7_gdn_bwd.argtypes = [i, i, i, i, i, i] + [p] * 6 + [i] + [p] * 9 + [ctypes.c_size_t, p]
     L.wkv7_gdn_bwd.restype = i
     L.wkv7_gdn_bwd_workspace_bytes.argtypes = [i] * 5
@@ -432,6 +436,60 @@ def gdn_fwd_varlen(q, k, v, g, beta, cu_seqlens, initial_state=None, state_map=N
     if st != OK:
         raise WKV7Error(st)
     return (o.unsqueeze(0) if lead1 else o), sf
+
+
+def gdn_bwd_varlen(q, k, v, g, beta, cu_seqlens, d_o, initial_state=None, state_map=None, d_final_state=None,
+                   workspace=None, need_initial_state_grad=True):
+    """Gradients of gdn_fwd_varlen.  Inputs as for gdn_fwd_varlen; d_o
+    shaped like v; d_final_state: [N,H,K,V] float32 or None.  Returns a dict
+    with q, k, v, g, beta (shaped like the inputs) and s0 ([N,H,K,V] float32:
+    the gradient of each sequence's initial state, or None)."""
+    dev = q.device
+    lead1 = q.dim() == 4
+    if lead1:
+        if q.shape[0] != 1:
+            raise ValueError("packed inputs take a leading dimension of 1, or none")
+        q, k, v, g, beta, d_o = (t.squeeze(0) for t in (q, k, v, g, beta, d_o))
+    TT, H, K = q.shape
+    V = v.shape[-1]
+    dt = q.dtype
+    code = _dtype_code(dt)
+    _check(k, "k", (TT, H, K), dt, dev)
+    _check(v, "v", (TT, H, V), dt, dev)
+    _check(g, "g", (TT, H), dt, dev)
+    _check(beta, "beta", (TT, H), dt, dev)
+    _check(d_o, "d_o", (TT, H, V), dt, dev)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be [N+1] with N >= 1")
+    N = cu_seqlens.numel() - 1
+    _check(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    n_state = 0
+    if initial_state is not None:
+        n_state = initial_state.shape[0]
+        _check(initial_state, "initial_state", (n_state, H, K, V), torch.float32, dev)
+    if state_map is not None:
+        _check(state_map, "state_map", (N,), torch.int32, dev)
+    if d_final_state is not None:
+        _check(d_final_state, "d_final_state", (N, H, K, V), torch.float32, dev)
+    need = int(lib().wkv7_gdn_bwd_varlen_workspace_bytes(N, TT, H, K, V))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    elif workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
+    out = {"q": torch.empty((TT, H, K), dtype=dt, device=dev), "k": torch.empty((TT, H, K), dtype=dt, device=dev),
+           "v": torch.empty((TT, H, V), dtype=dt, device=dev), "g": torch.empty((TT, H), dtype=dt, device=dev),
+           "beta": torch.empty((TT, H), dtype=dt, device=dev)}
+    out["s0"] = torch.empty((N, H, K, V), dtype=torch.float32, device=dev) if need_initial_state_grad else None
+    st = lib().wkv7_gdn_bwd_varlen(code, N, TT, H, K, V, _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                   _ptr(beta), _ptr(initial_state), n_state, _ptr(state_map), _ptr(d_o),
+                                   _ptr(d_final_state), *(_ptr(out[n]) for n in ("q", "k", "v", "g", "beta", "s0")),
+                                   _ptr(workspace), workspace.numel(), _stream(dev))
+    if st != OK:
+        raise WKV7Error(st)
+    if lead1:
+        for n in ("q", "k", "v", "g", "beta"):
+            out[n] = out[n].unsqueeze(0)
+    return out
 
 
 def gdn_step(q, k, v, g, beta, state=None, out=None, next_state=None):

@@ -27,14 +27,14 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert {"wkv7_fwd", "wkv7_fwd_varlen", "wkv7_gdn_fwd", "wkv7_bwd", "wkv7_bwd_workspace_bytes", "wkv7_gdn_step", "wkv7_gdn_fwd_varlen", "wkv7_gdn_bwd", "wkv7_gdn_bwd_workspace_bytes", "wkv7_bwd_varlen", "wkv7_bwd_varlen_workspace_bytes", "wkv7_step", "wkv7_strerror", "wkv7_fwd_path",
+    assert {"wkv7_fwd", "wkv7_fwd_varlen", "wkv7_gdn_fwd", "wkv7_bwd", "wkv7_bwd_workspace_bytes", "wkv7_gdn_step", "wkv7_gdn_fwd_varlen", "wkv7_gdn_bwd", "wkv7_gdn_bwd_workspace_bytes", "wkv7_bwd_varlen", "wkv7_bwd_varlen_workspace_bytes", "wkv7_gdn_bwd_varlen", "wkv7_gdn_bwd_varlen_workspace_bytes", "wkv7_step", "wkv7_strerror", "wkv7_fwd_path",
             "wkv7_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"{n} declared in wkv7.h but not exported"
 
 
 def test_version_and_strerror(L):
-    assert L.wkv7_version() == 107
+    assert L.wkv7_version() == 108
     for code in range(4):
         assert len(L.wkv7_strerror(code)) > 0
     assert L.wkv7_strerror(99) == b"unknown status"
@@ -322,6 +322,42 @@ def test_bwd_varlen_rejects_null_and_misaligned(L, slot):
     assert bwd_varlen(L, ptrs=ptrs) == wkv7.ERR_INVALID_ARG
     ptrs[slot] = ODD
     assert bwd_varlen(L, ptrs=ptrs) == wkv7.ERR_INVALID_ARG
+
+
+def gdn_bwd_varlen(L, dtype=1, N=3, TT=50, H=1, K=64, V=64, cu=GOOD, ptrs=None, s0=None, n_state=0, smap=None,
+                   dsf=None, ds0=None, ws=GOOD, ws_bytes=None):
+    ptrs = ptrs or [GOOD] * 11
+    if ws_bytes is None:
+        ws_bytes = L.wkv7_gdn_bwd_varlen_workspace_bytes(N, TT, H, K, V)
+    q, k, v, g, beta, do, dq, dk, dv, dg, dbeta = ptrs
+    return L.wkv7_gdn_bwd_varlen(dtype, N, TT, H, K, V, cu, q, k, v, g, beta, s0, n_state, smap, do, dsf,
+                                 dq, dk, dv, dg, dbeta, ds0, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), wkv7.ERR_INVALID_ARG),
+    (dict(N=0), wkv7.ERR_INVALID_ARG),
+    (dict(K=64, V=128), wkv7.ERR_UNSUPPORTED),
+    (dict(cu=None), wkv7.ERR_INVALID_ARG),
+    (dict(ws_bytes=1024), wkv7.ERR_INVALID_ARG),
+    (dict(s0=GOOD, n_state=2), wkv7.ERR_INVALID_ARG),         # no map: N rows or one shared row
+])
+def test_gdn_bwd_varlen_validation(L, kw, code):
+    assert gdn_bwd_varlen(L, **kw) == code
+
+
+def test_gdn_bwd_varlen_accepts_shared_row_without_launch(L):
+    # total_T = 0 and no gradient to write: validation only, no HIP call
+    assert gdn_bwd_varlen(L, TT=0, ws=None, ws_bytes=0, s0=GOOD, n_state=1) == wkv7.OK
+
+
+@pytest.mark.parametrize("slot", range(11))
+def test_gdn_bwd_varlen_rejects_null_and_misaligned(L, slot):
+    ptrs = [GOOD] * 11
+    ptrs[slot] = None
+    assert gdn_bwd_varlen(L, ptrs=ptrs) == wkv7.ERR_INVALID_ARG
+    ptrs[slot] = ODD
+    assert gdn_bwd_varlen(L, ptrs=ptrs) == wkv7.ERR_INVALID_ARG
 
 
 def gdn_step(L, dtype=1, B=2, H=1, K=64, V=64, ptrs=None, s_in=None, n_state=0, s_out=GOOD):

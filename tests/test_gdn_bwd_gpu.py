@@ -129,3 +129,39 @@ def test_gdn_bwd_reused_workspace_and_deterministic():
         fresh = run_gpu(*case)
         for n in got:
             np.testing.assert_array_equal(got[n], fresh[n], err_msg=n)
+
+
+@pytest.mark.parametrize("dtype,D,mapped", [("bf16", 64, True), ("f32", 64, False), ("bf16", 128, False)])
+def test_gdn_bwd_varlen_parity(dtype, D, mapped):
+    """Packed sequences (wkv7_gdn_bwd_varlen) against the oracle run on each
+    sequence alone, starting from its pool row (a state_map entry outside
+    the pool: zero state; no map and one pool row: that row for every
+    sequence)."""
+    lengths, H = [0, 30, 17, 64], 2
+    TT, N = sum(lengths), len(lengths)
+    gi = synth.make_gdn(1, TT, H, D, seed=7700 + D, dtype=dtype)
+    rng = np.random.default_rng(7701)
+    n_state = 3 if mapped else 1
+    pool = (rng.standard_normal((n_state, H, D, D)) * 0.1).astype(np.float32)
+    smap = np.array([1, 2, -1, 0], np.int32) if mapped else None
+    d_o = synth.round_to(rng.standard_normal((TT, H, D)).astype(np.float32), dtype)
+    d_sf = (rng.standard_normal((N, H, D, D)) * 0.5).astype(np.float32)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    dev = {n: synth.to_torch(gi[n][0], dtype, "cuda") for n in NAMES}
+    t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    g = wkv7.gdn_bwd_varlen(*(dev[n] for n in NAMES), t(cu), synth.to_torch(d_o, dtype, "cuda"),
+                            initial_state=t(pool), state_map=t(smap), d_final_state=t(d_sf))
+    torch.cuda.synchronize()
+    g = {n: hz.to_np(x) for n, x in g.items()}
+    for n in range(N):
+        tb, te = int(cu[n]), int(cu[n + 1])
+        row = (int(smap[n]) if mapped else 0)
+        s0 = pool[row][None] if 0 <= row < n_state else None
+        if te == tb:
+            np.testing.assert_array_equal(g["s0"][n], d_sf[n])
+            continue
+        sl = {k: gi[k][:, tb:te] for k in NAMES}
+        ref = oracle.gdn_bwd(*(sl[k] for k in NAMES), d_o[tb:te][None], s0, d_sf[n][None])
+        for k in NAMES:
+            check_grad(dtype, g[k][tb:te], ref[k][0], f"gdn bwd varlen {dtype} D{D} seq{n} d{k}")
+        check_grad("f32", g["s0"][n], ref["s0"][0], f"gdn bwd varlen {dtype} D{D} seq{n} ds0")
