@@ -51,6 +51,17 @@ class _GeneralizedDeltaRule(torch.autograd.Function):
         return g["r"], g["w"], g["k"], g["v"], g["a"], g["b"], g["s0"], None
 
 
+def _pool_grad(per_seq, pool, smap):
+    """Gradient of a pool of initial states from the per-sequence ones: row
+    n without a map (N rows), the sum over the sequences for one shared row,
+    else the sum over the sequences mapped to each row (a map entry outside
+    the pool started from zeros)."""
+    if smap is None:
+        return per_seq if pool.shape[0] == per_seq.shape[0] else per_seq.sum(dim=0, keepdim=True)
+    ok = (smap >= 0) & (smap < pool.shape[0])
+    return torch.zeros_like(pool).index_add_(0, smap[ok].long(), per_seq[ok])
+
+
 class _GeneralizedDeltaRulePacked(torch.autograd.Function):
     @staticmethod
     def forward(ctx, r, w, k, v, a, b, initial_state, cu_seqlens, state_map, mask):
@@ -68,15 +79,7 @@ class _GeneralizedDeltaRulePacked(torch.autograd.Function):
         g = wkv7.bwd_varlen(r, w, k, v, a, b, cu, d_o.contiguous(), initial_state=s0, state_map=smap, mask=mask,
                             d_final_state=None if d_sf is None else d_sf.contiguous(),
                             need_initial_state_grad=ctx.s0_grad)
-        ds0 = None
-        if ctx.s0_grad:
-            if smap is None:
-                ds0 = g["s0"]
-            else:
-                # pool rows: the sum over the sequences mapped to each row
-                # (a sequence whose entry is outside the pool started from zeros)
-                ok = (smap >= 0) & (smap < s0.shape[0])
-                ds0 = torch.zeros_like(s0).index_add_(0, smap[ok].long(), g["s0"][ok])
+        ds0 = _pool_grad(g["s0"], s0, smap) if ctx.s0_grad else None
         return g["r"], g["w"], g["k"], g["v"], g["a"], g["b"], ds0, None, None, None
 
 
@@ -133,16 +136,52 @@ class _GatedDeltaNet(torch.autograd.Function):
         return gr["q"], gr["k"], gr["v"], gr["g"], gr["beta"], gr["s0"]
 
 
-def gated_delta_net(q, k, v, g, beta, initial_state=None, output_final_state=True, head_first=False):
+class _GatedDeltaNetPacked(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, g, beta, initial_state, cu_seqlens, state_map):
+        o, sf = wkv7.gdn_fwd_varlen(q, k, v, g, beta, cu_seqlens, initial_state=initial_state,
+                                    state_map=state_map, output_final_state=True)
+        ctx.save_for_backward(q, k, v, g, beta, initial_state, cu_seqlens, state_map)
+        ctx.s0_grad = initial_state is not None and initial_state.requires_grad
+        return o, sf
+
+    @staticmethod
+    def backward(ctx, d_o, d_sf):
+        q, k, v, g, beta, s0, cu, smap = ctx.saved_tensors
+        if d_o is None:
+            d_o = torch.zeros_like(v)
+        gr = wkv7.gdn_bwd_varlen(q, k, v, g, beta, cu, d_o.contiguous(), initial_state=s0, state_map=smap,
+                                 d_final_state=None if d_sf is None else d_sf.contiguous(),
+                                 need_initial_state_grad=ctx.s0_grad)
+        ds0 = _pool_grad(gr["s0"], s0, smap) if ctx.s0_grad else None
+        return gr["q"], gr["k"], gr["v"], gr["g"], gr["beta"], ds0, None, None
+
+
+def gated_delta_net(q, k, v, g, beta, initial_state=None, output_final_state=True, head_first=False,
+                    cu_seqlens=None, state_map=None):
     """Gated DeltaNet with gradients (q and k are L2-normalised inside).
     q, k: [B,T,H,K]; v: [B,T,H,V]; g, beta: [B,T,H]; initial_state:
     [B,H,K,V] or [1,H,K,V] (shared) float32, or None.  Returns (o,
     final_state or None); gradients flow to q, k, v, g, beta and
-    initial_state."""
+    initial_state.
+
+    Packed sequences: with cu_seqlens (int32 [N+1]) the inputs are
+    [1,T,H,K] and g, beta [1,T,H]; initial_state is [N,H,K,V], one shared
+    row, or with state_map (int32 [N]) a pool; final_state is [N,H,K,V]."""
     _head_first(head_first)
-    _require_device([("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("initial_state", initial_state)])
+    _require_device([("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("initial_state", initial_state),
+                     ("cu_seqlens", cu_seqlens), ("state_map", state_map)])
     tensors = (q, k, v, g, beta) + (() if initial_state is None else (initial_state,))
-    if torch.is_grad_enabled() and any(t.requires_grad for t in tensors):
+    grad = torch.is_grad_enabled() and any(t.requires_grad for t in tensors)
+    if cu_seqlens is not None:
+        if grad:
+            o, sf = _GatedDeltaNetPacked.apply(q, k, v, g, beta, initial_state, cu_seqlens, state_map)
+        else:
+            o, sf = wkv7.gdn_fwd_varlen(q, k, v, g, beta, cu_seqlens, initial_state=initial_state,
+                                        state_map=state_map, output_final_state=True)
+    elif state_map is not None:
+        raise ValueError("state_map needs cu_seqlens (packed sequences)")
+    elif grad:
         o, sf = _GatedDeltaNet.apply(q, k, v, g, beta, initial_state)
     else:
         o, sf = wkv7.gdn_fwd(q, k, v, g, beta, initial_state=initial_state, output_final_state=True)
@@ -178,9 +217,10 @@ def rwkv7_op_rnn(r, w, k, v, a, b, initial_state=None, output_final_state=True, 
     return o.unsqueeze(1), (state if output_final_state else None)
 
 
-def gated_delta_net_recurrent(q, k, v, g, beta, initial_state=None, output_final_state=True, head_first=False):
+def gated_delta_net_recurrent(q, k, v, g, beta, initial_state=None, output_final_state=True, head_first=False,
+                              cu_seqlens=None, state_map=None):
     """gated_delta_net (with gradients); the kernel is chosen by size."""
-    return gated_delta_net(q, k, v, g, beta, initial_state, output_final_state, head_first)
+    return gated_delta_net(q, k, v, g, beta, initial_state, output_final_state, head_first, cu_seqlens, state_map)
 
 
 def gated_delta_net_recurrent_inference(q, k, v, g, beta, initial_state=None, output_final_state=True,

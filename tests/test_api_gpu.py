@@ -130,3 +130,34 @@ def test_generalized_delta_rule_packed_autograd():
         if 0 <= row < 3:
             ds0_pool[row] += ref["s0"][0]
     check_grad("f32", hz.to_np(pool.grad), ds0_pool, "api packed pool ds0")
+
+
+def test_gated_delta_net_packed_autograd_shared_row():
+    """Packed Gated DeltaNet through autograd with one pool row shared by
+    every sequence: its gradient is the sum of the oracle's per-sequence
+    initial-state gradients."""
+    lengths, H, D = [25, 0, 40], 2, 64
+    TT = sum(lengths)
+    gi = synth.make_gdn(1, TT, H, D, seed=8500)
+    rng = np.random.default_rng(8501)
+    pool_np = (rng.standard_normal((1, H, D, D)) * 0.1).astype(np.float32)
+    d_o = synth.round_to(rng.standard_normal((1, TT, H, D)).astype(np.float32), "bf16")
+    cu_np = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    x = {n: leaf(gi[n], "bf16") for n in GNAMES}
+    pool = torch.from_numpy(pool_np).cuda().requires_grad_(True)
+    o, sf = m.gated_delta_net(*(x[n] for n in GNAMES), initial_state=pool,
+                              cu_seqlens=torch.from_numpy(cu_np).cuda())
+    (o.float() * synth.to_torch(d_o, "f32", "cuda")).sum().backward()
+    torch.cuda.synchronize()
+    ds0 = np.zeros((1, H, D, D))
+    for n in range(len(lengths)):
+        tb, te = int(cu_np[n]), int(cu_np[n + 1])
+        sl = {k: gi[k][:, tb:te] for k in GNAMES}
+        o_ref, s_ref = oracle.gdn_fwd(*(sl[k] for k in GNAMES), pool_np)
+        hz.check("bf16", hz.to_np(o)[:, tb:te], o_ref, hz.to_np(sf)[n:n + 1], s_ref, what=f"api gdn packed seq{n} o")
+        ref = oracle.gdn_bwd(*(sl[k] for k in GNAMES), d_o[:, tb:te], pool_np)
+        if te > tb:
+            for k in GNAMES:
+                check_grad("bf16", hz.to_np(x[k].grad)[:, tb:te], ref[k], f"api gdn packed seq{n} d{k}")
+        ds0 += ref["s0"]
+    check_grad("f32", hz.to_np(pool.grad), ds0, "api gdn packed shared ds0")
