@@ -466,6 +466,23 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(D == 64 ?
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int q = lane >> 4, m = lane & 15;
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    // At D = 64 with bf16 I/O the state and dS' values of the value-column
+    // products are loaded into registers first, so that their latency
+    // overlaps the staging and chunk-matrix phases (measured 4 % faster; at
+    // D = 128, or with fp32 I/O, the extra registers cost occupancy).  Lane
+    // (q, m) holds rows 16 jb + 4 q + st, column 16 wave + m, at index
+    // 4 jb + st: the contraction order in which each lane reads the other
+    // operand as one 16-byte row segment per four MFMA steps.
+    constexpr bool kPre = D == 64 && sizeof(T_IO) == 2;
+    float scol[D / 4], dcol[D / 4];
+    if constexpr (kPre) {
+#pragma unroll
+        for (int i = 0; i < D / 4; ++i) {
+            const size_t e = (size_t)(16 * (i >> 2) + 4 * q + (i & 3)) * D + 16 * wave + m;
+            scol[i] = Sc[e];
+            dcol[i] = dSe[e];
+        }
+    }
 
     // raw inputs of the chunk, four channels per thread; a token that does
     // not update gets w = k = a = b = 0 and v = 0 (an exact identity step),
@@ -586,14 +603,34 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(D == 64 ?
     const int c0 = 16 * wave;
     auto dY = [&](int kk, int n) { return s.EGL[kk] * dSe[(size_t)kk * D + c0 + n]; };
     {
-        f32x4 X = mm16<D>(z, [&](int mm, int kk) { return s.B[mm][kk]; },
-                          [&](int kk, int n) { return Sc[(size_t)kk * D + c0 + n]; }, lane);
+        f32x4 X = z;
+        if constexpr (kPre) {
+#pragma unroll
+            for (int jb = 0; jb < D / 16; ++jb) {
+                const f32x4 bt = *(const f32x4 *)&s.B[m][16 * jb + 4 * q];
+#pragma unroll
+                for (int st = 0; st < 4; ++st) X = mfma_f32(bt[st], scol[4 * jb + st], X);
+            }
+        } else {
+            X = mm16<D>(z, [&](int mm, int kk) { return s.B[mm][kk]; },
+                        [&](int kk, int n) { return Sc[(size_t)kk * D + c0 + n]; }, lane);
+        }
         X = mm16<kL>(X, [&](int mm, int kk) { return s.M[M_BK][mm][kk]; },
                      [&](int kk, int n) { return tl(s.V[kk][c0 + n]); }, lane);
 #pragma unroll
         for (int i = 0; i < 4; ++i) s.U[4 * q + i][c0 + m] = X[i];
     }
-    f32x4 dU = mm16<D>(z, [&](int mm, int kk) { return s.A[mm][kk]; }, dY, lane);
+    f32x4 dU = z;
+    if constexpr (kPre) {
+#pragma unroll
+        for (int jb = 0; jb < D / 16; ++jb) {
+            const f32x4 at = *(const f32x4 *)&s.A[m][16 * jb + 4 * q], eg = *(const f32x4 *)&s.EGL[16 * jb + 4 * q];
+#pragma unroll
+            for (int st = 0; st < 4; ++st) dU = mfma_f32(at[st], eg[st] * dcol[4 * jb + st], dU);
+        }
+    } else {
+        dU = mm16<D>(z, [&](int mm, int kk) { return s.A[mm][kk]; }, dY, lane);
+    }
     dU = mm16<kL>(dU, [&](int mm, int kk) { return s.M[M_RA][kk][mm]; },
                   [&](int kk, int n) { return tl(s.DO[kk][c0 + n]); }, lane);
 #pragma unroll
@@ -617,8 +654,18 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(D == 64 ?
         // dV = K^ dY + M_rk^T dO + M_bk^T dX, formed transposed (value columns
         // c0 + 4q + i of token m in lane (q, m)) so that each lane stores four
         // adjacent columns
-        f32x4 dVt = mm16<D>(z, [&](int mm, int kk) { return dY(kk, mm); },
-                            [&](int kk, int n) { return s.K[n][kk]; }, lane);
+        f32x4 dVt = z;
+        if constexpr (kPre) {
+#pragma unroll
+            for (int jb = 0; jb < D / 16; ++jb) {
+                const f32x4 kt = *(const f32x4 *)&s.K[m][16 * jb + 4 * q], eg = *(const f32x4 *)&s.EGL[16 * jb + 4 * q];
+#pragma unroll
+                for (int st = 0; st < 4; ++st) dVt = mfma_f32(eg[st] * dcol[4 * jb + st], kt[st], dVt);
+            }
+        } else {
+            dVt = mm16<D>(z, [&](int mm, int kk) { return dY(kk, mm); },
+                          [&](int kk, int n) { return s.K[n][kk]; }, lane);
+        }
         dVt = mm16<kL>(dVt, [&](int mm, int kk) { return tl(s.DO[kk][c0 + mm]); },
                        [&](int kk, int n) { return s.M[M_RK][kk][n]; }, lane);
         dVt = mm16<kL>(dVt, [&](int mm, int kk) { return s.DX[kk][c0 + mm]; },
@@ -629,6 +676,17 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(D == 64 ?
     // wave 0 dM_ra = dO U^T, wave 1 dM_rk = dO V^T, wave 2 dM_ba = dX U^T,
     // wave 3 dM_bk = dX V^T; stored over the chunk matrices once every wave
     // is past the value gradient ---
+    // rows of S and dS' for the key-channel products below (kPre: loaded
+    // here, ahead of the chunk-matrix gradients)
+    f32x4 srow[D / 16], drow[D / 16];
+    if constexpr (kPre) {
+        const size_t rowp = (size_t)(16 * wave + m) * D + 4 * q;
+#pragma unroll
+        for (int jb = 0; jb < D / 16; ++jb) {
+            srow[jb] = *(const f32x4 *)(Sc + rowp + 16 * jb);
+            drow[jb] = *(const f32x4 *)(dSe + rowp + 16 * jb);
+        }
+    }
     f32x4 dmacc = z;
     {
         auto rowDO = [&](int mm, int j) { return tl4(&s.DO[mm][j]); };
@@ -666,7 +724,14 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(D == 64 ?
 #pragma unroll
         for (int j0b = 0; j0b < D; j0b += 16) {
             const int j = j0b + 4 * q;
-            const f32x4 sr = *(const f32x4 *)(Sc + rowm + j), dr4 = *(const f32x4 *)(dSe + rowm + j);
+            f32x4 sr, dr4;
+            if constexpr (kPre) {
+                sr = srow[j0b / 16];
+                dr4 = drow[j0b / 16];
+            } else {
+                sr = *(const f32x4 *)(Sc + rowm + j);
+                dr4 = *(const f32x4 *)(dSe + rowm + j);
+            }
             sds += dr4[0] * sr[0] + dr4[1] * sr[1] + dr4[2] * sr[2] + dr4[3] * sr[3];
             const f32x4 dy = dr4 * eglm;
             const f32x4 yo = tl4(&s.DO[m][j]), yx = *(const f32x4 *)&s.DX[m][j];
