@@ -20,6 +20,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# MI355X published fp32 vector peak: 256 CUs x 4 SIMDs x 16 lanes x 2 (packed fp32) x 2 flops (FMA)
+# x 2.4 GHz.  Code built without packed fp32 instructions issues at most half of it.
+FP32_VECTOR_PEAK_TFLOPS = 157.3
 PROFILE_NOTE = os.path.join(ROOT, "profiles", "wkv7_chunked_B8_T4096_H64_d64.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "rwkv_linear_attention_amd", "csrc", f)
                   for f in ("wkv7_chunked.hip", "wkv7_common.hpp")]
@@ -555,6 +558,38 @@ def small_latency(steps, warmup, cpu=True):
     return out
 
 
+def recurrent_workload(steps, warmup):
+    """The recurrent forward (fp32 I/O always takes it) at the workload-2
+    shape, B8 T4096 H64 d64: 512 sequences, each a serial scan of 4096 token
+    steps.  Per token and head it does 9 K V flops (b^T S, the decay, the two
+    rank-one updates, S^T r) on the fp32 vector units, so it is reported
+    against both the fp32 vector peak and HBM."""
+    import torch
+    from rwkv_linear_attention_amd import synth, wkv7
+    wl = synth.WORKLOADS[2]
+    B, T, H, D = wl["B"], wl["T"], wl["H"], wl["K"]
+    print("[bench] generating the fp32 recurrent workload", file=sys.stderr, flush=True)
+    inp = synth.make(2)
+    dev = {n: synth.to_torch(inp[n], "f32", "cuda") for n in ("r", "w", "k", "v", "a", "b")}
+    o = torch.empty((B, T, H, D), dtype=torch.float32, device="cuda")
+    sf = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
+    ms = _time_launches(lambda i: wkv7.fwd(*(dev[n] for n in ("r", "w", "k", "v", "a", "b")), out=o,
+                                           final_state=sf), max(3, steps // 5), warmup)
+    nbytes = algorithmic_bytes(B, T, H, D, 4, False, True, False)
+    flops = 9 * B * T * H * D * D
+    name = f"fwd_f32_B{B}_T{T}_H{H}_d{D}"
+    out = {name: {"ms": round(ms, 4), "Mtokens_per_s": round(B * T / ms / 1e3, 3),
+                  "GB_per_s": round(nbytes / ms / 1e6, 1), "frac_of_8TBps": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
+                  "algorithmic_bytes": nbytes,
+                  "roofline": {"bound": "alu", "unit": "TFLOP/s", "peak": FP32_VECTOR_PEAK_TFLOPS,
+                               "achieved": round(flops / ms / 1e9, 2),
+                               "frac": round(flops / ms / 1e9 / FP32_VECTOR_PEAK_TFLOPS, 4), "flops": flops,
+                               "note": "9 K V vector flops per token and head"},
+                  "kernel": "recurrent d64 (fp32 I/O)"}}
+    del dev, o, sf, inp
+    return out
+
+
 def other_workloads(steps, warmup, cpu=True):
     """Latency of the two small forward shapes, then head size 128 forward
     (B16 T4096 H32, trailing-padding mask, S0), the packed variable-length
@@ -564,6 +599,8 @@ def other_workloads(steps, warmup, cpu=True):
     import torch
     from rwkv_linear_attention_amd import synth, wkv7
     out = small_latency(steps, warmup, cpu)
+    out.update(recurrent_workload(steps, warmup))
+    torch.cuda.empty_cache()
     wl = synth.WORKLOADS[3]
     B, T, H, D = wl["B"], wl["T"], wl["H"], wl["K"]
     print(f"[bench] generating workload {wl['name']}", file=sys.stderr, flush=True)

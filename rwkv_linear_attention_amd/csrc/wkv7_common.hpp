@@ -53,6 +53,23 @@ template <> struct io<uint16_t> {
     __device__ __forceinline__ static void store(uint16_t *p, size_t i, float x) { p[i] = f32_to_bf16_bits(x); }
 };
 
+// Four consecutive elements kept in their I/O type (a prefetch register set).
+template <typename T> struct raw4;
+template <> struct raw4<float> {
+    typedef f32x4 type;
+    __device__ __forceinline__ static type load(const float *p, size_t i) { return *(const f32x4 *)(p + i); }
+    __device__ __forceinline__ static f32x4 f32(type x) { return x; }
+    __device__ __forceinline__ static type zero() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+};
+template <> struct raw4<uint16_t> {
+    typedef u32x2 type;
+    __device__ __forceinline__ static type load(const uint16_t *p, size_t i) { return *(const u32x2 *)(p + i); }
+    __device__ __forceinline__ static f32x4 f32(type u)
+    {
+        return f32x4{bf16_lo(u[0]), bf16_hi(u[0]), bf16_lo(u[1]), bf16_hi(u[1])};
+    }
+    __device__ __forceinline__ static type zero() { return u32x2{0u, 0u}; }
+};
 // ---- cross-lane ----------------------------------------------------------
 
 // row_shr:n inside each 16-lane row; lanes without a source receive `fill`.

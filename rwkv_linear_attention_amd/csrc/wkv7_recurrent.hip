@@ -13,8 +13,10 @@
 // column 16w + j in VGPRs, so b^T S and S^T r are in-lane FMA chains over D/4
 // rows plus a 4-way cross-lane sum.  Tokens are staged in LDS 16 at a time
 // (fp32, exp(w) precomputed); all lanes of a row group read the same LDS
-// address (broadcast).  This path is latency-bound and serves fp32 I/O,
-// short sequences and few (b, h) pairs.
+// address (broadcast).  The next block's inputs are loaded into registers
+// (one thread per token and four channels) while the current block runs.
+// This path is latency-bound and serves fp32 I/O, short sequences and few
+// (b, h) pairs.
 #include "wkv7_common.hpp"
 #include "wkv7_internal.hpp"
 
@@ -38,7 +40,6 @@ __global__ __launch_bounds__(D * 4) void recurrent_kernel(
     constexpr int RPL = D / 4;      // state rows per lane
     constexpr int NT = D * 4;       // threads
     __shared__ float s_ew[TB][D], s_a[TB][D], s_b[TB][D], s_k[TB][D], s_r[TB][D], s_v[TB][D];
-    __shared__ int s_upd[TB];
     __shared__ float s_gate[TB], s_beta[TB], s_iq[TB], s_ik[TB];
 
     const int bh = blockIdx.x;
@@ -79,6 +80,23 @@ __global__ __launch_bounds__(D * 4) void recurrent_kernel(
         for (int i = 0; i < RPL; ++i) S[i] = s0[st_in + (size_t)(row0 + i) * D + col];
     }
 
+    // generalized-rule inputs of one staged block: thread (tp, cp) holds
+    // channels cp .. cp + 3 of token tp (zeros past the sequence's end)
+    static_assert(NT == TB * D / 4, "one thread per (token, 4 channels)");
+    const int tp = tid / (D / 4), cp = 4 * (tid % (D / 4));
+    using R4 = raw4<T_IO>;
+    typename R4::type pf[6];
+    int pup = 0;
+    auto fetch = [&](int t0) {
+        const bool valid = t0 + tp < Tn;
+        const size_t gi = ((tok0 + t0 + tp) * H + h) * D + cp;
+        const T_IO *src[6] = {w, a, b, k, r, v};
+#pragma unroll
+        for (int x = 0; x < 6; ++x) pf[x] = valid ? R4::load(src[x], gi) : R4::zero();
+        pup = valid && (mask ? mask[tok0 + t0 + tp] != 0 : 1);
+    };
+    if (!GDN && Tn > 0) fetch(0);
+
     for (int t0 = 0; t0 < Tn; t0 += TB) {
         const int nt = min(TB, Tn - t0);
         __syncthreads();
@@ -99,7 +117,6 @@ __global__ __launch_bounds__(D * 4) void recurrent_kernel(
                 const size_t si = (tok0 + t0 + min(tid, nt - 1)) * H + h;
                 s_gate[tid] = io<T_IO>::load(w, si);
                 s_beta[tid] = io<T_IO>::load(a, si);
-                s_upd[tid] = tid < nt;
             }
             __syncthreads();
             // norms: four lanes per token, each over a quarter of the channels
@@ -129,27 +146,28 @@ __global__ __launch_bounds__(D * 4) void recurrent_kernel(
                 s_ew[tl][c] = eg;
             }
         } else {
-            for (int idx = tid; idx < TB * D; idx += NT) {
-                const int tl = idx / D, c = idx % D;
-                float ew = 1.f, av = 0.f, bv = 0.f, kv = 0.f, rv = 0.f, vv = 0.f;
-                if (tl < nt) {
-                    const size_t gi = ((tok0 + t0 + tl) * H + h) * D + c;
-                    ew = __expf(io<T_IO>::load(w, gi));
-                    av = io<T_IO>::load(a, gi);
-                    bv = io<T_IO>::load(b, gi);
-                    kv = io<T_IO>::load(k, gi);
-                    rv = io<T_IO>::load(r, gi);
-                    vv = io<T_IO>::load(v, gi);
-                }
-                s_ew[tl][c] = ew; s_a[tl][c] = av; s_b[tl][c] = bv;
-                s_k[tl][c] = kv; s_r[tl][c] = rv; s_v[tl][c] = vv;
-            }
-            if (tid < TB) s_upd[tid] = (tid < nt) && (mask ? mask[tok0 + t0 + tid] != 0 : 1);
+            // A token that does not update becomes an exact identity step
+            // (e^w = 1, a = b = k = v = 0), whatever its inputs hold, even
+            // inf or nan; its r still produces an output.
+            const f32x4 wv = R4::f32(pf[0]), z4 = {0.f, 0.f, 0.f, 0.f};
+            f32x4 ew;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ew[i] = pup ? __expf(wv[i]) : 1.0f;
+            *(f32x4 *)&s_ew[tp][cp] = ew;
+            *(f32x4 *)&s_a[tp][cp] = pup ? R4::f32(pf[1]) : z4;
+            *(f32x4 *)&s_b[tp][cp] = pup ? R4::f32(pf[2]) : z4;
+            *(f32x4 *)&s_k[tp][cp] = pup ? R4::f32(pf[3]) : z4;
+            *(f32x4 *)&s_r[tp][cp] = R4::f32(pf[4]);
+            *(f32x4 *)&s_v[tp][cp] = pup ? R4::f32(pf[5]) : z4;
+            if (t0 + TB < Tn) fetch(t0 + TB);
         }
         __syncthreads();
 
-        for (int tl = 0; tl < nt; ++tl) {
-            if (s_upd[tl]) {
+        // Every staged token updates (a masked one as the identity), so the
+        // steps have no branch and a full block is unrolled: the loads of a
+        // token's operands can then run ahead of the previous token's chain.
+        auto token = [&](int tl) {
+            {
                 float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
 #pragma unroll
                 for (int i = 0; i < RPL; i += 4) {
@@ -178,6 +196,12 @@ __global__ __launch_bounds__(D * 4) void recurrent_kernel(
             ov = xsum16(ov);
             ov = xsum32(ov);
             if (g == 0) io<T_IO>::store(o, ((tok0 + t0 + tl) * H + h) * D + col, ov);
+        };
+        if (nt == TB) {
+#pragma unroll
+            for (int tl = 0; tl < TB; ++tl) token(tl);
+        } else {
+            for (int tl = 0; tl < nt; ++tl) token(tl);
         }
     }
     if (sf) {
