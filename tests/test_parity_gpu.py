@@ -63,6 +63,23 @@ def test_full_size_workload_sampled(idx):
     assert torch.isfinite(o.float()).all()
 
 
+def test_full_size_fp32_recurrent_sampled():
+    """The workload-2 shape (B8 T4096 H64 d64) with fp32 I/O, which always
+    takes the recurrent kernel, as the benchmark times it; checked on sampled
+    sequences against the fp32 rule (max-abs 1e-4)."""
+    inp = dict(synth.make(2), dtype="f32")
+    B, T, H, D = inp["r"].shape
+    assert wkv7.fwd_path(torch.float32, B, T, H, D, D) == REC
+    dev = hz.to_dev(inp)
+    o, sf = hz.gpu_fwd(dev)
+    torch.cuda.synchronize()
+    pairs = sampled_pairs(B, H)
+    refs = hz.oracle_fwd(inp, pairs)
+    for (bb, h), (o_ref, s_ref) in zip(pairs, refs):
+        hz.check("f32", hz.to_np(o[bb, :, h]), o_ref, hz.to_np(sf[bb, h]), s_ref,
+                 f"fp32 workload-2 shape (b={bb}, h={h})")
+
+
 def test_workload4_decode_steps_sampled():
     """256 consecutive wkv7_step calls on B=512, H=40, d=64 (state in place),
     checked on sampled sequences against 256 oracle steps."""
