@@ -11,6 +11,12 @@ import oracle
 from rwkv_linear_attention_amd import synth, wkv7
 from test_bwd_gpu import check_grad
 
+
+def grad_scale(ref, names):
+    """RMS over all input gradients of one call: the scale floor for a
+    gradient tensor that vanishes identically (see check_grad)."""
+    return float(np.sqrt(np.mean(np.concatenate([np.ravel(ref[n]) for n in names]) ** 2)))
+
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
@@ -44,8 +50,9 @@ def test_random_fwd_and_bwd(seed):
     o_ref, s_ref = oracle.fwd(*(inp[n] for n in NAMES), inp["s0"], inp["mask"])
     hz.check(dt, hz.to_np(o), o_ref, hz.to_np(sf), s_ref, what=what + " fwd")
     ref = oracle.bwd(*(inp[n] for n in NAMES), d_o, inp["s0"], inp["mask"])
+    fl = grad_scale(ref, NAMES)
     for n in NAMES:
-        check_grad(dt, hz.to_np(g[n]), ref[n], f"{what} d{n}")
+        check_grad(dt, hz.to_np(g[n]), ref[n], f"{what} d{n}", floor=fl)
     check_grad("f32", hz.to_np(g["s0"]), ref["s0"], f"{what} ds0")
 
 
@@ -67,8 +74,9 @@ def test_random_gdn_fwd_and_bwd(seed):
     o_ref, s_ref = oracle.gdn_fwd(*(gi[n] for n in GNAMES), gi["s0"])
     hz.check(dt, hz.to_np(o), o_ref, hz.to_np(sf), s_ref, what=what + " fwd")
     ref = oracle.gdn_bwd(*(gi[n] for n in GNAMES), d_o, gi["s0"])
+    fl = grad_scale(ref, GNAMES)
     for n in GNAMES:
-        check_grad(dt, hz.to_np(g[n]), ref[n], f"{what} d{n}")
+        check_grad(dt, hz.to_np(g[n]), ref[n], f"{what} d{n}", floor=fl)
     check_grad("f32", hz.to_np(g["s0"]), ref["s0"], f"{what} ds0")
 
 
@@ -108,6 +116,7 @@ def test_random_packed_fwd_and_bwd(seed):
         o_ref, s_ref = oracle.fwd(*(sl[k] for k in NAMES), s0, mask[tb:te][None])
         hz.check(dt, o[tb:te], o_ref[0], sf[n], s_ref[0], what=what + " fwd")
         ref = oracle.bwd(*(sl[k] for k in NAMES), d_o[tb:te][None], s0, mask[tb:te][None])
+        fl = grad_scale(ref, NAMES)
         for k in NAMES:
-            check_grad(dt, g[k][tb:te], ref[k][0], f"{what} d{k}")
+            check_grad(dt, g[k][tb:te], ref[k][0], f"{what} d{k}", floor=fl)
         check_grad("f32", g["s0"][n], ref["s0"][0], f"{what} ds0")
