@@ -111,6 +111,47 @@ __device__ __forceinline__ float xsum32(float x)
     return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
+// Gated DeltaNet operands.  With kn = k / sqrt(|k|^2 + 1e-6) (qn likewise),
+// the gated delta rule S = e^g (I - beta kn kn^T) S + beta kn v^T, o = S^T qn
+// (rwkv-ops README, section "gdn_recurrent 使用方法", read as the textbook rule)
+// is the generalized rule with r = qn, w = g on every channel, k = beta kn,
+// a = -e^g beta kn and b = kn.  The staging steps below form those operands
+// from q, k, g and beta, one thread per four channels of a token; the D/4
+// threads of a token are adjacent lanes of one wave.
+constexpr float kGdnNormEps = 1e-6f;
+
+// Sum over the D/4 lanes of a token with DPP (no LDS traffic): swap lane
+// pairs, then pairs of pairs, then mirror within each 8- and 16-lane half
+// (row_half_mirror, row_mirror); at D = 128 also add the neighbouring 16-lane
+// row.  Each step adds two partial sums in either order, so every lane of the
+// token ends with the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+template <int D>
+__device__ __forceinline__ float token_sum(float x)
+{
+    static_assert(D == 64 || D == 128, "a token spans 16 or 32 lanes");
+    x += dpp_mov<0xB1>(x);    // quad_perm [1,0,3,2]
+    x += dpp_mov<0x4E>(x);    // quad_perm [2,3,0,1]
+    x += dpp_mov<0x141>(x);   // row_half_mirror
+    x += dpp_mov<0x140>(x);   // row_mirror
+    if constexpr (D == 128) x = xsum16(x);
+    return x;
+}
+
+__device__ __forceinline__ float dot4(f32x4 a, f32x4 b) { return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3]; }
+
+// 1 / sqrt(|x|^2 + eps) over the whole token row (x: this thread's 4 channels).
+template <int D>
+__device__ __forceinline__ float inv_norm(f32x4 x)
+{
+    return 1.0f / sqrtf(token_sum<D>(dot4(x, x)) + kGdnNormEps);
+}
+
 // ---- MFMA ----------------------------------------------------------------
 // 16x16x32 bf16: lane l supplies A[m = l%16][8 k-slots of group l/16] and
 // B[8 k-slots of group l/16][n = l%16]; the accumulator holds

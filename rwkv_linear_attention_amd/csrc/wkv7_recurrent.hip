@@ -40,7 +40,6 @@ __global__ __launch_bounds__(D * 4) void recurrent_kernel(
     constexpr int RPL = D / 4;      // state rows per lane
     constexpr int NT = D * 4;       // threads
     __shared__ float s_ew[TB][D], s_a[TB][D], s_b[TB][D], s_k[TB][D], s_r[TB][D], s_v[TB][D];
-    __shared__ float s_gate[TB], s_beta[TB], s_iq[TB], s_ik[TB];
 
     const int bh = blockIdx.x;
     // Sequence sq: tokens [tok0, tok0 + Tn) of the token axis (packed form:
@@ -80,71 +79,52 @@ __global__ __launch_bounds__(D * 4) void recurrent_kernel(
         for (int i = 0; i < RPL; ++i) S[i] = s0[st_in + (size_t)(row0 + i) * D + col];
     }
 
-    // generalized-rule inputs of one staged block: thread (tp, cp) holds
-    // channels cp .. cp + 3 of token tp (zeros past the sequence's end)
+    // Inputs of one staged block: thread (tp, cp) holds channels cp .. cp + 3
+    // of token tp (zeros past the sequence's end); the D/4 threads of a token
+    // are adjacent lanes.  Generalized rule: w, a, b, k, r, v.  Gated
+    // DeltaNet: q, k, v in slots 4, 3, 5 and the token's gate and strength.
     static_assert(NT == TB * D / 4, "one thread per (token, 4 channels)");
     const int tp = tid / (D / 4), cp = 4 * (tid % (D / 4));
     using R4 = raw4<T_IO>;
     typename R4::type pf[6];
     int pup = 0;
+    float pg = 0.f, pb = 0.f;
     auto fetch = [&](int t0) {
         const bool valid = t0 + tp < Tn;
         const size_t gi = ((tok0 + t0 + tp) * H + h) * D + cp;
-        const T_IO *src[6] = {w, a, b, k, r, v};
+        if constexpr (GDN) {
+            pf[4] = valid ? R4::load(r, gi) : R4::zero();
+            pf[3] = valid ? R4::load(k, gi) : R4::zero();
+            pf[5] = valid ? R4::load(v, gi) : R4::zero();
+            const size_t si = (tok0 + t0 + tp) * H + h;
+            pg = valid ? io<T_IO>::load(w, si) : 0.f;
+            pb = valid ? io<T_IO>::load(a, si) : 0.f;
+        } else {
+            const T_IO *src[6] = {w, a, b, k, r, v};
 #pragma unroll
-        for (int x = 0; x < 6; ++x) pf[x] = valid ? R4::load(src[x], gi) : R4::zero();
-        pup = valid && (mask ? mask[tok0 + t0 + tp] != 0 : 1);
+            for (int x = 0; x < 6; ++x) pf[x] = valid ? R4::load(src[x], gi) : R4::zero();
+            pup = valid && (mask ? mask[tok0 + t0 + tp] != 0 : 1);
+        }
     };
-    if (!GDN && Tn > 0) fetch(0);
+    if (Tn > 0) fetch(0);
 
     for (int t0 = 0; t0 < Tn; t0 += TB) {
         const int nt = min(TB, Tn - t0);
         __syncthreads();
         if constexpr (GDN) {
-            // stage q, k, v and the per-token gate and strength
-            for (int idx = tid; idx < TB * D; idx += NT) {
-                const int tl = idx / D, c = idx % D;
-                float qv = 0.f, kv = 0.f, vv = 0.f;
-                if (tl < nt) {
-                    const size_t gi = ((tok0 + t0 + tl) * H + h) * D + c;
-                    qv = io<T_IO>::load(r, gi);
-                    kv = io<T_IO>::load(k, gi);
-                    vv = io<T_IO>::load(v, gi);
-                }
-                s_r[tl][c] = qv; s_b[tl][c] = kv; s_v[tl][c] = vv;
-            }
-            if (tid < TB) {
-                const size_t si = (tok0 + t0 + min(tid, nt - 1)) * H + h;
-                s_gate[tid] = io<T_IO>::load(w, si);
-                s_beta[tid] = io<T_IO>::load(a, si);
-            }
-            __syncthreads();
-            // norms: four lanes per token, each over a quarter of the channels
-            if (tid < 4 * TB) {
-                const int tl = tid >> 2, part = tid & 3;
-                float nq = 0.f, nk = 0.f;
-                for (int c = part; c < D; c += 4) {
-                    nq = fmaf(s_r[tl][c], s_r[tl][c], nq);
-                    nk = fmaf(s_b[tl][c], s_b[tl][c], nk);
-                }
-                nq += __shfl_xor(nq, 1, kWave); nq += __shfl_xor(nq, 2, kWave);
-                nk += __shfl_xor(nk, 1, kWave); nk += __shfl_xor(nk, 2, kWave);
-                if (part == 0) {
-                    s_iq[tl] = 1.0f / sqrtf(nq + 1e-6f);
-                    s_ik[tl] = 1.0f / sqrtf(nk + 1e-6f);
-                }
-            }
-            __syncthreads();
-            for (int idx = tid; idx < TB * D; idx += NT) {
-                const int tl = idx / D, c = idx % D;
-                const float kn = s_b[tl][c] * s_ik[tl];
-                const float eg = __expf(s_gate[tl]);
-                s_r[tl][c] *= s_iq[tl];
-                s_b[tl][c] = kn;
-                s_k[tl][c] = s_beta[tl] * kn;
-                s_a[tl][c] = -eg * s_beta[tl] * kn;
-                s_ew[tl][c] = eg;
-            }
+            // qn = q / |q|, kn = k / |k| (norms over the token's lanes), then
+            // r = qn, w = g, k = beta kn, a = -e^g beta kn, b = kn
+            const f32x4 q4 = R4::f32(pf[4]), k4 = R4::f32(pf[3]);
+            const float iq = inv_norm<D>(q4), ik = inv_norm<D>(k4);
+            const f32x4 kn = k4 * ik;
+            const float eg = __expf(pg);
+            *(f32x4 *)&s_r[tp][cp] = q4 * iq;
+            *(f32x4 *)&s_b[tp][cp] = kn;
+            *(f32x4 *)&s_k[tp][cp] = kn * pb;
+            *(f32x4 *)&s_a[tp][cp] = kn * (-eg * pb);
+            *(f32x4 *)&s_ew[tp][cp] = f32x4{eg, eg, eg, eg};
+            *(f32x4 *)&s_v[tp][cp] = R4::f32(pf[5]);
+            if (t0 + TB < Tn) fetch(t0 + TB);
         } else {
             // A token that does not update becomes an exact identity step
             // (e^w = 1, a = b = k = v = 0), whatever its inputs hold, even
