@@ -11,11 +11,13 @@ namespace {
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Sequences shorter than this run on the recurrent kernel under AUTO.
-// Measured on MI355X (bf16, head size 64 and 128, 1 to 512 sequences): the
-// chunked kernel is faster from T = 16 on for every shape, by 1.1x at T = 16
-// up to 7x at T = 2048; below 16 the two are within launch-time noise except
-// at head size 128 with 512 sequences and T <= 4, where the recurrent kernel
-// is faster (15 vs 22 us).
+// Measured on MI355X (bf16, head size 64 and 128, 1 to 512 sequences): from
+// T = 16 on the chunked kernel is as fast or faster for every shape (equal
+// within call overhead for small batches at T = 16, up to 1.6x faster there
+// with 512 sequences; 4.7x to 8.9x at T = 2048).  Below 16 the two are within
+// call overhead except at head size 128 with 512 sequences, where the
+// recurrent kernel is faster at T <= 4 (12-16 vs 21 us) and slower at T = 8
+// (22.6 vs 20.9 us).
 constexpr int kChunkedMinT = 16;
 
 wkv7_status_t check_common(int dtype, int B, int H, int K, int V)
