@@ -89,3 +89,65 @@ def check(dtype, o, o_ref, s=None, s_ref=None, what="", scale=1.0):
         es = float(np.abs(s - s_ref).max(initial=0.0))
         assert es <= scale * 0.02 * srms or es == 0.0, f"{what}: max |dS| = {es:.3g} vs 0.02*RMS = {0.02 * srms:.3g}"
     return ratio
+
+
+def check_grad(dtype, got, ref, what, floor=0.0):
+    """Tolerance relative to the reference tensor's RMS.
+
+    floor: the scale for a gradient tensor that vanishes identically, such as
+    dw of a one-token sequence without an initial state (w only scales a zero
+    state there).  Such a tensor has no scale of its own, and the chunk form
+    builds it from O(1) terms that cancel exactly, so its fp32 rounding
+    follows the size of those terms (the call's other input gradients).  The
+    floor applies only when the oracle tensor is identically zero, or below
+    1e-6 of the floor (fp64 round-off of an exact zero); every other tensor is
+    held to its own RMS."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape
+    assert np.all(np.isfinite(got)), f"{what}: non-finite gradient"
+    rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
+    if floor > 0.0 and rms <= 1e-6 * floor:
+        rms = floor
+    if dtype == "bf16":
+        allow = 0.02 * rms + 2.0 ** -8 * np.abs(ref)
+    else:
+        allow = 1e-4 * rms + 1e-5 * np.abs(ref)
+    err = np.abs(got - ref)
+    ratio = float(np.max(err / np.maximum(allow, 1e-30))) if got.size else 0.0
+    _log(what, ratio)
+    assert ratio <= 1.0 or np.all(err == 0), f"{what}: worst error {ratio:.3f} x tolerance (RMS {rms:.3g})"
+
+
+def check_sequences(dtype, o, o_ref, s, s_ref, what):
+    """Element-by-element check of every (b, h) sequence of a full-size call,
+    each against its own output RMS: o, o_ref [B,T,H,V]; s, s_ref [B,H,K,V]
+    (torch tensors on the device or numpy arrays).  The rules are those of
+    check(); batches are converted one at a time to bound host memory.
+    Returns the worst (output, state) error / tolerance ratios."""
+    B, H = o_ref.shape[0], o_ref.shape[2]
+    worst_o = worst_s = 0.0
+    for bb in range(B):
+        ob = to_np(o[bb]) if not isinstance(o, np.ndarray) else np.asarray(o[bb], np.float64)
+        rb = np.asarray(o_ref[bb], np.float64)                      # [T, H, V]
+        sb = to_np(s[bb]) if not isinstance(s, np.ndarray) else np.asarray(s[bb], np.float64)
+        srb = np.asarray(s_ref[bb], np.float64)                     # [H, K, V]
+        assert np.all(np.isfinite(ob)), f"{what} b={bb}: non-finite output"
+        err = np.abs(ob - rb)
+        serr = np.abs(sb - srb).reshape(H, -1).max(axis=1)
+        if dtype == "f32":
+            ro = err.reshape(-1, H, err.shape[-1]).max(axis=(0, 2)) / 1e-4
+            rs = serr / 1e-4
+        else:
+            rms = np.sqrt(np.mean(rb ** 2, axis=(0, 2)))             # per head
+            allow = 0.02 * rms[None, :, None] + 2.0 ** -8 * np.abs(rb)
+            ro = (err / np.maximum(allow, 1e-30)).max(axis=(0, 2)) if rb.shape[0] else np.zeros(H)
+            srms = np.sqrt(np.mean(srb.reshape(H, -1) ** 2, axis=1))
+            rs = np.where(serr == 0.0, 0.0, serr / np.maximum(0.02 * srms, 1e-30))
+        ho, hs = int(np.argmax(ro)), int(np.argmax(rs))
+        assert ro[ho] <= 1.0, f"{what} (b={bb}, h={ho}): worst output error {ro[ho]:.3f} x tolerance"
+        assert rs[hs] <= 1.0, f"{what} (b={bb}, h={hs}): worst state error {rs[hs]:.3f} x tolerance"
+        worst_o, worst_s = max(worst_o, float(ro.max())), max(worst_s, float(rs.max()))
+    _log(what + " o", worst_o)
+    _log(what + " final state", worst_s)
+    return worst_o, worst_s

@@ -9,7 +9,7 @@ import harness as hz
 import oracle
 import rwkv_linear_attention_amd as m
 from rwkv_linear_attention_amd import synth
-from test_bwd_gpu import check_grad
+from harness import check_grad
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu

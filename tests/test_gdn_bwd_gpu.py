@@ -18,7 +18,7 @@ import pytest
 import harness as hz
 import oracle
 from rwkv_linear_attention_amd import synth, wkv7
-from test_bwd_gpu import check_grad
+from harness import check_grad
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu

@@ -1,10 +1,9 @@
 """GPU parity: the HIP kernels (through the C ABI) against the fp64 oracle.
 
 Inputs come from the seeded generator shared by both sides; the oracle sees
-exactly the values the GPU sees (already rounded to the I/O dtype).  Small
-cases are compared element by element over every output; the full-size
-workloads are compared on sampled (b, h) sequences that the oracle evaluates
-one by one.
+exactly the values the GPU sees (already rounded to the I/O dtype).  Every case
+is compared element by element over every output, the full-size workloads
+included (every (b, h) sequence, each against its own output RMS).
 """
 import numpy as np
 import pytest
@@ -46,63 +45,63 @@ def sampled_pairs(B, H):
 
 
 @pytest.mark.parametrize("idx", [2, 3])
-def test_full_size_workload_sampled(idx):
+def test_full_size_workload_all_sequences(idx):
     """Full-size workloads in the launch configuration the benchmark times
-    (ALGO_AUTO -> chunked kernel), checked on sampled sequences."""
+    (ALGO_AUTO -> chunked kernel): o and the final state of every (b, h)
+    sequence against the oracle (one OpenMP pass over all sequences)."""
     inp = synth.make(idx)
     B, T, H, D = inp["r"].shape
     assert wkv7.fwd_path(torch.bfloat16, B, T, H, D, D) == CHK
     dev = hz.to_dev(inp)
     o, sf = hz.gpu_fwd(dev)
     torch.cuda.synchronize()
-    pairs = sampled_pairs(B, H)
-    refs = hz.oracle_fwd(inp, pairs)
-    for (bb, h), (o_ref, s_ref) in zip(pairs, refs):
-        hz.check("bf16", hz.to_np(o[bb, :, h]), o_ref, hz.to_np(sf[bb, h]), s_ref,
-                 f"workload {idx} (b={bb}, h={h})")
-    assert torch.isfinite(o.float()).all()
+    del dev
+    o_ref, s_ref = hz.oracle_fwd(inp)
+    wo, ws = hz.check_sequences("bf16", o, o_ref, sf, s_ref, f"workload {idx} all sequences")
+    print(f"workload {idx}: worst output ratio {wo:.3f}, worst state ratio {ws:.3f}")
 
 
-def test_full_size_fp32_recurrent_sampled():
-    """The workload-2 shape (B8 T4096 H64 d64) with fp32 I/O, which always
-    takes the recurrent kernel, as the benchmark times it; checked on sampled
-    sequences against the fp32 rule (max-abs 1e-4)."""
+def test_full_size_fp32_recurrent_all_sequences():
+    """The workload-2 shape (B8 T4096 H64 d64) with fp32 I/O, as the
+    benchmark times it under ALGO_AUTO; every sequence against the fp32 rule
+    (max-abs 1e-4 on o and the final state)."""
     inp = dict(synth.make(2), dtype="f32")
     B, T, H, D = inp["r"].shape
-    assert wkv7.fwd_path(torch.float32, B, T, H, D, D) == REC
     dev = hz.to_dev(inp)
     o, sf = hz.gpu_fwd(dev)
     torch.cuda.synchronize()
-    pairs = sampled_pairs(B, H)
-    refs = hz.oracle_fwd(inp, pairs)
-    for (bb, h), (o_ref, s_ref) in zip(pairs, refs):
-        hz.check("f32", hz.to_np(o[bb, :, h]), o_ref, hz.to_np(sf[bb, h]), s_ref,
-                 f"fp32 workload-2 shape (b={bb}, h={h})")
+    del dev
+    o_ref, s_ref = hz.oracle_fwd(inp)
+    wo, ws = hz.check_sequences("f32", o, o_ref, sf, s_ref, "fp32 workload-2 shape all sequences")
+    print(f"fp32 B8 T4096 H64 d64: worst output ratio {wo:.3f}, worst state ratio {ws:.3f}")
 
 
-def test_workload4_decode_steps_sampled():
-    """256 consecutive wkv7_step calls on B=512, H=40, d=64 (state in place),
-    checked on sampled sequences against 256 oracle steps."""
+def test_workload4_decode_steps_all_sequences():
+    """256 consecutive wkv7_step calls on B=512, H=40, d=64 (state in
+    place).  Every output of every step and all 20480 final states are
+    compared with the oracle's forward over the same 256 tokens (a step loop
+    equals the forward, pinned on the oracle); two sequences are also
+    replayed step by step through the oracle's own step function."""
     inp = synth.make(4)
     B, T, H, D = inp["r"].shape
     dev = hz.to_dev(inp)
     state = dev["s0"].clone()
-    pairs = sampled_pairs(B, H)
-    o_hist = []
+    o_all = torch.empty((B, T, H, D), dtype=torch.bfloat16, device="cuda")
     for t in range(T):
-        o = wkv7.step(*(dev[n][:, t].contiguous() for n in hz.ARRAYS), state)
-        o_hist.append(torch.stack([o[bb, h] for bb, h in pairs]).float().cpu())
+        o_all[:, t] = wkv7.step(*(dev[n][:, t].contiguous() for n in hz.ARRAYS), state)
     torch.cuda.synchronize()
-    o_hist = torch.stack(o_hist, 1).numpy().astype(np.float64)    # [pairs, T, V]
-    for pi, (bb, h) in enumerate(pairs):
+    o_ref, s_ref = hz.oracle_fwd(inp)
+    wo, ws = hz.check_sequences("bf16", o_all, o_ref, state, s_ref, "decode 256 steps all sequences")
+    print(f"decode: worst output ratio {wo:.3f}, worst state ratio {ws:.3f}")
+    for bb, h in ((0, 0), (B - 1, H - 1)):
         S = inp["s0"][bb:bb + 1, h:h + 1].astype(np.float64)
-        o_ref = np.zeros((T, D))
+        o_step = np.zeros((T, D))
         for t in range(T):
             sl = lambda n: inp[n][bb:bb + 1, t, h:h + 1]
             ot, S = oracle.step(sl("r"), sl("w"), sl("k"), sl("v"), sl("a"), sl("b"), S)
-            o_ref[t] = ot[0, 0]
-        hz.check("bf16", o_hist[pi], o_ref, hz.to_np(state[bb, h]), S[0, 0],
-                 f"decode (b={bb}, h={h})")
+            o_step[t] = ot[0, 0]
+        hz.check("bf16", hz.to_np(o_all[bb, :, h]), o_step, hz.to_np(state[bb, h]), S[0, 0],
+                 f"decode step oracle (b={bb}, h={h})")
 
 
 # ---- shapes, tails and both kernels -----------------------------------------

@@ -9,7 +9,7 @@ import pytest
 import harness as hz
 import oracle
 from rwkv_linear_attention_amd import synth, wkv7
-from test_bwd_gpu import check_grad
+from harness import check_grad
 
 
 def grad_scale(ref, names):
