@@ -340,8 +340,10 @@ def varlen_workload(steps, warmup):
     # the backward of the same packed forward (seeded N(0, 1) output gradient)
     d_o = synth.to_torch(synth.round_to(rng.standard_normal((TT, H, D), dtype=np.float32), "bf16"), "bf16", "cuda")
     ws = torch.empty(wkv7.bwd_varlen_workspace_bytes(N, TT, H, D, D), dtype=torch.uint8, device="cuda")
+    gbuf = {n: torch.empty_like(dev[n]) for n in ("r", "w", "k", "v", "a", "b")}
+    gbuf["s0"] = torch.empty((N, H, D, D), dtype=torch.float32, device="cuda")
     ms = _time_launches(lambda i: wkv7.bwd_varlen(*(dev[n] for n in ("r", "w", "k", "v", "a", "b")), cu, d_o,
-                                                  initial_state=pool, state_map=smap, workspace=ws),
+                                                  initial_state=pool, state_map=smap, workspace=ws, out=gbuf),
                         max(3, steps // 4), max(1, warmup // 4))
     tok = TT * H * D * 2
     nbytes = 7 * tok + 6 * tok + 2 * N * H * D * D * 4

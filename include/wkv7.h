@@ -28,8 +28,9 @@
  *     call, so they work on a machine without a GPU.  Data values are not
  *     inspected: NaN / Inf propagate.
  *   - Supported sizes: K == V, K in {64, 128}.
- *   - Thread safety: the library holds no mutable global state; concurrent
- *     calls on different streams are independent.
+ *   - Thread safety: the library holds no mutable global state apart from
+ *     the wait-limit test hook (wkv7_set_wait_limit); concurrent calls on
+ *     different streams are independent.
  */
 #ifndef WKV7_H
 #define WKV7_H
@@ -67,13 +68,19 @@ typedef enum {
  *   K, V           key and value head size; K == V in {64, 128}.
  *   r,w,k,a,b      [B,T,H,K] dtype (seq-first layout).  Read only.
  *   v              [B,T,H,V] dtype.  Read only.
- *   initial_state  [B,H,K,V] fp32, or NULL for a zero state.  Read only.
+ *   initial_state  [n_state,H,K,V] fp32, or NULL for a zero state.  Read
+ *                  only.  n_state = 1 is one state shared by all B
+ *                  sequences (the (1,H,K,V) initial state of the rwkv-ops
+ *                  README argument tables, sections "gdn_recurrent 使用方法"
+ *                  and "rwkv7op_sane 使用方法").
+ *   n_state        B or 1 when initial_state is given; ignored otherwise.
  *   mask           [B,T] uint8 (nonzero = update, 0 = keep), or NULL for
  *                  all tokens updating.  Read only.
  *   o              [B,T,H,V] dtype.  Written (every element).
  *   final_state    [B,H,K,V] fp32, or NULL to skip it.  Written.  It may be
- *                  the same buffer as initial_state (in-place state passing);
- *                  any other overlap between buffers is undefined.
+ *                  the same buffer as initial_state (in-place state passing)
+ *                  when n_state == B (or B == 1); any other overlap between
+ *                  buffers is undefined.
  *   algo           WKV7_ALGO_AUTO picks the chunked kernel for bf16 when the
  *                  sequences are long enough to amortise it and the
  *                  recurrent kernel otherwise; fp32 always runs the recurrent
@@ -81,12 +88,12 @@ typedef enum {
  *                  WKV7_ERR_UNSUPPORTED.
  *   stream         hipStream_t to enqueue on.
  * With T == 0, o is empty and final_state (if given) receives initial_state
- * (zeros when initial_state is NULL).
+ * in every row (zeros when initial_state is NULL).
  */
 wkv7_status_t wkv7_fwd(int dtype, int B, int T, int H, int K, int V,
                        const void *r, const void *w, const void *k,
                        const void *v, const void *a, const void *b,
-                       const float *initial_state, const uint8_t *mask,
+                       const float *initial_state, int n_state, const uint8_t *mask,
                        void *o, float *final_state, int algo, void *stream);
 
 /*
@@ -117,15 +124,19 @@ wkv7_status_t wkv7_fwd(int dtype, int B, int T, int H, int K, int V,
  *   state_map      DEVICE int32 [N], 4-byte aligned, or NULL.  Sequence n
  *                  starts from pool row state_map[n]; an entry outside
  *                  [0, n_state) means a zero state.  NULL means row n, which
- *                  requires n_state == N when initial_state is given.
+ *                  requires n_state == N, or n_state == 1 (one row shared
+ *                  by every sequence), when initial_state is given.
  *   mask           [total_T] uint8 (nonzero = update), or NULL.
  *   o              [total_T,H,V] dtype.  Written at every token of every
  *                  sequence (tokens outside all sequences are not written).
  *   final_state    [N,H,K,V] fp32, or NULL.  Written.  May alias
- *                  initial_state only when state_map is NULL.
- *   algo           as for wkv7_fwd; under AUTO (bf16) the chunked kernel is
- *                  chosen when the mean sequence length total_T / N is at
- *                  least 16.
+ *                  initial_state only when state_map is NULL and the pool
+ *                  has a row per sequence.
+ *   algo           as for wkv7_fwd; under AUTO with bf16 the chunked kernel
+ *                  takes every packed batch with total_T > 0 (the lengths
+ *                  are on the device, so the choice cannot depend on them,
+ *                  and a batch of short sequences costs the chunked kernel
+ *                  no more than the recurrent one beyond call overhead).
  *   stream         hipStream_t to enqueue on.
  */
 wkv7_status_t wkv7_fwd_varlen(int dtype, int N, int total_T, int H, int K, int V,
@@ -204,32 +215,39 @@ wkv7_status_t wkv7_gdn_fwd_varlen(int dtype, int N, int total_T, int H, int K, i
  *                  and of the gradients dr..db.
  *   B,T,H,K,V      as for wkv7_fwd; K == V in {64, 128}.
  *   r,w,k,v,a,b    the forward's inputs, as for wkv7_fwd.  Read only.
- *   initial_state  [B,H,K,V] fp32 or NULL (zeros).  Read only.
+ *   initial_state  [n_state,H,K,V] fp32 or NULL (zeros).  Read only.
+ *   n_state        B or 1 (one state shared by all B sequences) when
+ *                  initial_state is given; ignored otherwise.
  *   mask           [B,T] uint8 or NULL.  Read only.
  *   d_o            [B,T,H,V] dtype.  Read only.
  *   d_final_state  [B,H,K,V] fp32 or NULL (zero).  Read only.
  *   dr,dw,dk,da,db [B,T,H,K] dtype; dv [B,T,H,V] dtype.  Written (every element).
- *   d_initial_state [B,H,K,V] fp32 or NULL (not written).  Written.
+ *   d_initial_state [n_state,H,K,V] fp32 ([B,H,K,V] without initial_state:
+ *                  the gradient of the zero start) or NULL (not written).
+ *                  Written.  With a shared state it is the sum over the B
+ *                  sequences, taken in sequence order (deterministic).
  *   workspace      DEVICE buffer of at least wkv7_bwd_workspace_bytes(B,T,H,K,V)
  *                  bytes, 16-byte aligned, owned by the caller; contents on
  *                  entry are ignored and on return are unspecified.  May be
  *                  NULL when T == 0.
  *   stream         hipStream_t to enqueue on.
  * Output buffers must not overlap any input or each other.  With T == 0,
- * d_initial_state receives d_final_state (zeros when NULL).
+ * d_initial_state receives d_final_state (summed over B for a shared state;
+ * zeros when NULL).
  */
 wkv7_status_t wkv7_bwd(int dtype, int B, int T, int H, int K, int V,
                        const void *r, const void *w, const void *k,
                        const void *v, const void *a, const void *b,
-                       const float *initial_state, const uint8_t *mask,
+                       const float *initial_state, int n_state, const uint8_t *mask,
                        const void *d_o, const float *d_final_state,
                        void *dr, void *dw, void *dk, void *dv, void *da, void *db,
                        float *d_initial_state, void *workspace, size_t workspace_bytes,
                        void *stream);
 
 /* Workspace bytes wkv7_bwd needs: 4 B 2 ceil(T/16) H K V (two fp32 states
- * per 16-token chunk and sequence), or 0 for arguments wkv7_bwd would
- * reject. */
+ * per 16-token chunk and sequence) rounded up to a multiple of 256, plus
+ * 4 B H K V (per-sequence gradients of a shared initial state), or 0 for
+ * arguments wkv7_bwd would reject. */
 size_t wkv7_bwd_workspace_bytes(int B, int T, int H, int K, int V);
 
 /*
@@ -408,7 +426,28 @@ const char *wkv7_strerror(int status);
  * would be rejected.  Host only; launches nothing. */
 int wkv7_fwd_path(int dtype, int B, int T, int H, int K, int V, int algo);
 
-/* ABI version of this header (major * 100 + minor): 101 adds wkv7_fwd_varlen,
+/*
+ * wkv7_set_wait_limit -- test hook for the failure path of the chunked
+ * forward.  Its producer and consumer waves hand chunks over through
+ * counters in on-chip memory, and every wait on a counter is bounded: after
+ * `polls` polls (default 2^20, about 30 ms) the wave gives up rather than
+ * hang the GPU.  A give-up is made visible in the results: the affected
+ * sequence's state becomes NaN, so the output rows of the chunk being
+ * processed, every later output and its final_state are NaN.
+ *
+ *   polls   new limit for launches made after this call: 0 gives up at once
+ *           (every wait fails, so every chunked output is NaN), a negative
+ *           value restores the default.
+ * Returns the previous limit.  This is the one piece of mutable state in
+ * the library (process-wide, read at each chunked launch); it is meant for
+ * tests that force the give-up from the host, and normal use never calls it.
+ */
+int wkv7_set_wait_limit(int polls);
+
+/* ABI version of this header (major * 100 + minor): 200 adds n_state (a
+ * broadcast initial state) to wkv7_fwd and wkv7_bwd, accepts a one-row pool
+ * without state_map in wkv7_fwd_varlen and wkv7_bwd_varlen, and adds
+ * wkv7_set_wait_limit; earlier: 101 adds wkv7_fwd_varlen,
  * 102 adds wkv7_gdn_fwd, 103 adds wkv7_bwd and wkv7_bwd_workspace_bytes,
  * 104 adds wkv7_gdn_step, 105 adds wkv7_gdn_fwd_varlen, 106 adds wkv7_gdn_bwd and
  * wkv7_gdn_bwd_workspace_bytes, 107 adds wkv7_bwd_varlen and

@@ -86,14 +86,16 @@ class _GeneralizedDeltaRulePacked(torch.autograd.Function):
 def generalized_delta_rule(r, w, k, v, a, b, initial_state=None, output_final_state=True, head_first=False,
                            mask=None, cu_seqlens=None, state_map=None):
     """WKV7 generalized delta rule with gradients.  r, w, k, a, b: [B,T,H,K];
-    v: [B,T,H,V] (float32 or bfloat16); initial_state: [B,H,K,V] float32 or
-    None; mask: [B,T] (nonzero = update) or None.  Returns (o, final_state or
+    v: [B,T,H,V] (float32 or bfloat16); initial_state: [B,H,K,V] float32,
+    [1,H,K,V] (one state shared by every sequence; its gradient is the sum
+    over them) or None; mask: [B,T] (nonzero = update) or None.  Returns (o, final_state or
     None); gradients flow to r, w, k, v, a, b and initial_state.
 
     Packed sequences: with cu_seqlens (int32 [N+1] token offsets) the inputs
     are [1,T,H,K] (N sequences back to back), mask is [T] or [1,T],
-    initial_state is [N,H,K,V] or, with state_map (int32 [N]), a pool of
-    rows; final_state is [N,H,K,V]."""
+    initial_state is [N,H,K,V], [1,H,K,V] (shared) or, with state_map
+    (int32 [N]), a pool of rows; final_state is [N,H,K,V].  Tokens outside
+    every sequence get a zero output and zero gradients."""
     _head_first(head_first)
     _require_device([("r", r), ("w", w), ("k", k), ("v", v), ("a", a), ("b", b),
                      ("initial_state", initial_state), ("mask", mask), ("cu_seqlens", cu_seqlens),

@@ -2,6 +2,8 @@
 // Declarations and the contract of every entry point: include/wkv7.h.
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/wkv7.h"
 #include "wkv7_common.hpp"
 #include "wkv7_internal.hpp"
@@ -38,11 +40,32 @@ int choose_path(int dtype, int T, int algo)
     return T >= kChunkedMinT ? WKV7_ALGO_CHUNKED : WKV7_ALGO_RECURRENT;
 }
 
+// Packed sequences: the lengths live on the device, so AUTO cannot look at
+// them.  With bf16 the chunked kernel takes any packed batch that has
+// tokens: per sequence it is as fast as the recurrent kernel within call
+// overhead below 16 tokens and faster from 16 on, so one long sequence among
+// many short ones (a mean length under 16) still runs at chunked speed.
+int choose_packed_path(int dtype, int total_T, int N, int algo)
+{
+    if (algo == WKV7_ALGO_AUTO && dtype == WKV7_BF16)
+        return total_T > 0 ? WKV7_ALGO_CHUNKED : WKV7_ALGO_RECURRENT;
+    return choose_path(dtype, total_T / N, algo);
+}
+
+std::atomic<int> g_wait_limit{wkv7::kDefaultWaitLimit};
+
 }  // namespace
+
+int wkv7::current_wait_limit() { return g_wait_limit.load(std::memory_order_relaxed); }
 
 extern "C" {
 
-int wkv7_version(void) { return 108; }
+int wkv7_set_wait_limit(int polls)
+{
+    return g_wait_limit.exchange(polls < 0 ? wkv7::kDefaultWaitLimit : polls);
+}
+
+int wkv7_version(void) { return 200; }
 
 const char *wkv7_strerror(int status)
 {
@@ -64,7 +87,7 @@ int wkv7_fwd_path(int dtype, int B, int T, int H, int K, int V, int algo)
 wkv7_status_t wkv7_fwd(int dtype, int B, int T, int H, int K, int V,
                        const void *r, const void *w, const void *k,
                        const void *v, const void *a, const void *b,
-                       const float *initial_state, const uint8_t *mask,
+                       const float *initial_state, int n_state, const uint8_t *mask,
                        void *o, float *final_state, int algo, void *stream)
 {
     wkv7_status_t st = check_common(dtype, B, H, K, V);
@@ -78,7 +101,12 @@ wkv7_status_t wkv7_fwd(int dtype, int B, int T, int H, int K, int V,
         for (const void *p : req)
             if (!p || !aligned16(p)) return WKV7_ERR_INVALID_ARG;
     }
-    if (initial_state && !aligned16(initial_state)) return WKV7_ERR_INVALID_ARG;
+    if (initial_state) {
+        if (!aligned16(initial_state)) return WKV7_ERR_INVALID_ARG;
+        if (n_state != 1 && n_state != B) return WKV7_ERR_INVALID_ARG;
+        // a shared state is read by every sequence: writing finals over it races
+        if (n_state == 1 && B > 1 && final_state == initial_state) return WKV7_ERR_INVALID_ARG;
+    }
     if (final_state && !aligned16(final_state)) return WKV7_ERR_INVALID_ARG;
     const int path = choose_path(dtype, T, algo);
     if (path < 0) return WKV7_ERR_UNSUPPORTED;
@@ -86,11 +114,17 @@ wkv7_status_t wkv7_fwd(int dtype, int B, int T, int H, int K, int V,
     hipStream_t s = (hipStream_t)stream;
     if (T == 0) {
         if (!final_state) return WKV7_OK;
-        const size_t n = (size_t)B * H * K * V;
-        return wkv7::launch_state_copy(initial_state, final_state, n, s) == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
+        if (!initial_state || n_state == B)
+            return wkv7::launch_state_copy(initial_state, final_state, (size_t)B * H * K * V, s) == hipSuccess
+                       ? WKV7_OK : WKV7_ERR_HIP;
+        const size_t one = (size_t)H * K * V;
+        for (int i = 0; i < B; ++i)
+            if (wkv7::launch_state_copy(initial_state, final_state + i * one, one, s) != hipSuccess)
+                return WKV7_ERR_HIP;
+        return WKV7_OK;
     }
     wkv7::FwdArgs args{B, T, H, K, r, w, k, v, a, b, initial_state, mask, o, final_state};
-    args.n_state = B;
+    args.n_state = initial_state ? n_state : 0;
     hipError_t e = path == WKV7_ALGO_CHUNKED ? wkv7::launch_chunked(args, s)
                                              : wkv7::launch_recurrent(dtype, args, s);
     return e == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
@@ -119,12 +153,12 @@ wkv7_status_t wkv7_fwd_varlen(int dtype, int N, int total_T, int H, int K, int V
     }
     if (initial_state) {
         if (!aligned16(initial_state) || n_state < 1) return WKV7_ERR_INVALID_ARG;
-        if (!state_map && n_state != N) return WKV7_ERR_INVALID_ARG;
-        if (state_map && final_state == initial_state) return WKV7_ERR_INVALID_ARG;
+        if (!state_map && n_state != N && n_state != 1) return WKV7_ERR_INVALID_ARG;
+        // a pool read through a map, or one shared row, may not be overwritten
+        if ((state_map || (n_state == 1 && N > 1)) && final_state == initial_state) return WKV7_ERR_INVALID_ARG;
     }
     if (final_state && !aligned16(final_state)) return WKV7_ERR_INVALID_ARG;
-    // Mean length decides AUTO (the lengths themselves live on the device).
-    const int path = choose_path(dtype, total_T / N, algo);
+    const int path = choose_packed_path(dtype, total_T, N, algo);
     if (path < 0) return WKV7_ERR_UNSUPPORTED;
     wkv7::FwdArgs args{N, total_T, H, K, r, w, k, v, a, b, initial_state, mask, o, final_state};
     args.cu_seqlens = cu_seqlens;
@@ -212,7 +246,7 @@ wkv7_status_t wkv7_gdn_fwd_varlen(int dtype, int N, int total_T, int H, int K, i
         if ((state_map || (n_state == 1 && N > 1)) && final_state == initial_state) return WKV7_ERR_INVALID_ARG;
     }
     if (final_state && !aligned16(final_state)) return WKV7_ERR_INVALID_ARG;
-    const int path = choose_path(dtype, total_T / N, algo);
+    const int path = choose_packed_path(dtype, total_T, N, algo);
     if (path < 0) return WKV7_ERR_UNSUPPORTED;
     wkv7::FwdArgs args{N, total_T, H, K, q, g, k, v, beta, nullptr, initial_state, nullptr, o, final_state};
     args.cu_seqlens = cu_seqlens;
@@ -234,7 +268,7 @@ size_t wkv7_bwd_workspace_bytes(int B, int T, int H, int K, int V)
 wkv7_status_t wkv7_bwd(int dtype, int B, int T, int H, int K, int V,
                        const void *r, const void *w, const void *k,
                        const void *v, const void *a, const void *b,
-                       const float *initial_state, const uint8_t *mask,
+                       const float *initial_state, int n_state, const uint8_t *mask,
                        const void *d_o, const float *d_final_state,
                        void *dr, void *dw, void *dk, void *dv, void *da, void *db,
                        float *d_initial_state, void *workspace, size_t workspace_bytes,
@@ -252,19 +286,31 @@ wkv7_status_t wkv7_bwd(int dtype, int B, int T, int H, int K, int V,
             if (!p || !aligned16(p)) return WKV7_ERR_INVALID_ARG;
         if (workspace_bytes < wkv7::bwd_workspace_bytes(B, T, H, K)) return WKV7_ERR_INVALID_ARG;
     }
+    if (initial_state && n_state != 1 && n_state != B) return WKV7_ERR_INVALID_ARG;
     const void *opt[] = {initial_state, d_final_state, d_initial_state};
     for (const void *p : opt)
         if (p && !aligned16(p)) return WKV7_ERR_INVALID_ARG;
+    const bool shared = initial_state && n_state == 1 && B > 1;
 
     hipStream_t s = (hipStream_t)stream;
     if (T == 0) {
         if (!d_initial_state) return WKV7_OK;
-        const size_t n = (size_t)B * H * K * V;
-        return wkv7::launch_state_copy(d_final_state, d_initial_state, n, s) == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
+        const size_t per = (size_t)H * K * V;
+        hipError_t e = shared ? wkv7::launch_state_sum(d_final_state, d_initial_state, B, per, s)
+                              : wkv7::launch_state_copy(d_final_state, d_initial_state, (size_t)B * per, s);
+        return e == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
     }
+    // A shared initial state's gradient is the sum over the B sequences:
+    // per-sequence gradients go to the workspace's tail, then one ordered sum.
+    float *ds0_rows = shared ? (float *)((char *)workspace + (wkv7::bwd_checkpoint_bytes(B, T, H, K) + 255) / 256 * 256)
+                             : d_initial_state;
     wkv7::BwdArgs args{B, T, H, K, r, w, k, v, a, b, initial_state, mask, d_o, d_final_state,
-                       dr, dw, dk, dv, da, db, d_initial_state, workspace};
-    return wkv7::launch_backward(dtype, args, s) == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
+                       dr, dw, dk, dv, da, db, d_initial_state ? ds0_rows : nullptr, workspace};
+    args.n_state = initial_state ? n_state : 0;
+    hipError_t e = wkv7::launch_backward(dtype, args, s);
+    if (e == hipSuccess && shared && d_initial_state)
+        e = wkv7::launch_state_sum(ds0_rows, d_initial_state, B, (size_t)H * K * V, s);
+    return e == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
 }
 
 size_t wkv7_bwd_varlen_workspace_bytes(int N, int total_T, int H, int K, int V)
@@ -299,7 +345,7 @@ wkv7_status_t wkv7_bwd_varlen(int dtype, int N, int total_T, int H, int K, int V
     }
     if (initial_state) {
         if (n_state < 1) return WKV7_ERR_INVALID_ARG;
-        if (!state_map && n_state != N) return WKV7_ERR_INVALID_ARG;
+        if (!state_map && n_state != N && n_state != 1) return WKV7_ERR_INVALID_ARG;
     }
     if (state_map && ((uintptr_t)state_map & 3)) return WKV7_ERR_INVALID_ARG;
     const void *opt[] = {initial_state, d_final_state, d_initial_state};

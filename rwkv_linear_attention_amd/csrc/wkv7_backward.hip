@@ -53,7 +53,8 @@ namespace {
 constexpr int kL = 16;                  // chunk length (= checkpoint interval)
 constexpr float kMinChunkLogDecay = -60.0f;
 
-// Packed sequences (cu == nullptr: the fixed-length form).  Sequence n owns
+// Packed sequences (cu == nullptr: the fixed-length form, in which
+// n_state == 1 means one initial state shared by every sequence).  Sequence n owns
 // tokens [cu[n], cu[n+1]) of the total_T-token axis, each offset clamped into
 // range as the forward does; its checkpoints are chunks ck_off[n] ..
 // ck_off[n+1] - 1 of the workspace (ck_off saturates at the capacity, so
@@ -851,7 +852,8 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(D == 64 ?
         tok0 = (size_t)bb * T;
         ck0 = (size_t)bh * ((T + kL - 1) / kL);
         nck_store = (T + kL - 1) / kL;
-        if (s0) s0p = s0 + st;
+        // one initial state shared by every sequence: row 0 of the pool
+        if (s0) s0p = vg.n_state == 1 ? s0 + (size_t)h * D * D : s0 + st;
     }
     const int nck = (T + kL - 1) / kL;
     auto ckidx = [&](int c) { return vg.cu ? (ck0 + c) * H + h : ck0 + c; };
@@ -1154,6 +1156,7 @@ hipError_t launch_bwd_d(const BwdArgs &p, hipStream_t stream)
     } else {
         nck = (size_t)(p.T + kL - 1) / kL;
         grid2 = nbh * nck;
+        vg.n_state = p.n_state;
     }
     float *ckpt = (float *)p.ws;
     float *dck = ckpt + (p.cu_seqlens ? nck * p.H : nbh * nck) * D * D;
@@ -1173,10 +1176,18 @@ hipError_t launch_bwd_d(const BwdArgs &p, hipStream_t stream)
 
 }  // namespace
 
-size_t bwd_workspace_bytes(int B, int T, int H, int D)
+size_t bwd_checkpoint_bytes(int B, int T, int H, int D)
 {
     const size_t nck = ((size_t)T + kL - 1) / kL;
     return sizeof(float) * (size_t)B * H * D * D * 2 * nck;
+}
+
+size_t bwd_workspace_bytes(int B, int T, int H, int D)
+{
+    // checkpoints, then per-sequence initial-state gradients (summed into
+    // the gradient of a shared initial state), 256-byte aligned
+    const size_t ck = (bwd_checkpoint_bytes(B, T, H, D) + 255) / 256 * 256;
+    return ck + sizeof(float) * (size_t)B * H * D * D;
 }
 
 long long bwd_varlen_chunk_capacity(int B, int T)

@@ -51,7 +51,6 @@ namespace wkv7 {
 // A chunk whose summed decay factor exp(G_L) falls below e^-60 in any channel
 // would need factors up to e^60 in the split form; it takes the exact path.
 constexpr float kMinChunkFactor = 8.75651076e-27f;   // e^-60
-constexpr int kSpinLimit = 1 << 20;
 
 template <int D> struct WS {
     static_assert(D == 64 || D == 128, "head size");
@@ -161,31 +160,42 @@ __device__ __forceinline__ void lds_store_relaxed(int *p, int v)
 {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
-// Wait until *p >= target; gives up after kSpinLimit polls so that a broken
-// hand-off ends the kernel (with wrong results) instead of hanging it.
-__device__ __forceinline__ int spin_ge(int *p, int target)
+// Wait until *p >= target, polling at most `limit` times.  Returns the last
+// value read: a value below target means the wait gave up (a broken hand-off
+// then ends the kernel instead of hanging it, and the caller poisons its
+// results so that the failure is visible).  *flag is read with every poll
+// (the sequence's failure flag, at no extra round trip).
+__device__ __forceinline__ int spin_ge(int *p, int target, int limit, int *flag, int &flag_value)
 {
-    int v = 0;
-    for (int it = 0; it < kSpinLimit; ++it) {
+    int v = 0, f = 0;
+    for (int it = 0; it < limit; ++it) {
         v = lds_load_relaxed(p);
+        f = lds_load_relaxed(flag);
         if (v >= target) break;
         __builtin_amdgcn_s_sleep(1);
     }
     asm volatile("" ::: "memory");
+    flag_value = f;
     return v;
 }
-// Wait until p[0..n) are all >= target (bounded like spin_ge).
+// Wait until p[0..n) are all >= target (bounded like spin_ge); false if the
+// wait gave up.
 template <int N>
-__device__ __forceinline__ void spin_all_ge(int *p, int target)
+__device__ __forceinline__ bool spin_all_ge(int *p, int target, int limit)
 {
-    for (int it = 0; it < kSpinLimit; ++it) {
+    bool ok = false;
+    for (int it = 0; it < limit; ++it) {
         int v = lds_load_relaxed(p);
 #pragma unroll
         for (int i = 1; i < N; ++i) v = min(v, lds_load_relaxed(p + i));
-        if (v >= target) break;
+        if (v >= target) {
+            ok = true;
+            break;
+        }
         __builtin_amdgcn_s_sleep(1);
     }
     asm volatile("" ::: "memory");
+    return ok;
 }
 
 // ---- global -> LDS staging ----------------------------------------------------
@@ -820,7 +830,7 @@ __attribute__((amdgpu_waves_per_eu(WS<D>::WAVES_PER_SIMD, WS<D>::WAVES_PER_SIMD)
     int n_state, const uint16_t *__restrict__ r, const uint16_t *__restrict__ w,
     const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, const uint16_t *__restrict__ a,
     const uint16_t *__restrict__ b, const float *__restrict__ s0, const uint8_t *__restrict__ mask,
-    uint16_t *__restrict__ o, float *__restrict__ sf)
+    uint16_t *__restrict__ o, float *__restrict__ sf, int wait_limit)
 {
     using C = WS<D>;
     // Separate LDS objects: the compiler must wait for outstanding
@@ -903,9 +913,12 @@ __attribute__((amdgpu_waves_per_eu(WS<D>::WAVES_PER_SIMD, WS<D>::WAVES_PER_SIMD)
     // Per sequence: ready[NSLOT], then one done counter per consumer (a sum
     // over consumers would let a consumer running ahead release a slot that
     // a slower one is still reading).
+    // The eighth counter is the sequence's failure flag: set when a producer
+    // gave up waiting for a slot and overwrote it while it may still be read.
     int *ready = lds_sync + 8 * seq;
     int *done = ready + C::NSLOT;
-    static_assert(C::NSLOT + C::NCONS <= 8, "hand-off counters of one sequence");
+    int *failed = ready + 7;
+    static_assert(C::NSLOT + C::NCONS <= 7, "hand-off counters of one sequence");
 
     if (is_cons) {
         // ---------------- consumer: columns cbase .. cbase + CW - 1 ----------------
@@ -926,11 +939,41 @@ __attribute__((amdgpu_waves_per_eu(WS<D>::WAVES_PER_SIMD, WS<D>::WAVES_PER_SIMD)
                     for (int i = 0; i < 4; ++i)
                         S[q][n][i] = s0[st_in + (size_t)(16 * q + 4 * g + i) * D + cbase + 16 * n + j];
         }
+        // A hand-off that gave up poisons the results: the state becomes NaN
+        // (so every later output and the final state are NaN), and so do the
+        // output rows of a chunk that may have been read from a slot in an
+        // unknown state.  A producer sets the failure flag before it
+        // overwrites a slot that may still be read, so a consumer whose slot
+        // reads for chunk c returned overwritten data sees the flag at its
+        // next poll (the wait for chunk c + 1, or the check after the loop):
+        // the chunk to poison is then the previous one.
+        bool poisoned = false;
+        auto poison = [&](int c_out) {
+#pragma unroll
+            for (int q = 0; q < C::NQ; ++q)
+#pragma unroll
+                for (int n = 0; n < C::NT; ++n) S[q][n] = f32x4{NAN, NAN, NAN, NAN};
+            if (c_out >= 0) {
+                f32x4 Ot[C::NT];
+#pragma unroll
+                for (int n = 0; n < C::NT; ++n) Ot[n] = f32x4{NAN, NAN, NAN, NAN};
+                ws_store_out<D>(Ot, o, tok0, Tn, H, h, c_out, cbase, lane);
+            }
+            poisoned = true;
+        };
         for (int c = 0; c < nchunks; ++c) {
             const char *slot = lds + (c % C::NSLOT) * C::SLOT;
             // ready[slot] = 2 (c + 1) + extreme-decay flag once chunk c is in the slot
-            const int rv = spin_ge(&ready[c % C::NSLOT], 2 * (c + 1));
-            if (rv & 1) {
+            int fail_seen;
+            const int rv = spin_ge(&ready[c % C::NSLOT], 2 * (c + 1), wait_limit, failed, fail_seen);
+            const bool gave_up = rv < 2 * (c + 1);
+            if (__builtin_expect(gave_up || (fail_seen && !poisoned), 0)) {
+                if (gave_up) lds_store_relaxed(failed, 1);
+                // S = NaN, so this chunk's outputs come out NaN; a flag seen
+                // for the first time also poisons the previous chunk
+                poison(fail_seen && !poisoned ? c - 1 : -1);
+            }
+            if (!gave_up && (rv & 1)) {
                 if constexpr (GDN)
                     ws_chunk_exact_gdn<D>(S, r, w, k, v, a, o, tok0, Tn, H, h, c, cbase, lane);
                 else
@@ -940,6 +983,7 @@ __attribute__((amdgpu_waves_per_eu(WS<D>::WAVES_PER_SIMD, WS<D>::WAVES_PER_SIMD)
             lds_wait();                          // all reads of the slot have returned
             lds_store_relaxed(&done[crank / C::NSEQ], c + 1);
         }
+        if (nchunks > 0 && !poisoned && lds_load_relaxed(failed)) poison(nchunks - 1);
         if (sf) {
 #pragma unroll
             for (int q = 0; q < C::NQ; ++q)
@@ -1011,7 +1055,10 @@ __attribute__((amdgpu_waves_per_eu(WS<D>::WAVES_PER_SIMD, WS<D>::WAVES_PER_SIMD)
             ws_precompute<D, GDN>(rt, op, lane, psel, ltri, sc);
             char *slot = lds + (c % C::NSLOT) * C::SLOT;
             // the slot's previous chunk is consumed by every consumer
-            spin_all_ge<C::NCONS>(done, c - C::NSLOT + 1);
+            if (!spin_all_ge<C::NCONS>(done, c - C::NSLOT + 1, wait_limit)) {
+                lds_store_relaxed(failed, 1);
+                lds_wait();                      // flag set before the slot is overwritten
+            }
             ws_issue_v<D>(lds_addr(slot + C::OFF_V), v, seq_base, tok_stride, Tn, c, lane);
             ws_store_ops<D, GDN>(op, slot, lane);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the value tile has landed
@@ -1039,7 +1086,7 @@ static hipError_t launch_ws(const FwdArgs &p, hipStream_t stream)
                        p.state_map, p.n_state,
                        (const uint16_t *)p.r, (const uint16_t *)p.w, (const uint16_t *)p.k,
                        (const uint16_t *)p.v, (const uint16_t *)p.a, (const uint16_t *)p.b, p.s0,
-                       p.mask, (uint16_t *)p.o, p.sf);
+                       p.mask, (uint16_t *)p.o, p.sf, current_wait_limit());
     return hipGetLastError();
 }
 

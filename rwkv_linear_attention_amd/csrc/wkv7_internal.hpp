@@ -6,6 +6,12 @@
 
 namespace wkv7 {
 
+// Polls a wave of the chunked forward makes on a hand-off counter before it
+// gives up and poisons its results with NaN: the default, and the value in
+// force for new launches (set by wkv7_set_wait_limit).
+constexpr int kDefaultWaitLimit = 1 << 20;
+int current_wait_limit();
+
 // Fixed-length form: B sequences of T tokens, [B,T,H,D] arrays,
 // cu_seqlens == state_map == nullptr, n_state == B.  Packed form: B
 // sequences with token ranges [cu_seqlens[n], cu_seqlens[n+1]) of a
@@ -28,7 +34,9 @@ struct FwdArgs {
 
 // Backward (fixed-length form): gradients of the forward for upstream d_o
 // [B,T,H,D] and d_sf [B,H,D,D] (or nullptr); dr..db in the I/O dtype, d_s0
-// fp32 (or nullptr).  ws: workspace of bwd_workspace_bytes(B,T,H,D) bytes.
+// fp32 [B,H,D,D] per sequence (or nullptr), also when n_state == 1 (one
+// initial state shared by every sequence).  ws: workspace of
+// bwd_workspace_bytes(B,T,H,D) bytes.
 struct BwdArgs {
     int B, T, H, D;
     const void *r, *w, *k, *v, *a, *b;
@@ -51,6 +59,10 @@ struct BwdArgs {
     const int32_t *state_map = nullptr;
     int n_state = 0;
 };
+// Fixed-length form: the checkpoints (two fp32 states per 16-token chunk
+// and sequence), then B per-sequence initial-state gradients at a 256-byte
+// aligned offset (used to sum the gradient of a shared initial state).
+size_t bwd_checkpoint_bytes(int B, int T, int H, int D);
 size_t bwd_workspace_bytes(int B, int T, int H, int D);
 // Packed form: chunk capacity ceil(T/16) + B (an upper bound on the sum of
 // the sequences' chunk counts), two fp32 states per chunk and head, then the

@@ -30,13 +30,13 @@ def lib():
                            "or python -m rwkv_linear_attention_amd.build")
     L = ctypes.CDLL(LIB_PATH)
     p, i = ctypes.c_void_p, ctypes.c_int
-    L.wkv7_fwd.argtypes = [i, i, i, i, i, i] + [p] * 10 + [i, p]
+    L.wkv7_fwd.argtypes = [i, i, i, i, i, i] + [p] * 7 + [i] + [p] * 3 + [i, p]
     L.wkv7_fwd.restype = i
     L.wkv7_fwd_varlen.argtypes = [i, i, i, i, i, i, p] + [p] * 7 + [i, p, p, p, p, i, p]
     L.wkv7_fwd_varlen.restype = i
     L.wkv7_gdn_fwd.argtypes = [i, i, i, i, i, i] + [p] * 6 + [i, p, p, i, p]
     L.wkv7_gdn_fwd.restype = i
-    L.wkv7_bwd.argtypes = [i, i, i, i, i, i] + [p] * 18 + [ctypes.c_size_t, p]
+    L.wkv7_bwd.argtypes = [i, i, i, i, i, i] + [p] * 7 + [i] + [p] * 11 + [ctypes.c_size_t, p]
     L.wkv7_bwd.restype = i
     L.wkv7_bwd_workspace_bytes.argtypes = [i] * 5
     L.wkv7_bwd_workspace_bytes.restype = ctypes.c_size_t
@@ -63,6 +63,8 @@ def lib():
     L.wkv7_fwd_path.argtypes = [i] * 7
     L.wkv7_fwd_path.restype = i
     L.wkv7_version.restype = i
+    L.wkv7_set_wait_limit.argtypes = [i]
+    L.wkv7_set_wait_limit.restype = i
     _lib = L
     return L
 
@@ -105,11 +107,12 @@ def _check(t, name, shape, dtype, device):
 def fwd(r, w, k, v, a, b, initial_state=None, mask=None, output_final_state=True,
         algo=ALGO_AUTO, out=None, final_state=None):
     """WKV7 forward.  r, w, k, a, b: [B,T,H,K]; v: [B,T,H,V] (float32 or
-    bfloat16, one device); initial_state: [B,H,K,V] float32 or None (zeros);
-    mask: [B,T] bool/uint8 (nonzero = update) or None.  Returns
-    (o [B,T,H,V] in the input dtype, final_state [B,H,K,V] float32 or None).
-    `final_state` may be passed as an output buffer, including the
-    initial_state tensor itself for in-place state passing."""
+    bfloat16, one device); initial_state: [B,H,K,V] or [1,H,K,V] (shared by
+    every sequence) float32, or None (zeros); mask: [B,T] bool/uint8
+    (nonzero = update) or None.  Returns (o [B,T,H,V] in the input dtype,
+    final_state [B,H,K,V] float32 or None).  `final_state` may be passed as
+    an output buffer, including a [B,H,K,V] initial_state tensor itself for
+    in-place state passing."""
     dev = r.device
     B, T, H, K = r.shape
     V = v.shape[-1]
@@ -118,8 +121,7 @@ def fwd(r, w, k, v, a, b, initial_state=None, mask=None, output_final_state=True
     for name, t in (("r", r), ("w", w), ("k", k), ("a", a), ("b", b)):
         _check(t, name, (B, T, H, K), dt, dev)
     _check(v, "v", (B, T, H, V), dt, dev)
-    if initial_state is not None:
-        _check(initial_state, "initial_state", (B, H, K, V), torch.float32, dev)
+    n_state = _state_rows(initial_state, B, H, K, V, dev)
     m = _mask_u8(mask)
     if m is not None:
         _check(m, "mask", (B, T), torch.uint8, dev)
@@ -130,10 +132,21 @@ def fwd(r, w, k, v, a, b, initial_state=None, mask=None, output_final_state=True
         sf = final_state if final_state is not None else torch.empty((B, H, K, V), dtype=torch.float32, device=dev)
         _check(sf, "final_state", (B, H, K, V), torch.float32, dev)
     st = lib().wkv7_fwd(code, B, T, H, K, V, _ptr(r), _ptr(w), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
-                        _ptr(initial_state), _ptr(m), _ptr(o), _ptr(sf), int(algo), _stream(dev))
+                        _ptr(initial_state), n_state, _ptr(m), _ptr(o), _ptr(sf), int(algo), _stream(dev))
     if st != OK:
         raise WKV7Error(st)
     return o, sf
+
+
+def _state_rows(initial_state, B, H, K, V, dev):
+    """Rows of an initial state with B rows or one shared row (0 for None)."""
+    if initial_state is None:
+        return 0
+    n_state = initial_state.shape[0] if initial_state.dim() == 4 else -1
+    if n_state not in (1, B):
+        raise ValueError(f"initial_state must be [{B} or 1,H,K,V], got {tuple(initial_state.shape)}")
+    _check(initial_state, "initial_state", (n_state, H, K, V), torch.float32, dev)
+    return n_state
 
 
 def _mask_u8(mask):
@@ -152,8 +165,11 @@ def fwd_varlen(r, w, k, v, a, b, cu_seqlens, initial_state=None, state_map=None,
     [T_total,H,K] (or [1,T_total,H,K]); v: [T_total,H,V]; cu_seqlens: int32
     [N+1] token offsets (device); initial_state: [n_state,H,K,V] float32 pool
     or None; state_map: int32 [N] pool row per sequence (out of range: zero
-    state) or None (row n); mask: [T_total] bool/uint8 or None.  Returns
-    (o shaped like v, final_state [N,H,K,V] float32 or None)."""
+    state) or None (row n, or the single row of a one-row pool); mask:
+    [T_total] bool/uint8 or None.  Returns (o shaped like v, final_state
+    [N,H,K,V] float32 or None).  A new o is zero-filled first, so tokens
+    outside every sequence (trailing padding, gaps) read as zeros; a
+    caller-provided `out` keeps whatever it holds there."""
     dev = r.device
     lead1 = r.dim() == 4
     if lead1:
@@ -183,7 +199,7 @@ def fwd_varlen(r, w, k, v, a, b, cu_seqlens, initial_state=None, state_map=None,
     if out is not None:
         o = out.squeeze(0) if (lead1 and out.dim() == 4) else out
     else:
-        o = torch.empty((TT, H, V), dtype=dt, device=dev)
+        o = torch.zeros((TT, H, V), dtype=dt, device=dev)
     _check(o, "out", (TT, H, V), dt, dev)
     sf = None
     if output_final_state:
@@ -208,7 +224,9 @@ def bwd(r, w, k, v, a, b, d_o, initial_state=None, mask=None, d_final_state=None
     dtype; d_final_state: [B,H,K,V] float32 or None.  workspace: a uint8
     device tensor of at least bwd_workspace_bytes(...) bytes, or None to
     allocate one.  Returns a dict with r, w, k, v, a, b (input dtype) and s0
-    ([B,H,K,V] float32, or None when need_initial_state_grad is False)."""
+    (float32, shaped like initial_state, [B,H,K,V] without one: for a shared
+    [1,H,K,V] state the sum over the sequences; None when
+    need_initial_state_grad is False)."""
     dev = r.device
     B, T, H, K = r.shape
     V = v.shape[-1]
@@ -218,8 +236,7 @@ def bwd(r, w, k, v, a, b, d_o, initial_state=None, mask=None, d_final_state=None
         _check(t, name, (B, T, H, K), dt, dev)
     _check(v, "v", (B, T, H, V), dt, dev)
     _check(d_o, "d_o", (B, T, H, V), dt, dev)
-    if initial_state is not None:
-        _check(initial_state, "initial_state", (B, H, K, V), torch.float32, dev)
+    n_state = _state_rows(initial_state, B, H, K, V, dev)
     if d_final_state is not None:
         _check(d_final_state, "d_final_state", (B, H, K, V), torch.float32, dev)
     m = _mask_u8(mask)
@@ -232,9 +249,10 @@ def bwd(r, w, k, v, a, b, d_o, initial_state=None, mask=None, d_final_state=None
         raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
     g = {n: torch.empty((B, T, H, K), dtype=dt, device=dev) for n in ("r", "w", "k", "a", "b")}
     g["v"] = torch.empty((B, T, H, V), dtype=dt, device=dev)
-    g["s0"] = torch.empty((B, H, K, V), dtype=torch.float32, device=dev) if need_initial_state_grad else None
+    g["s0"] = (torch.empty((n_state or B, H, K, V), dtype=torch.float32, device=dev)
+               if need_initial_state_grad else None)
     st = lib().wkv7_bwd(code, B, T, H, K, V, _ptr(r), _ptr(w), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
-                        _ptr(initial_state), _ptr(m), _ptr(d_o), _ptr(d_final_state),
+                        _ptr(initial_state), n_state, _ptr(m), _ptr(d_o), _ptr(d_final_state),
                         *(_ptr(g[n]) for n in ("r", "w", "k", "v", "a", "b", "s0")),
                         _ptr(workspace), workspace.numel(), _stream(dev))
     if st != OK:
@@ -248,12 +266,15 @@ def bwd_varlen_workspace_bytes(N, total_T, H, K, V):
 
 
 def bwd_varlen(r, w, k, v, a, b, cu_seqlens, d_o, initial_state=None, state_map=None, mask=None,
-               d_final_state=None, workspace=None, need_initial_state_grad=True):
+               d_final_state=None, workspace=None, need_initial_state_grad=True, out=None):
     """Gradients of fwd_varlen.  Inputs as for fwd_varlen ([T_total,H,K] or
     [1,T_total,H,K]); d_o shaped like v; d_final_state: [N,H,K,V] float32 or
     None.  Returns a dict with r, w, k, v, a, b (shaped like the inputs;
-    tokens outside every sequence are left as allocated) and s0 ([N,H,K,V]
-    float32: the gradient of each sequence's initial state, or None)."""
+    zero at tokens outside every sequence, which the forward does not read)
+    and s0 ([N,H,K,V] float32: the gradient of each sequence's initial
+    state, or None).  out: optional dict of preallocated gradient tensors
+    (r, w, k, v, a, b as [T_total,...], s0), used as they are: tokens outside
+    every sequence keep what they hold."""
     dev = r.device
     lead1 = r.dim() == 4
     if lead1:
@@ -288,9 +309,19 @@ def bwd_varlen(r, w, k, v, a, b, cu_seqlens, d_o, initial_state=None, state_map=
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     elif workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
-    g = {n: torch.empty((TT, H, K), dtype=dt, device=dev) for n in ("r", "w", "k", "a", "b")}
-    g["v"] = torch.empty((TT, H, V), dtype=dt, device=dev)
-    g["s0"] = torch.empty((N, H, K, V), dtype=torch.float32, device=dev) if need_initial_state_grad else None
+    if out is not None:
+        g = dict(out)
+        for n in ("r", "w", "k", "a", "b"):
+            _check(g[n], "out[" + n + "]", (TT, H, K), dt, dev)
+        _check(g["v"], "out[v]", (TT, H, V), dt, dev)
+        if not need_initial_state_grad:
+            g["s0"] = None
+        elif g.get("s0") is not None:
+            _check(g["s0"], "out[s0]", (N, H, K, V), torch.float32, dev)
+    else:
+        g = {n: torch.zeros((TT, H, K), dtype=dt, device=dev) for n in ("r", "w", "k", "a", "b")}
+        g["v"] = torch.zeros((TT, H, V), dtype=dt, device=dev)
+        g["s0"] = torch.empty((N, H, K, V), dtype=torch.float32, device=dev) if need_initial_state_grad else None
     st = lib().wkv7_bwd_varlen(code, N, TT, H, K, V, _ptr(cu_seqlens), _ptr(r), _ptr(w), _ptr(k), _ptr(v),
                                _ptr(a), _ptr(b), _ptr(initial_state), n_state, _ptr(state_map), _ptr(m),
                                _ptr(d_o), _ptr(d_final_state),
@@ -424,7 +455,7 @@ def gdn_fwd_varlen(q, k, v, g, beta, cu_seqlens, initial_state=None, state_map=N
     if out is not None:
         o = out.squeeze(0) if (lead1 and out.dim() == 4) else out
     else:
-        o = torch.empty((TT, H, V), dtype=dt, device=dev)
+        o = torch.zeros((TT, H, V), dtype=dt, device=dev)
     _check(o, "out", (TT, H, V), dt, dev)
     sf = None
     if output_final_state:
@@ -442,8 +473,9 @@ def gdn_bwd_varlen(q, k, v, g, beta, cu_seqlens, d_o, initial_state=None, state_
                    workspace=None, need_initial_state_grad=True):
     """Gradients of gdn_fwd_varlen.  Inputs as for gdn_fwd_varlen; d_o
     shaped like v; d_final_state: [N,H,K,V] float32 or None.  Returns a dict
-    with q, k, v, g, beta (shaped like the inputs) and s0 ([N,H,K,V] float32:
-    the gradient of each sequence's initial state, or None)."""
+    with q, k, v, g, beta (shaped like the inputs; zero at tokens outside
+    every sequence) and s0 ([N,H,K,V] float32: the gradient of each
+    sequence's initial state, or None)."""
     dev = q.device
     lead1 = q.dim() == 4
     if lead1:
@@ -476,9 +508,9 @@ def gdn_bwd_varlen(q, k, v, g, beta, cu_seqlens, d_o, initial_state=None, state_
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     elif workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
-    out = {"q": torch.empty((TT, H, K), dtype=dt, device=dev), "k": torch.empty((TT, H, K), dtype=dt, device=dev),
-           "v": torch.empty((TT, H, V), dtype=dt, device=dev), "g": torch.empty((TT, H), dtype=dt, device=dev),
-           "beta": torch.empty((TT, H), dtype=dt, device=dev)}
+    out = {"q": torch.zeros((TT, H, K), dtype=dt, device=dev), "k": torch.zeros((TT, H, K), dtype=dt, device=dev),
+           "v": torch.zeros((TT, H, V), dtype=dt, device=dev), "g": torch.zeros((TT, H), dtype=dt, device=dev),
+           "beta": torch.zeros((TT, H), dtype=dt, device=dev)}
     out["s0"] = torch.empty((N, H, K, V), dtype=torch.float32, device=dev) if need_initial_state_grad else None
     st = lib().wkv7_gdn_bwd_varlen(code, N, TT, H, K, V, _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                    _ptr(beta), _ptr(initial_state), n_state, _ptr(state_map), _ptr(d_o),
@@ -550,3 +582,11 @@ def step(r, w, k, v, a, b, state, out=None):
 def fwd_path(dtype, B, T, H, K, V, algo=ALGO_AUTO):
     """Kernel wkv7_fwd would launch (ALGO_RECURRENT / ALGO_CHUNKED), or -1."""
     return lib().wkv7_fwd_path(_dtype_code(dtype), B, T, H, K, V, int(algo))
+
+
+def set_wait_limit(polls):
+    """Test hook (wkv7_set_wait_limit): polls a chunked-forward wave makes on
+    a hand-off counter before it gives up and poisons its results with NaN;
+    0 gives up at once, a negative value restores the default.  Returns the
+    previous limit."""
+    return int(lib().wkv7_set_wait_limit(int(polls)))

@@ -28,13 +28,13 @@ def declared_functions():
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert {"wkv7_fwd", "wkv7_fwd_varlen", "wkv7_gdn_fwd", "wkv7_bwd", "wkv7_bwd_workspace_bytes", "wkv7_gdn_step", "wkv7_gdn_fwd_varlen", "wkv7_gdn_bwd", "wkv7_gdn_bwd_workspace_bytes", "wkv7_bwd_varlen", "wkv7_bwd_varlen_workspace_bytes", "wkv7_gdn_bwd_varlen", "wkv7_gdn_bwd_varlen_workspace_bytes", "wkv7_step", "wkv7_strerror", "wkv7_fwd_path",
-            "wkv7_version"} <= set(names)
+            "wkv7_version", "wkv7_set_wait_limit"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"{n} declared in wkv7.h but not exported"
 
 
 def test_version_and_strerror(L):
-    assert L.wkv7_version() == 108
+    assert L.wkv7_version() == 200
     for code in range(4):
         assert len(L.wkv7_strerror(code)) > 0
     assert L.wkv7_strerror(99) == b"unknown status"
@@ -45,10 +45,12 @@ GOOD = P(0x100000)       # 16-byte aligned stand-in; never dereferenced on the e
 ODD = P(0x100002)
 
 
-def fwd(L, dtype=1, B=1, T=4, H=1, K=64, V=64, ptrs=None, s0=None, mask=None, sf=None, algo=0):
+def fwd(L, dtype=1, B=1, T=4, H=1, K=64, V=64, ptrs=None, s0=None, n_state=None, mask=None, sf=None, algo=0):
     ptrs = ptrs or [GOOD] * 7
     r, w, k, v, a, b, o = ptrs
-    return L.wkv7_fwd(dtype, B, T, H, K, V, r, w, k, v, a, b, s0, mask, o, sf, algo, None)
+    if n_state is None:
+        n_state = B if s0 is not None else 0
+    return L.wkv7_fwd(dtype, B, T, H, K, V, r, w, k, v, a, b, s0, n_state, mask, o, sf, algo, None)
 
 
 def step(L, dtype=1, B=1, H=1, K=64, V=64, ptrs=None):
@@ -85,6 +87,25 @@ def test_fwd_rejects_null_and_misaligned(L, slot):
 def test_fwd_rejects_misaligned_states(L):
     assert fwd(L, s0=ODD) == wkv7.ERR_INVALID_ARG
     assert fwd(L, sf=ODD) == wkv7.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [
+    dict(B=2, s0=GOOD, n_state=0),             # state rows must be 1 or B
+    dict(B=2, s0=GOOD, n_state=3),
+    dict(B=2, s0=GOOD, n_state=1, sf=GOOD),    # a shared state overwritten by the finals
+])
+def test_fwd_state_rows(L, kw):
+    assert fwd(L, **kw) == wkv7.ERR_INVALID_ARG
+
+
+def test_wait_limit_hook(L):
+    prev = L.wkv7_set_wait_limit(5)
+    try:
+        assert L.wkv7_set_wait_limit(0) == 5
+        assert L.wkv7_set_wait_limit(-1) == 0       # negative: back to the default
+        assert L.wkv7_set_wait_limit(-1) == 1 << 20
+    finally:
+        L.wkv7_set_wait_limit(prev)
 
 
 @pytest.mark.parametrize("slot", range(8))
@@ -133,8 +154,9 @@ def varlen(L, dtype=1, N=2, TT=40, H=1, K=64, V=64, cu=GOOD, ptrs=None, s0=None,
     (dict(cu=P(0x100002)), wkv7.ERR_INVALID_ARG),                  # cu_seqlens not 4-byte aligned
     (dict(smap=P(0x100001)), wkv7.ERR_INVALID_ARG),                # state_map not 4-byte aligned
     (dict(s0=GOOD, n_state=0), wkv7.ERR_INVALID_ARG),              # pool without rows
-    (dict(s0=GOOD, n_state=3), wkv7.ERR_INVALID_ARG),              # no map: pool must have N rows
+    (dict(s0=GOOD, n_state=3), wkv7.ERR_INVALID_ARG),              # no map: pool must have N or 1 rows
     (dict(s0=GOOD, n_state=1, smap=GOOD, sf=GOOD), wkv7.ERR_INVALID_ARG),   # mapped pool aliased by output
+    (dict(s0=GOOD, n_state=1, sf=GOOD), wkv7.ERR_INVALID_ARG),     # shared row aliased by output
     (dict(s0=ODD, n_state=2), wkv7.ERR_INVALID_ARG),
     (dict(ptrs=[GOOD] * 6 + [None]), wkv7.ERR_INVALID_ARG),
     (dict(K=64, V=128), wkv7.ERR_UNSUPPORTED),
@@ -183,20 +205,23 @@ def test_gdn_rejects_null_and_misaligned(L, slot):
     assert gdn(L, ptrs=ptrs) == wkv7.ERR_INVALID_ARG
 
 
-def bwd(L, dtype=1, B=1, T=20, H=1, K=64, V=64, ptrs=None, s0=None, mask=None, dsf=None, ds0=None,
-        ws=GOOD, ws_bytes=None):
+def bwd(L, dtype=1, B=1, T=20, H=1, K=64, V=64, ptrs=None, s0=None, n_state=None, mask=None, dsf=None,
+        ds0=None, ws=GOOD, ws_bytes=None):
     ptrs = ptrs or [GOOD] * 13
     if ws_bytes is None:
         ws_bytes = L.wkv7_bwd_workspace_bytes(B, T, H, K, V)
+    if n_state is None:
+        n_state = B if s0 is not None else 0
     r, w, k, v, a, b, do, dr, dw, dk, dv, da, db = ptrs
-    return L.wkv7_bwd(dtype, B, T, H, K, V, r, w, k, v, a, b, s0, mask, do, dsf, dr, dw, dk, dv, da, db, ds0,
-                      ws, ws_bytes, None)
+    return L.wkv7_bwd(dtype, B, T, H, K, V, r, w, k, v, a, b, s0, n_state, mask, do, dsf,
+                      dr, dw, dk, dv, da, db, ds0, ws, ws_bytes, None)
 
 
 def test_bwd_workspace_size(L):
-    # two fp32 states per 16-token chunk and sequence
-    assert L.wkv7_bwd_workspace_bytes(2, 33, 3, 64, 64) == 4 * 2 * 3 * 64 * 64 * 2 * 3
-    assert L.wkv7_bwd_workspace_bytes(1, 16, 1, 128, 128) == 4 * 128 * 128 * 2
+    # two fp32 states per 16-token chunk and sequence (rounded up to 256
+    # bytes), then one state per sequence for a shared state's gradient
+    assert L.wkv7_bwd_workspace_bytes(2, 33, 3, 64, 64) == 4 * 2 * 3 * 64 * 64 * 2 * 3 + 4 * 2 * 3 * 64 * 64
+    assert L.wkv7_bwd_workspace_bytes(1, 16, 1, 128, 128) == 4 * 128 * 128 * 3
     assert L.wkv7_bwd_workspace_bytes(1, 16, 1, 64, 32) == 0
     assert L.wkv7_bwd_workspace_bytes(0, 16, 1, 64, 64) == 0
 
@@ -212,6 +237,8 @@ def test_bwd_workspace_size(L):
     (dict(s0=ODD), wkv7.ERR_INVALID_ARG),
     (dict(dsf=ODD), wkv7.ERR_INVALID_ARG),
     (dict(ds0=ODD), wkv7.ERR_INVALID_ARG),
+    (dict(B=2, s0=GOOD, n_state=3), wkv7.ERR_INVALID_ARG),         # state rows must be 1 or B
+    (dict(B=2, s0=GOOD, n_state=0), wkv7.ERR_INVALID_ARG),
     (dict(B=1 << 16, H=1 << 14, T=16), wkv7.ERR_UNSUPPORTED),      # 2 B H workgroups exceed the grid
 ])
 def test_bwd_validation(L, kw, code):
@@ -304,7 +331,7 @@ def test_bwd_varlen_workspace_size(L):
     (dict(ws=None), wkv7.ERR_INVALID_ARG),
     (dict(ws_bytes=1024), wkv7.ERR_INVALID_ARG),              # workspace too small
     (dict(s0=GOOD, n_state=0), wkv7.ERR_INVALID_ARG),
-    (dict(s0=GOOD, n_state=2), wkv7.ERR_INVALID_ARG),         # no map: one row per sequence needed
+    (dict(s0=GOOD, n_state=2), wkv7.ERR_INVALID_ARG),         # no map: N rows or one shared row
     (dict(s0=ODD, n_state=3), wkv7.ERR_INVALID_ARG),
     (dict(smap=P(0x100002)), wkv7.ERR_INVALID_ARG),
     (dict(dsf=ODD), wkv7.ERR_INVALID_ARG),
