@@ -57,7 +57,8 @@ typedef enum {
     WKV7_OK = 0,
     WKV7_ERR_INVALID_ARG = 1, /* NULL required pointer, bad size, misaligned */
     WKV7_ERR_UNSUPPORTED = 2, /* valid request this build does not implement */
-    WKV7_ERR_HIP = 3          /* a HIP launch failed                         */
+    WKV7_ERR_HIP = 3,         /* a HIP launch failed                         */
+    WKV7_ERR_TOO_LARGE = 4    /* exceeds the fixed scratch of wkv7_bwd_noalloc */
 } wkv7_status_t;
 
 /*
@@ -426,6 +427,42 @@ const char *wkv7_strerror(int status);
  * would be rejected.  Host only; launches nothing. */
 int wkv7_fwd_path(int dtype, int B, int T, int H, int K, int V, int algo);
 
+/* Bytes of the device array that backs wkv7_bwd_noalloc's scratch, one
+ * array per GPU, held from the first call on that GPU until the process
+ * ends. */
+#define WKV7_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * wkv7_bwd_noalloc -- wkv7_bwd for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight training loops, harnesses that
+ * forbid hipMalloc.  It computes exactly what wkv7_bwd computes (the same
+ * kernels), with the same arguments minus the workspace: the backward's
+ * scratch (state checkpoints, per-sequence gradients of a shared initial
+ * state) lives in a fixed device array of WKV7_NOALLOC_SCRATCH_BYTES bytes
+ * inside the library instead.  The call allocates nothing: no hipMalloc, no
+ * hipFree, no allocating library routine.  Its first call on a GPU looks up
+ * that GPU's copy of the array (with that GPU current); later calls reuse it.
+ *
+ *   arguments      as for wkv7_bwd, without workspace / workspace_bytes.
+ * Returns WKV7_ERR_TOO_LARGE when wkv7_bwd_workspace_bytes(B,T,H,K,V)
+ * exceeds WKV7_NOALLOC_SCRATCH_BYTES, that is when B H (2 ceil(T/16) + 1)
+ * exceeds 4096 at K = V = 64 or 1024 at K = V = 128 (for example one
+ * sequence of 8 heads up to T = 4080 at 64), after the same argument checks
+ * as wkv7_bwd.
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind (the backward reads nothing of it that it has not written in the
+ * same call, so nothing needs clearing): calls that overlap in time on one
+ * GPU, on different streams, race on it and must be serialised by the
+ * caller.
+ */
+wkv7_status_t wkv7_bwd_noalloc(int dtype, int B, int T, int H, int K, int V,
+                               const void *r, const void *w, const void *k,
+                               const void *v, const void *a, const void *b,
+                               const float *initial_state, int n_state, const uint8_t *mask,
+                               const void *d_o, const float *d_final_state,
+                               void *dr, void *dw, void *dk, void *dv, void *da, void *db,
+                               float *d_initial_state, void *stream);
+
 /*
  * wkv7_set_wait_limit -- test hook for the failure path of the chunked
  * forward.  Its producer and consumer waves hand chunks over through
@@ -447,7 +484,7 @@ int wkv7_set_wait_limit(int polls);
 /* ABI version of this header (major * 100 + minor): 200 adds n_state (a
  * broadcast initial state) to wkv7_fwd and wkv7_bwd, accepts a one-row pool
  * without state_map in wkv7_fwd_varlen and wkv7_bwd_varlen, and adds
- * wkv7_set_wait_limit; earlier: 101 adds wkv7_fwd_varlen,
+ * wkv7_set_wait_limit; 201 adds wkv7_bwd_noalloc; earlier: 101 adds wkv7_fwd_varlen,
  * 102 adds wkv7_gdn_fwd, 103 adds wkv7_bwd and wkv7_bwd_workspace_bytes,
  * 104 adds wkv7_gdn_step, 105 adds wkv7_gdn_fwd_varlen, 106 adds wkv7_gdn_bwd and
  * wkv7_gdn_bwd_workspace_bytes, 107 adds wkv7_bwd_varlen and

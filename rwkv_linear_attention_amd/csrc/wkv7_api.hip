@@ -58,6 +58,31 @@ std::atomic<int> g_wait_limit{wkv7::kDefaultWaitLimit};
 
 int wkv7::current_wait_limit() { return g_wait_limit.load(std::memory_order_relaxed); }
 
+// Host-only argument checks of wkv7_bwd apart from the workspace.
+int wkv7::check_bwd_args(int dtype, int B, int T, int H, int K, int V, const void *r, const void *w,
+                                   const void *k, const void *v, const void *a, const void *b,
+                                   const float *initial_state, int n_state, const void *d_o,
+                                   const float *d_final_state, const void *dr, const void *dw, const void *dk,
+                                   const void *dv, const void *da, const void *db, const float *d_initial_state)
+{
+    wkv7_status_t st = check_common(dtype, B, H, K, V);
+    if (st != WKV7_OK) return st;
+    if (T < 0) return WKV7_ERR_INVALID_ARG;
+    if ((long long)B * T * H * K > (1ll << 40)) return WKV7_ERR_UNSUPPORTED;
+    // launch grids: 2 B H workgroups, and B H ceil(T/16) workgroups
+    if (2ll * B * H > INT32_MAX || (long long)B * H * ((T + 15) / 16) > INT32_MAX) return WKV7_ERR_UNSUPPORTED;
+    if (T > 0) {
+        const void *req[] = {r, w, k, v, a, b, d_o, dr, dw, dk, dv, da, db};
+        for (const void *p : req)
+            if (!p || !aligned16(p)) return WKV7_ERR_INVALID_ARG;
+    }
+    if (initial_state && n_state != 1 && n_state != B) return WKV7_ERR_INVALID_ARG;
+    const void *opt[] = {initial_state, d_final_state, d_initial_state};
+    for (const void *p : opt)
+        if (p && !aligned16(p)) return WKV7_ERR_INVALID_ARG;
+    return WKV7_OK;
+}
+
 extern "C" {
 
 int wkv7_set_wait_limit(int polls)
@@ -65,7 +90,7 @@ int wkv7_set_wait_limit(int polls)
     return g_wait_limit.exchange(polls < 0 ? wkv7::kDefaultWaitLimit : polls);
 }
 
-int wkv7_version(void) { return 200; }
+int wkv7_version(void) { return 201; }
 
 const char *wkv7_strerror(int status)
 {
@@ -74,6 +99,7 @@ const char *wkv7_strerror(int status)
     case WKV7_ERR_INVALID_ARG: return "invalid argument (null pointer, bad size, dtype or alignment)";
     case WKV7_ERR_UNSUPPORTED: return "unsupported configuration (K == V in {64, 128} required; chunked path is bf16 only)";
     case WKV7_ERR_HIP: return "HIP kernel launch failed";
+    case WKV7_ERR_TOO_LARGE: return "request exceeds the fixed scratch buffer of the allocation-free entry point";
     default: return "unknown status";
     }
 }
@@ -274,22 +300,14 @@ wkv7_status_t wkv7_bwd(int dtype, int B, int T, int H, int K, int V,
                        float *d_initial_state, void *workspace, size_t workspace_bytes,
                        void *stream)
 {
-    wkv7_status_t st = check_common(dtype, B, H, K, V);
+    const wkv7_status_t st = (wkv7_status_t)wkv7::check_bwd_args(
+        dtype, B, T, H, K, V, r, w, k, v, a, b, initial_state, n_state, d_o, d_final_state, dr, dw, dk, dv, da, db,
+        d_initial_state);
     if (st != WKV7_OK) return st;
-    if (T < 0) return WKV7_ERR_INVALID_ARG;
-    if ((long long)B * T * H * K > (1ll << 40)) return WKV7_ERR_UNSUPPORTED;
-    // launch grids: 2 B H workgroups, and B H ceil(T/16) workgroups
-    if (2ll * B * H > INT32_MAX || (long long)B * H * ((T + 15) / 16) > INT32_MAX) return WKV7_ERR_UNSUPPORTED;
     if (T > 0) {
-        const void *req[] = {r, w, k, v, a, b, d_o, dr, dw, dk, dv, da, db, workspace};
-        for (const void *p : req)
-            if (!p || !aligned16(p)) return WKV7_ERR_INVALID_ARG;
+        if (!workspace || !aligned16(workspace)) return WKV7_ERR_INVALID_ARG;
         if (workspace_bytes < wkv7::bwd_workspace_bytes(B, T, H, K)) return WKV7_ERR_INVALID_ARG;
     }
-    if (initial_state && n_state != 1 && n_state != B) return WKV7_ERR_INVALID_ARG;
-    const void *opt[] = {initial_state, d_final_state, d_initial_state};
-    for (const void *p : opt)
-        if (p && !aligned16(p)) return WKV7_ERR_INVALID_ARG;
     const bool shared = initial_state && n_state == 1 && B > 1;
 
     hipStream_t s = (hipStream_t)stream;

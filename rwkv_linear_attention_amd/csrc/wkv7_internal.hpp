@@ -101,6 +101,13 @@ struct StepArgs {
     int n_state_in = 0;
 };
 
+// Host-only argument checks of wkv7_bwd apart from the workspace (status
+// values of wkv7_status_t).
+int check_bwd_args(int dtype, int B, int T, int H, int K, int V, const void *r, const void *w, const void *k,
+                   const void *v, const void *a, const void *b, const float *initial_state, int n_state,
+                   const void *d_o, const float *d_final_state, const void *dr, const void *dw, const void *dk,
+                   const void *dv, const void *da, const void *db, const float *d_initial_state);
+
 // dtype: 0 = fp32, 1 = bf16 (values of wkv7_dtype_t).
 hipError_t launch_recurrent(int dtype, const FwdArgs &args, hipStream_t stream);
 hipError_t launch_chunked(const FwdArgs &args, hipStream_t stream);     // bf16 only

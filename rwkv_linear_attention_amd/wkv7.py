@@ -15,7 +15,8 @@ LIB_PATH = os.path.join(_HERE, "libwkv7.so")
 
 F32, BF16 = 0, 1
 ALGO_AUTO, ALGO_RECURRENT, ALGO_CHUNKED = 0, 1, 2
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_TOO_LARGE = 0, 1, 2, 3, 4
+NOALLOC_SCRATCH_BYTES = 64 << 20   # WKV7_NOALLOC_SCRATCH_BYTES
 
 _lib = None
 
@@ -38,6 +39,8 @@ def lib():
     L.wkv7_gdn_fwd.restype = i
     L.wkv7_bwd.argtypes = [i, i, i, i, i, i] + [p] * 7 + [i] + [p] * 11 + [ctypes.c_size_t, p]
     L.wkv7_bwd.restype = i
+    L.wkv7_bwd_noalloc.argtypes = [i, i, i, i, i, i] + [p] * 7 + [i] + [p] * 11
+    L.wkv7_bwd_noalloc.restype = i
     L.wkv7_bwd_workspace_bytes.argtypes = [i] * 5
     L.wkv7_bwd_workspace_bytes.restype = ctypes.c_size_t
     L.wkv7_bwd_varlen.argtypes = [i] * 6 + [p] * 7 + [p, i, p, p, p, p] + [p] * 8 + [ctypes.c_size_t, p]
@@ -255,6 +258,52 @@ def bwd(r, w, k, v, a, b, d_o, initial_state=None, mask=None, d_final_state=None
                         _ptr(initial_state), n_state, _ptr(m), _ptr(d_o), _ptr(d_final_state),
                         *(_ptr(g[n]) for n in ("r", "w", "k", "v", "a", "b", "s0")),
                         _ptr(workspace), workspace.numel(), _stream(dev))
+    if st != OK:
+        raise WKV7Error(st)
+    return g
+
+
+def bwd_noalloc(r, w, k, v, a, b, d_o, initial_state=None, mask=None, d_final_state=None,
+                need_initial_state_grad=True, out=None):
+    """Gradients of fwd through wkv7_bwd_noalloc: the library's fixed
+    per-GPU scratch array instead of a workspace (bwd_workspace_bytes(...)
+    must not exceed NOALLOC_SCRATCH_BYTES, else WKV7Error with
+    ERR_TOO_LARGE).  Arguments and result as for bwd; out: optional dict of
+    preallocated gradient tensors (r, w, k, v, a, b, s0), so that a caller can
+    keep every allocation outside the call.  Calls that overlap in time on
+    one GPU share the scratch and race."""
+    dev = r.device
+    B, T, H, K = r.shape
+    V = v.shape[-1]
+    dt = r.dtype
+    code = _dtype_code(dt)
+    for name, t in (("r", r), ("w", w), ("k", k), ("a", a), ("b", b)):
+        _check(t, name, (B, T, H, K), dt, dev)
+    _check(v, "v", (B, T, H, V), dt, dev)
+    _check(d_o, "d_o", (B, T, H, V), dt, dev)
+    n_state = _state_rows(initial_state, B, H, K, V, dev)
+    if d_final_state is not None:
+        _check(d_final_state, "d_final_state", (B, H, K, V), torch.float32, dev)
+    m = _mask_u8(mask)
+    if m is not None:
+        _check(m, "mask", (B, T), torch.uint8, dev)
+    if out is not None:
+        g = dict(out)
+        for n in ("r", "w", "k", "a", "b"):
+            _check(g[n], "out[" + n + "]", (B, T, H, K), dt, dev)
+        _check(g["v"], "out[v]", (B, T, H, V), dt, dev)
+        if not need_initial_state_grad:
+            g["s0"] = None
+        elif g.get("s0") is not None:
+            _check(g["s0"], "out[s0]", (n_state or B, H, K, V), torch.float32, dev)
+    else:
+        g = {n: torch.empty((B, T, H, K), dtype=dt, device=dev) for n in ("r", "w", "k", "a", "b")}
+        g["v"] = torch.empty((B, T, H, V), dtype=dt, device=dev)
+        g["s0"] = (torch.empty((n_state or B, H, K, V), dtype=torch.float32, device=dev)
+                   if need_initial_state_grad else None)
+    st = lib().wkv7_bwd_noalloc(code, B, T, H, K, V, _ptr(r), _ptr(w), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
+                                _ptr(initial_state), n_state, _ptr(m), _ptr(d_o), _ptr(d_final_state),
+                                *(_ptr(g[n]) for n in ("r", "w", "k", "v", "a", "b", "s0")), _stream(dev))
     if st != OK:
         raise WKV7Error(st)
     return g

@@ -34,8 +34,8 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_strerror(L):
-    assert L.wkv7_version() == 200
-    for code in range(4):
+    assert L.wkv7_version() == 201
+    for code in range(5):
         assert len(L.wkv7_strerror(code)) > 0
     assert L.wkv7_strerror(99) == b"unknown status"
 
@@ -439,3 +439,46 @@ def gdn_varlen(L, dtype=1, N=2, TT=40, H=1, K=64, V=64, cu=GOOD, ptrs=None, s0=N
 ])
 def test_gdn_varlen_validation(L, kw, code):
     assert gdn_varlen(L, **kw) == code
+
+
+def bwd_noalloc(L, dtype=1, B=1, T=20, H=1, K=64, V=64, ptrs=None, s0=None, n_state=None, mask=None, dsf=None,
+                ds0=None):
+    ptrs = ptrs or [GOOD] * 13
+    if n_state is None:
+        n_state = B if s0 is not None else 0
+    r, w, k, v, a, b, do, dr, dw, dk, dv, da, db = ptrs
+    return L.wkv7_bwd_noalloc(dtype, B, T, H, K, V, r, w, k, v, a, b, s0, n_state, mask, do, dsf,
+                              dr, dw, dk, dv, da, db, ds0, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), wkv7.ERR_INVALID_ARG),
+    (dict(B=0), wkv7.ERR_INVALID_ARG),
+    (dict(T=-1), wkv7.ERR_INVALID_ARG),
+    (dict(K=64, V=128), wkv7.ERR_UNSUPPORTED),
+    (dict(B=2, s0=GOOD, n_state=3), wkv7.ERR_INVALID_ARG),
+    (dict(ds0=ODD), wkv7.ERR_INVALID_ARG),
+    # the scratch holds B H (2 ceil(T/16) + 1) fp32 states: 4096 at d64, 1024 at d128
+    (dict(B=1, H=8, T=4096), wkv7.ERR_TOO_LARGE),
+    (dict(B=1, H=1, T=8192, K=128, V=128), wkv7.ERR_TOO_LARGE),
+    (dict(B=64, H=64, T=16), wkv7.ERR_TOO_LARGE),
+])
+def test_bwd_noalloc_rejects_on_the_host(L, kw, code):
+    assert bwd_noalloc(L, **kw) == code
+
+
+@pytest.mark.parametrize("slot", range(13))
+def test_bwd_noalloc_rejects_null_and_misaligned(L, slot):
+    ptrs = [GOOD] * 13
+    ptrs[slot] = None
+    assert bwd_noalloc(L, ptrs=ptrs) == wkv7.ERR_INVALID_ARG
+    ptrs[slot] = ODD
+    assert bwd_noalloc(L, ptrs=ptrs) == wkv7.ERR_INVALID_ARG
+
+
+def test_bwd_noalloc_bound_matches_workspace_size(L):
+    """The largest accepted sizes are those whose wkv7_bwd workspace fits the
+    fixed scratch: one more chunk or head does not."""
+    limit = wkv7.NOALLOC_SCRATCH_BYTES
+    assert L.wkv7_bwd_workspace_bytes(1, 4080, 8, 64, 64) <= limit < L.wkv7_bwd_workspace_bytes(1, 4096, 8, 64, 64)
+    assert L.wkv7_bwd_workspace_bytes(1, 8176, 1, 128, 128) <= limit < L.wkv7_bwd_workspace_bytes(1, 8192, 1, 128, 128)
