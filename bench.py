@@ -24,13 +24,16 @@ HBM_PEAK_GBS = 8000.0
 # x 2.4 GHz.  Code built without packed fp32 instructions issues at most half of it.
 FP32_VECTOR_PEAK_TFLOPS = 157.3
 PROFILE_NOTE = os.path.join(ROOT, "profiles", "wkv7_chunked_B8_T4096_H64_d64.md")
-KERNEL_SOURCES = [os.path.join(ROOT, "rwkv_linear_attention_amd", "csrc", f)
-                  for f in ("wkv7_chunked.hip", "wkv7_common.hpp")]
+PROFILE_NOTE_D128 = os.path.join(ROOT, "profiles", "wkv7_chunked_B16_T4096_H32_d128.md")
+PROFILE_NOTE_STEP = os.path.join(ROOT, "profiles", "wkv7_step_B512_H40_d64.md")
+CSRC = os.path.join(ROOT, "rwkv_linear_attention_amd", "csrc")
+KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("wkv7_chunked.hip", "wkv7_common.hpp")]
+STEP_SOURCES = [os.path.join(CSRC, f) for f in ("wkv7_step.hip", "wkv7_common.hpp")]
 
 
-def kernel_sha():
+def kernel_sha(sources=None):
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources or KERNEL_SOURCES:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -43,14 +46,14 @@ def algorithmic_bytes(B, T, H, D, dtype_bytes, has_s0, has_final, has_mask):
     return 6 * tok + tok + (st if has_s0 else 0) + (st if has_final else 0) + (B * T if has_mask else 0)
 
 
-def measured_traffic(sha):
+def measured_traffic(sha, note=PROFILE_NOTE):
     """HBM bytes per launch from the committed rocprofv3 counter summary
     (FETCH_SIZE and WRITE_SIZE in KiB per dispatch, each scaled by what the
     counter reads for a plain copy of known size), if it was taken on this
     exact kernel source; otherwise None."""
-    if not os.path.exists(PROFILE_NOTE):
+    if not os.path.exists(note):
         return None
-    txt = open(PROFILE_NOTE).read()
+    txt = open(note).read()
     m = re.search(r"traffic: source_sha=(\w+) fetch_kib=([\d.]+) fetch_scale=([\d.]+) "
                   r"write_kib=([\d.]+) write_scale=([\d.]+)", txt)
     if not m or m.group(1) != sha:
@@ -164,6 +167,154 @@ def settle(fn, ms=SETTLE_MS):
     return n
 
 
+def time_steps(step, steps, warmup):
+    """Clock settle, W untimed steps, then K timed steps with a HIP event
+    pair around each launch (torch's current stream, where the library
+    launches) and one around all of them.  Returns (ms per step over the
+    whole timed region, mean launch duration in ms, settle step count)."""
+    import torch
+    n_settle = settle(step)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for e0, e1 in ev:
+        e0.record()
+        step()
+        e1.record()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps, sum(e0.elapsed_time(e1) for e0, e1 in ev) / steps, n_settle
+
+
+def _host_sequences(x, pairs, names):
+    """The listed (b, h) sequences of [B,T,H,K] device tensors as float64
+    host arrays [n, T, 1, K] (inputs for the oracle)."""
+    import numpy as np
+    import torch
+    idx_b = torch.tensor([p[0] for p in pairs], device=x[names[0]].device)
+    idx_h = torch.tensor([p[1] for p in pairs], device=x[names[0]].device)
+    return {n: x[n][idx_b, :, idx_h].float().cpu().numpy().astype(np.float64)[:, :, None, :] for n in names}
+
+
+def d128_entry(steps, warmup, cpu=True):
+    """Workload 3: bf16 B16 T4096 H32 K=V=128 forward with a random initial
+    state and a trailing-padding mask (10 % of each sequence), final state
+    written; chunked kernel under AUTO.  Inputs drawn on the device (same
+    recipe as the parity tests, torch's generator)."""
+    import torch
+    from rwkv_linear_attention_amd import synth, wkv7
+    wl = synth.WORKLOADS[3]
+    B, T, H, D = wl["B"], wl["T"], wl["H"], wl["K"]
+    print(f"[bench] generating workload {wl['name']} on the device", file=sys.stderr, flush=True)
+    x = synth.make_device(3, "cuda", seed=2003)
+    names = ("r", "w", "k", "v", "a", "b")
+    o = torch.empty((B, T, H, D), dtype=torch.bfloat16, device="cuda")
+    sf = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
+    path = wkv7.fwd_path(torch.bfloat16, B, T, H, D, D)
+    assert path == wkv7.ALGO_CHUNKED
+    step = lambda: wkv7.fwd(*(x[n] for n in names), initial_state=x["s0"], mask=x["mask"], out=o, final_state=sf)
+    ms_step, launch_ms, _ = time_steps(step, steps, warmup)
+    nbytes = algorithmic_bytes(B, T, H, D, 2, True, True, True)
+    achieved = nbytes / (launch_ms * 1e-3) / 1e9
+    sha = kernel_sha()
+    res = {"value": round(B * T / (ms_step * 1e-3) / 1e6, 3), "unit": "Mtokens/s", "steps": steps,
+           "ms_per_step": round(ms_step, 5), "dtype": "bf16", "data": "synthetic (device generator, seed 2003)",
+           "config": {"workload": wl["name"], "B": B, "T": T, "H": H, "K": D, "V": D, "C": H * D,
+                      "initial_state": "random N(0, 0.1)", "mask": "last 409 tokens of each sequence 0",
+                      "final_state": True, "kernel": "chunked"},
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(achieved / HBM_PEAK_GBS, 4),
+                        "traffic": measured_traffic(sha, PROFILE_NOTE_D128), "algorithmic_bytes": nbytes,
+                        "kernel_ms": round(launch_ms, 5), "kernel_sha": sha}}
+    if cpu:
+        import oracle
+
+        def call(sel):
+            h = _host_sequences(x, sel, names)
+            s0 = x["s0"][[p[0] for p in sel], [p[1] for p in sel]].cpu().numpy()[:, None]
+            m = x["mask"][[p[0] for p in sel]].cpu().numpy()
+            oracle.fwd(*(h[n] for n in names), s0, m)
+        print("[bench] timing the CPU oracle (head size 128) on a sample", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = oracle_sample_rate(call, B, H, T, budget_s=6.0)
+    del x, o, sf
+    torch.cuda.empty_cache()
+    return {wl["name"]: res}
+
+
+def decode_entry(reps, cpu=True):
+    """Workload 4: 256 consecutive wkv7_step calls (bf16 inputs, fp32 state
+    updated in place) on B512 H40 K=V=64 from a random initial state, fresh
+    inputs every step (256 distinct steps drawn on the device, step-major so
+    each step's inputs are contiguous).  The state is reset from a pristine
+    copy before each repetition, outside the timed region."""
+    import numpy as np
+    import torch
+    from rwkv_linear_attention_amd import synth, wkv7
+    wl = synth.WORKLOADS[4]
+    B, NSTEP, H, D = wl["B"], wl["T"], wl["H"], wl["K"]
+    print(f"[bench] generating workload {wl['name']} on the device", file=sys.stderr, flush=True)
+    x = synth.make_device(4, "cuda", seed=2004, step_major=True)      # [256, B, H, D]
+    names = ("r", "w", "k", "v", "a", "b")
+    state0 = x["s0"]
+    state = state0.clone()
+    obuf = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
+
+    def run():
+        state.copy_(state0)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for t in range(NSTEP):
+            wkv7.step(*(x[n][t] for n in names), state, out=obuf)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    settle(lambda: wkv7.step(*(x[n][0] for n in names), state, out=obuf))
+    run()
+    ms_total = sum(run() for _ in range(reps)) / reps
+    launch_ms = ms_total / NSTEP
+    step_bytes = 2 * B * H * D * D * 4 + 6 * B * H * D * 2 + B * H * D * 2
+    achieved = step_bytes / (launch_ms * 1e-3) / 1e9
+    sha = kernel_sha(STEP_SOURCES)
+    res = {"value": round(B * NSTEP / (ms_total * 1e-3) / 1e6, 3), "unit": "Mtokens/s", "steps": reps,
+           "ms_per_step": round(ms_total, 4), "us_per_decode_step": round(launch_ms * 1e3, 2), "dtype": "bf16",
+           "data": "synthetic (device generator, seed 2004)",
+           "config": {"workload": wl["name"], "B": B, "H": H, "K": D, "V": D, "C": H * D,
+                      "decode_steps": NSTEP, "initial_state": "random N(0, 0.1)", "kernel": "step"},
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(achieved / HBM_PEAK_GBS, 4),
+                        "traffic": measured_traffic(sha, PROFILE_NOTE_STEP), "algorithmic_bytes": step_bytes,
+                        "kernel_ms": round(launch_ms, 5), "kernel_sha": sha,
+                        "note": "per step launch: state read and written, inputs and o once"}}
+    if cpu:
+        import oracle
+        threads = min(16, len(os.sched_getaffinity(0)))
+        oracle.set_threads(threads)
+        print("[bench] timing the CPU oracle (decode) on whole steps", file=sys.stderr, flush=True)
+        S = state0.cpu().numpy().astype(np.float64)
+        n, t_used = 0, 0.0
+        while t_used < 4.0 and n < NSTEP:
+            h = {m: x[m][n].float().cpu().numpy() for m in names}
+            t0 = time.perf_counter()
+            _, S = oracle.step(*(h[m] for m in names), S)
+            t_used += time.perf_counter() - t0
+            n += 1
+        res["cpu_baseline"] = {"value": round(B * n / t_used / 1e6, 6), "unit": "Mtokens/s", "cores": threads,
+                               "kind": "oracle",
+                               "sample": f"the first {n} of the 256 decode steps, all {B * H} sequences each "
+                                         f"(fp64 C, OpenMP), {t_used:.1f} s"}
+    del x, state, state0, obuf
+    torch.cuda.empty_cache()
+    return {wl["name"]: res}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -216,25 +367,8 @@ def main():
         wkv7.fwd(dev["r"], dev["w"], dev["k"], dev["v"], dev["a"], dev["b"],
                  out=o, final_state=sf)
 
-    n_settle = settle(step)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    print(f"[bench] clock settle ({n_settle} steps) and warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    t_all0 = torch.cuda.Event(enable_timing=True)
-    t_all1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_all0.record()
-    for e0, e1 in ev:
-        e0.record()
-        step()
-        e1.record()
-    t_all1.record()
-    torch.cuda.synchronize()
-    total_ms = t_all0.elapsed_time(t_all1)
-    launch_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / args.steps
-    ms_per_step = total_ms / args.steps
+    print(f"[bench] clock settle, {args.warmup} warmup steps, {args.steps} timed steps", file=sys.stderr, flush=True)
+    ms_per_step, launch_ms, n_settle = time_steps(step, args.steps, args.warmup)
 
     alg_bytes = algorithmic_bytes(B, T, H, D, 2, False, True, False)
     achieved = alg_bytes / (launch_ms * 1e-3) / 1e9
@@ -266,9 +400,13 @@ def main():
     if not args.no_cpu:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(inp, H, T)
+    del dev, o, sf, inp
+    torch.cuda.empty_cache()
+    # the two other full-size workloads, each with its own roofline and CPU baseline
+    result["others"] = d128_entry(args.steps, args.warmup, not args.no_cpu)
+    result["others"].update(decode_entry(max(3, args.steps // 10), not args.no_cpu))
     if args.all:
-        del dev, o, sf, inp
-        result["others"] = other_workloads(args.steps, args.warmup, not args.no_cpu)
+        result["more"] = other_workloads(args.steps, args.warmup, not args.no_cpu)
     print(json.dumps(result), flush=True)
 
 
@@ -337,6 +475,31 @@ def varlen_workload(steps, warmup):
                   "frac_of_8TBps": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes,
                   "lengths": [int(x) for x in lens], "kernel": "chunked d64 (packed)"}}
     del o, sf
+    # a skewed packed batch under AUTO: 299 one-token sequences and one of
+    # 4096 tokens (mean length 14.6), beside the single 4096-token sequence
+    # alone on the chunked kernel
+    sk_lens = [1] * 299 + [4096]
+    STT = sum(sk_lens)
+    sk = synth.make(2, B=1, T=STT, H=H, K=D, seed=1209)
+    sdev = {n: synth.to_torch(sk[n][0], "bf16", "cuda") for n in ("r", "w", "k", "v", "a", "b")}
+    scu = torch.from_numpy(np.concatenate([[0], np.cumsum(sk_lens)]).astype(np.int32)).cuda()
+    so = torch.empty((STT, H, D), dtype=torch.bfloat16, device="cuda")
+    ssf = torch.empty((len(sk_lens), H, D, D), dtype=torch.float32, device="cuda")
+    ms_sk = _time_launches(lambda i: wkv7.fwd_varlen(*(sdev[n] for n in ("r", "w", "k", "v", "a", "b")), scu,
+                                                     out=so, final_state=ssf), steps, warmup)
+    one = {n: sdev[n][299:].unsqueeze(0) for n in sdev}
+    o1 = torch.empty((1, 4096, H, D), dtype=torch.bfloat16, device="cuda")
+    s1 = torch.empty((1, H, D, D), dtype=torch.float32, device="cuda")
+    ms_one = _time_launches(lambda i: wkv7.fwd(*(one[n] for n in ("r", "w", "k", "v", "a", "b")), out=o1,
+                                               final_state=s1, algo=wkv7.ALGO_CHUNKED), steps, warmup)
+    ms_rec = _time_launches(lambda i: wkv7.fwd_varlen(*(sdev[n] for n in ("r", "w", "k", "v", "a", "b")), scu,
+                                                      out=so, final_state=ssf, algo=wkv7.ALGO_RECURRENT),
+                            max(3, steps // 5), 1)
+    res[f"fwd_varlen_bf16_skewed_299x1_1x4096_H{H}_d{D}"] = {
+        "ms_auto": round(ms_sk, 5), "ms_forced_recurrent": round(ms_rec, 5),
+        "ms_long_sequence_alone_chunked": round(ms_one, 5),
+        "note": "AUTO takes the chunked kernel for packed bf16; the long sequence sets the time"}
+    del sk, sdev, so, ssf, one, o1, s1
     # the backward of the same packed forward (seeded N(0, 1) output gradient)
     d_o = synth.to_torch(synth.round_to(rng.standard_normal((TT, H, D), dtype=np.float32), "bf16"), "bf16", "cuda")
     ws = torch.empty(wkv7.bwd_varlen_workspace_bytes(N, TT, H, D, D), dtype=torch.uint8, device="cuda")
@@ -593,46 +756,17 @@ def recurrent_workload(steps, warmup):
 
 
 def other_workloads(steps, warmup, cpu=True):
-    """Latency of the two small forward shapes, then head size 128 forward
-    (B16 T4096 H32, trailing-padding mask, S0), the packed variable-length
-    forward, Gated DeltaNet (B8 T4096 H64 d64), the backward on the d64 and
-    d128 shapes, the Gated DeltaNet backward and the decode step (B512 H40
-    d64, 256 consecutive in-place steps)."""
+    """Latency of the two small forward shapes, the fp32 recurrent forward
+    at the B8 T4096 H64 d64 shape, the packed variable-length forward, Gated
+    DeltaNet (B8 T4096 H64 d64), the backward on the d64 and d128 shapes,
+    the Gated DeltaNet backward and the Gated DeltaNet decode step (B512 H40
+    d64, 256 consecutive in-place steps).  The d128 forward and the WKV7
+    decode are in every bench line (d128_entry, decode_entry)."""
     import torch
     from rwkv_linear_attention_amd import synth, wkv7
     out = small_latency(steps, warmup, cpu)
     out.update(recurrent_workload(steps, warmup))
     torch.cuda.empty_cache()
-    wl = synth.WORKLOADS[3]
-    B, T, H, D = wl["B"], wl["T"], wl["H"], wl["K"]
-    print(f"[bench] generating workload {wl['name']}", file=sys.stderr, flush=True)
-    inp = synth.make(3)
-    dev = {n: synth.to_torch(inp[n], "bf16", "cuda") for n in ("r", "w", "k", "v", "a", "b")}
-    s0 = torch.from_numpy(inp["s0"]).cuda()
-    mask = torch.from_numpy(inp["mask"]).cuda()
-    o = torch.empty((B, T, H, D), dtype=torch.bfloat16, device="cuda")
-    sf = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
-    ms = _time_launches(lambda i: wkv7.fwd(*(dev[n] for n in ("r", "w", "k", "v", "a", "b")),
-                                           initial_state=s0, mask=mask, out=o, final_state=sf),
-                        max(3, steps // 2), warmup)
-    nbytes = algorithmic_bytes(B, T, H, D, 2, True, True, True)
-    out[wl["name"]] = {"ms": round(ms, 5), "Mtokens_per_s": round(B * T / ms / 1e3, 3),
-                       "GB_per_s": round(nbytes / ms / 1e6, 1), "frac_of_8TBps": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
-                       "algorithmic_bytes": nbytes, "kernel": "chunked d128"}
-    if cpu:
-        import numpy as np
-        import oracle
-
-        def call(sel):
-            g = lambda x: np.stack([x[bb, :, h] for bb, h in sel])[:, :, None, :]
-            s0s = np.stack([inp["s0"][bb, h] for bb, h in sel])[:, None]
-            ms_ = np.stack([inp["mask"][bb] for bb, h in sel])
-            oracle.fwd(*(g(inp[n]) for n in ("r", "w", "k", "v", "a", "b")), s0s, ms_)
-        print("[bench] timing the CPU oracle (head size 128) on a sample", file=sys.stderr, flush=True)
-        out[wl["name"]]["cpu_oracle"] = oracle_sample_rate(call, B, H, T)
-    del dev, s0, mask, o, sf, inp
-    torch.cuda.empty_cache()
-
     out.update(varlen_workload(steps, warmup))
     torch.cuda.empty_cache()
     out.update(gdn_workload(steps, warmup, cpu))
@@ -646,54 +780,6 @@ def other_workloads(steps, warmup, cpu=True):
 
     wl = synth.WORKLOADS[4]
     B, NSTEP, H, D = wl["B"], wl["T"], wl["H"], wl["K"]
-    print(f"[bench] generating workload {wl['name']} (32 distinct steps, cycled)", file=sys.stderr, flush=True)
-    inp = synth.make(4, T=32)
-    dev = {n: synth.to_torch(inp[n], "bf16", "cuda") for n in ("r", "w", "k", "v", "a", "b")}
-    per_step = [{n: dev[n][:, t].contiguous() for n in dev} for t in range(32)]
-    state0 = torch.from_numpy(inp["s0"]).cuda()
-    state = state0.clone()
-    obuf = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
-
-    def run(i):
-        state.copy_(state0)
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for t in range(NSTEP):
-            x = per_step[t % 32]
-            wkv7.step(x["r"], x["w"], x["k"], x["v"], x["a"], x["b"], state, out=obuf)
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1)
-
-    settle(lambda: wkv7.step(per_step[0]["r"], per_step[0]["w"], per_step[0]["k"], per_step[0]["v"],
-                             per_step[0]["a"], per_step[0]["b"], state, out=obuf))
-    run(0)
-    times = [run(i) for i in range(3)]
-    ms_total = min(times)
-    step_bytes = 2 * B * H * D * D * 4 + 6 * B * H * D * 2 + B * H * D * 2
-    out[wl["name"]] = {"ms_256_steps": round(ms_total, 4), "us_per_step": round(ms_total * 1e3 / NSTEP, 2),
-                       "GB_per_s": round(step_bytes * NSTEP / ms_total / 1e6, 1),
-                       "frac_of_8TBps": round(step_bytes * NSTEP / ms_total / 1e6 / HBM_PEAK_GBS, 4),
-                       "bytes_per_step": step_bytes, "kernel": "step d64",
-                       "note": "inputs of 32 distinct steps cycled; state reset outside the timed region"}
-    if cpu:
-        import oracle
-        threads = min(16, len(os.sched_getaffinity(0)))
-        oracle.set_threads(threads)
-        sl = lambda n, t: inp[n][:, t]
-        t0 = time.perf_counter()
-        n = 0
-        while time.perf_counter() - t0 < 2.0:
-            oracle.step(*(sl(x, n % 32) for x in ("r", "w", "k", "v", "a", "b")), inp["s0"])
-            n += 1
-        dt = (time.perf_counter() - t0) / n
-        out[wl["name"]]["cpu_oracle"] = {"us_per_step": round(dt * 1e6, 1), "kind": "oracle", "cores": threads,
-                                         "sample": f"{n} whole steps (all B*H sequences)"}
-    del per_step, state, state0, obuf
-    torch.cuda.empty_cache()
-
     # Gated DeltaNet decode on the same shape: 256 consecutive in-place steps
     names = ("q", "k", "v", "g", "beta")
     print(f"[bench] generating Gated DeltaNet decode B{B} H{H} d{D} (32 distinct steps, cycled)",

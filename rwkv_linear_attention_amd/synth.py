@@ -134,3 +134,45 @@ def to_torch(x, dtype, device):
         return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
     bits = bf16_bits(x)
     return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(device)
+
+
+def make_device(workload, device, seed, B=None, T=None, H=None, K=None, step_major=False):
+    """Draw a workload with the same value recipe as make(), on the device
+    with torch's seeded generator (a different random stream from make()'s
+    numpy one, and much faster at full size).  Returns a dict of device
+    tensors in the I/O dtype -- r, w, k, v, a, b as [B,T,H,K], or [T,B,H,K]
+    with step_major (so that one decode step's inputs are contiguous) -- and
+    s0 (fp32 or None), mask (uint8 [B,T] or None), dtype."""
+    import torch
+    wl = WORKLOADS[workload] if isinstance(workload, int) else workload
+    B = wl["B"] if B is None else B
+    T = wl["T"] if T is None else T
+    H = wl["H"] if H is None else H
+    K = wl["K"] if K is None else K
+    dt = torch.float32 if wl["dtype"] == "f32" else torch.bfloat16
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    shp = (T, B, H, K) if step_major else (B, T, H, K)
+    randn = lambda: torch.randn(shp, generator=g, device=device, dtype=torch.float32)
+    unit = lambda x: x / torch.sqrt(torch.sum(x * x, dim=-1, keepdim=True))
+    out = {"dtype": wl["dtype"]}
+    out["r"] = randn().to(dt)
+    out["v"] = randn().to(dt)
+    out["k"] = unit(randn()).to(dt)
+    out["w"] = torch.clamp(-torch.exp(randn() * 0.5 - 0.5), -5.0, -0.01).to(dt)
+    kappa = unit(randn())
+    out["a"] = (-kappa).to(dt)
+    out["b"] = (kappa * torch.rand(shp, generator=g, device=device, dtype=torch.float32)).to(dt)
+    del kappa
+    out["s0"] = torch.randn((B, H, K, K), generator=g, device=device, dtype=torch.float32) * 0.1 \
+        if wl["init"] else None
+    if wl["mask"] == "trailing":
+        m = torch.ones((B, T), dtype=torch.uint8, device=device)
+        if T // 10:
+            m[:, T - T // 10:] = 0
+        out["mask"] = m
+    elif wl["mask"] == "bernoulli":
+        out["mask"] = (torch.rand((B, T), generator=g, device=device) < 0.9).to(torch.uint8)
+    else:
+        out["mask"] = None
+    return out
