@@ -410,25 +410,27 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def dispatch_sweep(reps=10):
-    """Recurrent vs chunked launch time (bf16, no state in, final state out)
-    for head sizes 64 and 128, B*H sequences in {1, 8, 64, 512} (as B = 1,
-    H = B*H), T from 16 to 2048.  One JSON line per shape."""
+def dispatch_sweep(reps=10, dtypes=("bf16", "f32")):
+    """Recurrent vs chunked launch time (no state in, final state out) for
+    both I/O types, head sizes 64 and 128, B*H sequences in {1, 8, 64, 512}
+    (as B = 1, H = B*H), T from 1 to 2048.  One JSON line per shape."""
     import torch
     from rwkv_linear_attention_amd import synth, wkv7
-    for D in (64, 128):
+    for dt in dtypes:
+      tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+      for D in (64, 128):
         for BH in (1, 8, 64, 512):
             for T in (1, 2, 4, 8, 16, 32, 48, 64, 96, 128, 256, 512, 1024, 2048):
-                inp = synth.make(2, B=1, T=T, H=BH, K=D, seed=7)
-                dev = {n: synth.to_torch(inp[n], "bf16", "cuda") for n in ("r", "w", "k", "v", "a", "b")}
-                o = torch.empty((1, T, BH, D), dtype=torch.bfloat16, device="cuda")
+                inp = synth.make(dict(synth.WORKLOADS[2], dtype=dt), B=1, T=T, H=BH, K=D, seed=7)
+                dev = {n: synth.to_torch(inp[n], dt, "cuda") for n in ("r", "w", "k", "v", "a", "b")}
+                o = torch.empty((1, T, BH, D), dtype=tdt, device="cuda")
                 sf = torch.empty((1, BH, D, D), dtype=torch.float32, device="cuda")
-                res = {"D": D, "BH": BH, "T": T}
+                res = {"dtype": dt, "D": D, "BH": BH, "T": T}
                 for name, algo in (("recurrent_us", wkv7.ALGO_RECURRENT), ("chunked_us", wkv7.ALGO_CHUNKED)):
                     ms = _time_launches(lambda i: wkv7.fwd(*(dev[n] for n in ("r", "w", "k", "v", "a", "b")),
                                                            out=o, final_state=sf, algo=algo), reps, 2)
                     res[name] = round(ms * 1e3, 2)
-                res["auto"] = "chunked" if wkv7.fwd_path(torch.bfloat16, 1, T, BH, D, D) == wkv7.ALGO_CHUNKED else "recurrent"
+                res["auto"] = "chunked" if wkv7.fwd_path(tdt, 1, T, BH, D, D) == wkv7.ALGO_CHUNKED else "recurrent"
                 print(json.dumps(res), flush=True)
                 del dev, o, sf, inp
 
@@ -723,41 +725,52 @@ def small_latency(steps, warmup, cpu=True):
     return out
 
 
-def recurrent_workload(steps, warmup):
-    """The recurrent forward (fp32 I/O always takes it) at the workload-2
-    shape, B8 T4096 H64 d64: 512 sequences, each a serial scan of 4096 token
-    steps.  Per token and head it does 9 K V flops (b^T S, the decay, the two
-    rank-one updates, S^T r) on the fp32 vector units, so it is reported
-    against both the fp32 vector peak and HBM."""
+def fp32_workload(steps, warmup):
+    """fp32 I/O at the workload-2 shape, B8 T4096 H64 d64, on both kernels.
+    The chunked kernel (AUTO) runs the chunk form on the fp32 matrix cores:
+    2 (8 L D + 4 D^2) flops per token and head at L = 16, 27 flop per HBM
+    byte, above the fp32-matrix ridge (157.3 TFLOP/s / 8 TB/s = 20 flop/B),
+    so it is reported against the fp32 matrix peak.  The recurrent kernel
+    does 9 D^2 vector flops per token and head and is reported against the
+    fp32 vector peak."""
     import torch
     from rwkv_linear_attention_amd import synth, wkv7
     wl = synth.WORKLOADS[2]
     B, T, H, D = wl["B"], wl["T"], wl["H"], wl["K"]
-    print("[bench] generating the fp32 recurrent workload", file=sys.stderr, flush=True)
+    print("[bench] generating the fp32 workload", file=sys.stderr, flush=True)
     inp = synth.make(2)
     dev = {n: synth.to_torch(inp[n], "f32", "cuda") for n in ("r", "w", "k", "v", "a", "b")}
     o = torch.empty((B, T, H, D), dtype=torch.float32, device="cuda")
     sf = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
-    ms = _time_launches(lambda i: wkv7.fwd(*(dev[n] for n in ("r", "w", "k", "v", "a", "b")), out=o,
-                                           final_state=sf), max(3, steps // 5), warmup)
     nbytes = algorithmic_bytes(B, T, H, D, 4, False, True, False)
-    flops = 9 * B * T * H * D * D
-    name = f"fwd_f32_B{B}_T{T}_H{H}_d{D}"
-    out = {name: {"ms": round(ms, 4), "Mtokens_per_s": round(B * T / ms / 1e3, 3),
-                  "GB_per_s": round(nbytes / ms / 1e6, 1), "frac_of_8TBps": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
-                  "algorithmic_bytes": nbytes,
-                  "roofline": {"bound": "alu", "unit": "TFLOP/s", "peak": FP32_VECTOR_PEAK_TFLOPS,
-                               "achieved": round(flops / ms / 1e9, 2),
-                               "frac": round(flops / ms / 1e9 / FP32_VECTOR_PEAK_TFLOPS, 4), "flops": flops,
-                               "note": "9 K V vector flops per token and head"},
-                  "kernel": "recurrent d64 (fp32 I/O)"}}
+    out = {}
+    for algo, kind in ((wkv7.ALGO_AUTO, "chunked"), (wkv7.ALGO_RECURRENT, "recurrent")):
+        ms = _time_launches(lambda i: wkv7.fwd(*(dev[n] for n in ("r", "w", "k", "v", "a", "b")), out=o,
+                                               final_state=sf, algo=algo), max(3, steps // 5), warmup)
+        if kind == "chunked":
+            assert wkv7.fwd_path(torch.float32, B, T, H, D, D) == wkv7.ALGO_CHUNKED
+            flops = 2 * (8 * 16 * D + 4 * D * D) * B * T * H
+            roof = {"bound": "mfma", "unit": "TFLOP/s", "peak": FP32_MFMA_PEAK_TFLOPS, "dtype": "f32",
+                    "note": "chunk-form flops, 2 (8 L D + 4 D^2) per token and head"}
+            peak = FP32_MFMA_PEAK_TFLOPS
+        else:
+            flops = 9 * B * T * H * D * D
+            roof = {"bound": "alu", "unit": "TFLOP/s", "peak": FP32_VECTOR_PEAK_TFLOPS,
+                    "note": "9 K V vector flops per token and head"}
+            peak = FP32_VECTOR_PEAK_TFLOPS
+        roof.update({"achieved": round(flops / ms / 1e9, 2), "frac": round(flops / ms / 1e9 / peak, 4),
+                     "flops": flops})
+        out[f"fwd_f32_B{B}_T{T}_H{H}_d{D}_{kind}"] = {
+            "ms": round(ms, 4), "Mtokens_per_s": round(B * T / ms / 1e3, 3), "GB_per_s": round(nbytes / ms / 1e6, 1),
+            "frac_of_8TBps": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes,
+            "roofline": roof, "kernel": f"{kind} d64 (fp32 I/O)"}
     del dev, o, sf, inp
     return out
 
 
 def other_workloads(steps, warmup, cpu=True):
-    """Latency of the two small forward shapes, the fp32 recurrent forward
-    at the B8 T4096 H64 d64 shape, the packed variable-length forward, Gated
+    """Latency of the two small forward shapes, the fp32 forward (chunked
+    and recurrent) at the B8 T4096 H64 d64 shape, the packed variable-length forward, Gated
     DeltaNet (B8 T4096 H64 d64), the backward on the d64 and d128 shapes,
     the Gated DeltaNet backward and the Gated DeltaNet decode step (B512 H40
     d64, 256 consecutive in-place steps).  The d128 forward and the WKV7
@@ -765,7 +778,7 @@ def other_workloads(steps, warmup, cpu=True):
     import torch
     from rwkv_linear_attention_amd import synth, wkv7
     out = small_latency(steps, warmup, cpu)
-    out.update(recurrent_workload(steps, warmup))
+    out.update(fp32_workload(steps, warmup))
     torch.cuda.empty_cache()
     out.update(varlen_workload(steps, warmup))
     torch.cuda.empty_cache()

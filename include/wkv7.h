@@ -50,7 +50,7 @@ typedef enum {
 typedef enum {
     WKV7_ALGO_AUTO = 0,       /* library chooses (see wkv7_fwd)            */
     WKV7_ALGO_RECURRENT = 1,  /* token-by-token fp32 recurrence            */
-    WKV7_ALGO_CHUNKED = 2     /* 16-token chunks on bf16 MFMA (bf16 only)  */
+    WKV7_ALGO_CHUNKED = 2     /* 16-token chunks on the matrix cores        */
 } wkv7_algo_t;
 
 typedef enum {
@@ -82,11 +82,11 @@ typedef enum {
  *                  the same buffer as initial_state (in-place state passing)
  *                  when n_state == B (or B == 1); any other overlap between
  *                  buffers is undefined.
- *   algo           WKV7_ALGO_AUTO picks the chunked kernel for bf16 when the
- *                  sequences are long enough to amortise it and the
- *                  recurrent kernel otherwise; fp32 always runs the recurrent
- *                  kernel.  WKV7_ALGO_CHUNKED with fp32 returns
- *                  WKV7_ERR_UNSUPPORTED.
+ *   algo           WKV7_ALGO_AUTO picks the chunked kernel when the
+ *                  sequences are long enough to amortise it (T >= 16; bf16
+ *                  I/O runs on bf16 matrix cores with fp32 accumulation,
+ *                  fp32 I/O on fp32 matrix cores) and the recurrent kernel
+ *                  otherwise.
  *   stream         hipStream_t to enqueue on.
  * With T == 0, o is empty and final_state (if given) receives initial_state
  * in every row (zeros when initial_state is NULL).
@@ -176,7 +176,9 @@ wkv7_status_t wkv7_fwd_varlen(int dtype, int N, int total_T, int H, int K, int V
  *   o              [B,T,H,V] dtype.  Written.
  *   final_state    [B,H,K,V] fp32, or NULL.  Written.  May be the same buffer
  *                  as initial_state only when n_state == B (or B == 1).
- *   algo           as for wkv7_fwd.
+ *   algo           as for wkv7_fwd, except that the chunked kernel takes
+ *                  bf16 only: AUTO runs fp32 on the recurrent kernel, and
+ *                  WKV7_ALGO_CHUNKED with fp32 returns WKV7_ERR_UNSUPPORTED.
  *   stream         hipStream_t to enqueue on.
  */
 wkv7_status_t wkv7_gdn_fwd(int dtype, int B, int T, int H, int K, int V,

@@ -21,6 +21,14 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 // recurrent kernel is faster at T <= 4 (12-16 vs 21 us) and slower at T = 8
 // (22.6 vs 20.9 us).
 constexpr int kChunkedMinT = 16;
+// fp32 I/O (WKV7; Gated DeltaNet fp32 runs on the recurrent kernel): the
+// same threshold, measured the same way.  From T = 16 the fp32 chunked kernel
+// is as fast or faster for every shape (within call overhead at T = 16 with
+// few sequences, 1.3x faster at head size 128 with 512 sequences), and 1.35x
+// (head size 64) to 1.7x (128) faster from T = 512; below 16 the recurrent
+// kernel is as fast or faster (13.8 vs 25.5 us at T = 1, head size 128, 512
+// sequences).
+constexpr int kChunkedMinTF32 = 16;
 
 wkv7_status_t check_common(int dtype, int B, int H, int K, int V)
 {
@@ -31,13 +39,21 @@ wkv7_status_t check_common(int dtype, int B, int H, int K, int V)
     return WKV7_OK;
 }
 
-int choose_path(int dtype, int T, int algo)
+// gdn: Gated DeltaNet inputs (the chunked kernel takes them with bf16 I/O only).
+int choose_path(int dtype, int T, int algo, bool gdn = false)
 {
+    const bool chunked_ok = dtype == WKV7_BF16 || !gdn;
     if (algo == WKV7_ALGO_RECURRENT) return WKV7_ALGO_RECURRENT;
-    if (algo == WKV7_ALGO_CHUNKED) return dtype == WKV7_BF16 ? WKV7_ALGO_CHUNKED : -1;
+    if (algo == WKV7_ALGO_CHUNKED) return chunked_ok ? WKV7_ALGO_CHUNKED : -1;
     if (algo != WKV7_ALGO_AUTO) return -1;
-    if (dtype == WKV7_F32) return WKV7_ALGO_RECURRENT;
-    return T >= kChunkedMinT ? WKV7_ALGO_CHUNKED : WKV7_ALGO_RECURRENT;
+    const int min_t = dtype == WKV7_BF16 ? kChunkedMinT : kChunkedMinTF32;
+    return chunked_ok && T >= min_t ? WKV7_ALGO_CHUNKED : WKV7_ALGO_RECURRENT;
+}
+
+hipError_t launch_path(int path, int dtype, const wkv7::FwdArgs &args, hipStream_t s)
+{
+    if (path != WKV7_ALGO_CHUNKED) return wkv7::launch_recurrent(dtype, args, s);
+    return dtype == WKV7_BF16 ? wkv7::launch_chunked(args, s) : wkv7::launch_chunked_f32(args, s);
 }
 
 // Packed sequences: the lengths live on the device, so AUTO cannot look at
@@ -45,11 +61,11 @@ int choose_path(int dtype, int T, int algo)
 // tokens: per sequence it is as fast as the recurrent kernel within call
 // overhead below 16 tokens and faster from 16 on, so one long sequence among
 // many short ones (a mean length under 16) still runs at chunked speed.
-int choose_packed_path(int dtype, int total_T, int N, int algo)
+int choose_packed_path(int dtype, int total_T, int N, int algo, bool gdn = false)
 {
     if (algo == WKV7_ALGO_AUTO && dtype == WKV7_BF16)
         return total_T > 0 ? WKV7_ALGO_CHUNKED : WKV7_ALGO_RECURRENT;
-    return choose_path(dtype, total_T / N, algo);
+    return choose_path(dtype, total_T / N, algo, gdn);
 }
 
 std::atomic<int> g_wait_limit{wkv7::kDefaultWaitLimit};
@@ -97,7 +113,7 @@ const char *wkv7_strerror(int status)
     switch (status) {
     case WKV7_OK: return "ok";
     case WKV7_ERR_INVALID_ARG: return "invalid argument (null pointer, bad size, dtype or alignment)";
-    case WKV7_ERR_UNSUPPORTED: return "unsupported configuration (K == V in {64, 128} required; chunked path is bf16 only)";
+    case WKV7_ERR_UNSUPPORTED: return "unsupported configuration (K == V in {64, 128} required; the chunked Gated DeltaNet path is bf16 only)";
     case WKV7_ERR_HIP: return "HIP kernel launch failed";
     case WKV7_ERR_TOO_LARGE: return "request exceeds the fixed scratch buffer of the allocation-free entry point";
     default: return "unknown status";
@@ -151,8 +167,7 @@ wkv7_status_t wkv7_fwd(int dtype, int B, int T, int H, int K, int V,
     }
     wkv7::FwdArgs args{B, T, H, K, r, w, k, v, a, b, initial_state, mask, o, final_state};
     args.n_state = initial_state ? n_state : 0;
-    hipError_t e = path == WKV7_ALGO_CHUNKED ? wkv7::launch_chunked(args, s)
-                                             : wkv7::launch_recurrent(dtype, args, s);
+    const hipError_t e = launch_path(path, dtype, args, s);
     return e == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
 }
 
@@ -191,8 +206,7 @@ wkv7_status_t wkv7_fwd_varlen(int dtype, int N, int total_T, int H, int K, int V
     args.state_map = state_map;
     args.n_state = initial_state ? n_state : 0;
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = path == WKV7_ALGO_CHUNKED ? wkv7::launch_chunked(args, s)
-                                             : wkv7::launch_recurrent(dtype, args, s);
+    const hipError_t e = launch_path(path, dtype, args, s);
     return e == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
 }
 
@@ -220,7 +234,7 @@ wkv7_status_t wkv7_gdn_fwd(int dtype, int B, int T, int H, int K, int V,
         if (n_state == 1 && B > 1 && final_state == initial_state) return WKV7_ERR_INVALID_ARG;
     }
     if (final_state && !aligned16(final_state)) return WKV7_ERR_INVALID_ARG;
-    const int path = choose_path(dtype, T, algo);
+    const int path = choose_path(dtype, T, algo, true);
     if (path < 0) return WKV7_ERR_UNSUPPORTED;
 
     hipStream_t s = (hipStream_t)stream;
@@ -239,8 +253,7 @@ wkv7_status_t wkv7_gdn_fwd(int dtype, int B, int T, int H, int K, int V,
     wkv7::FwdArgs args{B, T, H, K, q, g, k, v, beta, nullptr, initial_state, nullptr, o, final_state};
     args.n_state = initial_state ? n_state : 0;
     args.gdn = true;
-    hipError_t e = path == WKV7_ALGO_CHUNKED ? wkv7::launch_chunked(args, s)
-                                             : wkv7::launch_recurrent(dtype, args, s);
+    const hipError_t e = launch_path(path, dtype, args, s);
     return e == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
 }
 
@@ -272,7 +285,7 @@ wkv7_status_t wkv7_gdn_fwd_varlen(int dtype, int N, int total_T, int H, int K, i
         if ((state_map || (n_state == 1 && N > 1)) && final_state == initial_state) return WKV7_ERR_INVALID_ARG;
     }
     if (final_state && !aligned16(final_state)) return WKV7_ERR_INVALID_ARG;
-    const int path = choose_packed_path(dtype, total_T, N, algo);
+    const int path = choose_packed_path(dtype, total_T, N, algo, true);
     if (path < 0) return WKV7_ERR_UNSUPPORTED;
     wkv7::FwdArgs args{N, total_T, H, K, q, g, k, v, beta, nullptr, initial_state, nullptr, o, final_state};
     args.cu_seqlens = cu_seqlens;
@@ -280,8 +293,7 @@ wkv7_status_t wkv7_gdn_fwd_varlen(int dtype, int N, int total_T, int H, int K, i
     args.n_state = initial_state ? n_state : 0;
     args.gdn = true;
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = path == WKV7_ALGO_CHUNKED ? wkv7::launch_chunked(args, s)
-                                             : wkv7::launch_recurrent(dtype, args, s);
+    const hipError_t e = launch_path(path, dtype, args, s);
     return e == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
 }
 

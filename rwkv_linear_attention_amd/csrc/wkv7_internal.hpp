@@ -110,7 +110,8 @@ int check_bwd_args(int dtype, int B, int T, int H, int K, int V, const void *r, 
 
 // dtype: 0 = fp32, 1 = bf16 (values of wkv7_dtype_t).
 hipError_t launch_recurrent(int dtype, const FwdArgs &args, hipStream_t stream);
-hipError_t launch_chunked(const FwdArgs &args, hipStream_t stream);     // bf16 only
+hipError_t launch_chunked(const FwdArgs &args, hipStream_t stream);     // bf16 I/O
+hipError_t launch_chunked_f32(const FwdArgs &args, hipStream_t stream); // fp32 I/O, not Gated DeltaNet
 hipError_t launch_step(int dtype, const StepArgs &args, hipStream_t stream);
 hipError_t launch_backward(int dtype, const BwdArgs &args, hipStream_t stream);
 hipError_t launch_gdn_backward(int dtype, const GdnBwdArgs &args, hipStream_t stream);

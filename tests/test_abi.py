@@ -69,7 +69,6 @@ def step(L, dtype=1, B=1, H=1, K=64, V=64, ptrs=None):
     (dict(K=32, V=32), wkv7.ERR_UNSUPPORTED),
     (dict(K=256, V=256), wkv7.ERR_UNSUPPORTED),
     (dict(algo=7), wkv7.ERR_INVALID_ARG),
-    (dict(dtype=0, algo=2), wkv7.ERR_UNSUPPORTED),
 ])
 def test_fwd_rejects(L, kw, code):
     assert fwd(L, **kw) == code
@@ -129,8 +128,10 @@ def test_path_choice(L):
     R, C = wkv7.ALGO_RECURRENT, wkv7.ALGO_CHUNKED
     assert L.wkv7_fwd_path(1, 8, 4096, 64, 64, 64, 0) == C
     assert L.wkv7_fwd_path(1, 16, 4096, 32, 128, 128, 0) == C
-    assert L.wkv7_fwd_path(0, 1, 64, 1, 64, 64, 0) == R          # fp32 is never chunked
-    assert L.wkv7_fwd_path(0, 1, 64, 1, 64, 64, 2) == -1
+    assert L.wkv7_fwd_path(0, 1, 15, 1, 64, 64, 0) == R          # fp32: short sequences
+    assert L.wkv7_fwd_path(0, 1, 16, 1, 128, 128, 0) == C        # fp32 chunked from T = 16 (measured)
+    assert L.wkv7_fwd_path(0, 8, 4096, 64, 64, 64, 0) == C
+    assert L.wkv7_fwd_path(0, 1, 8, 1, 128, 128, 2) == C         # forced
     assert L.wkv7_fwd_path(1, 1, 8, 1, 64, 64, 0) == R           # very short sequences
     assert L.wkv7_fwd_path(1, 1, 15, 1, 128, 128, 0) == R
     assert L.wkv7_fwd_path(1, 1, 16, 1, 64, 64, 0) == C          # measured crossover
@@ -160,7 +161,6 @@ def varlen(L, dtype=1, N=2, TT=40, H=1, K=64, V=64, cu=GOOD, ptrs=None, s0=None,
     (dict(s0=ODD, n_state=2), wkv7.ERR_INVALID_ARG),
     (dict(ptrs=[GOOD] * 6 + [None]), wkv7.ERR_INVALID_ARG),
     (dict(K=64, V=128), wkv7.ERR_UNSUPPORTED),
-    (dict(dtype=0, algo=2), wkv7.ERR_UNSUPPORTED),
     (dict(algo=7), wkv7.ERR_INVALID_ARG),
 ])
 def test_varlen_validation(L, kw, code):

@@ -28,10 +28,9 @@ def run_case(inp, algo, what):
 
 # ---- the named workloads ------------------------------------------------------
 
-def test_workload0_fp32_full():
-    inp = synth.make(0)
-    assert wkv7.fwd_path(torch.float32, 1, 64, 1, 64, 64) == REC
-    run_case(inp, wkv7.ALGO_AUTO, "workload 0")
+@pytest.mark.parametrize("algo", [REC, CHK, wkv7.ALGO_AUTO])
+def test_workload0_fp32_full(algo):
+    run_case(synth.make(0), algo, f"workload 0 algo {algo}")
 
 
 @pytest.mark.parametrize("algo", [REC, CHK, wkv7.ALGO_AUTO])
@@ -61,19 +60,38 @@ def test_full_size_workload_all_sequences(idx):
     print(f"workload {idx}: worst output ratio {wo:.3f}, worst state ratio {ws:.3f}")
 
 
-def test_full_size_fp32_recurrent_all_sequences():
-    """The workload-2 shape (B8 T4096 H64 d64) with fp32 I/O, as the
-    benchmark times it under ALGO_AUTO; every sequence against the fp32 rule
-    (max-abs 1e-4 on o and the final state)."""
+@pytest.mark.parametrize("algo", [wkv7.ALGO_AUTO, REC])
+def test_full_size_fp32_all_sequences(algo):
+    """The workload-2 shape (B8 T4096 H64 d64) with fp32 I/O: under AUTO
+    (the fp32 chunked kernel, as the benchmark times it) and on the
+    recurrent kernel; every sequence against the fp32 rule (max-abs 1e-4 on
+    o and the final state)."""
     inp = dict(synth.make(2), dtype="f32")
     B, T, H, D = inp["r"].shape
+    if algo == wkv7.ALGO_AUTO:
+        assert wkv7.fwd_path(torch.float32, B, T, H, D, D) == CHK
+    dev = hz.to_dev(inp)
+    o, sf = hz.gpu_fwd(dev, algo=algo)
+    torch.cuda.synchronize()
+    del dev
+    o_ref, s_ref = hz.oracle_fwd(inp)
+    wo, ws = hz.check_sequences("f32", o, o_ref, sf, s_ref, f"fp32 workload-2 shape algo {algo} all sequences")
+    print(f"fp32 B8 T4096 H64 d64 algo {algo}: worst output ratio {wo:.3f}, worst state ratio {ws:.3f}")
+
+
+def test_full_size_fp32_d128_all_sequences():
+    """The workload-3 shape (B16 T4096 H32 d128, initial state, trailing
+    padding) with fp32 I/O under AUTO (fp32 chunked kernel), every sequence."""
+    inp = dict(synth.make(3), dtype="f32")
+    B, T, H, D = inp["r"].shape
+    assert wkv7.fwd_path(torch.float32, B, T, H, D, D) == CHK
     dev = hz.to_dev(inp)
     o, sf = hz.gpu_fwd(dev)
     torch.cuda.synchronize()
     del dev
     o_ref, s_ref = hz.oracle_fwd(inp)
-    wo, ws = hz.check_sequences("f32", o, o_ref, sf, s_ref, "fp32 workload-2 shape all sequences")
-    print(f"fp32 B8 T4096 H64 d64: worst output ratio {wo:.3f}, worst state ratio {ws:.3f}")
+    wo, ws = hz.check_sequences("f32", o, o_ref, sf, s_ref, "fp32 workload-3 shape all sequences")
+    print(f"fp32 B16 T4096 H32 d128: worst output ratio {wo:.3f}, worst state ratio {ws:.3f}")
 
 
 def test_workload4_decode_steps_all_sequences():
@@ -115,11 +133,65 @@ def test_shapes_bf16(D, T, algo):
 
 
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("T", [1, 17, 200])
-def test_shapes_fp32(D, T):
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 63, 64, 65, 200, 1000])
+@pytest.mark.parametrize("algo", [REC, CHK])
+def test_shapes_fp32(D, T, algo):
     wl = dict(synth.WORKLOADS[0], dtype="f32")
-    inp = synth.make(wl, B=3, T=T, H=1, K=D, seed=11 * T + D, init=True, mask="bernoulli")
-    run_case(inp, REC, f"fp32 D={D} T={T}")
+    inp = synth.make(wl, B=3, T=T, H=2, K=D, seed=11 * T + D, init=True, mask="bernoulli")
+    run_case(inp, algo, f"fp32 D={D} T={T} algo={algo}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("kind", ["zeros", "trailing", "leading", "nonfinite_masked", "extreme_decay", "no_state"])
+def test_fp32_chunked_cases(D, kind):
+    """The fp32 chunked kernel on masks, non-finite inputs at masked tokens,
+    chunks that need the exact token-by-token path, and no initial state."""
+    wl = dict(synth.WORKLOADS[0], dtype="f32")
+    B, T, H = 2, 100, 2
+    inp = synth.make(wl, B=B, T=T, H=H, K=D, seed=900 + D, init=kind != "no_state", mask="bernoulli")
+    if kind == "zeros":
+        inp["mask"] = np.zeros((B, T), np.uint8)
+    elif kind == "trailing":
+        inp["mask"] = np.ones((B, T), np.uint8)
+        inp["mask"][:, 83:] = 0
+    elif kind == "leading":
+        inp["mask"] = np.ones((B, T), np.uint8)
+        inp["mask"][:, :37] = 0
+    elif kind == "extreme_decay":
+        w = inp["w"].copy()
+        w[:, 20] = -1e9
+        w[1, 55, :, :8] = -1e9
+        w[0, 70, 1, 3] = 0.05
+        w[0, 80:96] = -20.0
+        inp["w"] = w
+    o_ref, s_ref = hz.oracle_fwd(inp)
+    if kind == "nonfinite_masked":
+        masked = inp["mask"] == 0
+        for n, val in zip("wkvab", (np.nan, np.inf, np.nan, -np.inf, np.nan)):
+            x = np.array(inp[n], copy=True)
+            x[masked] = val
+            inp[n] = x
+    dev = hz.to_dev(inp)
+    o, sf = hz.gpu_fwd(dev, algo=CHK)
+    torch.cuda.synchronize()
+    hz.check("f32", hz.to_np(o), o_ref, hz.to_np(sf), s_ref, f"fp32 chunked {kind} D={D}")
+    if kind == "zeros":
+        assert torch.equal(sf, dev["s0"]), "all-masked sequence must leave the state bit-exact"
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_fp32_chunked_equals_recurrent(D):
+    inp = synth.make(dict(synth.WORKLOADS[0], dtype="f32"), B=2, T=300, H=2, K=D, seed=97 + D, init=True,
+                     mask="bernoulli")
+    dev = hz.to_dev(inp)
+    o1, s1 = hz.gpu_fwd(dev, algo=REC)
+    o2, s2 = hz.gpu_fwd(dev, algo=CHK)
+    torch.cuda.synchronize()
+    o_ref, s_ref = hz.oracle_fwd(inp)
+    hz.check("f32", hz.to_np(o1), o_ref, hz.to_np(s1), s_ref, "fp32 recurrent")
+    hz.check("f32", hz.to_np(o2), o_ref, hz.to_np(s2), s_ref, "fp32 chunked")
+    hz.check("f32", hz.to_np(o2), hz.to_np(o1), hz.to_np(s2), hz.to_np(s1), "fp32 chunked vs recurrent",
+             scale=2.0)
 
 
 @pytest.mark.parametrize("D", [64, 128])
