@@ -440,21 +440,25 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(D == 64 ?
 
     // raw inputs of the chunk, four channels per thread; a token that does
     // not update gets w = k = a = b = 0 and v = 0 (an exact identity step),
-    // tokens past T are all zero
-    if (tid < kL) s.upd[tid] = (tid < Lc) && (GDN || !mask || mask[tok0 + t0 + tid] != 0);
-    __syncthreads();
+    // tokens past T are all zero.  The loads carry no condition (a token
+    // past the chunk's end reads the chunk's last token, then takes zeros)
+    // and the mask byte is applied afterwards, so that they are all in
+    // flight together.
     {
         static_assert(NT == kL * D / 4, "one thread per (token, 4 channels)");
         const int t = tid / (D / 4), c4 = 4 * (tid % (D / 4));
-        const bool valid = t < Lc, up = s.upd[t] != 0;
-        const size_t gi = tokbase + (size_t)t * H * D + c4;
+        const bool valid = t < Lc;
+        const size_t gi = tokbase + (size_t)min(t, Lc - 1) * H * D + c4;
         using R4 = raw4<T_IO>;
-        *(typename R4::type *)&s.DO[t][c4] = valid ? R4::load(d_o, gi) : R4::zero();
-        *(typename R4::type *)&s.V[t][c4] = up ? R4::load(v, gi) : R4::zero();
         if constexpr (GDN) {
-            const size_t si = tokbase / D + (size_t)t * H;
-            const f32x4 q4 = valid ? io4<T_IO>::load(r, gi) : z, k4 = valid ? io4<T_IO>::load(k, gi) : z;
-            const float gg = valid ? io<T_IO>::load(w, si) : 0.0f, bt = valid ? io<T_IO>::load(a, si) : 0.0f;
+            const size_t si = tokbase / D + (size_t)min(t, Lc - 1) * H;
+            const typename R4::type do4 = R4::load(d_o, gi), v4 = R4::load(v, gi);
+            const f32x4 q4l = io4<T_IO>::load(r, gi), k4l = io4<T_IO>::load(k, gi);
+            const float ggl = io<T_IO>::load(w, si), btl = io<T_IO>::load(a, si);
+            const f32x4 q4 = valid ? q4l : z, k4 = valid ? k4l : z;
+            const float gg = valid ? ggl : 0.0f, bt = valid ? btl : 0.0f;
+            *(typename R4::type *)&s.DO[t][c4] = valid ? do4 : R4::zero();
+            *(typename R4::type *)&s.V[t][c4] = valid ? v4 : R4::zero();
             const float iq = inv_norm<D>(q4), ik = inv_norm<D>(k4);
             const f32x4 kn = k4 * ik;
             *(f32x4 *)&s.R[t][c4] = q4 * iq;
@@ -467,13 +471,26 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(D == 64 ?
                 s.gs[1][t] = bt;
                 s.gs[2][t] = iq;
                 s.gs[3][t] = ik;
+                s.upd[t] = valid;
             }
         } else {
-            *(f32x4 *)&s.R[t][c4] = valid ? io4<T_IO>::load(r, gi) : z;
-            *(f32x4 *)&s.G[t][c4] = up ? io4<T_IO>::load(w, gi) : z;
-            *(f32x4 *)&s.K[t][c4] = up ? io4<T_IO>::load(k, gi) : z;
-            *(f32x4 *)&s.A[t][c4] = up ? io4<T_IO>::load(a, gi) : z;
-            *(f32x4 *)&s.B[t][c4] = up ? io4<T_IO>::load(b, gi) : z;
+            int mb = 1;
+            if (mask) mb = mask[tok0 + t0 + min(t, Lc - 1)];
+            const typename R4::type do4 = R4::load(d_o, gi), v4 = R4::load(v, gi);
+            const f32x4 r4 = io4<T_IO>::load(r, gi), w4 = io4<T_IO>::load(w, gi);
+            const f32x4 k4 = io4<T_IO>::load(k, gi), a4 = io4<T_IO>::load(a, gi);
+            const f32x4 b4 = io4<T_IO>::load(b, gi);
+            // (an empty asm keeps the compare of the mask byte after the loads)
+            asm volatile("" : "+v"(mb));
+            const bool up = valid && mb != 0;
+            *(typename R4::type *)&s.DO[t][c4] = valid ? do4 : R4::zero();
+            *(typename R4::type *)&s.V[t][c4] = up ? v4 : R4::zero();
+            *(f32x4 *)&s.R[t][c4] = valid ? r4 : z;
+            *(f32x4 *)&s.G[t][c4] = up ? w4 : z;
+            *(f32x4 *)&s.K[t][c4] = up ? k4 : z;
+            *(f32x4 *)&s.A[t][c4] = up ? a4 : z;
+            *(f32x4 *)&s.B[t][c4] = up ? b4 : z;
+            if (c4 == 0) s.upd[t] = up;
         }
     }
     __syncthreads();
@@ -761,72 +778,101 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(D == 64 ?
 
 // ---- launch 1: the two recurrences in chunk form -------------------------------
 
-template <int D> struct alignas(16) ChainLds {
-    static constexpr int LD = D + 4;    // row stride of the L x D tiles (16-byte aligned rows)
-    float W[kL][LD];                    // raw (masked) w
-    float G[kL][LD];                    // decay prefix
+// Value columns of the state are independent in both recurrences (column j
+// of S' reads only column j of S, and the same holds for dS), so a sequence's
+// state is split over workgroups of four waves and 64 columns (kChainCols);
+// each workgroup forms the chunk's token-by-token matrices itself.
+constexpr int kChainWaves = 4;
+constexpr int kChainCols = 16 * kChainWaves;
+
+// LDS of one chunk: under 40 KB at D = 128 with bf16 I/O, so four workgroups
+// share a CU.  v and d_o (this workgroup's columns only) stay in the I/O
+// type; the chunk matrices and T take the place of the decay prefix once
+// the operands are scaled.
+template <int D, typename T_IO> struct alignas(16) ChainLds {
+    static constexpr int LD = D + 4;                             // fp32 tile rows (16-byte aligned)
+    static constexpr int LDY = kChainCols + 16 / sizeof(T_IO);   // I/O-type tile rows (16-byte aligned)
+    union {
+        float G[kL][LD];                // w, then its decay prefix (exact path: raw w again)
+        // after the scaling: the chunk matrices as two partial sums each
+        // (the two halves of the channel contraction), M[2 mi + half]: mi 0
+        // M_ba (forward: transposed), mi 1 M_bk (forward) or M_ra (backward)
+        float M[4][kL][20];
+    };
     float A[kL][LD];                    // a, then A^ = a e^{-G}
     float B[kL][LD];                    // b, then B~ = b e^{G_{t-1}}
     float X[kL][LD];                    // forward: k, then K^ = k e^{-G}; backward: r, then R~ = r e^G
-    float Y[kL][LD];                    // forward: v; backward: d_o
-    float M[2][kL][kL + 1];             // M_ba; forward M_bk, backward M_ra
-    float Tm[kL][20];                   // T = (I - M_ba)^{-1}
+    T_IO Y[kL][LDY];                    // forward: v; backward: d_o (this workgroup's columns)
     float EGL[D];
     int upd[kL];
 };
 
-// Store a state slice held as St[ti][i] = S[16 ti + 4q + i][c0 + m] (lane (q, m))
-// into a row-major D x D matrix, through one running pointer (a separate
-// address per row would stay live across the chunk loop).
+// Store a state slice held as St[ti][i] = S[16 ti + 4q + i][col] (lane (q, m))
+// into a row-major D x D matrix at dst (the same address in every lane),
+// through one running 32-bit byte offset (a separate address per row would
+// stay live across the chunk loop).
 template <int D>
-__device__ __forceinline__ void store_slice(float *dst, const f32x4 *St, int q, int m, int c0)
+__device__ __forceinline__ void store_slice(float *dst, const f32x4 *St, int q, int col)
 {
-    float *p = dst + (size_t)(4 * q) * D + c0 + m;
+    unsigned off = (unsigned)(4 * q * D + col) * 4u;
 #pragma unroll
     for (int ti = 0; ti < D / 16; ++ti)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            *p = St[ti][i];
-            p += (i == 3) ? 13 * D : D;
-            asm volatile("" : "+v"(p));
+            *(float *)((char *)dst + off) = St[ti][i];
+            off += (i == 3) ? 13 * D * 4 : D * 4;
+            asm volatile("" : "+v"(off));
         }
 }
 
-// 2 B H workgroups of D/16 waves; wave w keeps columns 16w .. 16w + 15 of the
-// state (or state gradient) in MFMA accumulator layout, St[ti][i] = row
-// 16 ti + 4q + i, column 16w + m for lane (q, m).  Workgroups [0, nbh) run the
-// forward recurrence chunk by chunk,
+// Workgroups for the 2 nbh (role, sequence-head) pairs x D / 64 column
+// groups.  Role 0 (forward) runs the forward recurrence chunk by chunk,
 //   X = B~ S + M_bk V,  U = T X,  S <- diag(e^{G_L}) (S + A^T U + K^T V),
-// storing the state before every 16-token chunk (ckpt[bh][c]).  Workgroups [nbh, 2 nbh) run the state-gradient
-// recurrence backwards, with dS' the gradient at the chunk's end,
+// storing the state before every 16-token chunk (ckpt[bh][c]); role 1
+// runs the state-gradient recurrence backwards, with dS' the gradient at
+// the chunk's end,
 //   dY = diag(e^{G_L}) dS',  dU = A^ dY + M_ra^T dO,  dX = T^T dU,
 //   dS <- dY + R~^T dO + B~^T dX,
-// storing dS' of every chunk first (dck[bh][c]).  In every product that
+// storing dS' of every chunk first (dck[bh][c]).  Wave w keeps columns
+// col = 64 g + 16 w + m of its group g in MFMA accumulator layout,
+// St[ti][i] = row 16 ti + 4q + i, for lane (q, m).  In every product that
 // contracts over the state's rows or over the chunk's tokens, the
 // contraction index is taken in the order the accumulator layout holds it
 // (step st of tile ti takes rows 16 ti + 4q + st), so the state and the
 // intermediate tiles feed the matrix cores straight from registers.  A chunk
 // with a positive w, or whose decay reaches e^{-60}, runs token by token.
-// The next chunk's inputs are loaded while the current one is processed.
-// At D = 64, at most 128 VGPRs (four waves per SIMD): the 2 B H workgroups
-// of the benchmark shape then all fit on the machine at once, with no tail
-// round.  (At D = 128 the same limit spills, and measured slower.)
+// Workgroup numbering: blocks of eight consecutive (role, bh) pairs, each
+// block once per column group, so that the groups of one pair are eight
+// workgroups apart (the same XCD, whose L2 then serves the chunk inputs that
+// both read) and are dispatched together.  Four waves of at most 128 VGPRs
+// and under 40 KB of LDS: four workgroups per CU, so that each CU
+// interleaves the serial phases of one chunk (prefix, chunk matrices, T)
+// with the matrix-core products of others.
 template <int D, typename T_IO, bool GDN>
-__global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 1))) void chain_kernel(
+__global__ __launch_bounds__(kChainWaves * kWave) __attribute__((amdgpu_waves_per_eu(4))) void chain_kernel(
     int T, int H, int nbh, const T_IO *__restrict__ r, const T_IO *__restrict__ w,
     const T_IO *__restrict__ k, const T_IO *__restrict__ v, const T_IO *__restrict__ a,
     const T_IO *__restrict__ b, const float *__restrict__ s0, const uint8_t *__restrict__ mask,
     const T_IO *__restrict__ d_o, const float *__restrict__ d_sf, float *__restrict__ ckpt,
     float *__restrict__ dck, float *__restrict__ d_s0, SeqGeom vg)
 {
-    constexpr int NTILE = D / 16;
-    using Lds = ChainLds<D>;
+    constexpr int NTILE = D / 16;                    // row tiles of the state
+    constexpr int NCG = D / kChainCols;              // column groups
+    constexpr int NT = kChainWaves * kWave;
+    constexpr int NU = kL * (D / 4) / NT;            // staging units (token, 4 channels) per thread
+    static_assert(NCG >= 1 && NU >= 1 && NU * NT == kL * (D / 4), "chunk tiles split evenly");
+    static_assert(kL * kChainCols / 4 == NT, "one thread per (token, 4 columns) of the value tile");
+    using Lds = ChainLds<D, T_IO>;
     __shared__ Lds s;
-    const bool fwd = (int)blockIdx.x < nbh;
-    const int bh = fwd ? (int)blockIdx.x : (int)blockIdx.x - nbh;
+    const int pair = (int)(blockIdx.x / (8 * NCG)) * 8 + (int)(blockIdx.x % 8);
+    const int cg = (int)(blockIdx.x / 8) % NCG;
+    if (pair >= 2 * nbh) return;   // the whole workgroup, before any barrier
+    const bool fwd = pair < nbh;
+    const int bh = fwd ? pair : pair - nbh;
     const int bb = bh / H, h = bh % H;   // sequence, head
-    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-    const int q = lane >> 4, m = lane & 15, c0 = 16 * wave;
+    const int tid0 = threadIdx.x, wave = tid0 / kWave;
+    const int q0 = (tid0 % kWave) >> 4, m0 = tid0 & 15;
+    const int cw = kChainCols * cg + 16 * wave;   // this wave's first column
     const size_t st = (size_t)bh * D * D;   // this (sequence, head) in [B,H,D,D] arrays
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
     // tokens tok0 .. tok0 + T - 1; chunk c's checkpoints at index ckidx(c),
@@ -864,72 +910,119 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(D == 64 ?
 #pragma unroll
         for (int ti = 0; ti < NTILE; ++ti)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                St[ti][i] = init ? init[(size_t)(16 * ti + 4 * q + i) * D + c0 + m] : 0.0f;
+            for (int i = 0; i < 4; ++i) St[ti][i] = init ? init[(size_t)(16 * ti + 4 * q0 + i) * D + cw + m0] : 0.0f;
     }
-    // one thread per (token tp, channels cp .. cp + 3) of a chunk's tiles
-    const int tp = tid / (D / 4), cp = 4 * (tid % (D / 4));
+    // the initial state is complete before the chunk loop (otherwise every
+    // iteration's first checkpoint store would wait for all memory in flight)
+#pragma unroll
+    for (int ti = 0; ti < NTILE; ++ti)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(St[ti][i]));
+    // staging unit j of thread tid: token tpj, channels cpj .. cpj + 3 (the
+    // D/4 threads of a token are adjacent lanes of one wave); value tile:
+    // token tid / 16, columns 64 g + 4 (tid % 16) .. + 3
+    auto tpj = [](int tid, int j) { return (tid + NT * j) / (D / 4); };
+    auto cpj = [](int tid, int j) { return 4 * ((tid + NT * j) % (D / 4)); };
     using R4 = raw4<T_IO>;
-    typename R4::type pf[5];
-    int pm = 0;
-    float pg = 0.0f, pb = 0.0f;   // Gated DeltaNet: g and beta of the token
+    typename R4::type pf[NU][4], py;
+    int pm[NU], pmy;
+    float pg[NU], pb[NU];   // Gated DeltaNet: g and beta of the token
     const T_IO *const x_src = fwd ? k : r, *const y_src = fwd ? v : d_o;
-    auto fetch = [&](int c) {
+    // Global addresses: a base common to the workgroup (the chunk's first
+    // token, this head) plus a 32-bit per-lane byte offset.
+    auto ld4 = [](const T_IO *base, unsigned e) {
+        return *(const typename R4::type *)((const char *)base + e * (unsigned)sizeof(T_IO));
+    };
+    auto ld1 = [](const T_IO *base, unsigned e) {
+        return io<T_IO>::load((const T_IO *)((const char *)base + e * (unsigned)sizeof(T_IO)), 0);
+    };
+    auto fetch = [&](int c, int tid) {
         const int t0 = c * kL, nt = min(kL, T - t0);
-        const bool valid = tp < nt;
-        const size_t gi = ((tok0 + t0 + tp) * H + h) * D + cp;
-        if constexpr (GDN) {
-            // k, then v (forward) or d_o, then q (backward); every token updates
-            const size_t si = (tok0 + t0 + tp) * H + h;
-            pf[0] = valid ? R4::load(k, gi) : R4::zero();
-            pf[1] = valid ? R4::load(y_src, gi) : R4::zero();
-            pf[2] = (valid && !fwd) ? R4::load(r, gi) : R4::zero();
-            pg = valid ? io<T_IO>::load(w, si) : 0.0f;
-            pb = valid ? io<T_IO>::load(a, si) : 0.0f;
-            pm = valid;
-        } else {
-            const bool up = valid && (mask ? mask[tok0 + t0 + tp] != 0 : 1);
-            pf[0] = up ? R4::load(w, gi) : R4::zero();
-            pf[1] = up ? R4::load(a, gi) : R4::zero();
-            pf[2] = up ? R4::load(b, gi) : R4::zero();
-            // forward: k and v only where the token updates; backward: r and d_o
-            // at every valid token (a masked token still reads the state)
-            const bool xy = fwd ? up : valid;
-            pf[3] = xy ? R4::load(x_src, gi) : R4::zero();
-            pf[4] = xy ? R4::load(y_src, gi) : R4::zero();
-            pm = up;
+        const size_t cb = ((tok0 + t0) * H + h) * D;   // (token t0, channel 0)
+        const size_t sb = (tok0 + t0) * H + h;         // Gated DeltaNet: per-token values
+#pragma unroll
+        for (int j = 0; j < NU; ++j) {
+            const int tp = tpj(tid, j);
+            const bool valid = tp < nt;
+            const unsigned gi = (unsigned)(tp * H * D + cpj(tid, j));
+            if constexpr (GDN) {
+                // k, then q (backward); every token updates
+                const unsigned si = (unsigned)(tp * H);
+                pf[j][0] = valid ? ld4(k + cb, gi) : R4::zero();
+                pf[j][1] = (valid && !fwd) ? ld4(r + cb, gi) : R4::zero();
+                pg[j] = valid ? ld1(w + sb, si) : 0.0f;
+                pb[j] = valid ? ld1(a + sb, si) : 0.0f;
+                pm[j] = valid;
+            } else {
+                // every valid token is loaded; the mask byte is applied when
+                // the tiles are staged, so that no load waits for it
+                pf[j][0] = valid ? ld4(w + cb, gi) : R4::zero();
+                pf[j][1] = valid ? ld4(a + cb, gi) : R4::zero();
+                pf[j][2] = valid ? ld4(b + cb, gi) : R4::zero();
+                pf[j][3] = valid ? ld4(x_src + cb, gi) : R4::zero();
+                pm[j] = !valid ? 0 : mask ? (int)mask[tok0 + t0 + tp] : 1;   // raw mask byte
+            }
+        }
+        {
+            // v or d_o, this workgroup's columns
+            const int tp = tid / 16;
+            const bool valid = tp < nt;
+            py = valid ? ld4(y_src + cb, (unsigned)(tp * H * D + kChainCols * cg + 4 * (tid % 16))) : R4::zero();
+            pmy = !valid ? 0 : (GDN || !mask) ? 1 : (int)mask[tok0 + t0 + tp];
         }
     };
-    if (nck > 0) fetch(fwd ? 0 : nck - 1);
+    // With one staging unit per thread the next chunk's inputs are loaded
+    // while the current one is processed; with two (D = 128) the other
+    // workgroups on the CU cover the load latency instead.
+    constexpr bool kAhead = NU == 1;
+    if (kAhead && nck > 0) fetch(fwd ? 0 : nck - 1, tid0);
     for (int it = 0; it < nck; ++it) {
+        // The lane indices pass through an empty asm here, so that values
+        // derived from them (addresses, masks, constants) are formed inside
+        // the loop instead of being hoisted and held in registers next to
+        // the state across every chunk.
+        int tid = tid0, q = q0, m = m0;
+        asm volatile("" : "+v"(tid), "+v"(q), "+v"(m));
+        const int lane = 16 * q + m;
         const int c = fwd ? it : nck - 1 - it;
         const int Lc = min(kL, T - c * kL);
-        if (c < nck_store) store_slice<D>((fwd ? ckpt : dck) + ckidx(c) * D * D, St, q, m, c0);
-        if constexpr (GDN) {
-            const f32x4 k4 = R4::f32(pf[0]);
-            const f32x4 kn = k4 * inv_norm<D>(k4);
-            const f32x4 q4 = R4::f32(pf[2]);
-            const float iq = inv_norm<D>(q4);   // unused in the forward role (q4 = 0 there)
-            __syncthreads();
-            const f32x4 g4 = {pg, pg, pg, pg};
-            *(f32x4 *)&s.W[tp][cp] = g4;
-            *(f32x4 *)&s.G[tp][cp] = g4;
-            *(f32x4 *)&s.A[tp][cp] = kn * (-__expf(pg) * pb);
-            *(f32x4 *)&s.B[tp][cp] = kn;
-            *(f32x4 *)&s.X[tp][cp] = fwd ? kn * pb : q4 * iq;
-            *(f32x4 *)&s.Y[tp][cp] = R4::f32(pf[1]);
-        } else {
-            __syncthreads();
-            *(f32x4 *)&s.W[tp][cp] = R4::f32(pf[0]);
-            *(f32x4 *)&s.G[tp][cp] = R4::f32(pf[0]);
-            *(f32x4 *)&s.A[tp][cp] = R4::f32(pf[1]);
-            *(f32x4 *)&s.B[tp][cp] = R4::f32(pf[2]);
-            *(f32x4 *)&s.X[tp][cp] = R4::f32(pf[3]);
-            *(f32x4 *)&s.Y[tp][cp] = R4::f32(pf[4]);
+        if (!kAhead) fetch(c, tid);
+        if (c < nck_store) store_slice<D>((fwd ? ckpt : dck) + ckidx(c) * D * D, St, q, cw + m);
+        __syncthreads();   // every wave is done with the previous chunk's tiles
+        // the mask bytes enter the comparisons only here (an empty asm keeps
+        // the compiler from comparing them right after their loads, which
+        // would make the wave wait for every load and store in flight)
+        asm volatile("" : "+v"(pmy));
+#pragma unroll
+        for (int j = 0; j < NU; ++j) asm volatile("" : "+v"(pm[j]));
+#pragma unroll
+        for (int j = 0; j < NU; ++j) {
+            const int tp = tpj(tid, j), cp = cpj(tid, j);
+            if constexpr (GDN) {
+                const f32x4 k4 = R4::f32(pf[j][0]);
+                const f32x4 kn = k4 * inv_norm<D>(k4);
+                const f32x4 q4 = R4::f32(pf[j][1]);
+                const float iq = inv_norm<D>(q4);   // unused in the forward role (q4 = 0 there)
+                const float gg = pg[j], bt = pb[j];
+                *(f32x4 *)&s.G[tp][cp] = f32x4{gg, gg, gg, gg};
+                *(f32x4 *)&s.A[tp][cp] = kn * (-__expf(gg) * bt);
+                *(f32x4 *)&s.B[tp][cp] = kn;
+                *(f32x4 *)&s.X[tp][cp] = fwd ? kn * bt : q4 * iq;
+            } else {
+                // a token that does not update gets w = a = b = 0 (an identity
+                // step) and, in the forward role, k = v = 0; the backward role
+                // keeps r and d_o (a masked token still reads the state)
+                const bool up = pm[j] != 0;
+                *(f32x4 *)&s.G[tp][cp] = up ? R4::f32(pf[j][0]) : z;
+                *(f32x4 *)&s.A[tp][cp] = up ? R4::f32(pf[j][1]) : z;
+                *(f32x4 *)&s.B[tp][cp] = up ? R4::f32(pf[j][2]) : z;
+                *(f32x4 *)&s.X[tp][cp] = (up || !fwd) ? R4::f32(pf[j][3]) : z;
+            }
+            if (cp == 0) s.upd[tp] = pm[j] != 0;
         }
-        if (cp == 0) s.upd[tp] = pm;
+        *(typename R4::type *)&s.Y[tid / 16][4 * (tid % 16)] = (pmy != 0 || !fwd) ? py : R4::zero();
         __syncthreads();
-        if (it + 1 < nck) fetch(fwd ? c + 1 : c - 1);
+        if (kAhead && it + 1 < nck) fetch(fwd ? c + 1 : c - 1, tid);
         int extreme = 0;
         if (tid < D) {
             float x[kL];
@@ -945,52 +1038,78 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(D == 64 ?
             extreme |= acc < kMinChunkLogDecay;
             s.EGL[tid] = __expf(acc);
         }
+        const int cl = 16 * wave + m;   // this lane's column in the value tile
         if (__syncthreads_or(extreme)) {
-            // token by token on the raw operands
+            // token by token on the raw operands, with raw w read again into
+            // G (the prefix replaced it); tokens that do not update get w = 0
+            {
+                const size_t t0 = (size_t)c * kL;
+#pragma unroll
+                for (int j = 0; j < NU; ++j) {
+                    const int tp = tpj(tid, j), cp = cpj(tid, j);
+                    const bool up = s.upd[tp] != 0;
+                    if constexpr (GDN) {
+                        const float gg = up ? ld1(w + (tok0 + t0) * H + h, (unsigned)(tp * H)) : 0.0f;
+                        *(f32x4 *)&s.G[tp][cp] = f32x4{gg, gg, gg, gg};
+                    } else {
+                        *(f32x4 *)&s.G[tp][cp] =
+                            up ? R4::f32(ld4(w + ((tok0 + t0) * H + h) * D, (unsigned)(tp * H * D + cp))) : z;
+                    }
+                }
+            }
+            __syncthreads();
+            const auto &W = s.G;
             if (fwd) {
                 for (int t = 0; t < Lc; ++t) {
                     if (!s.upd[t]) continue;
                     float sb = 0.0f;
 #pragma unroll
-                    for (int ti = 0; ti < NTILE; ++ti)
+                    for (int ti = 0; ti < NTILE; ++ti) {
+                        const f32x4 bt = *(const f32x4 *)&s.B[t][16 * ti + 4 * q];
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) sb = fmaf(s.B[t][16 * ti + 4 * q + i], St[ti][i], sb);
+                        for (int i = 0; i < 4; ++i) sb = fmaf(bt[i], St[ti][i], sb);
+                    }
                     sb = xsum32(xsum16(sb));
-                    const float vj = s.Y[t][c0 + m];
+                    const float vj = tl(s.Y[t][cl]);
 #pragma unroll
-                    for (int ti = 0; ti < NTILE; ++ti)
+                    for (int ti = 0; ti < NTILE; ++ti) {
+                        const int r0 = 16 * ti + 4 * q;
+                        const f32x4 wt = *(const f32x4 *)&W[t][r0], at = *(const f32x4 *)&s.A[t][r0];
+                        const f32x4 xt = *(const f32x4 *)&s.X[t][r0];
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int row = 16 * ti + 4 * q + i;
-                            St[ti][i] = fmaf(__expf(s.W[t][row]), St[ti][i], fmaf(s.A[t][row], sb, s.X[t][row] * vj));
-                        }
+                        for (int i = 0; i < 4; ++i) St[ti][i] = fmaf(__expf(wt[i]), St[ti][i], fmaf(at[i], sb, xt[i] * vj));
+                    }
                 }
             } else {
                 for (int t = Lc - 1; t >= 0; --t) {
-                    const float doj = s.Y[t][c0 + m];
-#pragma unroll
-                    for (int ti = 0; ti < NTILE; ++ti)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) St[ti][i] = fmaf(s.X[t][16 * ti + 4 * q + i], doj, St[ti][i]);
-                    if (!s.upd[t]) continue;
+                    const float doj = tl(s.Y[t][cl]);
                     float ad = 0.0f;
 #pragma unroll
-                    for (int ti = 0; ti < NTILE; ++ti)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) ad = fmaf(s.A[t][16 * ti + 4 * q + i], St[ti][i], ad);
-                    ad = xsum32(xsum16(ad));
-#pragma unroll
-                    for (int ti = 0; ti < NTILE; ++ti)
+                    for (int ti = 0; ti < NTILE; ++ti) {
+                        const int r0 = 16 * ti + 4 * q;
+                        const f32x4 xt = *(const f32x4 *)&s.X[t][r0], at = *(const f32x4 *)&s.A[t][r0];
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            const int row = 16 * ti + 4 * q + i;
-                            St[ti][i] = fmaf(__expf(s.W[t][row]), St[ti][i], s.B[t][row] * ad);
+                            St[ti][i] = fmaf(xt[i], doj, St[ti][i]);
+                            ad = fmaf(at[i], St[ti][i], ad);
                         }
+                    }
+                    if (!s.upd[t]) continue;
+                    ad = xsum32(xsum16(ad));
+#pragma unroll
+                    for (int ti = 0; ti < NTILE; ++ti) {
+                        const int r0 = 16 * ti + 4 * q;
+                        const f32x4 wt = *(const f32x4 *)&W[t][r0], bt = *(const f32x4 *)&s.B[t][r0];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) St[ti][i] = fmaf(__expf(wt[i]), St[ti][i], bt[i] * ad);
+                    }
                 }
             }
             continue;
         }
-        {
+#pragma unroll
+        for (int j = 0; j < NU; ++j) {
+            const int tp = tpj(tid, j), cp = cpj(tid, j);
             const f32x4 G = *(const f32x4 *)&s.G[tp][cp];
             const f32x4 Gp = tp ? *(const f32x4 *)&s.G[tp - 1][cp] : z;
             f32x4 eG, enG, eGp;
@@ -1004,39 +1123,94 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(D == 64 ?
             *(f32x4 *)&s.B[tp][cp] *= eGp;
             *(f32x4 *)&s.X[tp][cp] *= fwd ? enG : eG;
         }
-        __syncthreads();
-        // M_ba (wave 0) and M_bk (forward) or M_ra (backward) (wave 1)
-        if (wave < 2) {
-            const float(*P)[Lds::LD] = (wave == 0 || fwd) ? s.B : s.X;
-            const float(*Q)[Lds::LD] = (wave == 1 && fwd) ? s.X : s.A;
-            const f32x4 acc = mm16_rows<D>(z, [&](int mm, int j) { return *(const f32x4 *)&P[mm][j]; },
-                                           [&](int n, int j) { return *(const f32x4 *)&Q[n][j]; }, lane);
-            const bool strict = wave == 0 || fwd;   // M_ba, M_bk strictly lower; M_ra with the diagonal
+        __syncthreads();   // G is dead from here: M and T take its place
+        // Chunk matrices, each wave one of the two over one half of the
+        // channels: mi = wave & 1 (M_ba; M_bk forward, M_ra backward), half
+        // wave >> 1.  M_ba and M_bk are strictly lower, M_ra keeps the
+        // diagonal; the forward role stores M_ba transposed (read by rows
+        // below).
+        {
+            const int mi = wave & 1, hf = wave >> 1;
+            const float(*P)[Lds::LD] = (mi == 0 || fwd) ? s.B : s.X;
+            const float(*Q)[Lds::LD] = (mi == 1 && fwd) ? s.X : s.A;
+            f32x4 acc = z;
+#pragma unroll
+            for (int j0b = 0; j0b < D / 2; j0b += 16) {
+                const int j = hf * (D / 2) + j0b + 4 * q;
+                const f32x4 xa = *(const f32x4 *)&P[m][j], yb = *(const f32x4 *)&Q[m][j];
+#pragma unroll
+                for (int st = 0; st < 4; ++st) acc = mfma_f32(xa[st], yb[st], acc);
+            }
+            const bool strict = mi == 0 || fwd;
+            f32x4 keep;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 4 * q + i;
-                s.M[wave][row][m] = (strict ? row > m : row >= m) ? acc[i] : 0.0f;
+                keep[i] = (strict ? row > m : row >= m) ? acc[i] : 0.0f;
+            }
+            float(*Mw)[20] = s.M[2 * mi + hf];
+            if (mi == 0 && fwd) {
+                *(f32x4 *)&Mw[m][4 * q] = keep;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Mw[4 * q + i][m] = keep[i];
             }
         }
         __syncthreads();
-        // T = (I - M_ba)^{-1} column by column (x_i = delta_ij + sum_{l<i} M_ba[i][l] x_l),
-        // four lanes per column each summing over l = q (mod 4)
-        if (wave == 0) {
-            float xr[4] = {0.f, 0.f, 0.f, 0.f};
+        // T = (I - M_ba)^{-1}, solved by every wave in registers.  Forward:
+        // lane m forms row m of T (T (I - M_ba) = I: x_j = delta_jm +
+        // sum_{l>j} x_l M_ba[l][j], j descending), the row U = T X reads;
+        // backward: column m (x_i = delta_im + sum_{l<i} M_ba[i][l] x_l), the
+        // column dX = T^T dU reads.  Either way lane (q, m) keeps x[4q .. 4q+3].
+        f32x4 tq;
+        {
+            auto mrow = [&](int r, int p) {
+                return *(const f32x4 *)&s.M[0][r][4 * p] + *(const f32x4 *)&s.M[1][r][4 * p];
+            };
+            float x[kL];
+            if (fwd) {
 #pragma unroll
-            for (int i = 0; i < kL; ++i) {
-                float part = 0.0f;
+                for (int j = kL - 1; j >= 0; --j) {
+                    float a0 = j == m ? 1.0f : 0.0f, a1 = 0.0f;
 #pragma unroll
-                for (int s4 = 0; s4 < 4; ++s4) {
-                    const int l = q + 4 * s4;
-                    if (l < i) part = fmaf(s.M[0][i][l], xr[s4], part);
+                    for (int p = 0; p < kL / 4; ++p) {
+                        if (4 * p + 3 <= j) continue;
+                        const f32x4 mv = mrow(j, p);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int l = 4 * p + e;
+                            if (l <= j) continue;
+                            if (l & 1) a1 = fmaf(mv[e], x[l], a1);
+                            else a0 = fmaf(mv[e], x[l], a0);
+                        }
+                    }
+                    x[j] = a0 + a1;
                 }
-                const float tot = xsum32(xsum16(part)) + (i == m ? 1.0f : 0.0f);
-                if ((i & 3) == q) xr[i >> 2] = tot;
-                if (q == 0) s.Tm[i][m] = tot;
+            } else {
+#pragma unroll
+                for (int i = 0; i < kL; ++i) {
+                    float a0 = i == m ? 1.0f : 0.0f, a1 = 0.0f;
+#pragma unroll
+                    for (int p = 0; p < kL / 4; ++p) {
+                        if (4 * p >= i) continue;
+                        const f32x4 mv = mrow(i, p);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int l = 4 * p + e;
+                            if (l >= i) continue;
+                            if (l & 1) a1 = fmaf(mv[e], x[l], a1);
+                            else a0 = fmaf(mv[e], x[l], a0);
+                        }
+                    }
+                    x[i] = a0 + a1;
+                }
             }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tq[i] = q == 0 ? x[i] : q == 1 ? x[4 + i] : q == 2 ? x[8 + i] : x[12 + i];
         }
-        __syncthreads();
+        // M_bk (forward) or M_ra (backward), the sum of its two halves
+        auto m2 = [&](int r, int c2) { return s.M[2][r][c2] + s.M[3][r][c2]; };
+        const int c0 = 16 * wave;   // this wave's columns in the value tile
         if (fwd) {
             // X = B~ S + M_bk V
             f32x4 Xa = z;
@@ -1046,23 +1220,23 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(D == 64 ?
 #pragma unroll
                 for (int i = 0; i < 4; ++i) Xa = mfma_f32(bt[i], St[ti][i], Xa);
             }
-            Xa = mm16<kL>(Xa, [&](int mm, int kk) { return s.M[1][mm][kk]; },
-                          [&](int kk, int n) { return s.Y[kk][c0 + n]; }, lane);
-            // U = T X (X's token rows 4q + i are this lane's)
+            Xa = mm16<kL>(Xa, [&](int mm, int kk) { return m2(mm, kk); },
+                          [&](int kk, int n) { return tl(s.Y[kk][c0 + n]); }, lane);
+            // U = T X (X's token rows 4q + i are this lane's; tq = T[m][4q + i])
             f32x4 U = z;
-            {
-                const f32x4 tr = *(const f32x4 *)&s.Tm[m][4 * q];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) U = mfma_f32(tr[i], Xa[i], U);
-            }
+            for (int i = 0; i < 4; ++i) U = mfma_f32(tq[i], Xa[i], U);
             // S <- diag(e^{G_L}) (S + A^T U + K^T V)
+            float vy[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) vy[i] = tl(s.Y[4 * q + i][c0 + m]);
 #pragma unroll
             for (int ti = 0; ti < NTILE; ++ti) {
                 f32x4 acc = St[ti];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) acc = mfma_f32(s.A[4 * q + i][16 * ti + m], U[i], acc);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc = mfma_f32(s.X[4 * q + i][16 * ti + m], s.Y[4 * q + i][c0 + m], acc);
+                for (int i = 0; i < 4; ++i) acc = mfma_f32(s.X[4 * q + i][16 * ti + m], vy[i], acc);
                 St[ti] = acc * *(const f32x4 *)&s.EGL[16 * ti + 4 * q];
             }
         } else {
@@ -1077,25 +1251,28 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(D == 64 ?
 #pragma unroll
                 for (int i = 0; i < 4; ++i) dU = mfma_f32(at[i], y[i], dU);
             }
-            dU = mm16<kL>(dU, [&](int mm, int kk) { return s.M[1][kk][mm]; },
-                          [&](int kk, int n) { return s.Y[kk][c0 + n]; }, lane);
-            // dX = T^T dU
+            dU = mm16<kL>(dU, [&](int mm, int kk) { return m2(kk, mm); },
+                          [&](int kk, int n) { return tl(s.Y[kk][c0 + n]); }, lane);
+            // dX = T^T dU (tq = T[4q + i][m])
             f32x4 dX = z;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dX = mfma_f32(s.Tm[4 * q + i][m], dU[i], dX);
+            for (int i = 0; i < 4; ++i) dX = mfma_f32(tq[i], dU[i], dX);
             // dS <- dY + R~^T dO + B~^T dX
+            float oy[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) oy[i] = tl(s.Y[4 * q + i][c0 + m]);
 #pragma unroll
             for (int ti = 0; ti < NTILE; ++ti) {
                 f32x4 acc = dY(ti);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc = mfma_f32(s.X[4 * q + i][16 * ti + m], s.Y[4 * q + i][c0 + m], acc);
+                for (int i = 0; i < 4; ++i) acc = mfma_f32(s.X[4 * q + i][16 * ti + m], oy[i], acc);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) acc = mfma_f32(s.B[4 * q + i][16 * ti + m], dX[i], acc);
                 St[ti] = acc;
             }
         }
     }
-    if (!fwd && d_s0) store_slice<D>(d_s0 + st, St, q, m, c0);
+    if (!fwd && d_s0) store_slice<D>(d_s0 + st, St, q0, cw + m0);
 }
 
 // ck_off[0..nseq]: exclusive prefix sums of the sequences' chunk counts
@@ -1160,7 +1337,9 @@ hipError_t launch_bwd_d(const BwdArgs &p, hipStream_t stream)
     }
     float *ckpt = (float *)p.ws;
     float *dck = ckpt + (p.cu_seqlens ? nck * p.H : nbh * nck) * D * D;
-    hipLaunchKernelGGL((chain_kernel<D, T_IO, GDN>), dim3((unsigned)(2 * nbh)), dim3(D * 4), 0, stream, p.T,
+    // (role, sequence-head) pairs in blocks of eight, each block once per column group
+    const size_t grid1 = (2 * nbh + 7) / 8 * 8 * (D / kChainCols);
+    hipLaunchKernelGGL((chain_kernel<D, T_IO, GDN>), dim3((unsigned)grid1), dim3(kChainWaves * kWave), 0, stream, p.T,
                        p.H, (int)nbh, (const T_IO *)p.r, (const T_IO *)p.w, (const T_IO *)p.k,
                        (const T_IO *)p.v, (const T_IO *)p.a, (const T_IO *)p.b, p.s0, p.mask,
                        (const T_IO *)p.d_o, p.d_sf, ckpt, dck, p.d_s0, vg);
