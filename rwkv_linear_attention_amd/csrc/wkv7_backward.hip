@@ -795,9 +795,10 @@ template <int D, typename T_IO> struct alignas(16) ChainLds {
     union {
         float G[kL][LD];                // w, then its decay prefix (exact path: raw w again)
         // after the scaling: the chunk matrices as two partial sums each
-        // (the two halves of the channel contraction), M[2 mi + half]: mi 0
-        // M_ba (forward: transposed), mi 1 M_bk (forward) or M_ra (backward)
-        float M[4][kL][20];
+        // (the two halves of the channel contraction): M[half] M_ba,
+        // M[2 + half] M_ba transposed, M[4 + half] M_bk (forward) or M_ra
+        // (backward)
+        float M[6][kL][20];
     };
     float A[kL][LD];                    // a, then A^ = a e^{-G}
     float B[kL][LD];                    // b, then B~ = b e^{G_{t-1}}
@@ -1127,8 +1128,7 @@ __global__ __launch_bounds__(kChainWaves * kWave) __attribute__((amdgpu_waves_pe
         // Chunk matrices, each wave one of the two over one half of the
         // channels: mi = wave & 1 (M_ba; M_bk forward, M_ra backward), half
         // wave >> 1.  M_ba and M_bk are strictly lower, M_ra keeps the
-        // diagonal; the forward role stores M_ba transposed (read by rows
-        // below).
+        // diagonal; M_ba is stored in both orientations.
         {
             const int mi = wave & 1, hf = wave >> 1;
             const float(*P)[Lds::LD] = (mi == 0 || fwd) ? s.B : s.X;
@@ -1148,68 +1148,43 @@ __global__ __launch_bounds__(kChainWaves * kWave) __attribute__((amdgpu_waves_pe
                 const int row = 4 * q + i;
                 keep[i] = (strict ? row > m : row >= m) ? acc[i] : 0.0f;
             }
-            float(*Mw)[20] = s.M[2 * mi + hf];
-            if (mi == 0 && fwd) {
-                *(f32x4 *)&Mw[m][4 * q] = keep;
-            } else {
+            float(*Mw)[20] = s.M[mi == 0 ? hf : 4 + hf];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) Mw[4 * q + i][m] = keep[i];
-            }
+            for (int i = 0; i < 4; ++i) Mw[4 * q + i][m] = keep[i];
+            if (mi == 0) *(f32x4 *)&s.M[2 + hf][m][4 * q] = keep;
         }
         __syncthreads();
-        // T = (I - M_ba)^{-1}, solved by every wave in registers.  Forward:
-        // lane m forms row m of T (T (I - M_ba) = I: x_j = delta_jm +
-        // sum_{l>j} x_l M_ba[l][j], j descending), the row U = T X reads;
-        // backward: column m (x_i = delta_im + sum_{l<i} M_ba[i][l] x_l), the
-        // column dX = T^T dU reads.  Either way lane (q, m) keeps x[4q .. 4q+3].
+        // T = (I - M_ba)^{-1} = (I + N)(I + N^2)(I + N^4)(I + N^8) with
+        // N = M_ba strictly lower (N^16 = 0), formed by every wave on the
+        // matrix cores.  acc(X) is the accumulator layout of X (lane (q, m)
+        // holds rows 4q .. 4q + 3 of column m); with the contraction index
+        // permuted as elsewhere, acc(X Y) = sum_st mfma(acc(X^T)[st],
+        // acc(Y)[st]), so each product needs its left factor transposed.  The
+        // forward role reads rows of T (U = T X): acc(T^T); the backward role
+        // reads columns (dX = T^T dU): acc(T).  Lane (q, m) ends with
+        // tq = T[m][4q + i] (forward) or T[4q + i][m] (backward).
         f32x4 tq;
         {
-            auto mrow = [&](int r, int p) {
-                return *(const f32x4 *)&s.M[0][r][4 * p] + *(const f32x4 *)&s.M[1][r][4 * p];
+            auto mm = [](f32x4 aT, f32x4 b) {
+                f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int st = 0; st < 4; ++st) c = mfma_f32(aT[st], b[st], c);
+                return c;
             };
-            float x[kL];
-            if (fwd) {
+            const f32x4 nA = *(const f32x4 *)&s.M[2][m][4 * q] + *(const f32x4 *)&s.M[3][m][4 * q];   // acc(N)
+            const f32x4 nT = *(const f32x4 *)&s.M[0][m][4 * q] + *(const f32x4 *)&s.M[1][m][4 * q];   // acc(N^T)
+            f32x4 eye;
 #pragma unroll
-                for (int j = kL - 1; j >= 0; --j) {
-                    float a0 = j == m ? 1.0f : 0.0f, a1 = 0.0f;
-#pragma unroll
-                    for (int p = 0; p < kL / 4; ++p) {
-                        if (4 * p + 3 <= j) continue;
-                        const f32x4 mv = mrow(j, p);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int l = 4 * p + e;
-                            if (l <= j) continue;
-                            if (l & 1) a1 = fmaf(mv[e], x[l], a1);
-                            else a0 = fmaf(mv[e], x[l], a0);
-                        }
-                    }
-                    x[j] = a0 + a1;
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < kL; ++i) {
-                    float a0 = i == m ? 1.0f : 0.0f, a1 = 0.0f;
-#pragma unroll
-                    for (int p = 0; p < kL / 4; ++p) {
-                        if (4 * p >= i) continue;
-                        const f32x4 mv = mrow(i, p);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int l = 4 * p + e;
-                            if (l >= i) continue;
-                            if (l & 1) a1 = fmaf(mv[e], x[l], a1);
-                            else a0 = fmaf(mv[e], x[l], a0);
-                        }
-                    }
-                    x[i] = a0 + a1;
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) tq[i] = q == 0 ? x[i] : q == 1 ? x[4 + i] : q == 2 ? x[8 + i] : x[12 + i];
+            for (int i = 0; i < 4; ++i) eye[i] = 4 * q + i == m ? 1.0f : 0.0f;
+            const f32x4 n2 = mm(nT, nA), n2T = mm(nA, nT);
+            const f32x4 n4 = mm(n2T, n2), n4T = mm(n2, n2T);
+            const f32x4 n8 = mm(n4T, n4);
+            const f32x4 p1T = mm(eye + n2, eye + nT);   // ((I + N)(I + N^2))^T
+            const f32x4 p2T = mm(eye + n4, p1T);        // (P1 (I + N^4))^T
+            tq = fwd ? mm(eye + n8, p2T) : mm(p2T, eye + n8);
         }
         // M_bk (forward) or M_ra (backward), the sum of its two halves
-        auto m2 = [&](int r, int c2) { return s.M[2][r][c2] + s.M[3][r][c2]; };
+        auto m2 = [&](int r, int c2) { return s.M[4][r][c2] + s.M[5][r][c2]; };
         const int c0 = 16 * wave;   // this wave's columns in the value tile
         if (fwd) {
             // X = B~ S + M_bk V
