@@ -556,17 +556,33 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(D == 64 ?
         }
     }
     __syncthreads();
-    // T = (I - M_ba)^{-1} by forward substitution, one column per lane
-    if (tid < kL) {
-        float x[kL];
+    // T = (I - M_ba)^{-1} = (I + N)(I + N^2)(I + N^4)(I + N^8) (N = M_ba
+    // strictly lower, N^16 = 0), formed by wave 0 on the matrix cores as in
+    // the chain kernel (acc(X Y) = sum_st mfma(acc(X^T)[st], acc(Y)[st])) and
+    // written over M_ba row-major.  The wave reads all of M_ba before it
+    // writes.
+    if (wave == 0) {
+        auto mm = [](f32x4 aT, f32x4 b) {
+            f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < kL; ++i) {
-            float acc = i == tid ? 1.0f : 0.0f;
+            for (int st = 0; st < 4; ++st) c = mfma_f32(aT[st], b[st], c);
+            return c;
+        };
+        f32x4 nA, nT, eye;   // acc(N), acc(N^T), I
 #pragma unroll
-            for (int mm = 0; mm < i; ++mm) acc = fmaf(s.M[M_BA][i][mm], x[mm], acc);
-            x[i] = acc;
-            s.M[M_T][i][tid] = acc;
+        for (int i = 0; i < 4; ++i) {
+            nA[i] = s.M[M_BA][4 * q + i][m];
+            nT[i] = s.M[M_BA][m][4 * q + i];
+            eye[i] = 4 * q + i == m ? 1.0f : 0.0f;
         }
+        const f32x4 n2 = mm(nT, nA), n2T = mm(nA, nT);
+        const f32x4 n4 = mm(n2T, n2), n4T = mm(n2, n2T);
+        const f32x4 n8 = mm(n4T, n4);
+        const f32x4 p1T = mm(eye + n2, eye + nT);   // ((I + N)(I + N^2))^T
+        const f32x4 p2T = mm(eye + n4, p1T);        // (P1 (I + N^4))^T
+        const f32x4 tA = mm(p2T, eye + n8);         // acc(T)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s.M[M_T][4 * q + i][m] = tA[i];
     }
     __syncthreads();
 
@@ -1155,16 +1171,18 @@ __global__ __launch_bounds__(kChainWaves * kWave) __attribute__((amdgpu_waves_pe
         }
         __syncthreads();
         // T = (I - M_ba)^{-1} = (I + N)(I + N^2)(I + N^4)(I + N^8) with
-        // N = M_ba strictly lower (N^16 = 0), formed by every wave on the
-        // matrix cores.  acc(X) is the accumulator layout of X (lane (q, m)
-        // holds rows 4q .. 4q + 3 of column m); with the contraction index
-        // permuted as elsewhere, acc(X Y) = sum_st mfma(acc(X^T)[st],
-        // acc(Y)[st]), so each product needs its left factor transposed.  The
-        // forward role reads rows of T (U = T X): acc(T^T); the backward role
-        // reads columns (dX = T^T dU): acc(T).  Lane (q, m) ends with
-        // tq = T[m][4q + i] (forward) or T[4q + i][m] (backward).
+        // N = M_ba strictly lower (N^16 = 0), formed by wave 0 on the matrix
+        // cores and handed to the other waves through LDS (each wave forming
+        // it itself loads the matrix cores with four times the products).
+        // acc(X) is the accumulator layout of X (lane (q, m) holds rows
+        // 4q .. 4q + 3 of column m); with the contraction index permuted as
+        // elsewhere, acc(X Y) = sum_st mfma(acc(X^T)[st], acc(Y)[st]), so each
+        // product needs its left factor transposed.  The forward role reads
+        // rows of T (U = T X): acc(T^T); the backward role reads columns
+        // (dX = T^T dU): acc(T).  Every lane (q, m) ends with tq =
+        // T[m][4q + i] (forward) or T[4q + i][m] (backward).
         f32x4 tq;
-        {
+        if (wave == 0) {
             auto mm = [](f32x4 aT, f32x4 b) {
                 f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1181,8 +1199,11 @@ __global__ __launch_bounds__(kChainWaves * kWave) __attribute__((amdgpu_waves_pe
             const f32x4 n8 = mm(n4T, n4);
             const f32x4 p1T = mm(eye + n2, eye + nT);   // ((I + N)(I + N^2))^T
             const f32x4 p2T = mm(eye + n4, p1T);        // (P1 (I + N^4))^T
-            tq = fwd ? mm(eye + n8, p2T) : mm(p2T, eye + n8);
+            // each lane's tq, over the transposed M_ba slot that only this wave reads
+            *(f32x4 *)&s.M[2][m][4 * q] = fwd ? mm(eye + n8, p2T) : mm(p2T, eye + n8);
         }
+        __syncthreads();
+        tq = *(const f32x4 *)&s.M[2][m][4 * q];
         // M_bk (forward) or M_ra (backward), the sum of its two halves
         auto m2 = [&](int r, int c2) { return s.M[4][r][c2] + s.M[5][r][c2]; };
         const int c0 = 16 * wave;   // this wave's columns in the value tile
