@@ -236,7 +236,10 @@ wkv7_status_t wkv7_gdn_fwd_varlen(int dtype, int N, int total_T, int H, int K, i
  *   stream         hipStream_t to enqueue on.
  * Output buffers must not overlap any input or each other.  With T == 0,
  * d_initial_state receives d_final_state (summed over B for a shared state;
- * zeros when NULL).
+ * zeros when NULL).  Returns WKV7_ERR_UNSUPPORTED when H*K reaches 2^25 (the
+ * kernels address one 16-token chunk with 32-bit offsets) or a launch grid
+ * would exceed 2^31 - 1 workgroups; the same limits hold for every backward
+ * entry point.
  */
 wkv7_status_t wkv7_bwd(int dtype, int B, int T, int H, int K, int V,
                        const void *r, const void *w, const void *k,

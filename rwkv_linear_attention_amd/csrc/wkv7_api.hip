@@ -68,6 +68,15 @@ int choose_packed_path(int dtype, int total_T, int N, int algo, bool gdn = false
     return choose_path(dtype, total_T / N, algo, gdn);
 }
 
+// Launch limits of the backward kernels: the recurrences' grid (2 nbh
+// (role, sequence-head) pairs in blocks of eight, each block once per
+// 64-column group), and their 32-bit per-lane byte offsets inside one
+// 16-token chunk (16 H K elements of at most 4 bytes).
+static bool bwd_launch_fits(long long nbh, int H, int K)
+{
+    return (2 * nbh + 7) / 8 * 8 * (K / 64) <= INT32_MAX && 64ll * H * K <= INT32_MAX;
+}
+
 std::atomic<int> g_wait_limit{wkv7::kDefaultWaitLimit};
 
 }  // namespace
@@ -85,8 +94,9 @@ int wkv7::check_bwd_args(int dtype, int B, int T, int H, int K, int V, const voi
     if (st != WKV7_OK) return st;
     if (T < 0) return WKV7_ERR_INVALID_ARG;
     if ((long long)B * T * H * K > (1ll << 40)) return WKV7_ERR_UNSUPPORTED;
-    // launch grids: 2 B H workgroups, and B H ceil(T/16) workgroups
-    if (2ll * B * H > INT32_MAX || (long long)B * H * ((T + 15) / 16) > INT32_MAX) return WKV7_ERR_UNSUPPORTED;
+    // launch grids and offsets of the two backward kernels
+    if (!bwd_launch_fits((long long)B * H, H, K) || (long long)B * H * ((T + 15) / 16) > INT32_MAX)
+        return WKV7_ERR_UNSUPPORTED;
     if (T > 0) {
         const void *req[] = {r, w, k, v, a, b, d_o, dr, dw, dk, dv, da, db};
         for (const void *p : req)
@@ -363,8 +373,8 @@ wkv7_status_t wkv7_bwd_varlen(int dtype, int N, int total_T, int H, int K, int V
     if (st != WKV7_OK) return st;
     if (total_T < 0) return WKV7_ERR_INVALID_ARG;
     if ((long long)total_T * H * K > (1ll << 40)) return WKV7_ERR_UNSUPPORTED;
-    // launch grids: 2 N H workgroups, and H per chunk of the capacity
-    if (2ll * N * H > INT32_MAX || wkv7::bwd_varlen_chunk_capacity(N, total_T) * H > INT32_MAX)
+    // launch grids and offsets of the two backward kernels (H per chunk of the capacity)
+    if (!bwd_launch_fits((long long)N * H, H, K) || wkv7::bwd_varlen_chunk_capacity(N, total_T) * H > INT32_MAX)
         return WKV7_ERR_UNSUPPORTED;
     if (total_T > 0) {
         const void *req[] = {r, w, k, v, a, b, d_o, dr, dw, dk, dv, da, db, workspace};
@@ -416,8 +426,9 @@ wkv7_status_t wkv7_gdn_bwd(int dtype, int B, int T, int H, int K, int V,
     if (st != WKV7_OK) return st;
     if (T < 0) return WKV7_ERR_INVALID_ARG;
     if ((long long)B * T * H * K > (1ll << 40)) return WKV7_ERR_UNSUPPORTED;
-    // launch grids of the WKV7 backward it runs: 2 B H and B H ceil(T/16) workgroups
-    if (2ll * B * H > INT32_MAX || (long long)B * H * ((T + 15) / 16) > INT32_MAX) return WKV7_ERR_UNSUPPORTED;
+    // launch grids and offsets of the WKV7 backward it runs
+    if (!bwd_launch_fits((long long)B * H, H, K) || (long long)B * H * ((T + 15) / 16) > INT32_MAX)
+        return WKV7_ERR_UNSUPPORTED;
     if (T > 0) {
         const void *req[] = {q, k, v, g, beta, d_o, dq, dk, dv, dg, dbeta, workspace};
         for (const void *p : req)
@@ -462,7 +473,7 @@ wkv7_status_t wkv7_gdn_bwd_varlen(int dtype, int N, int total_T, int H, int K, i
     if (st != WKV7_OK) return st;
     if (total_T < 0) return WKV7_ERR_INVALID_ARG;
     if ((long long)total_T * H * K > (1ll << 40)) return WKV7_ERR_UNSUPPORTED;
-    if (2ll * N * H > INT32_MAX || wkv7::bwd_varlen_chunk_capacity(N, total_T) * H > INT32_MAX)
+    if (!bwd_launch_fits((long long)N * H, H, K) || wkv7::bwd_varlen_chunk_capacity(N, total_T) * H > INT32_MAX)
         return WKV7_ERR_UNSUPPORTED;
     if (total_T > 0) {
         const void *req[] = {q, k, v, g, beta, d_o, dq, dk, dv, dg, dbeta, workspace};

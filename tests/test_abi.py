@@ -240,6 +240,8 @@ def test_bwd_workspace_size(L):
     (dict(B=2, s0=GOOD, n_state=3), wkv7.ERR_INVALID_ARG),         # state rows must be 1 or B
     (dict(B=2, s0=GOOD, n_state=0), wkv7.ERR_INVALID_ARG),
     (dict(B=1 << 16, H=1 << 14, T=16), wkv7.ERR_UNSUPPORTED),      # 2 B H workgroups exceed the grid
+    (dict(H=1 << 19, T=16), wkv7.ERR_UNSUPPORTED),                 # a chunk's H K D fp32 offsets reach 2^31
+    (dict(H=1 << 18, K=128, V=128, T=16), wkv7.ERR_UNSUPPORTED),
 ])
 def test_bwd_validation(L, kw, code):
     assert bwd(L, **kw) == code
@@ -289,6 +291,7 @@ def test_gdn_bwd_workspace_size(L):
     (dict(dsf=ODD), wkv7.ERR_INVALID_ARG),
     (dict(ds0=ODD), wkv7.ERR_INVALID_ARG),
     (dict(B=1 << 16, H=1 << 14, T=16), wkv7.ERR_UNSUPPORTED),     # 2 B H workgroups exceed the grid
+    (dict(B=1, H=1 << 19, T=16), wkv7.ERR_UNSUPPORTED),           # a chunk's H K D fp32 offsets reach 2^31
 ])
 def test_gdn_bwd_validation(L, kw, code):
     assert gdn_bwd(L, **kw) == code
@@ -337,6 +340,7 @@ def test_bwd_varlen_workspace_size(L):
     (dict(dsf=ODD), wkv7.ERR_INVALID_ARG),
     (dict(ds0=ODD), wkv7.ERR_INVALID_ARG),
     (dict(N=1 << 16, H=1 << 14, TT=16), wkv7.ERR_UNSUPPORTED),    # 2 N H workgroups exceed the grid
+    (dict(N=1, H=1 << 19, TT=16), wkv7.ERR_UNSUPPORTED),          # a chunk's H K D fp32 offsets reach 2^31
 ])
 def test_bwd_varlen_validation(L, kw, code):
     assert bwd_varlen(L, **kw) == code
@@ -368,6 +372,7 @@ def gdn_bwd_varlen(L, dtype=1, N=3, TT=50, H=1, K=64, V=64, cu=GOOD, ptrs=None, 
     (dict(cu=None), wkv7.ERR_INVALID_ARG),
     (dict(ws_bytes=1024), wkv7.ERR_INVALID_ARG),
     (dict(s0=GOOD, n_state=2), wkv7.ERR_INVALID_ARG),         # no map: N rows or one shared row
+    (dict(N=1, H=1 << 19, TT=16), wkv7.ERR_UNSUPPORTED),      # a chunk's H K D fp32 offsets reach 2^31
 ])
 def test_gdn_bwd_varlen_validation(L, kw, code):
     assert gdn_bwd_varlen(L, **kw) == code
