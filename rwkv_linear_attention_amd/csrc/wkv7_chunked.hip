@@ -24,13 +24,14 @@
 // slice depend only on that slice).
 // Producer waves prepare chunks c = p, p + NPROD, ... from raw tiles streamed
 // into a private LDS buffer with asynchronous global->LDS loads one chunk
-// ahead, and hand each chunk's operands to the consumers through a
-// three-slot LDS ring.  Hand-off uses LDS counters (ready[slot] =
-// 2 (chunk + 1) + extreme-decay flag once a slot is filled; done[i] = chunks
-// consumer i has finished reading), so producers and consumers never meet at
-// a workgroup barrier.  Every wait is bounded.  At D = 64 one workgroup runs
-// two sequences of one consumer and three producers (eight waves); at
-// D = 128 one sequence of four consumers and three producers (seven waves).
+// ahead, and hand each chunk's operands to the consumers through a ring of
+// LDS slots.  Hand-off uses LDS counters (ready[slot] = 2 (chunk + 1) +
+// extreme-decay flag once a slot is filled; done[i] = chunks consumer i has
+// finished reading), so producers and consumers never meet at a workgroup
+// barrier.  Every wait is bounded.  At D = 64 one workgroup runs two
+// sequences of one consumer and three producers with three slots each (eight
+// waves); at D = 128 one sequence of four consumers and four producers with
+// two slots (eight waves).
 //
 // Products on the consumer side pair operands along k so that each
 // 16x16x32 MFMA carries two 16-token contractions, and the output is formed
@@ -57,14 +58,17 @@ template <int D> struct WS {
     static constexpr int NCB = D / 32;                 // 32-channel blocks
     static constexpr int NQ = D / 16;                  // 16-row tiles of the state
     // D = 64: two sequences of one consumer (64 state columns) and three
-    // producers.  D = 128: one sequence of four consumers (32 columns each,
-    // so that a 128 x 32 state slice and its working set stay in ordinary
-    // VGPRs) and three producers.  Two waves per SIMD in both cases.
+    // producers, three slots each.  D = 128: one sequence of four consumers
+    // (32 columns each, so that a 128 x 32 state slice and its working set
+    // stay in ordinary VGPRs) and four producers, which leaves LDS for two
+    // slots only: a chunk costs a producer about four times what it costs a
+    // consumer, and a fourth producer (0.98 -> 0.875 ms on B16 T4096 H32)
+    // is worth more than a third slot.  Two waves per SIMD in both cases.
     static constexpr int NCONS = D == 64 ? 1 : 4;      // consumers per sequence
     static constexpr int CW = D / NCONS;               // state columns per consumer
     static constexpr int NT = CW / 16;                 // 16-column tiles per consumer
-    static constexpr int NPROD = 3;                    // producers per sequence
-    static constexpr int NSLOT = 3;                    // slot ring depth per sequence
+    static constexpr int NPROD = D == 64 ? 3 : 4;      // producers per sequence
+    static constexpr int NSLOT = D == 64 ? 3 : 2;      // slot ring depth per sequence
     static constexpr int NSEQ = D == 64 ? 2 : 1;       // sequences per workgroup
     static constexpr int NWAVE = NSEQ * (NCONS + NPROD);
     static constexpr int WAVES_PER_SIMD = (NWAVE + 3) / 4;
