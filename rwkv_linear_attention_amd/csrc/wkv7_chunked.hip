@@ -889,7 +889,19 @@ __attribute__((amdgpu_waves_per_eu(WS<D>::WAVES_PER_SIMD, WS<D>::WAVES_PER_SIMD)
         prank += (cr >= NC && key_of[w2] < key_of[wave]) ? 1 : 0;
     }
     const int seq = is_cons ? crank % C::NSEQ : prank % C::NSEQ;
-    const int bh = blockIdx.x * C::NSEQ + seq;
+    // Workgroups go to the eight XCDs round robin (workgroup i to XCD i % 8).
+    // With sequences of one length and a grid that divides evenly, each XCD
+    // takes a contiguous range of sequences, so that the heads of one token
+    // share an XCD and its L2 fetches the values every head of the token
+    // reads (the mask; the gate and strength of Gated DeltaNet) once: Gated
+    // DeltaNet's fetch fell from 1.073x to 1.0004x the algorithmic bytes.
+    // Packed sequences of mixed lengths keep the round robin, which spreads
+    // a long sequence's heads over all XCDs (contiguous ranges measured
+    // 0.490 against 0.470 ms on the packed benchmark batch).
+    const unsigned nwg = gridDim.x;
+    const unsigned wg = (!cu_seqlens && nwg % 8u == 0u) ? (blockIdx.x % 8u) * (nwg / 8u) + blockIdx.x / 8u
+                                                        : blockIdx.x;
+    const int bh = (int)wg * C::NSEQ + seq;
     if (bh >= nbh) return;
     // Sequence sq = bh / H: tokens [tok0, tok0 + Tn) of the (packed) token
     // axis, initial state row sidx of the state pool (-1: zeros).  Offsets
