@@ -22,11 +22,13 @@
 // state columns 16 i .. 16 i + 15 in MFMA accumulator registers (lane
 // (m, q) holds rows 16 ti + 4 q + r of column 16 i + m) for the whole
 // sequence.  Per chunk all waves stage the chunk's inputs into LDS (each
-// thread four channels of one token; the next chunk's loads are in flight
-// meanwhile), each thread forms its own decay prefix from the staged w rows,
-// the four waves 0..3 form one chunk matrix each, every wave forms T itself
-// (forward substitution, one column per lane) and then runs the products of
-// its own columns.  Contractions over state rows or chunk tokens take the
+// thread four channels of one token, a channel group's 16 tokens in one
+// 16-lane row; the next chunk's loads are in flight meanwhile), each thread
+// forms its decay prefix by a scan across its row, the four waves 0..3 form
+// one chunk matrix each, T is formed (D = 64: by every wave, forward
+// substitution with one column per lane; D = 128: by wave 0 on the matrix
+// cores, nilpotent doubling) and then each wave runs the products of its own
+// columns.  Contractions over state rows or chunk tokens take the
 // index in the order the accumulator layout holds it, so the state and the
 // intermediate tiles feed the matrix cores straight from registers; the
 // output is formed transposed (O^T = S^T R~^T + U^T M_ra^T + V^T M_rk^T) so
@@ -71,7 +73,9 @@ template <int D> struct alignas(16) F32Buf {
 
 template <int D> struct alignas(16) F32Lds {
     F32Buf<D> buf[F32Cfg<D>::NBUF];
-    float T[F32Cfg<D>::NW][kL][kL + 4];   // each wave's copy of T
+    // D = 64: each wave's copy of T.  D = 128: T^T as wave 0's accumulator,
+    // lane (q, m) at [0][m][4q].
+    float T[D == 64 ? F32Cfg<D>::NW : 1][kL][kL + 4];
 };
 
 template <int D>
@@ -122,9 +126,11 @@ chunked_f32_kernel(
             for (int i = 0; i < 4; ++i) St[ti][i] = init ? init[(size_t)(16 * ti + 4 * q + i) * D + c0 + m] : 0.0f;
     }
 
-    // Staging: thread (token tp, channels cp .. cp + 3); the next chunk's
-    // inputs are loaded into registers while the current chunk runs.
-    const int tp = tid / (D / 4), cp = 4 * (tid % (D / 4));
+    // Staging: thread (token tp, channels cp .. cp + 3), the 16 tokens of a
+    // channel group in the 16 lanes of one row of a wave, so that the decay
+    // prefix is a scan across the row; the next chunk's inputs are loaded
+    // into registers while the current chunk runs.
+    const int tp = lane & 15, cp = 4 * (4 * wave + (lane >> 4));
     // Every valid token's inputs are loaded; the mask byte is applied when
     // the chunk is staged (selects, so that nothing a masked token holds --
     // not even inf or nan -- reaches the state).
@@ -156,19 +162,16 @@ chunked_f32_kernel(
         *(f32x4 *)&bf.V[tp][cp] = v4;
         if (cp == 0) bf.upd[tp] = up;
         if (c + 1 < nck) fetch(c + 1);
-        __syncthreads();
 
-        // Decay prefix of this thread's four channels: G (token tp), the
-        // exclusive prefix Gp, and the chunk total G_L.
-        f32x4 wr[kL];
+        // Decay prefix of this thread's four channels, a scan over the row's
+        // 16 lanes (tokens): G (token tp), the exclusive prefix Gp, and the
+        // chunk total G_L.
+        f32x4 G, Gp, GL;
 #pragma unroll
-        for (int t = 0; t < kL; ++t) wr[t] = *(const f32x4 *)&bf.W[t][cp];
-        f32x4 G = z, Gp = z, GL = z;
-#pragma unroll
-        for (int t = 0; t < kL; ++t) {
-            if (t == tp) Gp = GL;
-            GL += wr[t];
-            if (t == tp) G = GL;
+        for (int i = 0; i < 4; ++i) {
+            G[i] = row_scan16(w4[i]);
+            Gp[i] = row_shr<1>(G[i], 0.0f);
+            GL[i] = row_bcast15(G[i]);
         }
         int extreme = (w4[0] > 0.0f) | (w4[1] > 0.0f) | (w4[2] > 0.0f) | (w4[3] > 0.0f);
         extreme |= (GL[0] < kMinChunkLogDecay) | (GL[1] < kMinChunkLogDecay) | (GL[2] < kMinChunkLogDecay) |
@@ -243,18 +246,49 @@ chunked_f32_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 4 * q + i;
-                bf.M[wave][row][m] = (strict ? row > m : row >= m) ? acc[i] : 0.0f;
+                acc[i] = (strict ? row > m : row >= m) ? acc[i] : 0.0f;
+                bf.M[wave][row][m] = acc[i];
+            }
+            if (D == 128 && wave == 0) {
+                // T = (I - M_ba)^-1 = (I + N)(I + N^2)(I + N^4)(I + N^8), N = M_ba
+                // strictly lower (N^16 = 0), on the matrix cores while waves 1..3
+                // form the other chunk matrices: with the contraction index
+                // permuted as in the products below, acc(X Y) = sum_st
+                // mfma(acc(X^T)[st], acc(Y)[st]).  acc(T^T) goes to LDS; lane
+                // (q, m) holds T[m][4q + i], the row operand of U = T X.
+                auto mm = [](f32x4 aT, f32x4 b) {
+                    f32x4 r4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int st = 0; st < 4; ++st) r4 = mfma_f32(aT[st], b[st], r4);
+                    return r4;
+                };
+                lds_wait();   // this wave's M_ba writes are complete before its transposed read
+                const f32x4 nA = acc, nT = *(const f32x4 *)&bf.M[0][m][4 * q];   // acc(N), acc(N^T)
+                f32x4 eye;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) eye[i] = 4 * q + i == m ? 1.0f : 0.0f;
+                const f32x4 n2 = mm(nT, nA), n2T = mm(nA, nT);
+                const f32x4 n4 = mm(n2T, n2), n4T = mm(n2, n2T);
+                const f32x4 n8 = mm(n4T, n4);
+                const f32x4 p1T = mm(eye + n2, eye + nT);   // ((I + N)(I + N^2))^T
+                const f32x4 p2T = mm(eye + n4, p1T);        // (P1 (I + N^4))^T
+                *(f32x4 *)&s.T[0][m][4 * q] = mm(eye + n8, p2T);   // (I + N^8)^T P2^T = T^T
             }
         }
         __syncthreads();
 
-        // ---- T = (I - M_ba)^-1, this wave's copy: lane j < 16 solves column j ----
-        // Column j = lane & 15 in every lane group: row i of M_ba is read as
-        // four-float pieces (the same address in every lane), all before the
-        // substitution, and each row's dot product is split over two
-        // accumulators so that only its last term waits for x_{i-1}.
-        float(*Tw)[kL + 4] = s.T[wave];
-        {
+        // ---- T = (I - M_ba)^-1.  D = 128: formed by wave 0 above (eight
+        // waves would each repeat a substitution: 4.05 -> 3.89 ms measured at
+        // B16 T4096 H32).  D = 64: this wave's copy, lane j < 16 solving
+        // column j; with four waves the substitution in every wave measured
+        // faster than wave 0 alone on the matrix cores (1.35 against 1.40 ms
+        // at B8 T4096 H64).  Column j = lane & 15 in every lane group: row i
+        // of M_ba is read as four-float pieces (the same address in every
+        // lane), all before the substitution, and each row's dot product is
+        // split over two accumulators so that only its last term waits for
+        // x_{i-1}. ----
+        float(*Tw)[kL + 4] = s.T[D == 64 ? wave : 0];
+        if constexpr (D == 64) {
             const int j = lane & 15;
             f32x4 mrow[kL - 1][4];
 #pragma unroll
@@ -278,8 +312,8 @@ chunked_f32_kernel(
 #pragma unroll
                 for (int i = 0; i < kL; ++i) Tw[i][j] = x[i];
             }
+            lds_wait();   // the wave's own T writes are complete before its reads
         }
-        lds_wait();   // the wave's own T writes are complete before its reads
 
         // ---- this wave's columns c0 .. c0 + 15 ----
         const float vm[4] = {bf.V[4 * q][c0 + m], bf.V[4 * q + 1][c0 + m], bf.V[4 * q + 2][c0 + m],
@@ -308,6 +342,7 @@ chunked_f32_kernel(
         // U = T X
         f32x4 U = z;
         {
+            // T[m][4q + i]: the wave's own copy (D = 64) or wave 0's T^T accumulator
             const f32x4 tr = *(const f32x4 *)&Tw[m][4 * q];
 #pragma unroll
             for (int i = 0; i < 4; ++i) U = mfma_f32(tr[i], X[i], U);
