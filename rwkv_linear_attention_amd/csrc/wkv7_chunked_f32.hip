@@ -277,16 +277,42 @@ chunked_f32_kernel(
         }
         __syncthreads();
 
-        // ---- T = (I - M_ba)^-1.  D = 128: formed by wave 0 above (eight
-        // waves would each repeat a substitution: 4.05 -> 3.89 ms measured at
-        // B16 T4096 H32).  D = 64: this wave's copy, lane j < 16 solving
-        // column j; with four waves the substitution in every wave measured
-        // faster than wave 0 alone on the matrix cores (1.35 against 1.40 ms
-        // at B8 T4096 H64).  Column j = lane & 15 in every lane group: row i
-        // of M_ba is read as four-float pieces (the same address in every
-        // lane), all before the substitution, and each row's dot product is
-        // split over two accumulators so that only its last term waits for
-        // x_{i-1}. ----
+        // ---- this wave's columns c0 .. c0 + 15 ----
+        const float vm[4] = {bf.V[4 * q][c0 + m], bf.V[4 * q + 1][c0 + m], bf.V[4 * q + 2][c0 + m],
+                             bf.V[4 * q + 3][c0 + m]};   // V[4q + i][c0 + m]
+        // X = B~ S + M_bk V
+        f32x4 X = z;
+#pragma unroll
+        for (int ti = 0; ti < NTILE; ++ti) {
+            const f32x4 bt = *(const f32x4 *)&bf.B[m][16 * ti + 4 * q];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) X = mfma_f32(bt[i], St[ti][i], X);
+        }
+        {
+            const f32x4 mb = *(const f32x4 *)&bf.M[1][m][4 * q];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) X = mfma_f32(mb[i], vm[i], X);
+        }
+        // O^T, state part (chunk-start state): S^T R~^T
+        f32x4 Ot = z;
+#pragma unroll
+        for (int ti = 0; ti < NTILE; ++ti) {
+            const f32x4 rt = *(const f32x4 *)&bf.R[m][16 * ti + 4 * q];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Ot = mfma_f32(St[ti][i], rt[i], Ot);
+        }
+        // ---- T = (I - M_ba)^-1, after the products above, which do not need
+        // it, so that their matrix-core work overlaps the substitution (1.35
+        // -> 1.33 ms at B8 T4096 H64).  D = 128: formed by wave 0 above
+        // (eight waves would each repeat a substitution: 4.05 -> 3.89 ms
+        // measured at B16 T4096 H32).  D = 64: this wave's copy, lane j < 16
+        // solving column j; with four waves the substitution in every wave
+        // measured faster than wave 0 alone on the matrix cores (1.35 against
+        // 1.40 ms at B8 T4096 H64).  Column j = lane & 15 in every lane group:
+        // row i of M_ba is read as four-float pieces (the same address in
+        // every lane), all before the substitution, and each row's dot
+        // product is split over two accumulators so that only its last term
+        // waits for x_{i-1}. ----
         float(*Tw)[kL + 4] = s.T[D == 64 ? wave : 0];
         if constexpr (D == 64) {
             const int j = lane & 15;
@@ -315,30 +341,6 @@ chunked_f32_kernel(
             lds_wait();   // the wave's own T writes are complete before its reads
         }
 
-        // ---- this wave's columns c0 .. c0 + 15 ----
-        const float vm[4] = {bf.V[4 * q][c0 + m], bf.V[4 * q + 1][c0 + m], bf.V[4 * q + 2][c0 + m],
-                             bf.V[4 * q + 3][c0 + m]};   // V[4q + i][c0 + m]
-        // X = B~ S + M_bk V
-        f32x4 X = z;
-#pragma unroll
-        for (int ti = 0; ti < NTILE; ++ti) {
-            const f32x4 bt = *(const f32x4 *)&bf.B[m][16 * ti + 4 * q];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) X = mfma_f32(bt[i], St[ti][i], X);
-        }
-        {
-            const f32x4 mb = *(const f32x4 *)&bf.M[1][m][4 * q];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) X = mfma_f32(mb[i], vm[i], X);
-        }
-        // O^T, state part (chunk-start state): S^T R~^T
-        f32x4 Ot = z;
-#pragma unroll
-        for (int ti = 0; ti < NTILE; ++ti) {
-            const f32x4 rt = *(const f32x4 *)&bf.R[m][16 * ti + 4 * q];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Ot = mfma_f32(St[ti][i], rt[i], Ot);
-        }
         // U = T X
         f32x4 U = z;
         {
