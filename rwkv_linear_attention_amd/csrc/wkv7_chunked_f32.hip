@@ -23,7 +23,7 @@
 // (m, q) holds rows 16 ti + 4 q + r of column 16 i + m) for the whole
 // sequence.  Per chunk all waves stage the chunk's inputs into LDS (each
 // thread four channels of one token, a channel group's 16 tokens in one
-// 16-lane row; the next chunk's loads are in flight meanwhile), each thread
+// 16-lane row; at D = 64 the next chunk's loads are in flight meanwhile), each thread
 // forms its decay prefix by a scan across its row, the four waves 0..3 form
 // one chunk matrix each, T is formed (D = 64: by every wave, forward
 // substitution with one column per lane; D = 128: by wave 0 on the matrix
