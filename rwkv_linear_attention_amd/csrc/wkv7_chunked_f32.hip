@@ -56,7 +56,6 @@ template <int D> struct F32Cfg {
     static constexpr int NTH = 64 * NW;         // threads: four channels of one token each
     static constexpr int NTILE = D / 16;        // 16-row tiles of the state
     static constexpr int LD = D + 4;            // padded row, floats
-    static constexpr int NBUF = D == 64 ? 2 : 1;   // chunk buffers (two: no end-of-chunk barrier)
 };
 
 // One chunk's tiles.  Tokens are rows; R, B, A, K hold the scaled operands
@@ -71,15 +70,21 @@ template <int D> struct alignas(16) F32Buf {
     int upd[kL];
 };
 
+// One chunk buffer, with a barrier at the end of each chunk before the next
+// one is staged.  At D = 64 that is 36.9 KB of LDS, room for three
+// workgroups per CU (their VGPRs fit too).  Two buffers (68.5 KB, no
+// end-of-chunk barrier, two workgroups per CU) measured 1.327 ms against
+// 1.283 ms at B8 T4096 H64 (512 workgroups), with bit-identical results; a
+// 128-VGPR cap for four workgroups per CU spilled and took 1.66 ms.
 template <int D> struct alignas(16) F32Lds {
-    F32Buf<D> buf[F32Cfg<D>::NBUF];
+    F32Buf<D> buf;
     // D = 64: each wave's copy of T.  D = 128: T^T as wave 0's accumulator,
     // lane (q, m) at [0][m][4q].
     float T[D == 64 ? F32Cfg<D>::NW : 1][kL][kL + 4];
 };
 
 template <int D>
-__global__ __launch_bounds__(F32Cfg<D>::NTH) __attribute__((amdgpu_waves_per_eu(D == 128 ? 4 : 2))) void
+__global__ __launch_bounds__(F32Cfg<D>::NTH) __attribute__((amdgpu_waves_per_eu(D == 128 ? 4 : 3))) void
 chunked_f32_kernel(
     int T, int H, const int32_t *__restrict__ cu_seqlens, const int32_t *__restrict__ state_map, int n_state,
     const float *__restrict__ r, const float *__restrict__ w, const float *__restrict__ k,
@@ -155,7 +160,7 @@ chunked_f32_kernel(
     if (D == 64 && nck > 0) fetch(0);
 
     for (int c = 0; c < nck; ++c) {
-        F32Buf<D> &bf = s.buf[c % C::NBUF];
+        F32Buf<D> &bf = s.buf;
         const int Lc = min(kL, Tn - c * kL);
         if (D == 128) fetch(c);
         // A token that does not update is an identity step whatever its
@@ -231,7 +236,7 @@ chunked_f32_kernel(
                 ov = xsum32(xsum16(ov));
                 if (q == 0) o[((tok0 + c * kL + t) * H + h) * D + c0 + m] = ov;
             }
-            if (C::NBUF == 1) __syncthreads();
+            __syncthreads();   // every wave is done with the buffer
             continue;
         }
 
@@ -375,7 +380,7 @@ chunked_f32_kernel(
         }
         // O^T lane (m, q): token m, columns c0 + 4q .. + 3
         if (m < Lc) *(f32x4 *)(o + ((tok0 + c * kL + m) * H + h) * D + c0 + 4 * q) = Ot;
-        if (C::NBUF == 1) __syncthreads();
+        __syncthreads();   // every wave is done with the buffer before the next chunk is staged
     }
 
     if (sf) {
