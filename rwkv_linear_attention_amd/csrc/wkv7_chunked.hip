@@ -824,6 +824,41 @@ __device__ __forceinline__ void ws_chunk_serial(f32x4 (*S)[WS<D>::NT], const cha
 
 // ---- kernel --------------------------------------------------------------------
 
+// Longest-first order of packed sequences (at most kLongestFirstMax of them,
+// so that every workgroup can rank them all in LDS at its start).  The rank
+// of sequence i is the number of sequences longer than it, or as long with
+// a smaller index: a permutation of 0 .. nseq - 1.  pick[s] becomes the
+// sequence of rank (bh0 + s) / H, the s-th (sequence, head) slot of this
+// workgroup; slots past the last sequence keep -1.  Lengths are clamped as
+// the kernel clamps them.  Every thread of the workgroup calls it (two
+// barriers).
+constexpr int kLongestFirstMax = 128;
+
+template <int NSEQ>
+__device__ __forceinline__ void longest_first(const int32_t *cu, int T, int nseq, int bh0, int H, int *len,
+                                              int *pick)
+{
+    const int tid = threadIdx.x, nt = blockDim.x;
+    for (int i = tid; i < nseq; i += nt) {
+        const int tb = min(max(cu[i], 0), T);
+        len[i] = min(max(cu[i + 1], tb), T) - tb;
+    }
+    if (tid < NSEQ) pick[tid] = -1;
+    __syncthreads();
+    for (int i = tid; i < nseq; i += nt) {
+        const int li = len[i];
+        int rank = 0;
+        for (int j = 0; j < nseq; ++j) {
+            const int lj = len[j];
+            rank += (lj > li || (lj == li && j < i)) ? 1 : 0;
+        }
+#pragma unroll
+        for (int sl = 0; sl < NSEQ; ++sl)
+            if (rank == (bh0 + sl) / H) pick[sl] = i;
+    }
+    __syncthreads();
+}
+
 // GDN = false: generalized-delta-rule inputs r, w, k, v, a, b.  GDN = true:
 // Gated DeltaNet inputs in the same argument slots: r = q, k = k, v = v,
 // w = g [.., H], a = beta [.., H] (b and mask unused).
@@ -902,11 +937,23 @@ __attribute__((amdgpu_waves_per_eu(WS<D>::WAVES_PER_SIMD, WS<D>::WAVES_PER_SIMD)
     const unsigned wg = (!cu_seqlens && nwg % 8u == 0u) ? (blockIdx.x % 8u) * (nwg / 8u) + blockIdx.x / 8u
                                                         : blockIdx.x;
     const int bh = (int)wg * C::NSEQ + seq;
+    // Packed calls with few sequences take them longest first: rank bh / H
+    // of the workgroup order is the sequence of that rank by length, so the
+    // longest chains start in the first dispatch round instead of running
+    // alone at the end when drawn late (the whole workgroup, before any wave
+    // leaves).
+    const int nseq = nbh / H;
+    int sq_ranked = -1;
+    if (cu_seqlens && nseq <= kLongestFirstMax) {
+        __shared__ int lf_len[kLongestFirstMax], lf_pick[C::NSEQ];
+        longest_first<C::NSEQ>(cu_seqlens, T, nseq, (int)wg * C::NSEQ, H, lf_len, lf_pick);
+        sq_ranked = lf_pick[seq];
+    }
     if (bh >= nbh) return;
-    // Sequence sq = bh / H: tokens [tok0, tok0 + Tn) of the (packed) token
-    // axis, initial state row sidx of the state pool (-1: zeros).  Offsets
-    // and state indices read from device memory are clamped into range.
-    const int sq = bh / H, h = bh % H;
+    // Sequence sq: tokens [tok0, tok0 + Tn) of the (packed) token axis,
+    // initial state row sidx of the state pool (-1: zeros).  Offsets and
+    // state indices read from device memory are clamped into range.
+    const int h = bh % H, sq = sq_ranked >= 0 ? sq_ranked : bh / H;
     size_t tok0;
     int Tn, sidx = sq;
     if (cu_seqlens) {
@@ -940,7 +987,7 @@ __attribute__((amdgpu_waves_per_eu(WS<D>::WAVES_PER_SIMD, WS<D>::WAVES_PER_SIMD)
         // ---------------- consumer: columns cbase .. cbase + CW - 1 ----------------
         const int cbase = C::CW * (crank / C::NSEQ);
         f32x4 S[C::NQ][C::NT];
-        const size_t st_base = (size_t)bh * D * D;                     // final state [N, H, D, D]
+        const size_t st_base = ((size_t)sq * H + h) * D * D;          // final state [N, H, D, D]
         const size_t st_in = ((size_t)(sidx < 0 ? 0 : sidx) * H + h) * D * D;   // initial state pool
 #pragma unroll
         for (int q = 0; q < C::NQ; ++q)

@@ -110,3 +110,24 @@ def test_varlen_shared_state_and_empty_axis():
     torch.cuda.synchronize()
     assert o0.shape == (0, H, D)
     assert torch.equal(s0[0], pool_t[1]) and torch.equal(s0[1], pool_t[0]) and torch.all(s0[2] == 0)
+
+
+@pytest.mark.parametrize("N", [128, 129])
+def test_varlen_many_sequences_with_equal_lengths(N):
+    """Many packed sequences with repeated lengths (ties in the chunked
+    kernel's longest-first order), at and just past the largest count that
+    order covers (128; above it the workgroups take the sequences in index
+    order): every sequence against the oracle."""
+    rng = np.random.default_rng(70 + N)
+    lengths = rng.choice([0, 1, 15, 16, 17, 33, 40], size=N).tolist()
+    smap = rng.integers(-1, 4, size=N).tolist()
+    arrs, cu, pool, smap, m = packed_case(lengths, H=3, D=64, seed=71 + N, n_state=3, state_map=smap)
+    o, sf = run_gpu(arrs, cu, pool, smap, m, CHK)
+    outs, states = oracle_varlen(arrs, cu, pool, smap, m, H=3, D=64)
+    for n in range(N):
+        s, e = int(cu[n]), int(cu[n + 1])
+        if e > s:
+            hz.check("bf16", o[s:e], outs[n], sf[n], states[n], f"N={N} seq {n} (T={e - s})")
+        else:
+            exp = np.zeros_like(sf[n]) if not (0 <= smap[n] < 3) else pool[smap[n]]
+            assert np.array_equal(sf[n], exp), f"empty sequence {n} must return its initial state"
