@@ -886,11 +886,19 @@ __global__ __launch_bounds__(kChainWaves * kWave) __attribute__((amdgpu_waves_pe
     if (pair >= 2 * nbh) return;   // the whole workgroup, before any barrier
     const bool fwd = pair < nbh;
     const int bh = fwd ? pair : pair - nbh;
-    const int bb = bh / H, h = bh % H;   // sequence, head
+    const int h = bh % H;   // head
+    // sequence: packed batches of few sequences run longest first (slot bh
+    // takes the sequence of rank bh / H by length; the whole workgroup)
+    int bb = bh / H;
+    if (vg.cu && vg.nseq <= kLongestFirstMax) {
+        __shared__ int lf_len[kLongestFirstMax], lf_pick[1];
+        longest_first<1>(vg.cu, vg.total_T, vg.nseq, bh, H, lf_len, lf_pick);
+        bb = lf_pick[0];
+    }
     const int tid0 = threadIdx.x, wave = tid0 / kWave;
     const int q0 = (tid0 % kWave) >> 4, m0 = tid0 & 15;
     const int cw = kChainCols * cg + 16 * wave;   // this wave's first column
-    const size_t st = (size_t)bh * D * D;   // this (sequence, head) in [B,H,D,D] arrays
+    const size_t st = ((size_t)bb * H + h) * D * D;   // this (sequence, head) in [B,H,D,D] arrays
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
     // tokens tok0 .. tok0 + T - 1; chunk c's checkpoints at index ckidx(c),
     // stored for c < nck_store (fewer than the chunks only for malformed

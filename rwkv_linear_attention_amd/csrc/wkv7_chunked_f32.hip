@@ -96,7 +96,15 @@ chunked_f32_kernel(
     constexpr int NTILE = C::NTILE;
     __shared__ __attribute__((aligned(16))) F32Lds<D> s;
     const int bh = blockIdx.x;
-    const int sq = bh / H, h = bh % H;
+    const int h = bh % H;
+    // Packed batches of few sequences run longest first: workgroup bh takes
+    // the sequence of rank bh / H by length.
+    int sq = bh / H;
+    if (cu_seqlens && (int)gridDim.x / H <= kLongestFirstMax) {
+        __shared__ int lf_len[kLongestFirstMax], lf_pick[1];
+        longest_first<1>(cu_seqlens, T, (int)gridDim.x / H, bh, H, lf_len, lf_pick);
+        sq = lf_pick[0];
+    }
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int q = lane >> 4, m = lane & 15, c0 = 16 * wave;
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
@@ -384,7 +392,7 @@ chunked_f32_kernel(
     }
 
     if (sf) {
-        float *dst = sf + (size_t)bh * D * D;
+        float *dst = sf + ((size_t)sq * H + h) * D * D;
 #pragma unroll
         for (int ti = 0; ti < NTILE; ++ti)
 #pragma unroll

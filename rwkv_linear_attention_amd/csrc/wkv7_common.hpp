@@ -170,4 +170,42 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 // Wave-local LDS ordering: all LDS traffic issued so far has completed.
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// ---- packed sequences ------------------------------------------------------
+// Longest-first order of packed sequences (at most kLongestFirstMax of them,
+// so that every workgroup can rank them all in LDS at its start).  Workgroups
+// are dispatched in index order; taking the longest sequences first keeps a
+// long sequence drawn late from running alone at the end.  The rank
+// of sequence i is the number of sequences longer than it, or as long with
+// a smaller index: a permutation of 0 .. nseq - 1.  pick[s] becomes the
+// sequence of rank (bh0 + s) / H, the s-th (sequence, head) slot of this
+// workgroup; slots past the last sequence keep -1.  Lengths are clamped as
+// the kernel clamps them.  Every thread of the workgroup calls it (two
+// barriers).
+constexpr int kLongestFirstMax = 128;
+
+template <int NSEQ>
+__device__ __forceinline__ void longest_first(const int32_t *cu, int T, int nseq, int bh0, int H, int *len,
+                                              int *pick)
+{
+    const int tid = threadIdx.x, nt = blockDim.x;
+    for (int i = tid; i < nseq; i += nt) {
+        const int tb = min(max(cu[i], 0), T);
+        len[i] = min(max(cu[i + 1], tb), T) - tb;
+    }
+    if (tid < NSEQ) pick[tid] = -1;
+    __syncthreads();
+    for (int i = tid; i < nseq; i += nt) {
+        const int li = len[i];
+        int rank = 0;
+        for (int j = 0; j < nseq; ++j) {
+            const int lj = len[j];
+            rank += (lj > li || (lj == li && j < i)) ? 1 : 0;
+        }
+#pragma unroll
+        for (int sl = 0; sl < NSEQ; ++sl)
+            if (rank == (bh0 + sl) / H) pick[sl] = i;
+    }
+    __syncthreads();
+}
+
 }  // namespace wkv7

@@ -131,3 +131,27 @@ def test_varlen_many_sequences_with_equal_lengths(N):
         else:
             exp = np.zeros_like(sf[n]) if not (0 <= smap[n] < 3) else pool[smap[n]]
             assert np.array_equal(sf[n], exp), f"empty sequence {n} must return its initial state"
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_varlen_f32_chunked_mixed_and_equal_lengths(D):
+    """fp32 I/O on the fp32 chunked kernel over packed sequences of mixed and
+    repeated lengths (its longest-first order), each against the oracle at
+    the fp32 bound."""
+    lengths = [17, 0, 40, 17, 1, 100, 16, 40, 33]
+    smap = [2, -1, 0, 1, 2, 7, 0, 1, 1]
+    arrs, cu, pool, smap, m = packed_case(lengths, H=3, D=D, seed=81 + D, n_state=3, state_map=smap)
+    dev = {x: synth.to_torch(arrs[x], "f32", "cuda") for x in "rwkvab"}
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    o, sf = wkv7.fwd_varlen(*(dev[x] for x in "rwkvab"), t(cu), initial_state=t(pool), state_map=t(smap),
+                            mask=t(m), algo=CHK)
+    torch.cuda.synchronize()
+    o, sf = hz.to_np(o), hz.to_np(sf)
+    outs, states = oracle_varlen(arrs, cu, pool, smap, m, H=3, D=D)
+    for n in range(len(lengths)):
+        s, e = int(cu[n]), int(cu[n + 1])
+        if e > s:
+            hz.check("f32", o[s:e], outs[n], sf[n], states[n], f"f32 varlen seq {n} (T={e - s}) D={D}")
+        else:
+            exp = np.zeros_like(sf[n]) if not (0 <= smap[n] < 3) else pool[smap[n]]
+            assert np.array_equal(sf[n], exp), f"empty sequence {n} must return its initial state"
