@@ -865,7 +865,7 @@ __device__ __forceinline__ void store_slice(float *dst, const f32x4 *St, int q, 
 // and under 40 KB of LDS: four workgroups per CU, so that each CU
 // interleaves the serial phases of one chunk (prefix, chunk matrices, T)
 // with the matrix-core products of others.
-template <int D, typename T_IO, bool GDN>
+template <int D, typename T_IO, bool GDN, bool ORDERED>
 __global__ __launch_bounds__(kChainWaves * kWave) __attribute__((amdgpu_waves_per_eu(4))) void chain_kernel(
     int T, int H, int nbh, const T_IO *__restrict__ r, const T_IO *__restrict__ w,
     const T_IO *__restrict__ k, const T_IO *__restrict__ v, const T_IO *__restrict__ a,
@@ -888,9 +888,10 @@ __global__ __launch_bounds__(kChainWaves * kWave) __attribute__((amdgpu_waves_pe
     const int bh = fwd ? pair : pair - nbh;
     const int h = bh % H;   // head
     // sequence: packed batches of few sequences run longest first (slot bh
-    // takes the sequence of rank bh / H by length; the whole workgroup)
+    // takes the sequence of rank bh / H by length; ORDERED is chosen on the
+    // host for packed calls of at most kLongestFirstMax sequences)
     int bb = bh / H;
-    if (vg.cu && vg.nseq <= kLongestFirstMax) {
+    if constexpr (ORDERED) {
         __shared__ int lf_len[kLongestFirstMax], lf_pick[1];
         longest_first<1>(vg.cu, vg.total_T, vg.nseq, bh, H, lf_len, lf_pick);
         bb = lf_pick[0];
@@ -898,7 +899,7 @@ __global__ __launch_bounds__(kChainWaves * kWave) __attribute__((amdgpu_waves_pe
     const int tid0 = threadIdx.x, wave = tid0 / kWave;
     const int q0 = (tid0 % kWave) >> 4, m0 = tid0 & 15;
     const int cw = kChainCols * cg + 16 * wave;   // this wave's first column
-    const size_t st = ((size_t)bb * H + h) * D * D;   // this (sequence, head) in [B,H,D,D] arrays
+    const size_t st = (size_t)(ORDERED ? bb * H + h : bh) * D * D;   // this (sequence, head) in [B,H,D,D] arrays
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
     // tokens tok0 .. tok0 + T - 1; chunk c's checkpoints at index ckidx(c),
     // stored for c < nck_store (fewer than the chunks only for malformed
@@ -1343,7 +1344,10 @@ hipError_t launch_bwd_d(const BwdArgs &p, hipStream_t stream)
     float *dck = ckpt + (p.cu_seqlens ? nck * p.H : nbh * nck) * D * D;
     // (role, sequence-head) pairs in blocks of eight, each block once per column group
     const size_t grid1 = (2 * nbh + 7) / 8 * 8 * (D / kChainCols);
-    hipLaunchKernelGGL((chain_kernel<D, T_IO, GDN>), dim3((unsigned)grid1), dim3(kChainWaves * kWave), 0, stream, p.T,
+    // packed calls of few sequences run the recurrences longest first
+    auto chain = (p.cu_seqlens && p.B <= kLongestFirstMax) ? chain_kernel<D, T_IO, GDN, true>
+                                                            : chain_kernel<D, T_IO, GDN, false>;
+    hipLaunchKernelGGL(chain, dim3((unsigned)grid1), dim3(kChainWaves * kWave), 0, stream, p.T,
                        p.H, (int)nbh, (const T_IO *)p.r, (const T_IO *)p.w, (const T_IO *)p.k,
                        (const T_IO *)p.v, (const T_IO *)p.a, (const T_IO *)p.b, p.s0, p.mask,
                        (const T_IO *)p.d_o, p.d_sf, ckpt, dck, p.d_s0, vg);

@@ -827,7 +827,7 @@ __device__ __forceinline__ void ws_chunk_serial(f32x4 (*S)[WS<D>::NT], const cha
 // GDN = false: generalized-delta-rule inputs r, w, k, v, a, b.  GDN = true:
 // Gated DeltaNet inputs in the same argument slots: r = q, k = k, v = v,
 // w = g [.., H], a = beta [.., H] (b and mask unused).
-template <int D, bool GDN>
+template <int D, bool GDN, bool ORDERED>
 __global__ __launch_bounds__(64 * WS<D>::NWAVE)
 __attribute__((amdgpu_waves_per_eu(WS<D>::WAVES_PER_SIMD, WS<D>::WAVES_PER_SIMD))) void chunked_ws_kernel(
     int T, int H, int nbh, const int32_t *__restrict__ cu_seqlens, const int32_t *__restrict__ state_map,
@@ -907,18 +907,19 @@ __attribute__((amdgpu_waves_per_eu(WS<D>::WAVES_PER_SIMD, WS<D>::WAVES_PER_SIMD)
     // longest chains start in the first dispatch round instead of running
     // alone at the end when drawn late (the whole workgroup, before any wave
     // leaves).
-    const int nseq = nbh / H;
+    // ORDERED (packed calls of at most kLongestFirstMax sequences, chosen
+    // on the host) compiles this in; the other calls keep the plain order.
     int sq_ranked = -1;
-    if (cu_seqlens && nseq <= kLongestFirstMax) {
+    if constexpr (ORDERED) {
         __shared__ int lf_len[kLongestFirstMax], lf_pick[C::NSEQ];
-        longest_first<C::NSEQ>(cu_seqlens, T, nseq, (int)wg * C::NSEQ, H, lf_len, lf_pick);
+        longest_first<C::NSEQ>(cu_seqlens, T, nbh / H, (int)wg * C::NSEQ, H, lf_len, lf_pick);
         sq_ranked = lf_pick[seq];
     }
     if (bh >= nbh) return;
     // Sequence sq: tokens [tok0, tok0 + Tn) of the (packed) token axis,
     // initial state row sidx of the state pool (-1: zeros).  Offsets and
     // state indices read from device memory are clamped into range.
-    const int h = bh % H, sq = sq_ranked >= 0 ? sq_ranked : bh / H;
+    const int h = bh % H, sq = ORDERED ? sq_ranked : bh / H;
     size_t tok0;
     int Tn, sidx = sq;
     if (cu_seqlens) {
@@ -952,7 +953,7 @@ __attribute__((amdgpu_waves_per_eu(WS<D>::WAVES_PER_SIMD, WS<D>::WAVES_PER_SIMD)
         // ---------------- consumer: columns cbase .. cbase + CW - 1 ----------------
         const int cbase = C::CW * (crank / C::NSEQ);
         f32x4 S[C::NQ][C::NT];
-        const size_t st_base = ((size_t)sq * H + h) * D * D;          // final state [N, H, D, D]
+        const size_t st_base = (size_t)(ORDERED ? sq * H + h : bh) * D * D;   // final state [N, H, D, D]
         const size_t st_in = ((size_t)(sidx < 0 ? 0 : sidx) * H + h) * D * D;   // initial state pool
 #pragma unroll
         for (int q = 0; q < C::NQ; ++q)
@@ -1121,13 +1122,13 @@ __attribute__((amdgpu_waves_per_eu(WS<D>::WAVES_PER_SIMD, WS<D>::WAVES_PER_SIMD)
     }
 }
 
-template <int D, bool GDN>
+template <int D, bool GDN, bool ORDERED>
 static hipError_t launch_ws(const FwdArgs &p, hipStream_t stream)
 {
     using C = WS<D>;
     const int nbh = p.B * p.H;
     const dim3 grid((unsigned)((nbh + C::NSEQ - 1) / C::NSEQ)), block(64 * C::NWAVE);
-    hipLaunchKernelGGL((chunked_ws_kernel<D, GDN>), grid, block, 0, stream, p.T, p.H, nbh, p.cu_seqlens,
+    hipLaunchKernelGGL((chunked_ws_kernel<D, GDN, ORDERED>), grid, block, 0, stream, p.T, p.H, nbh, p.cu_seqlens,
                        p.state_map, p.n_state,
                        (const uint16_t *)p.r, (const uint16_t *)p.w, (const uint16_t *)p.k,
                        (const uint16_t *)p.v, (const uint16_t *)p.a, (const uint16_t *)p.b, p.s0,
@@ -1137,8 +1138,13 @@ static hipError_t launch_ws(const FwdArgs &p, hipStream_t stream)
 
 hipError_t launch_chunked(const FwdArgs &p, hipStream_t stream)
 {
-    if (p.gdn) return p.D == 64 ? launch_ws<64, true>(p, stream) : launch_ws<128, true>(p, stream);
-    return p.D == 64 ? launch_ws<64, false>(p, stream) : launch_ws<128, false>(p, stream);
+    // packed calls of few sequences take them longest first
+    if (p.cu_seqlens && p.B <= kLongestFirstMax) {
+        if (p.gdn) return p.D == 64 ? launch_ws<64, true, true>(p, stream) : launch_ws<128, true, true>(p, stream);
+        return p.D == 64 ? launch_ws<64, false, true>(p, stream) : launch_ws<128, false, true>(p, stream);
+    }
+    if (p.gdn) return p.D == 64 ? launch_ws<64, true, false>(p, stream) : launch_ws<128, true, false>(p, stream);
+    return p.D == 64 ? launch_ws<64, false, false>(p, stream) : launch_ws<128, false, false>(p, stream);
 }
 
 }  // namespace wkv7

@@ -83,7 +83,7 @@ template <int D> struct alignas(16) F32Lds {
     float T[D == 64 ? F32Cfg<D>::NW : 1][kL][kL + 4];
 };
 
-template <int D>
+template <int D, bool ORDERED>
 __global__ __launch_bounds__(F32Cfg<D>::NTH) __attribute__((amdgpu_waves_per_eu(D == 128 ? 4 : 3))) void
 chunked_f32_kernel(
     int T, int H, const int32_t *__restrict__ cu_seqlens, const int32_t *__restrict__ state_map, int n_state,
@@ -98,9 +98,10 @@ chunked_f32_kernel(
     const int bh = blockIdx.x;
     const int h = bh % H;
     // Packed batches of few sequences run longest first: workgroup bh takes
-    // the sequence of rank bh / H by length.
+    // the sequence of rank bh / H by length (ORDERED, chosen on the host for
+    // packed calls of at most kLongestFirstMax sequences).
     int sq = bh / H;
-    if (cu_seqlens && (int)gridDim.x / H <= kLongestFirstMax) {
+    if constexpr (ORDERED) {
         __shared__ int lf_len[kLongestFirstMax], lf_pick[1];
         longest_first<1>(cu_seqlens, T, (int)gridDim.x / H, bh, H, lf_len, lf_pick);
         sq = lf_pick[0];
@@ -392,7 +393,7 @@ chunked_f32_kernel(
     }
 
     if (sf) {
-        float *dst = sf + ((size_t)sq * H + h) * D * D;
+        float *dst = sf + (size_t)(ORDERED ? sq * H + h : bh) * D * D;
 #pragma unroll
         for (int ti = 0; ti < NTILE; ++ti)
 #pragma unroll
@@ -404,7 +405,9 @@ template <int D>
 hipError_t launch_f32(const FwdArgs &p, hipStream_t stream)
 {
     const unsigned nbh = (unsigned)p.B * (unsigned)p.H;
-    hipLaunchKernelGGL(chunked_f32_kernel<D>, dim3(nbh), dim3(F32Cfg<D>::NTH), 0, stream, p.T, p.H, p.cu_seqlens,
+    // packed calls of few sequences take them longest first
+    auto kern = (p.cu_seqlens && p.B <= kLongestFirstMax) ? chunked_f32_kernel<D, true> : chunked_f32_kernel<D, false>;
+    hipLaunchKernelGGL(kern, dim3(nbh), dim3(F32Cfg<D>::NTH), 0, stream, p.T, p.H, p.cu_seqlens,
                        p.state_map, p.n_state, (const float *)p.r, (const float *)p.w, (const float *)p.k,
                        (const float *)p.v, (const float *)p.a, (const float *)p.b, p.s0, p.mask, (float *)p.o,
                        p.sf);
