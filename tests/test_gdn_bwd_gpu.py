@@ -165,3 +165,41 @@ def test_gdn_bwd_varlen_parity(dtype, D, mapped):
         for k in NAMES:
             check_grad(dtype, g[k][tb:te], ref[k][0], f"gdn bwd varlen {dtype} D{D} seq{n} d{k}")
         check_grad("f32", g["s0"][n], ref["s0"][0], f"gdn bwd varlen {dtype} D{D} seq{n} ds0")
+
+
+@pytest.mark.parametrize("N", [128, 129])
+def test_gdn_bwd_varlen_many_sequences_with_equal_lengths(N):
+    """Many packed sequences with repeated lengths (ties in the recurrences'
+    longest-first order), at and just past the largest count that order
+    covers: every sequence's gradients against the oracle.  A one-token
+    sequence from a zero state has dg = 0 identically (the gate only scales
+    a zero state); the documented floor, the sequence's gradient RMS,
+    applies to such tensors alone."""
+    rng = np.random.default_rng(7800 + N)
+    lengths = rng.choice([0, 1, 16, 17, 31], size=N).tolist()
+    TT, H, D = sum(lengths), 2, 64
+    gi = synth.make_gdn(1, TT, H, D, seed=7801 + N, dtype="bf16")
+    pool = (rng.standard_normal((3, H, D, D)) * 0.1).astype(np.float32)
+    smap = rng.integers(-1, 4, size=N).astype(np.int32)
+    d_o = synth.round_to(rng.standard_normal((TT, H, D)).astype(np.float32), "bf16")
+    d_sf = (rng.standard_normal((N, H, D, D)) * 0.5).astype(np.float32)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    dev = {n: synth.to_torch(gi[n][0], "bf16", "cuda") for n in NAMES}
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    g = wkv7.gdn_bwd_varlen(*(dev[n] for n in NAMES), t(cu), synth.to_torch(d_o, "bf16", "cuda"),
+                            initial_state=t(pool), state_map=t(smap), d_final_state=t(d_sf))
+    torch.cuda.synchronize()
+    g = {n: hz.to_np(x) for n, x in g.items()}
+    for n in range(N):
+        tb, te = int(cu[n]), int(cu[n + 1])
+        row = int(smap[n])
+        s0 = pool[row][None] if 0 <= row < 3 else None
+        if te == tb:
+            np.testing.assert_array_equal(g["s0"][n], d_sf[n])
+            continue
+        sl = {k: gi[k][:, tb:te] for k in NAMES}
+        ref = oracle.gdn_bwd(*(sl[k] for k in NAMES), d_o[tb:te][None], s0, d_sf[n][None])
+        fl = float(np.sqrt(np.mean(np.concatenate([ref[k].ravel() for k in NAMES]) ** 2)))
+        for k in NAMES:
+            check_grad("bf16", g[k][tb:te], ref[k][0], f"gdn bwd varlen N={N} seq{n} d{k}", floor=fl)
+        check_grad("f32", g["s0"][n], ref["s0"][0], f"gdn bwd varlen N={N} seq{n} ds0")

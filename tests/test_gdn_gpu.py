@@ -197,3 +197,33 @@ def test_gdn_varlen(D, algo, pool):
             hz.check("bf16", o[s_:e_], o_ref[0], sf[n], s_ref[0], what=f"gdn varlen D{D} seq{n}")
         else:
             np.testing.assert_array_equal(sf[n], s_ref[0])
+
+
+@pytest.mark.parametrize("N", [128, 129])
+def test_gdn_varlen_many_sequences_with_equal_lengths(N):
+    """Many packed Gated DeltaNet sequences with repeated lengths (ties in
+    the chunked kernel's longest-first order), at and just past the largest
+    count that order covers: every sequence against the oracle."""
+    rng = np.random.default_rng(4950 + N)
+    lengths = rng.choice([0, 1, 15, 16, 17, 40], size=N).tolist()
+    TT, H, D = sum(lengths), 3, 64
+    inp = synth.make_gdn(1, TT, H, D, seed=4951 + N, init=False)
+    poolv = (rng.standard_normal((3, H, D, D)) * 0.1).astype(np.float32)
+    smap = rng.integers(-1, 4, size=N).astype(np.int32)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    dev = {n: synth.to_torch(inp[n][0], "bf16", "cuda") for n in NAMES}
+    o, sf = wkv7.gdn_fwd_varlen(*(dev[n] for n in NAMES), torch.from_numpy(cu).cuda(),
+                                initial_state=torch.from_numpy(poolv).cuda(), state_map=torch.from_numpy(smap).cuda(),
+                                algo=CHK)
+    torch.cuda.synchronize()
+    o, sf = hz.to_np(o), hz.to_np(sf)
+    for n in range(N):
+        s_, e_ = int(cu[n]), int(cu[n + 1])
+        row = int(smap[n])
+        s0 = poolv[row:row + 1] if 0 <= row < 3 else None
+        sl = {x: inp[x][:, s_:e_] for x in NAMES}
+        o_ref, s_ref = oracle.gdn_fwd(*(sl[x] for x in NAMES), s0)
+        if e_ > s_:
+            hz.check("bf16", o[s_:e_], o_ref[0], sf[n], s_ref[0], what=f"gdn varlen N={N} seq{n}")
+        else:
+            np.testing.assert_array_equal(sf[n], s_ref[0])
