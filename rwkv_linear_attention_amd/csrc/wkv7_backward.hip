@@ -889,12 +889,14 @@ __global__ __launch_bounds__(kChainWaves * kWave) __attribute__((amdgpu_waves_pe
     const int h = bh % H;   // head
     // sequence: packed batches of few sequences run longest first (slot bh
     // takes the sequence of rank bh / H by length; ORDERED is chosen on the
-    // host for packed calls of at most kLongestFirstMax sequences)
-    int bb = bh / H;
+    // host, use_longest_first)
+    int bb = bh / H, lf_tb = 0, lf_te = 0;
     if constexpr (ORDERED) {
-        __shared__ int lf_len[kLongestFirstMax], lf_pick[1];
-        longest_first<1>(vg.cu, vg.total_T, vg.nseq, bh, H, lf_len, lf_pick);
+        __shared__ int lf_beg[kLongestFirstMax], lf_len[kLongestFirstMax], lf_rank[kLongestFirstMax], lf_pick[1];
+        longest_first<1>(vg.cu, vg.total_T, vg.nseq, bh, H, lf_beg, lf_len, lf_rank, lf_pick);
         bb = lf_pick[0];
+        lf_tb = lf_beg[bb];
+        lf_te = lf_tb + lf_len[bb];
     }
     const int tid0 = threadIdx.x, wave = tid0 / kWave;
     const int q0 = (tid0 % kWave) >> 4, m0 = tid0 & 15;
@@ -908,8 +910,8 @@ __global__ __launch_bounds__(kChainWaves * kWave) __attribute__((amdgpu_waves_pe
     int nck_store;
     const float *s0p = nullptr;
     if (vg.cu) {
-        int tb, te;
-        seq_range(vg, bb, tb, te);
+        int tb = lf_tb, te = lf_te;   // ORDERED: clamped by longest_first
+        if (!ORDERED) seq_range(vg, bb, tb, te);
         tok0 = (size_t)tb;
         T = te - tb;
         ck0 = (size_t)vg.ck_off[bb];
@@ -1345,7 +1347,7 @@ hipError_t launch_bwd_d(const BwdArgs &p, hipStream_t stream)
     // (role, sequence-head) pairs in blocks of eight, each block once per column group
     const size_t grid1 = (2 * nbh + 7) / 8 * 8 * (D / kChainCols);
     // packed calls of few sequences run the recurrences longest first
-    auto chain = (p.cu_seqlens && p.B <= kLongestFirstMax) ? chain_kernel<D, T_IO, GDN, true>
+    auto chain = use_longest_first(p.cu_seqlens != nullptr, p.B, p.T) ? chain_kernel<D, T_IO, GDN, true>
                                                             : chain_kernel<D, T_IO, GDN, false>;
     hipLaunchKernelGGL(chain, dim3((unsigned)grid1), dim3(kChainWaves * kWave), 0, stream, p.T,
                        p.H, (int)nbh, (const T_IO *)p.r, (const T_IO *)p.w, (const T_IO *)p.k,

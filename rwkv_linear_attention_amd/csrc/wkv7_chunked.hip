@@ -907,13 +907,18 @@ __attribute__((amdgpu_waves_per_eu(WS<D>::WAVES_PER_SIMD, WS<D>::WAVES_PER_SIMD)
     // longest chains start in the first dispatch round instead of running
     // alone at the end when drawn late (the whole workgroup, before any wave
     // leaves).
-    // ORDERED (packed calls of at most kLongestFirstMax sequences, chosen
-    // on the host) compiles this in; the other calls keep the plain order.
-    int sq_ranked = -1;
+    // ORDERED (chosen on the host, use_longest_first) compiles this in;
+    // the other calls keep the plain order.
+    int sq_ranked = -1, lf_tb = 0, lf_tn = 0;
     if constexpr (ORDERED) {
-        __shared__ int lf_len[kLongestFirstMax], lf_pick[C::NSEQ];
-        longest_first<C::NSEQ>(cu_seqlens, T, nbh / H, (int)wg * C::NSEQ, H, lf_len, lf_pick);
+        __shared__ int lf_beg[kLongestFirstMax], lf_len[kLongestFirstMax], lf_rank[kLongestFirstMax],
+            lf_pick[C::NSEQ];
+        longest_first<C::NSEQ>(cu_seqlens, T, nbh / H, (int)wg * C::NSEQ, H, lf_beg, lf_len, lf_rank, lf_pick);
         sq_ranked = lf_pick[seq];
+        if (sq_ranked >= 0) {
+            lf_tb = lf_beg[sq_ranked];
+            lf_tn = lf_len[sq_ranked];
+        }
     }
     if (bh >= nbh) return;
     // Sequence sq: tokens [tok0, tok0 + Tn) of the (packed) token axis,
@@ -922,7 +927,10 @@ __attribute__((amdgpu_waves_per_eu(WS<D>::WAVES_PER_SIMD, WS<D>::WAVES_PER_SIMD)
     const int h = bh % H, sq = ORDERED ? sq_ranked : bh / H;
     size_t tok0;
     int Tn, sidx = sq;
-    if (cu_seqlens) {
+    if (ORDERED) {
+        tok0 = (size_t)lf_tb;   // clamped by longest_first
+        Tn = lf_tn;
+    } else if (cu_seqlens) {
         const int t_beg = min(max(cu_seqlens[sq], 0), T);
         const int t_end = min(max(cu_seqlens[sq + 1], t_beg), T);
         tok0 = (size_t)t_beg;
@@ -1138,8 +1146,8 @@ static hipError_t launch_ws(const FwdArgs &p, hipStream_t stream)
 
 hipError_t launch_chunked(const FwdArgs &p, hipStream_t stream)
 {
-    // packed calls of few sequences take them longest first
-    if (p.cu_seqlens && p.B <= kLongestFirstMax) {
+    // packed calls of few, long enough sequences take them longest first
+    if (use_longest_first(p.cu_seqlens != nullptr, p.B, p.T)) {
         if (p.gdn) return p.D == 64 ? launch_ws<64, true, true>(p, stream) : launch_ws<128, true, true>(p, stream);
         return p.D == 64 ? launch_ws<64, false, true>(p, stream) : launch_ws<128, false, true>(p, stream);
     }

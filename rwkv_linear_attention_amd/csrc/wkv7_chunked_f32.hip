@@ -98,13 +98,15 @@ chunked_f32_kernel(
     const int bh = blockIdx.x;
     const int h = bh % H;
     // Packed batches of few sequences run longest first: workgroup bh takes
-    // the sequence of rank bh / H by length (ORDERED, chosen on the host for
-    // packed calls of at most kLongestFirstMax sequences).
-    int sq = bh / H;
+    // the sequence of rank bh / H by length (ORDERED, chosen on the host:
+    // use_longest_first).
+    int sq = bh / H, lf_tb = 0, lf_tn = 0;
     if constexpr (ORDERED) {
-        __shared__ int lf_len[kLongestFirstMax], lf_pick[1];
-        longest_first<1>(cu_seqlens, T, (int)gridDim.x / H, bh, H, lf_len, lf_pick);
+        __shared__ int lf_beg[kLongestFirstMax], lf_len[kLongestFirstMax], lf_rank[kLongestFirstMax], lf_pick[1];
+        longest_first<1>(cu_seqlens, T, (int)gridDim.x / H, bh, H, lf_beg, lf_len, lf_rank, lf_pick);
         sq = lf_pick[0];
+        lf_tb = lf_beg[sq];
+        lf_tn = lf_len[sq];
     }
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int q = lane >> 4, m = lane & 15, c0 = 16 * wave;
@@ -114,7 +116,10 @@ chunked_f32_kernel(
     // initial-state row sidx of the pool (-1: zeros), clamped into range.
     size_t tok0;
     int Tn, sidx = sq;
-    if (cu_seqlens) {
+    if (ORDERED) {
+        tok0 = (size_t)lf_tb;   // clamped by longest_first
+        Tn = lf_tn;
+    } else if (cu_seqlens) {
         const int t_beg = min(max(cu_seqlens[sq], 0), T);
         const int t_end = min(max(cu_seqlens[sq + 1], t_beg), T);
         tok0 = (size_t)t_beg;
@@ -406,7 +411,7 @@ hipError_t launch_f32(const FwdArgs &p, hipStream_t stream)
 {
     const unsigned nbh = (unsigned)p.B * (unsigned)p.H;
     // packed calls of few sequences take them longest first
-    auto kern = (p.cu_seqlens && p.B <= kLongestFirstMax) ? chunked_f32_kernel<D, true> : chunked_f32_kernel<D, false>;
+    auto kern = use_longest_first(p.cu_seqlens != nullptr, p.B, p.T) ? chunked_f32_kernel<D, true> : chunked_f32_kernel<D, false>;
     hipLaunchKernelGGL(kern, dim3(nbh), dim3(F32Cfg<D>::NTH), 0, stream, p.T, p.H, p.cu_seqlens,
                        p.state_map, p.n_state, (const float *)p.r, (const float *)p.w, (const float *)p.k,
                        (const float *)p.v, (const float *)p.a, (const float *)p.b, p.s0, p.mask, (float *)p.o,

@@ -176,7 +176,8 @@ def test_gdn_bwd_varlen_many_sequences_with_equal_lengths(N):
     a zero state); the documented floor, the sequence's gradient RMS,
     applies to such tensors alone."""
     rng = np.random.default_rng(7800 + N)
-    lengths = rng.choice([0, 1, 16, 17, 31], size=N).tolist()
+    lengths = rng.choice([0, 1, 17, 400, 517, 600, 700], size=N).tolist()
+    assert N > 128 or sum(lengths) >= 256 * N   # the longest-first order applies
     TT, H, D = sum(lengths), 2, 64
     gi = synth.make_gdn(1, TT, H, D, seed=7801 + N, dtype="bf16")
     pool = (rng.standard_normal((3, H, D, D)) * 0.1).astype(np.float32)

@@ -205,7 +205,8 @@ def test_gdn_varlen_many_sequences_with_equal_lengths(N):
     the chunked kernel's longest-first order), at and just past the largest
     count that order covers: every sequence against the oracle."""
     rng = np.random.default_rng(4950 + N)
-    lengths = rng.choice([0, 1, 15, 16, 17, 40], size=N).tolist()
+    lengths = rng.choice([0, 1, 16, 400, 517, 600, 700], size=N).tolist()
+    assert N > 128 or sum(lengths) >= 256 * N   # the longest-first order applies
     TT, H, D = sum(lengths), 3, 64
     inp = synth.make_gdn(1, TT, H, D, seed=4951 + N, init=False)
     poolv = (rng.standard_normal((3, H, D, D)) * 0.1).astype(np.float32)

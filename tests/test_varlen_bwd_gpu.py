@@ -121,11 +121,13 @@ def test_bwd_varlen_malformed_offsets_stay_in_bounds():
 @pytest.mark.parametrize("N", [128, 129])
 def test_bwd_varlen_many_sequences_with_equal_lengths(N):
     """Many packed sequences with repeated lengths (ties in the recurrences'
-    longest-first order), at and just past the largest count that order
-    covers (128; above it the index order): every sequence's gradients
+    longest-first order, taken by packed calls of at most 128 sequences
+    averaging at least 256 tokens), at and just past the largest count that
+    order covers (above it the index order): every sequence's gradients
     against the oracle."""
     rng = np.random.default_rng(9300 + N)
-    lengths = rng.choice([0, 1, 16, 17, 31], size=N).tolist()
+    lengths = rng.choice([0, 1, 17, 400, 517, 600, 700], size=N).tolist()
+    assert N > 128 or sum(lengths) >= 256 * N
     smap = rng.integers(-1, 4, size=N).astype(np.int32)
     c = packed_case(lengths, 2, 64, "bf16", seed=9301 + N, n_state=3, smap=smap)
     # one-token sequences from a zero state have dw = 0 identically: the

@@ -115,11 +115,13 @@ def test_varlen_shared_state_and_empty_axis():
 @pytest.mark.parametrize("N", [128, 129])
 def test_varlen_many_sequences_with_equal_lengths(N):
     """Many packed sequences with repeated lengths (ties in the chunked
-    kernel's longest-first order), at and just past the largest count that
-    order covers (128; above it the workgroups take the sequences in index
-    order): every sequence against the oracle."""
+    kernel's longest-first order, which packed calls of at most 128
+    sequences averaging at least 256 tokens take), at and just past the
+    largest count that order covers (above it the workgroups take the
+    sequences in index order): every sequence against the oracle."""
     rng = np.random.default_rng(70 + N)
-    lengths = rng.choice([0, 1, 15, 16, 17, 33, 40], size=N).tolist()
+    lengths = rng.choice([0, 1, 16, 400, 517, 600, 700], size=N).tolist()
+    assert N > 128 or sum(lengths) >= 256 * N
     smap = rng.integers(-1, 4, size=N).tolist()
     arrs, cu, pool, smap, m = packed_case(lengths, H=3, D=64, seed=71 + N, n_state=3, state_map=smap)
     o, sf = run_gpu(arrs, cu, pool, smap, m, CHK)
@@ -136,9 +138,10 @@ def test_varlen_many_sequences_with_equal_lengths(N):
 @pytest.mark.parametrize("D", [64, 128])
 def test_varlen_f32_chunked_mixed_and_equal_lengths(D):
     """fp32 I/O on the fp32 chunked kernel over packed sequences of mixed and
-    repeated lengths (its longest-first order), each against the oracle at
-    the fp32 bound."""
-    lengths = [17, 0, 40, 17, 1, 100, 16, 40, 33]
+    repeated lengths averaging over 256 tokens (its longest-first order),
+    each against the oracle at the fp32 bound."""
+    lengths = [300, 0, 517, 300, 1, 700, 16, 517, 33]
+    assert sum(lengths) >= 256 * len(lengths)
     smap = [2, -1, 0, 1, 2, 7, 0, 1, 1]
     arrs, cu, pool, smap, m = packed_case(lengths, H=3, D=D, seed=81 + D, n_state=3, state_map=smap)
     dev = {x: synth.to_torch(arrs[x], "f32", "cuda") for x in "rwkvab"}
