@@ -133,3 +133,18 @@ def test_bwd_varlen_many_sequences_with_equal_lengths(N):
     # one-token sequences from a zero state have dw = 0 identically: the
     # documented floor (the call's gradient RMS) applies to those alone
     check_against_oracle(c, run_gpu(c), f"bwd varlen N={N}", vanishing_floor=True)
+
+
+def test_bwd_varlen_longest_first_malformed_offsets_stay_in_bounds():
+    """The same saturation under the recurrences' longest-first order (3
+    sequences averaging 341 tokens, overlapping): the call returns
+    normally with finite state gradients, and the first sequence, whose
+    checkpoints precede the overlap in chunk order, is still right."""
+    H, D = 1, 64
+    c = packed_case([1024], H, D, "bf16", seed=9510, masked=False)
+    c["cu"] = np.array([0, 1024, 0, 1024], np.int32)   # 64 + 0 + 64 chunks > capacity 67
+    c["d_sf"] = np.zeros((3, H, D, D), np.float32)
+    g = run_gpu(c)
+    assert np.all(np.isfinite(g["s0"]))
+    ref = oracle.bwd(*(c["x"][k][None] for k in NAMES), c["d_o"][None], None, None, None)
+    check_grad("f32", g["s0"][0], ref["s0"][0], "bwd varlen malformed (longest first) seq0 ds0")

@@ -158,3 +158,27 @@ def test_varlen_f32_chunked_mixed_and_equal_lengths(D):
         else:
             exp = np.zeros_like(sf[n]) if not (0 <= smap[n] < 3) else pool[smap[n]]
             assert np.array_equal(sf[n], exp), f"empty sequence {n} must return its initial state"
+
+
+def test_varlen_longest_first_with_decreasing_offsets():
+    """Decreasing offsets under the longest-first order (3 sequences
+    averaging 400 tokens): lengths are clamped as in index order, so
+    sequence 1 is empty and sequences 0 and 2 overlap on tokens 300..599.
+    Each final state is that of its clamped range; outputs outside the
+    overlap are those of the one sequence that covers them."""
+    H, D, TT = 2, 64, 1200
+    arrs, _, pool, _, m = packed_case([TT], H=H, D=D, seed=91, n_state=3, state_map=[0])
+    cu = np.array([0, 600, 300, 1200], np.int32)
+    smap = np.array([0, 1, 2], np.int32)
+    o, sf = run_gpu(arrs, cu, pool, smap, m, CHK)
+    ranges = [(0, 600), (600, 600), (300, 1200)]
+    for n, (s, e) in enumerate(ranges):
+        inp = {x: arrs[x][None, s:e] for x in "rwkvab"}
+        inp["s0"] = pool[n:n + 1]
+        inp["mask"] = m[None, s:e]
+        if e == s:
+            assert np.array_equal(sf[n], pool[n]), "an empty sequence returns its initial state"
+            continue
+        o_ref, s_ref = hz.oracle_fwd(inp)
+        keep = slice(0, 300) if n == 0 else slice(300, 900)   # rows outside the overlap
+        hz.check("bf16", o[s:e][keep], o_ref[0][keep], sf[n], s_ref[0], f"decreasing offsets seq {n}")
